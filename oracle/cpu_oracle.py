@@ -1,0 +1,352 @@
+"""Plain CPU oracle of the DFlash 2 draft-select-verify step (test infrastructure).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg use this
+module; the HIP product path shares no code with it.
+
+Sources (cited by page title and section):
+  [POST]   "DFlash 2: Keep Drafting Parallel" (Inco AI; Chinese translations
+           on the mynewscn and twiscan pages).
+  [GLONCE] "Inco AI's DFlash 2 lifts LLM decoding output 16-25%" (Glonce).
+
+Readings of points the pages leave open are stated where they are used.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+
+K = 16  # candidates kept per position ([POST] "A lightweight path selector")
+
+
+# ------------------------------------------------------------------ numbers
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns (uint16) as fp64: a bf16 number is the
+    upper half of an IEEE single."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def round_to_bf16(v: np.ndarray) -> np.ndarray:
+    """Round fp64 values to the nearest bf16 value, ties to even; result in fp64.
+
+    bf16 keeps 8 significant bits, so a value in [2^(e-1), 2^e) is rounded to
+    a multiple of 2^(e-8); below the smallest normal (2^-126) the spacing stays
+    2^-133.  Values past the largest finite bf16 after rounding become inf.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)
+    e = np.maximum(e, -125)
+    q = np.ldexp(np.rint(np.ldexp(v, 8 - e)), e - 8)
+    big = np.abs(q) > _BF16_MAX
+    if np.any(big):
+        q = np.where(big, np.copysign(np.inf, q), q)
+    return q
+
+
+def round_to_dtype(v: np.ndarray, dtype: str) -> np.ndarray:
+    """Round fp64 values once to the storage type ("bf16" or "f32"); fp64 out."""
+    if dtype == "bf16":
+        return round_to_bf16(v)
+    return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def as_f64(a, dtype: str) -> np.ndarray:
+    """Exact fp64 value of a stored tensor (bf16 bits or fp32)."""
+    if dtype == "bf16":
+        return bf16_bits_to_f64(a)
+    return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------------ a1 conv
+def twotap_conv(x: np.ndarray, anchor_h: Optional[np.ndarray], k0: np.ndarray,
+                k1: np.ndarray, proj: Optional[np.ndarray] = None,
+                groups: int = 1) -> np.ndarray:
+    """Two-tap dynamic depthwise convolution over one block, exact in fp64.
+
+    [POST] "A lightweight local convolution", eq. Conv_k: every position t
+    mixes its own representation with its predecessor's through two
+    per-channel taps,  y_t = k_{t,0} * x_t + k_{t,1} * x_{t-1}.
+    Each tap is a learnable base tap plus a small correction computed from the
+    current hidden state x_t, one correction shared by a group of channels
+    (the post shares one per 16 channels; the conv-heavy workload uses a single
+    [H x 2] projection, i.e. one group).  Position 0 reads the last verified
+    token's representation (the anchor) in place of x_{-1} (same section and
+    Fig. 4).
+
+    Readings: the correction is linear in x_t with no bias or activation
+    (Delta[t, g, j] = sum_c x_t[c] * proj[c, 2g + j]); channel c belongs to
+    group c // (H / groups); no residual is added; a missing anchor is zero
+    and a missing proj means static taps.
+
+    x [B, L, H], anchor_h [B, H] or None, k0/k1 [H], proj [H, 2*groups] or
+    None, all fp64.  Returns the exact y [B, L, H] in fp64 (unrounded).
+    """
+    B, L, H = x.shape
+    if anchor_h is None:
+        anchor_h = np.zeros((B, H))
+    prev = np.concatenate([anchor_h[:, None, :], x[:, :-1, :]], axis=1)
+    if proj is None:
+        c0 = np.broadcast_to(k0, (B, L, H))
+        c1 = np.broadcast_to(k1, (B, L, H))
+    else:
+        delta = (x.reshape(B * L, H) @ proj).reshape(B, L, groups, 2)
+        group_of_channel = np.arange(H) // (H // groups)
+        c0 = k0[None, None, :] + delta[:, :, group_of_channel, 0]
+        c1 = k1[None, None, :] + delta[:, :, group_of_channel, 1]
+    return c0 * x + c1 * prev
+
+
+def conv_chain(x: np.ndarray, convs, dtype: str) -> np.ndarray:
+    """Chained conv applications as the drafter body places them, one before
+    and one after each sublayer ([POST] "A lightweight local convolution",
+    Fig. 4); the sublayers themselves need trained weights and are taken as
+    identity.  Each application's output is rounded once to the storage type
+    and feeds the next.  x fp64 [B, L, H]; returns fp64 values of the stored
+    output."""
+    y = x
+    for c in convs:
+        ah = c["anchor_h"]
+        y = round_to_dtype(twotap_conv(y, ah, c["k0"], c["k1"], c.get("proj"),
+                                       c.get("groups", 1)), dtype)
+    return y
+
+
+# ------------------------------------------------------------------ a2 logits
+def lm_logits(y: np.ndarray, W: np.ndarray, w_dtype: str, chunk_elems: int = 1 << 26) -> np.ndarray:
+    """Drafter logits U_t(b) for every token b ([POST] "A lightweight path
+    selector": the unary term is the drafter's own logit).
+
+    z[m, n] = sum_c y[m, c] * W[n, c], evaluated in fp64 from the exact
+    operand values and rounded once to fp32.  y [M, H] fp64; W [V, H] stored
+    (bf16 bits or fp32), decoded a slice of rows at a time.  Returns fp32 [M, V].
+    """
+    M, H = y.shape
+    V = W.shape[0]
+    z = np.empty((M, V), dtype=np.float32)
+    step = max(1, chunk_elems // H)
+    for n0 in range(0, V, step):
+        Wc = as_f64(W[n0:n0 + step], w_dtype)
+        z[:, n0:n0 + step] = (y @ Wc.T).astype(np.float32)
+    return z
+
+
+# ------------------------------------------------------------------ a3 top-16
+def canonical_logits(z: np.ndarray) -> np.ndarray:
+    """Order-canonical copy of fp32 logits: -0 becomes +0 and NaN becomes
+    -inf (reading: NaN ranks below every number)."""
+    z = np.asarray(z, dtype=np.float32)
+    z = np.where(np.isnan(z), np.float32(-np.inf), z)
+    return z + np.float32(0.0)
+
+
+def topk16(z: np.ndarray):
+    """Top-16 candidates per row ([POST] "A lightweight path selector": the
+    drafter keeps its 16 best tokens at every position).
+
+    The first 16 indices of the row sorted by (value descending, index
+    ascending): equal values go to the lowest token id first (the stress
+    workload's tie rule).  Decided on the fp32 logits.  z [M, V] fp32.
+    Returns (top_val fp32 [M, 16], top_idx int32 [M, 16]).
+    """
+    zc = canonical_logits(z)
+    M, V = zc.shape
+    idx = np.broadcast_to(np.arange(V), (M, V))
+    order = np.lexsort((idx, -zc), axis=-1)[:, :K]
+    return np.take_along_axis(zc, order, axis=1), order.astype(np.int32)
+
+
+def topk_gaps(z: np.ndarray, top_val: np.ndarray) -> np.ndarray:
+    """Per slot s, the smaller gap to its neighbours in the sorted order
+    (slot 15 also against the 17th largest value): how far a candidate is
+    from swapping with the next one.  Returns fp64 [M, 16]."""
+    zc = canonical_logits(z).astype(np.float64)
+    M = zc.shape[0]
+    v17 = -np.sort(-zc, axis=1)[:, K]  # the 17th value
+    vals = np.concatenate([top_val.astype(np.float64), v17[:, None]], axis=1)
+    d = vals[:, :-1] - vals[:, 1:]              # gap below slot s
+    up = np.concatenate([np.full((M, 1), np.inf), d[:, :-1]], axis=1)
+    return np.minimum(up, d)
+
+
+# ------------------------------------------------------------------ a4 pair scores
+def pair_scores(top_val: np.ndarray, top_idx: np.ndarray, anchor_tok: Optional[np.ndarray],
+                U: np.ndarray, Vf: np.ndarray, uv_dtype: str):
+    """Scores of every adjacent candidate pair ([POST] "A lightweight path
+    selector", eq. S_t(a, b)): the candidate's own logit plus a low-rank
+    match between the previous token a and the candidate b.
+
+    In the workloads' ungated form the match is u_a . v_b with per-token
+    factor tables U, V [vocab, r] (the post's context gate is taken as all
+    ones).  Position 0's previous token is the last verified token (the walk
+    starts from it); with anchor_tok None its match term is 0.
+
+      S0[b, j]        = top_val[b, 0, j] + U[anchor_tok[b]] . V[top_idx[b, 0, j]]
+      S[b, t-1, i, j] = top_val[b, t, j] + U[top_idx[b, t-1, i]] . V[top_idx[b, t, j]]
+
+    Evaluated in fp64 from the exact inputs, rounded once to fp32.
+    top_val fp32 [B, L, 16], top_idx int [B, L, 16].
+    Returns S0 fp32 [B, 16], S fp32 [B, L-1, 16, 16].
+    """
+    Uf = as_f64(U, uv_dtype)
+    Vff = as_f64(Vf, uv_dtype)
+    tv = top_val.astype(np.float64)
+    cu = Uf[top_idx]        # [B, L, 16, r]  factor of each candidate as "previous"
+    cv = Vff[top_idx]       # [B, L, 16, r]  factor of each candidate as "current"
+    if anchor_tok is None:
+        s0 = tv[:, 0, :]
+    else:
+        ua = Uf[np.asarray(anchor_tok)]                      # [B, r]
+        s0 = tv[:, 0, :] + np.einsum("br,bjr->bj", ua, cv[:, 0])
+    match = np.einsum("btir,btjr->btij", cu[:, :-1], cv[:, 1:])
+    S = tv[:, 1:, None, :] + match
+    return s0.astype(np.float32), S.astype(np.float32)
+
+
+# ------------------------------------------------------------------ a5 path walk
+def path_select(S0: np.ndarray, S: np.ndarray, top_idx: np.ndarray):
+    """Exact max-plus (Viterbi) walk over the precomputed pair scores.
+
+    [POST] "A lightweight path selector": the only serial step walks the
+    precomputed scores from the last verified token to one path.  The post's
+    walk follows the best successor greedily; the step built here takes the
+    exact maximum over all 16^L slot paths of S0[p0] + sum_t S[t-1, p_{t-1}, p_t],
+    by the max-plus recursion
+
+      delta_0 = S0,  delta_t[j] = max_i fl32(delta_{t-1}[i] + S[t-1, i, j]),
+
+    deciding in fp32 (the kernel's precision).  Ties go to the lowest slot at
+    every maximum and at the final argmax, which selects, among optimal paths,
+    the one smallest in (p_{L-1}, p_{L-2}, ..., p_0) order.
+
+    S0 fp32 [B, 16], S fp32 [B, L-1, 16, 16], top_idx [B, L, 16].
+    Returns (path_slot int32 [B, L], path_tok int32 [B, L], path_score fp32 [B]).
+    """
+    S0 = np.asarray(S0, dtype=np.float32)
+    S = np.asarray(S, dtype=np.float32)
+    B = S0.shape[0]
+    L = S.shape[1] + 1
+    delta = S0.copy()
+    back = np.zeros((B, L, K), dtype=np.int64)
+    for t in range(1, L):
+        cand = delta[:, :, None] + S[:, t - 1]          # [B, i, j], fp32 sums
+        back[:, t] = np.argmax(cand, axis=1)             # first (lowest) i at the max
+        delta = np.take_along_axis(cand, back[:, t][:, None, :], axis=1)[:, 0]
+    slot = np.zeros((B, L), dtype=np.int64)
+    slot[:, L - 1] = np.argmax(delta, axis=1)
+    score = delta[np.arange(B), slot[:, L - 1]]
+    for t in range(L - 1, 0, -1):
+        slot[:, t - 1] = back[np.arange(B), t, slot[:, t]]
+    tok = np.take_along_axis(np.asarray(top_idx), slot[:, :, None], axis=2)[:, :, 0]
+    return slot.astype(np.int32), tok.astype(np.int32), score.astype(np.float32)
+
+
+def path_scores_f64(S0: np.ndarray, S: np.ndarray, slot: np.ndarray) -> np.ndarray:
+    """fp64 score of given slot paths: S0[p0] + sum_t S[t-1, p_{t-1}, p_t]."""
+    S0 = np.asarray(S0, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    B, L = slot.shape
+    b = np.arange(B)
+    sc = S0[b, slot[:, 0]]
+    for t in range(1, L):
+        sc = sc + S[b, t - 1, slot[:, t - 1], slot[:, t]]
+    return sc
+
+
+def path_margin(S0: np.ndarray, S: np.ndarray) -> np.ndarray:
+    """Gap between the best and the second-best path score, in fp64.
+
+    Forward maxima alpha_t[j] (best score of a prefix ending at slot j) and
+    backward maxima beta_t[j] (best score of a suffix leaving slot j) give
+    mu_t[j] = alpha_t[j] + beta_t[j], the best score of any path through j
+    at t.  Every path other than the best differs from it somewhere, so the
+    second-best score is max over t and j != p*_t of mu_t[j].  Returns [B].
+    """
+    S0 = np.asarray(S0, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    B = S0.shape[0]
+    L = S.shape[1] + 1
+    alpha = np.zeros((B, L, K))
+    beta = np.zeros((B, L, K))
+    alpha[:, 0] = S0
+    for t in range(1, L):
+        alpha[:, t] = np.max(alpha[:, t - 1][:, :, None] + S[:, t - 1], axis=1)
+    for t in range(L - 2, -1, -1):
+        beta[:, t] = np.max(S[:, t] + beta[:, t + 1][:, None, :], axis=2)
+    mu = alpha + beta
+    best = np.max(mu[:, L - 1], axis=1)
+    pstar = np.argmax(mu, axis=2)                    # best path's slot at each t
+    masked = mu.copy()
+    np.put_along_axis(masked, pstar[:, :, None], -np.inf, axis=2)
+    second = np.max(masked.reshape(B, -1), axis=1)
+    return best - second
+
+
+# ------------------------------------------------------------------ a6 verify
+def verify_greedy(path_tok: np.ndarray, target: np.ndarray):
+    """Greedy verification and acceptance length ([POST] "The right token is
+    already in the candidates", Table 1 caption: the acceptance length counts
+    the verifier's next token).
+
+    The target's argmax per position target [B, L+1] (target[:, L] is the
+    verifier's token after a fully accepted block).  n = number of leading
+    positions where the path equals the target; accept_len = n + 1 and the
+    verifier contributes target[b, n].  Returns (accept_len, next_tok) int32 [B].
+    """
+    path_tok = np.asarray(path_tok)
+    target = np.asarray(target)
+    B, L = path_tok.shape
+    match = path_tok == target[:, :L]
+    n = np.cumprod(match, axis=1).sum(axis=1)
+    return (n + 1).astype(np.int32), target[np.arange(B), n].astype(np.int32)
+
+
+def oracle_selector(top_idx: np.ndarray, target: np.ndarray) -> np.ndarray:
+    """The post's oracle selector ([POST] "The right token is already in the
+    candidates"): at every position it picks the target's token whenever it is
+    among the 16 candidates (else the top-1).  Returns path_tok [B, L]."""
+    top_idx = np.asarray(top_idx)
+    B, L, _ = top_idx.shape
+    tgt = np.asarray(target)[:, :L]
+    hit = (top_idx == tgt[:, :, None]).any(axis=2)
+    return np.where(hit, tgt, top_idx[:, :, 0]).astype(np.int32)
+
+
+def expected_acceptance(p) -> float:
+    """Mean acceptance length when position t is right with probability p[t],
+    given all earlier positions are right (Table 1's conditional recall):
+    E = 1 + sum_k prod_{t <= k} p[t]  (the 1 is the verifier's token)."""
+    return float(1.0 + np.sum(np.cumprod(np.asarray(p, dtype=np.float64))))
+
+
+# ------------------------------------------------------------------ composition
+def run_step_front(w, inp: Dict[str, object], blocks: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """conv chain -> logits -> top-16 -> pair scores -> path, for the given
+    blocks (all when None).  Verification needs targets and is run by the
+    caller with verify_greedy.  Returns every intermediate."""
+    x = inp["x"]
+    convs = inp["convs"]
+    anchor_tok = inp["anchor_tok"]
+    if blocks is not None:
+        x = x[blocks]
+        convs = [dict(c, anchor_h=c["anchor_h"][blocks]) for c in convs]
+        anchor_tok = anchor_tok[blocks]
+    xd = as_f64(x, w.dtype)
+    cd = []
+    for c in convs:
+        cd.append({"anchor_h": as_f64(c["anchor_h"], w.dtype),
+                   "k0": np.asarray(c["k0"], np.float64), "k1": np.asarray(c["k1"], np.float64),
+                   "proj": None if c["proj"] is None else np.asarray(c["proj"], np.float64)})
+    y = conv_chain(xd, cd, w.dtype)
+    Bs, L, H = y.shape
+    z = lm_logits(y.reshape(Bs * L, H), inp["W"], w.dtype)
+    top_val, top_idx = topk16(z)
+    tv = top_val.reshape(Bs, L, K)
+    ti = top_idx.reshape(Bs, L, K)
+    S0, S = pair_scores(tv, ti, anchor_tok, inp["U"], inp["Vf"], w.dtype)
+    slot, tok, score = path_select(S0, S, ti)
+    return {"y": y, "z": z, "top_val": tv, "top_idx": ti, "S0": S0, "S": S,
+            "path_slot": slot, "path_tok": tok, "path_score": score}

@@ -1,0 +1,411 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test ties one oracle function to brute force, a closed form, the pages'
+printed numbers, an invariant, or a special case with a known answer, chosen
+so that a plausible slip (a dropped term, a swapped index, a transposed
+operand, a wrong tie rule, double rounding) fails at least one of them.
+"""
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as WL
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------ bf16 rounding
+def test_bf16_round_matches_torch_cast_on_f32_values():
+    import torch
+
+    g = np.random.default_rng(1)
+    v = np.concatenate([
+        g.standard_normal(20000).astype(np.float32),
+        (g.standard_normal(2000) * 1e-39).astype(np.float32),   # subnormal range
+        (g.standard_normal(2000) * 1e30).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, -1.0, 3.0e38], dtype=np.float32),
+    ])
+    want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.round_to_bf16(v.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_bf16_round_ties_to_even_and_rounds_once():
+    one = 1.0
+    u = 2.0 ** -7                      # bf16 spacing at 1
+    cases = {
+        one + u / 2: one,              # midpoint -> even (1.0)
+        one + 3 * u / 2: one + 2 * u,  # midpoint -> even (1 + 2u)
+        one + u / 2 + 2.0 ** -30: one + u,   # just above a midpoint: up.  An fp32
+        # intermediate would first drop 2^-30 and then round the midpoint down.
+        -(one + u / 2 + 2.0 ** -30): -(one + u),
+        2.0 ** -133 * 0.75: 2.0 ** -133,     # smallest subnormal spacing
+    }
+    for v, want in cases.items():
+        assert O.round_to_bf16(np.array([v]))[0] == want, v
+
+
+# ------------------------------------------------------------------ conv
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def test_conv_identity_taps_return_input_exactly():
+    x, a = _rand((3, 5, 16), 2), _rand((3, 16), 3)
+    y = O.twotap_conv(x, a, np.ones(16), np.zeros(16))
+    np.testing.assert_array_equal(y, x)
+
+
+def test_conv_shift_taps_read_predecessor_and_anchor():
+    x, a = _rand((3, 5, 16), 4), _rand((3, 16), 5)
+    y = O.twotap_conv(x, a, np.zeros(16), np.ones(16))
+    np.testing.assert_array_equal(y[:, 1:], x[:, :-1])
+    np.testing.assert_array_equal(y[:, 0], a)           # position 0 reads the anchor
+    y0 = O.twotap_conv(x, None, np.zeros(16), np.ones(16))
+    np.testing.assert_array_equal(y0[:, 0], np.zeros((3, 16)))
+
+
+def test_conv_one_hot_rows_recover_taps_and_corrections():
+    H, G = 32, 4
+    k0, k1 = _rand(H, 6), _rand(H, 7)
+    P = _rand((H, 2 * G), 8)
+    group = np.array([0] * 8 + [1] * 8 + [2] * 8 + [3] * 8)   # channel -> group, written out
+    c, t = 9, 2
+    x = np.zeros((1, 4, H))
+    x[0, t, c] = 1.0
+    y = O.twotap_conv(x, np.zeros((1, H)), k0, k1, P, G)
+    # position t: only channel c is live, with tap k0[c] + P[c, 2*group(c)]
+    want_t = np.zeros(H)
+    want_t[c] = k0[c] + P[c, 2 * group[c]]
+    np.testing.assert_allclose(y[0, t], want_t, rtol=0, atol=1e-15)
+    # position t+1 (x_{t+1} = 0, so no correction) reads x_t through k1
+    want_t1 = np.zeros(H)
+    want_t1[c] = k1[c]
+    np.testing.assert_allclose(y[0, t + 1], want_t1, rtol=0, atol=1e-15)
+    # predecessor all ones: every channel shows its own group's second correction,
+    # taken from x_t's channel c
+    x2 = np.zeros((1, 4, H))
+    x2[0, t - 1, :] = 1.0
+    x2[0, t, c] = 1.0
+    y2 = O.twotap_conv(x2, np.zeros((1, H)), k0, k1, P, G)
+    want = k1 + P[c, 2 * group + 1]
+    want[c] += k0[c] + P[c, 2 * group[c]]
+    np.testing.assert_allclose(y2[0, t], want, rtol=1e-14, atol=1e-15)
+
+
+def test_conv_chain_rounds_each_application_to_storage_type():
+    x = np.full((1, 2, 8), 1.0)
+    conv = {"anchor_h": np.zeros((1, 8)), "k0": np.full(8, 1.0 + 2.0 ** -8),
+            "k1": np.zeros(8), "proj": None}
+    # 1 * (1 + 2^-8) is a bf16 midpoint: rounds to 1.0 (even) each time
+    y = O.conv_chain(x, [conv, conv, conv], "bf16")
+    np.testing.assert_array_equal(y, x)
+    y32 = O.conv_chain(x, [conv], "f32")
+    np.testing.assert_array_equal(y32, np.full((1, 2, 8), 1.0 + 2.0 ** -8))
+
+
+# ------------------------------------------------------------------ logits
+def test_logits_one_hot_rows_return_weight_columns():
+    V, H = 40, 12
+    W = np.random.default_rng(9).standard_normal((V, H)).astype(np.float32)
+    y = np.eye(H)[[3, 0, 11]]
+    z = O.lm_logits(y, W, "f32")
+    np.testing.assert_array_equal(z, W[:, [3, 0, 11]].T)
+
+
+def test_logits_bf16_weights_decode_exactly():
+    V, H = 16, 8
+    vals = np.random.default_rng(10).standard_normal((V, H)).astype(np.float32)
+    bits = WL.to_bf16_bits(vals)
+    z = O.lm_logits(np.eye(H), bits, "bf16")
+    import torch
+    want = torch.from_numpy(vals).to(torch.bfloat16).float().numpy().T
+    np.testing.assert_array_equal(z, want)
+
+
+def test_logits_are_exact_sums_rounded_once():
+    # 2^24 + 1 + 1: exact 16777218 is an fp32 number; a running fp32 sum
+    # would stall at 2^24.
+    y = np.array([[2.0 ** 24, 1.0, 1.0]])
+    W = np.ones((2, 3), dtype=np.float32)
+    np.testing.assert_array_equal(O.lm_logits(y, W, "f32"), [[16777218.0, 16777218.0]])
+    # chunking over the vocabulary does not change anything
+    W2 = np.random.default_rng(11).standard_normal((50, 7)).astype(np.float32)
+    y2 = np.random.default_rng(12).standard_normal((3, 7))
+    np.testing.assert_array_equal(O.lm_logits(y2, W2, "f32", chunk_elems=7 * 3),
+                                  O.lm_logits(y2, W2, "f32"))
+
+
+# ------------------------------------------------------------------ top-16
+def _brute_topk(z):
+    """Rank by counting: rank(n) = #{m beating n}; m beats n if its value is
+    larger, or equal with a smaller index.  NaN counts as -inf, -0 == +0."""
+    z = [(-np.inf if np.isnan(v) else float(v)) for v in z]
+    V = len(z)
+    rank = [sum(1 for m in range(V) if z[m] > z[n] or (z[m] == z[n] and m < n)) for n in range(V)]
+    by_rank = sorted(range(V), key=lambda n: rank[n])
+    return by_rank[:16]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_topk_matches_rank_counting_with_ties_zeros_nan_inf(seed):
+    g = np.random.default_rng(seed)
+    V = 200
+    z = np.round(g.standard_normal((3, V)) * 4) / 4          # many exact ties
+    z[0, 5], z[0, 77], z[0, 150] = np.inf, np.nan, -np.inf
+    z[1, :30] = 0.0
+    z[1, 30:60] = -0.0
+    z[1, 60:] = -1.0
+    z[2, ::7] = z[2].max()
+    z = z.astype(np.float32)
+    tv, ti = O.topk16(z)
+    for m in range(3):
+        want = _brute_topk(z[m])
+        assert ti[m].tolist() == want
+        zc = np.where(np.isnan(z[m]), -np.inf, z[m])
+        np.testing.assert_array_equal(tv[m], zc[want])
+    assert not np.signbit(tv[1]).any()   # -0 is reported as +0
+
+
+def test_topk_gaps():
+    z = np.array([[5.0, 1.0, 3.0] + [0.0] * 14 + [-1.0]], dtype=np.float32)
+    tv, ti = O.topk16(z)
+    gaps = O.topk_gaps(z, tv)
+    assert ti[0, :3].tolist() == [0, 2, 1]
+    assert gaps[0, 0] == 2.0 and gaps[0, 1] == 2.0 and gaps[0, 2] == 1.0
+    assert gaps[0, 3] == 0.0     # tied zeros
+    z2 = np.array([np.arange(17, 0, -1)], dtype=np.float32)   # 17, 16, ..., 1
+    g2 = O.topk_gaps(z2, O.topk16(z2)[0])
+    np.testing.assert_array_equal(g2[0], np.ones(16))
+
+
+# ------------------------------------------------------------------ pair scores
+def test_pair_scores_zero_factors_reduce_to_unary():
+    g = np.random.default_rng(13)
+    B, L, V, r = 2, 5, 64, 8
+    tv = g.standard_normal((B, L, 16)).astype(np.float32)
+    ti = g.integers(0, V, (B, L, 16)).astype(np.int32)
+    Z = np.zeros((V, r), dtype=np.float32)
+    F = g.standard_normal((V, r)).astype(np.float32)
+    for U, Vf in ((Z, F), (F, Z)):
+        S0, S = O.pair_scores(tv, ti, g.integers(0, V, B), U, Vf, "f32")
+        np.testing.assert_array_equal(S0, tv[:, 0])
+        np.testing.assert_array_equal(S, np.broadcast_to(tv[:, 1:, None, :], S.shape))
+    S0, _ = O.pair_scores(tv, ti, None, F, F, "f32")
+    np.testing.assert_array_equal(S0, tv[:, 0])
+
+
+def test_pair_scores_one_hot_factors_give_indicator_matches():
+    # U[tok] = e_{f(tok)}, V[tok] = e_{g(tok)}: u_a . v_b = [f(a) == g(b)].
+    g = np.random.default_rng(14)
+    B, L, V, r = 2, 4, 60, 6
+    f = lambda tok: tok % r
+    gg = lambda tok: (tok // 2) % r
+    U = np.eye(r, dtype=np.float32)[f(np.arange(V))]
+    Vf = np.eye(r, dtype=np.float32)[gg(np.arange(V))]
+    tv = np.round(g.standard_normal((B, L, 16)) * 8).astype(np.float32) / 8
+    ti = g.integers(0, V, (B, L, 16)).astype(np.int32)
+    anchor = g.integers(0, V, B)
+    S0, S = O.pair_scores(tv, ti, anchor, U, Vf, "f32")
+    for b in range(B):
+        for j in range(16):
+            assert S0[b, j] == tv[b, 0, j] + (f(anchor[b]) == gg(ti[b, 0, j]))
+        for t in range(1, L):
+            for i in range(16):
+                for j in range(16):
+                    want = tv[b, t, j] + (f(ti[b, t - 1, i]) == gg(ti[b, t, j]))
+                    assert S[b, t - 1, i, j] == want
+
+
+# ------------------------------------------------------------------ path walk
+def _brute_paths(S0, S):
+    """All 16^L paths with fp64 scores; best under the tie rule (smallest
+    (p_{L-1}, ..., p_0)), its score and the second-best score."""
+    L = S.shape[0] + 1
+    best_key, best, scores = None, -np.inf, []
+    for p in itertools.product(range(16), repeat=L):
+        s = float(S0[p[0]]) + sum(float(S[t - 1, p[t - 1], p[t]]) for t in range(1, L))
+        scores.append(s)
+        key = tuple(reversed(p))
+        if s > best or (s == best and key < best_key):
+            best, best_key = s, key
+    scores = np.sort(np.array(scores))[::-1]
+    return list(reversed(best_key)), best, scores[1]
+
+
+@pytest.mark.parametrize("L,seed", [(1, 0), (2, 1), (3, 2), (4, 3), (4, 4)])
+def test_path_select_matches_brute_force_on_dyadic_scores_with_ties(L, seed):
+    # values on a coarse 1/4 grid: fp32 sums exact, many exact ties
+    g = np.random.default_rng(seed)
+    B = 2 if L == 4 else 4
+    S0 = (np.round(g.standard_normal((B, 16)) * 2) / 4).astype(np.float32)
+    S = (np.round(g.standard_normal((B, L - 1, 16, 16)) * 2) / 4).astype(np.float32)
+    ti = g.integers(0, 1000, (B, L, 16)).astype(np.int32)
+    slot, tok, score = O.path_select(S0, S, ti)
+    margin = O.path_margin(S0, S)
+    for b in range(B):
+        p, best, second = _brute_paths(S0[b], S[b])
+        assert slot[b].tolist() == p
+        assert score[b] == best
+        assert tok[b].tolist() == [ti[b, t, p[t]] for t in range(L)]
+        assert margin[b] == best - second
+
+
+@pytest.mark.parametrize("L,seed", [(2, 5), (3, 6), (4, 7)])
+def test_path_select_matches_brute_force_on_continuous_scores(L, seed):
+    g = np.random.default_rng(seed)
+    B = 3
+    S0 = g.standard_normal((B, 16)).astype(np.float32)
+    S = g.standard_normal((B, L - 1, 16, 16)).astype(np.float32)
+    slot, _, score = O.path_select(S0, S, np.zeros((B, L, 16), np.int32))
+    margin = O.path_margin(S0, S)
+    for b in range(B):
+        p, best, second = _brute_paths(S0[b], S[b])
+        assert best - second > 1e-4   # decided: fp32 rounding cannot flip it
+        assert slot[b].tolist() == p
+        assert abs(score[b] - best) < 1e-5
+        assert abs(margin[b] - (best - second)) < 1e-9
+
+
+def test_path_select_invariances():
+    g = np.random.default_rng(15)
+    B, L = 6, 6
+    S0 = g.standard_normal((B, 16)).astype(np.float32)
+    S = g.standard_normal((B, L - 1, 16, 16)).astype(np.float32)
+    ti = np.stack([np.stack([g.permutation(500)[:16] for _ in range(L)]) for _ in range(B)]).astype(np.int32)
+    slot, tok, score = O.path_select(S0, S, ti)
+    # per-position constants shift every path alike (constants exact in fp32 sums)
+    c = np.array([0.5, -2.0, 1.0, 0.25, 4.0, -1.0], dtype=np.float32)
+    slot2, _, score2 = O.path_select(S0 + c[0], S + c[1:, None, None], ti)
+    np.testing.assert_array_equal(slot2, slot)
+    np.testing.assert_allclose(score2, score + c.sum(), atol=1e-4)
+    # permuting each position's slots (and candidates) consistently keeps the tokens
+    perm = [g.permutation(16) for _ in range(L)]
+    S0p = S0[:, perm[0]]
+    Sp = np.stack([S[:, t - 1][:, perm[t - 1]][:, :, perm[t]] for t in range(1, L)], axis=1)
+    tip = np.stack([ti[:, t][:, perm[t]] for t in range(L)], axis=1)
+    _, tok3, score3 = O.path_select(S0p, Sp, tip)
+    np.testing.assert_array_equal(tok3, tok)
+    np.testing.assert_array_equal(score3, score)
+
+
+def test_path_select_without_pair_terms_is_top1():
+    g = np.random.default_rng(16)
+    B, L = 5, 8
+    tv = -np.sort(-g.standard_normal((B, L, 16)), axis=2).astype(np.float32)
+    tv[0, 3, :] = 1.0     # an all-tied position still takes slot 0
+    ti = g.integers(0, 100, (B, L, 16)).astype(np.int32)
+    S0, S = O.pair_scores(tv, ti, np.zeros(B, int), np.zeros((100, 4), np.float32),
+                          np.zeros((100, 4), np.float32), "f32")
+    slot, tok, _ = O.path_select(S0, S, ti)
+    np.testing.assert_array_equal(slot, 0)
+    np.testing.assert_array_equal(tok, ti[:, :, 0])
+
+
+# ------------------------------------------------------------------ verify
+def test_verify_hand_cases():
+    path = np.array([[1, 2, 3, 4], [1, 2, 3, 4], [1, 2, 3, 4], [9, 2, 3, 4]])
+    tgt = np.array([[1, 2, 3, 4, 50], [1, 2, 7, 4, 51], [1, 2, 3, 8, 52], [1, 2, 3, 4, 53]])
+    acc, nxt = O.verify_greedy(path, tgt)
+    assert acc.tolist() == [5, 3, 4, 1]
+    assert nxt.tolist() == [50, 7, 8, 1]
+
+
+def test_verify_invariants_random():
+    g = np.random.default_rng(17)
+    B, L = 2000, 8
+    path = g.integers(0, 3, (B, L))
+    tgt = g.integers(0, 3, (B, L + 1))
+    acc, nxt = O.verify_greedy(path, tgt)
+    assert ((acc >= 1) & (acc <= L + 1)).all()
+    for b in range(0, B, 97):
+        n = 0
+        while n < L and path[b, n] == tgt[b, n]:
+            n += 1
+        assert acc[b] == n + 1 and nxt[b] == tgt[b, n]
+
+
+# ------------------------------------------------------------------ the pages' Table 1
+def _table1():
+    rows = {}
+    with open(os.path.join(GOLDEN, "table1_recall.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            parts = line.split()
+            rows[parts[0]] = (np.array([float(v) / 100 for v in parts[1:8]]), float(parts[8]))
+    return rows
+
+
+def test_table1_acceptance_follows_from_recall_rows():
+    rows = _table1()
+    for name, (p, printed) in rows.items():
+        e = O.expected_acceptance(p)
+        # printed to two decimals (truncated): 4.2746 -> 4.27, 6.7981 -> 6.79
+        assert printed <= e < printed + 0.01, (name, e, printed)
+    assert O.expected_acceptance(WL.PROFILE_P1) == pytest.approx(4.23307, abs=1e-5)   # .85+.68+.5372+.419016+.322642+.245208+.179002 + 1
+
+
+def _mc_acceptance(p1, p16, L, n_blocks, seed):
+    g = np.random.default_rng(seed)
+    V = 4096
+    cands = np.stack([g.permutation(V)[:16 * L].reshape(L, 16) for _ in range(n_blocks)]).astype(np.int32)
+    tgt = WL.planted_targets(cands, V, p1, p16, seed=seed)
+    acc_top1, _ = O.verify_greedy(cands[:, :, 0], tgt)
+    acc_orc, _ = O.verify_greedy(O.oracle_selector(cands, tgt), tgt)
+    return acc_top1, acc_orc, cands, tgt
+
+
+def test_planted_targets_and_verify_reproduce_closed_form():
+    w = WL.WORKLOADS[0]
+    p1, p16 = w.recall_profile()
+    acc1, acco, cands, tgt = _mc_acceptance(p1, p16, w.L, 20000, seed=123)
+    for acc, p in ((acc1, p1), (acco, p16)):
+        e = O.expected_acceptance(p)
+        se = acc.std() / np.sqrt(len(acc))
+        assert abs(acc.mean() - e) < 4 * se, (acc.mean(), e, se)
+    assert (acc1 <= acco).all()
+    # the outside-the-candidates draws really are outside
+    inside = (cands == tgt[:, :w.L, None]).any(axis=2)
+    assert inside.mean() == pytest.approx(np.mean(p16), abs=0.01)
+
+
+def test_oracle_selector_reaches_recall16_bound():
+    L = 8
+    acc1, acco, _, _ = _mc_acceptance(np.full(L, 0.8), np.ones(L), L, 3000, seed=7)
+    assert (acco == L + 1).all()
+    assert (acc1 <= acco).all()
+
+
+# ------------------------------------------------------------------ whole step, tiny workload
+def test_tiny_step_invariants():
+    w = WL.WORKLOADS[0]
+    inp = WL.make_inputs(w)
+    out = O.run_step_front(w, inp)
+    L = w.L
+    assert out["top_idx"].shape == (1, L, 16)
+    tgt = WL.make_targets(w, out["top_idx"], out["path_tok"])
+    acc, nxt = O.verify_greedy(out["path_tok"], tgt)
+    acc_orc, _ = O.verify_greedy(O.oracle_selector(out["top_idx"], tgt), tgt)
+    assert 1 <= acc[0] <= L + 1
+    assert acc[0] <= acc_orc[0]
+    # planting the chosen path as the target gives a full block
+    tgt2 = np.concatenate([out["path_tok"], tgt[:, L:]], axis=1)
+    assert O.verify_greedy(out["path_tok"], tgt2)[0][0] == L + 1
+    # the path score equals the fp64 score of the path up to fp32 rounding
+    sc = O.path_scores_f64(out["S0"], out["S"], out["path_slot"].astype(np.int64))
+    assert abs(sc[0] - out["path_score"][0]) < 1e-4
+
+
+def test_stress_construction_is_dyadic():
+    w = WL.WORKLOADS[4].shrink(B=2, V=512, H=64)
+    inp = WL.make_inputs(w)
+    x = O.as_f64(inp["x"], "bf16")
+    assert np.all(x == np.round(x)) and np.abs(x).max() <= 4
+    W = O.as_f64(inp["W"], "bf16") * 64
+    assert np.all(W == np.round(W)) and np.abs(W).max() <= 8
+    U = O.as_f64(inp["U"], "bf16") * 8
+    assert np.all(U == np.round(U))
