@@ -1,0 +1,335 @@
+"""DFlash 2 draft-select-verify step on MI355X (gfx950): Python binding.
+
+A thin ctypes layer over libdflash2.so (include/dflash2.h).  It checks the
+torch tensors it is given (device, dtype, shape, contiguity), passes raw
+device pointers and the current HIP stream, and raises on a non-zero status.
+Every stage of the step runs in the library's HIP kernels; PyTorch only
+provides device memory and streams.  There is no fallback: without the built
+library every call raises.
+
+The five stages (names as in the C ABI):
+  twotap_conv     two-tap local conv around the drafter's sublayers
+  logits_topk     LM-head logits and per-position top-16 candidates
+                  (= lmhead_logits then topk16)
+  pair_score      16x16 scores of neighbouring candidates
+  path_select     max-plus walk to one path per block
+  verify_greedy   greedy verification, acceptance length
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "DFlash2Error", "lib", "library_path", "twotap_conv", "lmhead_logits", "topk16",
+    "topk16_workspace", "logits_topk", "logits_topk_workspace", "pair_score", "path_select",
+    "verify_greedy", "StepBuffers", "run_step", "TOPK",
+]
+
+TOPK = 16
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libdflash2.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_Z = ctypes.c_size_t
+
+_SIGS = {
+    "dflash2_version": ([], _I),
+    "dflash2_strerror": ([_I], ctypes.c_char_p),
+    "dflash2_twotap_conv": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
+    "dflash2_lmhead_logits": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "dflash2_topk16_workspace": ([_I, _I, _I], _Z),
+    "dflash2_topk16": ([_P, _P, _P, _I, _I, _I, _P, _Z, _P], _I),
+    "dflash2_logits_topk_workspace": ([_I, _I, _I, _I, _I, _I], _Z),
+    "dflash2_logits_topk": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
+    "dflash2_pair_score": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
+    "dflash2_path_select": ([_P, _P, _P, _I, _I, _P, _P, _P, _P], _I),
+    "dflash2_verify_greedy": ([_P, _P, _I, _I, _P, _P, _P], _I),
+}
+
+
+class DFlash2Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().dflash2_strerror(status).decode()
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libdflash2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"{library_path} is not built; run `python -m block_drafting_amd.build` "
+                "(the HIP library is required, there is no fallback)")
+        L = ctypes.CDLL(library_path)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise DFlash2Error(fn, status)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return 1
+    if t.dtype == torch.float32:
+        return 0
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(*ts: Optional[torch.Tensor]):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors must share one device")
+    return dev
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _shape(t: torch.Tensor, shape, name: str, dtype=None):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
+# ---------------------------------------------------------------- stages
+def twotap_conv(x: torch.Tensor, k0: torch.Tensor, k1: torch.Tensor,
+                anchor_h: Optional[torch.Tensor] = None, proj: Optional[torch.Tensor] = None,
+                groups: int = 1, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = two-tap conv of x [B, L, H] (bf16 or fp32); see dflash2_twotap_conv."""
+    B, L, H = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _shape(out, x.shape, "out", x.dtype)
+    _shape(k0, (H,), "k0", torch.float32)
+    _shape(k1, (H,), "k1", torch.float32)
+    if anchor_h is not None:
+        _shape(anchor_h, (B, H), "anchor_h", x.dtype)
+    if proj is not None:
+        _shape(proj, (H, 2 * groups), "proj", torch.float32)
+    dev = _dev(x, k0, k1, anchor_h, proj, out)
+    _check("dflash2_twotap_conv", lib().dflash2_twotap_conv(
+        _ptr(x), _ptr(anchor_h), _ptr(out), _ptr(k0), _ptr(k1), _ptr(proj), groups,
+        B, L, H, _dt(x), _stream(dev)))
+    return out
+
+
+def lmhead_logits(h: torch.Tensor, W: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """logits [M, V] fp32 = h [M, H] . W [V, H]^T."""
+    M, H = h.shape
+    V = W.shape[0]
+    _shape(W, (V, H), "W", h.dtype)
+    if out is None:
+        out = torch.empty((M, V), dtype=torch.float32, device=h.device)
+    _shape(out, (M, V), "out", torch.float32)
+    dev = _dev(h, W, out)
+    _check("dflash2_lmhead_logits", lib().dflash2_lmhead_logits(
+        _ptr(h), _ptr(W), _ptr(out), M, H, V, _dt(h), _stream(dev)))
+    return out
+
+
+def topk16_workspace(M: int, V: int) -> int:
+    return int(lib().dflash2_topk16_workspace(M, V, TOPK))
+
+
+def _workspace(nbytes: int, dev, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return ws
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace smaller than {nbytes} bytes")
+    return ws
+
+
+def topk16(logits: torch.Tensor, top_val: Optional[torch.Tensor] = None,
+           top_idx: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-row top-16 (value desc, id asc) of fp32 logits [M, V]."""
+    M, V = logits.shape
+    if logits.dtype != torch.float32:
+        raise TypeError("logits must be fp32")
+    dev = logits.device
+    if top_val is None:
+        top_val = torch.empty((M, TOPK), dtype=torch.float32, device=dev)
+    if top_idx is None:
+        top_idx = torch.empty((M, TOPK), dtype=torch.int32, device=dev)
+    _shape(top_val, (M, TOPK), "top_val", torch.float32)
+    _shape(top_idx, (M, TOPK), "top_idx", torch.int32)
+    need = topk16_workspace(M, V)
+    ws = _workspace(need, dev, workspace)
+    _dev(logits, top_val, top_idx, ws)
+    _check("dflash2_topk16", lib().dflash2_topk16(
+        _ptr(logits), _ptr(top_val), _ptr(top_idx), M, V, TOPK, _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(dev)))
+    return top_val, top_idx
+
+
+def logits_topk_workspace(M: int, H: int, V: int, dtype: torch.dtype, logits_given: bool) -> int:
+    return int(lib().dflash2_logits_topk_workspace(
+        M, H, V, TOPK, 1 if dtype == torch.bfloat16 else 0, int(bool(logits_given))))
+
+
+def logits_topk(h: torch.Tensor, W: torch.Tensor, logits: Optional[torch.Tensor] = None,
+                top_val: Optional[torch.Tensor] = None, top_idx: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None):
+    """LM-head logits (into `logits` when given, else into the workspace) and
+    the per-row top-16.  Returns (top_val, top_idx)."""
+    M, H = h.shape
+    V = W.shape[0]
+    _shape(W, (V, H), "W", h.dtype)
+    dev = h.device
+    if logits is not None:
+        _shape(logits, (M, V), "logits", torch.float32)
+    if top_val is None:
+        top_val = torch.empty((M, TOPK), dtype=torch.float32, device=dev)
+    if top_idx is None:
+        top_idx = torch.empty((M, TOPK), dtype=torch.int32, device=dev)
+    need = logits_topk_workspace(M, H, V, h.dtype, logits is not None)
+    ws = _workspace(need, dev, workspace)
+    _dev(h, W, logits, top_val, top_idx, ws)
+    _check("dflash2_logits_topk", lib().dflash2_logits_topk(
+        _ptr(h), _ptr(W), _ptr(logits), _ptr(top_val), _ptr(top_idx), M, H, V, TOPK, _dt(h),
+        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(dev)))
+    return top_val, top_idx
+
+
+def pair_score(top_val: torch.Tensor, top_idx: torch.Tensor, anchor_tok: Optional[torch.Tensor],
+               U: torch.Tensor, Vf: torch.Tensor, S0: Optional[torch.Tensor] = None,
+               S: Optional[torch.Tensor] = None):
+    """S0 [B, 16], S [B, L-1, 16, 16] from candidates [B, L, 16] and factors [V, r]."""
+    B, L, K = top_val.shape
+    V, r = U.shape
+    _shape(top_idx, (B, L, K), "top_idx", torch.int32)
+    _shape(Vf, (V, r), "Vf", U.dtype)
+    if anchor_tok is not None:
+        _shape(anchor_tok, (B,), "anchor_tok", torch.int32)
+    dev = top_val.device
+    if S0 is None:
+        S0 = torch.empty((B, TOPK), dtype=torch.float32, device=dev)
+    if S is None:
+        S = torch.empty((B, max(L - 1, 0), TOPK, TOPK), dtype=torch.float32, device=dev)
+    _shape(S0, (B, TOPK), "S0", torch.float32)
+    _shape(S, (B, L - 1, TOPK, TOPK), "S", torch.float32)
+    _dev(top_val, top_idx, anchor_tok, U, Vf, S0, S)
+    _check("dflash2_pair_score", lib().dflash2_pair_score(
+        _ptr(top_val), _ptr(top_idx), _ptr(anchor_tok), _ptr(U), _ptr(Vf), B, L, V, r, _dt(U),
+        _ptr(S0), _ptr(S) if L > 1 else None, _stream(dev)))
+    return S0, S
+
+
+def path_select(S0: torch.Tensor, S: Optional[torch.Tensor], top_idx: Optional[torch.Tensor],
+                path_slot=None, path_tok=None, path_score=None):
+    """Max-plus best path per block.  Returns (path_slot, path_tok, path_score)."""
+    B = S0.shape[0]
+    if top_idx is not None:
+        L = top_idx.shape[1]
+    else:
+        L = 1 if S is None else S.shape[1] + 1
+    dev = S0.device
+    if path_slot is None:
+        path_slot = torch.empty((B, L), dtype=torch.int32, device=dev)
+    if path_tok is None and top_idx is not None:
+        path_tok = torch.empty((B, L), dtype=torch.int32, device=dev)
+    if path_score is None:
+        path_score = torch.empty((B,), dtype=torch.float32, device=dev)
+    _dev(S0, S, top_idx, path_slot, path_tok, path_score)
+    _check("dflash2_path_select", lib().dflash2_path_select(
+        _ptr(S0), _ptr(S) if L > 1 else None, _ptr(top_idx), B, L, _ptr(path_slot),
+        _ptr(path_tok), _ptr(path_score), _stream(dev)))
+    return path_slot, path_tok, path_score
+
+
+def verify_greedy(path_tok: torch.Tensor, target: torch.Tensor, accept_len=None, next_tok=None):
+    """Greedy verification: (accept_len [B], next_tok [B])."""
+    B, L = path_tok.shape
+    _shape(target, (B, L + 1), "target", torch.int32)
+    dev = path_tok.device
+    if accept_len is None:
+        accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if next_tok is None:
+        next_tok = torch.empty((B,), dtype=torch.int32, device=dev)
+    _dev(path_tok, target, accept_len, next_tok)
+    _check("dflash2_verify_greedy", lib().dflash2_verify_greedy(
+        _ptr(path_tok), _ptr(target), B, L, _ptr(accept_len), _ptr(next_tok), _stream(dev)))
+    return accept_len, next_tok
+
+
+# ---------------------------------------------------------------- whole step
+class StepBuffers:
+    """Preallocated device buffers for one step shape (B, L, H, V) so repeated
+    steps allocate nothing.  `keep_logits` materialises the [M, V] logits in
+    their own tensor (else they live in the workspace)."""
+
+    def __init__(self, B: int, L: int, H: int, V: int, dtype: torch.dtype, device,
+                 n_convs: int = 1, keep_logits: bool = True):
+        M = B * L
+        kw = dict(device=device)
+        self.B, self.L, self.H, self.V = B, L, H, V
+        self.y = [torch.empty((B, L, H), dtype=dtype, **kw) for _ in range(min(n_convs, 2))]
+        self.logits = torch.empty((M, V), dtype=torch.float32, **kw) if keep_logits else None
+        ws = logits_topk_workspace(M, H, V, dtype, keep_logits)
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, **kw)
+        self.top_val = torch.empty((M, TOPK), dtype=torch.float32, **kw)
+        self.top_idx = torch.empty((M, TOPK), dtype=torch.int32, **kw)
+        self.S0 = torch.empty((B, TOPK), dtype=torch.float32, **kw)
+        self.S = torch.empty((B, max(L - 1, 0), TOPK, TOPK), dtype=torch.float32, **kw)
+        self.path_slot = torch.empty((B, L), dtype=torch.int32, **kw)
+        self.path_tok = torch.empty((B, L), dtype=torch.int32, **kw)
+        self.path_score = torch.empty((B,), dtype=torch.float32, **kw)
+        self.accept_len = torch.empty((B,), dtype=torch.int32, **kw)
+        self.next_tok = torch.empty((B,), dtype=torch.int32, **kw)
+
+
+def run_step(buf: StepBuffers, x: torch.Tensor, convs, W: torch.Tensor, U: torch.Tensor,
+             Vf: torch.Tensor, anchor_tok: Optional[torch.Tensor],
+             target: Optional[torch.Tensor]) -> StepBuffers:
+    """One draft-select-verify step: the conv chain (each entry of `convs` is a
+    dict with k0, k1, anchor_h, proj, groups), logits + top-16, pair scores,
+    path walk and, when `target` is given, greedy verification.  Every call
+    is enqueued on the current stream; nothing is synchronised."""
+    B, L, H, V = buf.B, buf.L, buf.H, buf.V
+    cur = x
+    for j, c in enumerate(convs):
+        out = buf.y[j % len(buf.y)]
+        twotap_conv(cur, c["k0"], c["k1"], c.get("anchor_h"), c.get("proj"), c.get("groups", 1),
+                    out=out)
+        cur = out
+    M = B * L
+    logits_topk(cur.view(M, H), W, buf.logits, buf.top_val, buf.top_idx, buf.workspace)
+    tv = buf.top_val.view(B, L, TOPK)
+    ti = buf.top_idx.view(B, L, TOPK)
+    pair_score(tv, ti, anchor_tok, U, Vf, buf.S0, buf.S)
+    path_select(buf.S0, buf.S, ti, buf.path_slot, buf.path_tok, buf.path_score)
+    if target is not None:
+        verify_greedy(buf.path_tok, target, buf.accept_len, buf.next_tok)
+    return buf

@@ -1,0 +1,238 @@
+// extern "C" entry points of libdflash2: argument validation on the host,
+// then kernel launches on the caller's stream.  Nothing is launched and no
+// output is touched unless every check passes.
+#include "dflash2.h"
+#include "common.hpp"
+
+#define DFLASH2_API extern "C" __attribute__((visibility("default")))
+
+using namespace dflash2;
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+size_t esize(int dtype) { return dtype == DFLASH2_BF16 ? 2 : 4; }
+bool valid_dtype(int dtype) { return dtype == DFLASH2_F32 || dtype == DFLASH2_BF16; }
+
+// Byte ranges [a, a+na) and [b, b+nb) overlap.
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? DFLASH2_OK : DFLASH2_EHIP; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+const long long kInt32Max = 2147483647LL;
+
+}  // namespace
+
+DFLASH2_API int dflash2_version(void) { return kVersion; }
+
+DFLASH2_API const char* dflash2_strerror(int status) {
+  switch (status) {
+    case DFLASH2_OK: return "ok";
+    case DFLASH2_EINVAL: return "invalid argument (pointer, size, shape, alignment or aliasing)";
+    case DFLASH2_EUNSUPPORTED: return "unsupported configuration";
+    case DFLASH2_EHIP: return "HIP launch or runtime error";
+    case DFLASH2_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+DFLASH2_API int dflash2_twotap_conv(const void* x, const void* anchor_h, void* y,
+                                    const float* k0, const float* k1, const float* proj,
+                                    int groups, int B, int L, int H, int dtype, void* stream) {
+  if (!valid_dtype(dtype) || B < 0 || L < 1 || H < 8 || H % 8 != 0) return DFLASH2_EINVAL;
+  if ((long long)B * L * H > (1LL << 40)) return DFLASH2_EINVAL;
+  if (B == 0) return DFLASH2_OK;
+  if (!x || !y || !k0 || !k1) return DFLASH2_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(k0) || !aligned16(k1)) return DFLASH2_EINVAL;
+  if (anchor_h && !aligned16(anchor_h)) return DFLASH2_EINVAL;
+  if (proj) {
+    if (groups < 1 || H % groups != 0 || !aligned16(proj)) return DFLASH2_EINVAL;
+    if (groups > 1 && (size_t)(H + 2 * groups) * sizeof(double) > 65536)
+      return DFLASH2_EUNSUPPORTED;
+  }
+  const size_t es = esize(dtype);
+  const size_t xbytes = (size_t)B * L * H * es;
+  if (overlap(x, xbytes, y, xbytes)) return DFLASH2_EINVAL;
+  if (anchor_h && overlap(anchor_h, (size_t)B * H * es, y, xbytes)) return DFLASH2_EINVAL;
+  return status_of(launch_twotap_conv(x, anchor_h, y, k0, k1, proj, proj ? groups : 1, B, L, H,
+                                      dtype, as_stream(stream)));
+}
+
+namespace {
+int check_lmhead(const void* h, const void* W, int M, int H, int V, int dtype) {
+  if (!valid_dtype(dtype) || M < 0 || H < 8 || H % 8 != 0 || V < kTopK) return DFLASH2_EINVAL;
+  if ((long long)M * V > (1LL << 40) || (long long)V * H > (1LL << 40)) return DFLASH2_EINVAL;
+  if (M > 0 && (!h || !W || !aligned16(h) || !aligned16(W))) return DFLASH2_EINVAL;
+  if (H > (1 << 21)) return DFLASH2_EUNSUPPORTED;  // 32-bit tile offsets
+  return DFLASH2_OK;
+}
+}  // namespace
+
+DFLASH2_API int dflash2_lmhead_logits(const void* h, const void* W, float* logits, int M, int H,
+                                      int V, int dtype, void* stream) {
+  int st = check_lmhead(h, W, M, H, V, dtype);
+  if (st != DFLASH2_OK) return st;
+  if (M == 0) return DFLASH2_OK;
+  if (!logits || !aligned16(logits)) return DFLASH2_EINVAL;
+  const size_t zb = (size_t)M * V * sizeof(float);
+  if (overlap(logits, zb, h, (size_t)M * H * esize(dtype)) ||
+      overlap(logits, zb, W, (size_t)V * H * esize(dtype)))
+    return DFLASH2_EINVAL;
+  return status_of(launch_lmhead(h, W, logits, M, H, V, dtype, as_stream(stream)));
+}
+
+DFLASH2_API size_t dflash2_topk16_workspace(int M, int V, int K) {
+  if (M < 0 || V < kTopK || K != kTopK) return 0;
+  return topk16_workspace_bytes(M, V);
+}
+
+namespace {
+int check_topk_out(float* top_val, int32_t* top_idx, int M) {
+  if (M > 0 && (!top_val || !top_idx || !aligned4(top_val) || !aligned4(top_idx)))
+    return DFLASH2_EINVAL;
+  return DFLASH2_OK;
+}
+}  // namespace
+
+DFLASH2_API int dflash2_topk16(const float* logits, float* top_val, int32_t* top_idx, int M, int V,
+                               int K, void* workspace, size_t workspace_bytes, void* stream) {
+  if (K != kTopK || M < 0 || V < kTopK || (long long)M * V > (1LL << 40)) return DFLASH2_EINVAL;
+  if (M == 0) return DFLASH2_OK;
+  if (!logits || !aligned4(logits)) return DFLASH2_EINVAL;
+  int st = check_topk_out(top_val, top_idx, M);
+  if (st != DFLASH2_OK) return st;
+  const size_t need = topk16_workspace_bytes(M, V);
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   (reinterpret_cast<uintptr_t>(workspace) & 255) != 0))
+    return DFLASH2_EWORKSPACE;
+  const size_t zb = (size_t)M * V * sizeof(float);
+  if (overlap(top_val, (size_t)M * kTopK * 4, logits, zb) ||
+      overlap(top_idx, (size_t)M * kTopK * 4, logits, zb) ||
+      overlap(top_val, (size_t)M * kTopK * 4, top_idx, (size_t)M * kTopK * 4) ||
+      (need && overlap(workspace, need, logits, zb)))
+    return DFLASH2_EINVAL;
+  return status_of(launch_topk16(logits, top_val, top_idx, M, V, workspace, as_stream(stream)));
+}
+
+DFLASH2_API size_t dflash2_logits_topk_workspace(int M, int H, int V, int K, int dtype,
+                                                 int logits_given) {
+  if (K != kTopK || M < 0 || V < kTopK || H < 8 || !valid_dtype(dtype)) return 0;
+  size_t ws = (topk16_workspace_bytes(M, V) + 255) & ~(size_t)255;
+  if (!logits_given) ws += (size_t)M * V * sizeof(float);
+  return ws;
+}
+
+DFLASH2_API int dflash2_logits_topk(const void* h, const void* W, float* logits, float* top_val,
+                                    int32_t* top_idx, int M, int H, int V, int K, int dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (K != kTopK) return DFLASH2_EINVAL;
+  int st = check_lmhead(h, W, M, H, V, dtype);
+  if (st != DFLASH2_OK) return st;
+  if (M == 0) return DFLASH2_OK;
+  st = check_topk_out(top_val, top_idx, M);
+  if (st != DFLASH2_OK) return st;
+  if (logits && !aligned16(logits)) return DFLASH2_EINVAL;
+  const size_t need = dflash2_logits_topk_workspace(M, H, V, K, dtype, logits != nullptr);
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   (reinterpret_cast<uintptr_t>(workspace) & 255) != 0))
+    return DFLASH2_EWORKSPACE;
+  const size_t part = (topk16_workspace_bytes(M, V) + 255) & ~(size_t)255;
+  float* z = logits ? logits : reinterpret_cast<float*>(static_cast<char*>(workspace) + part);
+  const size_t zb = (size_t)M * V * sizeof(float);
+  const size_t es = esize(dtype);
+  if (overlap(z, zb, h, (size_t)M * H * es) || overlap(z, zb, W, (size_t)V * H * es) ||
+      overlap(top_val, (size_t)M * kTopK * 4, z, zb) ||
+      overlap(top_idx, (size_t)M * kTopK * 4, z, zb) ||
+      (logits && need && overlap(workspace, need, logits, zb)))
+    return DFLASH2_EINVAL;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = launch_lmhead(h, W, z, M, H, V, dtype, s);
+  if (e != hipSuccess) return DFLASH2_EHIP;
+  return status_of(launch_topk16(z, top_val, top_idx, M, V, workspace, s));
+}
+
+DFLASH2_API int dflash2_pair_score(const float* top_val, const int32_t* top_idx,
+                                   const int32_t* anchor_tok, const void* U, const void* Vf,
+                                   int B, int L, int V, int r, int dtype, float* S0, float* S,
+                                   void* stream) {
+  if (!valid_dtype(dtype) || B < 0 || L < 1 || L > DFLASH2_MAX_L || V < kTopK || r < 1 ||
+      r > DFLASH2_MAX_RANK)
+    return DFLASH2_EINVAL;
+  if (B == 0) return DFLASH2_OK;
+  if (!top_val || !top_idx || !U || !Vf || !S0 || (L > 1 && !S)) return DFLASH2_EINVAL;
+  if ((long long)V * r > (1LL << 40) || (long long)B * L * kTopK > kInt32Max)
+    return DFLASH2_EINVAL;
+  if (!aligned4(top_val) || !aligned4(top_idx) || !aligned4(S0) || (S && !aligned16(S)) ||
+      (anchor_tok && !aligned4(anchor_tok)))
+    return DFLASH2_EINVAL;
+  const size_t es = esize(dtype);
+  if (dtype == DFLASH2_BF16 ? ((reinterpret_cast<uintptr_t>(U) | reinterpret_cast<uintptr_t>(Vf)) & 1)
+                            : (!aligned4(U) || !aligned4(Vf)))
+    return DFLASH2_EINVAL;
+  const size_t s0b = (size_t)B * kTopK * 4;
+  const size_t sb = L > 1 ? (size_t)B * (L - 1) * kTopK * kTopK * 4 : 0;
+  const size_t tb = (size_t)B * L * kTopK * 4;
+  const void* ins[] = {top_val, top_idx, U, Vf, anchor_tok};
+  const size_t insz[] = {tb, tb, (size_t)V * r * es, (size_t)V * r * es, (size_t)B * 4};
+  for (int i = 0; i < 5; ++i) {
+    if (overlap(S0, s0b, ins[i], insz[i]) || (sb && overlap(S, sb, ins[i], insz[i])))
+      return DFLASH2_EINVAL;
+  }
+  if (sb && overlap(S0, s0b, S, sb)) return DFLASH2_EINVAL;
+  return status_of(launch_pair_score(top_val, top_idx, anchor_tok, U, Vf, B, L, V, r, dtype, S0,
+                                     L > 1 ? S : nullptr, as_stream(stream)));
+}
+
+DFLASH2_API int dflash2_path_select(const float* S0, const float* S, const int32_t* top_idx,
+                                    int B, int L, int32_t* path_slot, int32_t* path_tok,
+                                    float* path_score, void* stream) {
+  if (B < 0 || L < 1 || L > DFLASH2_MAX_L) return DFLASH2_EINVAL;
+  if (B == 0) return DFLASH2_OK;
+  if (!S0 || (L > 1 && !S) || !path_slot || !path_score) return DFLASH2_EINVAL;
+  if ((top_idx == nullptr) != (path_tok == nullptr)) return DFLASH2_EINVAL;
+  if (!aligned4(S0) || (S && !aligned4(S)) || !aligned4(path_slot) || !aligned4(path_score) ||
+      (top_idx && !aligned4(top_idx)) || (path_tok && !aligned4(path_tok)))
+    return DFLASH2_EINVAL;
+  const size_t s0b = (size_t)B * kTopK * 4;
+  const size_t sb = L > 1 ? (size_t)B * (L - 1) * kTopK * kTopK * 4 : 0;
+  const size_t tib = (size_t)B * L * kTopK * 4;
+  const size_t pb = (size_t)B * L * 4;
+  const void* outs[] = {path_slot, path_tok, path_score};
+  const size_t outsz[] = {pb, pb, (size_t)B * 4};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(outs[i], outsz[i], S0, s0b) || (sb && overlap(outs[i], outsz[i], S, sb)) ||
+        overlap(outs[i], outsz[i], top_idx, tib))
+      return DFLASH2_EINVAL;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return DFLASH2_EINVAL;
+  }
+  return status_of(launch_path_select(S0, L > 1 ? S : nullptr, top_idx, B, L, path_slot, path_tok,
+                                      path_score, as_stream(stream)));
+}
+
+DFLASH2_API int dflash2_verify_greedy(const int32_t* path_tok, const int32_t* target, int B, int L,
+                                      int32_t* accept_len, int32_t* next_tok, void* stream) {
+  if (B < 0 || L < 1) return DFLASH2_EINVAL;
+  if (B == 0) return DFLASH2_OK;
+  if (!path_tok || !target || !accept_len) return DFLASH2_EINVAL;
+  if (!aligned4(path_tok) || !aligned4(target) || !aligned4(accept_len) ||
+      (next_tok && !aligned4(next_tok)))
+    return DFLASH2_EINVAL;
+  const size_t pb = (size_t)B * L * 4, tb = (size_t)B * (L + 1) * 4, ob = (size_t)B * 4;
+  if (overlap(accept_len, ob, path_tok, pb) || overlap(accept_len, ob, target, tb) ||
+      overlap(next_tok, ob, path_tok, pb) || overlap(next_tok, ob, target, tb) ||
+      overlap(accept_len, ob, next_tok, ob))
+    return DFLASH2_EINVAL;
+  return status_of(
+      launch_verify_greedy(path_tok, target, B, L, accept_len, next_tok, as_stream(stream)));
+}

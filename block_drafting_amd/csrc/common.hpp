@@ -1,0 +1,56 @@
+// Internal declarations shared by the HIP sources of libdflash2 (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dflash2 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kTopK = 16;
+constexpr int kWave = 64;
+
+// bf16 storage <-> fp32 arithmetic.  A bf16 value is the upper half of an
+// IEEE single, so widening is a shift; narrowing uses the gfx950 hardware
+// convert (round to nearest even).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------- launches
+// Each returns hipSuccess or the launch error; arguments are already valid.
+hipError_t launch_twotap_conv(const void* x, const void* anchor_h, void* y, const float* k0,
+                              const float* k1, const float* proj, int groups, int B, int L,
+                              int H, int dtype, hipStream_t s);
+
+hipError_t launch_lmhead(const void* h, const void* W, float* logits, int M, int H, int V,
+                         int dtype, hipStream_t s);
+
+int topk16_splits(int M, int V);
+size_t topk16_workspace_bytes(int M, int V);
+hipError_t launch_topk16(const float* logits, float* top_val, int32_t* top_idx, int M, int V,
+                         void* workspace, hipStream_t s);
+
+hipError_t launch_pair_score(const float* top_val, const int32_t* top_idx,
+                             const int32_t* anchor_tok, const void* U, const void* Vf, int B,
+                             int L, int V, int r, int dtype, float* S0, float* S, hipStream_t s);
+
+hipError_t launch_path_select(const float* S0, const float* S, const int32_t* top_idx, int B,
+                              int L, int32_t* path_slot, int32_t* path_tok, float* path_score,
+                              hipStream_t s);
+
+hipError_t launch_verify_greedy(const int32_t* path_tok, const int32_t* target, int B, int L,
+                                int32_t* accept_len, int32_t* next_tok, hipStream_t s);
+
+}  // namespace dflash2

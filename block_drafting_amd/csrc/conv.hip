@@ -1,0 +1,268 @@
+// Two-tap dynamic depthwise conv ("DFlash 2: Keep Drafting Parallel",
+// section "A lightweight local convolution", eq. Conv_k and Fig. 4):
+//   y_t = (k0 + D_t[g,0]) * x_t + (k1 + D_t[g,1]) * x_{t-1},  x_{-1} = anchor,
+//   D_t[g,j] = x_t . proj[:, 2g+j].
+// HBM-bound elementwise work: every thread moves 16-byte vectors (8 bf16 or
+// 4+4 fp32 channels); the correction needs a row reduction first.
+//
+// Arithmetic is fp64 (taps, corrections, products and the sum), then one
+// rounding to the storage type: fp64 -> fp32 by round-to-odd, then fp32 ->
+// bf16 by the hardware round-to-nearest-even.  Round-to-odd at 24 bits
+// followed by rounding to 8 bits equals a single correct rounding, so each
+// output is the exactly rounded value of the formula (up to the 2^-53
+// relative error of the fp64 evaluation).  Chained convs therefore do not
+// drift apart from the definition through double rounding.  The kernel is
+// HBM-bound, so the fp64 rate is not the limit.
+#include "common.hpp"
+
+namespace dflash2 {
+namespace {
+
+// Eight consecutive channels of one row, widened to fp32.
+template <typename T>
+struct Row8;
+
+// fp64 -> fp32 rounding to odd: truncate toward zero and make the last bit 1
+// when anything was cut off.
+__device__ __forceinline__ float f64_to_f32_odd(double v) {
+  float f = (float)v;
+  uint32_t u = __float_as_uint(f);
+  const double back = (double)f;
+  if (back != v) {
+    if (fabs(back) > fabs(v)) u -= 1;  // stepped past v: move one ulp toward zero
+    u |= 1u;
+  }
+  return __uint_as_float(u);
+}
+
+template <>
+struct Row8<uint16_t> {
+  __device__ static void load(const uint16_t* p, double v[8]) {
+    u32x4_t w = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = (double)bf16_lo(w[i]);
+      v[2 * i + 1] = (double)bf16_hi(w[i]);
+    }
+  }
+  __device__ static void store(uint16_t* p, const double v[8]) {
+    u32x4_t w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = pack_bf16x2(f64_to_f32_odd(v[2 * i]), f64_to_f32_odd(v[2 * i + 1]));
+    *reinterpret_cast<u32x4_t*>(p) = w;
+  }
+};
+
+template <>
+struct Row8<float> {
+  __device__ static void load(const float* p, double v[8]) {
+    f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0];
+    f32x4_t b = reinterpret_cast<const f32x4_t*>(p)[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = (double)a[i];
+      v[4 + i] = (double)b[i];
+    }
+  }
+  __device__ static void store(float* p, const double v[8]) {
+    f32x4_t a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = (float)v[i];
+      b[i] = (float)v[4 + i];
+    }
+    reinterpret_cast<f32x4_t*>(p)[0] = a;
+    reinterpret_cast<f32x4_t*>(p)[1] = b;
+  }
+};
+
+__device__ __forceinline__ void load_f32x8(const float* p, double v[8]) {
+  f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0];
+  f32x4_t b = reinterpret_cast<const f32x4_t*>(p)[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = (double)a[i];
+    v[4 + i] = (double)b[i];
+  }
+}
+
+// y for 8 channels from fp64 taps c0, c1.
+template <typename T>
+__device__ __forceinline__ void mix8(const T* xp, const T* pp, T* yp, const double c0[8],
+                                     const double c1[8]) {
+  double xv[8], pv[8], yv[8];
+  Row8<T>::load(xp, xv);
+  if (pp) {
+    Row8<T>::load(pp, pv);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pv[i] = 0.0;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) yv[i] = c0[i] * xv[i] + c1[i] * pv[i];
+  Row8<T>::store(yp, yv);
+}
+
+// Static taps: one thread per 8 channels of one (block, position) row.
+template <typename T>
+__global__ __launch_bounds__(256) void conv_static_kernel(const T* __restrict__ x,
+                                                          const T* __restrict__ anchor,
+                                                          T* __restrict__ y,
+                                                          const float* __restrict__ k0,
+                                                          const float* __restrict__ k1,
+                                                          int L, int H, long long total8) {
+  const int H8 = H >> 3;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total8;
+       i += (long long)gridDim.x * blockDim.x) {
+    const long long row = i / H8;
+    const int c = (int)(i - row * H8) * 8;
+    const int t = (int)(row % L);
+    const long long b = row / L;
+    const T* xp = x + row * H + c;
+    const T* pp = t > 0 ? xp - H : (anchor ? anchor + b * H + c : nullptr);
+    double c0[8], c1[8];
+    load_f32x8(k0 + c, c0);
+    load_f32x8(k1 + c, c1);
+    mix8<T>(xp, pp, y + row * H + c, c0, c1);
+  }
+}
+
+__device__ __forceinline__ double block_sum_256(double v, double* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  double s = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return s;
+}
+
+// One correction pair per row (groups == 1): a 256-thread block per row
+// reduces x_t . proj[:,0] and x_t . proj[:,1], then mixes.
+template <typename T>
+__global__ __launch_bounds__(256) void conv_dyn1_kernel(const T* __restrict__ x,
+                                                        const T* __restrict__ anchor,
+                                                        T* __restrict__ y,
+                                                        const float* __restrict__ k0,
+                                                        const float* __restrict__ k1,
+                                                        const float* __restrict__ proj, int L,
+                                                        int H) {
+  __shared__ double red[4];
+  const long long row = blockIdx.x;
+  const int t = (int)(row % L);
+  const long long b = row / L;
+  const T* xr = x + row * H;
+  double d0 = 0.0, d1 = 0.0;
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    double xv[8], p[16];
+    Row8<T>::load(xr + c, xv);
+    load_f32x8(proj + 2 * c, p);
+    load_f32x8(proj + 2 * c + 8, p + 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      d0 += xv[i] * p[2 * i];
+      d1 += xv[i] * p[2 * i + 1];
+    }
+  }
+  d0 = block_sum_256(d0, red);
+  d1 = block_sum_256(d1, red);
+  const T* pr = t > 0 ? xr - H : (anchor ? anchor + b * H : nullptr);
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    double c0[8], c1[8];
+    load_f32x8(k0 + c, c0);
+    load_f32x8(k1 + c, c1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      c0[i] += d0;
+      c1[i] += d1;
+    }
+    mix8<T>(xr + c, pr ? pr + c : nullptr, y + row * H + c, c0, c1);
+  }
+}
+
+// General group count: the row is staged in LDS as fp32, all 2*groups
+// corrections are computed (threads over outputs, coalesced proj reads), then
+// each channel mixes with its group's pair.  Dynamic LDS: (H + 2*groups) doubles.
+template <typename T>
+__global__ __launch_bounds__(256) void conv_dyng_kernel(const T* __restrict__ x,
+                                                        const T* __restrict__ anchor,
+                                                        T* __restrict__ y,
+                                                        const float* __restrict__ k0,
+                                                        const float* __restrict__ k1,
+                                                        const float* __restrict__ proj,
+                                                        int groups, int L, int H) {
+  extern __shared__ double ldsd[];
+  double* xs = ldsd;
+  double* dl = ldsd + H;
+  const long long row = blockIdx.x;
+  const int t = (int)(row % L);
+  const long long b = row / L;
+  const T* xr = x + row * H;
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    double xv[8];
+    Row8<T>::load(xr + c, xv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xs[c + i] = xv[i];
+  }
+  __syncthreads();
+  const int q2 = 2 * groups;
+  for (int q = threadIdx.x; q < q2; q += 256) {
+    double acc = 0.0;
+    for (int c = 0; c < H; ++c) acc += xs[c] * (double)proj[(long long)c * q2 + q];
+    dl[q] = acc;
+  }
+  __syncthreads();
+  const int per = H / groups;
+  const T* pr = t > 0 ? xr - H : (anchor ? anchor + b * H : nullptr);
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    double c0[8], c1[8];
+    load_f32x8(k0 + c, c0);
+    load_f32x8(k1 + c, c1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int g = (c + i) / per;
+      c0[i] += dl[2 * g];
+      c1[i] += dl[2 * g + 1];
+    }
+    mix8<T>(xr + c, pr ? pr + c : nullptr, y + row * H + c, c0, c1);
+  }
+}
+
+template <typename T>
+hipError_t launch_typed(const void* x, const void* anchor_h, void* y, const float* k0,
+                        const float* k1, const float* proj, int groups, int B, int L, int H,
+                        hipStream_t s) {
+  const T* xp = static_cast<const T*>(x);
+  const T* ap = static_cast<const T*>(anchor_h);
+  T* yp = static_cast<T*>(y);
+  const long long rows = (long long)B * L;
+  if (!proj) {
+    const long long total8 = rows * (H / 8);
+    long long blocks = (total8 + 255) / 256;
+    if (blocks > (1 << 20)) blocks = 1 << 20;
+    hipLaunchKernelGGL(conv_static_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, s, xp, ap,
+                       yp, k0, k1, L, H, total8);
+  } else if (groups == 1) {
+    hipLaunchKernelGGL(conv_dyn1_kernel<T>, dim3((unsigned)rows), dim3(256), 0, s, xp, ap, yp,
+                       k0, k1, proj, L, H);
+  } else {
+    const size_t lds = (size_t)(H + 2 * groups) * sizeof(double);
+    hipLaunchKernelGGL(conv_dyng_kernel<T>, dim3((unsigned)rows), dim3(256), lds, s, xp, ap,
+                       yp, k0, k1, proj, groups, L, H);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_twotap_conv(const void* x, const void* anchor_h, void* y, const float* k0,
+                              const float* k1, const float* proj, int groups, int B, int L,
+                              int H, int dtype, hipStream_t s) {
+  if (dtype == 1)
+    return launch_typed<uint16_t>(x, anchor_h, y, k0, k1, proj, groups, B, L, H, s);
+  return launch_typed<float>(x, anchor_h, y, k0, k1, proj, groups, B, L, H, s);
+}
+
+}  // namespace dflash2

@@ -1,0 +1,269 @@
+// LM-head logits z = h . W^T ("DFlash 2: Keep Drafting Parallel", section
+// "A lightweight path selector": the pair score's unary term is the drafter's
+// own logit, computed once per position).  The only dense contraction of the
+// step: M = blocks x positions rows, N = vocabulary, K = hidden.
+//
+// bf16 path: v_mfma_f32_32x32x16_bf16 tiles.  A workgroup owns a BM x BN
+// output tile and walks K in BK slices; both operands are K-contiguous, so a
+// thread moves 16-byte runs of 8 bf16 from HBM/L2 into padded LDS rows (row
+// pitch BK + 8 elements keeps the 16-byte fragment reads conflict-free), with
+// the next slice's loads in flight while the current slice feeds the matrix
+// cores.  Each wave accumulates a (BM/WM) x (BN/WN) sub-tile in registers.
+// Tiles are numbered so that the M-tiles sharing one W slice run back to back
+// on the same XCD (workgroup i is dispatched to XCD i mod 8), so W is pulled
+// from HBM about once and re-read from that XCD's L2.
+//
+// fp32 path (fp32 workloads): a plain per-output fp32 dot product.
+#include "common.hpp"
+
+namespace dflash2 {
+namespace {
+
+constexpr int kXcds = 8;
+
+// Bijection from dispatch order to tile order: XCD x gets a contiguous range
+// of tiles.
+__device__ __forceinline__ int xcd_tile(int pid, int ntiles) {
+  const int xcd = pid % kXcds;
+  const int local = pid / kXcds;
+  const int q = ntiles / kXcds;
+  const int rem = ntiles % kXcds;
+  return xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+}
+
+template <int BM, int BN, int BK, int WM, int WN>
+struct GemmCfg {
+  static constexpr int kThreads = WM * WN * 64;
+  static constexpr int kLdk = BK + 8;            // padded LDS row pitch (elements)
+  static constexpr int kTm = BM / WM / 32;       // 32x32 blocks per wave along M
+  static constexpr int kTn = BN / WN / 32;       // ... along N
+  static constexpr int kChunksPerRow = BK / 8;   // 16-byte runs per tile row
+  static constexpr int kAPer = BM * kChunksPerRow / kThreads;
+  static constexpr int kBPer = BN * kChunksPerRow / kThreads;
+  static constexpr int kStage = (BM + BN) * kLdk;  // elements per LDS stage
+  static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "wave tile");
+  static_assert(BK % 16 == 0, "k step");
+  static_assert((BM * kChunksPerRow) % kThreads == 0, "A load split");
+  static_assert((BN * kChunksPerRow) % kThreads == 0, "B load split");
+};
+
+template <int BM, int BN, int BK, int WM, int WN, bool KTAIL>
+__global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bw, float* __restrict__ C,
+    int M, int N, int K, int mtiles, int ntiles) {
+  using Cfg = GemmCfg<BM, BN, BK, WM, WN>;
+  constexpr int kT = Cfg::kThreads;
+  constexpr int kLdk = Cfg::kLdk;
+  constexpr int kCpr = Cfg::kChunksPerRow;
+  constexpr int kTm = Cfg::kTm;
+  constexpr int kTn = Cfg::kTn;
+  constexpr int kSteps = BK / 16;
+  constexpr int kLoads = Cfg::kAPer + Cfg::kBPer;
+  static_assert(kSteps >= 3 && kSteps % 2 == 0, "pipeline needs an even step count >= 4");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg::kStage];
+
+  const int tile = xcd_tile(blockIdx.x, mtiles * ntiles);
+  const int mt = tile % mtiles;
+  const int nt = tile / mtiles;
+  const int m0 = mt * BM;
+  const int n0 = nt * BN;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave % WM;
+  const int wn = wave / WM;
+
+  // Each thread moves kLoads 16-byte runs per K slice through buffer loads:
+  // one descriptor per operand tile (base = first row of the tile, size = the
+  // rows that exist) and a 32-bit byte offset per run.  Every access is range
+  // checked by the hardware: rows past the matrix edge, and the prefetches
+  // past the end of K that the last slices issue, read as zero or as rows of
+  // this tile that are never used, so the loads need no branches.
+  constexpr int kRowStep = kT / kCpr;  // tile rows covered by one pass of the block
+  const int row0 = tid / kCpr;
+  const int kof = (tid % kCpr) * 8;
+  const int rowsA = min(BM, M - m0);
+  const int rowsB = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A + (size_t)m0 * K), (short)0, rowsA * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Bw + (size_t)n0 * K), (short)0, rowsB * K * 2, 0x00020000);
+  const int voff0 = (row0 * K + kof) * 2;
+  const int vstep = kRowStep * K * 2;
+  u32x4_t R[kLoads];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const bool isA = i < Cfg::kAPer;
+      const int ii = isA ? i : i - Cfg::kAPer;
+      // the whole offset sits in the per-lane part so the range check covers it
+      u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(isA ? rsA : rsB,
+                                                         voff0 + ii * vstep + k0 * 2, 0, 0);
+      if (KTAIL && k0 + kof >= K) v = u32x4_t{0, 0, 0, 0};
+      R[i] = v;
+    }
+  };
+  // LDS destination of run i: row (row0 + ii * kRowStep) of the A or B part.
+  uint16_t* const dstA = lds + row0 * kLdk + kof;
+  auto sstore = [&](uint16_t* stage) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const bool isA = i < Cfg::kAPer;
+      const int ii = isA ? i : i - Cfg::kAPer;
+      *reinterpret_cast<u32x4_t*>(stage + (dstA - lds) + ((isA ? 0 : BM) + ii * kRowStep) * kLdk) =
+          R[i];
+    }
+  };
+
+  f32x16_t acc[kTm][kTn];
+#pragma unroll
+  for (int i = 0; i < kTm; ++i)
+#pragma unroll
+    for (int j = 0; j < kTn; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Fragment offsets (elements) inside a stage: lane l supplies row l % 32 of
+  // a 32-row block and the 8 k values starting at 8 * (l / 32).
+  const int a_frag = (wm * (BM / WM) + (lane & 31)) * kLdk + (lane >> 5) * 8;
+  const int b_frag = (BM + wn * (BN / WN) + (lane & 31)) * kLdk + (lane >> 5) * 8;
+  bf16x8_t FA[2][kTm], FB[2][kTn];
+  auto fread = [&](const uint16_t* st, int kk, int slot) {
+#pragma unroll
+    for (int i = 0; i < kTm; ++i)
+      FA[slot][i] = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + a_frag + i * 32 * kLdk + kk * 16));
+#pragma unroll
+    for (int j = 0; j < kTn; ++j)
+      FB[slot][j] = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + b_frag + j * 32 * kLdk + kk * 16));
+  };
+  auto mfma = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < kTm; ++i)
+#pragma unroll
+      for (int j = 0; j < kTn; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[slot][i], FB[slot][j], acc[i][j], 0,
+                                                            0, 0);
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  gload(0);
+  sstore(lds);
+  gload(BK);  // past the end of K this reads zeros or unused rows
+  __syncthreads();
+  fread(lds, 0, 0);
+
+  // Per K slice (kSteps k-steps of 16):
+  //   step kk:   read fragments of step kk+1 | 16 MFMAs on step kk
+  //   step 1:    + write the next slice (loaded one slice ago) to the other stage
+  //   step S-2:  + barrier, then issue the global loads of the slice after next
+  //   step S-1:  the fragment reads come from the next stage (visible after the barrier)
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint16_t* cur = lds + (kt & 1) * Cfg::kStage;
+    uint16_t* nxt = lds + ((kt & 1) ^ 1) * Cfg::kStage;
+    const bool has_next = kt + 1 < nk;
+#pragma unroll
+    for (int kk = 0; kk < kSteps; ++kk) {
+      if (kk + 1 < kSteps) {
+        fread(cur, kk + 1, (kk + 1) & 1);
+      } else {
+        fread(nxt, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk == 1) {
+        // interleave the stage writes with the MFMAs
+        mfma(kk & 1);
+        sstore(nxt);
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
+        }
+      } else {
+        mfma(kk & 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk == kSteps - 2) {
+        __syncthreads();
+        gload((kt + 2) * BK);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // Accumulator layout of a 32x32 block: register r of lane l holds
+  // row 8*(r/4) + 4*(l/32) + r%4, column l%32.  Half-waves store 128-byte runs.
+#pragma unroll
+  for (int i = 0; i < kTm; ++i) {
+#pragma unroll
+    for (int j = 0; j < kTn; ++j) {
+      const int col = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < M) __builtin_nontemporal_store(acc[i][j][r], C + (size_t)row * N + col);
+      }
+    }
+  }
+}
+
+// fp32 operands: thread per vocabulary row, 8 output rows per block row.
+__global__ __launch_bounds__(256) void lmhead_f32_kernel(const float* __restrict__ A,
+                                                         const float* __restrict__ W,
+                                                         float* __restrict__ C, int M, int N,
+                                                         int K) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int m0 = blockIdx.y * 8;
+  if (n >= N) return;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const float* w = W + (size_t)n * K;
+  for (int k = 0; k < K; k += 4) {
+    const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(w + k);
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm) {
+      if (m0 + mm < M) {
+        const f32x4_t av = *reinterpret_cast<const f32x4_t*>(A + (size_t)(m0 + mm) * K + k);
+        acc[mm] = fmaf(av[0], wv[0], acc[mm]);
+        acc[mm] = fmaf(av[1], wv[1], acc[mm]);
+        acc[mm] = fmaf(av[2], wv[2], acc[mm]);
+        acc[mm] = fmaf(av[3], wv[3], acc[mm]);
+      }
+    }
+  }
+#pragma unroll
+  for (int mm = 0; mm < 8; ++mm)
+    if (m0 + mm < M) C[(size_t)(m0 + mm) * N + n] = acc[mm];
+}
+
+template <int BM, int BN, int BK, int WM, int WN>
+hipError_t launch_bf16(const uint16_t* h, const uint16_t* W, float* z, int M, int H, int V,
+                       hipStream_t s) {
+  const int mt = (M + BM - 1) / BM;
+  const int nt = (V + BN - 1) / BN;
+  if (H % BK == 0)
+    hipLaunchKernelGGL((lmhead_bf16_kernel<BM, BN, BK, WM, WN, false>), dim3((unsigned)(mt * nt)),
+                       dim3(WM * WN * 64), 0, s, h, W, z, M, V, H, mt, nt);
+  else
+    hipLaunchKernelGGL((lmhead_bf16_kernel<BM, BN, BK, WM, WN, true>), dim3((unsigned)(mt * nt)),
+                       dim3(WM * WN * 64), 0, s, h, W, z, M, V, H, mt, nt);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_lmhead(const void* h, const void* W, float* logits, int M, int H, int V,
+                         int dtype, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (dtype == 1) {
+    return launch_bf16<256, 256, 64, 2, 2>(static_cast<const uint16_t*>(h),
+                                           static_cast<const uint16_t*>(W), logits, M, H, V, s);
+  }
+  const dim3 grid((unsigned)((V + 255) / 256), (unsigned)((M + 7) / 8));
+  hipLaunchKernelGGL(lmhead_f32_kernel, grid, dim3(256), 0, s, static_cast<const float*>(h),
+                     static_cast<const float*>(W), logits, M, V, H);
+  return hipGetLastError();
+}
+
+}  // namespace dflash2

@@ -1,0 +1,285 @@
+// Per-row top-16 of fp32 logits ("DFlash 2: Keep Drafting Parallel", section
+// "A lightweight path selector": 16 candidates per position).
+//
+// Order: value descending, then token id ascending.  Each (value, id) pair is
+// packed into one 64-bit key that is larger exactly when the pair ranks
+// higher:  key = ord(value) << 32 | ~id,  ord() mapping canonical floats
+// (-0 -> +0, NaN -> -inf) onto uint32 in the same order.  Every key of a
+// real element is > 0, so 0 marks an empty list slot.
+//
+// A wavefront keeps its best 16 keys sorted in lanes 0..15 of each 16-lane
+// row (the four rows hold the same list) and streams its share of the row
+// with 16-byte loads.  An element is inspected only when its value is not
+// below the current 16th value (one compare per element in the common case);
+// survivors are inserted one at a time by a shift-insert across the row.
+// A row is split over several workgroups; their lists are merged by a second
+// one-wave-per-row kernel.
+#include "common.hpp"
+
+namespace dflash2 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxSplits = 32;
+
+__device__ __forceinline__ uint32_t ord_of(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (f != f) u = 0xff800000u;          // NaN ranks as -inf
+  if (u == 0x80000000u) u = 0u;         // -0 ranks as +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float val_of(uint32_t o) {
+  const uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t key_of(float f, uint32_t idx) {
+  return ((uint64_t)ord_of(f) << 32) | (uint32_t)(~idx);
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Sorted list of 16 keys per 16-lane row; slot = lane & 15.
+struct WaveTop16 {
+  uint64_t key;   // this lane's slot
+  uint64_t thr;   // 16th key (wave-uniform)
+  float thr_f;    // value of the 16th key; -inf while the list is not full
+
+  __device__ void init() {
+    key = 0;
+    thr = 0;
+    thr_f = -INFINITY;
+  }
+  __device__ void refresh() {
+    thr = readlane64(key, 15);
+    thr_f = thr ? val_of((uint32_t)(thr >> 32)) : -INFINITY;
+  }
+  // Insert c (wave-uniform, c > thr).  Slot s takes max(l[s], min(l[s-1], c)),
+  // l[-1] = +inf; the shift by one slot is a DPP row_shr:1 (slot 0 keeps the
+  // all-ones sentinel).
+  __device__ void insert(uint64_t c) {
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0xffffffffu, (uint32_t)key, 0x111, 0xf, 0xf, false);
+    const uint32_t hi =
+        __builtin_amdgcn_update_dpp(0xffffffffu, (uint32_t)(key >> 32), 0x111, 0xf, 0xf, false);
+    const uint64_t up = ((uint64_t)hi << 32) | lo;
+    const uint64_t m = up < c ? up : c;
+    key = key > m ? key : m;
+    refresh();
+  }
+  // Offer one (value, id) pair (wave-uniform).
+  __device__ void offer(float v, uint32_t idx) {
+    const uint64_t c = key_of(v, idx);
+    if (c > thr) insert(c);
+  }
+};
+
+__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
+  const uint32_t lo = __shfl((int)(uint32_t)v, src, 64);
+  const uint32_t hi = __shfl((int)(uint32_t)(v >> 32), src, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Bitonic sort of one key per lane across the wavefront, descending (lane 0
+// ends with the largest).
+__device__ uint64_t wave_sort_desc(uint64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t o = shfl64(v, lane ^ j);
+      const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+      v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
+    }
+  }
+  return v;
+}
+
+// A candidate may rank in the list unless it is strictly below the 16th value
+// (NaN always passes here and is decided exactly in offer()).
+__device__ __forceinline__ bool may_enter(float v, float thr_f) { return !(v < thr_f); }
+
+// Stream [c0, c1) of one row; VEC = 4 uses 16-byte loads (row and c0 16-byte
+// aligned), VEC = 1 scalar loads.  The four waves of the block interleave in
+// 64*VEC-element runs; each lane keeps kUnroll loads in flight.
+//
+// Warm start: on its first vector each lane finds its own largest key; the
+// wave sorts those 64 keys and takes the top 16 as its initial list (they are
+// real elements, so the list is exact), then offers only the other values of
+// that vector.  This replaces ~64*VEC serial inserts per wave with one sort.
+template <int VEC>
+__device__ void scan_range(const float* __restrict__ row, int c0, int c1, WaveTop16& top) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  constexpr int kUnroll = 8;
+  const int stride = kThreads * VEC;  // elements per block-wide step
+  bool first = true;
+  for (int base = c0 + wave * 64 * VEC; base < c1; base += stride * kUnroll) {
+    float v[kUnroll][VEC];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int e = base + u * stride + lane * VEC;
+      ok[u] = e < c1;
+      if (VEC == 4) {
+        f32x4_t q = ok[u] ? *reinterpret_cast<const f32x4_t*>(row + e) : f32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) v[u][k] = q[k];
+      } else {
+        v[u][0] = ok[u] ? row[e] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int e0 = base + u * stride;
+      int skip = -1;  // the lane's own maximum, already in the list (warm start)
+      if (first && u == 0) {
+        first = false;
+        uint64_t best = 0;
+        if (ok[0]) {
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) {
+            const uint64_t c = key_of(v[0][k], (uint32_t)(e0 + lane * VEC + k));
+            if (c > best) {
+              best = c;
+              skip = k;
+            }
+          }
+        }
+        top.key = shfl64(wave_sort_desc(best), lane & 15);
+        top.refresh();
+      }
+      bool pass = false;
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) pass |= (k != skip) && may_enter(v[u][k], top.thr_f);
+      pass &= ok[u];
+      uint64_t mask = __ballot(pass);
+      while (mask) {
+        const int src = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        const int sk = __builtin_amdgcn_readlane(skip, src);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+          const float vv = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v[u][k]), src));
+          if (k != sk) top.offer(vv, (uint32_t)(e0 + src * VEC + k));
+        }
+      }
+    }
+  }
+}
+
+// Merge the four waves' lists of a block into wave 0.
+__device__ void merge_block(WaveTop16& top, uint64_t* lds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  if (lane < 16) lds[wave * 16 + lane] = top.key;
+  __syncthreads();
+  if (wave == 0) {
+    for (int i = 16; i < 64; ++i) {
+      const uint64_t c = lds[i];
+      if (c > top.thr) top.insert(c);
+    }
+  }
+}
+
+__device__ __forceinline__ void write_final(const WaveTop16& top, float* val, int32_t* idx) {
+  const int lane = threadIdx.x & 63;
+  if (lane < 16) {
+    val[lane] = val_of((uint32_t)(top.key >> 32));
+    idx[lane] = (int32_t)(~(uint32_t)top.key);
+  }
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kThreads) void topk16_scan_kernel(const float* __restrict__ logits,
+                                                               int V, int splits, int chunk,
+                                                               float* __restrict__ top_val,
+                                                               int32_t* __restrict__ top_idx,
+                                                               uint64_t* __restrict__ part) {
+  __shared__ uint64_t lds[64];
+  const int m = blockIdx.x / splits;
+  const int sp = blockIdx.x - m * splits;
+  const float* row = logits + (size_t)m * V;
+  const int c0 = sp * chunk;
+  const int c1 = min(V, c0 + chunk);
+  WaveTop16 top;
+  top.init();
+  if (c0 < c1) scan_range<VEC>(row, c0, c1, top);
+  merge_block(top, lds);
+  if ((threadIdx.x >> 6) != 0) return;
+  if (splits == 1) {
+    write_final(top, top_val + (size_t)m * kTopK, top_idx + (size_t)m * kTopK);
+  } else if ((threadIdx.x & 63) < 16) {
+    part[((size_t)m * splits + sp) * kTopK + (threadIdx.x & 15)] = top.key;
+  }
+}
+
+// One wave per row merges `splits` partial lists.
+__global__ __launch_bounds__(64) void topk16_merge_kernel(const uint64_t* __restrict__ part,
+                                                          int splits, float* __restrict__ top_val,
+                                                          int32_t* __restrict__ top_idx) {
+  const int m = blockIdx.x;
+  const int lane = threadIdx.x;
+  const uint64_t* p = part + (size_t)m * splits * kTopK;
+  const int n = splits * kTopK;
+  WaveTop16 top;
+  top.init();
+  for (int base = 0; base < n; base += 64) {
+    const int e = base + lane;
+    const uint64_t c = e < n ? p[e] : 0ull;
+    uint64_t mask = __ballot(c > top.thr);
+    while (mask) {
+      const int src = __builtin_ctzll(mask);
+      mask &= mask - 1;
+      const uint64_t cc = readlane64(c, src);
+      if (cc > top.thr) top.insert(cc);
+    }
+  }
+  write_final(top, top_val + (size_t)m * kTopK, top_idx + (size_t)m * kTopK);
+}
+
+}  // namespace
+
+int topk16_splits(int M, int V) {
+  // About 512 blocks (2048 waves, each with 8 loads per lane in flight) and
+  // chunks of at least 4096 values; fewer splits mean fewer lists to warm up.
+  int s = M > 0 ? (512 + M - 1) / M : 1;
+  const int by_len = V / 4096;
+  if (s > by_len) s = by_len;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : s;
+}
+
+size_t topk16_workspace_bytes(int M, int V) {
+  const int s = topk16_splits(M, V);
+  return s > 1 ? (size_t)M * s * kTopK * sizeof(uint64_t) : 0;
+}
+
+hipError_t launch_topk16(const float* logits, float* top_val, int32_t* top_idx, int M, int V,
+                         void* workspace, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int splits = topk16_splits(M, V);
+  const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
+  int chunk = (V + splits - 1) / splits;
+  chunk = (chunk + 3) & ~3;  // keep every chunk start 16-byte aligned
+  uint64_t* part = static_cast<uint64_t*>(workspace);
+  const dim3 grid((unsigned)((long long)M * splits));
+  if (vec)
+    hipLaunchKernelGGL(topk16_scan_kernel<4>, grid, dim3(kThreads), 0, s, logits, V, splits,
+                       chunk, top_val, top_idx, part);
+  else
+    hipLaunchKernelGGL(topk16_scan_kernel<1>, grid, dim3(kThreads), 0, s, logits, V, splits,
+                       chunk, top_val, top_idx, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  hipLaunchKernelGGL(topk16_merge_kernel, dim3((unsigned)M), dim3(64), 0, s, part, splits,
+                     top_val, top_idx);
+  return hipGetLastError();
+}
+
+}  // namespace dflash2

@@ -1,0 +1,175 @@
+/*
+ * dflash2.h -- C ABI of the DFlash 2 draft-select-verify step on MI355X (gfx950).
+ *
+ * The step (per block of L drafted positions):
+ *   1. two-tap local conv            dflash2_twotap_conv
+ *   2. LM-head logits + top-16       dflash2_logits_topk  (= dflash2_lmhead_logits
+ *                                                            then dflash2_topk16)
+ *   3. adjacent-pair scores          dflash2_pair_score
+ *   4. max-plus path walk            dflash2_path_select
+ *   5. greedy verification           dflash2_verify_greedy
+ *
+ * Sources are cited by page title and section:
+ *   [POST]   "DFlash 2: Keep Drafting Parallel" (Inco AI).
+ *   [GLONCE] "Inco AI's DFlash 2 lifts LLM decoding output 16-25%".
+ *
+ * Conventions shared by every call
+ *   - Every tensor argument is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or keeps a pointer past the call.
+ *   - Tensors are dense row-major, last index fastest.
+ *   - Each call validates its arguments on the host BEFORE launching anything.
+ *     On failure it returns a negative dflash2_status and no output is
+ *     touched.  On success it has only enqueued kernels on `stream` (a
+ *     hipStream_t passed as void*, NULL = the default stream) and returns
+ *     without synchronising; a fault inside a kernel surfaces at the caller's
+ *     next synchronisation.  Launch errors return DFLASH2_EHIP.
+ *   - Calls are re-entrant and keep no state; concurrent calls on different
+ *     streams may share read-only inputs.
+ *   - Token ids are int32 in [0, V).  Kernels never read outside their
+ *     buffers: an id outside [0, V) yields NaN scores instead of a read.
+ *   - dtype selects the storage type of activations and weights:
+ *     DFLASH2_F32 (fp32) or DFLASH2_BF16 (bf16).  Accumulation is fp32.
+ */
+#ifndef DFLASH2_H
+#define DFLASH2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFLASH2_OK = 0,
+  DFLASH2_EINVAL = -1,        /* bad pointer, size, shape or aliasing */
+  DFLASH2_EUNSUPPORTED = -2,  /* valid request this build does not implement */
+  DFLASH2_EHIP = -3,          /* a HIP launch or runtime call failed */
+  DFLASH2_EWORKSPACE = -4     /* workspace missing or smaller than queried */
+} dflash2_status;
+
+typedef enum { DFLASH2_F32 = 0, DFLASH2_BF16 = 1 } dflash2_dtype;
+
+#define DFLASH2_TOPK 16      /* candidates per position ([POST] "A lightweight path selector") */
+#define DFLASH2_MAX_L 64     /* longest block the path walk accepts */
+#define DFLASH2_MAX_RANK 256 /* largest pair-factor rank */
+
+/* Library version as 10000*major + 100*minor + patch. */
+int dflash2_version(void);
+
+/* Static text for a status code. */
+const char* dflash2_strerror(int status);
+
+/*
+ * Two-tap dynamic depthwise conv over each block.
+ * [POST] "A lightweight local convolution", eq. Conv_k and Fig. 4:
+ *   y[b,t,c] = (k0[c] + D[b,t,g(c),0]) * x[b,t,c] + (k1[c] + D[b,t,g(c),1]) * p[b,t,c]
+ *   p[b,t,:] = x[b,t-1,:] for t > 0, anchor_h[b,:] for t = 0 (the last verified
+ *              token's representation; zeros when anchor_h is NULL)
+ *   D[b,t,g,j] = sum_c x[b,t,c] * proj[c, 2g+j]   (0 when proj is NULL)
+ *   g(c) = c / (H / groups)
+ * x, y     [B, L, H] of dtype; y must not overlap x (or anchor_h).
+ * anchor_h [B, H] of dtype, or NULL.
+ * k0, k1   [H] fp32 base taps.
+ * proj     [H, 2*groups] fp32 correction map, or NULL for static taps.
+ * groups   >= 1, divides H (ignored when proj is NULL).
+ * B >= 0 (0 is a no-op), L >= 1, H >= 8 with H % 8 == 0.  All pointers 16-byte aligned.
+ * Arithmetic in fp32; each output is rounded once to dtype (round to nearest even).
+ */
+int dflash2_twotap_conv(const void* x, const void* anchor_h, void* y,
+                        const float* k0, const float* k1,
+                        const float* proj, int groups,
+                        int B, int L, int H, int dtype, void* stream);
+
+/*
+ * LM-head logits: logits[m, n] = sum_c h[m, c] * W[n, c]  (fp32 accumulate).
+ * [POST] "A lightweight path selector": the unary term of every pair score is
+ * the drafter's own logit, computed once and reused.
+ * h [M, H] of dtype, W [V, H] of dtype (K-contiguous: "NT" product),
+ * logits [M, V] fp32.  M >= 0, H >= 8 with H % 8 == 0, V >= 16; h, W, logits
+ * 16-byte aligned.
+ * bf16 operands run on the gfx950 bf16 matrix cores.
+ */
+int dflash2_lmhead_logits(const void* h, const void* W, float* logits,
+                          int M, int H, int V, int dtype, void* stream);
+
+/* Bytes of workspace dflash2_topk16 needs for an [M, V] problem with K = 16. */
+size_t dflash2_topk16_workspace(int M, int V, int K);
+
+/*
+ * Per-row top-16 of fp32 logits [M, V]:
+ * [POST] "A lightweight path selector": the drafter keeps its 16 best tokens
+ * at every position.  Order: value descending, equal values by lower token id
+ * first.  -0 compares equal to +0 and is reported as +0; NaN ranks as -inf
+ * and is reported as -inf.
+ * top_val [M, 16] fp32, top_idx [M, 16] int32 (slot 0 = top-1).
+ * K must be 16; V >= 16.  workspace: at least dflash2_topk16_workspace bytes
+ * (may be NULL when that is 0), 256-byte aligned.
+ */
+int dflash2_topk16(const float* logits, float* top_val, int32_t* top_idx,
+                   int M, int V, int K, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
+ * Workspace for dflash2_logits_topk.  logits_given != 0: the caller passes a
+ * logits buffer; 0: the logits are produced in the workspace.
+ */
+size_t dflash2_logits_topk_workspace(int M, int H, int V, int K, int dtype, int logits_given);
+
+/*
+ * Logits and top-16 in one call (dflash2_lmhead_logits then dflash2_topk16).
+ * logits may be NULL (then the workspace holds them, see the query above).
+ */
+int dflash2_logits_topk(const void* h, const void* W, float* logits,
+                        float* top_val, int32_t* top_idx,
+                        int M, int H, int V, int K, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Adjacent-pair scores.  [POST] "A lightweight path selector", eq. S_t(a,b):
+ * the candidate's own logit plus a low-rank match with the previous token, in
+ * the ungated form (context gate = 1) with per-token factors U, V:
+ *   S0[b, j]        = top_val[b,0,j] + U[anchor_tok[b]] . Vf[top_idx[b,0,j]]
+ *   S[b, t-1, i, j] = top_val[b,t,j] + U[top_idx[b,t-1,i]] . Vf[top_idx[b,t,j]],  t = 1..L-1
+ * top_val [B, L, 16] fp32, top_idx [B, L, 16] int32 in [0, V).
+ * anchor_tok [B] int32 (last verified token), or NULL for no match term at t = 0.
+ * U, Vf [V, r] of dtype; 1 <= r <= 256.
+ * S0 [B, 16] fp32; S [B, L-1, 16, 16] fp32 (may be NULL when L == 1).
+ * fp32 accumulation; ids outside [0, V) give NaN entries.
+ */
+int dflash2_pair_score(const float* top_val, const int32_t* top_idx,
+                       const int32_t* anchor_tok, const void* U, const void* Vf,
+                       int B, int L, int V, int r, int dtype,
+                       float* S0, float* S, void* stream);
+
+/*
+ * Max-plus (Viterbi) path over the pair scores, one wavefront per block.
+ * [POST] "A lightweight path selector" walks the precomputed scores serially
+ * from the last verified token; this call takes the exact best path:
+ *   d_0 = S0,  d_t[j] = max_i fl32(d_{t-1}[i] + S[t-1,i,j]),
+ * the lowest slot wins every tie (each max and the final argmax).
+ * S0 [B,16], S [B,L-1,16,16] (NULL allowed when L == 1), 1 <= L <= 64.
+ * path_slot [B, L] int32 slots; path_score [B] fp32 = d_{L-1}[final slot].
+ * top_idx [B, L, 16] and path_tok [B, L]: both given (path_tok[b,t] =
+ * top_idx[b,t,path_slot[b,t]]) or both NULL.
+ */
+int dflash2_path_select(const float* S0, const float* S, const int32_t* top_idx,
+                        int B, int L, int32_t* path_slot, int32_t* path_tok,
+                        float* path_score, void* stream);
+
+/*
+ * Greedy verification.  [POST] "The right token is already in the candidates",
+ * Table 1: the acceptance length counts the verifier's next token.
+ *   n = number of leading t with path_tok[b,t] == target[b,t]  (0 <= n <= L)
+ *   accept_len[b] = n + 1,  next_tok[b] = target[b, n]
+ * path_tok [B, L], target [B, L+1] (target[b, L] is the token after a fully
+ * accepted block), accept_len [B], next_tok [B] (may be NULL).
+ */
+int dflash2_verify_greedy(const int32_t* path_tok, const int32_t* target,
+                          int B, int L, int32_t* accept_len, int32_t* next_tok,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH2_H */

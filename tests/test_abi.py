@@ -1,0 +1,138 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/dflash2.h declares, and rejects bad arguments on the host before any
+launch (fake device addresses are safe here: validation fails first)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_drafting_amd as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash2.h")
+
+EINVAL, EUNSUP, EHIP, EWS = -1, -2, -3, -4
+P = 0x7f0000001000          # 4 KiB-aligned fake device address (never dereferenced)
+Q = 0x7f0000100000          # another, far from P
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(dflash2_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_five_step_calls():
+    names = _declared()
+    for n in ("dflash2_twotap_conv", "dflash2_logits_topk", "dflash2_pair_score",
+              "dflash2_path_select", "dflash2_verify_greedy"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = bd.lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", bd.library_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (dflash2_\w+)", out))
+    assert exported == set(_declared())      # nothing undeclared leaks out
+
+
+def test_version_and_strerror():
+    L = bd.lib()
+    assert L.dflash2_version() >= 10000
+    for s in (0, EINVAL, EUNSUP, EHIP, EWS):
+        assert len(L.dflash2_strerror(s)) > 0
+    assert L.dflash2_strerror(12345) == b"unknown status"
+
+
+def test_conv_validation():
+    f = bd.lib().dflash2_twotap_conv
+    ok = dict(x=P, a=None, y=Q, k0=P + 0x80000, k1=P + 0x90000, pr=None, g=1, B=2, L=8, H=64, dt=1)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["a"], a["y"], a["k0"], a["k1"], a["pr"], a["g"], a["B"], a["L"],
+                 a["H"], a["dt"], None)
+
+    assert call(B=0) == 0                     # empty batch: nothing to do
+    assert call(x=None) == EINVAL
+    assert call(k1=None) == EINVAL
+    assert call(L=0) == EINVAL
+    assert call(H=12) == EINVAL               # H % 8
+    assert call(dt=7) == EINVAL
+    assert call(y=P) == EINVAL                # y aliases x
+    assert call(y=P + 64) == EINVAL           # partial overlap
+    assert call(x=P + 4) == EINVAL            # misaligned
+    assert call(pr=P + 0xa0000, g=3) == EINVAL   # groups must divide H
+    assert call(pr=P + 0xa0000, g=0) == EINVAL
+    assert call(B=-1) == EINVAL
+
+
+def test_lmhead_and_topk_validation():
+    L = bd.lib()
+    assert L.dflash2_lmhead_logits(P, Q, P + 0x10000000, 8, 64, 15, 1, None) == EINVAL  # V < 16
+    assert L.dflash2_lmhead_logits(P, Q, P + 0x10000000, 8, 60, 64, 1, None) == EINVAL  # H % 8
+    assert L.dflash2_lmhead_logits(P, Q, None, 8, 64, 64, 1, None) == EINVAL
+    assert L.dflash2_lmhead_logits(P, Q, P, 8, 64, 64, 1, None) == EINVAL              # aliasing
+    assert L.dflash2_lmhead_logits(P, Q, None, 0, 64, 64, 1, None) == 0                 # M == 0
+    assert L.dflash2_topk16(P, Q, Q + 4096, 4, 100, 8, None, 0, None) == EINVAL         # K != 16
+    assert L.dflash2_topk16(P, None, Q, 4, 100, 16, None, 0, None) == EINVAL
+    need = L.dflash2_topk16_workspace(64, 151936, 16)     # short batch: rows split
+    assert need > 0 and L.dflash2_topk16_workspace(64, 151936, 8) == 0
+    big = 0x7e0000000000
+    assert L.dflash2_topk16(big, Q, Q + 65536, 64, 151936, 16, None, 0, None) == EWS
+    assert L.dflash2_topk16(big, Q, Q + 65536, 64, 151936, 16, P, need - 1, None) == EWS
+    assert L.dflash2_topk16(big, Q, Q + 65536, 64, 151936, 16, P + 16, need, None) == EWS  # align
+    ws_given = L.dflash2_logits_topk_workspace(512, 5120, 151936, 16, 1, 1)
+    ws_none = L.dflash2_logits_topk_workspace(512, 5120, 151936, 16, 1, 0)
+    assert ws_none - ws_given == 512 * 151936 * 4
+    assert L.dflash2_logits_topk(P, Q, None, P + 4096, P + 8192, 512, 5120, 151936, 16, 1,
+                                 None, 0, None) == EWS                             # no room for logits
+
+
+def test_pair_select_verify_validation():
+    L = bd.lib()
+    ps = L.dflash2_pair_score
+    #        tv  ti          anc   U   V             B  L  V    r  dt S0           S
+    args = [P, P + 0x10000, None, Q, Q + 0x100000, 2, 4, 100, 8, 1, P + 0x20000, P + 0x30000]
+    assert ps(*args[:8], 0, *args[9:], None) == EINVAL       # r = 0
+    assert ps(*args[:8], 257, *args[9:], None) == EINVAL     # r > 256
+    assert ps(*args[:6], 65, *args[7:], None) == EINVAL      # L > 64
+    assert ps(*args[:6], 0, *args[7:], None) == EINVAL       # L = 0
+    assert ps(*args[:7], 15, *args[8:], None) == EINVAL      # V < 16
+    bad = list(args)
+    bad[11] = P                                              # S overlaps top_val
+    assert ps(*bad, None) == EINVAL
+    bad = list(args)
+    bad[11] = None                                           # S missing with L > 1
+    assert ps(*bad, None) == EINVAL
+    bad = list(args)
+    bad[11] = P + 0x30004                                    # S misaligned
+    assert ps(*bad, None) == EINVAL
+    assert ps(*args[:5], 0, *args[6:], None) == 0            # B = 0
+
+    sel = L.dflash2_path_select
+    assert sel(P, Q, None, 2, 0, P + 0x1000, None, P + 0x2000, None) == EINVAL
+    assert sel(P, Q, None, 2, 65, P + 0x1000, None, P + 0x2000, None) == EINVAL
+    assert sel(P, Q, P + 0x9000, 2, 4, P + 0x1000, None, P + 0x2000, None) == EINVAL  # tok pair
+    assert sel(P, None, None, 2, 4, P + 0x1000, None, P + 0x2000, None) == EINVAL     # S missing
+    assert sel(P, Q, None, 2, 4, P + 0x1000, None, P + 0x1000, None) == EINVAL        # outs alias
+    assert sel(P, Q, None, 0, 4, P + 0x1000, None, P + 0x2000, None) == 0
+
+    ver = L.dflash2_verify_greedy
+    assert ver(P, Q, 4, 0, P + 0x1000, None, None) == EINVAL
+    assert ver(None, Q, 4, 8, P + 0x1000, None, None) == EINVAL
+    assert ver(P, Q, 4, 8, P, None, None) == EINVAL           # accept_len aliases path_tok
+    assert ver(P, Q, 4, 8, P + 0x1000, P + 0x1000, None) == EINVAL
+    assert ver(P, Q, 0, 8, P + 0x1000, None, None) == 0
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((1, 8, 64), dtype=torch.bfloat16)
+    k = torch.zeros(64)
+    with pytest.raises(ValueError):
+        bd.twotap_conv(x, k, k)

@@ -1,0 +1,248 @@
+"""Stage-by-stage parity of the HIP library with the CPU oracle (GPU).
+
+Every GPU stage is fed the oracle's own inputs for that stage and compared
+element by element, at sizes the oracle finishes in seconds that still span
+several tiles and ragged tails, plus the edge cases each stage has.
+
+Bars (floating point from the arithmetic, integers exact):
+  conv      |y - y_ora| <= ulp_storage(y_ora) + (H + 4) 2^-24 * bound, bound =
+            the conv of absolute values; bf16 outputs bit-exact (the kernel
+            evaluates in fp64 and rounds once)
+  logits    |z - z_ora| <= 1e-3 max(|z_ora|, 1); bit-exact on dyadic inputs
+  top-16    bit-exact ids and values (decided on the same fp32 logits)
+  pairs     |S - S_ora| <= 1e-4
+  path      bit-exact slots, tokens and fp32 score (the oracle decides in fp32)
+  verify    exact
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_drafting_amd as bd
+import oracle as O
+import workloads as WL
+from _devutil import bf16_ulp, to_dev, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _bits_or_f32(a, dt):
+    return WL.to_bf16_bits(a) if dt == "bf16" else a.astype(np.float32)
+
+
+# ------------------------------------------------------------------ conv
+def _conv_case(B, L, H, dt, mode, groups, seed, anchor=True):
+    g = np.random.default_rng(seed)
+    x = _bits_or_f32(g.standard_normal((B, L, H)).astype(np.float32), dt)
+    a = _bits_or_f32(g.standard_normal((B, H)).astype(np.float32), dt) if anchor else None
+    k0 = (g.standard_normal(H) * 0.7).astype(np.float32)
+    k1 = (g.standard_normal(H) * 0.7).astype(np.float32)
+    P = (g.standard_normal((H, 2 * groups)) * np.sqrt(0.01 / H)).astype(np.float32) if mode else None
+    return x, a, k0, k1, P
+
+
+def _conv_check(x, a, k0, k1, P, groups, dt):
+    B, L, H = x.shape
+    xo = O.as_f64(x, dt)
+    ao = None if a is None else O.as_f64(a, dt)
+    Pd = None if P is None else P.astype(np.float64)
+    want = O.round_to_dtype(O.twotap_conv(xo, ao, k0.astype(np.float64), k1.astype(np.float64),
+                                          Pd, groups), dt)
+    bound = O.twotap_conv(np.abs(xo), None if ao is None else np.abs(ao), np.abs(k0.astype(np.float64)),
+                          np.abs(k1.astype(np.float64)), None if Pd is None else np.abs(Pd), groups)
+    y = bd.twotap_conv(to_dev(x, dt), torch.from_numpy(k0).to(DEV), torch.from_numpy(k1).to(DEV),
+                       None if a is None else to_dev(a, dt),
+                       None if P is None else torch.from_numpy(P).to(DEV), groups)
+    got = O.as_f64(to_host_bits(y), dt)
+    tol = (bf16_ulp(want) if dt == "bf16" else 0.0) + (H + 4) * 2.0 ** -24 * bound
+    err = np.abs(got - want)
+    assert np.all(err <= tol), f"max err {err.max()} (tol {tol[err > tol][:4]})"
+    return float(np.mean(got != want))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,H,mode,groups", [
+    (3, 5, 64, 0, 1), (2, 1, 8, 0, 1), (4, 16, 5120, 0, 1), (5, 8, 136, 1, 1),
+    (2, 16, 5120, 1, 1), (3, 4, 256, 1, 16), (2, 3, 5120, 1, 320), (1, 2, 64, 1, 64),
+])
+def test_conv_parity(dt, B, L, H, mode, groups):
+    x, a, k0, k1, P = _conv_case(B, L, H, dt, mode, groups, seed=B * 100 + L * 10 + mode)
+    frac = _conv_check(x, a, k0, k1, P, groups, dt)
+    # the kernel evaluates in fp64 and rounds once (round-to-odd, then RNE):
+    # only values within ~2^-52 relative of a rounding boundary can differ
+    assert frac == 0.0 if dt == "bf16" else frac < 1e-4
+
+
+def test_conv_no_anchor_and_special_taps_bit_exact():
+    B, L, H = 3, 6, 128
+    x, a, _, _, _ = _conv_case(B, L, H, "bf16", 0, 1, seed=5)
+    ones, zeros = np.ones(H, np.float32), np.zeros(H, np.float32)
+    xd, ad = to_dev(x, "bf16"), to_dev(a, "bf16")
+    y = to_host_bits(bd.twotap_conv(xd, torch.from_numpy(ones).to(DEV), torch.from_numpy(zeros).to(DEV), ad))
+    np.testing.assert_array_equal(y, x)                                  # identity
+    y = to_host_bits(bd.twotap_conv(xd, torch.from_numpy(zeros).to(DEV), torch.from_numpy(ones).to(DEV), ad))
+    np.testing.assert_array_equal(y[:, 1:], x[:, :-1])                   # shift
+    np.testing.assert_array_equal(y[:, 0], a)                            # anchor
+    y = to_host_bits(bd.twotap_conv(xd, torch.from_numpy(zeros).to(DEV), torch.from_numpy(ones).to(DEV), None))
+    assert not np.any(y[:, 0] & 0x7fff)                                  # zero anchor
+    _conv_check(x, None, (np.arange(H) % 3).astype(np.float32), np.full(H, 0.5, np.float32), None, 1, "bf16")
+
+
+def test_conv_empty_batch_is_noop():
+    x = torch.empty((0, 8, 64), dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros(64, device=DEV)
+    assert bd.twotap_conv(x, k, k).shape == (0, 8, 64)
+
+
+# ------------------------------------------------------------------ logits
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("M,H,V", [(1, 8, 16), (37, 64, 1000), (300, 136, 4099), (513, 520, 2048),
+                                   (64, 5120, 300), (257, 2560, 777)])
+def test_lmhead_parity(dt, M, H, V):
+    g = np.random.default_rng(M + H + V)
+    y = _bits_or_f32(g.standard_normal((M, H)).astype(np.float32), dt)
+    W = _bits_or_f32((g.standard_normal((V, H)) / np.sqrt(H)).astype(np.float32), dt)
+    want = O.lm_logits(O.as_f64(y, dt), W, dt).astype(np.float64)
+    got = bd.lmhead_logits(to_dev(y, dt), to_dev(W, dt)).cpu().numpy().astype(np.float64)
+    err = np.abs(got - want)
+    assert np.all(err <= 1e-3 * np.maximum(np.abs(want), 1.0)), err.max()
+
+
+def test_lmhead_one_hot_and_dyadic_bit_exact():
+    M, H, V = 70, 256, 1100
+    g = np.random.default_rng(3)
+    W = WL.to_bf16_bits((g.standard_normal((V, H)) / 16).astype(np.float32))
+    y = np.zeros((M, H), np.float32)
+    cols = g.integers(0, H, M)
+    y[np.arange(M), cols] = 1.0
+    got = bd.lmhead_logits(to_dev(WL.to_bf16_bits(y), "bf16"), to_dev(W, "bf16")).cpu().numpy()
+    np.testing.assert_array_equal(got, O.as_f64(W, "bf16")[:, cols].T.astype(np.float32))
+    # small integers and 1/64 multiples: every partial sum is exact in fp32
+    yi = np.clip(np.round(g.standard_normal((M, H)) * 3), -16, 16).astype(np.float32)
+    Wi = (np.clip(np.round(g.standard_normal((V, H)) * 2), -8, 8) / 64).astype(np.float32)
+    got = bd.lmhead_logits(to_dev(WL.to_bf16_bits(yi), "bf16"), to_dev(WL.to_bf16_bits(Wi), "bf16"))
+    want = O.lm_logits(yi.astype(np.float64), WL.to_bf16_bits(Wi), "bf16")
+    np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
+# ------------------------------------------------------------------ top-16
+def _topk_check(z):
+    tv, ti = bd.topk16(torch.from_numpy(z).to(DEV))
+    wv, wi = O.topk16(z)
+    np.testing.assert_array_equal(ti.cpu().numpy(), wi)
+    np.testing.assert_array_equal(tv.cpu().numpy().view(np.uint32), wv.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,V", [(1, 16), (3, 17), (7, 4099), (33, 151936), (512, 4096), (5, 100003)])
+def test_topk_parity_random(M, V):
+    g = np.random.default_rng(M * 7 + V)
+    _topk_check(g.standard_normal((M, V)).astype(np.float32))
+
+
+def test_topk_ties_zeros_nan_inf_and_adversarial_order():
+    V = 20000
+    g = np.random.default_rng(11)
+    rows = [
+        np.zeros(V),                                   # all tied: lowest 16 ids
+        np.where(np.arange(V) % 2 == 0, 0.0, -0.0),    # +0 / -0 mix
+        np.arange(V, dtype=np.float64),                # ascending: every value inserts
+        -np.arange(V, dtype=np.float64),               # descending
+        np.round(g.standard_normal(V) * 64) / 64,      # 1/64 grid: many ties
+        np.full(V, -np.inf),
+        np.where(g.random(V) < 0.5, np.nan, g.standard_normal(V)),
+        np.concatenate([[np.inf, np.nan, -np.inf], g.standard_normal(V - 3)]),
+    ]
+    z = np.stack(rows).astype(np.float32)
+    z[4, 1000:1040] = z[4].max()                       # 40-way tie at the top
+    _topk_check(z)
+    nan_rows = np.full((2, 64), np.nan, np.float32)    # everything ranks as -inf
+    _topk_check(nan_rows)
+
+
+# ------------------------------------------------------------------ pair scores
+def _pair_case(B, L, V, r, dt, seed, anchor=True):
+    g = np.random.default_rng(seed)
+    tv = g.standard_normal((B, L, 16)).astype(np.float32)
+    ti = g.integers(0, V, (B, L, 16)).astype(np.int32)
+    U = _bits_or_f32((g.standard_normal((V, r)) * np.sqrt(0.1)).astype(np.float32), dt)
+    Vf = _bits_or_f32((g.standard_normal((V, r)) * np.sqrt(0.1)).astype(np.float32), dt)
+    at = g.integers(0, V, B).astype(np.int32) if anchor else None
+    return tv, ti, at, U, Vf
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,V,r", [(1, 1, 64, 1), (3, 2, 500, 7), (4, 8, 4096, 32),
+                                     (5, 16, 151936, 64), (2, 16, 2000, 128), (2, 5, 300, 256),
+                                     (1, 64, 1000, 16)])
+def test_pair_parity(dt, B, L, V, r):
+    tv, ti, at, U, Vf = _pair_case(B, L, V, r, dt, seed=B + L + r)
+    wS0, wS = O.pair_scores(tv, ti, at, U, Vf, dt)
+    S0, S = bd.pair_score(torch.from_numpy(tv).to(DEV), torch.from_numpy(ti).to(DEV),
+                          torch.from_numpy(at).to(DEV), to_dev(U, dt), to_dev(Vf, dt))
+    assert np.abs(S0.cpu().numpy() - wS0).max() <= 1e-4
+    if L > 1:
+        assert np.abs(S.cpu().numpy() - wS).max() <= 1e-4
+
+
+def test_pair_without_anchor_and_bad_ids_give_nan():
+    tv, ti, _, U, Vf = _pair_case(2, 3, 100, 8, "f32", seed=1, anchor=False)
+    wS0, wS = O.pair_scores(tv, ti, None, U, Vf, "f32")
+    S0, S = bd.pair_score(torch.from_numpy(tv).to(DEV), torch.from_numpy(ti).to(DEV), None,
+                          torch.from_numpy(U).to(DEV), torch.from_numpy(Vf).to(DEV))
+    np.testing.assert_array_equal(S0.cpu().numpy(), wS0)
+    ti_bad = ti.copy()
+    ti_bad[1, 1, 5] = 100          # == V: out of range, at position 1
+    ti_bad[0, 0, 3] = -7           # negative, at position 0
+    S0, S = bd.pair_score(torch.from_numpy(tv).to(DEV), torch.from_numpy(ti_bad).to(DEV), None,
+                          torch.from_numpy(U).to(DEV), torch.from_numpy(Vf).to(DEV))
+    S, S0 = S.cpu().numpy(), S0.cpu().numpy()
+    assert np.isnan(S[1, 0, :, 5]).all() and np.isnan(S[1, 0]).sum() == 16   # as current token
+    assert np.isnan(S[1, 1, 5, :]).all() and np.isnan(S[1, 1]).sum() == 16   # as previous token
+    assert np.isnan(S0[0, 3]) and np.isnan(S0).sum() == 1
+    assert np.isnan(S[0, 0, 3, :]).all() and np.isnan(S[0, 0]).sum() == 16
+    ok = ~np.isnan(S)
+    np.testing.assert_allclose(S[ok], wS[ok], atol=1e-4, rtol=0)
+
+
+# ------------------------------------------------------------------ path walk
+@pytest.mark.parametrize("B,L,dyadic", [(1, 1, False), (7, 2, True), (64, 8, False), (64, 8, True),
+                                        (33, 16, True), (5, 64, False), (300, 3, True)])
+def test_path_select_bit_exact(B, L, dyadic):
+    g = np.random.default_rng(B * L)
+    if dyadic:
+        S0 = (np.round(g.standard_normal((B, 16)) * 2) / 4).astype(np.float32)
+        S = (np.round(g.standard_normal((B, L - 1, 16, 16)) * 2) / 4).astype(np.float32)
+    else:
+        S0 = g.standard_normal((B, 16)).astype(np.float32) * 4
+        S = g.standard_normal((B, L - 1, 16, 16)).astype(np.float32)
+    ti = g.integers(0, 151936, (B, L, 16)).astype(np.int32)
+    ws, wt, wsc = O.path_select(S0, S, ti)
+    slot, tok, score = bd.path_select(torch.from_numpy(S0).to(DEV),
+                                      torch.from_numpy(S).to(DEV) if L > 1 else None,
+                                      torch.from_numpy(ti).to(DEV))
+    np.testing.assert_array_equal(slot.cpu().numpy(), ws)
+    np.testing.assert_array_equal(tok.cpu().numpy(), wt)
+    np.testing.assert_array_equal(score.cpu().numpy().view(np.uint32), wsc.view(np.uint32))
+
+
+def test_path_select_all_tied_takes_slot_zero():
+    B, L = 4, 8
+    S0 = np.zeros((B, 16), np.float32)
+    S = np.zeros((B, L - 1, 16, 16), np.float32)
+    slot, _, score = bd.path_select(torch.from_numpy(S0).to(DEV), torch.from_numpy(S).to(DEV), None)
+    assert (slot.cpu().numpy() == 0).all() and (score.cpu().numpy() == 0).all()
+
+
+# ------------------------------------------------------------------ verify
+def test_verify_parity():
+    g = np.random.default_rng(5)
+    for B, L in ((1, 1), (100, 8), (1000, 16), (3, 64)):
+        path = g.integers(0, 3, (B, L)).astype(np.int32)
+        tgt = g.integers(0, 3, (B, L + 1)).astype(np.int32)
+        tgt[: B // 3, :L] = path[: B // 3]            # some full blocks
+        wa, wn = O.verify_greedy(path, tgt)
+        a, n = bd.verify_greedy(torch.from_numpy(path).to(DEV), torch.from_numpy(tgt).to(DEV))
+        np.testing.assert_array_equal(a.cpu().numpy(), wa)
+        np.testing.assert_array_equal(n.cpu().numpy(), wn)

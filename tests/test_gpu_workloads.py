@@ -1,0 +1,223 @@
+"""Full-size parity on the five workloads (GPU).
+
+The GPU runs the whole step on every block, in the same launch configuration
+the benchmark times.  The oracle recomputes a seeded subset of blocks
+(workloads.parity_subset) from the same inputs.  Checks:
+
+stage-wise (each GPU stage fed the oracle's input for that stage):
+  every conv application (<= 1 bf16 ulp), top-16 (bit-exact), pair scores
+  (<= 1e-4; bit-exact on the dyadic stress workload), path walk (bit-exact),
+  verification (exact);
+end to end (GPU stages fed by GPU stages), with the margin rule:
+  logits within 1e-3 max(|z|, 1); a top-16 slot must match where the
+  oracle's gap to its neighbours exceeds 1e-3; the path and acceptance length
+  must match where the oracle's best-vs-second path margin exceeds 1e-3 plus
+  the score drift the logits tolerance allows, else the GPU path must be
+  near-optimal under the oracle's scores;
+over all blocks (properties that hold at any size):
+  sorted distinct in-range candidates whose values are their logits, path
+  tokens are candidates, path score equals the path's score, acceptance in
+  [1, L+1] and equal to the oracle's verification of the GPU path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_drafting_amd as bd
+import oracle as O
+import workloads as WL
+from _devutil import bf16_ulp, convs_to_dev, to_dev, to_host_bits
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL_LOGIT = 1e-3
+MARGIN = 1e-3
+
+
+def _dt(w):
+    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+
+@pytest.fixture(scope="module", params=[0, 1, 2, 3, 4], ids=lambda c: f"w{c}")
+def case(request):
+    w = WL.WORKLOADS[request.param]
+    print(f"\n[workload {w.cid} {w.name}] B={w.B} L={w.L} H={w.H} V={w.V} r={w.r}", flush=True)
+    inp = WL.make_inputs(w)
+    dev = {
+        "x": to_dev(inp["x"], w.dtype),
+        "convs": convs_to_dev(inp["convs"], w.dtype),
+        "W": to_dev(inp["W"], w.dtype),
+        "U": to_dev(inp["U"], w.dtype),
+        "Vf": to_dev(inp["Vf"], w.dtype),
+        "anchor_tok": to_dev(inp["anchor_tok"], "i32"),
+    }
+    buf = bd.StepBuffers(w.B, w.L, w.H, w.V, _dt(w), DEV, n_convs=w.n_convs, keep_logits=True)
+    bd.run_step(buf, dev["x"], dev["convs"], dev["W"], dev["U"], dev["Vf"], dev["anchor_tok"], None)
+    torch.cuda.synchronize()
+    blocks = WL.parity_subset(w)
+    ora = O.run_step_front(w, inp, blocks)
+    # targets: planted from the oracle's candidates (or around its path) on the
+    # subset; the other blocks get targets from the GPU's own candidates
+    tgt_sub = WL.make_targets(w, ora["top_idx"], ora["path_tok"])
+    gpu_ti = buf.top_idx.view(w.B, w.L, 16).cpu().numpy()
+    gpu_tok = buf.path_tok.cpu().numpy()
+    tgt = WL.make_targets(w, gpu_ti, gpu_tok)
+    tgt[blocks] = tgt_sub
+    tgt_dev = to_dev(tgt, "i32")
+    bd.verify_greedy(buf.path_tok, tgt_dev, buf.accept_len, buf.next_tok)
+    torch.cuda.synchronize()
+    yield {"w": w, "inp": inp, "dev": dev, "buf": buf, "blocks": blocks, "ora": ora,
+           "tgt": tgt, "tgt_sub": tgt_sub}
+    del dev, buf
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ stage-wise
+def test_conv_stagewise(case):
+    w, inp, blocks = case["w"], case["inp"], case["blocks"]
+    x = O.as_f64(inp["x"][blocks], w.dtype)
+    worst = 0
+    for j, c in enumerate(inp["convs"]):
+        a = O.as_f64(c["anchor_h"][blocks], w.dtype)
+        k0, k1 = c["k0"].astype(np.float64), c["k1"].astype(np.float64)
+        P = None if c["proj"] is None else c["proj"].astype(np.float64)
+        want = O.round_to_dtype(O.twotap_conv(x, a, k0, k1, P, 1), w.dtype)
+        xin = torch.from_numpy(x).to(_dt(w)).to(DEV)           # exact: x is storage-valued
+        ain = torch.from_numpy(a).to(_dt(w)).to(DEV)
+        y = bd.twotap_conv(xin, torch.from_numpy(c["k0"]).to(DEV), torch.from_numpy(c["k1"]).to(DEV),
+                           ain, None if c["proj"] is None else torch.from_numpy(c["proj"]).to(DEV), 1)
+        got = y.double().cpu().numpy()
+        bound = O.twotap_conv(np.abs(x), np.abs(a), np.abs(k0), np.abs(k1), None if P is None else np.abs(P), 1)
+        tol = (bf16_ulp(want) if w.dtype == "bf16" else 0.0) + (w.H + 4) * 2.0 ** -24 * bound
+        bad = np.abs(got - want) > tol
+        assert not bad.any(), f"conv {j}: {bad.sum()} elements beyond tolerance"
+        worst = max(worst, int((got != want).sum()))
+        x = want
+    print(f"conv: {len(inp['convs'])} applications, max elements off by 1 ulp in one: {worst}")
+
+
+def test_topk_pair_select_verify_stagewise(case):
+    w, ora = case["w"], case["ora"]
+    z = ora["z"]
+    tv, ti = bd.topk16(torch.from_numpy(z).to(DEV))
+    np.testing.assert_array_equal(ti.cpu().numpy(), ora["top_idx"].reshape(-1, 16))
+    np.testing.assert_array_equal(tv.cpu().numpy(), ora["top_val"].reshape(-1, 16))
+    Bs = len(case["blocks"])
+    at = case["inp"]["anchor_tok"][case["blocks"]]
+    S0, S = bd.pair_score(torch.from_numpy(ora["top_val"]).to(DEV), torch.from_numpy(ora["top_idx"]).to(DEV),
+                          to_dev(at, "i32"), case["dev"]["U"], case["dev"]["Vf"])
+    S0, S = S0.cpu().numpy(), S.cpu().numpy()
+    if w.dyadic:
+        np.testing.assert_array_equal(S0, ora["S0"])
+        np.testing.assert_array_equal(S, ora["S"])
+    else:
+        assert np.abs(S0 - ora["S0"]).max() <= 1e-4
+        assert np.abs(S - ora["S"]).max() <= 1e-4
+    slot, tok, score = bd.path_select(torch.from_numpy(ora["S0"]).to(DEV), torch.from_numpy(ora["S"]).to(DEV),
+                                      torch.from_numpy(ora["top_idx"]).to(DEV))
+    np.testing.assert_array_equal(slot.cpu().numpy(), ora["path_slot"])
+    np.testing.assert_array_equal(tok.cpu().numpy(), ora["path_tok"])
+    np.testing.assert_array_equal(score.cpu().numpy(), ora["path_score"])
+    acc, nxt = bd.verify_greedy(tok, to_dev(case["tgt_sub"], "i32"))
+    wa, wn = O.verify_greedy(ora["path_tok"], case["tgt_sub"])
+    np.testing.assert_array_equal(acc.cpu().numpy(), wa)
+    np.testing.assert_array_equal(nxt.cpu().numpy(), wn)
+    assert Bs == len(wa)
+
+
+# ------------------------------------------------------------------ end to end
+def test_end_to_end_subset(case):
+    w, buf, ora, blocks = case["w"], case["buf"], case["ora"], case["blocks"]
+    B, L, V = w.B, w.L, w.V
+    rows = (blocks[:, None] * L + np.arange(L)[None, :]).reshape(-1)
+    z = buf.logits[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+    zo = ora["z"].astype(np.float64)
+    err = np.abs(z - zo)
+    assert np.all(err <= TOL_LOGIT * np.maximum(np.abs(zo), 1.0)), err.max()
+    zdrift = float(err.max())
+
+    ti = buf.top_idx.view(B, L, 16).cpu().numpy()[blocks]
+    tv = buf.top_val.view(B, L, 16).cpu().numpy()[blocks]
+    gaps = O.topk_gaps(ora["z"], ora["top_val"].reshape(-1, 16)).reshape(ti.shape)
+    decided = gaps > MARGIN
+    assert np.array_equal(ti[decided], ora["top_idx"][decided])
+    # undecided slots hold near-tied tokens
+    zo_b = zo.reshape(len(blocks), L, V)
+    got_vals = np.take_along_axis(zo_b, ti.astype(np.int64), axis=2)
+    assert np.all(np.abs(got_vals - ora["top_val"]) <= 2 * MARGIN + 2 * zdrift)
+
+    slot = buf.path_slot.cpu().numpy()[blocks]
+    tok = buf.path_tok.cpu().numpy()[blocks]
+    acc = buf.accept_len.cpu().numpy()[blocks]
+    margin = O.path_margin(ora["S0"], ora["S"])
+    same_cands = (ti == ora["top_idx"]).all(axis=(1, 2))
+    S_g = buf.S.cpu().numpy()[blocks]
+    S0_g = buf.S0.cpu().numpy()[blocks]
+    n_exact = 0
+    for k in range(len(blocks)):
+        if not same_cands[k]:
+            continue
+        drift = max(np.abs(S_g[k] - ora["S"][k]).max() if L > 1 else 0.0,
+                    np.abs(S0_g[k] - ora["S0"][k]).max())
+        if margin[k] > MARGIN + 2 * L * drift:
+            n_exact += 1
+            assert slot[k].tolist() == ora["path_slot"][k].tolist(), k
+            assert tok[k].tolist() == ora["path_tok"][k].tolist(), k
+            wa, _ = O.verify_greedy(ora["path_tok"][k:k + 1], case["tgt_sub"][k:k + 1])
+            assert acc[k] == wa[0]
+        else:
+            best = O.path_scores_f64(ora["S0"][k:k + 1], ora["S"][k:k + 1], ora["path_slot"][k:k + 1].astype(np.int64))
+            mine = O.path_scores_f64(ora["S0"][k:k + 1], ora["S"][k:k + 1], slot[k:k + 1].astype(np.int64))
+            assert mine[0] >= best[0] - MARGIN - 2 * L * drift
+    print(f"e2e: logits max |dz| {zdrift:.2e}; decided top-16 slots {decided.mean():.4f}; "
+          f"paths checked exactly {n_exact}/{len(blocks)}")
+
+
+def test_properties_all_blocks(case):
+    w, buf = case["w"], case["buf"]
+    B, L, V = w.B, w.L, w.V
+    tv = buf.top_val.view(B, L, 16).cpu().numpy()
+    ti = buf.top_idx.view(B, L, 16).cpu().numpy()
+    assert ((ti >= 0) & (ti < V)).all()
+    assert (np.diff(tv, axis=2) <= 0).all()
+    srt = np.sort(ti, axis=2)
+    assert (np.diff(srt, axis=2) > 0).all()                        # distinct
+    rows = torch.arange(B * L, device=DEV)[:, None]
+    vals = buf.logits[rows, buf.top_idx.long()].view(B, L, 16).cpu().numpy()
+    np.testing.assert_array_equal(vals, tv)                        # values are their logits
+    # nothing outside the list beats slot 15 (checked on a sample of rows)
+    g = np.random.default_rng(0)
+    for m in g.choice(B * L, size=min(64, B * L), replace=False):
+        row = buf.logits[int(m)].cpu().numpy()
+        b, t = divmod(int(m), L)
+        last = tv[b, t, 15]
+        mask = np.ones(V, bool)
+        mask[ti[b, t]] = False
+        above = (row[mask] > last) | ((row[mask] == last) & (np.arange(V)[mask] < ti[b, t, 15]))
+        assert not above.any(), m
+    slot = buf.path_slot.cpu().numpy()
+    tok = buf.path_tok.cpu().numpy()
+    np.testing.assert_array_equal(tok, np.take_along_axis(ti, slot[:, :, None].astype(np.int64), 2)[:, :, 0])
+    S0_g, S_g = buf.S0.cpu().numpy(), buf.S.cpu().numpy()
+    sc = O.path_scores_f64(S0_g, S_g, slot.astype(np.int64))
+    mag = O.path_scores_f64(np.abs(S0_g), np.abs(S_g), slot.astype(np.int64))
+    assert np.all(np.abs(sc - buf.path_score.cpu().numpy()) <= L * 2.0 ** -23 * mag)
+    acc = buf.accept_len.cpu().numpy()
+    wa, wn = O.verify_greedy(tok, case["tgt"])
+    np.testing.assert_array_equal(acc, wa)
+    np.testing.assert_array_equal(buf.next_tok.cpu().numpy(), wn)
+    assert ((acc >= 1) & (acc <= L + 1)).all()
+    print(f"mean acceptance {acc.mean():.3f} over {B} blocks")
+
+
+def test_step_is_deterministic(case):
+    w, buf, dev = case["w"], case["buf"], case["dev"]
+    if w.cid not in (0, 2):
+        pytest.skip("checked on the tiny and the benchmark workload")
+    snap = [t.clone() for t in (buf.logits, buf.top_val, buf.top_idx, buf.S0, buf.S, buf.path_slot,
+                                buf.path_score)]
+    bd.run_step(buf, dev["x"], dev["convs"], dev["W"], dev["U"], dev["Vf"], dev["anchor_tok"], None)
+    torch.cuda.synchronize()
+    for a, b in zip(snap, (buf.logits, buf.top_val, buf.top_idx, buf.S0, buf.S, buf.path_slot,
+                           buf.path_score)):
+        assert torch.equal(a, b)
