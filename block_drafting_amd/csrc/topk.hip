@@ -11,9 +11,9 @@
 // row (the four rows hold the same list) and streams its share of the row
 // with 16-byte loads.  An element is inspected only when its value is not
 // below the current 16th value (one compare per element in the common case);
-// survivors are inserted one at a time by a shift-insert across the row.
-// A row is split over several workgroups; their lists are merged by a second
-// one-wave-per-row kernel.
+// survivors are compacted into a small LDS buffer and merged into the list
+// by a 64-lane bitonic sort when the buffer fills.  A row may be split over
+// several workgroups; their lists are merged by a one-wave-per-row kernel.
 #include "common.hpp"
 
 namespace dflash2 {
@@ -59,23 +59,6 @@ struct WaveTop16 {
     thr = readlane64(key, 15);
     thr_f = thr ? val_of((uint32_t)(thr >> 32)) : -INFINITY;
   }
-  // Insert c (wave-uniform, c > thr).  Slot s takes max(l[s], min(l[s-1], c)),
-  // l[-1] = +inf; the shift by one slot is a DPP row_shr:1 (slot 0 keeps the
-  // all-ones sentinel).
-  __device__ void insert(uint64_t c) {
-    const uint32_t lo = __builtin_amdgcn_update_dpp(0xffffffffu, (uint32_t)key, 0x111, 0xf, 0xf, false);
-    const uint32_t hi =
-        __builtin_amdgcn_update_dpp(0xffffffffu, (uint32_t)(key >> 32), 0x111, 0xf, 0xf, false);
-    const uint64_t up = ((uint64_t)hi << 32) | lo;
-    const uint64_t m = up < c ? up : c;
-    key = key > m ? key : m;
-    refresh();
-  }
-  // Offer one (value, id) pair (wave-uniform).
-  __device__ void offer(float v, uint32_t idx) {
-    const uint64_t c = key_of(v, idx);
-    if (c > thr) insert(c);
-  }
 };
 
 __device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
@@ -84,25 +67,103 @@ __device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Value of lane (lane ^ J) for 32-bit data.  Partners within a 16-lane row
+// use DPP (quad_perm; xor 4 = quad reverse after row_half_mirror; xor 8 =
+// row_half_mirror after row_mirror), xor 16 uses ds_swizzle (bit-mask mode),
+// xor 32 a ds_bpermute.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  if constexpr (J == 1) {
+    return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4) {
+    const uint32_t h = __builtin_amdgcn_update_dpp(0u, v, 0x141, 0xf, 0xf, false);
+    return __builtin_amdgcn_update_dpp(0u, h, 0x1B, 0xf, 0xf, false);
+  } else if constexpr (J == 8) {
+    const uint32_t m = __builtin_amdgcn_update_dpp(0u, v, 0x140, 0xf, 0xf, false);
+    return __builtin_amdgcn_update_dpp(0u, m, 0x141, 0xf, 0xf, false);
+  } else if constexpr (J == 16) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+  } else {
+    return (uint32_t)__shfl_xor((int)v, 32, 64);
+  }
+}
+
+template <int J>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {
+  const uint32_t lo = xor_lane<J>((uint32_t)v);
+  const uint32_t hi = xor_lane<J>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int K, int J>
+__device__ __forceinline__ uint64_t bitonic_step(uint64_t v, int lane) {
+  const uint64_t o = xor_lane64<J>(v);
+  const bool keep_max = ((lane & J) == 0) == ((lane & K) == 0);
+  return keep_max ? (v > o ? v : o) : (v < o ? v : o);
+}
+
+template <int K, int J>
+__device__ __forceinline__ uint64_t bitonic_merge(uint64_t v, int lane) {
+  v = bitonic_step<K, J>(v, lane);
+  if constexpr (J > 1) v = bitonic_merge<K, J / 2>(v, lane);
+  return v;
+}
+
 // Bitonic sort of one key per lane across the wavefront, descending (lane 0
 // ends with the largest).
 __device__ uint64_t wave_sort_desc(uint64_t v) {
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t o = shfl64(v, lane ^ j);
-      const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
-      v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
-    }
-  }
+  v = bitonic_merge<2, 1>(v, lane);
+  v = bitonic_merge<4, 2>(v, lane);
+  v = bitonic_merge<8, 4>(v, lane);
+  v = bitonic_merge<16, 8>(v, lane);
+  v = bitonic_merge<32, 16>(v, lane);
+  v = bitonic_merge<64, 32>(v, lane);
   return v;
 }
 
 // A candidate may rank in the list unless it is strictly below the 16th value
-// (NaN always passes here and is decided exactly in offer()).
+// (NaN always passes here and is decided exactly by its key later).
 __device__ __forceinline__ bool may_enter(float v, float thr_f) { return !(v < thr_f); }
+
+// Per-wave candidate buffer in LDS (kBuf keys).  Survivors of the filter are
+// appended with a ballot/mbcnt compaction; when the buffer would overflow, the
+// list (16 keys) and the buffer (<= 48 keys) are merged by one 64-lane sort.
+constexpr int kBuf = 48;
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+__device__ void flush(WaveTop16& top, const uint64_t* buf, int& count) {
+  const int lane = threadIdx.x & 63;
+  uint64_t v = lane < 16 ? top.key : (lane - 16 < count ? buf[lane - 16] : 0ull);
+  v = wave_sort_desc(v);
+  top.key = shfl64(v, lane & 15);
+  top.refresh();
+  count = 0;
+}
+
+// Append the keys of lanes with `pass` set (wave-uniform control flow).
+__device__ void append(WaveTop16& top, uint64_t* buf, int& count, bool pass, uint64_t key) {
+  const uint64_t m = __ballot(pass);
+  if (!m) return;
+  const int n = __popcll(m);
+  if (count + n > kBuf && count) flush(top, buf, count);
+  const int lane = threadIdx.x & 63;
+  if (n > kBuf) {
+    // more survivors than the buffer holds (adversarial order): keep the
+    // batch's own best 16, which contain every survivor that can matter
+    const uint64_t v = wave_sort_desc(pass ? key : 0ull);
+    if (lane < 16) buf[lane] = v;
+    count = 16;
+    return;
+  }
+  if (pass) buf[count + lanes_below(m)] = key;
+  count += n;
+}
 
 // Stream [c0, c1) of one row; VEC = 4 uses 16-byte loads (row and c0 16-byte
 // aligned), VEC = 1 scalar loads.  The four waves of the block interleave in
@@ -110,15 +171,17 @@ __device__ __forceinline__ bool may_enter(float v, float thr_f) { return !(v < t
 //
 // Warm start: on its first vector each lane finds its own largest key; the
 // wave sorts those 64 keys and takes the top 16 as its initial list (they are
-// real elements, so the list is exact), then offers only the other values of
-// that vector.  This replaces ~64*VEC serial inserts per wave with one sort.
+// real elements, so the list is exact); the other values of that vector go
+// through the filter like every later one.
 template <int VEC>
-__device__ void scan_range(const float* __restrict__ row, int c0, int c1, WaveTop16& top) {
+__device__ void scan_range(const float* __restrict__ row, int c0, int c1, WaveTop16& top,
+                           uint64_t* buf) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   constexpr int kUnroll = 8;
   const int stride = kThreads * VEC;  // elements per block-wide step
   bool first = true;
+  int count = 0;
   for (int base = c0 + wave * 64 * VEC; base < c1; base += stride * kUnroll) {
     float v[kUnroll][VEC];
     bool ok[kUnroll];
@@ -136,7 +199,7 @@ __device__ void scan_range(const float* __restrict__ row, int c0, int c1, WaveTo
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int e0 = base + u * stride;
+      const int e0 = base + u * stride + lane * VEC;
       int skip = -1;  // the lane's own maximum, already in the list (warm start)
       if (first && u == 0) {
         first = false;
@@ -144,7 +207,7 @@ __device__ void scan_range(const float* __restrict__ row, int c0, int c1, WaveTo
         if (ok[0]) {
 #pragma unroll
           for (int k = 0; k < VEC; ++k) {
-            const uint64_t c = key_of(v[0][k], (uint32_t)(e0 + lane * VEC + k));
+            const uint64_t c = key_of(v[0][k], (uint32_t)(e0 + k));
             if (c > best) {
               best = c;
               skip = k;
@@ -154,36 +217,29 @@ __device__ void scan_range(const float* __restrict__ row, int c0, int c1, WaveTo
         top.key = shfl64(wave_sort_desc(best), lane & 15);
         top.refresh();
       }
-      bool pass = false;
+      bool any = false;
 #pragma unroll
-      for (int k = 0; k < VEC; ++k) pass |= (k != skip) && may_enter(v[u][k], top.thr_f);
-      pass &= ok[u];
-      uint64_t mask = __ballot(pass);
-      while (mask) {
-        const int src = __builtin_ctzll(mask);
-        mask &= mask - 1;
-        const int sk = __builtin_amdgcn_readlane(skip, src);
+      for (int k = 0; k < VEC; ++k) any |= ok[u] && (k != skip) && may_enter(v[u][k], top.thr_f);
+      if (!__ballot(any)) continue;
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-          const float vv = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v[u][k]), src));
-          if (k != sk) top.offer(vv, (uint32_t)(e0 + src * VEC + k));
-        }
+      for (int k = 0; k < VEC; ++k) {
+        const bool p = ok[u] && (k != skip) && may_enter(v[u][k], top.thr_f);
+        append(top, buf, count, p, key_of(v[u][k], (uint32_t)(e0 + k)));
       }
     }
   }
+  if (count) flush(top, buf, count);
 }
 
-// Merge the four waves' lists of a block into wave 0.
+// Merge the four waves' lists of a block into wave 0 with one 64-lane sort.
 __device__ void merge_block(WaveTop16& top, uint64_t* lds) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   if (lane < 16) lds[wave * 16 + lane] = top.key;
   __syncthreads();
   if (wave == 0) {
-    for (int i = 16; i < 64; ++i) {
-      const uint64_t c = lds[i];
-      if (c > top.thr) top.insert(c);
-    }
+    top.key = shfl64(wave_sort_desc(lds[lane]), lane & 15);
+    top.refresh();
   }
 }
 
@@ -202,6 +258,7 @@ __global__ __launch_bounds__(kThreads) void topk16_scan_kernel(const float* __re
                                                                int32_t* __restrict__ top_idx,
                                                                uint64_t* __restrict__ part) {
   __shared__ uint64_t lds[64];
+  __shared__ uint64_t cand[kThreads / 64][kBuf];
   const int m = blockIdx.x / splits;
   const int sp = blockIdx.x - m * splits;
   const float* row = logits + (size_t)m * V;
@@ -209,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void topk16_scan_kernel(const float* __re
   const int c1 = min(V, c0 + chunk);
   WaveTop16 top;
   top.init();
-  if (c0 < c1) scan_range<VEC>(row, c0, c1, top);
+  if (c0 < c1) scan_range<VEC>(row, c0, c1, top, cand[threadIdx.x >> 6]);
   merge_block(top, lds);
   if ((threadIdx.x >> 6) != 0) return;
   if (splits == 1) {
@@ -229,17 +286,13 @@ __global__ __launch_bounds__(64) void topk16_merge_kernel(const uint64_t* __rest
   const int n = splits * kTopK;
   WaveTop16 top;
   top.init();
-  for (int base = 0; base < n; base += 64) {
-    const int e = base + lane;
-    const uint64_t c = e < n ? p[e] : 0ull;
-    uint64_t mask = __ballot(c > top.thr);
-    while (mask) {
-      const int src = __builtin_ctzll(mask);
-      mask &= mask - 1;
-      const uint64_t cc = readlane64(c, src);
-      if (cc > top.thr) top.insert(cc);
-    }
+  // list (lanes 0..15) + the next 48 partial keys (lanes 16..63), one sort each
+  for (int base = 0; base < n; base += 48) {
+    const int e = base + lane - 16;
+    const uint64_t c = lane < 16 ? top.key : (e < n ? p[e] : 0ull);
+    top.key = shfl64(wave_sort_desc(c), lane & 15);
   }
+  top.refresh();
   write_final(top, top_val + (size_t)m * kTopK, top_idx + (size_t)m * kTopK);
 }
 
