@@ -65,7 +65,7 @@ def measured_traffic(workload: str):
         return None
     kv = {}
     for line in open(TRAFFIC_FILE):
-        m = re.match(r"^\s*([a-z_]+)\s*[:=]\s*(\S+)", line)
+        m = re.match(r"^\s*([a-z0-9_]+)\s*[:=]\s*(\S+)", line)
         if m:
             kv[m.group(1)] = m.group(2)
     if kv.get("kernel_source_sha256_16") != kernel_source_hash() or kv.get("workload") != workload:
