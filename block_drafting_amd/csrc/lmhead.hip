@@ -3,13 +3,13 @@
 // own logit, computed once per position).  The only dense contraction of the
 // step: M = blocks x positions rows, N = vocabulary, K = hidden.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 tiles.  A workgroup owns a 256 x 256
-// output tile and walks K in slices; each of its four waves accumulates a
-// 128 x 128 sub-tile in the 256 accumulation registers.  Both operands are
-// K-contiguous.  When K is a multiple of 32 the slices go straight from
-// HBM/L2 into a 4-stage LDS ring with direct-to-LDS buffer loads
-// (lmhead_bf16_dma_kernel); otherwise 16-byte runs are staged through
-// registers into padded LDS rows (lmhead_bf16_kernel).
+// bf16 path: v_mfma_f32_32x32x16_bf16 tiles.  A workgroup of eight waves
+// (two per SIMD, so one wave's MFMAs cover the other's memory waits) owns a
+// 256 x 256 output tile; each wave accumulates a 128 x 64 sub-tile.  K is
+// walked in 64-wide slices through two padded LDS stages; both operands are
+// K-contiguous, so every thread moves 16-byte runs of 8 bf16 with buffer
+// loads into one of two register staging sets (two slices ahead of use)
+// and writes them to LDS between MFMAs.
 // Tiles are numbered so that the M-tiles sharing one W slice run back to back
 // on the same XCD (workgroup i is dispatched to XCD i mod 8), so W is pulled
 // from HBM about once and re-read from that XCD's L2.
@@ -222,170 +222,6 @@ __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
   }
 }
 
-// Direct-to-LDS variant (K a multiple of 32): the operand slices never pass
-// through VGPRs.  Each wave issues buffer_load_dwordx4 ... lds instructions
-// that write 1 KB (16 tile rows x 64 bytes) into a 4-stage LDS ring, three
-// slices ahead of the MFMAs.  Rows are 64 bytes (BK = 32) with the four
-// 16-byte chunks of row r stored at positions chunk ^ swz(r); swz(r) =
-// ((r >> 1) ^ (r >> 2)) & 3 makes every 8 (and every 16) consecutive lanes of
-// a fragment read hit distinct banks.  One barrier per slice, in the middle
-// of it: before the barrier each wave waits for its own loads of the next
-// slice (vmcnt) and for its own reads of the current stage (lgkmcnt); after
-// it, the stage just consumed is refilled with the slice four ahead.
-__device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-
-// s_waitcnt immediate for gfx9: wait until at most `vm` vector-memory
-// operations (and, if lgkm0, no LDS operations) are outstanding.
-__host__ __device__ constexpr int waitcnt_imm(int vm, bool lgkm0) {
-  return (vm & 0xf) | ((vm >> 4) << 14) | (0x7 << 4) | ((lgkm0 ? 0 : 0xf) << 8);
-}
-
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_dma_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bw, float* __restrict__ C,
-    int M, int N, int K, int mtiles, int ntiles) {
-  constexpr int BK = 32;
-  constexpr int kWaves = WM * WN;
-  constexpr int kStages = 4;
-  constexpr int kRow = BK * 2;                       // bytes per LDS row
-  constexpr int kStageBytes = (BM + BN) * kRow;
-  constexpr int kGA = BM / 16 / kWaves;               // 1 KB DMA groups per wave, A part
-  constexpr int kGB = BN / 16 / kWaves;               // ... B part
-  constexpr int kDma = kGA + kGB;                     // DMA instructions per wave per slice
-  constexpr int kTm = BM / WM / 32;
-  constexpr int kTn = BN / WN / 32;
-  static_assert(BM % (16 * kWaves) == 0 && BN % (16 * kWaves) == 0, "DMA split");
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes];
-
-  const int tile = xcd_tile(blockIdx.x, mtiles * ntiles);
-  const int mt = tile % mtiles;
-  const int nt = tile / mtiles;
-  const int m0 = mt * BM;
-  const int n0 = nt * BN;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave % WM;
-  const int wn = wave / WM;
-  const int nk = K / BK;
-
-  const int rowsA = min(BM, M - m0);
-  const int rowsB = min(BN, N - n0);
-  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(A + (size_t)m0 * K), (short)0, rowsA * K * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Bw + (size_t)n0 * K), (short)0, rowsB * K * 2, 0x00020000);
-
-  // DMA lane mapping: lane l fills row l/4 of a 16-row group at chunk
-  // position l%4, i.e. it loads global chunk (l%4) ^ swz(l/4) of that row.
-  const int dr = lane >> 2;
-  const int dvoff = (dr * K + ((lane & 3) ^ lds_swz(dr)) * 8) * 2;
-  auto dma = [&](int slice, int stage) {
-    const int kb = min(slice, nk - 1) * BK * 2;  // past the end: reload the last slice
-    char* st = lds + stage * kStageBytes;
-#pragma unroll
-    for (int i = 0; i < kGA; ++i) {
-      const int g = wave * kGA + i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsA, (__attribute__((address_space(3))) void*)(st + g * 1024), 16,
-          dvoff + g * 16 * K * 2 + kb, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < kGB; ++i) {
-      const int g = wave * kGB + i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsB, (__attribute__((address_space(3))) void*)(st + BM * kRow + g * 1024), 16,
-          dvoff + g * 16 * K * 2 + kb, 0, 0, 0);
-    }
-  };
-
-  f32x16_t acc[kTm][kTn];
-#pragma unroll
-  for (int i = 0; i < kTm; ++i)
-#pragma unroll
-    for (int j = 0; j < kTn; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // Fragment reads: lane l takes row l%32 of a 32-row block and global
-  // chunk 2*kk + l/32 of the slice, stored at position chunk ^ swz(row).
-  const int sw = lds_swz(lane & 15);
-  const int hi = lane >> 5;
-  const int q0 = ((0 + hi) ^ sw) * 16;
-  const int q1 = ((2 + hi) ^ sw) * 16;
-  const int rowA = (wm * (BM / WM) + (lane & 31)) * kRow;
-  const int rowB = BM * kRow + (wn * (BN / WN) + (lane & 31)) * kRow;
-  // Two fragment sets, each holding both k-steps of one slice: the set of
-  // slice kt+1 is read right after the barrier of slice kt, so the MFMAs of
-  // the first half of slice kt+1 never wait on LDS.
-  bf16x8_t F[2][2][kTm + kTn];
-  auto fread = [&](int stage, int set) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const char* st = lds + stage * kStageBytes + (kk ? q1 : q0);
-#pragma unroll
-      for (int i = 0; i < kTm; ++i)
-        F[set][kk][i] = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + rowA + i * 32 * kRow));
-#pragma unroll
-      for (int j = 0; j < kTn; ++j)
-        F[set][kk][kTm + j] = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + rowB + j * 32 * kRow));
-    }
-  };
-  auto mfma = [&](int set, int kk) {
-#pragma unroll
-    for (int i = 0; i < kTm; ++i)
-#pragma unroll
-      for (int j = 0; j < kTn; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[set][kk][i], F[set][kk][kTm + j],
-                                                            acc[i][j], 0, 0, 0);
-  };
-  // One slice: first k-step | wait + barrier | refill the consumed stage with
-  // the slice four ahead, read the next slice's fragments | second k-step.
-  auto slice = [&](int kt, int set) {
-    const int s = kt & (kStages - 1);
-    mfma(set, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    // this wave's reads of stage s and loads of slice kt+1 are complete
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm((kStages - 2) * kDma, true));
-    __builtin_amdgcn_s_barrier();
-    dma(kt + kStages, s);
-    fread((kt + 1) & (kStages - 1), set ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma(set, 1);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-#pragma unroll
-  for (int s = 0; s < kStages; ++s) dma(s, s);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm((kStages - 1) * kDma, false));
-  __builtin_amdgcn_s_barrier();
-  fread(0, 0);
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    slice(kt, 0);
-    slice(kt + 1, 1);
-  }
-  if (kt < nk) slice(kt, 0);
-  // no LDS write may land after the workgroup's LDS is released
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, true));
-
-#pragma unroll
-  for (int i = 0; i < kTm; ++i) {
-#pragma unroll
-    for (int j = 0; j < kTn; ++j) {
-      const int col = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
-      if (col >= N) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < M) __builtin_nontemporal_store(acc[i][j][r], C + (size_t)row * N + col);
-      }
-    }
-  }
-}
-
 // fp32 operands: thread per vocabulary row, 8 output rows per block row.
 __global__ __launch_bounds__(256) void lmhead_f32_kernel(const float* __restrict__ A,
                                                          const float* __restrict__ W,
@@ -428,16 +264,6 @@ hipError_t launch_bf16(const uint16_t* h, const uint16_t* W, float* z, int M, in
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN>
-hipError_t launch_bf16_dma(const uint16_t* h, const uint16_t* W, float* z, int M, int H, int V,
-                           hipStream_t s) {
-  const int mt = (M + BM - 1) / BM;
-  const int nt = (V + BN - 1) / BN;
-  hipLaunchKernelGGL((lmhead_bf16_dma_kernel<BM, BN, WM, WN>), dim3((unsigned)(mt * nt)),
-                     dim3(WM * WN * 64), 0, s, h, W, z, M, V, H, mt, nt);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_lmhead(const void* h, const void* W, float* logits, int M, int H, int V,
@@ -446,8 +272,7 @@ hipError_t launch_lmhead(const void* h, const void* W, float* logits, int M, int
   if (dtype == 1) {
     const uint16_t* hb = static_cast<const uint16_t*>(h);
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
-    if (H % 32 == 0) return launch_bf16_dma<256, 256, 2, 2>(hb, Wb, logits, M, H, V, s);
-    return launch_bf16<256, 256, 64, 2, 2>(hb, Wb, logits, M, H, V, s);
+    return launch_bf16<256, 256, 64, 2, 4>(hb, Wb, logits, M, H, V, s);
   }
   const dim3 grid((unsigned)((V + 255) / 256), (unsigned)((M + 7) / 8));
   hipLaunchKernelGGL(lmhead_f32_kernel, grid, dim3(256), 0, s, static_cast<const float*>(h),
