@@ -2,8 +2,9 @@
 """Benchmark of the DFlash 2 draft-select-verify step on one MI355X.
 
 One step = one pass of the whole hot path over one batch:
-  two-tap conv(s) -> LM-head logits -> top-16 -> pair scores -> path walk ->
-  greedy verification,
+  two-tap conv(s) -> LM-head logits -> top-16 -> [context gate] -> pair
+  scores -> path walk (max-plus, or greedy with --walk greedy / the gated
+  workload) -> greedy verification,
 each stage a call into libdflash2 on the current HIP stream.  Inputs are
 seeded synthetic tensors already resident in HBM when timing starts.
 
@@ -39,7 +40,9 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4, 5])
+    ap.add_argument("--walk", choices=["viterbi", "greedy"], default=None,
+                    help="path walk (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=64,
                     help="blocks the CPU oracle runs for the baseline")
@@ -128,6 +131,8 @@ def main(argv=None):
     import workloads as WL
 
     w = WL.WORKLOADS[a.workload]
+    if a.walk is not None:
+        w = w.shrink(walk=a.walk)
     bf16 = w.dtype == "bf16"
     tdt = torch.bfloat16 if bf16 else torch.float32
     log(f"[bench] workload {w.cid} {w.name}: B={w.B} L={w.L} H={w.H} V={w.V} r={w.r} "
@@ -152,19 +157,21 @@ def main(argv=None):
     U = dev(inp["U"], "act")
     Vf = dev(inp["Vf"], "act")
     anchor = dev(inp["anchor_tok"], "i32")
+    Wg = dev(inp["Wg"], "act") if w.gate else None
     B, L, H, V = w.B, w.L, w.H, w.V
     M = B * L
-    buf = bd.StepBuffers(B, L, H, V, tdt, "cuda", n_convs=w.n_convs, keep_logits=True)
+    buf = bd.StepBuffers(B, L, H, V, tdt, "cuda", n_convs=w.n_convs, keep_logits=True,
+                         gate_rank=w.r if w.gate else 0)
     topk_ws = torch.empty(max(bd.topk16_workspace(M, V), 1), dtype=torch.uint8, device="cuda")
 
     # one untimed step gives the candidates the verification targets are planted on
-    bd.run_step(buf, x, convs, W, U, Vf, anchor, None)
+    bd.run_step(buf, x, convs, W, U, Vf, anchor, None, Wg=Wg, walk=w.walk)
     torch.cuda.synchronize()
     tgt_np = WL.make_targets(w, buf.top_idx.view(B, L, 16).cpu().numpy(), buf.path_tok.cpu().numpy())
     target = torch.from_numpy(tgt_np).cuda()
 
-    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
-          for k in ("conv", "gemm", "topk", "pair", "select", "verify")}
+    order = ["conv", "gemm", "topk"] + (["gate"] if w.gate else []) + ["pair", "select", "verify"]
+    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)] for k in order}
     ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
 
     def step(i=None):
@@ -181,12 +188,19 @@ def main(argv=None):
         if i is not None:
             ev["topk"][i].record()
         bd.topk16(buf.logits, buf.top_val, buf.top_idx, topk_ws)
+        gate = None
+        if w.gate:
+            if i is not None:
+                ev["gate"][i].record()
+            gate = bd.context_gate(cur.view(M, H), Wg, buf.gate)
         if i is not None:
             ev["pair"][i].record()
-        bd.pair_score(buf.top_val.view(B, L, 16), buf.top_idx.view(B, L, 16), anchor, U, Vf, buf.S0, buf.S)
+        bd.pair_score(buf.top_val.view(B, L, 16), buf.top_idx.view(B, L, 16), anchor, U, Vf, buf.S0, buf.S,
+                      gate=gate)
         if i is not None:
             ev["select"][i].record()
-        bd.path_select(buf.S0, buf.S, buf.top_idx.view(B, L, 16), buf.path_slot, buf.path_tok, buf.path_score)
+        bd.path_select(buf.S0, buf.S, buf.top_idx.view(B, L, 16), buf.path_slot, buf.path_tok, buf.path_score,
+                       mode=w.walk)
         if i is not None:
             ev["verify"][i].record()
         bd.verify_greedy(buf.path_tok, target, buf.accept_len, buf.next_tok)
@@ -209,7 +223,6 @@ def main(argv=None):
     tv = buf.top_val.cpu().numpy()
     assert ((acc >= 1) & (acc <= L + 1)).all() and (np.diff(tv, axis=1) <= 0).all()
 
-    order = ["conv", "gemm", "topk", "pair", "select", "verify"]
     stage_ms = {k: 0.0 for k in order}
     for i in range(a.steps):
         marks = [ev[k][i] for k in order] + [ev_end[i]]
@@ -245,7 +258,7 @@ def main(argv=None):
         "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "L": L, "H": H, "V": V, "r": w.r,
-                   "convs": w.n_convs, "topk": 16},
+                   "convs": w.n_convs, "topk": 16, "gate": w.gate, "walk": w.walk},
         "tokens_per_s": round(M / (ms_step * 1e-3), 1),
         "accepted_tokens_per_s": round(float(acc.sum()) / (ms_step * 1e-3), 1),
         "mean_accept_len": round(float(acc.mean()), 3),

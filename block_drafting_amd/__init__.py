@@ -11,8 +11,10 @@ The five stages (names as in the C ABI):
   twotap_conv     two-tap local conv around the drafter's sublayers
   logits_topk     LM-head logits and per-position top-16 candidates
                   (= lmhead_logits then topk16)
-  pair_score      16x16 scores of neighbouring candidates
-  path_select     max-plus walk to one path per block
+  pair_score      16x16 scores of neighbouring candidates (optionally
+                  weighted by a context gate from context_gate)
+  path_select     max-plus walk (or the greedy best-successor walk) to one
+                  path per block
   verify_greedy   greedy verification, acceptance length
 """
 from __future__ import annotations
@@ -25,11 +27,12 @@ import torch
 
 __all__ = [
     "DFlash2Error", "lib", "library_path", "twotap_conv", "lmhead_logits", "topk16",
-    "topk16_workspace", "logits_topk", "logits_topk_workspace", "pair_score", "path_select",
-    "verify_greedy", "StepBuffers", "run_step", "TOPK",
+    "topk16_workspace", "logits_topk", "logits_topk_workspace", "context_gate", "pair_score",
+    "path_select", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
 ]
 
 TOPK = 16
+PATH_MODES = {"viterbi": 0, "greedy": 1}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libdflash2.so")
 _lib = None
@@ -48,7 +51,10 @@ _SIGS = {
     "dflash2_logits_topk_workspace": ([_I, _I, _I, _I, _I, _I], _Z),
     "dflash2_logits_topk": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
     "dflash2_pair_score": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
+    "dflash2_context_gate": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "dflash2_pair_score_gated": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "dflash2_path_select": ([_P, _P, _P, _I, _I, _P, _P, _P, _P], _I),
+    "dflash2_path_select_mode": ([_P, _P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
     "dflash2_verify_greedy": ([_P, _P, _I, _I, _P, _P, _P], _I),
 }
 
@@ -223,16 +229,35 @@ def logits_topk(h: torch.Tensor, W: torch.Tensor, logits: Optional[torch.Tensor]
     return top_val, top_idx
 
 
+def context_gate(h: torch.Tensor, Wg: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """Context gate sigmoid(h . Wg^T): h [M, H], Wg [r, H] -> fp32 [M, r]."""
+    M, H = h.shape
+    r = Wg.shape[0]
+    _shape(Wg, (r, H), "Wg", h.dtype)
+    if out is None:
+        out = torch.empty((M, r), dtype=torch.float32, device=h.device)
+    _shape(out, (M, r), "gate", torch.float32)
+    dev = _dev(h, Wg, out)
+    _check("dflash2_context_gate", lib().dflash2_context_gate(
+        _ptr(h), _ptr(Wg), _ptr(out), M, H, r, _dt(h), _stream(dev)))
+    return out
+
+
 def pair_score(top_val: torch.Tensor, top_idx: torch.Tensor, anchor_tok: Optional[torch.Tensor],
                U: torch.Tensor, Vf: torch.Tensor, S0: Optional[torch.Tensor] = None,
-               S: Optional[torch.Tensor] = None):
-    """S0 [B, 16], S [B, L-1, 16, 16] from candidates [B, L, 16] and factors [V, r]."""
+               S: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None):
+    """S0 [B, 16], S [B, L-1, 16, 16] from candidates [B, L, 16] and factors
+    [V, r]; with `gate` ([B, L, r] or [B*L, r] fp32) the gated scores."""
     B, L, K = top_val.shape
     V, r = U.shape
     _shape(top_idx, (B, L, K), "top_idx", torch.int32)
     _shape(Vf, (V, r), "Vf", U.dtype)
     if anchor_tok is not None:
         _shape(anchor_tok, (B,), "anchor_tok", torch.int32)
+    if gate is not None:
+        if gate.dim() == 2:
+            gate = gate.view(B, L, r) if gate.shape[0] == B * L else gate
+        _shape(gate, (B, L, r), "gate", torch.float32)
     dev = top_val.device
     if S0 is None:
         S0 = torch.empty((B, TOPK), dtype=torch.float32, device=dev)
@@ -240,16 +265,24 @@ def pair_score(top_val: torch.Tensor, top_idx: torch.Tensor, anchor_tok: Optiona
         S = torch.empty((B, max(L - 1, 0), TOPK, TOPK), dtype=torch.float32, device=dev)
     _shape(S0, (B, TOPK), "S0", torch.float32)
     _shape(S, (B, L - 1, TOPK, TOPK), "S", torch.float32)
-    _dev(top_val, top_idx, anchor_tok, U, Vf, S0, S)
-    _check("dflash2_pair_score", lib().dflash2_pair_score(
-        _ptr(top_val), _ptr(top_idx), _ptr(anchor_tok), _ptr(U), _ptr(Vf), B, L, V, r, _dt(U),
-        _ptr(S0), _ptr(S) if L > 1 else None, _stream(dev)))
+    _dev(top_val, top_idx, anchor_tok, U, Vf, S0, S, gate)
+    if gate is None:
+        _check("dflash2_pair_score", lib().dflash2_pair_score(
+            _ptr(top_val), _ptr(top_idx), _ptr(anchor_tok), _ptr(U), _ptr(Vf), B, L, V, r,
+            _dt(U), _ptr(S0), _ptr(S) if L > 1 else None, _stream(dev)))
+    else:
+        _check("dflash2_pair_score_gated", lib().dflash2_pair_score_gated(
+            _ptr(top_val), _ptr(top_idx), _ptr(anchor_tok), _ptr(U), _ptr(Vf), _ptr(gate), B, L,
+            V, r, _dt(U), _ptr(S0), _ptr(S) if L > 1 else None, _stream(dev)))
     return S0, S
 
 
 def path_select(S0: torch.Tensor, S: Optional[torch.Tensor], top_idx: Optional[torch.Tensor],
-                path_slot=None, path_tok=None, path_score=None):
-    """Max-plus best path per block.  Returns (path_slot, path_tok, path_score)."""
+                path_slot=None, path_tok=None, path_score=None, mode: str = "viterbi"):
+    """Best path per block: max-plus ("viterbi") or best-successor ("greedy").
+    Returns (path_slot, path_tok, path_score)."""
+    if mode not in PATH_MODES:
+        raise ValueError(f"mode must be one of {sorted(PATH_MODES)}, got {mode!r}")
     B = S0.shape[0]
     if top_idx is not None:
         L = top_idx.shape[1]
@@ -263,9 +296,9 @@ def path_select(S0: torch.Tensor, S: Optional[torch.Tensor], top_idx: Optional[t
     if path_score is None:
         path_score = torch.empty((B,), dtype=torch.float32, device=dev)
     _dev(S0, S, top_idx, path_slot, path_tok, path_score)
-    _check("dflash2_path_select", lib().dflash2_path_select(
-        _ptr(S0), _ptr(S) if L > 1 else None, _ptr(top_idx), B, L, _ptr(path_slot),
-        _ptr(path_tok), _ptr(path_score), _stream(dev)))
+    _check("dflash2_path_select_mode", lib().dflash2_path_select_mode(
+        _ptr(S0), _ptr(S) if L > 1 else None, _ptr(top_idx), B, L, PATH_MODES[mode],
+        _ptr(path_slot), _ptr(path_tok), _ptr(path_score), _stream(dev)))
     return path_slot, path_tok, path_score
 
 
@@ -291,7 +324,7 @@ class StepBuffers:
     their own tensor (else they live in the workspace)."""
 
     def __init__(self, B: int, L: int, H: int, V: int, dtype: torch.dtype, device,
-                 n_convs: int = 1, keep_logits: bool = True):
+                 n_convs: int = 1, keep_logits: bool = True, gate_rank: int = 0):
         M = B * L
         kw = dict(device=device)
         self.B, self.L, self.H, self.V = B, L, H, V
@@ -308,15 +341,20 @@ class StepBuffers:
         self.path_score = torch.empty((B,), dtype=torch.float32, **kw)
         self.accept_len = torch.empty((B,), dtype=torch.int32, **kw)
         self.next_tok = torch.empty((B,), dtype=torch.int32, **kw)
+        self.gate = (torch.empty((M, gate_rank), dtype=torch.float32, **kw)
+                     if gate_rank else None)
 
 
 def run_step(buf: StepBuffers, x: torch.Tensor, convs, W: torch.Tensor, U: torch.Tensor,
              Vf: torch.Tensor, anchor_tok: Optional[torch.Tensor],
-             target: Optional[torch.Tensor]) -> StepBuffers:
+             target: Optional[torch.Tensor], Wg: Optional[torch.Tensor] = None,
+             walk: str = "viterbi") -> StepBuffers:
     """One draft-select-verify step: the conv chain (each entry of `convs` is a
-    dict with k0, k1, anchor_h, proj, groups), logits + top-16, pair scores,
-    path walk and, when `target` is given, greedy verification.  Every call
-    is enqueued on the current stream; nothing is synchronised."""
+    dict with k0, k1, anchor_h, proj, groups), logits + top-16, pair scores
+    (context-gated from the final hidden states when `Wg` is given), the path
+    walk (`walk`: "viterbi" or "greedy") and, when `target` is given, greedy
+    verification.  Every call is enqueued on the current stream; nothing is
+    synchronised."""
     B, L, H, V = buf.B, buf.L, buf.H, buf.V
     cur = x
     for j, c in enumerate(convs):
@@ -328,8 +366,13 @@ def run_step(buf: StepBuffers, x: torch.Tensor, convs, W: torch.Tensor, U: torch
     logits_topk(cur.view(M, H), W, buf.logits, buf.top_val, buf.top_idx, buf.workspace)
     tv = buf.top_val.view(B, L, TOPK)
     ti = buf.top_idx.view(B, L, TOPK)
-    pair_score(tv, ti, anchor_tok, U, Vf, buf.S0, buf.S)
-    path_select(buf.S0, buf.S, ti, buf.path_slot, buf.path_tok, buf.path_score)
+    gate = None
+    if Wg is not None:
+        if buf.gate is None:
+            raise ValueError("StepBuffers were made without gate_rank")
+        gate = context_gate(cur.view(M, H), Wg, buf.gate)
+    pair_score(tv, ti, anchor_tok, U, Vf, buf.S0, buf.S, gate=gate)
+    path_select(buf.S0, buf.S, ti, buf.path_slot, buf.path_tok, buf.path_score, mode=walk)
     if target is not None:
         verify_greedy(buf.path_tok, target, buf.accept_len, buf.next_tok)
     return buf

@@ -161,10 +161,9 @@ DFLASH2_API int dflash2_logits_topk(const void* h, const void* W, float* logits,
   return status_of(launch_topk16(z, top_val, top_idx, M, V, workspace, s));
 }
 
-DFLASH2_API int dflash2_pair_score(const float* top_val, const int32_t* top_idx,
-                                   const int32_t* anchor_tok, const void* U, const void* Vf,
-                                   int B, int L, int V, int r, int dtype, float* S0, float* S,
-                                   void* stream) {
+static int pair_score(const float* top_val, const int32_t* top_idx, const int32_t* anchor_tok,
+                      const void* U, const void* Vf, const float* gate, int B, int L, int V, int r,
+                      int dtype, float* S0, float* S, void* stream) {
   if (!valid_dtype(dtype) || B < 0 || L < 1 || L > DFLASH2_MAX_L || V < kTopK || r < 1 ||
       r > DFLASH2_MAX_RANK)
     return DFLASH2_EINVAL;
@@ -173,7 +172,7 @@ DFLASH2_API int dflash2_pair_score(const float* top_val, const int32_t* top_idx,
   if ((long long)V * r > (1LL << 40) || (long long)B * L * kTopK > kInt32Max)
     return DFLASH2_EINVAL;
   if (!aligned4(top_val) || !aligned4(top_idx) || !aligned4(S0) || (S && !aligned16(S)) ||
-      (anchor_tok && !aligned4(anchor_tok)))
+      (anchor_tok && !aligned4(anchor_tok)) || (gate && !aligned4(gate)))
     return DFLASH2_EINVAL;
   const size_t es = esize(dtype);
   if (dtype == DFLASH2_BF16 ? ((reinterpret_cast<uintptr_t>(U) | reinterpret_cast<uintptr_t>(Vf)) & 1)
@@ -182,23 +181,57 @@ DFLASH2_API int dflash2_pair_score(const float* top_val, const int32_t* top_idx,
   const size_t s0b = (size_t)B * kTopK * 4;
   const size_t sb = L > 1 ? (size_t)B * (L - 1) * kTopK * kTopK * 4 : 0;
   const size_t tb = (size_t)B * L * kTopK * 4;
-  const void* ins[] = {top_val, top_idx, U, Vf, anchor_tok};
-  const size_t insz[] = {tb, tb, (size_t)V * r * es, (size_t)V * r * es, (size_t)B * 4};
-  for (int i = 0; i < 5; ++i) {
+  const void* ins[] = {top_val, top_idx, U, Vf, anchor_tok, gate};
+  const size_t insz[] = {tb, tb, (size_t)V * r * es, (size_t)V * r * es, (size_t)B * 4,
+                         (size_t)B * L * r * 4};
+  for (int i = 0; i < 6; ++i) {
     if (overlap(S0, s0b, ins[i], insz[i]) || (sb && overlap(S, sb, ins[i], insz[i])))
       return DFLASH2_EINVAL;
   }
   if (sb && overlap(S0, s0b, S, sb)) return DFLASH2_EINVAL;
-  return status_of(launch_pair_score(top_val, top_idx, anchor_tok, U, Vf, B, L, V, r, dtype, S0,
-                                     L > 1 ? S : nullptr, as_stream(stream)));
+  return status_of(launch_pair_score(top_val, top_idx, anchor_tok, U, Vf, gate, B, L, V, r, dtype,
+                                     S0, L > 1 ? S : nullptr, as_stream(stream)));
 }
 
-DFLASH2_API int dflash2_path_select(const float* S0, const float* S, const int32_t* top_idx,
-                                    int B, int L, int32_t* path_slot, int32_t* path_tok,
-                                    float* path_score, void* stream) {
+DFLASH2_API int dflash2_pair_score(const float* top_val, const int32_t* top_idx,
+                                   const int32_t* anchor_tok, const void* U, const void* Vf,
+                                   int B, int L, int V, int r, int dtype, float* S0, float* S,
+                                   void* stream) {
+  return pair_score(top_val, top_idx, anchor_tok, U, Vf, nullptr, B, L, V, r, dtype, S0, S,
+                    stream);
+}
+
+DFLASH2_API int dflash2_pair_score_gated(const float* top_val, const int32_t* top_idx,
+                                         const int32_t* anchor_tok, const void* U, const void* Vf,
+                                         const float* gate, int B, int L, int V, int r, int dtype,
+                                         float* S0, float* S, void* stream) {
+  if (!gate && B > 0) return DFLASH2_EINVAL;
+  return pair_score(top_val, top_idx, anchor_tok, U, Vf, gate, B, L, V, r, dtype, S0, S, stream);
+}
+
+DFLASH2_API int dflash2_context_gate(const void* h, const void* Wg, float* gate, int M, int H,
+                                     int r, int dtype, void* stream) {
+  if (!valid_dtype(dtype) || M < 0 || H < 8 || H % 8 != 0 || r < 1 || r > DFLASH2_MAX_RANK)
+    return DFLASH2_EINVAL;
+  if (M == 0) return DFLASH2_OK;
+  if (!h || !Wg || !gate) return DFLASH2_EINVAL;
+  if (!aligned16(h) || !aligned16(Wg) || !aligned4(gate)) return DFLASH2_EINVAL;
+  if (H > (1 << 21) || (long long)M * r > kInt32Max) return DFLASH2_EUNSUPPORTED;
+  const size_t es = esize(dtype);
+  const size_t gb = (size_t)M * r * 4;
+  if (overlap(gate, gb, h, (size_t)M * H * es) || overlap(gate, gb, Wg, (size_t)r * H * es))
+    return DFLASH2_EINVAL;
+  return status_of(launch_context_gate(h, Wg, gate, M, H, r, dtype, as_stream(stream)));
+}
+
+static int path_select(const float* S0, const float* S, const int32_t* top_idx, int B, int L,
+                       int mode, int32_t* path_slot, int32_t* path_tok, float* path_score,
+                       void* stream) {
   if (B < 0 || L < 1 || L > DFLASH2_MAX_L) return DFLASH2_EINVAL;
+  if (mode != DFLASH2_PATH_VITERBI && mode != DFLASH2_PATH_GREEDY) return DFLASH2_EINVAL;
   if (B == 0) return DFLASH2_OK;
   if (!S0 || (L > 1 && !S) || !path_slot || !path_score) return DFLASH2_EINVAL;
+  if (mode == DFLASH2_PATH_GREEDY && L > 1 && !aligned16(S)) return DFLASH2_EINVAL;
   if ((top_idx == nullptr) != (path_tok == nullptr)) return DFLASH2_EINVAL;
   if (!aligned4(S0) || (S && !aligned4(S)) || !aligned4(path_slot) || !aligned4(path_score) ||
       (top_idx && !aligned4(top_idx)) || (path_tok && !aligned4(path_tok)))
@@ -216,8 +249,22 @@ DFLASH2_API int dflash2_path_select(const float* S0, const float* S, const int32
     for (int j = i + 1; j < 3; ++j)
       if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return DFLASH2_EINVAL;
   }
-  return status_of(launch_path_select(S0, L > 1 ? S : nullptr, top_idx, B, L, path_slot, path_tok,
+  return status_of(launch_path_select(S0, L > 1 ? S : nullptr, top_idx, B, L,
+                                      mode == DFLASH2_PATH_GREEDY, path_slot, path_tok,
                                       path_score, as_stream(stream)));
+}
+
+DFLASH2_API int dflash2_path_select(const float* S0, const float* S, const int32_t* top_idx,
+                                    int B, int L, int32_t* path_slot, int32_t* path_tok,
+                                    float* path_score, void* stream) {
+  return path_select(S0, S, top_idx, B, L, DFLASH2_PATH_VITERBI, path_slot, path_tok, path_score,
+                     stream);
+}
+
+DFLASH2_API int dflash2_path_select_mode(const float* S0, const float* S, const int32_t* top_idx,
+                                         int B, int L, int mode, int32_t* path_slot,
+                                         int32_t* path_tok, float* path_score, void* stream) {
+  return path_select(S0, S, top_idx, B, L, mode, path_slot, path_tok, path_score, stream);
 }
 
 DFLASH2_API int dflash2_verify_greedy(const int32_t* path_tok, const int32_t* target, int B, int L,

@@ -43,12 +43,16 @@ hipError_t launch_topk16(const float* logits, float* top_val, int32_t* top_idx, 
                          void* workspace, hipStream_t s);
 
 hipError_t launch_pair_score(const float* top_val, const int32_t* top_idx,
-                             const int32_t* anchor_tok, const void* U, const void* Vf, int B,
-                             int L, int V, int r, int dtype, float* S0, float* S, hipStream_t s);
+                             const int32_t* anchor_tok, const void* U, const void* Vf,
+                             const float* gate, int B, int L, int V, int r, int dtype, float* S0,
+                             float* S, hipStream_t s);
+
+hipError_t launch_context_gate(const void* h, const void* Wg, float* gate, int M, int H, int r,
+                               int dtype, hipStream_t s);
 
 hipError_t launch_path_select(const float* S0, const float* S, const int32_t* top_idx, int B,
-                              int L, int32_t* path_slot, int32_t* path_tok, float* path_score,
-                              hipStream_t s);
+                              int L, int greedy, int32_t* path_slot, int32_t* path_tok,
+                              float* path_score, hipStream_t s);
 
 hipError_t launch_verify_greedy(const int32_t* path_tok, const int32_t* target, int B, int L,
                                 int32_t* accept_len, int32_t* next_tok, hipStream_t s);

@@ -1,7 +1,8 @@
 // Adjacent-pair scores ("DFlash 2: Keep Drafting Parallel", section
-// "A lightweight path selector", eq. S_t(a,b)) in the ungated low-rank form
-//   S_t[i, j] = logit_t(c_{t,j}) + U[c_{t-1,i}] . V[c_{t,j}],
-// with the last verified token as the previous token of position 0.
+// "A lightweight path selector", eq. S_t(a,b)) in low-rank form
+//   S_t[i, j] = logit_t(c_{t,j}) + (U[c_{t-1,i}] * g_t) . V[c_{t,j}],
+// with the last verified token as the previous token of position 0.  g_t is
+// the context gate of position t (an r-vector); without one it is all ones.
 //
 // One wavefront per (block, position): it gathers the 16 (or 1) previous
 // factor rows and the 16 current factor rows into LDS as fp32, then each lane
@@ -88,8 +89,9 @@ __global__ __launch_bounds__(64) void pair_score_kernel(const float* __restrict_
                                                         const int32_t* __restrict__ top_idx,
                                                         const int32_t* __restrict__ anchor_tok,
                                                         const T* __restrict__ U,
-                                                        const T* __restrict__ Vf, int L, int V,
-                                                        int r, float* __restrict__ S0,
+                                                        const T* __restrict__ Vf,
+                                                        const float* __restrict__ gate, int L,
+                                                        int V, int r, float* __restrict__ S0,
                                                         float* __restrict__ S) {
   extern __shared__ float lds[];
   const int b = blockIdx.x / L;
@@ -101,10 +103,19 @@ __global__ __launch_bounds__(64) void pair_score_kernel(const float* __restrict_
   const int32_t* cur = top_idx + ((size_t)b * L + t) * kTopK;
   const float* tv = top_val + ((size_t)b * L + t) * kTopK;
 
+  float* sg = lds + 32 * stride;   // gate of this position
+  if (gate) {
+    const float* g = gate + ((size_t)b * L + t) * r;
+    for (int k = lane; k < r; k += 64) sg[k] = g[k];
+  }
   gather_rows<T, VEC>(Vf, cur, kTopK, r, V, sv);
   if (t == 0) {
     if (anchor_tok) gather_rows<T, VEC>(U, anchor_tok + b, 1, r, V, su);
     __syncthreads();
+    if (gate && anchor_tok) {
+      for (int k = lane; k < r; k += 64) su[k] *= sg[k];
+      __syncthreads();
+    }
     if (lane < kTopK) {
       float acc = 0.f;
       if (anchor_tok) {
@@ -118,6 +129,15 @@ __global__ __launch_bounds__(64) void pair_score_kernel(const float* __restrict_
   }
   gather_rows<T, VEC>(U, cur - kTopK, kTopK, r, V, su);
   __syncthreads();
+  if (gate) {
+    // A(a) (.) H(h_t): scale the previous-token rows once, before the dots
+    for (int e = lane; e < kTopK * r; e += 64) {
+      const int i = e / r;
+      const int k = e - i * r;
+      su[i * stride + k] *= sg[k];
+    }
+    __syncthreads();
+  }
   const int i = lane >> 2;
   const int j0 = (lane & 3) * 4;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -137,11 +157,11 @@ __global__ __launch_bounds__(64) void pair_score_kernel(const float* __restrict_
 }  // namespace
 
 hipError_t launch_pair_score(const float* top_val, const int32_t* top_idx,
-                             const int32_t* anchor_tok, const void* U, const void* Vf, int B,
-                             int L, int V, int r, int dtype, float* S0, float* S,
-                             hipStream_t s) {
+                             const int32_t* anchor_tok, const void* U, const void* Vf,
+                             const float* gate, int B, int L, int V, int r, int dtype, float* S0,
+                             float* S, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  const size_t lds = (size_t)2 * kTopK * (r + 1) * sizeof(float);
+  const size_t lds = ((size_t)2 * kTopK * (r + 1) + (gate ? r : 0)) * sizeof(float);
   const dim3 grid((unsigned)((long long)B * L));
   const bool vec_bf16 = r % 8 == 0 && ((reinterpret_cast<uintptr_t>(U) | reinterpret_cast<uintptr_t>(Vf)) & 15) == 0;
   const bool vec_f32 = r % 4 == 0 && ((reinterpret_cast<uintptr_t>(U) | reinterpret_cast<uintptr_t>(Vf)) & 15) == 0;
@@ -151,16 +171,16 @@ hipError_t launch_pair_score(const float* top_val, const int32_t* top_idx,
   const float* Vff = static_cast<const float*>(Vf);
   if (dtype == 1 && vec_bf16)
     hipLaunchKernelGGL((pair_score_kernel<uint16_t, true>), grid, dim3(64), lds, s, top_val, top_idx,
-                       anchor_tok, Ub, Vb, L, V, r, S0, S);
+                       anchor_tok, Ub, Vb, gate, L, V, r, S0, S);
   else if (dtype == 1)
     hipLaunchKernelGGL((pair_score_kernel<uint16_t, false>), grid, dim3(64), lds, s, top_val,
-                       top_idx, anchor_tok, Ub, Vb, L, V, r, S0, S);
+                       top_idx, anchor_tok, Ub, Vb, gate, L, V, r, S0, S);
   else if (vec_f32)
     hipLaunchKernelGGL((pair_score_kernel<float, true>), grid, dim3(64), lds, s, top_val, top_idx,
-                       anchor_tok, Uf, Vff, L, V, r, S0, S);
+                       anchor_tok, Uf, Vff, gate, L, V, r, S0, S);
   else
     hipLaunchKernelGGL((pair_score_kernel<float, false>), grid, dim3(64), lds, s, top_val, top_idx,
-                       anchor_tok, Uf, Vff, L, V, r, S0, S);
+                       anchor_tok, Uf, Vff, gate, L, V, r, S0, S);
   return hipGetLastError();
 }
 

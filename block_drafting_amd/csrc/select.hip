@@ -88,6 +88,71 @@ __global__ __launch_bounds__(64) void path_select_kernel(const float* __restrict
   }
 }
 
+// Index-tracking max over one aligned group of 16 lanes (lowest slot on ties);
+// every lane of the group ends with the winner.
+__device__ __forceinline__ void argmax16(float& bv, int& bi) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) better(bv, bi, __shfl_xor(bv, m, 64), __shfl_xor(bi, m, 64));
+}
+
+// Best-successor walk, the post's own decoder: p_0 = argmax S0, then
+// p_t = argmax_j S[t-1, p_{t-1}, j], lowest slot on ties; the score is the fp32
+// running sum along the walk.  Each step depends on the previous argmax, so
+// the wave first copies every row the walk might visit ((L-1) x 16 x 16
+// floats, all loads in flight at once) into LDS and then walks there: one
+// memory latency per block instead of one per position.  Lanes j = lane & 15
+// hold candidate j; the four quarters of the wave walk the same block.
+__global__ __launch_bounds__(64) void path_greedy_kernel(const float* __restrict__ S0,
+                                                         const float* __restrict__ S,
+                                                         const int32_t* __restrict__ top_idx,
+                                                         int L, int32_t* __restrict__ path_slot,
+                                                         int32_t* __restrict__ path_tok,
+                                                         float* __restrict__ path_score) {
+  extern __shared__ f32x4_t stage[];  // (L-1) * 64 vectors of 4 scores
+  constexpr int kUnroll = 8;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int j = lane & 15;
+  const int n4 = (L - 1) * kTopK * kTopK / 4;
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(S + (size_t)b * (L - 1) * kTopK * kTopK);
+  for (int base = 0; base < n4; base += 64 * kUnroll) {
+    f32x4_t v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int e = base + u * 64 + lane;
+      if (e < n4) v[u] = src[e];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int e = base + u * 64 + lane;
+      if (e < n4) stage[e] = v[u];
+    }
+  }
+  float bv = S0[(size_t)b * kTopK + j];
+  int p = j;
+  argmax16(bv, p);
+  float score = bv;
+  const size_t row = (size_t)b * L;
+  if (lane == 0) {
+    path_slot[row] = p;
+    if (path_tok) path_tok[row] = top_idx[row * kTopK + p];
+  }
+  __syncthreads();
+  const float* sS = reinterpret_cast<const float*>(stage);
+  for (int t = 1; t < L; ++t) {
+    bv = sS[((t - 1) * kTopK + p) * kTopK + j];
+    int bi = j;
+    argmax16(bv, bi);
+    score = score + bv;
+    p = bi;
+    if (lane == 0) {
+      path_slot[row + t] = p;
+      if (path_tok) path_tok[row + t] = top_idx[(row + t) * kTopK + p];
+    }
+  }
+  if (lane == 0) path_score[b] = score;
+}
+
 __global__ __launch_bounds__(256) void verify_greedy_kernel(const int32_t* __restrict__ path_tok,
                                                             const int32_t* __restrict__ target,
                                                             int B, int L,
@@ -106,11 +171,17 @@ __global__ __launch_bounds__(256) void verify_greedy_kernel(const int32_t* __res
 }  // namespace
 
 hipError_t launch_path_select(const float* S0, const float* S, const int32_t* top_idx, int B,
-                              int L, int32_t* path_slot, int32_t* path_tok, float* path_score,
-                              hipStream_t s) {
+                              int L, int greedy, int32_t* path_slot, int32_t* path_tok,
+                              float* path_score, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  hipLaunchKernelGGL(path_select_kernel, dim3((unsigned)B), dim3(64), 0, s, S0, S, top_idx, L,
-                     path_slot, path_tok, path_score);
+  if (greedy) {
+    const size_t lds = (size_t)(L - 1) * kTopK * kTopK * sizeof(float);
+    hipLaunchKernelGGL(path_greedy_kernel, dim3((unsigned)B), dim3(64), lds, s, S0, S, top_idx, L,
+                       path_slot, path_tok, path_score);
+  } else {
+    hipLaunchKernelGGL(path_select_kernel, dim3((unsigned)B), dim3(64), 0, s, S0, S, top_idx, L,
+                       path_slot, path_tok, path_score);
+  }
   return hipGetLastError();
 }
 

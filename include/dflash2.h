@@ -9,6 +9,10 @@
  *   4. max-plus path walk            dflash2_path_select
  *   5. greedy verification           dflash2_verify_greedy
  *
+ * Variants of steps 3 and 4 that follow the pages more literally:
+ *   context-gated pair scores        dflash2_context_gate, dflash2_pair_score_gated
+ *   best-successor (greedy) walk     dflash2_path_select_mode(..., DFLASH2_PATH_GREEDY, ...)
+ *
  * Sources are cited by page title and section:
  *   [POST]   "DFlash 2: Keep Drafting Parallel" (Inco AI).
  *   [GLONCE] "Inco AI's DFlash 2 lifts LLM decoding output 16-25%".
@@ -49,6 +53,9 @@ typedef enum {
 } dflash2_status;
 
 typedef enum { DFLASH2_F32 = 0, DFLASH2_BF16 = 1 } dflash2_dtype;
+
+/* Path walks of dflash2_path_select_mode. */
+typedef enum { DFLASH2_PATH_VITERBI = 0, DFLASH2_PATH_GREEDY = 1 } dflash2_path_mode;
 
 #define DFLASH2_TOPK 16      /* candidates per position ([POST] "A lightweight path selector") */
 #define DFLASH2_MAX_L 64     /* longest block the path walk accepts */
@@ -143,6 +150,35 @@ int dflash2_pair_score(const float* top_val, const int32_t* top_idx,
                        float* S0, float* S, void* stream);
 
 /*
+ * Context gate of the gated pair score.  [POST] "A lightweight path selector",
+ * eq. S_t(a,b): the match of A(a) with B(b) is weighted per channel by H(h_t),
+ * computed from the drafter's hidden state at position t.  The pages give no
+ * form for H; this call takes a sigmoid of a linear map:
+ *   gate[m, k] = 1 / (1 + exp(-sum_c h[m, c] * Wg[k, c]))
+ * h [M, H] of dtype (the hidden states fed to the LM head, m = b*L + t),
+ * Wg [r, H] of dtype (K-contiguous), gate [M, r] fp32.  M >= 0, H >= 8 with
+ * H % 8 == 0, 1 <= r <= 256.  h and Wg 16-byte aligned, gate 4-byte aligned,
+ * gate must not overlap h or Wg.  bf16 operands run on the matrix cores;
+ * fp32 accumulation, fp32 sigmoid.
+ */
+int dflash2_context_gate(const void* h, const void* Wg, float* gate,
+                         int M, int H, int r, int dtype, void* stream);
+
+/*
+ * Gated pair scores: dflash2_pair_score with the previous-token factor
+ * scaled channel by channel by the gate of the CURRENT position,
+ *   S0[b, j]        = top_val[b,0,j] + (U[anchor_tok[b]] * gate[b,0]) . Vf[top_idx[b,0,j]]
+ *   S[b, t-1, i, j] = top_val[b,t,j] + (U[top_idx[b,t-1,i]] * gate[b,t]) . Vf[top_idx[b,t,j]]
+ * gate [B, L, r] fp32 (required, 4-byte aligned, not overlapping the outputs);
+ * a gate of all ones gives dflash2_pair_score's result.  Every other
+ * argument, limit and error is as for dflash2_pair_score.
+ */
+int dflash2_pair_score_gated(const float* top_val, const int32_t* top_idx,
+                             const int32_t* anchor_tok, const void* U, const void* Vf,
+                             const float* gate, int B, int L, int V, int r, int dtype,
+                             float* S0, float* S, void* stream);
+
+/*
  * Max-plus (Viterbi) path over the pair scores, one wavefront per block.
  * [POST] "A lightweight path selector" walks the precomputed scores serially
  * from the last verified token; this call takes the exact best path:
@@ -152,10 +188,25 @@ int dflash2_pair_score(const float* top_val, const int32_t* top_idx,
  * path_slot [B, L] int32 slots; path_score [B] fp32 = d_{L-1}[final slot].
  * top_idx [B, L, 16] and path_tok [B, L]: both given (path_tok[b,t] =
  * top_idx[b,t,path_slot[b,t]]) or both NULL.
+ * Scores are expected finite (or -inf); a NaN score leaves the slot it
+ * decides unspecified (but in [0, 16)).
  */
 int dflash2_path_select(const float* S0, const float* S, const int32_t* top_idx,
                         int B, int L, int32_t* path_slot, int32_t* path_tok,
                         float* path_score, void* stream);
+
+/*
+ * dflash2_path_select with a choice of walk.  DFLASH2_PATH_VITERBI is
+ * dflash2_path_select.  DFLASH2_PATH_GREEDY is the pages' own walk ([POST]
+ * "A lightweight path selector": from the last verified token, follow the
+ * best successor at each step):
+ *   p_0 = argmax_j S0[j],  p_t = argmax_j S[t-1, p_{t-1}, j]  (lowest slot on ties),
+ *   path_score = fl32 running sum S0[p_0] + S[0,p_0,p_1] + ... in position order.
+ * Greedy mode needs S 16-byte aligned (when L > 1).  Other mode values: EINVAL.
+ */
+int dflash2_path_select_mode(const float* S0, const float* S, const int32_t* top_idx,
+                             int B, int L, int mode, int32_t* path_slot, int32_t* path_tok,
+                             float* path_score, void* stream);
 
 /*
  * Greedy verification.  [POST] "The right token is already in the candidates",

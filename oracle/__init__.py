@@ -28,7 +28,10 @@ from .cpu_oracle import (  # noqa: F401
     topk16,
     topk_gaps,
     pair_scores,
+    context_gate,
     path_select,
+    path_select_greedy,
+    greedy_margin,
     path_scores_f64,
     path_margin,
     verify_greedy,

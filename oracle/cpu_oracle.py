@@ -174,7 +174,7 @@ def topk_gaps(z: np.ndarray, top_val: np.ndarray) -> np.ndarray:
 
 # ------------------------------------------------------------------ a4 pair scores
 def pair_scores(top_val: np.ndarray, top_idx: np.ndarray, anchor_tok: Optional[np.ndarray],
-                U: np.ndarray, Vf: np.ndarray, uv_dtype: str):
+                U: np.ndarray, Vf: np.ndarray, uv_dtype: str, gate: Optional[np.ndarray] = None):
     """Scores of every adjacent candidate pair ([POST] "A lightweight path
     selector", eq. S_t(a, b)): the candidate's own logit plus a low-rank
     match between the previous token a and the candidate b.
@@ -187,6 +187,10 @@ def pair_scores(top_val: np.ndarray, top_idx: np.ndarray, anchor_tok: Optional[n
       S0[b, j]        = top_val[b, 0, j] + U[anchor_tok[b]] . V[top_idx[b, 0, j]]
       S[b, t-1, i, j] = top_val[b, t, j] + U[top_idx[b, t-1, i]] . V[top_idx[b, t, j]]
 
+    With a context gate (the post's H(h_t), [B, L, r] values for the
+    position of the current candidate), the match becomes
+    sum_k U[a, k] * gate[b, t, k] * V[b', k]: A(a) (.) H(h_t) matched with B(b').
+
     Evaluated in fp64 from the exact inputs, rounded once to fp32.
     top_val fp32 [B, L, 16], top_idx int [B, L, 16].
     Returns S0 fp32 [B, 16], S fp32 [B, L-1, 16, 16].
@@ -196,14 +200,36 @@ def pair_scores(top_val: np.ndarray, top_idx: np.ndarray, anchor_tok: Optional[n
     tv = top_val.astype(np.float64)
     cu = Uf[top_idx]        # [B, L, 16, r]  factor of each candidate as "previous"
     cv = Vff[top_idx]       # [B, L, 16, r]  factor of each candidate as "current"
+    g = None if gate is None else np.asarray(gate, dtype=np.float32).astype(np.float64)
     if anchor_tok is None:
         s0 = tv[:, 0, :]
     else:
         ua = Uf[np.asarray(anchor_tok)]                      # [B, r]
+        if g is not None:
+            ua = ua * g[:, 0, :]
         s0 = tv[:, 0, :] + np.einsum("br,bjr->bj", ua, cv[:, 0])
-    match = np.einsum("btir,btjr->btij", cu[:, :-1], cv[:, 1:])
+    prev = cu[:, :-1]
+    if g is not None:
+        prev = prev * g[:, 1:, None, :]                      # gate of position t
+    match = np.einsum("btir,btjr->btij", prev, cv[:, 1:])
     S = tv[:, 1:, None, :] + match
     return s0.astype(np.float32), S.astype(np.float32)
+
+
+def context_gate(y: np.ndarray, Wg: np.ndarray, w_dtype: str) -> np.ndarray:
+    """Context gate H(h_t) of the gated pair score ([POST] "A lightweight
+    path selector", eq. S_t(a, b): the gate, a function of the drafter's
+    hidden state at position t, decides which channels of the match count).
+
+    Reading: the pages give no form for H; the plainest gate is a logistic
+    sigmoid of a linear map of h_t,
+      gate[m, k] = 1 / (1 + exp(-sum_c y[m, c] * Wg[k, c])),
+    evaluated in fp64 from the exact inputs and rounded once to fp32.
+    y fp64 [M, H] (the hidden states the LM head reads), Wg [r, H] stored.
+    Returns fp32 [M, r].
+    """
+    a = np.asarray(y, dtype=np.float64) @ as_f64(Wg, w_dtype).T
+    return (1.0 / (1.0 + np.exp(-a))).astype(np.float32)
 
 
 # ------------------------------------------------------------------ a5 path walk
@@ -242,6 +268,53 @@ def path_select(S0: np.ndarray, S: np.ndarray, top_idx: np.ndarray):
         slot[:, t - 1] = back[np.arange(B), t, slot[:, t]]
     tok = np.take_along_axis(np.asarray(top_idx), slot[:, :, None], axis=2)[:, :, 0]
     return slot.astype(np.int32), tok.astype(np.int32), score.astype(np.float32)
+
+
+def path_select_greedy(S0: np.ndarray, S: np.ndarray, top_idx: np.ndarray):
+    """The post's own walk ([POST] "A lightweight path selector"; [GLONCE]:
+    the final step picks a path by greedy selection): start from the last
+    verified token and at every position take the best successor of the
+    token chosen before,
+
+      p_0 = argmax_j S0[j],  p_t = argmax_j S[t-1, p_{t-1}, j],
+
+    lowest slot on ties.  The returned score is the fp32 running sum
+    S0[p_0] + S[0, p_0, p_1] + ... in position order.
+    Returns (path_slot int32 [B, L], path_tok int32 [B, L], path_score fp32 [B]).
+    """
+    S0 = np.asarray(S0, dtype=np.float32)
+    S = np.asarray(S, dtype=np.float32)
+    B = S0.shape[0]
+    L = S.shape[1] + 1
+    b = np.arange(B)
+    slot = np.zeros((B, L), dtype=np.int64)
+    slot[:, 0] = np.argmax(S0, axis=1)
+    score = S0[b, slot[:, 0]].copy()
+    for t in range(1, L):
+        row = S[b, t - 1, slot[:, t - 1]]                  # [B, 16] successors of p_{t-1}
+        slot[:, t] = np.argmax(row, axis=1)
+        score = (score + row[b, slot[:, t]]).astype(np.float32)
+    tok = np.take_along_axis(np.asarray(top_idx), slot[:, :, None], axis=2)[:, :, 0]
+    return slot.astype(np.int32), tok.astype(np.int32), score.astype(np.float32)
+
+
+def greedy_margin(S0: np.ndarray, S: np.ndarray, slot: np.ndarray) -> np.ndarray:
+    """Smallest gap, along a greedy walk's slots, between the chosen entry and
+    the runner-up of the row it was chosen from (fp64, [B]).  A perturbation
+    of the scores smaller than half of it cannot change the walk."""
+    S0 = np.asarray(S0, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    B, L = slot.shape
+    b = np.arange(B)
+
+    def gap(row):
+        srt = -np.sort(-row, axis=1)
+        return srt[:, 0] - srt[:, 1]
+
+    m = gap(S0)
+    for t in range(1, L):
+        m = np.minimum(m, gap(S[b, t - 1, slot[:, t - 1]]))
+    return m
 
 
 def path_scores_f64(S0: np.ndarray, S: np.ndarray, slot: np.ndarray) -> np.ndarray:
@@ -346,7 +419,11 @@ def run_step_front(w, inp: Dict[str, object], blocks: Optional[np.ndarray] = Non
     top_val, top_idx = topk16(z)
     tv = top_val.reshape(Bs, L, K)
     ti = top_idx.reshape(Bs, L, K)
-    S0, S = pair_scores(tv, ti, anchor_tok, inp["U"], inp["Vf"], w.dtype)
-    slot, tok, score = path_select(S0, S, ti)
-    return {"y": y, "z": z, "top_val": tv, "top_idx": ti, "S0": S0, "S": S,
+    gate = None
+    if getattr(w, "gate", False):
+        gate = context_gate(y.reshape(Bs * L, H), inp["Wg"], w.dtype).reshape(Bs, L, -1)
+    S0, S = pair_scores(tv, ti, anchor_tok, inp["U"], inp["Vf"], w.dtype, gate)
+    walk = path_select_greedy if getattr(w, "walk", "viterbi") == "greedy" else path_select
+    slot, tok, score = walk(S0, S, ti)
+    return {"y": y, "z": z, "top_val": tv, "top_idx": ti, "gate": gate, "S0": S0, "S": S,
             "path_slot": slot, "path_tok": tok, "path_score": score}

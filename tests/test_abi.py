@@ -130,6 +130,50 @@ def test_pair_select_verify_validation():
     assert ver(P, Q, 0, 8, P + 0x1000, None, None) == 0
 
 
+def test_gate_and_gated_pair_validation():
+    L = bd.lib()
+    cg = L.dflash2_context_gate
+    #          h  Wg          gate          M   H    r   dt
+    ok = [P, P + 0x100000, Q, 8, 64, 16, 1]
+    assert cg(*ok[:4], 60, *ok[5:], None) == EINVAL              # H % 8
+    assert cg(*ok[:5], 0, 1, None) == EINVAL                     # r = 0
+    assert cg(*ok[:5], 257, 1, None) == EINVAL                   # r > 256
+    assert cg(*ok[:6], 3, None) == EINVAL                        # dtype
+    assert cg(None, *ok[1:], None) == EINVAL
+    assert cg(P + 4, *ok[1:], None) == EINVAL                    # h misaligned
+    assert cg(P, P + 0x100000, P + 64, 8, 64, 16, 1, None) == EINVAL   # gate overlaps h
+    assert cg(P, P + 0x100000, Q, 8, (1 << 21) + 8, 16, 1, None) == EUNSUP
+    assert cg(*ok[:3], 0, *ok[4:], None) == 0                    # M = 0
+    pg = L.dflash2_pair_score_gated
+    #       tv  ti          anc   U   V             gate          B  L  V    r  dt S0           S
+    args = [P, P + 0x10000, None, Q, Q + 0x100000, P + 0x40000, 2, 4, 100, 8, 1, P + 0x20000,
+            P + 0x30000]
+    bad = list(args)
+    bad[5] = None                                                # gate required
+    assert pg(*bad, None) == EINVAL
+    bad[5] = P + 0x40002                                         # misaligned
+    assert pg(*bad, None) == EINVAL
+    bad[5] = P + 0x30000                                         # gate overlaps S
+    assert pg(*bad, None) == EINVAL
+    bad = list(args)
+    bad[9] = 300                                                 # r > 256
+    assert pg(*bad, None) == EINVAL
+    assert pg(*args[:6], 0, *args[7:], None) == 0                # B = 0
+
+
+def test_path_select_mode_validation():
+    sm = bd.lib().dflash2_path_select_mode
+    assert sm(P, Q, None, 2, 4, 2, P + 0x1000, None, P + 0x2000, None) == EINVAL   # mode
+    assert sm(P, Q, None, 2, 4, -1, P + 0x1000, None, P + 0x2000, None) == EINVAL
+    assert sm(P, Q + 4, None, 2, 4, 1, P + 0x1000, None, P + 0x2000, None) == EINVAL  # S align
+    assert sm(P, Q, None, 2, 65, 1, P + 0x1000, None, P + 0x2000, None) == EINVAL
+    assert sm(P, Q, None, 2, 4, 1, P + 0x1000, None, P + 0x1000, None) == EINVAL     # alias
+    assert sm(P, Q, None, 0, 4, 1, P + 0x1000, None, P + 0x2000, None) == 0
+    assert bd.PATH_MODES == {"viterbi": 0, "greedy": 1}
+    text = open(HEADER).read()
+    assert "DFLASH2_PATH_VITERBI = 0" in text and "DFLASH2_PATH_GREEDY = 1" in text
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros((1, 8, 64), dtype=torch.bfloat16)

@@ -10,8 +10,12 @@ Bars (floating point from the arithmetic, integers exact):
             evaluates in fp64 and rounds once)
   logits    |z - z_ora| <= 1e-3 max(|z_ora|, 1); bit-exact on dyadic inputs
   top-16    bit-exact ids and values (decided on the same fp32 logits)
-  pairs     |S - S_ora| <= 1e-4
-  path      bit-exact slots, tokens and fp32 score (the oracle decides in fp32)
+  gate      |g - g_ora| <= (1/4) H 2^-24 sum_c |h_c w_c| + 4 2^-24 (fp32
+            accumulation through the sigmoid's slope), mean error < 1e-6
+  pairs     |S - S_ora| <= 1e-4 (gated and ungated); a gate of ones
+            reproduces the ungated kernel bit for bit
+  path      bit-exact slots, tokens and fp32 score for both walks (the
+            oracle decides in fp32)
   verify    exact
 """
 import numpy as np
@@ -206,6 +210,53 @@ def test_pair_without_anchor_and_bad_ids_give_nan():
     np.testing.assert_allclose(S[ok], wS[ok], atol=1e-4, rtol=0)
 
 
+# ------------------------------------------------------------------ context gate
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("M,H,r", [(1, 8, 1), (37, 136, 7), (300, 520, 64), (64, 2568, 33),
+                                   (513, 5120, 256), (4096, 256, 40)])
+def test_context_gate_parity(dt, M, H, r):
+    g = np.random.default_rng(M + H + r)
+    h = _bits_or_f32(g.standard_normal((M, H)).astype(np.float32), dt)
+    Wg = _bits_or_f32((g.standard_normal((r, H)) / np.sqrt(H)).astype(np.float32), dt)
+    hd, Wd = O.as_f64(h, dt), O.as_f64(Wg, dt)
+    want = O.context_gate(hd, Wg, dt).astype(np.float64)
+    got = bd.context_gate(to_dev(h, dt), to_dev(Wg, dt)).cpu().numpy()
+    err = np.abs(got - want)
+    tol = 0.25 * H * 2.0 ** -24 * (np.abs(hd) @ np.abs(Wd).T) + 4 * 2.0 ** -24
+    assert (err <= tol).all(), err.max()
+    assert err.mean() < 1e-6, err.mean()
+
+
+def test_context_gate_saturates_and_empty():
+    h = np.zeros((3, 16), np.float32)
+    h[0, 0], h[1, 0] = 200.0, -200.0                 # sigmoid saturates to exactly 1 and 0
+    Wg = np.zeros((2, 16), np.float32)
+    Wg[0, 0] = 1.0
+    got = bd.context_gate(torch.from_numpy(h).to(DEV), torch.from_numpy(Wg).to(DEV)).cpu().numpy()
+    np.testing.assert_array_equal(got, [[1.0, 0.5], [0.0, 0.5], [0.5, 0.5]])
+    out = bd.context_gate(torch.empty((0, 16), device=DEV), torch.from_numpy(Wg).to(DEV))
+    assert out.shape == (0, 2)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,V,r", [(1, 1, 64, 1), (3, 2, 500, 7), (4, 8, 4096, 32),
+                                     (5, 16, 151936, 64), (2, 5, 300, 256), (64, 8, 151936, 256)])
+def test_gated_pair_parity(dt, B, L, V, r):
+    tv, ti, at, U, Vf = _pair_case(B, L, V, r, dt, seed=B + L + r + 1)
+    gate = np.random.default_rng(r).random((B, L, r)).astype(np.float32)
+    wS0, wS = O.pair_scores(tv, ti, at, U, Vf, dt, gate)
+    args = (torch.from_numpy(tv).to(DEV), torch.from_numpy(ti).to(DEV),
+            torch.from_numpy(at).to(DEV), to_dev(U, dt), to_dev(Vf, dt))
+    S0, S = bd.pair_score(*args, gate=torch.from_numpy(gate).to(DEV))
+    assert np.abs(S0.cpu().numpy() - wS0).max() <= 1e-4
+    if L > 1:
+        assert np.abs(S.cpu().numpy() - wS).max() <= 1e-4
+    # a gate of ones is the ungated kernel, bit for bit
+    G0, G = bd.pair_score(*args, gate=torch.ones((B, L, r), device=DEV))
+    P0, P = bd.pair_score(*args)
+    assert torch.equal(G0, P0) and torch.equal(G, P)
+
+
 # ------------------------------------------------------------------ path walk
 @pytest.mark.parametrize("B,L,dyadic", [(1, 1, False), (7, 2, True), (64, 8, False), (64, 8, True),
                                         (33, 16, True), (5, 64, False), (300, 3, True)])
@@ -225,6 +276,45 @@ def test_path_select_bit_exact(B, L, dyadic):
     np.testing.assert_array_equal(slot.cpu().numpy(), ws)
     np.testing.assert_array_equal(tok.cpu().numpy(), wt)
     np.testing.assert_array_equal(score.cpu().numpy().view(np.uint32), wsc.view(np.uint32))
+
+
+@pytest.mark.parametrize("B,L,dyadic", [(1, 1, False), (7, 2, True), (64, 8, False), (64, 8, True),
+                                        (33, 16, True), (5, 64, False), (5, 64, True), (300, 3, True)])
+def test_path_greedy_bit_exact(B, L, dyadic):
+    g = np.random.default_rng(B * L + 1)
+    if dyadic:
+        S0 = (np.round(g.standard_normal((B, 16)) * 2) / 4).astype(np.float32)
+        S = (np.round(g.standard_normal((B, L - 1, 16, 16)) * 2) / 4).astype(np.float32)
+    else:
+        S0 = g.standard_normal((B, 16)).astype(np.float32) * 4
+        S = g.standard_normal((B, L - 1, 16, 16)).astype(np.float32)
+    ti = g.integers(0, 151936, (B, L, 16)).astype(np.int32)
+    ws, wt, wsc = O.path_select_greedy(S0, S, ti)
+    slot, tok, score = bd.path_select(torch.from_numpy(S0).to(DEV),
+                                      torch.from_numpy(S).to(DEV) if L > 1 else None,
+                                      torch.from_numpy(ti).to(DEV), mode="greedy")
+    np.testing.assert_array_equal(slot.cpu().numpy(), ws)
+    np.testing.assert_array_equal(tok.cpu().numpy(), wt)
+    np.testing.assert_array_equal(score.cpu().numpy().view(np.uint32), wsc.view(np.uint32))
+
+
+def test_path_greedy_trap_and_ties():
+    # the pins' hand case: greedy [0, 3, 7] (score 5), max-plus [1, 2, 5] (score 9)
+    S0 = np.zeros((1, 16), np.float32)
+    S0[0, 0], S0[0, 1] = 5.0, 4.0
+    S = np.full((1, 2, 16, 16), -10.0, np.float32)
+    S[0, 0, 0, 3], S[0, 0, 1, 2], S[0, 0, 3, 0] = -1.0, 3.0, 8.0
+    S[0, 1] = 0.0
+    S[0, 1, 2, 5], S[0, 1, 3, 7] = 2.0, 1.0
+    d0, d = torch.from_numpy(S0).to(DEV), torch.from_numpy(S).to(DEV)
+    slot, _, score = bd.path_select(d0, d, None, mode="greedy")
+    assert slot.cpu().tolist() == [[0, 3, 7]] and score.cpu().tolist() == [5.0]
+    slot, _, score = bd.path_select(d0, d, None, mode="viterbi")
+    assert slot.cpu().tolist() == [[1, 2, 5]] and score.cpu().tolist() == [9.0]
+    z0 = torch.zeros((3, 16), device=DEV)
+    z = torch.zeros((3, 4, 16, 16), device=DEV)
+    slot, _, score = bd.path_select(z0, z, None, mode="greedy")
+    assert (slot.cpu().numpy() == 0).all() and (score.cpu().numpy() == 0).all()
 
 
 def test_path_select_all_tied_takes_slot_zero():

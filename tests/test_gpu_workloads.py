@@ -1,22 +1,25 @@
-"""Full-size parity on the five workloads (GPU).
+"""Full-size parity on the workloads (GPU).
 
 The GPU runs the whole step on every block, in the same launch configuration
 the benchmark times.  The oracle recomputes a seeded subset of blocks
 (workloads.parity_subset) from the same inputs.  Checks:
 
 stage-wise (each GPU stage fed the oracle's input for that stage):
-  every conv application (<= 1 bf16 ulp), top-16 (bit-exact), pair scores
-  (<= 1e-4; bit-exact on the dyadic stress workload), path walk (bit-exact),
-  verification (exact);
+  every conv application (<= 1 bf16 ulp), context gate (gated workload:
+  within the fp32 accumulation bound), top-16 (bit-exact), pair scores
+  (<= 1e-4; bit-exact on the dyadic stress workload), path walk, max-plus or
+  greedy (bit-exact), verification (exact);
 end to end (GPU stages fed by GPU stages), with the margin rule:
   logits within 1e-3 max(|z|, 1); a top-16 slot must match where the
   oracle's gap to its neighbours exceeds 1e-3; the path and acceptance length
-  must match where the oracle's best-vs-second path margin exceeds 1e-3 plus
-  the score drift the logits tolerance allows, else the GPU path must be
-  near-optimal under the oracle's scores;
+  must match where the oracle's decision margin (best-vs-second path for the
+  max-plus walk, smallest best-vs-runner-up step gap for the greedy walk)
+  exceeds 1e-3 plus the score drift the logits tolerance allows, else a
+  max-plus path must be near-optimal under the oracle's scores;
 over all blocks (properties that hold at any size):
   sorted distinct in-range candidates whose values are their logits, path
-  tokens are candidates, path score equals the path's score, acceptance in
+  tokens are candidates, the path is the oracle's walk of the GPU's own
+  scores (bit-exact), path score equals the path's score, acceptance in
   [1, L+1] and equal to the oracle's verification of the GPU path.
 """
 import numpy as np
@@ -38,7 +41,19 @@ def _dt(w):
     return torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
 
-@pytest.fixture(scope="module", params=[0, 1, 2, 3, 4], ids=lambda c: f"w{c}")
+def _walk(w):
+    return O.path_select_greedy if w.walk == "greedy" else O.path_select
+
+
+def gate_tolerance(y, Wg_f64):
+    """Bound on |gate_gpu - gate_ora|: fp32 accumulation of H products
+    (<= H 2^-24 sum|y w|) through the sigmoid's slope (<= 1/4), plus a few
+    fp32 roundings of the sigmoid itself."""
+    H = y.shape[1]
+    return 0.25 * H * 2.0 ** -24 * (np.abs(y) @ np.abs(Wg_f64).T) + 4 * 2.0 ** -24
+
+
+@pytest.fixture(scope="module", params=sorted(WL.WORKLOADS), ids=lambda c: f"w{c}")
 def case(request):
     w = WL.WORKLOADS[request.param]
     print(f"\n[workload {w.cid} {w.name}] B={w.B} L={w.L} H={w.H} V={w.V} r={w.r}", flush=True)
@@ -50,9 +65,12 @@ def case(request):
         "U": to_dev(inp["U"], w.dtype),
         "Vf": to_dev(inp["Vf"], w.dtype),
         "anchor_tok": to_dev(inp["anchor_tok"], "i32"),
+        "Wg": to_dev(inp["Wg"], w.dtype) if w.gate else None,
     }
-    buf = bd.StepBuffers(w.B, w.L, w.H, w.V, _dt(w), DEV, n_convs=w.n_convs, keep_logits=True)
-    bd.run_step(buf, dev["x"], dev["convs"], dev["W"], dev["U"], dev["Vf"], dev["anchor_tok"], None)
+    buf = bd.StepBuffers(w.B, w.L, w.H, w.V, _dt(w), DEV, n_convs=w.n_convs, keep_logits=True,
+                         gate_rank=w.r if w.gate else 0)
+    bd.run_step(buf, dev["x"], dev["convs"], dev["W"], dev["U"], dev["Vf"], dev["anchor_tok"], None,
+                Wg=dev["Wg"], walk=w.walk)
     torch.cuda.synchronize()
     blocks = WL.parity_subset(w)
     ora = O.run_step_front(w, inp, blocks)
@@ -104,8 +122,9 @@ def test_topk_pair_select_verify_stagewise(case):
     np.testing.assert_array_equal(tv.cpu().numpy(), ora["top_val"].reshape(-1, 16))
     Bs = len(case["blocks"])
     at = case["inp"]["anchor_tok"][case["blocks"]]
+    gate = None if ora["gate"] is None else torch.from_numpy(ora["gate"]).to(DEV)
     S0, S = bd.pair_score(torch.from_numpy(ora["top_val"]).to(DEV), torch.from_numpy(ora["top_idx"]).to(DEV),
-                          to_dev(at, "i32"), case["dev"]["U"], case["dev"]["Vf"])
+                          to_dev(at, "i32"), case["dev"]["U"], case["dev"]["Vf"], gate=gate)
     S0, S = S0.cpu().numpy(), S.cpu().numpy()
     if w.dyadic:
         np.testing.assert_array_equal(S0, ora["S0"])
@@ -114,7 +133,7 @@ def test_topk_pair_select_verify_stagewise(case):
         assert np.abs(S0 - ora["S0"]).max() <= 1e-4
         assert np.abs(S - ora["S"]).max() <= 1e-4
     slot, tok, score = bd.path_select(torch.from_numpy(ora["S0"]).to(DEV), torch.from_numpy(ora["S"]).to(DEV),
-                                      torch.from_numpy(ora["top_idx"]).to(DEV))
+                                      torch.from_numpy(ora["top_idx"]).to(DEV), mode=w.walk)
     np.testing.assert_array_equal(slot.cpu().numpy(), ora["path_slot"])
     np.testing.assert_array_equal(tok.cpu().numpy(), ora["path_tok"])
     np.testing.assert_array_equal(score.cpu().numpy(), ora["path_score"])
@@ -123,6 +142,20 @@ def test_topk_pair_select_verify_stagewise(case):
     np.testing.assert_array_equal(acc.cpu().numpy(), wa)
     np.testing.assert_array_equal(nxt.cpu().numpy(), wn)
     assert Bs == len(wa)
+
+
+def test_context_gate_stagewise(case):
+    w, ora, inp = case["w"], case["ora"], case["inp"]
+    if not w.gate:
+        pytest.skip("ungated workload")
+    B, L, H = len(case["blocks"]), w.L, w.H
+    y = ora["y"].reshape(B * L, H)
+    g = bd.context_gate(torch.from_numpy(y).to(_dt(w)).to(DEV), case["dev"]["Wg"]).cpu().numpy()
+    want = ora["gate"].reshape(B * L, -1).astype(np.float64)
+    err = np.abs(g - want)
+    assert (err <= gate_tolerance(y, O.as_f64(inp["Wg"], w.dtype))).all(), err.max()
+    assert err.mean() < 1e-6, err.mean()
+    print(f"gate: max |dg| {err.max():.2e}, mean {err.mean():.2e}")
 
 
 # ------------------------------------------------------------------ end to end
@@ -146,10 +179,21 @@ def test_end_to_end_subset(case):
     got_vals = np.take_along_axis(zo_b, ti.astype(np.int64), axis=2)
     assert np.all(np.abs(got_vals - ora["top_val"]) <= 2 * MARGIN + 2 * zdrift)
 
+    if w.gate:
+        g = buf.gate.view(B, L, -1).cpu().numpy()[blocks].reshape(len(blocks) * L, -1)
+        y = ora["y"].reshape(len(blocks) * L, w.H)
+        # the GPU gate reads the GPU's conv output, equal to the oracle's up to 1 ulp
+        tol = gate_tolerance(y, O.as_f64(case["inp"]["Wg"], w.dtype)) + 0.25 * (
+            np.abs(O.as_f64(case["inp"]["Wg"], w.dtype)) @ bf16_ulp(y).T).T
+        assert (np.abs(g - ora["gate"].reshape(g.shape)) <= tol).all()
+
     slot = buf.path_slot.cpu().numpy()[blocks]
     tok = buf.path_tok.cpu().numpy()[blocks]
     acc = buf.accept_len.cpu().numpy()[blocks]
-    margin = O.path_margin(ora["S0"], ora["S"])
+    if w.walk == "greedy":
+        margin = O.greedy_margin(ora["S0"], ora["S"], ora["path_slot"])
+    else:
+        margin = O.path_margin(ora["S0"], ora["S"])
     same_cands = (ti == ora["top_idx"]).all(axis=(1, 2))
     S_g = buf.S.cpu().numpy()[blocks]
     S0_g = buf.S0.cpu().numpy()[blocks]
@@ -165,7 +209,7 @@ def test_end_to_end_subset(case):
             assert tok[k].tolist() == ora["path_tok"][k].tolist(), k
             wa, _ = O.verify_greedy(ora["path_tok"][k:k + 1], case["tgt_sub"][k:k + 1])
             assert acc[k] == wa[0]
-        else:
+        elif w.walk == "viterbi":
             best = O.path_scores_f64(ora["S0"][k:k + 1], ora["S"][k:k + 1], ora["path_slot"][k:k + 1].astype(np.int64))
             mine = O.path_scores_f64(ora["S0"][k:k + 1], ora["S"][k:k + 1], slot[k:k + 1].astype(np.int64))
             assert mine[0] >= best[0] - MARGIN - 2 * L * drift
@@ -199,6 +243,9 @@ def test_properties_all_blocks(case):
     tok = buf.path_tok.cpu().numpy()
     np.testing.assert_array_equal(tok, np.take_along_axis(ti, slot[:, :, None].astype(np.int64), 2)[:, :, 0])
     S0_g, S_g = buf.S0.cpu().numpy(), buf.S.cpu().numpy()
+    ws, _, wsc = _walk(w)(S0_g, S_g, ti)                           # same fp32 scores: exact
+    np.testing.assert_array_equal(slot, ws)
+    np.testing.assert_array_equal(buf.path_score.cpu().numpy(), wsc)
     sc = O.path_scores_f64(S0_g, S_g, slot.astype(np.int64))
     mag = O.path_scores_f64(np.abs(S0_g), np.abs(S_g), slot.astype(np.int64))
     assert np.all(np.abs(sc - buf.path_score.cpu().numpy()) <= L * 2.0 ** -23 * mag)
@@ -212,11 +259,12 @@ def test_properties_all_blocks(case):
 
 def test_step_is_deterministic(case):
     w, buf, dev = case["w"], case["buf"], case["dev"]
-    if w.cid not in (0, 2):
-        pytest.skip("checked on the tiny and the benchmark workload")
+    if w.cid not in (0, 2, 5):
+        pytest.skip("checked on the tiny, the benchmark and the gated workload")
     snap = [t.clone() for t in (buf.logits, buf.top_val, buf.top_idx, buf.S0, buf.S, buf.path_slot,
                                 buf.path_score)]
-    bd.run_step(buf, dev["x"], dev["convs"], dev["W"], dev["U"], dev["Vf"], dev["anchor_tok"], None)
+    bd.run_step(buf, dev["x"], dev["convs"], dev["W"], dev["U"], dev["Vf"], dev["anchor_tok"], None,
+                Wg=dev["Wg"], walk=w.walk)
     torch.cuda.synchronize()
     for a, b in zip(snap, (buf.logits, buf.top_val, buf.top_idx, buf.S0, buf.S, buf.path_slot,
                            buf.path_score)):

@@ -220,6 +220,69 @@ def test_pair_scores_one_hot_factors_give_indicator_matches():
                     assert S[b, t - 1, i, j] == want
 
 
+def test_context_gate_hand_values_and_orientation():
+    # gate[m, k] = sigmoid(y[m] . Wg[k]); sigmoid(ln 3) = 3/4, sigmoid(-ln 3) = 1/4
+    l3 = np.log(3.0)
+    y = np.array([[1.0, 0.0], [0.0, 1.0]])
+    Wg = np.array([[l3, 0.0], [-l3, 0.0], [0.0, l3]], dtype=np.float32)
+    got = O.context_gate(y, Wg, "f32")
+    assert got.dtype == np.float32 and got.shape == (2, 3)
+    np.testing.assert_array_equal(got, [[0.75, 0.25, 0.5], [0.5, 0.5, 0.75]])
+    assert (O.context_gate(y, np.zeros((3, 2), np.float32), "f32") == 0.5).all()
+
+
+def test_context_gate_symmetry_and_library_logistic():
+    from scipy.special import expit
+
+    g = np.random.default_rng(21)
+    y = g.standard_normal((7, 24))
+    Wg = (g.standard_normal((5, 24)) * 0.3).astype(np.float32)
+    a = O.context_gate(y, Wg, "f32").astype(np.float64)
+    b = O.context_gate(y, -Wg, "f32").astype(np.float64)
+    np.testing.assert_allclose(a + b, 1.0, atol=2 ** -23)
+    want = expit(y @ Wg.astype(np.float64).T)
+    np.testing.assert_allclose(a, want, rtol=2 ** -23)
+    bits = WL.to_bf16_bits(Wg)
+    np.testing.assert_allclose(O.context_gate(y, bits, "bf16"),
+                               expit(y @ O.bf16_bits_to_f64(bits).T), rtol=2 ** -23)
+
+
+def test_gated_pair_scores_reduce_and_use_the_current_positions_gate():
+    g = np.random.default_rng(22)
+    B, L, V, r = 2, 4, 60, 6
+    tv = np.round(g.standard_normal((B, L, 16)) * 8).astype(np.float32) / 8
+    ti = g.integers(0, V, (B, L, 16)).astype(np.int32)
+    anchor = g.integers(0, V, B)
+    F1 = g.standard_normal((V, r)).astype(np.float32)
+    F2 = g.standard_normal((V, r)).astype(np.float32)
+    ones = np.ones((B, L, r), np.float32)
+    for got, want in zip(O.pair_scores(tv, ti, anchor, F1, F2, "f32", ones),
+                         O.pair_scores(tv, ti, anchor, F1, F2, "f32")):
+        np.testing.assert_array_equal(got, want)
+    zero = np.zeros((B, L, r), np.float32)
+    S0, S = O.pair_scores(tv, ti, anchor, F1, F2, "f32", zero)
+    np.testing.assert_array_equal(S0, tv[:, 0])
+    np.testing.assert_array_equal(S, np.broadcast_to(tv[:, 1:, None, :], S.shape))
+    # one-hot factors and a one-channel gate per position: the match is
+    # [f(a) == k_t == h(b)] with k_t the channel position t lets through
+    f = lambda tok: tok % r
+    h = lambda tok: (tok // 2) % r
+    U = np.eye(r, dtype=np.float32)[f(np.arange(V))]
+    Vf = np.eye(r, dtype=np.float32)[h(np.arange(V))]
+    kt = g.integers(0, r, (B, L))
+    gate = np.eye(r, dtype=np.float32)[kt]
+    S0, S = O.pair_scores(tv, ti, anchor, U, Vf, "f32", gate)
+    for b in range(B):
+        for j in range(16):
+            want = f(anchor[b]) == kt[b, 0] == h(ti[b, 0, j])
+            assert S0[b, j] == tv[b, 0, j] + want
+        for t in range(1, L):
+            for i in range(16):
+                for j in range(16):
+                    want = f(ti[b, t - 1, i]) == kt[b, t] == h(ti[b, t, j])
+                    assert S[b, t - 1, i, j] == tv[b, t, j] + want
+
+
 # ------------------------------------------------------------------ path walk
 def _brute_paths(S0, S):
     """All 16^L paths with fp64 scores; best under the tie rule (smallest
@@ -303,6 +366,65 @@ def test_path_select_without_pair_terms_is_top1():
     slot, tok, _ = O.path_select(S0, S, ti)
     np.testing.assert_array_equal(slot, 0)
     np.testing.assert_array_equal(tok, ti[:, :, 0])
+
+
+def test_greedy_walk_hand_trap_differs_from_viterbi():
+    # Greedy takes slot 0 first (5 > 4) and is then stuck with its poor
+    # successors; the best path starts from slot 1.
+    S0 = np.zeros((1, 16), np.float32)
+    S0[0, 0], S0[0, 1] = 5.0, 4.0
+    S = np.full((1, 2, 16, 16), -10.0, np.float32)
+    S[0, 0, 0, 3] = -1.0          # best successor of slot 0
+    S[0, 0, 1, 2] = 3.0           # best successor of slot 1
+    S[0, 0, 3, 0] = 8.0           # row/column swap trap: entry (3, 0), not (0, 3)
+    S[0, 1] = 0.0
+    S[0, 1, 2, 5] = 2.0
+    S[0, 1, 3, 7] = 1.0
+    ti = np.arange(48, dtype=np.int32).reshape(1, 3, 16) + 100
+    slot, tok, score = O.path_select_greedy(S0, S, ti)
+    assert slot.tolist() == [[0, 3, 7]]
+    assert tok.tolist() == [[100, 119, 139]]
+    assert score.tolist() == [5.0]
+    vslot, _, vscore = O.path_select(S0, S, ti)
+    assert vslot.tolist() == [[1, 2, 5]] and vscore.tolist() == [9.0]
+    # the walk's margin: gaps 1 (5 vs 4), 9 (-1 vs -10), 1 (1 vs 0)
+    assert O.greedy_margin(S0, S, slot).tolist() == [1.0]
+
+
+def test_greedy_walk_equals_viterbi_without_pair_terms_or_at_L1():
+    g = np.random.default_rng(23)
+    B = 6
+    for L in (1, 5):
+        S0 = (np.round(g.standard_normal((B, 16)) * 2) / 4).astype(np.float32)
+        # rows independent of the predecessor i: both walks pick each column's max
+        cols = (np.round(g.standard_normal((B, L - 1, 1, 16)) * 2) / 4).astype(np.float32)
+        S = np.broadcast_to(cols, (B, L - 1, 16, 16)).copy()
+        ti = g.integers(0, 500, (B, L, 16)).astype(np.int32)
+        gs, gt, gsc = O.path_select_greedy(S0, S, ti)
+        vs, vt, vsc = O.path_select(S0, S, ti)
+        np.testing.assert_array_equal(gs, vs)
+        np.testing.assert_array_equal(gt, vt)
+        np.testing.assert_array_equal(gsc, vsc)
+
+
+def test_greedy_walk_is_never_better_than_the_best_path():
+    g = np.random.default_rng(24)
+    B, L = 40, 6
+    S0 = g.standard_normal((B, 16)).astype(np.float32)
+    S = g.standard_normal((B, L - 1, 16, 16)).astype(np.float32)
+    ti = np.zeros((B, L, 16), np.int32)
+    gs, _, gsc = O.path_select_greedy(S0, S, ti)
+    vs, _, vsc = O.path_select(S0, S, ti)
+    exact_g = O.path_scores_f64(S0, S, gs)
+    assert (exact_g <= O.path_scores_f64(S0, S, vs) + 1e-12).all()
+    assert (exact_g < O.path_scores_f64(S0, S, vs) - 1e-6).any()   # differs somewhere
+    np.testing.assert_allclose(gsc, exact_g, atol=1e-5)
+    # each greedy step ends on a row maximum; ties go to the lowest slot
+    S0t = np.zeros((1, 16), np.float32)
+    St = np.zeros((1, 3, 16, 16), np.float32)
+    St[0, 1, 0, [4, 9]] = 1.0
+    s, _, _ = O.path_select_greedy(S0t, St, np.zeros((1, 4, 16), np.int32))
+    assert s.tolist() == [[0, 0, 4, 0]]
 
 
 # ------------------------------------------------------------------ verify

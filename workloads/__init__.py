@@ -19,14 +19,16 @@ Every tensor has its own PCG64 stream keyed by ``(seed, tensor_tag)``; large
 tensors are filled in a fixed number of chunks, each with its own child key,
 so the values do not depend on how many threads fill them.
 
-The five workloads
-------------------
+The workloads
+-------------
 0. tiny: 1 block, L=8, H=256, V=4096, r=32, fp32 end to end.
 1. 4B-shaped head: 32 blocks, L=8, H=2560, V=151936, r=64, bf16.
 2. 27B-shaped head: 64 blocks, L=8, H=5120, V=151936, r=64, bf16.
 3. conv-heavy body: 128 blocks, L=16, H=5120, 20 chained dynamic convs, r=64.
 4. stress: 256 blocks, L=16, H=5120, r=128, logits on a 1/64 grid (ties),
    targets a 50/50 mix of all-correct and random-miss blocks.
+5. 27B-shaped head with the pages' own selector: rank-256 factors weighted
+   by a context gate from the final hidden state, greedy best-successor walk.
 
 The planted-target recall profile of workloads 0-2 and 4 is the per-position
 Recall@1 / Recall@16 of Table 1 of "DFlash 2: Keep Drafting Parallel"
@@ -77,6 +79,8 @@ class Workload:
     target_mode: str      # "planted" or "mix"
     dyadic: bool          # integer / dyadic construction (exact sums, ties)
     parity_blocks: int    # seeded block subset the oracle checks at full size
+    gate: bool = False    # pair match weighted by a context gate from h_t (Wg [r, H])
+    walk: str = "viterbi"  # path walk: "viterbi" (max-plus) or "greedy" (best successor)
 
     @property
     def M(self) -> int:
@@ -110,6 +114,10 @@ WORKLOADS: Dict[int, Workload] = {
     2: Workload(2, "27b-head", 64, 8, 5120, 151936, 64, "bf16", 1, False, "planted", False, 8),
     3: Workload(3, "conv-heavy", 128, 16, 5120, 151936, 64, "bf16", 20, True, "planted", False, 4),
     4: Workload(4, "stress", 256, 16, 5120, 151936, 128, "bf16", 1, False, "mix", True, 4),
+    # The pages' own selector on the 27B-shaped head: rank-256 factors, the
+    # context gate and the greedy best-successor walk.
+    5: Workload(5, "27b-gated-greedy", 64, 8, 5120, 151936, 256, "bf16", 1, False, "planted",
+                False, 8, gate=True, walk="greedy"),
 }
 
 
@@ -172,7 +180,7 @@ def to_bf16_bits(a: np.ndarray) -> np.ndarray:
 
 # Tensor tags (stable: changing them changes every workload).
 TAG_X, TAG_ANCHOR_H, TAG_K0, TAG_K1, TAG_PROJ, TAG_W, TAG_U, TAG_V = range(1, 9)
-TAG_ANCHOR_TOK, TAG_TARGET = 9, 10
+TAG_ANCHOR_TOK, TAG_TARGET, TAG_WG = 9, 10, 11
 TAG_CONV_STRIDE = 16  # conv j of a chain uses tags TAG_* + TAG_CONV_STRIDE * j
 
 
@@ -184,6 +192,7 @@ def make_inputs(w: Workload, with_head: bool = True) -> Dict[str, object]:
       convs    list of n_convs dicts {anchor_h [B,H], k0 [H], k1 [H], proj [H,2] or None}
       W        [V, H]      LM-head weight (omitted when with_head is False)
       U, Vf    [V, r]      low-rank pair factors (omitted when with_head is False)
+      Wg       [r, H]      context-gate map, N(0, 1/H) (gated workloads only)
       anchor_tok [B]       last verified token id of each block
     Activation and weight tensors are bf16 bits or fp32 according to w.dtype.
     """
@@ -224,6 +233,9 @@ def make_inputs(w: Workload, with_head: bool = True) -> Dict[str, object]:
         if bf16:
             Wv, Uv, Vv = to_bf16_bits(Wv), to_bf16_bits(Uv), to_bf16_bits(Vv)
         out["W"], out["U"], out["Vf"] = Wv, Uv, Vv
+        if w.gate:
+            Wg = normal_f32((r, H), 1.0 / H, s, TAG_WG)
+            out["Wg"] = to_bf16_bits(Wg) if bf16 else Wg
     out["anchor_tok"] = _rng(s, TAG_ANCHOR_TOK).integers(0, V, size=B, dtype=np.int32)
     return out
 
