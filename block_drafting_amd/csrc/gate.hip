@@ -6,12 +6,14 @@
 //   gate[m, k] = sigmoid( sum_c h[m, c] * Wg[k, c] ),   Wg [r, H] (K-contiguous).
 //
 // bf16: a [M x H] x [H x r] product with r <= 256 is far too narrow for the
-// LM-head tiling, so each workgroup owns one 32 x 32 output tile and splits
-// the K range over its eight waves.  A wave multiplies straight from global
-// memory (its operand fragment per k-step is one 16-byte run of a row, the
-// whole tile's rows stay hot in L2 across the workgroups that share them),
-// then the eight partial tiles are added in LDS in wave order, so the result
-// does not depend on timing.
+// LM-head tiling, so each workgroup owns one 32 x 32 output tile and walks
+// the whole K range.  The operand rows are staged through LDS in K slices:
+// every 16-byte load of a slice belongs to a run of 16 threads reading 256
+// contiguous bytes of one row, so each cache line is fetched whole (matrix
+// fragments gathered straight from global memory touch 32 rows per
+// instruction and run at a fraction of the L2 bandwidth).  The four waves
+// take alternate k-steps of each slice; their partial tiles are added in LDS
+// in wave order, so the result does not depend on timing.
 #include "common.hpp"
 
 namespace dflash2 {
@@ -19,58 +21,95 @@ namespace {
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-constexpr int kGateWaves = 8;
-constexpr int kGateBatch = 4;  // k-steps whose loads are issued together
+constexpr int kGateWaves = 4;
+constexpr int kGateBK = 128;                    // k per LDS slice
+constexpr int kGateLd = kGateBK + 8;            // padded LDS row (bf16)
+constexpr int kGateCpr = kGateBK / 8;           // 16-byte chunks per row slice
+constexpr int kGateRowsPerPass = 64 * kGateWaves / kGateCpr;  // 16
+constexpr int kGatePasses = 32 / kGateRowsPerPass;            // 2 per operand
 
 __global__ __launch_bounds__(64 * kGateWaves) void gate_bf16_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ Wg, float* __restrict__ gate,
     int M, int H, int r) {
+  __shared__ __attribute__((aligned(16))) uint16_t stage[2][2][32 * kGateLd];  // [buf][A/B]
   __shared__ float part[kGateWaves][16][64];
   const int m0 = blockIdx.x * 32;
   const int n0 = blockIdx.y * 32;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  // Lane l supplies row l % 32 of each 32-row operand and k values
-  // 8 * (l / 32) .. +7 of each 16-wide k-step.  Rows past the edge repeat the
-  // last row (their results are never stored).
   const int rowsA = min(32, M - m0);
   const int rowsB = min(32, r - n0);
-  const int ra = min(lane & 31, rowsA - 1);
-  const int rb = min(lane & 31, rowsB - 1);
-  const int kof = (lane >> 5) * 8;
+  // Loader role: rows (tid / kGateCpr) + 16 p of each operand, chunk tid % kGateCpr.
+  // Rows past the edge repeat the last row (their results are never stored).
+  const int lrow = tid / kGateCpr;
+  const int lk = (tid % kGateCpr) * 8;
   const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(h + (size_t)m0 * H), (short)0, rowsA * H * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Wg + (size_t)n0 * H), (short)0, rowsB * H * 2, 0x00020000);
-  const int offA = (ra * H + kof) * 2;
-  const int offB = (rb * H + kof) * 2;
+  int offA[kGatePasses], offB[kGatePasses];
+#pragma unroll
+  for (int p = 0; p < kGatePasses; ++p) {
+    offA[p] = (min(lrow + p * kGateRowsPerPass, rowsA - 1) * H + lk) * 2;
+    offB[p] = (min(lrow + p * kGateRowsPerPass, rowsB - 1) * H + lk) * 2;
+  }
+  const int nslices = (H + kGateBK - 1) / kGateBK;
+  // Two register staging sets keep two slices of loads in flight while the
+  // one before them is multiplied.  Slices past the end re-read the last
+  // slice (in range, never used).
+  u32x4_t R0[2 * kGatePasses], R1[2 * kGatePasses];
+  auto gload = [&](u32x4_t(&R)[2 * kGatePasses], int sl) {
+    const int k = min(sl, nslices - 1) * kGateBK;
+    const bool in = k + lk < H;  // H % 8 == 0: a chunk is wholly inside or outside
+    const u32x4_t z = {0, 0, 0, 0};
+#pragma unroll
+    for (int p = 0; p < kGatePasses; ++p) {
+      const u32x4_t va = __builtin_amdgcn_raw_buffer_load_b128(rsA, offA[p] + k * 2, 0, 0);
+      const u32x4_t vb = __builtin_amdgcn_raw_buffer_load_b128(rsB, offB[p] + k * 2, 0, 0);
+      R[p] = in ? va : z;
+      R[kGatePasses + p] = in ? vb : z;
+    }
+  };
+  auto sstore = [&](const u32x4_t(&R)[2 * kGatePasses], int buf) {
+#pragma unroll
+    for (int p = 0; p < kGatePasses; ++p) {
+      const int at = (lrow + p * kGateRowsPerPass) * kGateLd + lk;
+      *reinterpret_cast<u32x4_t*>(&stage[buf][0][at]) = R[p];
+      *reinterpret_cast<u32x4_t*>(&stage[buf][1][at]) = R[kGatePasses + p];
+    }
+  };
 
-  const int ksteps = (H + 15) / 16;
-  const int per = (ksteps + kGateWaves - 1) / kGateWaves;
-  const int ks0 = min(ksteps, wave * per);
-  const int ks1 = min(ksteps, ks0 + per);
   f32x16_t acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  for (int ks = ks0; ks < ks1; ks += kGateBatch) {
-    u32x4_t a[kGateBatch], b[kGateBatch];
+  // MFMA fragment of lane l: row l % 32, k values 8 (l / 32) .. +7 of a k-step.
+  const int frag = (lane & 31) * kGateLd + (lane >> 5) * 8;
+  auto multiply = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < kGateBatch; ++u) {
-      // steps past ks1 re-read step ks (in range) and are discarded below
-      const int kk = ks + u < ks1 ? ks + u : ks;
-      a[u] = __builtin_amdgcn_raw_buffer_load_b128(rsA, offA + kk * 32, 0, 0);
-      b[u] = __builtin_amdgcn_raw_buffer_load_b128(rsB, offB + kk * 32, 0, 0);
+    for (int j = 0; j < kGateBK / 16 / kGateWaves; ++j) {
+      const int ks = wave + j * kGateWaves;
+      const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(&stage[buf][0][frag + ks * 16]);
+      const bf16x8_t fb = *reinterpret_cast<const bf16x8_t*>(&stage[buf][1][frag + ks * 16]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc, 0, 0, 0);
     }
-#pragma unroll
-    for (int u = 0; u < kGateBatch; ++u) {
-      // H % 16 == 8 leaves the upper half of the last k-step past the row end
-      const bool live = ks + u < ks1 && (ks + u) * 16 + kof < H;
-      const u32x4_t z = {0, 0, 0, 0};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          __builtin_bit_cast(bf16x8_t, live ? a[u] : z),
-          __builtin_bit_cast(bf16x8_t, live ? b[u] : z), acc, 0, 0, 0);
-    }
+  };
+  gload(R0, 0);
+  gload(R1, 1);
+  sstore(R0, 0);
+  __syncthreads();
+  // Slice sl sits in LDS buffer sl & 1; the set that carried it reloads
+  // slice sl + 2, the other set (slice sl + 1) is stored after the MFMAs.
+  for (int sl = 0; sl < nslices; sl += 2) {
+    gload(R0, sl + 2);
+    multiply(0);
+    sstore(R1, 1);
+    __syncthreads();
+    if (sl + 1 >= nslices) break;
+    gload(R1, sl + 3);
+    multiply(1);
+    sstore(R0, 0);
+    __syncthreads();
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) part[wave][i][lane] = acc[i];

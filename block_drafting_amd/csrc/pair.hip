@@ -4,87 +4,86 @@
 // with the last verified token as the previous token of position 0.  g_t is
 // the context gate of position t (an r-vector); without one it is all ones.
 //
-// One wavefront per (block, position): it gathers the 16 (or 1) previous
-// factor rows and the 16 current factor rows into LDS as fp32, then each lane
-// produces four neighbouring outputs (one 16-byte store).  All pairs of all
-// positions are independent, so the whole tensor is scored in one launch.
+// One wavefront per (block, position) computes the whole 16 x 16 match
+// matrix as one fp32 matrix-core product, [16 x r] x [r x 16], with
+// v_mfma_f32_16x16x4f32.  The four k-rows of each MFMA step are four
+// contiguous quarters of the rank: lane l = 16 q + i feeds row i of the
+// previous-token factors and column i of the candidate factors with the
+// elements k = q * rc + s (rc = ceil(r / 4)) at step s, so every lane
+// gathers one contiguous run of each factor row straight into registers
+// (16-byte loads, all in flight at once) and no LDS is needed.  Products and
+// sums are fp32, as in a plain fp32 dot.
 #include "common.hpp"
 
 namespace dflash2 {
 namespace {
 
-template <typename T>
-__device__ __forceinline__ float widen(T v);
-template <>
-__device__ __forceinline__ float widen<float>(float v) { return v; }
-template <>
-__device__ __forceinline__ float widen<uint16_t>(uint16_t v) {
-  return __uint_as_float((uint32_t)v << 16);
-}
-
-// Gather `rows` factor rows (ids[0..rows)) of rank r into lds (stride r+1).
-// Ids outside [0, V) fill their row with NaN.  When a row is a whole number
-// of 16-byte runs (VEC), every lane issues all of its runs before using any,
-// so the wave pays one memory latency for the random rows instead of one per
-// element.
-template <typename T, bool VEC>
-__device__ void gather_rows(const T* __restrict__ F, const int32_t* ids, int rows, int r, int V,
-                            float* lds) {
-  const int lane = threadIdx.x;
-  if (VEC) {
-    constexpr int kPer = 16 / sizeof(T);        // elements per 16-byte run
-    constexpr int kMaxRuns = 16 * 256 / kPer / 64;  // runs per lane at r = 256
-    const int cpr = r / kPer;                    // runs per row
-    const int total = rows * cpr;
-    u32x4_t buf[kMaxRuns];
-    int rowof[kMaxRuns];
-#pragma unroll
-    for (int q = 0; q < kMaxRuns; ++q) {
-      const int e = lane + q * 64;
-      rowof[q] = -1;
-      if (e < total) {
-        const int row = e / cpr;
-        const int id = ids[row];
-        if (id >= 0 && id < V) {
-          buf[q] = *reinterpret_cast<const u32x4_t*>(F + (size_t)id * r + (e - row * cpr) * kPer);
-          rowof[q] = row;
-        } else {
-          rowof[q] = -2 - row;
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < kMaxRuns; ++q) {
-      const int e = lane + q * 64;
-      if (e >= total) continue;
-      const int row = rowof[q] >= 0 ? rowof[q] : -2 - rowof[q];
-      float* dst = lds + row * (r + 1) + (e - row * cpr) * kPer;
-      if (rowof[q] < 0) {
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) dst[k] = __builtin_nanf("");
-      } else if (sizeof(T) == 2) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          dst[2 * k] = bf16_lo(buf[q][k]);
-          dst[2 * k + 1] = bf16_hi(buf[q][k]);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) dst[k] = __uint_as_float(buf[q][k]);
-      }
-    }
-    return;
+// Raw storage of RC consecutive elements of one factor row.
+template <typename T, int RC>
+struct Chunk;
+template <int RC>
+struct Chunk<uint16_t, RC> {
+  static constexpr int kRuns = RC / 8;  // 16-byte runs of 8 bf16
+  u32x4_t w[kRuns];
+  __device__ __forceinline__ float get(int k) const {
+    const uint32_t v = w[k >> 3][(k >> 1) & 3];
+    return (k & 1) ? bf16_hi(v) : bf16_lo(v);
   }
-  for (int e = lane; e < rows * r; e += 64) {
-    const int row = e / r;
-    const int k = e - row * r;
-    const int id = ids[row];
-    lds[row * (r + 1) + k] =
-        (id >= 0 && id < V) ? widen<T>(F[(size_t)id * r + k]) : __builtin_nanf("");
+};
+template <int RC>
+struct Chunk<float, RC> {
+  static constexpr int kRuns = RC / 4;  // 16-byte runs of 4 fp32
+  u32x4_t w[kRuns];
+  __device__ __forceinline__ float get(int k) const { return __uint_as_float(w[k >> 2][k & 3]); }
+};
+
+// Elements [k0, k0 + n) of row `id` of F [V, r] (n <= RC); elements past n
+// read as 0.  An id outside [0, V) gives a NaN row; `zero` gives a zero row.
+// VEC: the run start k0 and n are whole 16-byte runs and rows are 16-byte
+// aligned, so each run is one vector load; else element by element.
+template <typename T, int RC, bool VEC>
+__device__ __forceinline__ void load_chunk(Chunk<T, RC>& c, const T* __restrict__ F, int id, int V,
+                                           int r, int k0, int n, bool zero) {
+  constexpr int kPer = 16 / sizeof(T);
+  const bool bad = !zero && (id < 0 || id >= V);
+  const bool live = !zero && !bad;
+  const T* row = F + (size_t)(live ? id : 0) * r + k0;
+  const uint32_t nan_bits = sizeof(T) == 2 ? 0x7fc0u : 0x7fc00000u;
+#pragma unroll
+  for (int q = 0; q < Chunk<T, RC>::kRuns; ++q) {
+    const int k = q * kPer;
+    if (VEC) {
+      const uint32_t f = sizeof(T) == 2 ? (nan_bits | nan_bits << 16) : nan_bits;
+      if (live && k < n)
+        c.w[q] = *reinterpret_cast<const u32x4_t*>(row + k);
+      else if (bad && k < n)
+        c.w[q] = u32x4_t{f, f, f, f};
+      else
+        c.w[q] = u32x4_t{0u, 0u, 0u, 0u};
+    } else {
+      uint32_t v[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        uint32_t bits = 0u;
+        if (k + e < n) {
+          if (bad)
+            bits = nan_bits;
+          else if (live)
+            bits = sizeof(T) == 2 ? (uint32_t)reinterpret_cast<const uint16_t*>(row)[k + e]
+                                  : __float_as_uint(reinterpret_cast<const float*>(row)[k + e]);
+        }
+        if (sizeof(T) == 2)
+          v[e >> 1] |= bits << (16 * (e & 1));
+        else
+          v[e] = bits;
+      }
+      c.w[q] = u32x4_t{v[0], v[1], v[2], v[3]};
+    }
   }
 }
 
-template <typename T, bool VEC>
+// RC: the most elements one lane holds per factor row (>= ceil(r / 4)).
+template <typename T, int RC, bool VEC>
 __global__ __launch_bounds__(64) void pair_score_kernel(const float* __restrict__ top_val,
                                                         const int32_t* __restrict__ top_idx,
                                                         const int32_t* __restrict__ anchor_tok,
@@ -93,65 +92,99 @@ __global__ __launch_bounds__(64) void pair_score_kernel(const float* __restrict_
                                                         const float* __restrict__ gate, int L,
                                                         int V, int r, float* __restrict__ S0,
                                                         float* __restrict__ S) {
-  extern __shared__ float lds[];
   const int b = blockIdx.x / L;
   const int t = blockIdx.x - b * L;
   const int lane = threadIdx.x;
-  const int stride = r + 1;
-  float* su = lds;                 // previous-token factors, up to 16 rows
-  float* sv = lds + 16 * stride;   // current-candidate factors, 16 rows
-  const int32_t* cur = top_idx + ((size_t)b * L + t) * kTopK;
-  const float* tv = top_val + ((size_t)b * L + t) * kTopK;
+  const int i = lane & 15;  // row of the previous factors / column of the current ones
+  const int q = lane >> 4;  // quarter of the rank this lane feeds
+  const int rc = (r + 3) >> 2;
+  const int k0 = q * rc;
+  const int n = min(rc, r - k0);  // may be <= 0 for tiny r: then all padding
+  const size_t bt = (size_t)b * L + t;
+  const int32_t* cur = top_idx + bt * kTopK;
 
-  float* sg = lds + 32 * stride;   // gate of this position
-  if (gate) {
-    const float* g = gate + ((size_t)b * L + t) * r;
-    for (int k = lane; k < r; k += 64) sg[k] = g[k];
-  }
-  gather_rows<T, VEC>(Vf, cur, kTopK, r, V, sv);
+  int prev_id = 0;
+  bool prev_zero = false;
   if (t == 0) {
-    if (anchor_tok) gather_rows<T, VEC>(U, anchor_tok + b, 1, r, V, su);
-    __syncthreads();
-    if (gate && anchor_tok) {
-      for (int k = lane; k < r; k += 64) su[k] *= sg[k];
-      __syncthreads();
-    }
-    if (lane < kTopK) {
-      float acc = 0.f;
-      if (anchor_tok) {
-        for (int k = 0; k < r; ++k) acc = fmaf(su[k], sv[lane * stride + k], acc);
-      } else if (cur[lane] < 0 || cur[lane] >= V) {
-        acc = __builtin_nanf("");
+    prev_zero = anchor_tok == nullptr;       // no match term at t = 0
+    if (!prev_zero) prev_id = anchor_tok[b];  // the same row for all 16 i
+  } else {
+    prev_id = cur[i - kTopK];
+  }
+  Chunk<T, RC> cu, cv;
+  load_chunk<T, RC, VEC>(cu, U, prev_id, V, r, k0, n, prev_zero);
+  load_chunk<T, RC, VEC>(cv, Vf, cur[i], V, r, k0, n, false);
+  float g[RC];
+  if (gate) {
+    const float* gr = gate + bt * r + k0;
+#pragma unroll
+    for (int s = 0; s < RC; s += 4) {
+      if (VEC && s < n) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(gr + s);
+        g[s] = v[0];
+        g[s + 1] = v[1];
+        g[s + 2] = v[2];
+        g[s + 3] = v[3];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) g[s + e] = (!VEC && s + e < n) ? gr[s + e] : 1.0f;
       }
-      S0[(size_t)b * kTopK + lane] = tv[lane] + acc;
     }
+  }
+  const float tv = top_val[bt * kTopK + i];
+
+  // C[i][j] = sum_k A[i][k] B[k][j]; two accumulators alternate so that
+  // consecutive steps do not wait on each other.
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < RC; ++s) {
+    float a = cu.get(s);
+    if (gate) a *= g[s];
+    const float bb = cv.get(s);
+    if (s & 1)
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc1, 0, 0, 0);
+    else
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc0, 0, 0, 0);
+  }
+  // Lane l holds C[4 (l / 16) + e][l % 16] in element e: column j = i, whose
+  // own logit this lane already holds.
+  if (t == 0) {
+    if (q == 0) S0[(size_t)b * kTopK + i] = tv + (acc0[0] + acc1[0]);
     return;
   }
-  gather_rows<T, VEC>(U, cur - kTopK, kTopK, r, V, su);
-  __syncthreads();
-  if (gate) {
-    // A(a) (.) H(h_t): scale the previous-token rows once, before the dots
-    for (int e = lane; e < kTopK * r; e += 64) {
-      const int i = e / r;
-      const int k = e - i * r;
-      su[i * stride + k] *= sg[k];
-    }
-    __syncthreads();
-  }
-  const int i = lane >> 2;
-  const int j0 = (lane & 3) * 4;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  const float* ui = su + i * stride;
-  for (int k = 0; k < r; ++k) {
-    const float u = ui[k];
+  float* dst = S + ((size_t)b * (L - 1) + (t - 1)) * kTopK * kTopK;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = fmaf(u, sv[(j0 + q) * stride + k], acc[q]);
-  }
-  f32x4_t out;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) out[q] = tv[j0 + q] + acc[q];
-  float* dst = S + (((size_t)b * (L - 1) + (t - 1)) * kTopK + i) * kTopK + j0;
-  *reinterpret_cast<f32x4_t*>(dst) = out;
+  for (int e = 0; e < 4; ++e) dst[(4 * q + e) * kTopK + i] = tv + (acc0[e] + acc1[e]);
+}
+
+template <typename T, int RC>
+void launch_rc(bool vec, dim3 grid, hipStream_t s, const float* top_val, const int32_t* top_idx,
+               const int32_t* anchor_tok, const void* U, const void* Vf, const float* gate, int L,
+               int V, int r, float* S0, float* S) {
+  const T* u = static_cast<const T*>(U);
+  const T* v = static_cast<const T*>(Vf);
+  if (vec)
+    hipLaunchKernelGGL((pair_score_kernel<T, RC, true>), grid, dim3(64), 0, s, top_val, top_idx,
+                       anchor_tok, u, v, gate, L, V, r, S0, S);
+  else
+    hipLaunchKernelGGL((pair_score_kernel<T, RC, false>), grid, dim3(64), 0, s, top_val, top_idx,
+                       anchor_tok, u, v, gate, L, V, r, S0, S);
+}
+
+template <typename T>
+void launch_t(bool vec, dim3 grid, hipStream_t s, const float* top_val, const int32_t* top_idx,
+              const int32_t* anchor_tok, const void* U, const void* Vf, const float* gate, int L,
+              int V, int r, float* S0, float* S) {
+  const int rc = (r + 3) / 4;
+  if (rc <= 8)
+    launch_rc<T, 8>(vec, grid, s, top_val, top_idx, anchor_tok, U, Vf, gate, L, V, r, S0, S);
+  else if (rc <= 16)
+    launch_rc<T, 16>(vec, grid, s, top_val, top_idx, anchor_tok, U, Vf, gate, L, V, r, S0, S);
+  else if (rc <= 32)
+    launch_rc<T, 32>(vec, grid, s, top_val, top_idx, anchor_tok, U, Vf, gate, L, V, r, S0, S);
+  else
+    launch_rc<T, 64>(vec, grid, s, top_val, top_idx, anchor_tok, U, Vf, gate, L, V, r, S0, S);
 }
 
 }  // namespace
@@ -161,26 +194,18 @@ hipError_t launch_pair_score(const float* top_val, const int32_t* top_idx,
                              const float* gate, int B, int L, int V, int r, int dtype, float* S0,
                              float* S, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  const size_t lds = ((size_t)2 * kTopK * (r + 1) + (gate ? r : 0)) * sizeof(float);
   const dim3 grid((unsigned)((long long)B * L));
-  const bool vec_bf16 = r % 8 == 0 && ((reinterpret_cast<uintptr_t>(U) | reinterpret_cast<uintptr_t>(Vf)) & 15) == 0;
-  const bool vec_f32 = r % 4 == 0 && ((reinterpret_cast<uintptr_t>(U) | reinterpret_cast<uintptr_t>(Vf)) & 15) == 0;
-  const uint16_t* Ub = static_cast<const uint16_t*>(U);
-  const uint16_t* Vb = static_cast<const uint16_t*>(Vf);
-  const float* Uf = static_cast<const float*>(U);
-  const float* Vff = static_cast<const float*>(Vf);
-  if (dtype == 1 && vec_bf16)
-    hipLaunchKernelGGL((pair_score_kernel<uint16_t, true>), grid, dim3(64), lds, s, top_val, top_idx,
-                       anchor_tok, Ub, Vb, gate, L, V, r, S0, S);
-  else if (dtype == 1)
-    hipLaunchKernelGGL((pair_score_kernel<uint16_t, false>), grid, dim3(64), lds, s, top_val,
-                       top_idx, anchor_tok, Ub, Vb, gate, L, V, r, S0, S);
-  else if (vec_f32)
-    hipLaunchKernelGGL((pair_score_kernel<float, true>), grid, dim3(64), lds, s, top_val, top_idx,
-                       anchor_tok, Uf, Vff, gate, L, V, r, S0, S);
-  else
-    hipLaunchKernelGGL((pair_score_kernel<float, false>), grid, dim3(64), lds, s, top_val, top_idx,
-                       anchor_tok, Uf, Vff, gate, L, V, r, S0, S);
+  // 16-byte runs: every lane's quarter (r / 4 elements) must be whole runs
+  // and every row, gate row and base 16-byte aligned.
+  const uintptr_t bases = reinterpret_cast<uintptr_t>(U) | reinterpret_cast<uintptr_t>(Vf) |
+                          reinterpret_cast<uintptr_t>(gate);
+  if (dtype == 1) {
+    const bool vec = r % 32 == 0 && (bases & 15) == 0;
+    launch_t<uint16_t>(vec, grid, s, top_val, top_idx, anchor_tok, U, Vf, gate, L, V, r, S0, S);
+  } else {
+    const bool vec = r % 16 == 0 && (bases & 15) == 0;
+    launch_t<float>(vec, grid, s, top_val, top_idx, anchor_tok, U, Vf, gate, L, V, r, S0, S);
+  }
   return hipGetLastError();
 }
 
