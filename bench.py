@@ -40,7 +40,7 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4, 5, 6])
     ap.add_argument("--walk", choices=["viterbi", "greedy"], default=None,
                     help="path walk (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -151,7 +151,8 @@ def main(argv=None):
 
     x = dev(inp["x"], "act")
     convs = [{"k0": dev(c["k0"], "f32"), "k1": dev(c["k1"], "f32"), "anchor_h": dev(c["anchor_h"], "act"),
-              "proj": None if c["proj"] is None else dev(c["proj"], "f32"), "groups": 1}
+              "proj": None if c["proj"] is None else dev(c["proj"], "f32"), "groups": c["groups"],
+              "projT": None if c["projT"] is None else dev(c["projT"], "act")}
              for c in inp["convs"]]
     W = dev(inp["W"], "act")
     U = dev(inp["U"], "act")
@@ -180,7 +181,10 @@ def main(argv=None):
             ev["conv"][i].record()
         for j, c in enumerate(convs):
             out = buf.y[j % len(buf.y)]
-            bd.twotap_conv(cur, c["k0"], c["k1"], c["anchor_h"], c["proj"], 1, out=out)
+            if c["projT"] is not None:
+                bd.twotap_conv_mm(cur, c["k0"], c["k1"], c["projT"], c["anchor_h"], out=out)
+            else:
+                bd.twotap_conv(cur, c["k0"], c["k1"], c["anchor_h"], c["proj"], c["groups"], out=out)
             cur = out
         if i is not None:
             ev["gemm"][i].record()
@@ -243,6 +247,8 @@ def main(argv=None):
     # algorithmic HBM rates of the streaming stages
     es = 2 if bf16 else 4
     conv_bytes = w.n_convs * (2 * L + 1) * B * H * es
+    if w.dynamic and w.groups > 1:
+        conv_bytes += w.n_convs * 2 * w.groups * H * es      # the correction maps
     topk_bytes = M * V * 4
     out = {
         "metric": "draft-select-verify blocks/s at B=64,L=8,V=151936; % MFMA / HBM roofline",
@@ -258,7 +264,8 @@ def main(argv=None):
         "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "L": L, "H": H, "V": V, "r": w.r,
-                   "convs": w.n_convs, "topk": 16, "gate": w.gate, "walk": w.walk},
+                   "convs": w.n_convs, "conv_groups": w.groups if w.dynamic else 0, "topk": 16,
+                   "gate": w.gate, "walk": w.walk},
         "tokens_per_s": round(M / (ms_step * 1e-3), 1),
         "accepted_tokens_per_s": round(float(acc.sum()) / (ms_step * 1e-3), 1),
         "mean_accept_len": round(float(acc.mean()), 3),
@@ -267,6 +274,10 @@ def main(argv=None):
                           "topk": round(topk_bytes / (stage_ms["topk"] * 1e-3) / 1e9, 1)},
         "roofline": roof,
     }
+    if w.dynamic and w.groups > 1:
+        # the per-group corrections are a [M x H] x [H x 2G] product per application
+        conv_flops = w.n_convs * 2.0 * M * H * 2 * w.groups
+        out["stage_tflops"] = {"conv": round(conv_flops / (stage_ms["conv"] * 1e-3) / 1e12, 1)}
     if not a.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {a.cpu_blocks} blocks")
         out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_blocks)

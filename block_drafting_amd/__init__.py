@@ -9,6 +9,8 @@ library every call raises.
 
 The five stages (names as in the C ABI):
   twotap_conv     two-tap local conv around the drafter's sublayers
+                  (twotap_conv_mm: one correction per 16 channels, on the
+                  matrix cores)
   logits_topk     LM-head logits and per-position top-16 candidates
                   (= lmhead_logits then topk16)
   pair_score      16x16 scores of neighbouring candidates (optionally
@@ -26,7 +28,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "DFlash2Error", "lib", "library_path", "twotap_conv", "lmhead_logits", "topk16",
+    "DFlash2Error", "lib", "library_path", "twotap_conv", "twotap_conv_mm", "lmhead_logits", "topk16",
     "topk16_workspace", "logits_topk", "logits_topk_workspace", "context_gate", "pair_score",
     "path_select", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
 ]
@@ -45,6 +47,7 @@ _SIGS = {
     "dflash2_version": ([], _I),
     "dflash2_strerror": ([_I], ctypes.c_char_p),
     "dflash2_twotap_conv": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
+    "dflash2_twotap_conv_mm": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
     "dflash2_lmhead_logits": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "dflash2_topk16_workspace": ([_I, _I, _I], _Z),
     "dflash2_topk16": ([_P, _P, _P, _I, _I, _I, _P, _Z, _P], _I),
@@ -145,6 +148,30 @@ def twotap_conv(x: torch.Tensor, k0: torch.Tensor, k1: torch.Tensor,
     dev = _dev(x, k0, k1, anchor_h, proj, out)
     _check("dflash2_twotap_conv", lib().dflash2_twotap_conv(
         _ptr(x), _ptr(anchor_h), _ptr(out), _ptr(k0), _ptr(k1), _ptr(proj), groups,
+        B, L, H, _dt(x), _stream(dev)))
+    return out
+
+
+def twotap_conv_mm(x: torch.Tensor, k0: torch.Tensor, k1: torch.Tensor, projT: torch.Tensor,
+                   anchor_h: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Two-tap conv with one correction pair per group computed on the matrix
+    cores: projT [2 * groups, H] bf16; see dflash2_twotap_conv_mm."""
+    B, L, H = x.shape
+    if projT.dim() != 2 or projT.shape[1] != H or projT.shape[0] % 2:
+        raise ValueError(f"projT: expected [2 * groups, {H}], got {tuple(projT.shape)}")
+    groups = projT.shape[0] // 2
+    if out is None:
+        out = torch.empty_like(x)
+    _shape(out, x.shape, "out", x.dtype)
+    _shape(k0, (H,), "k0", torch.float32)
+    _shape(k1, (H,), "k1", torch.float32)
+    _shape(projT, (2 * groups, H), "projT", x.dtype)
+    if anchor_h is not None:
+        _shape(anchor_h, (B, H), "anchor_h", x.dtype)
+    dev = _dev(x, k0, k1, anchor_h, projT, out)
+    _check("dflash2_twotap_conv_mm", lib().dflash2_twotap_conv_mm(
+        _ptr(x), _ptr(anchor_h), _ptr(out), _ptr(k0), _ptr(k1), _ptr(projT), groups,
         B, L, H, _dt(x), _stream(dev)))
     return out
 
@@ -350,7 +377,8 @@ def run_step(buf: StepBuffers, x: torch.Tensor, convs, W: torch.Tensor, U: torch
              target: Optional[torch.Tensor], Wg: Optional[torch.Tensor] = None,
              walk: str = "viterbi") -> StepBuffers:
     """One draft-select-verify step: the conv chain (each entry of `convs` is a
-    dict with k0, k1, anchor_h, proj, groups), logits + top-16, pair scores
+    dict with k0, k1, anchor_h and either proj + groups, or projT for the
+    matrix-core corrections), logits + top-16, pair scores
     (context-gated from the final hidden states when `Wg` is given), the path
     walk (`walk`: "viterbi" or "greedy") and, when `target` is given, greedy
     verification.  Every call is enqueued on the current stream; nothing is
@@ -359,8 +387,11 @@ def run_step(buf: StepBuffers, x: torch.Tensor, convs, W: torch.Tensor, U: torch
     cur = x
     for j, c in enumerate(convs):
         out = buf.y[j % len(buf.y)]
-        twotap_conv(cur, c["k0"], c["k1"], c.get("anchor_h"), c.get("proj"), c.get("groups", 1),
-                    out=out)
+        if c.get("projT") is not None:
+            twotap_conv_mm(cur, c["k0"], c["k1"], c["projT"], c.get("anchor_h"), out=out)
+        else:
+            twotap_conv(cur, c["k0"], c["k1"], c.get("anchor_h"), c.get("proj"),
+                        c.get("groups", 1), out=out)
         cur = out
     M = B * L
     logits_topk(cur.view(M, H), W, buf.logits, buf.top_val, buf.top_idx, buf.workspace)

@@ -68,6 +68,29 @@ DFLASH2_API int dflash2_twotap_conv(const void* x, const void* anchor_h, void* y
                                       dtype, as_stream(stream)));
 }
 
+DFLASH2_API int dflash2_twotap_conv_mm(const void* x, const void* anchor_h, void* y,
+                                       const float* k0, const float* k1, const void* projT,
+                                       int groups, int B, int L, int H, int dtype, void* stream) {
+  if (!valid_dtype(dtype) || B < 0 || L < 1 || H < 8 || H % 8 != 0) return DFLASH2_EINVAL;
+  if (groups < 1 || H % groups != 0) return DFLASH2_EINVAL;
+  if ((long long)B * L * H > (1LL << 40)) return DFLASH2_EINVAL;
+  if (dtype != DFLASH2_BF16) return DFLASH2_EUNSUPPORTED;  // matrix cores take bf16 operands
+  if (B == 0) return DFLASH2_OK;
+  if (!x || !y || !k0 || !k1 || !projT) return DFLASH2_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(k0) || !aligned16(k1) || !aligned16(projT))
+    return DFLASH2_EINVAL;
+  if (anchor_h && !aligned16(anchor_h)) return DFLASH2_EINVAL;
+  // 32-bit byte offsets inside a 64-row tile; tile and grid counts in int
+  if (H > (1 << 21) || (long long)B * L > kInt32Max / 2) return DFLASH2_EUNSUPPORTED;
+  const size_t xbytes = (size_t)B * L * H * 2;
+  if (overlap(x, xbytes, y, xbytes) ||
+      (anchor_h && overlap(anchor_h, (size_t)B * H * 2, y, xbytes)) ||
+      overlap(projT, (size_t)2 * groups * H * 2, y, xbytes))
+    return DFLASH2_EINVAL;
+  return status_of(launch_twotap_conv_mm(x, anchor_h, y, k0, k1, projT, groups, B, L, H,
+                                         as_stream(stream)));
+}
+
 namespace {
 int check_lmhead(const void* h, const void* W, int M, int H, int V, int dtype) {
   if (!valid_dtype(dtype) || M < 0 || H < 8 || H % 8 != 0 || V < kTopK) return DFLASH2_EINVAL;

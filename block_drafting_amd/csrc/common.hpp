@@ -28,11 +28,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// Workgroup i of a launch runs on XCD i mod 8, and each XCD has its own L2.
+// Bijection from dispatch order to tile order that gives XCD x a contiguous
+// range of tiles, so tiles that share operand rows share an L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_tile(int pid, int ntiles) {
+  const int xcd = pid % kXcds;
+  const int local = pid / kXcds;
+  const int q = ntiles / kXcds;
+  const int rem = ntiles % kXcds;
+  return xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+}
+
 // ---------------------------------------------------------------- launches
 // Each returns hipSuccess or the launch error; arguments are already valid.
 hipError_t launch_twotap_conv(const void* x, const void* anchor_h, void* y, const float* k0,
                               const float* k1, const float* proj, int groups, int B, int L,
                               int H, int dtype, hipStream_t s);
+
+hipError_t launch_twotap_conv_mm(const void* x, const void* anchor_h, void* y, const float* k0,
+                                 const float* k1, const void* projT, int groups, int B, int L,
+                                 int H, hipStream_t s);
 
 hipError_t launch_lmhead(const void* h, const void* W, float* logits, int M, int H, int V,
                          int dtype, hipStream_t s);

@@ -3,7 +3,8 @@
 //   y_t = (k0 + D_t[g,0]) * x_t + (k1 + D_t[g,1]) * x_{t-1},  x_{-1} = anchor,
 //   D_t[g,j] = x_t . proj[:, 2g+j].
 // HBM-bound elementwise work: every thread moves 16-byte vectors (8 bf16 or
-// 4+4 fp32 channels); the correction needs a row reduction first.
+// 4+4 fp32 channels); the correction needs a row reduction first, or, with
+// one correction per 16 channels, a matrix product (conv_mm_kernel).
 //
 // Arithmetic is fp64 (taps, corrections, products and the sum), then one
 // rounding to the storage type: fp64 -> fp32 by round-to-odd, then fp32 ->
@@ -230,6 +231,154 @@ __global__ __launch_bounds__(256) void conv_dyng_kernel(const T* __restrict__ x,
   }
 }
 
+// ---------------------------------------------------------------- corrections on the matrix cores
+// The post's coefficients carry one correction pair per 16 channels, so the
+// correction of a whole batch is a real product D = X . P^T, [M x H] by
+// [H x 2G] (2G = H/8 at G = H/16, 13.4 GFLOP per application at 2048 rows of
+// 5120).  One workgroup owns a 64-row x 64-column tile of D (32 groups) and
+// then applies the conv to exactly the channels of those groups for its
+// rows, so D never leaves the chip.
+//
+// Product: bf16 x and P^T (both K-contiguous), v_mfma_f32_32x32x16_bf16,
+// fp32 accumulation; each of the four waves owns a 32 x 32 quarter of the
+// tile.  K is staged through LDS in 128-wide slices, every 16-byte load part
+// of a run of 16 threads reading 256 contiguous bytes of a row, with two
+// register staging sets keeping two slices in flight.  Mix: fp64 from the
+// fp32 corrections, rounded once as in the kernels above.
+constexpr int kMmBM = 64;
+constexpr int kMmBN = 64;
+constexpr int kMmBK = 128;
+constexpr int kMmLd = kMmBK + 8;                    // padded LDS row (bf16)
+constexpr int kMmCpr = kMmBK / 8;                   // 16-byte chunks per row slice
+constexpr int kMmRowsPerPass = 256 / kMmCpr;        // 16
+constexpr int kMmPasses = kMmBM / kMmRowsPerPass;   // 4 per operand
+constexpr int kMmLoads = 2 * kMmPasses;
+constexpr int kMmDLd = kMmBN + 1;                   // fp32 D tile pitch
+static_assert(kMmBM == kMmBN, "one loader layout serves both operands");
+static_assert(kMmBM * kMmDLd * 4 <= 2 * 2 * kMmBM * kMmLd * 2, "D tile fits in the stages");
+
+__global__ __launch_bounds__(256) void conv_mm_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ anchor,
+    uint16_t* __restrict__ y, const float* __restrict__ k0, const float* __restrict__ k1,
+    const uint16_t* __restrict__ pt, int M, int N, int H, int L, int gw, int mtiles,
+    int ntiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t stage[2][2][kMmBM * kMmLd];  // [buf][x/P]
+  // Tiles that share x rows run on one XCD: n fastest.
+  const int tile = xcd_tile(blockIdx.x, mtiles * ntiles);
+  const int mt = tile / ntiles;
+  const int nt = tile - mt * ntiles;
+  const int m0 = mt * kMmBM;
+  const int n0 = nt * kMmBN;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rowsA = min(kMmBM, M - m0);
+  const int rowsB = min(kMmBN, N - n0);
+  // Loader role: rows (tid / kMmCpr) + 16 p of each operand, chunk tid % kMmCpr.
+  // Rows past the edge repeat the last row (their results are never used).
+  const int lrow = tid / kMmCpr;
+  const int lk = (tid % kMmCpr) * 8;
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x + (size_t)m0 * H), (short)0, rowsA * H * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(pt + (size_t)n0 * H), (short)0, rowsB * H * 2, 0x00020000);
+  int offA[kMmPasses], offB[kMmPasses];
+#pragma unroll
+  for (int p = 0; p < kMmPasses; ++p) {
+    offA[p] = (min(lrow + p * kMmRowsPerPass, rowsA - 1) * H + lk) * 2;
+    offB[p] = (min(lrow + p * kMmRowsPerPass, rowsB - 1) * H + lk) * 2;
+  }
+  const int nslices = (H + kMmBK - 1) / kMmBK;
+  // Slices past the end re-read the last slice (in range, never used).
+  u32x4_t R0[kMmLoads], R1[kMmLoads];
+  auto gload = [&](u32x4_t(&R)[kMmLoads], int sl) {
+    const int k = min(sl, nslices - 1) * kMmBK;
+    const bool in = k + lk < H;  // H % 8 == 0: a chunk is wholly inside or outside
+    const u32x4_t z = {0, 0, 0, 0};
+#pragma unroll
+    for (int p = 0; p < kMmPasses; ++p) {
+      const u32x4_t va = __builtin_amdgcn_raw_buffer_load_b128(rsA, offA[p] + k * 2, 0, 0);
+      const u32x4_t vb = __builtin_amdgcn_raw_buffer_load_b128(rsB, offB[p] + k * 2, 0, 0);
+      R[p] = in ? va : z;
+      R[kMmPasses + p] = in ? vb : z;
+    }
+  };
+  auto sstore = [&](const u32x4_t(&R)[kMmLoads], int buf) {
+#pragma unroll
+    for (int p = 0; p < kMmPasses; ++p) {
+      const int at = (lrow + p * kMmRowsPerPass) * kMmLd + lk;
+      *reinterpret_cast<u32x4_t*>(&stage[buf][0][at]) = R[p];
+      *reinterpret_cast<u32x4_t*>(&stage[buf][1][at]) = R[kMmPasses + p];
+    }
+  };
+  f32x16_t acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  // Wave (wm, wn) owns rows 32 wm.. and columns 32 wn.. of the tile; lane l
+  // supplies fragment row l % 32 and k values 8 (l / 32) .. +7 of a k-step.
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+  const int fa = (wm * 32 + (lane & 31)) * kMmLd + (lane >> 5) * 8;
+  const int fb = (wn * 32 + (lane & 31)) * kMmLd + (lane >> 5) * 8;
+  auto multiply = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < kMmBK / 16; ++ks) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&stage[buf][0][fa + ks * 16]);
+      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(&stage[buf][1][fb + ks * 16]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
+  };
+  gload(R0, 0);
+  gload(R1, 1);
+  sstore(R0, 0);
+  __syncthreads();
+  // Slice sl sits in LDS buffer sl & 1; the set that carried it reloads
+  // slice sl + 2, the other set (slice sl + 1) is stored after the MFMAs.
+  for (int sl = 0; sl < nslices; sl += 2) {
+    gload(R0, sl + 2);
+    multiply(0);
+    sstore(R1, 1);
+    __syncthreads();
+    if (sl + 1 >= nslices) break;
+    gload(R1, sl + 3);
+    multiply(1);
+    sstore(R0, 0);
+    __syncthreads();
+  }
+  // D tile to LDS (over the stages, which are free now): accumulator
+  // register r of lane l holds C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+  float* dt = reinterpret_cast<float*>(&stage[0][0][0]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    dt[row * kMmDLd + wn * 32 + (lane & 31)] = acc[r];
+  }
+  __syncthreads();
+  // Mix the channels of this tile's groups for its rows.
+  const int g0 = n0 >> 1;
+  const int c0 = g0 * gw;
+  const int c1 = min(N >> 1, g0 + kMmBN / 2) * gw;
+  const int nvec = (c1 - c0) >> 3;
+  for (int e = tid; e < rowsA * nvec; e += 256) {
+    const int row = e / nvec;
+    const int c = c0 + (e - row * nvec) * 8;
+    const int m = m0 + row;
+    const int t = m % L;
+    const uint16_t* xp = x + (size_t)m * H + c;
+    const uint16_t* pp = t > 0 ? xp - H : (anchor ? anchor + (size_t)(m / L) * H + c : nullptr);
+    double a0[8], a1[8];
+    load_f32x8(k0 + c, a0);
+    load_f32x8(k1 + c, a1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int col = 2 * ((c + i) / gw - g0);
+      a0[i] += (double)dt[row * kMmDLd + col];
+      a1[i] += (double)dt[row * kMmDLd + col + 1];
+    }
+    mix8<uint16_t>(xp, pp, y + (size_t)m * H + c, a0, a1);
+  }
+}
+
 template <typename T>
 hipError_t launch_typed(const void* x, const void* anchor_h, void* y, const float* k0,
                         const float* k1, const float* proj, int groups, int B, int L, int H,
@@ -256,6 +405,20 @@ hipError_t launch_typed(const void* x, const void* anchor_h, void* y, const floa
 }
 
 }  // namespace
+
+hipError_t launch_twotap_conv_mm(const void* x, const void* anchor_h, void* y, const float* k0,
+                                 const float* k1, const void* projT, int groups, int B, int L,
+                                 int H, hipStream_t s) {
+  const int M = B * L;
+  const int N = 2 * groups;
+  const int mtiles = (M + kMmBM - 1) / kMmBM;
+  const int ntiles = (N + kMmBN - 1) / kMmBN;
+  hipLaunchKernelGGL(conv_mm_kernel, dim3((unsigned)(mtiles * ntiles)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(anchor_h),
+                     static_cast<uint16_t*>(y), k0, k1, static_cast<const uint16_t*>(projT), M, N,
+                     H, L, H / groups, mtiles, ntiles);
+  return hipGetLastError();
+}
 
 hipError_t launch_twotap_conv(const void* x, const void* anchor_h, void* y, const float* k0,
                               const float* k1, const float* proj, int groups, int B, int L,

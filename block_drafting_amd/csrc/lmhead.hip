@@ -20,18 +20,6 @@
 namespace dflash2 {
 namespace {
 
-constexpr int kXcds = 8;
-
-// Bijection from dispatch order to tile order: XCD x gets a contiguous range
-// of tiles.
-__device__ __forceinline__ int xcd_tile(int pid, int ntiles) {
-  const int xcd = pid % kXcds;
-  const int local = pid / kXcds;
-  const int q = ntiles / kXcds;
-  const int rem = ntiles % kXcds;
-  return xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
-}
-
 template <int BM, int BN, int BK, int WM, int WN>
 struct GemmCfg {
   static constexpr int kThreads = WM * WN * 64;

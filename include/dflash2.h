@@ -9,7 +9,8 @@
  *   4. max-plus path walk            dflash2_path_select
  *   5. greedy verification           dflash2_verify_greedy
  *
- * Variants of steps 3 and 4 that follow the pages more literally:
+ * Variants that follow the pages more literally:
+ *   per-16-channel conv corrections  dflash2_twotap_conv_mm
  *   context-gated pair scores        dflash2_context_gate, dflash2_pair_score_gated
  *   best-successor (greedy) walk     dflash2_path_select_mode(..., DFLASH2_PATH_GREEDY, ...)
  *
@@ -87,6 +88,25 @@ int dflash2_twotap_conv(const void* x, const void* anchor_h, void* y,
                         const float* k0, const float* k1,
                         const float* proj, int groups,
                         int B, int L, int H, int dtype, void* stream);
+
+/*
+ * Two-tap conv with the corrections on the matrix cores, for many groups.
+ * [POST] "A lightweight local convolution": each coefficient is a base tap
+ * plus a small correction from the current hidden state, one correction
+ * shared by every 16 channels (groups = H / 16).  At that width the
+ * corrections of a batch are a matrix product, so the map is given
+ * transposed, in bf16, like a weight matrix:
+ *   D[b,t,g,j] = sum_c x[b,t,c] * projT[2g+j, c]
+ * and y is dflash2_twotap_conv's formula with these D.
+ * projT [2*groups, H] bf16; groups >= 1 divides H; dtype must be
+ * DFLASH2_BF16 (DFLASH2_F32 returns DFLASH2_EUNSUPPORTED).  Other arguments
+ * as for dflash2_twotap_conv; y must not overlap x, anchor_h or projT.
+ * D is accumulated in fp32 from the exact bf16 products; the mix is
+ * evaluated in fp64 from it and rounded once to bf16.
+ */
+int dflash2_twotap_conv_mm(const void* x, const void* anchor_h, void* y,
+                           const float* k0, const float* k1, const void* projT, int groups,
+                           int B, int L, int H, int dtype, void* stream);
 
 /*
  * LM-head logits: logits[m, n] = sum_c h[m, c] * W[n, c]  (fp32 accumulate).

@@ -410,9 +410,15 @@ def run_step_front(w, inp: Dict[str, object], blocks: Optional[np.ndarray] = Non
     xd = as_f64(x, w.dtype)
     cd = []
     for c in convs:
+        if c.get("projT") is not None:          # [2G, H] storage -> [H, 2G] map
+            proj = as_f64(c["projT"], w.dtype).T
+        elif c["proj"] is not None:
+            proj = np.asarray(c["proj"], np.float64)
+        else:
+            proj = None
         cd.append({"anchor_h": as_f64(c["anchor_h"], w.dtype),
                    "k0": np.asarray(c["k0"], np.float64), "k1": np.asarray(c["k1"], np.float64),
-                   "proj": None if c["proj"] is None else np.asarray(c["proj"], np.float64)})
+                   "proj": proj, "groups": c.get("groups", 1)})
     y = conv_chain(xd, cd, w.dtype)
     Bs, L, H = y.shape
     z = lm_logits(y.reshape(Bs * L, H), inp["W"], w.dtype)

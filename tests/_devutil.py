@@ -31,6 +31,7 @@ def convs_to_dev(convs, dtype: str, device="cuda"):
             "proj": None if c.get("proj") is None
             else torch.from_numpy(np.ascontiguousarray(c["proj"], np.float32)).to(device),
             "groups": c.get("groups", 1),
+            "projT": None if c.get("projT") is None else to_dev(c["projT"], dtype, device),
         })
     return out
 

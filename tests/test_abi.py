@@ -71,6 +71,28 @@ def test_conv_validation():
     assert call(B=-1) == EINVAL
 
 
+def test_conv_mm_validation():
+    f = bd.lib().dflash2_twotap_conv_mm
+    ok = dict(x=P, a=None, y=Q, k0=P + 0x80000, k1=P + 0x90000, pt=P + 0xa0000, g=4, B=2, L=8,
+              H=64, dt=1)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["a"], a["y"], a["k0"], a["k1"], a["pt"], a["g"], a["B"], a["L"],
+                 a["H"], a["dt"], None)
+
+    assert call(B=0) == 0
+    assert call(dt=0) == EUNSUP               # matrix cores take bf16
+    assert call(pt=None) == EINVAL
+    assert call(pt=P + 0xa0004) == EINVAL     # misaligned map
+    assert call(g=3) == EINVAL                # groups must divide H
+    assert call(g=0) == EINVAL
+    assert call(y=P + 0xa0000) == EINVAL      # y overlaps the map
+    assert call(y=P) == EINVAL                # y aliases x
+    assert call(H=12) == EINVAL
+    assert call(H=(1 << 21) + 64, g=1) == EUNSUP
+
+
 def test_lmhead_and_topk_validation():
     L = bd.lib()
     assert L.dflash2_lmhead_logits(P, Q, P + 0x10000000, 8, 64, 15, 1, None) == EINVAL  # V < 16

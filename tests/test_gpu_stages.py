@@ -94,6 +94,51 @@ def test_conv_no_anchor_and_special_taps_bit_exact():
     _conv_check(x, None, (np.arange(H) % 3).astype(np.float32), np.full(H, 0.5, np.float32), None, 1, "bf16")
 
 
+def conv_mm_tolerance(xo, ao, P, groups, want):
+    """1 bf16 ulp for the final rounding, plus the fp32 accumulation of the
+    corrections (|dD| <= H 2^-24 sum_c |x_c P_c|) carried through |x| and |prev|."""
+    H = xo.shape[2]
+    k = np.zeros(H)
+    dD = O.twotap_conv(np.abs(xo), None if ao is None else np.abs(ao), k, k,
+                       H * 2.0 ** -24 * np.abs(P), groups)
+    return bf16_ulp(want) + dD
+
+
+@pytest.mark.parametrize("B,L,H,G,anchor", [(1, 1, 64, 4, True), (3, 5, 136, 17, True),
+                                            (2, 16, 5120, 320, True), (37, 1, 128, 8, False),
+                                            (5, 7, 2560, 160, True), (1, 3, 256, 256, True),
+                                            (4, 8, 1024, 1, True), (9, 8, 520, 65, False)])
+def test_conv_mm_parity(B, L, H, G, anchor):
+    g = np.random.default_rng(B * 1000 + G)
+    x = WL.to_bf16_bits(g.standard_normal((B, L, H)).astype(np.float32))
+    a = WL.to_bf16_bits(g.standard_normal((B, H)).astype(np.float32)) if anchor else None
+    k0 = (g.standard_normal(H) * 0.7).astype(np.float32)
+    k1 = (g.standard_normal(H) * 0.7).astype(np.float32)
+    pt = WL.to_bf16_bits((g.standard_normal((2 * G, H)) * np.sqrt(0.01 / H)).astype(np.float32))
+    xo = O.as_f64(x, "bf16")
+    ao = None if a is None else O.as_f64(a, "bf16")
+    P = O.as_f64(pt, "bf16").T
+    want = O.round_to_bf16(O.twotap_conv(xo, ao, k0.astype(np.float64), k1.astype(np.float64),
+                                         P, G))
+    y = bd.twotap_conv_mm(to_dev(x, "bf16"), torch.from_numpy(k0).to(DEV),
+                          torch.from_numpy(k1).to(DEV), to_dev(pt, "bf16"),
+                          None if a is None else to_dev(a, "bf16"))
+    got = O.as_f64(to_host_bits(y), "bf16")
+    err = np.abs(got - want)
+    assert (err <= conv_mm_tolerance(xo, ao, P, G, want)).all(), err.max()
+    assert (got != want).mean() <= 1e-3, (got != want).mean()
+
+
+def test_conv_mm_zero_map_is_the_static_conv_bit_exact():
+    B, L, H, G = 3, 8, 640, 40
+    x, a, k0, k1, _ = _conv_case(B, L, H, "bf16", False, 1, seed=31)
+    pt = np.zeros((2 * G, H), np.uint16)
+    args = (to_dev(x, "bf16"), torch.from_numpy(k0).to(DEV), torch.from_numpy(k1).to(DEV))
+    y_mm = bd.twotap_conv_mm(*args, to_dev(pt, "bf16"), to_dev(a, "bf16"))
+    y_st = bd.twotap_conv(*args, to_dev(a, "bf16"))
+    assert torch.equal(y_mm.view(torch.int16), y_st.view(torch.int16))
+
+
 def test_conv_empty_batch_is_noop():
     x = torch.empty((0, 8, 64), dtype=torch.bfloat16, device=DEV)
     k = torch.zeros(64, device=DEV)

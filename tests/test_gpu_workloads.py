@@ -30,6 +30,7 @@ import block_drafting_amd as bd
 import oracle as O
 import workloads as WL
 from _devutil import bf16_ulp, convs_to_dev, to_dev, to_host_bits
+from test_gpu_stages import conv_mm_tolerance
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -98,15 +99,28 @@ def test_conv_stagewise(case):
     for j, c in enumerate(inp["convs"]):
         a = O.as_f64(c["anchor_h"][blocks], w.dtype)
         k0, k1 = c["k0"].astype(np.float64), c["k1"].astype(np.float64)
-        P = None if c["proj"] is None else c["proj"].astype(np.float64)
-        want = O.round_to_dtype(O.twotap_conv(x, a, k0, k1, P, 1), w.dtype)
+        G = c.get("groups", 1)
+        mm = c.get("projT") is not None
+        if mm:
+            P = O.as_f64(c["projT"], w.dtype).T
+        else:
+            P = None if c["proj"] is None else c["proj"].astype(np.float64)
+        want = O.round_to_dtype(O.twotap_conv(x, a, k0, k1, P, G), w.dtype)
         xin = torch.from_numpy(x).to(_dt(w)).to(DEV)           # exact: x is storage-valued
         ain = torch.from_numpy(a).to(_dt(w)).to(DEV)
-        y = bd.twotap_conv(xin, torch.from_numpy(c["k0"]).to(DEV), torch.from_numpy(c["k1"]).to(DEV),
-                           ain, None if c["proj"] is None else torch.from_numpy(c["proj"]).to(DEV), 1)
+        kd0, kd1 = torch.from_numpy(c["k0"]).to(DEV), torch.from_numpy(c["k1"]).to(DEV)
+        if mm:
+            y = bd.twotap_conv_mm(xin, kd0, kd1, case["dev"]["convs"][j]["projT"], ain)
+        else:
+            y = bd.twotap_conv(xin, kd0, kd1, ain,
+                               None if c["proj"] is None else torch.from_numpy(c["proj"]).to(DEV), 1)
         got = y.double().cpu().numpy()
-        bound = O.twotap_conv(np.abs(x), np.abs(a), np.abs(k0), np.abs(k1), None if P is None else np.abs(P), 1)
-        tol = (bf16_ulp(want) if w.dtype == "bf16" else 0.0) + (w.H + 4) * 2.0 ** -24 * bound
+        if mm:   # corrections accumulated in fp32 on the matrix cores
+            tol = conv_mm_tolerance(x, a, P, G, want)
+        else:
+            bound = O.twotap_conv(np.abs(x), np.abs(a), np.abs(k0), np.abs(k1),
+                                  None if P is None else np.abs(P), 1)
+            tol = (bf16_ulp(want) if w.dtype == "bf16" else 0.0) + (w.H + 4) * 2.0 ** -24 * bound
         bad = np.abs(got - want) > tol
         assert not bad.any(), f"conv {j}: {bad.sum()} elements beyond tolerance"
         worst = max(worst, int((got != want).sum()))
@@ -158,9 +172,42 @@ def test_context_gate_stagewise(case):
     print(f"gate: max |dg| {err.max():.2e}, mean {err.mean():.2e}")
 
 
+def test_first_conv_all_blocks(case):
+    """The first conv application over every block (all tiles of the launch)."""
+    w, inp = case["w"], case["inp"]
+    c = inp["convs"][0]
+    if not w.dynamic:
+        pytest.skip("static taps: covered by the stage-wise test")
+    x = O.as_f64(inp["x"], w.dtype)
+    a = O.as_f64(c["anchor_h"], w.dtype)
+    G = c.get("groups", 1)
+    mm = c.get("projT") is not None
+    P = O.as_f64(c["projT"], w.dtype).T if mm else c["proj"].astype(np.float64)
+    want = O.round_to_dtype(O.twotap_conv(x, a, c["k0"].astype(np.float64),
+                                          c["k1"].astype(np.float64), P, G), w.dtype)
+    d = case["dev"]["convs"][0]
+    if mm:
+        y = bd.twotap_conv_mm(case["dev"]["x"], d["k0"], d["k1"], d["projT"], d["anchor_h"])
+    else:
+        y = bd.twotap_conv(case["dev"]["x"], d["k0"], d["k1"], d["anchor_h"], d["proj"], G)
+    got = y.double().cpu().numpy()
+    if mm:
+        assert (np.abs(got - want) <= conv_mm_tolerance(x, a, P, G, want)).all()
+        assert (got != want).mean() <= 1e-3
+    else:
+        np.testing.assert_array_equal(got, want)
+    print(f"first conv over {w.B} blocks: {(got != want).mean():.2e} of elements off by 1 ulp")
+
+
 # ------------------------------------------------------------------ end to end
 def test_end_to_end_subset(case):
     w, buf, ora, blocks = case["w"], case["buf"], case["ora"], case["blocks"]
+    if w.dynamic and w.groups > 1 and w.n_convs > 1:
+        pytest.skip("20 chained applications with fp32-accumulated per-group corrections are "
+                    "chaotic (a 1e-7 relative change of the corrections changes over 1% of the "
+                    "final activations: test_oracle_pins.py::"
+                    "test_conv_g16_chain_amplifies_rounding_of_the_corrections); parity is "
+                    "per application (stage-wise on the subset, first application on all blocks)")
     B, L, V = w.B, w.L, w.V
     rows = (blocks[:, None] * L + np.arange(L)[None, :]).reshape(-1)
     z = buf.logits[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)

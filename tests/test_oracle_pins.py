@@ -96,6 +96,27 @@ def test_conv_one_hot_rows_recover_taps_and_corrections():
     np.testing.assert_allclose(y2[0, t], want, rtol=1e-14, atol=1e-15)
 
 
+def test_conv_per_16_channel_groups_reduce_to_one_group():
+    # G = H/16 with every group's pair of columns equal to one pair (p0, p1)
+    # is the single-group conv with proj [p0, p1]
+    H = 64
+    g = np.random.default_rng(25)
+    x, a = g.standard_normal((2, 5, H)), g.standard_normal((2, H))
+    k0, k1 = g.standard_normal(H), g.standard_normal(H)
+    p = g.standard_normal((H, 2)) * 0.1
+    y1 = O.twotap_conv(x, a, k0, k1, p, 1)
+    y16 = O.twotap_conv(x, a, k0, k1, np.tile(p, (1, H // 16)), H // 16)
+    np.testing.assert_allclose(y16, y1, rtol=1e-13, atol=1e-14)
+    # and a correction column read by exactly its 16 channels
+    P = np.zeros((H, 2 * (H // 16)))
+    P[:, 2 * 2] = 1.0                      # group 2's first tap correction = sum(x_t)
+    y = O.twotap_conv(x, a, np.zeros(H), np.zeros(H), P, H // 16)
+    s = x.sum(axis=2, keepdims=True)
+    want = np.zeros_like(x)
+    want[:, :, 32:48] = s * x[:, :, 32:48]
+    np.testing.assert_allclose(y, want, rtol=1e-13, atol=1e-13)
+
+
 def test_conv_chain_rounds_each_application_to_storage_type():
     x = np.full((1, 2, 8), 1.0)
     conv = {"anchor_h": np.zeros((1, 8)), "k0": np.full(8, 1.0 + 2.0 ** -8),
@@ -520,6 +541,35 @@ def test_tiny_step_invariants():
     # the path score equals the fp64 score of the path up to fp32 rounding
     sc = O.path_scores_f64(out["S0"], out["S"], out["path_slot"].astype(np.int64))
     assert abs(sc[0] - out["path_score"][0]) < 1e-4
+
+
+def test_conv_g16_chain_amplifies_rounding_of_the_corrections():
+    """A property of the conv-heavy chain with one correction per 16 channels
+    (the workload, not the oracle): the corrections are quadratic in the
+    activations, so over 20 chained applications a 1e-7 relative change of
+    the correction map, the size of an fp32 accumulation error, changes far
+    more of the final bf16 activations than of the first application's.
+    Bit-level end-to-end parity of such a chain is therefore not a property
+    any fp32-accumulating implementation can have."""
+    w = WL.WORKLOADS[6].with_blocks(1)
+    inp = WL.make_inputs(w, with_head=False)
+    x = O.as_f64(inp["x"], "bf16")
+    g = np.random.default_rng(26)
+
+    def convs(noise):
+        out = []
+        for c in inp["convs"]:
+            P = O.as_f64(c["projT"], "bf16").T
+            out.append({"anchor_h": O.as_f64(c["anchor_h"], "bf16"), "k0": c["k0"].astype(np.float64),
+                        "k1": c["k1"].astype(np.float64), "groups": c["groups"],
+                        "proj": P * (1.0 + noise * g.standard_normal(P.shape))})
+        return out
+
+    exact, nudged = convs(0.0), convs(1e-7)
+    first = (O.conv_chain(x, exact[:1], "bf16") != O.conv_chain(x, nudged[:1], "bf16")).mean()
+    last = (O.conv_chain(x, exact, "bf16") != O.conv_chain(x, nudged, "bf16")).mean()
+    assert first < 1e-3
+    assert last > 0.01 and last > 20 * first
 
 
 def test_stress_construction_is_dyadic():

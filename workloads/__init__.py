@@ -29,6 +29,8 @@ The workloads
    targets a 50/50 mix of all-correct and random-miss blocks.
 5. 27B-shaped head with the pages' own selector: rank-256 factors weighted
    by a context gate from the final hidden state, greedy best-successor walk.
+6. conv-heavy body with one correction pair per 16 channels (G = H/16), the
+   correction map stored transposed in bf16.
 
 The planted-target recall profile of workloads 0-2 and 4 is the per-position
 Recall@1 / Recall@16 of Table 1 of "DFlash 2: Keep Drafting Parallel"
@@ -81,6 +83,8 @@ class Workload:
     parity_blocks: int    # seeded block subset the oracle checks at full size
     gate: bool = False    # pair match weighted by a context gate from h_t (Wg [r, H])
     walk: str = "viterbi"  # path walk: "viterbi" (max-plus) or "greedy" (best successor)
+    groups: int = 1       # correction groups of a dynamic conv (H/16: one per 16 channels)
+    profile: str = "table1"  # recall profile: "table1" or "decay" (linear 0.85 -> 0.60)
 
     @property
     def M(self) -> int:
@@ -93,7 +97,7 @@ class Workload:
     def recall_profile(self):
         """(p1, p16): per-position probabilities that the planted target is
         the top-1 candidate, and that it is inside the top-16."""
-        if self.cid == 3:
+        if self.profile == "decay":
             p1 = 0.85 - 0.25 * np.arange(self.L) / (self.L - 1)
             p16 = np.maximum(hold_last(PROFILE_P16, self.L), p1)
             return p1, p16
@@ -112,12 +116,17 @@ WORKLOADS: Dict[int, Workload] = {
     0: Workload(0, "tiny", 1, 8, 256, 4096, 32, "f32", 1, False, "planted", False, 1),
     1: Workload(1, "4b-head", 32, 8, 2560, 151936, 64, "bf16", 1, False, "planted", False, 32),
     2: Workload(2, "27b-head", 64, 8, 5120, 151936, 64, "bf16", 1, False, "planted", False, 8),
-    3: Workload(3, "conv-heavy", 128, 16, 5120, 151936, 64, "bf16", 20, True, "planted", False, 4),
+    3: Workload(3, "conv-heavy", 128, 16, 5120, 151936, 64, "bf16", 20, True, "planted", False, 4,
+                profile="decay"),
     4: Workload(4, "stress", 256, 16, 5120, 151936, 128, "bf16", 1, False, "mix", True, 4),
     # The pages' own selector on the 27B-shaped head: rank-256 factors, the
     # context gate and the greedy best-successor walk.
     5: Workload(5, "27b-gated-greedy", 64, 8, 5120, 151936, 256, "bf16", 1, False, "planted",
                 False, 8, gate=True, walk="greedy"),
+    # The conv-heavy body with the post's own coefficients: one correction
+    # pair per 16 channels (320 groups at H = 5120).
+    6: Workload(6, "conv-heavy-g16", 128, 16, 5120, 151936, 64, "bf16", 20, True, "planted",
+                False, 4, groups=320, profile="decay"),
 }
 
 
@@ -189,7 +198,9 @@ def make_inputs(w: Workload, with_head: bool = True) -> Dict[str, object]:
 
     Returns a dict with
       x        [B, L, H]   activations entering the first conv
-      convs    list of n_convs dicts {anchor_h [B,H], k0 [H], k1 [H], proj [H,2] or None}
+      convs    list of n_convs dicts {anchor_h [B,H], k0 [H], k1 [H], proj [H,2] or None,
+               groups, projT}: with groups > 1 the correction map is given as
+               projT [2*groups, H] in the storage dtype (proj is None)
       W        [V, H]      LM-head weight (omitted when with_head is False)
       U, Vf    [V, r]      low-rank pair factors (omitted when with_head is False)
       Wg       [r, H]      context-gate map, N(0, 1/H) (gated workloads only)
@@ -216,9 +227,14 @@ def make_inputs(w: Workload, with_head: bool = True) -> Dict[str, object]:
         else:
             k0 = normal_f32((H,), 0.5, s, TAG_K0 + o)
             k1 = normal_f32((H,), 0.5, s, TAG_K1 + o)
-        proj = normal_f32((H, 2), 0.01 / H, s, TAG_PROJ + o) if w.dynamic else None
+        proj = projT = None
+        if w.dynamic and w.groups == 1:
+            proj = normal_f32((H, 2), 0.01 / H, s, TAG_PROJ + o)
+        elif w.dynamic:
+            projT = normal_f32((2 * w.groups, H), 0.01 / H, s, TAG_PROJ + o)
+            projT = to_bf16_bits(projT) if bf16 else projT
         convs.append({"anchor_h": act((B, H), TAG_ANCHOR_H + o), "k0": k0, "k1": k1,
-                      "proj": proj})
+                      "proj": proj, "projT": projT, "groups": w.groups})
     out["convs"] = convs
     if with_head:
         if w.dyadic:
