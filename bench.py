@@ -40,7 +40,7 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--walk", choices=["viterbi", "greedy"], default=None,
                     help="path walk (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -103,8 +103,13 @@ def cpu_baseline(w, inp, n_blocks: int):
     cores = max([i.get("num_threads", 1) for i in info] + [1])
     t0 = time.perf_counter()
     ora = O.run_step_front(w, inp, blocks)
-    tgt = WL.make_targets(w, ora["top_idx"], ora["path_tok"])
-    O.verify_greedy(ora["path_tok"], tgt)
+    if w.temperature > 0:
+        zt = WL.planted_target_logits(w, ora["top_idx"], blocks)
+        O.rejection_verify(ora["path_tok"], ora["q"], ora["top_idx"], zt, w.temperature,
+                           inp["u_acc"][blocks], inp["u_res"][blocks])
+    else:
+        tgt = WL.make_targets(w, ora["top_idx"], ora["path_tok"])
+        O.verify_greedy(ora["path_tok"], tgt)
     dt = time.perf_counter() - t0
     return {"value": len(blocks) / dt, "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {len(blocks)} of {w.B} blocks of the {w.name} workload "
@@ -161,17 +166,26 @@ def main(argv=None):
     Wg = dev(inp["Wg"], "act") if w.gate else None
     B, L, H, V = w.B, w.L, w.H, w.V
     M = B * L
+    sampled = w.temperature > 0
     buf = bd.StepBuffers(B, L, H, V, tdt, "cuda", n_convs=w.n_convs, keep_logits=True,
-                         gate_rank=w.r if w.gate else 0)
+                         gate_rank=w.r if w.gate else 0, sample=sampled)
     topk_ws = torch.empty(max(bd.topk16_workspace(M, V), 1), dtype=torch.uint8, device="cuda")
+    if sampled:
+        u_path, u_acc, u_res = (dev(inp[k], "f32") for k in ("u_path", "u_acc", "u_res"))
 
     # one untimed step gives the candidates the verification targets are planted on
-    bd.run_step(buf, x, convs, W, U, Vf, anchor, None, Wg=Wg, walk=w.walk)
+    bd.run_step(buf, x, convs, W, U, Vf, anchor, None, Wg=Wg, walk=w.walk,
+                temperature=w.temperature, u_path=u_path if sampled else None)
     torch.cuda.synchronize()
-    tgt_np = WL.make_targets(w, buf.top_idx.view(B, L, 16).cpu().numpy(), buf.path_tok.cpu().numpy())
-    target = torch.from_numpy(tgt_np).cuda()
+    cand = buf.top_idx.view(B, L, 16).cpu().numpy()
+    if sampled:
+        # the target model's logits for every drafted position (+ the bonus one)
+        z_target = torch.from_numpy(WL.planted_target_logits(w, cand)).cuda()
+    else:
+        target = torch.from_numpy(WL.make_targets(w, cand, buf.path_tok.cpu().numpy())).cuda()
 
-    order = ["conv", "gemm", "topk"] + (["gate"] if w.gate else []) + ["pair", "select", "verify"]
+    order = (["conv", "gemm", "topk"] + (["gate"] if w.gate else []) + ["pair", "select"] +
+             (["lse"] if sampled else []) + ["verify"])
     ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)] for k in order}
     ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
 
@@ -203,11 +217,21 @@ def main(argv=None):
                       gate=gate)
         if i is not None:
             ev["select"][i].record()
-        bd.path_select(buf.S0, buf.S, buf.top_idx.view(B, L, 16), buf.path_slot, buf.path_tok, buf.path_score,
-                       mode=w.walk)
-        if i is not None:
-            ev["verify"][i].record()
-        bd.verify_greedy(buf.path_tok, target, buf.accept_len, buf.next_tok)
+        ti = buf.top_idx.view(B, L, 16)
+        if sampled:
+            bd.path_sample(buf.S0, buf.S, ti, u_path, w.temperature, buf.path_slot, buf.path_tok, buf.q)
+            if i is not None:
+                ev["lse"][i].record()
+            bd.target_lse(z_target, w.temperature, buf.lse)
+            if i is not None:
+                ev["verify"][i].record()
+            bd.verify_rejection(buf.path_slot, buf.path_tok, buf.q, ti, z_target, buf.lse, w.temperature,
+                                u_acc, u_res, buf.accept_len, buf.next_tok)
+        else:
+            bd.path_select(buf.S0, buf.S, ti, buf.path_slot, buf.path_tok, buf.path_score, mode=w.walk)
+            if i is not None:
+                ev["verify"][i].record()
+            bd.verify_greedy(buf.path_tok, target, buf.accept_len, buf.next_tok)
         if i is not None:
             ev_end[i].record()
 
@@ -250,6 +274,10 @@ def main(argv=None):
     if w.dynamic and w.groups > 1:
         conv_bytes += w.n_convs * 2 * w.groups * H * es      # the correction maps
     topk_bytes = M * V * 4
+    hbm = {"conv": round(conv_bytes / (stage_ms["conv"] * 1e-3) / 1e9, 1),
+           "topk": round(topk_bytes / (stage_ms["topk"] * 1e-3) / 1e9, 1)}
+    if sampled:
+        hbm["lse"] = round(B * (L + 1) * V * 4 / (stage_ms["lse"] * 1e-3) / 1e9, 1)
     out = {
         "metric": "draft-select-verify blocks/s at B=64,L=8,V=151936; % MFMA / HBM roofline",
         "value": round(B / (ms_step * 1e-3), 1),
@@ -265,13 +293,12 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "L": L, "H": H, "V": V, "r": w.r,
                    "convs": w.n_convs, "conv_groups": w.groups if w.dynamic else 0, "topk": 16,
-                   "gate": w.gate, "walk": w.walk},
+                   "gate": w.gate, "walk": w.walk, "temperature": w.temperature},
         "tokens_per_s": round(M / (ms_step * 1e-3), 1),
         "accepted_tokens_per_s": round(float(acc.sum()) / (ms_step * 1e-3), 1),
         "mean_accept_len": round(float(acc.mean()), 3),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "stage_hbm_gbs": {"conv": round(conv_bytes / (stage_ms["conv"] * 1e-3) / 1e9, 1),
-                          "topk": round(topk_bytes / (stage_ms["topk"] * 1e-3) / 1e9, 1)},
+        "stage_hbm_gbs": hbm,
         "roofline": roof,
     }
     if w.dynamic and w.groups > 1:

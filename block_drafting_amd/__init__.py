@@ -18,6 +18,8 @@ The five stages (names as in the C ABI):
   path_select     max-plus walk (or the greedy best-successor walk) to one
                   path per block
   verify_greedy   greedy verification, acceptance length
+At T > 0: path_sample (sampled walk), target_lse + verify_rejection (lossless
+speculative-sampling verification against target logits).
 """
 from __future__ import annotations
 
@@ -30,7 +32,7 @@ import torch
 __all__ = [
     "DFlash2Error", "lib", "library_path", "twotap_conv", "twotap_conv_mm", "lmhead_logits", "topk16",
     "topk16_workspace", "logits_topk", "logits_topk_workspace", "context_gate", "pair_score",
-    "path_select", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
+    "path_select", "path_sample", "target_lse", "verify_rejection", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
 ]
 
 TOPK = 16
@@ -59,6 +61,10 @@ _SIGS = {
     "dflash2_path_select": ([_P, _P, _P, _I, _I, _P, _P, _P, _P], _I),
     "dflash2_path_select_mode": ([_P, _P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
     "dflash2_verify_greedy": ([_P, _P, _I, _I, _P, _P, _P], _I),
+    "dflash2_path_sample": ([_P, _P, _P, _P, ctypes.c_float, _I, _I, _P, _P, _P, _P], _I),
+    "dflash2_target_lse": ([_P, _I, _I, ctypes.c_float, _P, _P], _I),
+    "dflash2_verify_rejection": ([_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _I,
+                                  _P, _P, _P], _I),
 }
 
 
@@ -344,6 +350,68 @@ def verify_greedy(path_tok: torch.Tensor, target: torch.Tensor, accept_len=None,
     return accept_len, next_tok
 
 
+def path_sample(S0: torch.Tensor, S: Optional[torch.Tensor], top_idx: Optional[torch.Tensor],
+                u: torch.Tensor, temperature: float, path_slot=None, path_tok=None, q=None):
+    """Sampling walk at temperature T with uniforms u [B, L].
+    Returns (path_slot, path_tok, q [B, L, 16])."""
+    B = S0.shape[0]
+    L = u.shape[1]
+    _shape(u, (B, L), "u", torch.float32)
+    dev = S0.device
+    if path_slot is None:
+        path_slot = torch.empty((B, L), dtype=torch.int32, device=dev)
+    if path_tok is None and top_idx is not None:
+        path_tok = torch.empty((B, L), dtype=torch.int32, device=dev)
+    if q is None:
+        q = torch.empty((B, L, TOPK), dtype=torch.float32, device=dev)
+    _dev(S0, S, top_idx, u, path_slot, path_tok, q)
+    _check("dflash2_path_sample", lib().dflash2_path_sample(
+        _ptr(S0), _ptr(S) if L > 1 else None, _ptr(top_idx), _ptr(u), float(temperature), B, L,
+        _ptr(path_slot), _ptr(path_tok), _ptr(q), _stream(dev)))
+    return path_slot, path_tok, q
+
+
+def target_lse(z: torch.Tensor, temperature: float, out: Optional[torch.Tensor] = None):
+    """log sum exp(z / T) over the last axis of fp32 target logits."""
+    V = z.shape[-1]
+    R = z.numel() // V
+    if out is None:
+        out = torch.empty(z.shape[:-1], dtype=torch.float32, device=z.device)
+    if out.numel() != R or out.dtype != torch.float32:
+        raise ValueError("lse: expected one fp32 value per row")
+    dev = _dev(z, out)
+    _check("dflash2_target_lse", lib().dflash2_target_lse(
+        _ptr(z), R, V, float(temperature), _ptr(out), _stream(dev)))
+    return out
+
+
+def verify_rejection(path_slot: torch.Tensor, path_tok: torch.Tensor, q: torch.Tensor,
+                     top_idx: torch.Tensor, z: torch.Tensor, lse: torch.Tensor,
+                     temperature: float, u_acc: torch.Tensor, u_res: torch.Tensor,
+                     accept_len=None, next_tok=None):
+    """Speculative-sampling verification: (accept_len [B], next_tok [B])."""
+    B, L = path_tok.shape
+    V = z.shape[-1]
+    _shape(path_slot, (B, L), "path_slot", torch.int32)
+    _shape(q, (B, L, TOPK), "q", torch.float32)
+    _shape(top_idx, (B, L, TOPK), "top_idx", torch.int32)
+    _shape(z, (B, L + 1, V), "z", torch.float32)
+    _shape(lse, (B, L + 1), "lse", torch.float32)
+    _shape(u_acc, (B, L), "u_acc", torch.float32)
+    _shape(u_res, (B,), "u_res", torch.float32)
+    dev = path_tok.device
+    if accept_len is None:
+        accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if next_tok is None:
+        next_tok = torch.empty((B,), dtype=torch.int32, device=dev)
+    _dev(path_slot, path_tok, q, top_idx, z, lse, u_acc, u_res, accept_len, next_tok)
+    _check("dflash2_verify_rejection", lib().dflash2_verify_rejection(
+        _ptr(path_slot), _ptr(path_tok), _ptr(q), _ptr(top_idx), _ptr(z), _ptr(lse),
+        float(temperature), _ptr(u_acc), _ptr(u_res), B, L, V, _ptr(accept_len), _ptr(next_tok),
+        _stream(dev)))
+    return accept_len, next_tok
+
+
 # ---------------------------------------------------------------- whole step
 class StepBuffers:
     """Preallocated device buffers for one step shape (B, L, H, V) so repeated
@@ -351,7 +419,8 @@ class StepBuffers:
     their own tensor (else they live in the workspace)."""
 
     def __init__(self, B: int, L: int, H: int, V: int, dtype: torch.dtype, device,
-                 n_convs: int = 1, keep_logits: bool = True, gate_rank: int = 0):
+                 n_convs: int = 1, keep_logits: bool = True, gate_rank: int = 0,
+                 sample: bool = False):
         M = B * L
         kw = dict(device=device)
         self.B, self.L, self.H, self.V = B, L, H, V
@@ -370,19 +439,26 @@ class StepBuffers:
         self.next_tok = torch.empty((B,), dtype=torch.int32, **kw)
         self.gate = (torch.empty((M, gate_rank), dtype=torch.float32, **kw)
                      if gate_rank else None)
+        self.q = torch.empty((B, L, TOPK), dtype=torch.float32, **kw) if sample else None
+        self.lse = torch.empty((B, L + 1), dtype=torch.float32, **kw) if sample else None
 
 
 def run_step(buf: StepBuffers, x: torch.Tensor, convs, W: torch.Tensor, U: torch.Tensor,
              Vf: torch.Tensor, anchor_tok: Optional[torch.Tensor],
              target: Optional[torch.Tensor], Wg: Optional[torch.Tensor] = None,
-             walk: str = "viterbi") -> StepBuffers:
+             walk: str = "viterbi", temperature: float = 0.0,
+             u_path: Optional[torch.Tensor] = None, z_target: Optional[torch.Tensor] = None,
+             u_acc: Optional[torch.Tensor] = None,
+             u_res: Optional[torch.Tensor] = None) -> StepBuffers:
     """One draft-select-verify step: the conv chain (each entry of `convs` is a
     dict with k0, k1, anchor_h and either proj + groups, or projT for the
     matrix-core corrections), logits + top-16, pair scores
     (context-gated from the final hidden states when `Wg` is given), the path
-    walk (`walk`: "viterbi" or "greedy") and, when `target` is given, greedy
-    verification.  Every call is enqueued on the current stream; nothing is
-    synchronised."""
+    walk (`walk`: "viterbi", "greedy", or "sample" at `temperature` with the
+    uniforms `u_path`) and verification: greedy against `target` argmax ids,
+    or, for a sampled walk given target logits `z_target` [B, L+1, V], the
+    lossless rejection rule with uniforms `u_acc`, `u_res`.  Every call is
+    enqueued on the current stream; nothing is synchronised."""
     B, L, H, V = buf.B, buf.L, buf.H, buf.V
     cur = x
     for j, c in enumerate(convs):
@@ -403,6 +479,15 @@ def run_step(buf: StepBuffers, x: torch.Tensor, convs, W: torch.Tensor, U: torch
             raise ValueError("StepBuffers were made without gate_rank")
         gate = context_gate(cur.view(M, H), Wg, buf.gate)
     pair_score(tv, ti, anchor_tok, U, Vf, buf.S0, buf.S, gate=gate)
+    if walk == "sample":
+        if buf.q is None or u_path is None:
+            raise ValueError("a sampled walk needs StepBuffers(sample=True) and u_path")
+        path_sample(buf.S0, buf.S, ti, u_path, temperature, buf.path_slot, buf.path_tok, buf.q)
+        if z_target is not None:
+            target_lse(z_target, temperature, buf.lse)
+            verify_rejection(buf.path_slot, buf.path_tok, buf.q, ti, z_target, buf.lse,
+                             temperature, u_acc, u_res, buf.accept_len, buf.next_tok)
+        return buf
     path_select(buf.S0, buf.S, ti, buf.path_slot, buf.path_tok, buf.path_score, mode=walk)
     if target is not None:
         verify_greedy(buf.path_tok, target, buf.accept_len, buf.next_tok)

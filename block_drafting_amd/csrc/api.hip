@@ -290,6 +290,78 @@ DFLASH2_API int dflash2_path_select_mode(const float* S0, const float* S, const 
   return path_select(S0, S, top_idx, B, L, mode, path_slot, path_tok, path_score, stream);
 }
 
+static bool valid_temperature(float T) { return T > 0.f && T <= 1e30f && T == T; }
+
+DFLASH2_API int dflash2_path_sample(const float* S0, const float* S, const int32_t* top_idx,
+                                    const float* u, float temperature, int B, int L,
+                                    int32_t* path_slot, int32_t* path_tok, float* q,
+                                    void* stream) {
+  if (B < 0 || L < 1 || L > DFLASH2_MAX_L || !valid_temperature(temperature))
+    return DFLASH2_EINVAL;
+  if (B == 0) return DFLASH2_OK;
+  if (!S0 || (L > 1 && !S) || !u || !path_slot || !q) return DFLASH2_EINVAL;
+  if ((top_idx == nullptr) != (path_tok == nullptr)) return DFLASH2_EINVAL;
+  if (!aligned4(S0) || (L > 1 && !aligned16(S)) || !aligned4(u) || !aligned4(path_slot) ||
+      !aligned4(q) || (top_idx && !aligned4(top_idx)) || (path_tok && !aligned4(path_tok)))
+    return DFLASH2_EINVAL;
+  const size_t s0b = (size_t)B * kTopK * 4;
+  const size_t sb = L > 1 ? (size_t)B * (L - 1) * kTopK * kTopK * 4 : 0;
+  const size_t tib = (size_t)B * L * kTopK * 4;
+  const size_t pb = (size_t)B * L * 4;
+  const void* ins[] = {S0, S, top_idx, u};
+  const size_t insz[] = {s0b, sb, tib, pb};
+  void* outs[] = {path_slot, path_tok, q};
+  const size_t outsz[] = {pb, pb, tib};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (insz[j] && overlap(outs[i], outsz[i], ins[j], insz[j])) return DFLASH2_EINVAL;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return DFLASH2_EINVAL;
+  }
+  return status_of(launch_path_sample(S0, L > 1 ? S : nullptr, top_idx, u, temperature, B, L,
+                                      path_slot, path_tok, q, as_stream(stream)));
+}
+
+DFLASH2_API int dflash2_target_lse(const float* z, int R, int V, float temperature, float* lse,
+                                   void* stream) {
+  if (R < 0 || V < 1 || !valid_temperature(temperature)) return DFLASH2_EINVAL;
+  if ((long long)R * V > (1LL << 40)) return DFLASH2_EINVAL;
+  if (R == 0) return DFLASH2_OK;
+  if (!z || !lse || !aligned16(z) || !aligned4(lse)) return DFLASH2_EINVAL;
+  if (overlap(lse, (size_t)R * 4, z, (size_t)R * V * 4)) return DFLASH2_EINVAL;
+  return status_of(launch_target_lse(z, R, V, temperature, lse, as_stream(stream)));
+}
+
+DFLASH2_API int dflash2_verify_rejection(const int32_t* path_slot, const int32_t* path_tok,
+                                         const float* q, const int32_t* top_idx, const float* z,
+                                         const float* lse, float temperature, const float* u_acc,
+                                         const float* u_res, int B, int L, int V,
+                                         int32_t* accept_len, int32_t* next_tok, void* stream) {
+  if (B < 0 || L < 1 || L > DFLASH2_MAX_L || V < kTopK || !valid_temperature(temperature))
+    return DFLASH2_EINVAL;
+  if ((long long)B * (L + 1) * V > (1LL << 40)) return DFLASH2_EINVAL;
+  if (verify_rejection_lds(V) > 65536) return DFLASH2_EUNSUPPORTED;  // tile sums in LDS
+  if (B == 0) return DFLASH2_OK;
+  if (!path_slot || !path_tok || !q || !top_idx || !z || !lse || !u_acc || !u_res ||
+      !accept_len || !next_tok)
+    return DFLASH2_EINVAL;
+  const void* all[] = {path_slot, path_tok, q, top_idx, z, lse, u_acc, u_res, accept_len,
+                       next_tok};
+  for (const void* p : all)
+    if (!aligned4(p)) return DFLASH2_EINVAL;
+  const size_t pb = (size_t)B * L * 4, tib = (size_t)B * L * kTopK * 4, ob = (size_t)B * 4;
+  const void* ins[] = {path_slot, path_tok, q, top_idx, z, lse, u_acc, u_res};
+  const size_t insz[] = {pb, pb, tib, tib, (size_t)B * (L + 1) * V * 4, (size_t)B * (L + 1) * 4,
+                         pb, ob};
+  for (int j = 0; j < 8; ++j)
+    if (overlap(accept_len, ob, ins[j], insz[j]) || overlap(next_tok, ob, ins[j], insz[j]))
+      return DFLASH2_EINVAL;
+  if (overlap(accept_len, ob, next_tok, ob)) return DFLASH2_EINVAL;
+  return status_of(launch_verify_rejection(path_slot, path_tok, q, top_idx, z, lse, temperature,
+                                           u_acc, u_res, B, L, V, accept_len, next_tok,
+                                           as_stream(stream)));
+}
+
 DFLASH2_API int dflash2_verify_greedy(const int32_t* path_tok, const int32_t* target, int B, int L,
                                       int32_t* accept_len, int32_t* next_tok, void* stream) {
   if (B < 0 || L < 1) return DFLASH2_EINVAL;

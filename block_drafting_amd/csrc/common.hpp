@@ -70,6 +70,20 @@ hipError_t launch_path_select(const float* S0, const float* S, const int32_t* to
                               int L, int greedy, int32_t* path_slot, int32_t* path_tok,
                               float* path_score, hipStream_t s);
 
+hipError_t launch_path_sample(const float* S0, const float* S, const int32_t* top_idx,
+                              const float* u, float temperature, int B, int L,
+                              int32_t* path_slot, int32_t* path_tok, float* q, hipStream_t s);
+
+hipError_t launch_target_lse(const float* z, int R, int V, float temperature, float* lse,
+                             hipStream_t s);
+
+size_t verify_rejection_lds(int V);
+hipError_t launch_verify_rejection(const int32_t* path_slot, const int32_t* path_tok,
+                                   const float* q, const int32_t* top_idx, const float* z,
+                                   const float* lse, float temperature, const float* u_acc,
+                                   const float* u_res, int B, int L, int V, int32_t* accept_len,
+                                   int32_t* next_tok, hipStream_t s);
+
 hipError_t launch_verify_greedy(const int32_t* path_tok, const int32_t* target, int B, int L,
                                 int32_t* accept_len, int32_t* next_tok, hipStream_t s);
 

@@ -1,0 +1,360 @@
+// Sampling at T > 0 and lossless verification ("DFlash 2: Keep Drafting
+// Parallel", section "A lightweight path selector": besides the greedy walk,
+// sampling draws from the same precomputed scores, and rejection sampling
+// restores the target's exact distribution).
+//
+// path_sample_kernel    the sampling twin of the greedy walk: position t's
+//                       slot is drawn from softmax(row / T) of the successors
+//                       of the slot drawn before, by inverse CDF with the
+//                       caller's uniforms.  One wave per block, scores staged
+//                       in LDS as in the greedy walk.
+// target_lse_kernel     log sum_v exp(z[v] / T) of every target row: one
+//                       streaming pass with a running max, rescaled once per
+//                       batch of 16 values (HBM-bound).
+// verify_rejection_kernel  the speculative-sampling rule: accept x_t when
+//                       u * q_t(x_t) < p_t(x_t); at the first rejection (or
+//                       after L acceptances) draw the verifier's token from
+//                       max(0, p - q) (or p) by inverse CDF in token order.
+//                       One workgroup per block; the draw sums p over
+//                       256-token tiles wave by wave, moves the 16
+//                       candidates' corrections into their tiles, scans the
+//                       tile sums, then scans inside the chosen tile.
+#include "common.hpp"
+
+namespace dflash2 {
+namespace {
+
+// ---------------------------------------------------------------- path sampling
+__global__ __launch_bounds__(64) void path_sample_kernel(
+    const float* __restrict__ S0, const float* __restrict__ S, const int32_t* __restrict__ top_idx,
+    const float* __restrict__ u, float inv_t, int L, int32_t* __restrict__ path_slot,
+    int32_t* __restrict__ path_tok, float* __restrict__ q) {
+  extern __shared__ f32x4_t stage[];  // (L-1) * 64 vectors of 4 scores
+  constexpr int kUnroll = 8;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int j = lane & 15;
+  const int n4 = (L - 1) * kTopK * kTopK / 4;
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(S + (size_t)b * (L - 1) * kTopK * kTopK);
+  for (int base = 0; base < n4; base += 64 * kUnroll) {
+    f32x4_t v[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int e = base + k * 64 + lane;
+      if (e < n4) v[k] = src[e];
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int e = base + k * 64 + lane;
+      if (e < n4) stage[e] = v[k];
+    }
+  }
+  float s = S0[(size_t)b * kTopK + j];
+  const size_t row = (size_t)b * L;
+  __syncthreads();
+  const float* sS = reinterpret_cast<const float*>(stage);
+  int p = 0;
+  for (int t = 0; t < L; ++t) {
+    if (t > 0) s = sS[((t - 1) * kTopK + p) * kTopK + j];
+    // softmax over the 16 lanes of each quarter (all four quarters agree)
+    float m = s;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float e = expf((s - m) * inv_t);
+    float z = e;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
+    const float qj = e / z;
+    // inclusive prefix sum in slot order
+    float c = qj;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const float n = __shfl_up(c, o, 16);
+      if (j >= o) c += n;
+    }
+    const float ut = u[row + t];
+    // first slot with u < c_j = number of slots with c_j <= u; rounding can
+    // leave u above every c_j: then the last slot with q > 0
+    const uint64_t le = __ballot(c <= ut) & 0xffffull;
+    const uint64_t pos = __ballot(qj > 0.f) & 0xffffull;
+    const int first = __popcll(le);
+    const int last = pos ? 63 - __clzll(pos) : 0;  // no finite score: slot 0 (q is NaN)
+    p = min(first, last);
+    if (lane < kTopK) q[(row + t) * kTopK + j] = qj;
+    if (lane == 0) {
+      path_slot[row + t] = p;
+      if (path_tok) path_tok[row + t] = top_idx[(row + t) * kTopK + p];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- target log-sum-exp
+// Running (max, sum) pairs in base 2: a value a contributes 2^(a - m).
+// Exponentials use the hardware exp2 (v_exp_f32, about 1 ulp).
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ void lse_merge(float& m, float& s, float om, float os) {
+  const float nm = fmaxf(m, om);
+  if (nm == -__builtin_inff()) return;  // both empty
+  s = s * exp2f(m - nm) + os * exp2f(om - nm);
+  m = nm;
+}
+
+// One batch of values (already scaled to base 2) into (m, s): one rescale
+// per batch instead of a branch per value.  -inf values carry no mass.
+template <int N>
+__device__ __forceinline__ void lse_batch(float& m, float& s, const float (&a)[N]) {
+  float bm = a[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) bm = fmaxf(bm, a[i]);
+  const float nm = fmaxf(m, bm);
+  if (nm == -__builtin_inff()) return;
+  float acc = s * exp2f(m - nm);
+#pragma unroll
+  for (int i = 0; i < N; ++i) acc += exp2f(a[i] - nm);
+  s = acc;
+  m = nm;
+}
+
+__global__ __launch_bounds__(256) void target_lse_kernel(const float* __restrict__ z, int V,
+                                                         float scale2, float* __restrict__ lse) {
+  __shared__ float red_m[4], red_s[4];
+  const size_t r = blockIdx.x;
+  const float* row = z + r * V;
+  const int tid = threadIdx.x;
+  constexpr float kNeg = -__builtin_inff();
+  float m = kNeg, s = 0.f;
+  if ((V & 3) == 0) {  // 16-byte loads (rows stay 16-byte aligned)
+    const f32x4_t* r4 = reinterpret_cast<const f32x4_t*>(row);
+    const int n4 = V >> 2;
+    constexpr int kU = 4;
+    for (int base = tid; base < n4; base += 256 * kU) {
+      f32x4_t v[kU];
+#pragma unroll
+      for (int k = 0; k < kU; ++k) {
+        const int e = base + k * 256;
+        v[k] = e < n4 ? r4[e] : f32x4_t{kNeg, kNeg, kNeg, kNeg};
+      }
+      float a[4 * kU];
+#pragma unroll
+      for (int k = 0; k < kU; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[4 * k + i] = v[k][i] * scale2;
+      lse_batch(m, s, a);
+    }
+  } else {
+    for (int e = tid; e < V; e += 256) {
+      const float a[1] = {row[e] * scale2};
+      lse_batch(m, s, a);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) lse_merge(m, s, __shfl_xor(m, o, 64), __shfl_xor(s, o, 64));
+  if ((tid & 63) == 0) {
+    red_m[tid >> 6] = m;
+    red_s[tid >> 6] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float mm = red_m[0], ss = red_s[0];
+    for (int w = 1; w < 4; ++w) lse_merge(mm, ss, red_m[w], red_s[w]);
+    lse[r] = (mm + log2f(ss)) * kLn2;  // back to natural log
+  }
+}
+
+// ---------------------------------------------------------------- rejection verification
+constexpr int kTile = 256;      // tokens per tile: 64 lanes x 4
+constexpr int kTileBatch = 8;   // tiles a wave has in flight
+constexpr int kVerWaves = 16;   // 128 KB of the row in flight per workgroup
+
+__global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_kernel(
+    const int32_t* __restrict__ path_slot, const int32_t* __restrict__ path_tok,
+    const float* __restrict__ q, const int32_t* __restrict__ top_idx,
+    const float* __restrict__ z, const float* __restrict__ lse, float inv_t,
+    const float* __restrict__ u_acc, const float* __restrict__ u_res, int L, int V,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ next_tok) {
+  extern __shared__ float tsum[];  // tile sums, then their inclusive prefix
+  __shared__ int s_n;
+  __shared__ int32_t cand_id[kTopK];
+  __shared__ float cand_q[kTopK];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const size_t brow = (size_t)b * L;
+  const size_t zrow = (size_t)b * (L + 1);
+  // 1. every position's accept test at once (thread t, t < L; a token
+  //    outside [0, V) or a slot outside [0, 16) fails), then n = the
+  //    number of leading passes
+  if (tid == 0) s_n = L;
+  __syncthreads();
+  if (tid < L) {
+    const size_t bt = brow + tid;
+    const int x = path_tok[bt];
+    const int sl = path_slot[bt];
+    bool pass = false;
+    if (x >= 0 && x < V && sl >= 0 && sl < kTopK) {
+      const float qx = q[bt * kTopK + sl];
+      const float px = expf(z[(zrow + tid) * V + x] * inv_t - lse[zrow + tid]);
+      pass = u_acc[bt] * qx < px;
+    }
+    if (!pass) atomicMin(&s_n, tid);
+  }
+  __syncthreads();
+  const int n = s_n;
+  const bool resid = n < L;  // draw from max(0, p - q) at the rejected position, else from p
+  if (tid < kTopK) {
+    cand_id[tid] = resid ? top_idx[(brow + n) * kTopK + tid] : -1;
+    cand_q[tid] = resid ? q[(brow + n) * kTopK + tid] : 0.f;
+  }
+  const float* zr = z + (zrow + n) * V;
+  // p(v) = 2^(z[v] * s2 - l2): base-2 form of exp(z / T - lse)
+  const float s2 = inv_t * kLog2e;
+  const float l2 = lse[zrow + n] * kLog2e;
+  const int ntiles = (V + kTile - 1) / kTile;
+  const bool vec = (V & 3) == 0;
+  auto load4 = [&](int v0, float (&o)[4]) {
+    if (vec && v0 + 4 <= V) {
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(zr + v0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = x[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = v0 + i < V ? zr[v0 + i] : -__builtin_inff();
+    }
+  };
+  // 2. tile sums of p (candidates corrected below): wave w takes tiles
+  //    w, w + kVerWaves, ..., kTileBatch of them in flight
+  for (int t0 = wave; t0 < ntiles; t0 += kVerWaves * kTileBatch) {
+    float zv[kTileBatch][4];
+#pragma unroll
+    for (int k = 0; k < kTileBatch; ++k) {
+      const int v0 = (t0 + kVerWaves * k) * kTile + lane * 4;
+      if (v0 < V) {
+        load4(v0, zv[k]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zv[k][i] = -__builtin_inff();
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kTileBatch; ++k) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc += exp2f(zv[k][i] * s2 - l2);  // -inf -> 0
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      const int tl = t0 + kVerWaves * k;
+      if (lane == 0 && tl < ntiles) tsum[tl] = acc;
+    }
+  }
+  __syncthreads();
+  // 3. wave 0: the candidates' residual corrections -min(p, q) into their
+  //    tiles (in slot order), the inclusive prefix of the tile sums in token
+  //    order, 64 at a time, then the first tile whose prefix passes u * total
+  if (wave == 0) {
+    if (lane == 0 && resid) {
+      for (int c = 0; c < kTopK; ++c) {
+        const int v = cand_id[c];
+        if (v < 0 || v >= V) continue;
+        const float p = exp2f(zr[v] * s2 - l2);
+        tsum[v / kTile] -= fminf(p, cand_q[c]);
+      }
+    }
+    float carry = 0.f;
+    for (int c0 = 0; c0 < ntiles; c0 += 64) {
+      const int i = c0 + lane;
+      float c = i < ntiles ? fmaxf(tsum[i], 0.f) : 0.f;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float nb = __shfl_up(c, o, 64);
+        if (lane >= o) c += nb;
+      }
+      if (i < ntiles) tsum[i] = carry + c;
+      carry += __shfl(c, 63, 64);
+    }
+    const float target = u_res[b] * carry;
+    int k = 0x7fffffff;
+    for (int c0 = 0; c0 < ntiles && k == 0x7fffffff; c0 += 64) {
+      const int i = c0 + lane;
+      const uint64_t pass = __ballot(i < ntiles && tsum[i] > target);
+      if (pass) k = c0 + (int)__builtin_ctzll(pass);
+    }
+    if (k == 0x7fffffff) k = ntiles - 1;  // rounding: the last tile
+    // 4. inside tile k: the first token whose running sum passes the target
+    const float base = k > 0 ? tsum[k - 1] : 0.f;
+    const int v0 = k * kTile + lane * 4;
+    float zv[4], r[4];
+    load4(v0, zv);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float p = v0 + i < V ? exp2f(zv[i] * s2 - l2) : 0.f;
+#pragma unroll
+      for (int c = 0; c < kTopK; ++c)
+        if (cand_id[c] == v0 + i) p = fmaxf(p - cand_q[c], 0.f);
+      r[i] = p;
+    }
+    const float mine = r[0] + r[1] + r[2] + r[3];
+    float c = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float nb = __shfl_up(c, o, 64);
+      if (lane >= o) c += nb;
+    }
+    float run = base + (c - mine);
+    int hit = 0x7fffffff;
+    int lastv = -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      run += r[i];
+      if (hit == 0x7fffffff && r[i] > 0.f && run > target) hit = v0 + i;
+      if (r[i] > 0.f) lastv = v0 + i;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      hit = min(hit, __shfl_xor(hit, o, 64));
+      lastv = max(lastv, __shfl_xor(lastv, o, 64));
+    }
+    if (lane == 0) {
+      accept_len[b] = n + 1;
+      next_tok[b] = hit != 0x7fffffff ? hit : lastv;  // rounding overshoot: last token with mass
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_path_sample(const float* S0, const float* S, const int32_t* top_idx,
+                              const float* u, float temperature, int B, int L,
+                              int32_t* path_slot, int32_t* path_tok, float* q, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const size_t lds = (size_t)(L - 1) * kTopK * kTopK * sizeof(float);
+  hipLaunchKernelGGL(path_sample_kernel, dim3((unsigned)B), dim3(64), lds, s, S0, S, top_idx, u,
+                     1.0f / temperature, L, path_slot, path_tok, q);
+  return hipGetLastError();
+}
+
+hipError_t launch_target_lse(const float* z, int R, int V, float temperature, float* lse,
+                             hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  hipLaunchKernelGGL(target_lse_kernel, dim3((unsigned)R), dim3(256), 0, s, z, V,
+                     kLog2e / temperature, lse);
+  return hipGetLastError();
+}
+
+size_t verify_rejection_lds(int V) { return (size_t)((V + kTile - 1) / kTile) * sizeof(float); }
+
+hipError_t launch_verify_rejection(const int32_t* path_slot, const int32_t* path_tok,
+                                   const float* q, const int32_t* top_idx, const float* z,
+                                   const float* lse, float temperature, const float* u_acc,
+                                   const float* u_res, int B, int L, int V, int32_t* accept_len,
+                                   int32_t* next_tok, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  hipLaunchKernelGGL(verify_rejection_kernel, dim3((unsigned)B), dim3(64 * kVerWaves),
+                     verify_rejection_lds(V), s, path_slot, path_tok, q, top_idx, z, lse,
+                     1.0f / temperature, u_acc, u_res, L, V, accept_len, next_tok);
+  return hipGetLastError();
+}
+
+}  // namespace dflash2

@@ -13,6 +13,8 @@
  *   per-16-channel conv corrections  dflash2_twotap_conv_mm
  *   context-gated pair scores        dflash2_context_gate, dflash2_pair_score_gated
  *   best-successor (greedy) walk     dflash2_path_select_mode(..., DFLASH2_PATH_GREEDY, ...)
+ *   sampling at T > 0, lossless      dflash2_path_sample, dflash2_target_lse,
+ *   rejection verification           dflash2_verify_rejection
  *
  * Sources are cited by page title and section:
  *   [POST]   "DFlash 2: Keep Drafting Parallel" (Inco AI).
@@ -227,6 +229,50 @@ int dflash2_path_select(const float* S0, const float* S, const int32_t* top_idx,
 int dflash2_path_select_mode(const float* S0, const float* S, const int32_t* top_idx,
                              int B, int L, int mode, int32_t* path_slot, int32_t* path_tok,
                              float* path_score, void* stream);
+
+/*
+ * Sampling walk at temperature T > 0.  [POST] "A lightweight path selector":
+ * besides the greedy walk, sampling draws from the same precomputed scores.
+ * The sampling twin of the greedy walk, with the caller's uniforms:
+ *   q[b,0,:] = softmax(S0[b] / T),  q[b,t,:] = softmax(S[b,t-1,p_{t-1},:] / T),
+ *   p_t = first slot j with u[b,t] < q[b,t,0] + ... + q[b,t,j]
+ *         (if rounding leaves u above the last sum: the last slot with q > 0).
+ * u [B, L] fp32 in [0, 1).  q [B, L, 16] fp32 receives each position's
+ * proposal distribution (what dflash2_verify_rejection needs).  Scores must
+ * be finite or -inf with at least one finite per row.  S 16-byte aligned.
+ * Other arguments as for dflash2_path_select.  fp32 softmax and sums.
+ */
+int dflash2_path_sample(const float* S0, const float* S, const int32_t* top_idx,
+                        const float* u, float temperature, int B, int L,
+                        int32_t* path_slot, int32_t* path_tok, float* q, void* stream);
+
+/*
+ * Log-sum-exp of target logits at temperature T:
+ *   lse[r] = log sum_v exp(z[r, v] / T),  z [R, V] fp32 (16-byte aligned),
+ * lse [R] fp32.  -inf entries carry no mass.  One pass over z.
+ */
+int dflash2_target_lse(const float* z, int R, int V, float temperature, float* lse,
+                       void* stream);
+
+/*
+ * Lossless verification of a sampled path.  [POST] "A lightweight path
+ * selector": rejection sampling restores the target's exact distribution.
+ * The speculative-sampling rule: with p_t = softmax(z[b,t,:] / T) (lse from
+ * dflash2_target_lse on the same z) and q_t the proposal of position t,
+ *   accept x_t = path_tok[b,t] while u_acc[b,t] * q[b,t,path_slot[b,t]] < p_t(x_t);
+ *   n = number accepted, accept_len[b] = n + 1;
+ *   next_tok[b] = a draw from max(0, p_n - q_n) (n < L; q_n lives on the
+ *   candidates top_idx[b,n,:]) or from p_L (n = L), by inverse CDF in token
+ *   order with u_res[b] scaled by the residual mass.
+ * z [B, L+1, V] fp32 (position L: the token after a fully accepted block),
+ * lse [B, L+1], u_acc [B, L], u_res [B], q [B, L, 16], path_slot/path_tok
+ * [B, L], top_idx [B, L, 16].  V >= 16, V <= 4194304.  fp32 arithmetic.
+ */
+int dflash2_verify_rejection(const int32_t* path_slot, const int32_t* path_tok,
+                             const float* q, const int32_t* top_idx, const float* z,
+                             const float* lse, float temperature, const float* u_acc,
+                             const float* u_res, int B, int L, int V,
+                             int32_t* accept_len, int32_t* next_tok, void* stream);
 
 /*
  * Greedy verification.  [POST] "The right token is already in the candidates",

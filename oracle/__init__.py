@@ -35,6 +35,10 @@ from .cpu_oracle import (  # noqa: F401
     path_scores_f64,
     path_margin,
     verify_greedy,
+    sample_path,
+    sample_margin,
+    target_lse,
+    rejection_verify,
     oracle_selector,
     expected_acceptance,
     run_step_front,

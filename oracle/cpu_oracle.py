@@ -358,6 +358,109 @@ def path_margin(S0: np.ndarray, S: np.ndarray) -> np.ndarray:
     return best - second
 
 
+# ------------------------------------------------------------------ f4 sampling
+def sample_path(S0: np.ndarray, S: np.ndarray, top_idx: np.ndarray, T: float, u: np.ndarray):
+    """The sampling walk ([POST] "A lightweight path selector": besides the
+    greedy walk, sampling draws from the same precomputed scores; [GLONCE]:
+    the final step picks a path by greedy selection, sampling or rejection
+    sampling).
+
+    Reading: the sampling twin of the greedy best-successor walk.  Starting
+    from the last verified token, each position's slot is drawn from the
+    temperature softmax of the scores of the successors of the slot drawn
+    before:
+      q_0 = softmax(S0 / T),  q_t = softmax(S[t-1, p_{t-1}, :] / T),
+    p_t = the first slot j with u[b, t] < q_t[0] + ... + q_t[j] (inverse CDF
+    with the given uniforms; if rounding leaves u above the last sum, the
+    last slot with q > 0).  fp64 throughout.
+    Returns (slot int32 [B, L], tok int32 [B, L], q fp64 [B, L, 16]): q[b, t]
+    is the proposal distribution position t's token was drawn from.
+    """
+    S0 = np.asarray(S0, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    B = S0.shape[0]
+    L = S.shape[1] + 1
+    b = np.arange(B)
+    slot = np.zeros((B, L), dtype=np.int64)
+    q = np.zeros((B, L, K))
+    for t in range(L):
+        row = S0 if t == 0 else S[b, t - 1, slot[:, t - 1]]
+        e = np.exp((row - row.max(axis=1, keepdims=True)) / T)
+        q[:, t] = e / e.sum(axis=1, keepdims=True)
+        cum = np.cumsum(q[:, t], axis=1)
+        j = (u[:, t, None] >= cum).sum(axis=1)          # first j with u < cum_j
+        last = K - 1 - np.argmax(q[:, t, ::-1] > 0, axis=1)
+        slot[:, t] = np.minimum(j, last)
+    tok = np.take_along_axis(np.asarray(top_idx), slot[:, :, None], axis=2)[:, :, 0]
+    return slot.astype(np.int32), tok.astype(np.int32), q
+
+
+def sample_margin(q: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """Distance of each uniform to the nearest boundary of its inverse-CDF
+    bins (fp64, [B, L]): a perturbation of the probabilities smaller than
+    this cannot change the drawn slot."""
+    cum = np.concatenate([np.zeros(q.shape[:-1] + (1,)), np.cumsum(q, axis=-1)], axis=-1)
+    return np.min(np.abs(cum - np.asarray(u, np.float64)[..., None]), axis=-1)
+
+
+def target_lse(z_target: np.ndarray, T: float) -> np.ndarray:
+    """log sum_v exp(z[v] / T) of every target row, fp64 ([..., V] -> [...])."""
+    a = np.asarray(z_target, dtype=np.float64) / T
+    m = a.max(axis=-1, keepdims=True)
+    return (m + np.log(np.exp(a - m).sum(axis=-1, keepdims=True)))[..., 0]
+
+
+def rejection_verify(path_tok: np.ndarray, q: np.ndarray, top_idx: np.ndarray,
+                     z_target: np.ndarray, T: float, u_acc: np.ndarray, u_res: np.ndarray):
+    """Lossless verification of a sampled path ([POST] "A lightweight path
+    selector": rejection sampling restores the exact target distribution;
+    [GLONCE]: it preserves the target model's exact output distribution).
+
+    The standard speculative-sampling rule (Leviathan et al. 2023; Chen et
+    al. 2023).  The target's distribution at position t is
+    p_t = softmax(z_target[b, t] / T) over the whole vocabulary (position L
+    is the one after a fully accepted block); the proposal q_t is the
+    16-candidate distribution the path's token was drawn from (zero off the
+    candidates).  For t = 0, 1, ...: accept x_t when u_acc[b, t] * q_t(x_t) <
+    p_t(x_t) (probability min(1, p/q)); at the first rejection n, the
+    verifier's token is drawn from the residual max(0, p_n - q_n), normalised;
+    if all L are accepted, it is drawn from p_L.  Draws use the inverse CDF
+    in token-id order with u_res[b] scaled by the residual mass.
+    Returns (accept_len int32 [B] = n + 1, next_tok int32 [B]).
+    """
+    path_tok = np.asarray(path_tok)
+    top_idx = np.asarray(top_idx)
+    B, L = path_tok.shape
+    z = np.asarray(z_target, dtype=np.float64)
+    lse = target_lse(z, T)                                  # [B, L+1]
+    acc = np.zeros(B, dtype=np.int32)
+    nxt = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        n = 0
+        while n < L:
+            x = path_tok[b, n]
+            p_x = np.exp(z[b, n, x] / T - lse[b, n])
+            q_x = q[b, n][top_idx[b, n] == x].sum()
+            if u_acc[b, n] * q_x < p_x:
+                n += 1
+            else:
+                break
+        p = np.exp(z[b, n] / T - lse[b, n])
+        if n < L:
+            qv = np.zeros_like(p)
+            np.add.at(qv, top_idx[b, n], q[b, n])
+            r = np.maximum(p - qv, 0.0)
+        else:
+            r = p
+        cum = np.cumsum(r)
+        v = int(np.searchsorted(cum, u_res[b] * cum[-1], side="right"))
+        if v >= len(r) or r[v] == 0.0:                       # rounding past the end
+            v = int(np.nonzero(r > 0)[0][-1])
+        acc[b], nxt[b] = n + 1, v
+    return acc, nxt
+
+
 # ------------------------------------------------------------------ a6 verify
 def verify_greedy(path_tok: np.ndarray, target: np.ndarray):
     """Greedy verification and acceptance length ([POST] "The right token is
@@ -399,14 +502,17 @@ def expected_acceptance(p) -> float:
 def run_step_front(w, inp: Dict[str, object], blocks: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """conv chain -> logits -> top-16 -> pair scores -> path, for the given
     blocks (all when None).  Verification needs targets and is run by the
-    caller with verify_greedy.  Returns every intermediate."""
+    caller (verify_greedy, or rejection_verify for a sampled walk, whose
+    proposal distributions come back as "q").  Returns every intermediate."""
     x = inp["x"]
     convs = inp["convs"]
     anchor_tok = inp["anchor_tok"]
+    u_path = inp.get("u_path")
     if blocks is not None:
         x = x[blocks]
         convs = [dict(c, anchor_h=c["anchor_h"][blocks]) for c in convs]
         anchor_tok = anchor_tok[blocks]
+        u_path = None if u_path is None else u_path[blocks]
     xd = as_f64(x, w.dtype)
     cd = []
     for c in convs:
@@ -429,7 +535,11 @@ def run_step_front(w, inp: Dict[str, object], blocks: Optional[np.ndarray] = Non
     if getattr(w, "gate", False):
         gate = context_gate(y.reshape(Bs * L, H), inp["Wg"], w.dtype).reshape(Bs, L, -1)
     S0, S = pair_scores(tv, ti, anchor_tok, inp["U"], inp["Vf"], w.dtype, gate)
-    walk = path_select_greedy if getattr(w, "walk", "viterbi") == "greedy" else path_select
-    slot, tok, score = walk(S0, S, ti)
+    walk = getattr(w, "walk", "viterbi")
+    q = score = None
+    if walk == "sample":
+        slot, tok, q = sample_path(S0, S, ti, w.temperature, u_path)
+    else:
+        slot, tok, score = (path_select_greedy if walk == "greedy" else path_select)(S0, S, ti)
     return {"y": y, "z": z, "top_val": tv, "top_idx": ti, "gate": gate, "S0": S0, "S": S,
-            "path_slot": slot, "path_tok": tok, "path_score": score}
+            "path_slot": slot, "path_tok": tok, "path_score": score, "q": q}

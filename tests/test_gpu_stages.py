@@ -16,6 +16,15 @@ Bars (floating point from the arithmetic, integers exact):
             reproduces the ungated kernel bit for bit
   path      bit-exact slots, tokens and fp32 score for both walks (the
             oracle decides in fp32)
+  sampling  slots equal wherever the uniform is more than 1e-5 from a bin
+            edge of the oracle's fp64 inverse CDF (decided before the first
+            closer one); |q - q_ora| <= 2e-6
+  lse       |lse - lse_ora| <= (V/256 + 16) 2^-24 + 2^-23 |lse| (fp32 sums of
+            V/256 terms per thread, then a tree)
+  rejection accept lengths equal wherever every accept decision is clear by
+            2e-4 relative; the verifier's token equal wherever u * mass is
+            1e-5 of the mass away from every bin edge, else inside that
+            window; emitted tokens follow the target (chi-square, GPU)
   verify    exact
 """
 import numpy as np
@@ -368,6 +377,167 @@ def test_path_select_all_tied_takes_slot_zero():
     S = np.zeros((B, L - 1, 16, 16), np.float32)
     slot, _, score = bd.path_select(torch.from_numpy(S0).to(DEV), torch.from_numpy(S).to(DEV), None)
     assert (slot.cpu().numpy() == 0).all() and (score.cpu().numpy() == 0).all()
+
+
+# ------------------------------------------------------------------ sampling + rejection
+SAMPLE_TOL = 1e-5
+
+
+def decided_prefix(margin, tol):
+    """Per block, the number of leading positions whose decision is clear."""
+    bad = margin <= tol
+    return np.where(bad.any(axis=1), bad.argmax(axis=1), margin.shape[1])
+
+
+@pytest.mark.parametrize("B,L,T", [(1, 1, 1.0), (7, 2, 0.7), (64, 8, 1.0), (33, 16, 2.0),
+                                   (5, 64, 1.0), (300, 3, 0.3)])
+def test_path_sample_parity(B, L, T):
+    g = np.random.default_rng(B * L + 7)
+    S0 = (g.standard_normal((B, 16)) * 2).astype(np.float32)
+    S = g.standard_normal((B, L - 1, 16, 16)).astype(np.float32)
+    ti = g.integers(0, 151936, (B, L, 16)).astype(np.int32)
+    u = g.random((B, L)).astype(np.float32)
+    ws, wt, wq = O.sample_path(S0, S, ti, T, u)
+    slot, tok, q = bd.path_sample(torch.from_numpy(S0).to(DEV),
+                                  torch.from_numpy(S).to(DEV) if L > 1 else None,
+                                  torch.from_numpy(ti).to(DEV), torch.from_numpy(u).to(DEV), T)
+    slot, tok, q = slot.cpu().numpy(), tok.cpu().numpy(), q.cpu().numpy()
+    k = decided_prefix(O.sample_margin(wq, u), SAMPLE_TOL)
+    assert (k == L).mean() >= 0.95
+    for b in range(B):
+        assert slot[b, :k[b]].tolist() == ws[b, :k[b]].tolist(), b
+        assert tok[b, :k[b]].tolist() == wt[b, :k[b]].tolist(), b
+        upto = min(k[b] + 1, L)                 # q of the first undecided position still matches
+        assert np.abs(q[b, :upto] - wq[b, :upto]).max() <= 2e-6, b
+    np.testing.assert_allclose(q.sum(axis=2), 1.0, atol=2e-6)
+
+
+@pytest.mark.parametrize("R,V,T,neg", [(1, 16, 1.0, False), (7, 1001, 0.7, False),
+                                       (64, 151936, 1.0, False), (3, 4096, 2.0, True)])
+def test_target_lse_parity(R, V, T, neg):
+    g = np.random.default_rng(R + V)
+    z = (g.standard_normal((R, V)) * 3).astype(np.float32)
+    if neg:
+        z[:, ::3] = -np.inf                     # tokens with no mass
+    want = O.target_lse(z, T)
+    got = bd.target_lse(torch.from_numpy(z).to(DEV), T).cpu().numpy()
+    tol = (V / 256 + 16) * 2.0 ** -24 + 2.0 ** -23 * np.abs(want)
+    assert (np.abs(got - want) <= tol).all(), np.abs(got - want).max()
+
+
+def _spec_case(g, B, L, V, T):
+    """Candidates, a sampled path with its proposals (fp32), target logits
+    where some drafted tokens are likely under the target, and uniforms."""
+    ti = np.stack([np.stack([g.choice(V, 16, replace=False) for _ in range(L)])
+                   for _ in range(B)]).astype(np.int32)
+    S0 = g.standard_normal((B, 16)).astype(np.float32)
+    S = g.standard_normal((B, L - 1, 16, 16)).astype(np.float32)
+    u = g.random((B, L)).astype(np.float32)
+    slot, tok, q = O.sample_path(S0, S, ti, T, u)
+    q = q.astype(np.float32)
+    z = g.standard_normal((B, L + 1, V)).astype(np.float32)
+    bump = g.random((B, L)) < 0.6
+    for b in range(B):
+        for t in range(L):
+            if bump[b, t]:
+                z[b, t, tok[b, t]] += np.float32(np.log(V) + g.standard_normal())
+    return ti, slot, tok, q, z, g.random((B, L)).astype(np.float32), g.random(B).astype(np.float32)
+
+
+# Window for the verifier's token: the GPU's fp32 inverse CDF (4-term lane
+# sums and a 6-level tree per 256-token tile, a chunked scan over the tiles,
+# a 6-level scan inside the chosen tile, 2-ulp exponentials) stays within
+# about 40 2^-24 of the mass; 1e-5 of the mass is 4x that.  At V = 151936
+# one token's bin (~7e-6 of the mass) is narrower than the window, so there
+# the token is checked against the window only.
+RES_WIN = 1e-5
+
+
+def check_rejection(ti, slot, tok, q, z, T, ua, ur, acc, nxt):
+    """Compare GPU (acc, nxt) with the oracle under the margin rules; returns
+    how many blocks were compared exactly."""
+    B, L = tok.shape
+    V = z.shape[-1]
+    wa, wn = O.rejection_verify(tok, q.astype(np.float64), ti, z, T, ua.astype(np.float64),
+                                ur.astype(np.float64))
+    lse = O.target_lse(z, T)
+    exact = 0
+    for b in range(B):
+        clear = True
+        for t in range(min(wa[b], L)):           # every decision the oracle took
+            px = np.exp(z[b, t, tok[b, t]] / T - lse[b, t])
+            d = float(ua[b, t]) * float(q[b, t, slot[b, t]]) - px
+            if abs(d) <= 2e-4 * px:
+                clear = False
+                break
+        if not clear:
+            continue
+        assert acc[b] == wa[b], b
+        n = wa[b] - 1
+        p = np.exp(z[b, n] / T - lse[b, n])
+        if n < L:
+            qv = np.zeros(V)
+            np.add.at(qv, ti[b, n], q[b, n].astype(np.float64))
+            r = np.maximum(p - qv, 0.0)
+        else:
+            r = p
+        cum = np.cumsum(r)
+        target = float(ur[b]) * cum[-1]
+        win = RES_WIN * cum[-1]
+        v = int(nxt[b])
+        assert 0 <= v < V and r[v] > 0, b
+        lo = cum[v - 1] if v > 0 else 0.0
+        assert lo - win <= target <= cum[v] + win, b
+        edges = np.concatenate([[0.0], cum])
+        if np.min(np.abs(edges - target)) > win:
+            assert v == wn[b], b
+            exact += 1
+    return exact
+
+
+@pytest.mark.parametrize("B,L,V,T", [(50, 1, 16, 1.0), (200, 4, 1000, 1.0), (24, 8, 151936, 1.0),
+                                     (31, 3, 4099, 0.5)])
+def test_verify_rejection_parity(B, L, V, T):
+    g = np.random.default_rng(B + L + V)
+    ti, slot, tok, q, z, ua, ur = _spec_case(g, B, L, V, T)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    zd = d(z)
+    lse = bd.target_lse(zd, T)
+    acc, nxt = bd.verify_rejection(d(slot), d(tok), d(q), d(ti), zd, lse, T, d(ua), d(ur))
+    exact = check_rejection(ti, slot, tok, q, z, T, ua, ur, acc.cpu().numpy(), nxt.cpu().numpy())
+    if V <= 10000:                      # bins wider than the window: most draws decided
+        assert exact >= 0.9 * B, exact
+    a = acc.cpu().numpy()
+    assert ((a >= 1) & (a <= L + 1)).all() and len(np.unique(a)) > 1
+
+
+def test_rejection_sampling_is_lossless_on_gpu():
+    # the whole sampled walk + verification on the GPU: emitted tokens follow
+    # the target's softmax (chi-square on a 24-token vocabulary)
+    from scipy.stats import chisquare
+
+    g = np.random.default_rng(41)
+    N, L, V, T = 60000, 2, 24, 1.0
+    S0 = np.broadcast_to(g.standard_normal(16).astype(np.float32), (N, 16)).copy()
+    S = np.broadcast_to(g.standard_normal((L - 1, 16, 16)).astype(np.float32),
+                        (N, L - 1, 16, 16)).copy()
+    ti = np.broadcast_to(np.stack([g.permutation(V)[:16] for _ in range(L)]).astype(np.int32),
+                         (N, L, 16)).copy()
+    zt = (g.standard_normal((L + 1, V)) * 1.5).astype(np.float32)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    slot, tok, q = bd.path_sample(d(S0), d(S), d(ti), d(g.random((N, L)).astype(np.float32)), T)
+    zd = d(np.broadcast_to(zt, (N, L + 1, V)))
+    lse = bd.target_lse(zd, T)
+    acc, nxt = bd.verify_rejection(slot, tok, q, d(ti), zd, lse, T,
+                                   d(g.random((N, L)).astype(np.float32)),
+                                   d(g.random(N).astype(np.float32)))
+    acc, nxt, tok = acc.cpu().numpy(), nxt.cpu().numpy(), tok.cpu().numpy()
+    p = np.exp(zt / T - O.target_lse(zt, T)[:, None])
+    first = np.where(acc > 1, tok[:, 0], nxt)
+    assert chisquare(np.bincount(first, minlength=V), p[0] * N).pvalue > 1e-4
+    has2 = acc >= 2
+    second = np.where(acc > 2, tok[:, 1], nxt)[has2]
+    assert chisquare(np.bincount(second, minlength=V), p[1] * has2.sum()).pvalue > 1e-4
 
 
 # ------------------------------------------------------------------ verify

@@ -16,11 +16,18 @@ end to end (GPU stages fed by GPU stages), with the margin rule:
   max-plus walk, smallest best-vs-runner-up step gap for the greedy walk)
   exceeds 1e-3 plus the score drift the logits tolerance allows, else a
   max-plus path must be near-optimal under the oracle's scores;
-over all blocks (properties that hold at any size):
+over all blocks (properties that hold at any size, checked with test-local
+numpy on the GPU's own outputs, not through the oracle):
   sorted distinct in-range candidates whose values are their logits, path
-  tokens are candidates, the path is the oracle's walk of the GPU's own
-  scores (bit-exact), path score equals the path's score, acceptance in
-  [1, L+1] and equal to the oracle's verification of the GPU path.
+  tokens are candidates; greedy: every step is its row's first maximum;
+  max-plus: the score is the fp32 max-plus optimum of the GPU's scores;
+  the score is the path's fp32 running sum; sampled: each slot is the
+  inverse-CDF draw of its row's softmax where the uniform is clear of the
+  bin edges, and q is that softmax; acceptance in [1, L+1] and, for greedy
+  verification, the count of leading matches.
+The sampled workload compares draws and verification under margin rules
+(a uniform within 1e-5 of a bin edge, or an accept decision within 2e-4
+relative, is undecided).
 """
 import numpy as np
 import pytest
@@ -30,7 +37,7 @@ import block_drafting_amd as bd
 import oracle as O
 import workloads as WL
 from _devutil import bf16_ulp, convs_to_dev, to_dev, to_host_bits
-from test_gpu_stages import conv_mm_tolerance
+from test_gpu_stages import SAMPLE_TOL, check_rejection, conv_mm_tolerance, decided_prefix
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -40,10 +47,6 @@ MARGIN = 1e-3
 
 def _dt(w):
     return torch.bfloat16 if w.dtype == "bf16" else torch.float32
-
-
-def _walk(w):
-    return O.path_select_greedy if w.walk == "greedy" else O.path_select
 
 
 def gate_tolerance(y, Wg_f64):
@@ -68,25 +71,40 @@ def case(request):
         "anchor_tok": to_dev(inp["anchor_tok"], "i32"),
         "Wg": to_dev(inp["Wg"], w.dtype) if w.gate else None,
     }
+    sampled = w.temperature > 0
+    if sampled:
+        for k in ("u_path", "u_acc", "u_res"):
+            dev[k] = to_dev(inp[k], "f32")
     buf = bd.StepBuffers(w.B, w.L, w.H, w.V, _dt(w), DEV, n_convs=w.n_convs, keep_logits=True,
-                         gate_rank=w.r if w.gate else 0)
+                         gate_rank=w.r if w.gate else 0, sample=sampled)
     bd.run_step(buf, dev["x"], dev["convs"], dev["W"], dev["U"], dev["Vf"], dev["anchor_tok"], None,
-                Wg=dev["Wg"], walk=w.walk)
+                Wg=dev["Wg"], walk=w.walk, temperature=w.temperature, u_path=dev.get("u_path"))
     torch.cuda.synchronize()
     blocks = WL.parity_subset(w)
     ora = O.run_step_front(w, inp, blocks)
     # targets: planted from the oracle's candidates (or around its path) on the
     # subset; the other blocks get targets from the GPU's own candidates
-    tgt_sub = WL.make_targets(w, ora["top_idx"], ora["path_tok"])
     gpu_ti = buf.top_idx.view(w.B, w.L, 16).cpu().numpy()
     gpu_tok = buf.path_tok.cpu().numpy()
-    tgt = WL.make_targets(w, gpu_ti, gpu_tok)
-    tgt[blocks] = tgt_sub
-    tgt_dev = to_dev(tgt, "i32")
-    bd.verify_greedy(buf.path_tok, tgt_dev, buf.accept_len, buf.next_tok)
+    out = {"w": w, "inp": inp, "dev": dev, "buf": buf, "blocks": blocks, "ora": ora}
+    if sampled:
+        zt_sub = WL.planted_target_logits(w, ora["top_idx"], blocks)
+        zt = WL.planted_target_logits(w, gpu_ti)
+        zt[blocks] = zt_sub
+        dev["z_target"] = torch.from_numpy(zt).to(DEV)
+        bd.target_lse(dev["z_target"], w.temperature, buf.lse)
+        bd.verify_rejection(buf.path_slot, buf.path_tok, buf.q, buf.top_idx.view(w.B, w.L, 16),
+                            dev["z_target"], buf.lse, w.temperature, dev["u_acc"], dev["u_res"],
+                            buf.accept_len, buf.next_tok)
+        out.update(zt=zt, zt_sub=zt_sub)
+    else:
+        tgt_sub = WL.make_targets(w, ora["top_idx"], ora["path_tok"])
+        tgt = WL.make_targets(w, gpu_ti, gpu_tok)
+        tgt[blocks] = tgt_sub
+        bd.verify_greedy(buf.path_tok, to_dev(tgt, "i32"), buf.accept_len, buf.next_tok)
+        out.update(tgt=tgt, tgt_sub=tgt_sub)
     torch.cuda.synchronize()
-    yield {"w": w, "inp": inp, "dev": dev, "buf": buf, "blocks": blocks, "ora": ora,
-           "tgt": tgt, "tgt_sub": tgt_sub}
+    yield out
     del dev, buf
     torch.cuda.empty_cache()
 
@@ -146,8 +164,33 @@ def test_topk_pair_select_verify_stagewise(case):
     else:
         assert np.abs(S0 - ora["S0"]).max() <= 1e-4
         assert np.abs(S - ora["S"]).max() <= 1e-4
-    slot, tok, score = bd.path_select(torch.from_numpy(ora["S0"]).to(DEV), torch.from_numpy(ora["S"]).to(DEV),
-                                      torch.from_numpy(ora["top_idx"]).to(DEV), mode=w.walk)
+    dS0, dS = torch.from_numpy(ora["S0"]).to(DEV), torch.from_numpy(ora["S"]).to(DEV)
+    dti = torch.from_numpy(ora["top_idx"]).to(DEV)
+    if w.temperature > 0:
+        u = case["inp"]["u_path"][case["blocks"]]
+        slot, tok, q = bd.path_sample(dS0, dS, dti, to_dev(u, "f32"), w.temperature)
+        k = decided_prefix(O.sample_margin(ora["q"], u), SAMPLE_TOL)
+        slot, tok, q = slot.cpu().numpy(), tok.cpu().numpy(), q.cpu().numpy()
+        for b in range(Bs):
+            assert slot[b, :k[b]].tolist() == ora["path_slot"][b, :k[b]].tolist()
+            upto = min(k[b] + 1, w.L)
+            assert np.abs(q[b, :upto] - ora["q"][b, :upto]).max() <= 2e-6
+        # verification fed the oracle's path and proposals (as fp32)
+        qf = ora["q"].astype(np.float32)
+        zt = case["zt_sub"]
+        zd = torch.from_numpy(zt).to(DEV)
+        lse = bd.target_lse(zd, w.temperature)
+        ua = case["inp"]["u_acc"][case["blocks"]]
+        ur = case["inp"]["u_res"][case["blocks"]]
+        acc, nxt = bd.verify_rejection(to_dev(ora["path_slot"], "i32"), to_dev(ora["path_tok"], "i32"),
+                                       to_dev(qf, "f32"), dti, zd, lse, w.temperature,
+                                       to_dev(ua, "f32"), to_dev(ur, "f32"))
+        exact = check_rejection(ora["top_idx"], ora["path_slot"], ora["path_tok"], qf, zt,
+                                w.temperature, ua, ur, acc.cpu().numpy(), nxt.cpu().numpy())
+        print(f"sampled walk: {int((k == w.L).sum())}/{Bs} paths decided; rejection: "
+              f"{exact}/{Bs} verifier tokens compared exactly")
+        return
+    slot, tok, score = bd.path_select(dS0, dS, dti, mode=w.walk)
     np.testing.assert_array_equal(slot.cpu().numpy(), ora["path_slot"])
     np.testing.assert_array_equal(tok.cpu().numpy(), ora["path_tok"])
     np.testing.assert_array_equal(score.cpu().numpy(), ora["path_score"])
@@ -237,6 +280,24 @@ def test_end_to_end_subset(case):
     slot = buf.path_slot.cpu().numpy()[blocks]
     tok = buf.path_tok.cpu().numpy()[blocks]
     acc = buf.accept_len.cpu().numpy()[blocks]
+    if w.walk == "sample":
+        # a draw is decided when its uniform is farther from every bin edge
+        # than the scores' drift can move the edges (|dq| <= 2 |dS| / T)
+        S_g = buf.S.cpu().numpy()[blocks]
+        S0_g = buf.S0.cpu().numpy()[blocks]
+        same_cands = (ti == ora["top_idx"]).all(axis=(1, 2))
+        n_exact = 0
+        for k in range(len(blocks)):
+            if not same_cands[k]:
+                continue
+            drift = max(np.abs(S_g[k] - ora["S"][k]).max() if L > 1 else 0.0,
+                        np.abs(S0_g[k] - ora["S0"][k]).max())
+            m = O.sample_margin(ora["q"][k:k + 1], case["inp"]["u_path"][blocks[k:k + 1]])
+            if (m > SAMPLE_TOL + 2 * 16 * drift / w.temperature).all():
+                n_exact += 1
+                assert slot[k].tolist() == ora["path_slot"][k].tolist(), k
+        print(f"e2e: logits max |dz| {zdrift:.2e}; sampled paths checked exactly {n_exact}/{len(blocks)}")
+        return
     if w.walk == "greedy":
         margin = O.greedy_margin(ora["S0"], ora["S"], ora["path_slot"])
     else:
@@ -286,32 +347,61 @@ def test_properties_all_blocks(case):
         mask[ti[b, t]] = False
         above = (row[mask] > last) | ((row[mask] == last) & (np.arange(V)[mask] < ti[b, t, 15]))
         assert not above.any(), m
-    slot = buf.path_slot.cpu().numpy()
+    slot = buf.path_slot.cpu().numpy().astype(np.int64)
     tok = buf.path_tok.cpu().numpy()
-    np.testing.assert_array_equal(tok, np.take_along_axis(ti, slot[:, :, None].astype(np.int64), 2)[:, :, 0])
+    np.testing.assert_array_equal(tok, np.take_along_axis(ti, slot[:, :, None], 2)[:, :, 0])
     S0_g, S_g = buf.S0.cpu().numpy(), buf.S.cpu().numpy()
-    ws, _, wsc = _walk(w)(S0_g, S_g, ti)                           # same fp32 scores: exact
-    np.testing.assert_array_equal(slot, ws)
-    np.testing.assert_array_equal(buf.path_score.cpu().numpy(), wsc)
-    sc = O.path_scores_f64(S0_g, S_g, slot.astype(np.int64))
-    mag = O.path_scores_f64(np.abs(S0_g), np.abs(S_g), slot.astype(np.int64))
-    assert np.all(np.abs(sc - buf.path_score.cpu().numpy()) <= L * 2.0 ** -23 * mag)
+    # the rows the walk read: S0, then the successors of each chosen slot
+    bb = np.arange(B)
+    rows = np.stack([S0_g] + [S_g[bb, t - 1, slot[:, t - 1]] for t in range(1, L)], axis=1)
     acc = buf.accept_len.cpu().numpy()
-    wa, wn = O.verify_greedy(tok, case["tgt"])
-    np.testing.assert_array_equal(acc, wa)
-    np.testing.assert_array_equal(buf.next_tok.cpu().numpy(), wn)
+    nxt = buf.next_tok.cpu().numpy()
     assert ((acc >= 1) & (acc <= L + 1)).all()
+    if w.walk == "sample":
+        # each slot is the inverse-CDF draw of the softmax of its row, where
+        # the uniform is clear of the bin edges; q is that softmax
+        u = case["inp"]["u_path"]
+        e = np.exp((rows - rows.max(axis=2, keepdims=True)) / w.temperature)
+        qq = e / e.sum(axis=2, keepdims=True)
+        np.testing.assert_allclose(buf.q.cpu().numpy(), qq, atol=2e-6)
+        cum = np.cumsum(qq, axis=2)
+        clear = np.abs(cum - u[:, :, None]).min(axis=2) > SAMPLE_TOL
+        draw = (u[:, :, None] >= cum).sum(axis=2)
+        assert (slot[clear] == draw[clear]).all()
+        assert ((nxt >= 0) & (nxt < V)).all()
+        print(f"mean acceptance {acc.mean():.3f} over {B} blocks (sampled, T = {w.temperature})")
+        return
+    if w.walk == "greedy":
+        # every step takes the first maximum of its row
+        np.testing.assert_array_equal(slot, rows.argmax(axis=2))
+    else:
+        # the path's fp32 score in position order is the max-plus optimum
+        # (the same fp32 additions along the path, maxima exact)
+        delta = S0_g.copy()
+        for t in range(1, L):
+            delta = (delta[:, :, None] + S_g[:, t - 1]).max(axis=1)
+        np.testing.assert_array_equal(buf.path_score.cpu().numpy(), delta.max(axis=1))
+    run = rows[bb, 0, slot[:, 0]].copy()
+    for t in range(1, L):
+        run = (run + rows[bb, t, slot[:, t]]).astype(np.float32)
+    np.testing.assert_array_equal(buf.path_score.cpu().numpy(), run)
+    # greedy verification: leading matches with the target ids
+    tgt = case["tgt"]
+    n = np.cumprod(tok == tgt[:, :L], axis=1).sum(axis=1)
+    np.testing.assert_array_equal(acc, n + 1)
+    np.testing.assert_array_equal(nxt, tgt[bb, n])
     print(f"mean acceptance {acc.mean():.3f} over {B} blocks")
 
 
 def test_step_is_deterministic(case):
     w, buf, dev = case["w"], case["buf"], case["dev"]
-    if w.cid not in (0, 2, 5):
-        pytest.skip("checked on the tiny, the benchmark and the gated workload")
+    if w.cid not in (0, 2, 5, 7):
+        pytest.skip("checked on the tiny, the benchmark, the gated and the sampled workload")
     snap = [t.clone() for t in (buf.logits, buf.top_val, buf.top_idx, buf.S0, buf.S, buf.path_slot,
                                 buf.path_score)]
     bd.run_step(buf, dev["x"], dev["convs"], dev["W"], dev["U"], dev["Vf"], dev["anchor_tok"], None,
-                Wg=dev["Wg"], walk=w.walk)
+                Wg=dev["Wg"], walk=w.walk, temperature=w.temperature, u_path=dev.get("u_path"),
+                z_target=dev.get("z_target"), u_acc=dev.get("u_acc"), u_res=dev.get("u_res"))
     torch.cuda.synchronize()
     for a, b in zip(snap, (buf.logits, buf.top_val, buf.top_idx, buf.S0, buf.S, buf.path_slot,
                            buf.path_score)):

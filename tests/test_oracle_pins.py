@@ -448,6 +448,110 @@ def test_greedy_walk_is_never_better_than_the_best_path():
     assert s.tolist() == [[0, 0, 4, 0]]
 
 
+# ------------------------------------------------------------------ sampling walk + rejection
+def test_sample_path_inverse_cdf_hand_case():
+    # q_0 = [0.1, 0.2, 0.7, 0, ...] at T = 1 (exp(-inf) = 0 for the rest)
+    S0 = np.full((1, 16), -np.inf)
+    S0[0, :3] = np.log([1.0, 2.0, 7.0])
+    S = np.zeros((1, 1, 16, 16))
+    S[0, 0, 2, 9] = 50.0          # slot 2's successors: almost surely slot 9
+    S[0, 0, 9, 2] = 50.0          # transposed trap
+    ti = np.arange(32, dtype=np.int32).reshape(1, 2, 16)
+    for u0, want0 in ((0.05, 0), (0.1000001, 1), (0.25, 1), (0.31, 2), (0.999999, 2)):
+        slot, tok, q = O.sample_path(S0, S, ti, 1.0, np.array([[u0, 0.5]]))
+        assert slot[0, 0] == want0, u0
+        np.testing.assert_allclose(q[0, 0, :3], [0.1, 0.2, 0.7], rtol=1e-14)
+        assert q[0, 0, 3:].sum() == 0.0
+    slot, tok, q = O.sample_path(S0, S, ti, 1.0, np.array([[0.5, 0.5]]))
+    assert slot.tolist() == [[2, 9]] and tok.tolist() == [[2, 25]]
+    # temperature: q proportional to [1, 2, 7]^(1/T)
+    _, _, q = O.sample_path(S0, S, ti, 0.5, np.array([[0.5, 0.5]]))
+    np.testing.assert_allclose(q[0, 0, :3], np.array([1.0, 4.0, 49.0]) / 54.0, rtol=1e-14)
+
+
+def test_sample_path_frequencies_and_low_temperature_limit():
+    from scipy.stats import chisquare
+
+    g = np.random.default_rng(27)
+    N = 40000
+    S0 = g.standard_normal(16)
+    S = g.standard_normal((1, 16, 16))
+    u = g.random((N, 2))
+    slot, _, _ = O.sample_path(np.broadcast_to(S0, (N, 16)), np.broadcast_to(S, (N, 1, 16, 16)),
+                               np.zeros((N, 2, 16), np.int32), 1.0, u)
+    q0 = np.exp(S0) / np.exp(S0).sum()
+    q1 = np.exp(S[0]) / np.exp(S[0]).sum(axis=1, keepdims=True)      # row i: successors of i
+    joint = (q0[:, None] * q1).ravel()
+    cnt = np.bincount(slot[:, 0] * 16 + slot[:, 1], minlength=256)
+    assert chisquare(cnt, joint * N).pvalue > 1e-4
+    # T -> 0: the sampling walk becomes the greedy walk
+    B, L = 20, 5
+    S0 = g.standard_normal((B, 16))
+    S = g.standard_normal((B, L - 1, 16, 16))
+    ti = g.integers(0, 99, (B, L, 16)).astype(np.int32)
+    gs, _, _ = O.path_select_greedy(S0.astype(np.float32), S.astype(np.float32), ti)
+    ss, _, _ = O.sample_path(S0, S, ti, 1e-4, g.uniform(0.001, 0.999, (B, L)))
+    np.testing.assert_array_equal(ss, gs)
+
+
+def _tiny_spec_case(g, N, V=24, L=2):
+    S0 = g.standard_normal(16)
+    S = g.standard_normal((L - 1, 16, 16))
+    top = np.broadcast_to(np.stack([g.permutation(V)[:16] for _ in range(L)]), (N, L, 16)).copy()
+    zt = g.standard_normal((L + 1, V)) * 1.5
+    return S0, S, top.astype(np.int32), zt
+
+
+def test_rejection_verify_preserves_the_target_distribution():
+    # the losslessness claim: emitted tokens follow the target's softmax,
+    # whatever the proposal (chi-square on a 24-token vocabulary)
+    from scipy.stats import chisquare
+
+    g = np.random.default_rng(28)
+    N, V, L = 60000, 24, 2
+    S0, S, top, zt = _tiny_spec_case(g, N, V, L)
+    for T in (1.0, 0.7):
+        _, tok, q = O.sample_path(np.broadcast_to(S0, (N, 16)), np.broadcast_to(S, (N, L - 1, 16, 16)),
+                                  top, T, g.random((N, L)))
+        acc, nxt = O.rejection_verify(tok, q, top, np.broadcast_to(zt, (N, L + 1, V)), T,
+                                      g.random((N, L)), g.random(N))
+        assert ((acc >= 1) & (acc <= L + 1)).all()
+        p = np.exp(zt / T - O.target_lse(zt, T)[:, None])
+        first = np.where(acc > 1, tok[:, 0], nxt)
+        assert chisquare(np.bincount(first, minlength=V), p[0] * N).pvalue > 1e-4
+        has2 = acc >= 2
+        second = np.where(acc > 2, tok[:, 1], nxt)[has2]
+        assert chisquare(np.bincount(second, minlength=V), p[1] * has2.sum()).pvalue > 1e-4
+        has3 = acc == 3                                     # bonus token after a full block
+        assert chisquare(np.bincount(nxt[has3], minlength=V), p[2] * has3.sum()).pvalue > 1e-4
+
+
+def test_rejection_verify_limits():
+    g = np.random.default_rng(29)
+    N, V, L = 200, 40, 3
+    S0, S, top, _ = _tiny_spec_case(g, N, V, L)
+    u = g.random((N, L))
+    _, tok, q = O.sample_path(np.broadcast_to(S0, (N, 16)), np.broadcast_to(S, (N, L - 1, 16, 16)),
+                              top, 1.0, u)
+    # target = the proposal on the candidates (and nothing else): all accepted
+    zt = np.full((N, L + 1, V), -np.inf)
+    for t in range(L):
+        np.put_along_axis(zt[:, t], top[:, t].astype(np.int64), np.log(q[:, t]), axis=1)
+    zt[:, L] = 0.0
+    acc, nxt = O.rejection_verify(tok, q, top, zt, 1.0, g.random((N, L)), g.random(N))
+    assert (acc == L + 1).all()
+    # target with no mass on position 0's candidates: rejected at once, and the
+    # replacement is a non-candidate drawn by inverse CDF in token order
+    zt = np.zeros((N, L + 1, V))
+    np.put_along_axis(zt[:, 0], top[:, 0].astype(np.int64), -np.inf, axis=1)
+    ur = g.random(N)
+    acc, nxt = O.rejection_verify(tok, q, top, zt, 1.0, g.random((N, L)), ur)
+    assert (acc == 1).all()
+    for b in range(N):
+        rest = np.setdiff1d(np.arange(V), top[b, 0])       # uniform over V - 16 tokens
+        assert nxt[b] == rest[int(ur[b] * len(rest))]
+
+
 # ------------------------------------------------------------------ verify
 def test_verify_hand_cases():
     path = np.array([[1, 2, 3, 4], [1, 2, 3, 4], [1, 2, 3, 4], [9, 2, 3, 4]])

@@ -31,6 +31,8 @@ The workloads
    by a context gate from the final hidden state, greedy best-successor walk.
 6. conv-heavy body with one correction pair per 16 channels (G = H/16), the
    correction map stored transposed in bf16.
+7. 27B-shaped head sampled at T = 1, verified losslessly against synthetic
+   target logits (planted tokens over noise).
 
 The planted-target recall profile of workloads 0-2 and 4 is the per-position
 Recall@1 / Recall@16 of Table 1 of "DFlash 2: Keep Drafting Parallel"
@@ -85,6 +87,7 @@ class Workload:
     walk: str = "viterbi"  # path walk: "viterbi" (max-plus) or "greedy" (best successor)
     groups: int = 1       # correction groups of a dynamic conv (H/16: one per 16 channels)
     profile: str = "table1"  # recall profile: "table1" or "decay" (linear 0.85 -> 0.60)
+    temperature: float = 0.0  # > 0: sampled walk and lossless rejection verification
 
     @property
     def M(self) -> int:
@@ -127,6 +130,10 @@ WORKLOADS: Dict[int, Workload] = {
     # pair per 16 channels (320 groups at H = 5120).
     6: Workload(6, "conv-heavy-g16", 128, 16, 5120, 151936, 64, "bf16", 20, True, "planted",
                 False, 4, groups=320, profile="decay"),
+    # Sampling at T = 1 (the post's Table 2 T = 1 column) with lossless
+    # rejection verification against synthetic target logits.
+    7: Workload(7, "27b-sampled", 64, 8, 5120, 151936, 64, "bf16", 1, False, "logits", False, 8,
+                walk="sample", temperature=1.0),
 }
 
 
@@ -189,7 +196,7 @@ def to_bf16_bits(a: np.ndarray) -> np.ndarray:
 
 # Tensor tags (stable: changing them changes every workload).
 TAG_X, TAG_ANCHOR_H, TAG_K0, TAG_K1, TAG_PROJ, TAG_W, TAG_U, TAG_V = range(1, 9)
-TAG_ANCHOR_TOK, TAG_TARGET, TAG_WG = 9, 10, 11
+TAG_ANCHOR_TOK, TAG_TARGET, TAG_WG, TAG_UNIFORM, TAG_ZTARGET = 9, 10, 11, 12, 13
 TAG_CONV_STRIDE = 16  # conv j of a chain uses tags TAG_* + TAG_CONV_STRIDE * j
 
 
@@ -205,6 +212,7 @@ def make_inputs(w: Workload, with_head: bool = True) -> Dict[str, object]:
       U, Vf    [V, r]      low-rank pair factors (omitted when with_head is False)
       Wg       [r, H]      context-gate map, N(0, 1/H) (gated workloads only)
       anchor_tok [B]       last verified token id of each block
+      u_path, u_acc [B, L], u_res [B]   uniforms (sampled workloads only)
     Activation and weight tensors are bf16 bits or fp32 according to w.dtype.
     """
     B, L, H, V, r, s = w.B, w.L, w.H, w.V, w.r, w.seed
@@ -253,6 +261,8 @@ def make_inputs(w: Workload, with_head: bool = True) -> Dict[str, object]:
             Wg = normal_f32((r, H), 1.0 / H, s, TAG_WG)
             out["Wg"] = to_bf16_bits(Wg) if bf16 else Wg
     out["anchor_tok"] = _rng(s, TAG_ANCHOR_TOK).integers(0, V, size=B, dtype=np.int32)
+    if w.temperature > 0:
+        out.update(make_uniforms(w))
     return out
 
 
@@ -269,6 +279,9 @@ def select_blocks(inp: Dict[str, object], blocks: np.ndarray) -> Dict[str, objec
     out["x"] = inp["x"][blocks]
     out["convs"] = [dict(c, anchor_h=c["anchor_h"][blocks]) for c in inp["convs"]]
     out["anchor_tok"] = inp["anchor_tok"][blocks]
+    for k in ("u_path", "u_acc", "u_res"):
+        if k in inp:
+            out[k] = inp[k][blocks]
     return out
 
 
@@ -326,6 +339,42 @@ def mixed_targets(path_tok: np.ndarray, V: int, seed: int, tag: int = TAG_TARGET
                 tok = int(g.integers(0, V))
             tgt[b, m] = tok
     return tgt
+
+
+def make_uniforms(w: Workload) -> Dict[str, np.ndarray]:
+    """The sampled walk's and the rejection step's random numbers, drawn here
+    and passed to both sides: u_path [B, L], u_acc [B, L], u_res [B], float32
+    in [0, 1)."""
+    g = _rng(w.seed, TAG_UNIFORM)
+    top = np.float32(np.nextafter(np.float32(1.0), np.float32(0.0)))
+
+    def unif(shape):
+        return np.minimum(g.random(shape).astype(np.float32), top)
+
+    return {"u_path": unif((w.B, w.L)), "u_acc": unif((w.B, w.L)), "u_res": unif((w.B,))}
+
+
+# Target logits: N(0, 1) noise plus a bump on the planted token.  With V =
+# 151936 the bump of 15 gives the planted token about 93% of the target's
+# probability at T = 1.
+TARGET_BUMP = 15.0
+
+
+def planted_target_logits(w: Workload, top_idx: np.ndarray, blocks: Optional[np.ndarray] = None
+                          ) -> np.ndarray:
+    """Synthetic target logits [Bs, L + 1, V] (float32) for the given blocks'
+    candidates top_idx [Bs, L, 16]: the planted token of each position is
+    chosen as planted_targets chooses it (same recall profile, same streams)
+    and gets TARGET_BUMP over N(0, 1) noise drawn per block."""
+    Bs, L, _ = top_idx.shape
+    blocks = np.arange(Bs) if blocks is None else np.asarray(blocks)
+    p1, p16 = w.recall_profile()
+    planted = planted_targets(top_idx, w.V, p1, p16, w.seed)     # [Bs, L + 1]
+    z = np.empty((Bs, L + 1, w.V), dtype=np.float32)
+    for i, b in enumerate(blocks):
+        z[i] = normal_f32((L + 1, w.V), 1.0, w.seed, TAG_ZTARGET * 1000003 + int(b))
+        z[i, np.arange(L + 1), planted[i]] += np.float32(TARGET_BUMP)
+    return z
 
 
 def make_targets(w: Workload, top_idx: np.ndarray, path_tok: Optional[np.ndarray]) -> np.ndarray:
