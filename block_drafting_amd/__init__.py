@@ -30,7 +30,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "DFlash2Error", "lib", "library_path", "twotap_conv", "twotap_conv_mm", "lmhead_logits", "topk16",
+    "DFlash2Error", "lib", "library_path", "twotap_conv", "twotap_conv_mm", "lmhead_logits",
+    "lmhead_logits_tilemax", "topk16", "topk16_tilemax",
     "topk16_workspace", "logits_topk", "logits_topk_workspace", "context_gate", "pair_score",
     "path_select", "path_sample", "target_lse", "verify_rejection", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
 ]
@@ -51,6 +52,8 @@ _SIGS = {
     "dflash2_twotap_conv": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
     "dflash2_twotap_conv_mm": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
     "dflash2_lmhead_logits": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "dflash2_lmhead_logits_tilemax": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "dflash2_topk16_tilemax": ([_P, _P, _P, _P, _I, _I, _I, _P], _I),
     "dflash2_topk16_workspace": ([_I, _I, _I], _Z),
     "dflash2_topk16": ([_P, _P, _P, _I, _I, _I, _P, _Z, _P], _I),
     "dflash2_logits_topk_workspace": ([_I, _I, _I, _I, _I, _I], _Z),
@@ -194,6 +197,43 @@ def lmhead_logits(h: torch.Tensor, W: torch.Tensor, out: Optional[torch.Tensor] 
     _check("dflash2_lmhead_logits", lib().dflash2_lmhead_logits(
         _ptr(h), _ptr(W), _ptr(out), M, H, V, _dt(h), _stream(dev)))
     return out
+
+
+TILEMAX_COLS = 256
+
+
+def lmhead_logits_tilemax(h: torch.Tensor, W: torch.Tensor, out: Optional[torch.Tensor] = None,
+                          tilemax: Optional[torch.Tensor] = None):
+    """Logits [M, V] and their 256-column tile maxima [M, ceil(V / 256)]."""
+    M, H = h.shape
+    V = W.shape[0]
+    _shape(W, (V, H), "W", h.dtype)
+    nt = (V + TILEMAX_COLS - 1) // TILEMAX_COLS
+    if out is None:
+        out = torch.empty((M, V), dtype=torch.float32, device=h.device)
+    if tilemax is None:
+        tilemax = torch.empty((M, nt), dtype=torch.float32, device=h.device)
+    _shape(out, (M, V), "logits", torch.float32)
+    _shape(tilemax, (M, nt), "tilemax", torch.float32)
+    dev = _dev(h, W, out, tilemax)
+    _check("dflash2_lmhead_logits_tilemax", lib().dflash2_lmhead_logits_tilemax(
+        _ptr(h), _ptr(W), _ptr(out), _ptr(tilemax), M, H, V, _dt(h), _stream(dev)))
+    return out, tilemax
+
+
+def topk16_tilemax(logits: torch.Tensor, tilemax: torch.Tensor, top_val=None, top_idx=None):
+    """Top-16 of logits [M, V] that reads only the tiles its maxima allow."""
+    M, V = logits.shape
+    _shape(tilemax, (M, (V + TILEMAX_COLS - 1) // TILEMAX_COLS), "tilemax", torch.float32)
+    dev = logits.device
+    if top_val is None:
+        top_val = torch.empty((M, TOPK), dtype=torch.float32, device=dev)
+    if top_idx is None:
+        top_idx = torch.empty((M, TOPK), dtype=torch.int32, device=dev)
+    _dev(logits, tilemax, top_val, top_idx)
+    _check("dflash2_topk16_tilemax", lib().dflash2_topk16_tilemax(
+        _ptr(logits), _ptr(tilemax), _ptr(top_val), _ptr(top_idx), M, V, TOPK, _stream(dev)))
+    return top_val, top_idx
 
 
 def topk16_workspace(M: int, V: int) -> int:

@@ -111,7 +111,45 @@ DFLASH2_API int dflash2_lmhead_logits(const void* h, const void* W, float* logit
   if (overlap(logits, zb, h, (size_t)M * H * esize(dtype)) ||
       overlap(logits, zb, W, (size_t)V * H * esize(dtype)))
     return DFLASH2_EINVAL;
-  return status_of(launch_lmhead(h, W, logits, M, H, V, dtype, as_stream(stream)));
+  return status_of(launch_lmhead(h, W, logits, nullptr, M, H, V, dtype, as_stream(stream)));
+}
+
+static size_t tilemax_bytes(int M, int V) {
+  return (size_t)M * ((V + kTileMaxCols - 1) / kTileMaxCols) * sizeof(float);
+}
+
+DFLASH2_API int dflash2_lmhead_logits_tilemax(const void* h, const void* W, float* logits,
+                                              float* tilemax, int M, int H, int V, int dtype,
+                                              void* stream) {
+  int st = check_lmhead(h, W, M, H, V, dtype);
+  if (st != DFLASH2_OK) return st;
+  if (M == 0) return DFLASH2_OK;
+  if (!logits || !aligned16(logits) || !tilemax || !aligned4(tilemax)) return DFLASH2_EINVAL;
+  const size_t zb = (size_t)M * V * sizeof(float);
+  const size_t tb = tilemax_bytes(M, V);
+  const size_t es = esize(dtype);
+  if (overlap(logits, zb, h, (size_t)M * H * es) || overlap(logits, zb, W, (size_t)V * H * es) ||
+      overlap(tilemax, tb, h, (size_t)M * H * es) || overlap(tilemax, tb, W, (size_t)V * H * es) ||
+      overlap(tilemax, tb, logits, zb))
+    return DFLASH2_EINVAL;
+  return status_of(launch_lmhead(h, W, logits, tilemax, M, H, V, dtype, as_stream(stream)));
+}
+
+DFLASH2_API int dflash2_topk16_tilemax(const float* logits, const float* tilemax, float* top_val,
+                                       int32_t* top_idx, int M, int V, int K, void* stream) {
+  if (K != kTopK || M < 0 || V < kTopK || (long long)M * V > (1LL << 40)) return DFLASH2_EINVAL;
+  if (M == 0) return DFLASH2_OK;
+  if (!logits || !aligned4(logits) || !tilemax || !aligned4(tilemax)) return DFLASH2_EINVAL;
+  if (!top_val || !top_idx || !aligned4(top_val) || !aligned4(top_idx)) return DFLASH2_EINVAL;
+  const size_t zb = (size_t)M * V * sizeof(float);
+  const size_t ob = (size_t)M * kTopK * 4;
+  const size_t tb = tilemax_bytes(M, V);
+  if (overlap(top_val, ob, logits, zb) || overlap(top_idx, ob, logits, zb) ||
+      overlap(top_val, ob, tilemax, tb) || overlap(top_idx, ob, tilemax, tb) ||
+      overlap(top_val, ob, top_idx, ob))
+    return DFLASH2_EINVAL;
+  return status_of(
+      launch_topk16_tilemax(logits, tilemax, top_val, top_idx, M, V, as_stream(stream)));
 }
 
 DFLASH2_API size_t dflash2_topk16_workspace(int M, int V, int K) {
@@ -147,10 +185,12 @@ DFLASH2_API int dflash2_topk16(const float* logits, float* top_val, int32_t* top
   return status_of(launch_topk16(logits, top_val, top_idx, M, V, workspace, as_stream(stream)));
 }
 
+// Workspace of dflash2_logits_topk: the tile maxima, then (when the caller
+// gives no logits buffer) the logits, each start 256-byte aligned.
 DFLASH2_API size_t dflash2_logits_topk_workspace(int M, int H, int V, int K, int dtype,
                                                  int logits_given) {
   if (K != kTopK || M < 0 || V < kTopK || H < 8 || !valid_dtype(dtype)) return 0;
-  size_t ws = (topk16_workspace_bytes(M, V) + 255) & ~(size_t)255;
+  size_t ws = (tilemax_bytes(M, V) + 255) & ~(size_t)255;
   if (!logits_given) ws += (size_t)M * V * sizeof(float);
   return ws;
 }
@@ -169,7 +209,8 @@ DFLASH2_API int dflash2_logits_topk(const void* h, const void* W, float* logits,
   if (need > 0 && (!workspace || workspace_bytes < need ||
                    (reinterpret_cast<uintptr_t>(workspace) & 255) != 0))
     return DFLASH2_EWORKSPACE;
-  const size_t part = (topk16_workspace_bytes(M, V) + 255) & ~(size_t)255;
+  const size_t part = (tilemax_bytes(M, V) + 255) & ~(size_t)255;
+  float* tmax = static_cast<float*>(workspace);
   float* z = logits ? logits : reinterpret_cast<float*>(static_cast<char*>(workspace) + part);
   const size_t zb = (size_t)M * V * sizeof(float);
   const size_t es = esize(dtype);
@@ -178,10 +219,15 @@ DFLASH2_API int dflash2_logits_topk(const void* h, const void* W, float* logits,
       overlap(top_idx, (size_t)M * kTopK * 4, z, zb) ||
       (logits && need && overlap(workspace, need, logits, zb)))
     return DFLASH2_EINVAL;
+  if (overlap(top_val, (size_t)M * kTopK * 4, workspace, need) ||
+      overlap(top_idx, (size_t)M * kTopK * 4, workspace, need) ||
+      overlap(workspace, need, h, (size_t)M * H * es) ||
+      overlap(workspace, need, W, (size_t)V * H * es))
+    return DFLASH2_EINVAL;
   hipStream_t s = as_stream(stream);
-  hipError_t e = launch_lmhead(h, W, z, M, H, V, dtype, s);
+  hipError_t e = launch_lmhead(h, W, z, tmax, M, H, V, dtype, s);
   if (e != hipSuccess) return DFLASH2_EHIP;
-  return status_of(launch_topk16(z, top_val, top_idx, M, V, workspace, s));
+  return status_of(launch_topk16_tilemax(z, tmax, top_val, top_idx, M, V, s));
 }
 
 static int pair_score(const float* top_val, const int32_t* top_idx, const int32_t* anchor_tok,

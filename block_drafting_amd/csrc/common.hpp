@@ -28,6 +28,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// Value of lane (lane ^ J) for 32-bit data.  Partners within a 16-lane row
+// use DPP (quad_perm; xor 4 = quad reverse after row_half_mirror; xor 8 =
+// row_half_mirror after row_mirror), xor 16 uses ds_swizzle (bit-mask mode),
+// xor 32 a ds_bpermute.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  if constexpr (J == 1) {
+    return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4) {
+    const uint32_t h = __builtin_amdgcn_update_dpp(0u, v, 0x141, 0xf, 0xf, false);
+    return __builtin_amdgcn_update_dpp(0u, h, 0x1B, 0xf, 0xf, false);
+  } else if constexpr (J == 8) {
+    const uint32_t m = __builtin_amdgcn_update_dpp(0u, v, 0x140, 0xf, 0xf, false);
+    return __builtin_amdgcn_update_dpp(0u, m, 0x141, 0xf, 0xf, false);
+  } else if constexpr (J == 16) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+  } else {
+    return (uint32_t)__shfl_xor((int)v, 32, 64);
+  }
+}
+
 // Workgroup i of a launch runs on XCD i mod 8, and each XCD has its own L2.
 // Bijection from dispatch order to tile order that gives XCD x a contiguous
 // range of tiles, so tiles that share operand rows share an L2.
@@ -50,13 +73,18 @@ hipError_t launch_twotap_conv_mm(const void* x, const void* anchor_h, void* y, c
                                  const float* k1, const void* projT, int groups, int B, int L,
                                  int H, hipStream_t s);
 
-hipError_t launch_lmhead(const void* h, const void* W, float* logits, int M, int H, int V,
-                         int dtype, hipStream_t s);
+// Columns per tile maximum (the bf16 GEMM's N tile).
+constexpr int kTileMaxCols = 256;
+
+hipError_t launch_lmhead(const void* h, const void* W, float* logits, float* tmax, int M, int H,
+                         int V, int dtype, hipStream_t s);
 
 int topk16_splits(int M, int V);
 size_t topk16_workspace_bytes(int M, int V);
 hipError_t launch_topk16(const float* logits, float* top_val, int32_t* top_idx, int M, int V,
                          void* workspace, hipStream_t s);
+hipError_t launch_topk16_tilemax(const float* logits, const float* tmax, float* top_val,
+                                 int32_t* top_idx, int M, int V, hipStream_t s);
 
 hipError_t launch_pair_score(const float* top_val, const int32_t* top_idx,
                              const int32_t* anchor_tok, const void* U, const void* Vf,

@@ -15,6 +15,14 @@
 // from HBM about once and re-read from that XCD's L2.
 //
 // fp32 path (fp32 workloads): a plain per-output fp32 dot product.
+//
+// Optionally the kernel also writes, for every row, the maximum over each
+// 256-column N tile (tmax [M, ceil(N / 256)]).  The 16th largest of a row's
+// tile maxima bounds its 16th largest logit from below, so the top-16 only
+// has to read the tiles whose maximum reaches that bound (usually 16 of the
+// 594 at V = 151936) instead of the whole row.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace dflash2 {
@@ -39,7 +47,7 @@ struct GemmCfg {
 template <int BM, int BN, int BK, int WM, int WN, bool KTAIL>
 __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bw, float* __restrict__ C,
-    int M, int N, int K, int mtiles, int ntiles) {
+    float* __restrict__ tmax, int M, int N, int K, int mtiles, int ntiles) {
   using Cfg = GemmCfg<BM, BN, BK, WM, WN>;
   constexpr int kT = Cfg::kThreads;
   constexpr int kLdk = Cfg::kLdk;
@@ -143,11 +151,13 @@ __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
   };
 
   // One K slice (kSteps k-steps of 16).  Rs holds slice kt+1 on entry; it is
-  // written to the other LDS stage during step 1 and then reloaded with
-  // slice kt+3.
+  // written to the other LDS stage during step 1 and reloaded with slice
+  // kt+3 right after (the earlier the loads go out, the more of their
+  // latency the next two slices hide: ~2% faster than issuing them after
+  // the barrier).
   //   step kk:   read fragments of step kk+1 | 16 MFMAs on step kk
-  //   step 1:    + the stage writes, one per MFMA
-  //   step S-2:  + barrier, then the global loads of slice kt+3
+  //   step 1:    + the stage writes, one per MFMA, then the global loads of slice kt+3
+  //   step S-2:  + barrier
   //   step S-1:  the fragment reads come from the next stage (visible after the barrier)
   // The body has no branches: a conditional body makes the register
   // allocator spill the accumulators.
@@ -172,9 +182,12 @@ __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (kk == 1) {
+        gload(Rs, (kt + 3) * BK);  // Rs is in LDS now: reload it at once
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (kk == kSteps - 2) {
         __syncthreads();
-        gload(Rs, (kt + 3) * BK);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -195,6 +208,69 @@ __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
 
   // Accumulator layout of a 32x32 block: register r of lane l holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.  Half-waves store 128-byte runs.
+  if (tmax) {
+    // Maximum of every row over this tile's BN columns (columns past N
+    // excluded, NaN ignored by fmaxf).  Each lane holds kTm * 16 rows of its
+    // half-wave's 32 columns; a reduce-scatter across the 32 lanes (each
+    // exchange step halves the values a lane keeps: 62 lane exchanges in
+    // place of 64 full butterflies) leaves every lane two finished rows,
+    // and the WN waves of a row band meet in LDS.
+    static_assert(kTm * 16 == 64, "reduce-scatter sized for 64 rows per lane");
+    float* red = reinterpret_cast<float*>(lds);  // [WN][BM]; the stages are done
+    float v[64];
+#pragma unroll
+    for (int i = 0; i < kTm; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kTn; ++j) {
+          const int col = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
+          if (col < N) x = fmaxf(x, acc[i][j][r]);
+        }
+        v[i * 16 + r] = x;
+      }
+    // step with partner lane ^ D on N values: the lane with bit D set keeps
+    // the upper half, the other the lower half, each taking the partner's max
+    auto step = [&](auto dtag, int n) {
+      constexpr int D = decltype(dtag)::value;
+      const bool hi = (lane & D) != 0;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        if (k < n / 2) {
+          const float send = hi ? v[k] : v[k + n / 2];
+          const float keep = hi ? v[k + n / 2] : v[k];
+          const float recv = __uint_as_float(xor_lane<D>(__float_as_uint(send)));
+          v[k] = fmaxf(keep, recv);
+        }
+      }
+    };
+    step(std::integral_constant<int, 1>{}, 64);
+    step(std::integral_constant<int, 2>{}, 32);
+    step(std::integral_constant<int, 4>{}, 16);
+    step(std::integral_constant<int, 8>{}, 8);
+    step(std::integral_constant<int, 16>{}, 4);
+    __syncthreads();  // every wave is done with the stages
+    // v[j] now holds value index 32 b0 + 16 b1 + 8 b2 + 4 b3 + 2 b4 + j
+    // (b_s = bit s of the lane within its half), index = i * 16 + r
+    const int l5 = lane & 31;
+    const int base = ((l5 & 1) << 5) | ((l5 & 2) << 3) | ((l5 & 4) << 1) | ((l5 & 8) >> 1) |
+                     ((l5 & 16) >> 3);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int idx = base + j;
+      const int i = idx >> 4;
+      const int r = idx & 15;
+      red[wn * BM + wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)] = v[j];
+    }
+    __syncthreads();
+    for (int row = tid; row < BM; row += kT) {
+      float v = red[row];
+#pragma unroll
+      for (int w = 1; w < WN; ++w) v = fmaxf(v, red[w * BM + row]);
+      if (m0 + row < M) tmax[(size_t)(m0 + row) * ntiles + nt] = v;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < kTm; ++i) {
 #pragma unroll
@@ -238,33 +314,57 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(const float* __restrict
     if (m0 + mm < M) C[(size_t)(m0 + mm) * N + n] = acc[mm];
 }
 
+// Row maxima of every kTileMaxCols-column tile of finished logits (the
+// fp32 path, whose GEMM does not produce them): one wave per (row, tile).
+__global__ __launch_bounds__(256) void tilemax_kernel(const float* __restrict__ z, int M, int V,
+                                                      int nt, float* __restrict__ tmax) {
+  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (long long)M * nt) return;
+  const int lane = threadIdx.x & 63;
+  const int m = (int)(w / nt);
+  const int t = (int)(w - (long long)m * nt);
+  float v = -INFINITY;
+  for (int c = t * kTileMaxCols + lane; c < min(V, (t + 1) * kTileMaxCols); c += 64)
+    v = fmaxf(v, z[(size_t)m * V + c]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  if (lane == 0) tmax[w] = v;
+}
+
 template <int BM, int BN, int BK, int WM, int WN>
-hipError_t launch_bf16(const uint16_t* h, const uint16_t* W, float* z, int M, int H, int V,
-                       hipStream_t s) {
+hipError_t launch_bf16(const uint16_t* h, const uint16_t* W, float* z, float* tmax, int M, int H,
+                       int V, hipStream_t s) {
+  static_assert(BN == kTileMaxCols, "tile maxima follow the N tiles");
   const int mt = (M + BM - 1) / BM;
   const int nt = (V + BN - 1) / BN;
   if (H % BK == 0)
     hipLaunchKernelGGL((lmhead_bf16_kernel<BM, BN, BK, WM, WN, false>), dim3((unsigned)(mt * nt)),
-                       dim3(WM * WN * 64), 0, s, h, W, z, M, V, H, mt, nt);
+                       dim3(WM * WN * 64), 0, s, h, W, z, tmax, M, V, H, mt, nt);
   else
     hipLaunchKernelGGL((lmhead_bf16_kernel<BM, BN, BK, WM, WN, true>), dim3((unsigned)(mt * nt)),
-                       dim3(WM * WN * 64), 0, s, h, W, z, M, V, H, mt, nt);
+                       dim3(WM * WN * 64), 0, s, h, W, z, tmax, M, V, H, mt, nt);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_lmhead(const void* h, const void* W, float* logits, int M, int H, int V,
-                         int dtype, hipStream_t s) {
+hipError_t launch_lmhead(const void* h, const void* W, float* logits, float* tmax, int M, int H,
+                         int V, int dtype, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if (dtype == 1) {
     const uint16_t* hb = static_cast<const uint16_t*>(h);
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
-    return launch_bf16<256, 256, 64, 2, 4>(hb, Wb, logits, M, H, V, s);
+    return launch_bf16<256, 256, 64, 2, 4>(hb, Wb, logits, tmax, M, H, V, s);
   }
   const dim3 grid((unsigned)((V + 255) / 256), (unsigned)((M + 7) / 8));
   hipLaunchKernelGGL(lmhead_f32_kernel, grid, dim3(256), 0, s, static_cast<const float*>(h),
                      static_cast<const float*>(W), logits, M, V, H);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !tmax) return e;
+  const int nt = (V + kTileMaxCols - 1) / kTileMaxCols;
+  const long long waves = (long long)M * nt;
+  hipLaunchKernelGGL(tilemax_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, logits, M,
+                     V, nt, tmax);
   return hipGetLastError();
 }
 

@@ -48,16 +48,19 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
 struct WaveTop16 {
   uint64_t key;   // this lane's slot
   uint64_t thr;   // 16th key (wave-uniform)
-  float thr_f;    // value of the 16th key; -inf while the list is not full
+  float thr_f;    // filter value: the 16th key's value (-inf while the list is
+                  // not full), raised to floor_f
+  float floor_f;  // a known lower bound of the final 16th value (-inf if none)
 
   __device__ void init() {
     key = 0;
     thr = 0;
     thr_f = -INFINITY;
+    floor_f = -INFINITY;
   }
   __device__ void refresh() {
     thr = readlane64(key, 15);
-    thr_f = thr ? val_of((uint32_t)(thr >> 32)) : -INFINITY;
+    thr_f = fmaxf(thr ? val_of((uint32_t)(thr >> 32)) : -INFINITY, floor_f);
   }
 };
 
@@ -65,29 +68,6 @@ __device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
   const uint32_t lo = __shfl((int)(uint32_t)v, src, 64);
   const uint32_t hi = __shfl((int)(uint32_t)(v >> 32), src, 64);
   return ((uint64_t)hi << 32) | lo;
-}
-
-// Value of lane (lane ^ J) for 32-bit data.  Partners within a 16-lane row
-// use DPP (quad_perm; xor 4 = quad reverse after row_half_mirror; xor 8 =
-// row_half_mirror after row_mirror), xor 16 uses ds_swizzle (bit-mask mode),
-// xor 32 a ds_bpermute.
-template <int J>
-__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
-  if constexpr (J == 1) {
-    return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
-  } else if constexpr (J == 2) {
-    return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
-  } else if constexpr (J == 4) {
-    const uint32_t h = __builtin_amdgcn_update_dpp(0u, v, 0x141, 0xf, 0xf, false);
-    return __builtin_amdgcn_update_dpp(0u, h, 0x1B, 0xf, 0xf, false);
-  } else if constexpr (J == 8) {
-    const uint32_t m = __builtin_amdgcn_update_dpp(0u, v, 0x140, 0xf, 0xf, false);
-    return __builtin_amdgcn_update_dpp(0u, m, 0x141, 0xf, 0xf, false);
-  } else if constexpr (J == 16) {
-    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
-  } else {
-    return (uint32_t)__shfl_xor((int)v, 32, 64);
-  }
 }
 
 template <int J>
@@ -296,7 +276,113 @@ __global__ __launch_bounds__(64) void topk16_merge_kernel(const uint64_t* __rest
   write_final(top, top_val + (size_t)m * kTopK, top_idx + (size_t)m * kTopK);
 }
 
+// Top-16 of a row that comes with its tile maxima tmax [nt] (tile t covers
+// columns [256 t, 256 t + 256)).  Any 16 tile maxima are 16 distinct
+// elements, so if tau is at most the 16th largest of some 16 of them, the
+// row's 16th best value is >= tau and every top-16 element lies in a tile
+// whose maximum is >= tau (an element of any other tile is below tau and
+// below 16 others).  One wave per row: each lane takes the maximum of its
+// share of the tile maxima, tau = the 16th largest of those 64 lane maxima
+// (one sort; usually 16-20 tiles then reach it), and only the tiles that
+// reach tau are streamed, kPruneBatch at a time in flight, through the same
+// filter and list as the full scan.  The result is the full scan's, bit for
+// bit.
+constexpr int kPruneBatch = 16;
+constexpr int kMaxChunk = 16;  // tile maxima per lane per pass (1024 tiles)
+
+template <int VEC>
+__global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restrict__ logits,
+                                                           const float* __restrict__ tmax, int V,
+                                                           int nt, float* __restrict__ top_val,
+                                                           int32_t* __restrict__ top_idx) {
+  __shared__ uint64_t buf[kBuf];
+  __shared__ int list[64 * kMaxChunk];
+  __shared__ float tcache[64 * kMaxChunk];
+  __shared__ f32x4_t park[kPruneBatch][64];
+  const int m = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* tm = tmax + (size_t)m * nt;
+  const float* row = logits + (size_t)m * V;
+  // 1. tau from the lane maxima (all loads of a pass in flight at once)
+  uint32_t lmax = 0;  // ord of this lane's largest tile maximum (0: none)
+  for (int c0 = 0; c0 < nt; c0 += 64 * kMaxChunk) {
+    float v[kMaxChunk];
+#pragma unroll
+    for (int k = 0; k < kMaxChunk; ++k) {
+      const int t = c0 + k * 64 + lane;
+      v[k] = t < nt ? tm[t] : -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxChunk; ++k) {
+      if (c0 + k * 64 + lane < nt) lmax = max(lmax, ord_of(v[k]));
+      if (c0 == 0) tcache[k * 64 + lane] = v[k];  // the first pass is read again below
+    }
+  }
+  const uint64_t srt = wave_sort_desc(((uint64_t)lmax << 32) | (uint32_t)(~lane));
+  const uint32_t tau = nt >= 16 ? (uint32_t)(readlane64(srt, 15) >> 32) : 0u;
+  // 2. stream the tiles that reach tau, listed in LDS in tile order; no
+  //    element below tau can rank, so the filter starts at tau
+  WaveTop16 top;
+  top.init();
+  if (tau) top.floor_f = top.thr_f = val_of(tau);
+  int count = 0;
+  for (int c0 = 0; c0 < nt; c0 += 64 * kMaxChunk) {
+    int nsel = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxChunk; ++k) {
+      const int t = c0 + k * 64 + lane;
+      const bool s = t < nt && ord_of(c0 == 0 ? tcache[k * 64 + lane] : tm[t]) >= tau;
+      const uint64_t sel = __ballot(s);
+      if (s) list[nsel + lanes_below(sel)] = t;
+      nsel += __popcll(sel);
+    }
+    for (int b0 = 0; b0 < nsel; b0 += kPruneBatch) {
+      const int ns = min(kPruneBatch, nsel - b0);
+      // all of the batch's loads in flight, then parked in LDS so that the
+      // filter loop below can walk them without indexing registers
+#pragma unroll
+      for (int k = 0; k < kPruneBatch; ++k) {
+        const bool live = k < ns;
+        const int c = (live ? list[b0 + k] : 0) * kTileMaxCols + lane * 4;
+        f32x4_t q;
+        if (VEC == 4 && live && c + 4 <= V) {
+          q = *reinterpret_cast<const f32x4_t*>(row + c);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) q[i] = (live && c + i < V) ? row[c + i] : 0.f;
+        }
+        park[k][lane] = q;
+      }
+      for (int k = 0; k < ns; ++k) {  // wave-uniform
+        const int c = list[b0 + k] * kTileMaxCols + lane * 4;
+        const f32x4_t q = park[k][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool p = c + i < V && may_enter(q[i], top.thr_f);
+          append(top, buf, count, p, key_of(q[i], (uint32_t)(c + i)));
+        }
+      }
+    }
+  }
+  if (count) flush(top, buf, count);
+  write_final(top, top_val + (size_t)m * kTopK, top_idx + (size_t)m * kTopK);
+}
+
 }  // namespace
+
+hipError_t launch_topk16_tilemax(const float* logits, const float* tmax, float* top_val,
+                                 int32_t* top_idx, int M, int V, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int nt = (V + kTileMaxCols - 1) / kTileMaxCols;
+  const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
+  if (vec)
+    hipLaunchKernelGGL(topk16_pruned_kernel<4>, dim3((unsigned)M), dim3(64), 0, s, logits, tmax, V,
+                       nt, top_val, top_idx);
+  else
+    hipLaunchKernelGGL(topk16_pruned_kernel<1>, dim3((unsigned)M), dim3(64), 0, s, logits, tmax, V,
+                       nt, top_val, top_idx);
+  return hipGetLastError();
+}
 
 int topk16_splits(int M, int V) {
   // About 512 blocks (2048 waves, each with 8 loads per lane in flight) and

@@ -3,8 +3,8 @@
  *
  * The step (per block of L drafted positions):
  *   1. two-tap local conv            dflash2_twotap_conv
- *   2. LM-head logits + top-16       dflash2_logits_topk  (= dflash2_lmhead_logits
- *                                                            then dflash2_topk16)
+ *   2. LM-head logits + top-16       dflash2_logits_topk  (= dflash2_lmhead_logits_tilemax
+ *                                                            then dflash2_topk16_tilemax)
  *   3. adjacent-pair scores          dflash2_pair_score
  *   4. max-plus path walk            dflash2_path_select
  *   5. greedy verification           dflash2_verify_greedy
@@ -122,6 +122,32 @@ int dflash2_twotap_conv_mm(const void* x, const void* anchor_h, void* y,
 int dflash2_lmhead_logits(const void* h, const void* W, float* logits,
                           int M, int H, int V, int dtype, void* stream);
 
+/* Columns covered by one tile maximum (see dflash2_lmhead_logits_tilemax). */
+#define DFLASH2_TILEMAX_COLS 256
+
+/*
+ * dflash2_lmhead_logits that also writes the row maxima of every
+ * DFLASH2_TILEMAX_COLS-column tile of the logits:
+ *   tilemax[m, t] = max over n in [256 t, min(256 t + 256, V)) of logits[m, n]
+ * (NaN entries ignored; a tile with nothing else gives -inf).
+ * tilemax [M, ceil(V / 256)] fp32,
+ * 4-byte aligned, overlapping nothing else.  The bf16 GEMM computes them in
+ * its epilogue from the values it stores; fp32 runs one extra pass.
+ */
+int dflash2_lmhead_logits_tilemax(const void* h, const void* W, float* logits, float* tilemax,
+                                  int M, int H, int V, int dtype, void* stream);
+
+/*
+ * dflash2_topk16 given the tile maxima of the same logits (exactly as
+ * dflash2_lmhead_logits_tilemax writes them).  The 16 largest tile maxima
+ * are 16 distinct elements, so every top-16 element lies in a tile whose
+ * maximum reaches the 16th largest maximum; only those tiles are read
+ * (usually 16 of them).  Same order, ties and special values as
+ * dflash2_topk16, bit for bit.  Needs no workspace.
+ */
+int dflash2_topk16_tilemax(const float* logits, const float* tilemax, float* top_val,
+                           int32_t* top_idx, int M, int V, int K, void* stream);
+
 /* Bytes of workspace dflash2_topk16 needs for an [M, V] problem with K = 16. */
 size_t dflash2_topk16_workspace(int M, int V, int K);
 
@@ -140,14 +166,16 @@ int dflash2_topk16(const float* logits, float* top_val, int32_t* top_idx,
                    void* stream);
 
 /*
- * Workspace for dflash2_logits_topk.  logits_given != 0: the caller passes a
- * logits buffer; 0: the logits are produced in the workspace.
+ * Workspace for dflash2_logits_topk: the tile maxima, and the logits too
+ * when logits_given == 0 (the caller passes no logits buffer).
  */
 size_t dflash2_logits_topk_workspace(int M, int H, int V, int K, int dtype, int logits_given);
 
 /*
- * Logits and top-16 in one call (dflash2_lmhead_logits then dflash2_topk16).
- * logits may be NULL (then the workspace holds them, see the query above).
+ * Logits and top-16 in one call: dflash2_lmhead_logits_tilemax then
+ * dflash2_topk16_tilemax, the tile maxima in the workspace.  logits may be
+ * NULL (then the workspace holds them, see the query above).  The workspace
+ * is required (256-byte aligned) whenever M > 0.
  */
 int dflash2_logits_topk(const void* h, const void* W, float* logits,
                         float* top_val, int32_t* top_idx,

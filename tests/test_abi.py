@@ -115,6 +115,24 @@ def test_lmhead_and_topk_validation():
                                  None, 0, None) == EWS                             # no room for logits
 
 
+def test_tilemax_validation():
+    L = bd.lib()
+    f = L.dflash2_lmhead_logits_tilemax
+    z, tm = P + 0x10000000, P + 0x20000000
+    assert f(P, Q, z, None, 8, 64, 1000, 1, None) == EINVAL              # tilemax missing
+    assert f(P, Q, z, z + 64, 8, 64, 1000, 1, None) == EINVAL            # overlaps the logits
+    assert f(P, Q, z, tm + 2, 8, 64, 1000, 1, None) == EINVAL            # misaligned
+    assert f(P, Q, z, tm, 8, 60, 1000, 1, None) == EINVAL                # H % 8
+    assert f(P, Q, z, tm, 0, 64, 1000, 1, None) == 0
+    k = L.dflash2_topk16_tilemax
+    assert k(z, tm, P, P + 4096, 8, 1000, 8, None) == EINVAL             # K != 16
+    assert k(z, None, P, P + 4096, 8, 1000, 16, None) == EINVAL
+    assert k(z, tm, tm, P + 4096, 8, 1000, 16, None) == EINVAL           # top_val over tilemax
+    assert k(z, tm, P, P, 8, 1000, 16, None) == EINVAL                   # outputs alias
+    assert k(z, tm, P, P + 4096, 0, 1000, 16, None) == 0
+    assert L.dflash2_logits_topk_workspace(512, 5120, 151936, 16, 1, 1) >= 512 * 594 * 4
+
+
 def test_pair_select_verify_validation():
     L = bd.lib()
     ps = L.dflash2_pair_score

@@ -219,6 +219,63 @@ def test_topk_ties_zeros_nan_inf_and_adversarial_order():
     _topk_check(nan_rows)
 
 
+def _tile_max(z):
+    """Row maxima of 256-column tiles, NaN ignored (a tile of only NaN gives
+    -inf), test-local numpy."""
+    M, V = z.shape
+    nt = (V + 255) // 256
+    pad = np.full((M, nt * 256), -np.inf, np.float32)
+    pad[:, :V] = np.where(np.isnan(z), -np.inf, z)
+    return pad.reshape(M, nt, 256).max(axis=2).astype(np.float32)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("M,H,V", [(1, 8, 16), (37, 64, 1000), (300, 136, 4099), (64, 256, 151936)])
+def test_lmhead_tilemax_is_the_max_of_the_stored_logits(dt, M, H, V):
+    g = np.random.default_rng(M + V)
+    h = _bits_or_f32(g.standard_normal((M, H)).astype(np.float32), dt)
+    W = _bits_or_f32((g.standard_normal((V, H)) / np.sqrt(H)).astype(np.float32), dt)
+    z, tm = bd.lmhead_logits_tilemax(to_dev(h, dt), to_dev(W, dt))
+    z = z.cpu().numpy()
+    np.testing.assert_array_equal(tm.cpu().numpy(), _tile_max(z))
+    want = O.lm_logits(O.as_f64(h, dt), W, dt).astype(np.float64)
+    assert np.all(np.abs(z - want) <= 1e-3 * np.maximum(np.abs(want), 1.0))
+
+
+def _topk_tilemax_check(z):
+    tv, ti = bd.topk16_tilemax(torch.from_numpy(z).to(DEV), torch.from_numpy(_tile_max(z)).to(DEV))
+    wv, wi = O.topk16(z)
+    np.testing.assert_array_equal(ti.cpu().numpy(), wi)
+    np.testing.assert_array_equal(tv.cpu().numpy().view(np.uint32), wv.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,V", [(1, 16), (3, 17), (7, 4099), (33, 151936), (512, 4096),
+                                 (5, 100003), (4, 255), (2, 257)])
+def test_topk_tilemax_parity_random(M, V):
+    g = np.random.default_rng(M * V + 3)
+    _topk_tilemax_check((g.standard_normal((M, V)) * 3).astype(np.float32))
+
+
+def test_topk_tilemax_ties_zeros_nan_inf():
+    g = np.random.default_rng(11)
+    z = (np.round(g.standard_normal((6, 5000)) * 2) / 4).astype(np.float32)   # many ties
+    z[0] = 1.0                                       # every tile ties at the bound
+    z[1, :] = -0.0
+    z[1, 700:900] = 0.0                              # +0 and -0 tie
+    z[2, ::7] = np.nan
+    z[3, 1000:1300] = np.nan                         # a whole tile of NaN
+    z[4, 4990] = np.inf
+    z[4, 3] = -np.inf
+    z[5, :] = -np.inf
+    z[5, 4242] = -1.0
+    _topk_tilemax_check(z)
+    # top values spread over 16 different tiles vs packed in one
+    z = np.zeros((2, 151936), np.float32)
+    z[0, np.arange(16) * 9000] = 5.0
+    z[1, 77000:77016] = 5.0
+    _topk_tilemax_check(z)
+
+
 # ------------------------------------------------------------------ pair scores
 def _pair_case(B, L, V, r, dt, seed, anchor=True):
     g = np.random.default_rng(seed)
