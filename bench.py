@@ -9,7 +9,9 @@ each stage a call into libdflash2 on the current HIP stream.  Inputs are
 seeded synthetic tensors already resident in HBM when timing starts.
 
 Prints ONE JSON line (rank 0, N = 1):
-  value = blocks/s over the timed steps (B / seconds per step);
+  value = blocks/s over the timed steps (B / seconds per step), the step
+  captured once as a HIP graph and replayed (--eager: plain launches);
+  stage_ms = per-stage times from a second, eager pass with events;
   roofline = the LM-head GEMM kernel (the dominant kernel) against the bf16
   matrix-core peak, its duration measured with HIP events on its stream;
   cpu_baseline = the CPU oracle on a bounded block sample, same inputs.
@@ -49,6 +51,8 @@ def parse_args(argv=None):
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of replays of the captured step")
     return ap.parse_args(argv)
 
 
@@ -239,19 +243,52 @@ def main(argv=None):
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"[bench] warmup done ({a.warmup} steps); timing {a.steps} steps")
+    outs = (buf.top_val, buf.top_idx, buf.path_slot, buf.path_tok, buf.accept_len, buf.next_tok)
+    eager_out = [t.clone() for t in outs]
+
+    # The whole step captured once as a HIP graph (every call enqueues on the
+    # current stream, nothing allocates or clears memory), then replayed:
+    # the timed loop pays no per-kernel launch cost on the host.
+    graph = None
+    if not a.eager:
+        try:
+            cap = torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cap):
+                step()
+                torch.cuda.synchronize()
+                with torch.cuda.graph(graph, stream=cap):
+                    step()
+            torch.cuda.current_stream().wait_stream(cap)
+            torch.cuda.synchronize()
+            for _ in range(a.warmup):
+                graph.replay()
+            torch.cuda.synchronize()
+        except Exception as e:  # pragma: no cover - capture unsupported
+            log(f"[bench] graph capture failed ({e}); timing eager steps")
+            graph = None
+    run = graph.replay if graph is not None else step
+    log(f"[bench] warmup done ({a.warmup} steps); timing {a.steps} steps "
+        f"({'graph replays' if graph is not None else 'eager'})")
     t_start = time.perf_counter()
-    for i in range(a.steps):
-        step(i)
+    for _ in range(a.steps):
+        run()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     log(f"[bench] timed {a.steps} steps in {wall:.3f} s")
+    for t, r in zip(outs, eager_out):          # the replays computed what eager steps do
+        assert torch.equal(t, r), "graph replay differs from the eager step"
 
     # light sanity on the last step's outputs
     acc = buf.accept_len.cpu().numpy()
     tv = buf.top_val.cpu().numpy()
     assert ((acc >= 1) & (acc <= L + 1)).all() and (np.diff(tv, axis=1) <= 0).all()
 
+    # per-stage times: a second pass of eager steps with events between stages
+    for i in range(a.steps):
+        step(i)
+    torch.cuda.synchronize()
     stage_ms = {k: 0.0 for k in order}
     for i in range(a.steps):
         marks = [ev[k][i] for k in order] + [ev_end[i]]
@@ -294,7 +331,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "L": L, "H": H, "V": V, "r": w.r,
                    "convs": w.n_convs, "conv_groups": w.groups if w.dynamic else 0, "topk": 16,
-                   "gate": w.gate, "walk": w.walk, "temperature": w.temperature},
+                   "gate": w.gate, "walk": w.walk, "temperature": w.temperature,
+                   "launch": "hip-graph" if graph is not None else "eager"},
         "tokens_per_s": round(M / (ms_step * 1e-3), 1),
         "accepted_tokens_per_s": round(float(acc.sum()) / (ms_step * 1e-3), 1),
         "mean_accept_len": round(float(acc.mean()), 3),

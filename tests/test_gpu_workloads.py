@@ -406,3 +406,42 @@ def test_step_is_deterministic(case):
     for a, b in zip(snap, (buf.logits, buf.top_val, buf.top_idx, buf.S0, buf.S, buf.path_slot,
                            buf.path_score)):
         assert torch.equal(a, b)
+
+
+def test_step_graph_replays_match_eager(case):
+    """The whole step captured as a HIP graph (as the benchmark times it):
+    every replay, with eager steps and synchronisations in between, gives the
+    eager step's outputs."""
+    w, buf, dev = case["w"], case["buf"], case["dev"]
+    if w.cid not in (2, 5, 7):
+        pytest.skip("checked on the benchmark, the gated and the sampled workload")
+    kw = dict(Wg=dev["Wg"], walk=w.walk, temperature=w.temperature, u_path=dev.get("u_path"),
+              z_target=dev.get("z_target"), u_acc=dev.get("u_acc"), u_res=dev.get("u_res"))
+
+    def step():
+        bd.run_step(buf, dev["x"], dev["convs"], dev["W"], dev["U"], dev["Vf"], dev["anchor_tok"],
+                    None, **kw)
+
+    outs = (buf.logits, buf.top_val, buf.top_idx, buf.S0, buf.S, buf.path_slot, buf.path_tok)
+    step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outs]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for t in outs:
+            t.zero_()                     # the replay must rewrite every output
+        g.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(outs, want):
+            assert torch.equal(t, r)
+        step()                            # eager work between replays
+        torch.cuda.synchronize()
