@@ -240,28 +240,47 @@ __global__ __launch_bounds__(256) void conv_dyng_kernel(const T* __restrict__ x,
 // rows, so D never leaves the chip.
 //
 // Product: bf16 x and P^T (both K-contiguous), v_mfma_f32_32x32x16_bf16,
-// fp32 accumulation; each of the four waves owns a 32 x 32 quarter of the
-// tile.  K is staged through LDS in 128-wide slices, every 16-byte load part
-// of a run of 16 threads reading 256 contiguous bytes of a row, with two
-// register staging sets keeping two slices in flight.  Mix: fp64 from the
+// fp32 accumulation.  Four waves own the four 32 x 32 quarters of the tile;
+// with few tiles a second group of four takes the second half of every K
+// slice (partial quarters added at the end).  K is staged through LDS in
+// 128-wide slices per group, every 16-byte load part of a run of threads
+// reading contiguous bytes of one row, with two register staging sets
+// keeping two slices in flight.  Mix: fp64 from the
 // fp32 corrections, rounded once as in the kernels above.
 constexpr int kMmBM = 64;
 constexpr int kMmBN = 64;
-constexpr int kMmBK = 128;
-constexpr int kMmLd = kMmBK + 8;                    // padded LDS row (bf16)
-constexpr int kMmCpr = kMmBK / 8;                   // 16-byte chunks per row slice
-constexpr int kMmRowsPerPass = 256 / kMmCpr;        // 16
-constexpr int kMmPasses = kMmBM / kMmRowsPerPass;   // 4 per operand
-constexpr int kMmLoads = 2 * kMmPasses;
-constexpr int kMmDLd = kMmBN + 1;                   // fp32 D tile pitch
-static_assert(kMmBM == kMmBN, "one loader layout serves both operands");
-static_assert(kMmBM * kMmDLd * 4 <= 2 * 2 * kMmBM * kMmLd * 2, "D tile fits in the stages");
+constexpr int kMmDLd = kMmBN + 1;  // fp32 D tile pitch
 
-__global__ __launch_bounds__(256) void conv_mm_kernel(
+// KH wave groups of four (2 x 2 quarters of the tile) split each K slice.
+template <int KH>
+struct MmCfg {
+  static constexpr int kThreads = 256 * KH;
+  static constexpr int kBK = 128 * KH;                   // K per LDS slice: 128 per group
+  static constexpr int kLd = kBK + 8;                    // padded LDS row (bf16)
+  static constexpr int kCpr = kBK / 8;                   // 16-byte chunks per row slice
+  static constexpr int kRowsPerPass = kThreads / kCpr;   // 16
+  static constexpr int kPasses = kMmBM / kRowsPerPass;   // 4 per operand
+  static constexpr int kLoads = 2 * kPasses;
+  static_assert(16 * 64 * 4 * 4 + kMmBM * kMmDLd * 4 <= 2 * 2 * kMmBM * kLd * 2,
+                "partial tiles and the D tile fit in the stages");
+};
+static_assert(kMmBM == kMmBN, "one loader layout serves both operands");
+
+template <int KH>
+__global__ __launch_bounds__(MmCfg<KH>::kThreads) void conv_mm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ anchor,
     uint16_t* __restrict__ y, const float* __restrict__ k0, const float* __restrict__ k1,
     const uint16_t* __restrict__ pt, int M, int N, int H, int L, int gw, int mtiles,
     int ntiles) {
+  using C = MmCfg<KH>;
+  constexpr int kMmThreads = C::kThreads;
+  constexpr int kMmKH = KH;
+  constexpr int kMmBK = C::kBK;
+  constexpr int kMmLd = C::kLd;
+  constexpr int kMmCpr = C::kCpr;
+  constexpr int kMmRowsPerPass = C::kRowsPerPass;
+  constexpr int kMmPasses = C::kPasses;
+  constexpr int kMmLoads = C::kLoads;
   __shared__ __attribute__((aligned(16))) uint16_t stage[2][2][kMmBM * kMmLd];  // [buf][x/P]
   // Tiles that share x rows run on one XCD: n fastest.
   const int tile = xcd_tile(blockIdx.x, mtiles * ntiles);
@@ -314,15 +333,17 @@ __global__ __launch_bounds__(256) void conv_mm_kernel(
   f32x16_t acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  // Wave (wm, wn) owns rows 32 wm.. and columns 32 wn.. of the tile; lane l
-  // supplies fragment row l % 32 and k values 8 (l / 32) .. +7 of a k-step.
+  // Wave (kh, wm, wn): K half kh of every slice, rows 32 wm.. and columns
+  // 32 wn.. of the tile; lane l supplies fragment row l % 32 and k values
+  // 8 (l / 32) .. +7 of a k-step.
+  const int kh = KH > 1 ? wave >> 2 : 0;
   const int wm = wave & 1;
-  const int wn = wave >> 1;
-  const int fa = (wm * 32 + (lane & 31)) * kMmLd + (lane >> 5) * 8;
-  const int fb = (wn * 32 + (lane & 31)) * kMmLd + (lane >> 5) * 8;
+  const int wn = (wave >> 1) & 1;
+  const int fa = (wm * 32 + (lane & 31)) * kMmLd + (lane >> 5) * 8 + kh * (kMmBK / kMmKH);
+  const int fb = (wn * 32 + (lane & 31)) * kMmLd + (lane >> 5) * 8 + kh * (kMmBK / kMmKH);
   auto multiply = [&](int buf) {
 #pragma unroll
-    for (int ks = 0; ks < kMmBK / 16; ++ks) {
+    for (int ks = 0; ks < kMmBK / kMmKH / 16; ++ks) {
       const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&stage[buf][0][fa + ks * 16]);
       const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(&stage[buf][1][fb + ks * 16]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
@@ -345,13 +366,29 @@ __global__ __launch_bounds__(256) void conv_mm_kernel(
     sstore(R0, 0);
     __syncthreads();
   }
-  // D tile to LDS (over the stages, which are free now): accumulator
+  // The second K half's partial quarters meet the first's in LDS (over the
+  // stages, which are free now), then the D tile goes to LDS: accumulator
   // register r of lane l holds C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
-  float* dt = reinterpret_cast<float*>(&stage[0][0][0]);
+  float* part = reinterpret_cast<float*>(&stage[0][0][0]);  // [4 quarters][16][64]
+  float* dt = part + 4 * 16 * 64;
+  const int quarter = wave & 3;
+  if (KH > 1) {
+    if (kh == 1) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    dt[row * kMmDLd + wn * 32 + (lane & 31)] = acc[r];
+      for (int r = 0; r < 16; ++r) part[(quarter * 16 + r) * 64 + lane] = acc[r];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] += part[(quarter * 16 + r) * 64 + lane];
+    }
+  }
+  if (kh == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      dt[row * kMmDLd + wn * 32 + (lane & 31)] = acc[r];
+    }
   }
   __syncthreads();
   // Mix the channels of this tile's groups for its rows.
@@ -359,23 +396,76 @@ __global__ __launch_bounds__(256) void conv_mm_kernel(
   const int c0 = g0 * gw;
   const int c1 = min(N >> 1, g0 + kMmBN / 2) * gw;
   const int nvec = (c1 - c0) >> 3;
-  for (int e = tid; e < rowsA * nvec; e += 256) {
-    const int row = e / nvec;
-    const int c = c0 + (e - row * nvec) * 8;
-    const int m = m0 + row;
-    const int t = m % L;
-    const uint16_t* xp = x + (size_t)m * H + c;
-    const uint16_t* pp = t > 0 ? xp - H : (anchor ? anchor + (size_t)(m / L) * H + c : nullptr);
-    double a0[8], a1[8];
-    load_f32x8(k0 + c, a0);
-    load_f32x8(k1 + c, a1);
+  // kMixU vectors of 8 channels per thread per round, all their loads in
+  // flight before any arithmetic (a round trip per vector would dominate).
+  const bool whole = (gw & 7) == 0;  // a vector never straddles two groups
+  const int nv = rowsA * nvec;
+  constexpr int kMixU = 4;
+  for (int e0 = tid; e0 < nv; e0 += kMmThreads * kMixU) {
+    u32x4_t xr[kMixU], pr[kMixU];
+    f32x4_t ka[kMixU][2], kb[kMixU][2];
+    int rw[kMixU], cc[kMixU];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int col = 2 * ((c + i) / gw - g0);
-      a0[i] += (double)dt[row * kMmDLd + col];
-      a1[i] += (double)dt[row * kMmDLd + col + 1];
+    for (int u = 0; u < kMixU; ++u) {
+      const int e = min(e0 + kMmThreads * u, nv - 1);  // tail rounds redo the last vector (not stored)
+      const int row = e / nvec;
+      const int c = c0 + (e - row * nvec) * 8;
+      const int m = m0 + row;
+      const int b = m / L;
+      const int t = m - b * L;
+      rw[u] = row;
+      cc[u] = c;
+      const uint16_t* xp = x + (size_t)m * H + c;
+      xr[u] = *reinterpret_cast<const u32x4_t*>(xp);
+      if (t > 0)
+        pr[u] = *reinterpret_cast<const u32x4_t*>(xp - H);
+      else if (anchor)
+        pr[u] = *reinterpret_cast<const u32x4_t*>(anchor + (size_t)b * H + c);
+      else
+        pr[u] = u32x4_t{0u, 0u, 0u, 0u};
+      ka[u][0] = *reinterpret_cast<const f32x4_t*>(k0 + c);
+      ka[u][1] = *reinterpret_cast<const f32x4_t*>(k0 + c + 4);
+      kb[u][0] = *reinterpret_cast<const f32x4_t*>(k1 + c);
+      kb[u][1] = *reinterpret_cast<const f32x4_t*>(k1 + c + 4);
     }
-    mix8<uint16_t>(xp, pp, y + (size_t)m * H + c, a0, a1);
+#pragma unroll
+    for (int u = 0; u < kMixU; ++u) {
+      if (e0 + kMmThreads * u >= nv) break;
+      const int c = cc[u];
+      const float* drow = dt + rw[u] * kMmDLd;
+      double d0[8], d1[8];
+      if (whole) {
+        const int col = 2 * (c / gw - g0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          d0[i] = (double)drow[col];
+          d1[i] = (double)drow[col + 1];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int col = 2 * ((c + i) / gw - g0);
+          d0[i] = (double)drow[col];
+          d1[i] = (double)drow[col + 1];
+        }
+      }
+      u32x4_t out;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        double yv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int i = 2 * w + h;
+          const double xv = (double)(h ? bf16_hi(xr[u][w]) : bf16_lo(xr[u][w]));
+          const double pv = (double)(h ? bf16_hi(pr[u][w]) : bf16_lo(pr[u][w]));
+          const double a0 = (double)ka[u][i >> 2][i & 3] + d0[i];
+          const double a1 = (double)kb[u][i >> 2][i & 3] + d1[i];
+          yv[h] = a0 * xv + a1 * pv;
+        }
+        out[w] = pack_bf16x2(f64_to_f32_odd(yv[0]), f64_to_f32_odd(yv[1]));
+      }
+      *reinterpret_cast<u32x4_t*>(y + (size_t)(m0 + rw[u]) * H + c) = out;
+    }
   }
 }
 
@@ -413,10 +503,20 @@ hipError_t launch_twotap_conv_mm(const void* x, const void* anchor_h, void* y, c
   const int N = 2 * groups;
   const int mtiles = (M + kMmBM - 1) / kMmBM;
   const int ntiles = (N + kMmBN - 1) / kMmBN;
-  hipLaunchKernelGGL(conv_mm_kernel, dim3((unsigned)(mtiles * ntiles)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(anchor_h),
-                     static_cast<uint16_t*>(y), k0, k1, static_cast<const uint16_t*>(projT), M, N,
-                     H, L, H / groups, mtiles, ntiles);
+  const unsigned tiles = (unsigned)(mtiles * ntiles);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* ab = static_cast<const uint16_t*>(anchor_h);
+  uint16_t* yb = static_cast<uint16_t*>(y);
+  const uint16_t* pb = static_cast<const uint16_t*>(projT);
+  // One round of tiles over the CUs: two wave groups per tile (a tile's K
+  // loop is latency-bound, the second group halves it; 135 KB of LDS, one
+  // tile per CU).  More tiles than CUs: one group, two tiles per CU.
+  if (tiles <= 256)
+    hipLaunchKernelGGL(conv_mm_kernel<2>, dim3(tiles), dim3(MmCfg<2>::kThreads), 0, s, xb, ab, yb,
+                       k0, k1, pb, M, N, H, L, H / groups, mtiles, ntiles);
+  else
+    hipLaunchKernelGGL(conv_mm_kernel<1>, dim3(tiles), dim3(MmCfg<1>::kThreads), 0, s, xb, ab, yb,
+                       k0, k1, pb, M, N, H, L, H / groups, mtiles, ntiles);
   return hipGetLastError();
 }
 

@@ -48,19 +48,16 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
 struct WaveTop16 {
   uint64_t key;   // this lane's slot
   uint64_t thr;   // 16th key (wave-uniform)
-  float thr_f;    // filter value: the 16th key's value (-inf while the list is
-                  // not full), raised to floor_f
-  float floor_f;  // a known lower bound of the final 16th value (-inf if none)
+  float thr_f;    // value of the 16th key; -inf while the list is not full
 
   __device__ void init() {
     key = 0;
     thr = 0;
     thr_f = -INFINITY;
-    floor_f = -INFINITY;
   }
   __device__ void refresh() {
     thr = readlane64(key, 15);
-    thr_f = fmaxf(thr ? val_of((uint32_t)(thr >> 32)) : -INFINITY, floor_f);
+    thr_f = thr ? val_of((uint32_t)(thr >> 32)) : -INFINITY;
   }
 };
 
@@ -279,26 +276,36 @@ __global__ __launch_bounds__(64) void topk16_merge_kernel(const uint64_t* __rest
 // Top-16 of a row that comes with its tile maxima tmax [nt] (tile t covers
 // columns [256 t, 256 t + 256)).  Any 16 tile maxima are 16 distinct
 // elements, so if tau is at most the 16th largest of some 16 of them, the
-// row's 16th best value is >= tau and every top-16 element lies in a tile
-// whose maximum is >= tau (an element of any other tile is below tau and
-// below 16 others).  One wave per row: each lane takes the maximum of its
-// share of the tile maxima, tau = the 16th largest of those 64 lane maxima
-// (one sort; usually 16-20 tiles then reach it), and only the tiles that
-// reach tau are streamed, kPruneBatch at a time in flight, through the same
-// filter and list as the full scan.  The result is the full scan's, bit for
-// bit.
+// row's 16th best value is >= tau and every top-16 element is >= tau and
+// lies in a tile whose maximum is >= tau.  One wave per row: each lane takes
+// the maximum of its share of the tile maxima, tau = the 16th largest of
+// those 64 lane maxima (one sort; usually 16-20 tiles reach it), then only
+// the tiles that reach tau are read, kPruneBatch at a time in flight, and
+// their elements >= tau are compacted into an LDS buffer with one ballot
+// per 64 elements.  The buffer is merged into the sorted list 48 keys per
+// 64-lane sort.  Exact: the result is the full scan's, bit for bit.
 constexpr int kPruneBatch = 16;
-constexpr int kMaxChunk = 16;  // tile maxima per lane per pass (1024 tiles)
+constexpr int kMaxChunk = 16;      // tile maxima per lane per pass (1024 tiles)
+constexpr int kCandCap = 1024;     // LDS candidate keys before a merge
+
+// Merge n keys of cand into the list, 48 per sort.
+__device__ void merge_cands(WaveTop16& top, const uint64_t* cand, int n) {
+  const int lane = threadIdx.x & 63;
+  for (int b = 0; b < n; b += 48) {
+    const int e = b + lane - 16;
+    const uint64_t c = lane < 16 ? top.key : (e < n ? cand[e] : 0ull);
+    top.key = shfl64(wave_sort_desc(c), lane & 15);
+  }
+  top.refresh();
+}
 
 template <int VEC>
 __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restrict__ logits,
                                                            const float* __restrict__ tmax, int V,
                                                            int nt, float* __restrict__ top_val,
                                                            int32_t* __restrict__ top_idx) {
-  __shared__ uint64_t buf[kBuf];
+  __shared__ uint64_t cand[kCandCap];
   __shared__ int list[64 * kMaxChunk];
-  __shared__ float tcache[64 * kMaxChunk];
-  __shared__ f32x4_t park[kPruneBatch][64];
   const int m = blockIdx.x;
   const int lane = threadIdx.x;
   const float* tm = tmax + (size_t)m * nt;
@@ -313,58 +320,67 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
       v[k] = t < nt ? tm[t] : -INFINITY;
     }
 #pragma unroll
-    for (int k = 0; k < kMaxChunk; ++k) {
+    for (int k = 0; k < kMaxChunk; ++k)
       if (c0 + k * 64 + lane < nt) lmax = max(lmax, ord_of(v[k]));
-      if (c0 == 0) tcache[k * 64 + lane] = v[k];  // the first pass is read again below
-    }
   }
   const uint64_t srt = wave_sort_desc(((uint64_t)lmax << 32) | (uint32_t)(~lane));
   const uint32_t tau = nt >= 16 ? (uint32_t)(readlane64(srt, 15) >> 32) : 0u;
-  // 2. stream the tiles that reach tau, listed in LDS in tile order; no
-  //    element below tau can rank, so the filter starts at tau
+  // 2. read the tiles that reach tau; keep their elements >= tau
   WaveTop16 top;
   top.init();
-  if (tau) top.floor_f = top.thr_f = val_of(tau);
-  int count = 0;
+  int ncand = 0;
   for (int c0 = 0; c0 < nt; c0 += 64 * kMaxChunk) {
     int nsel = 0;
+    float tv[kMaxChunk];
 #pragma unroll
     for (int k = 0; k < kMaxChunk; ++k) {
       const int t = c0 + k * 64 + lane;
-      const bool s = t < nt && ord_of(c0 == 0 ? tcache[k * 64 + lane] : tm[t]) >= tau;
+      tv[k] = t < nt ? tm[t] : -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxChunk; ++k) {
+      const int t = c0 + k * 64 + lane;
+      const bool s = t < nt && ord_of(tv[k]) >= tau;
       const uint64_t sel = __ballot(s);
       if (s) list[nsel + lanes_below(sel)] = t;
       nsel += __popcll(sel);
     }
     for (int b0 = 0; b0 < nsel; b0 += kPruneBatch) {
       const int ns = min(kPruneBatch, nsel - b0);
-      // all of the batch's loads in flight, then parked in LDS so that the
-      // filter loop below can walk them without indexing registers
+      f32x4_t q[kPruneBatch];
+      int cbase[kPruneBatch];
 #pragma unroll
       for (int k = 0; k < kPruneBatch; ++k) {
         const bool live = k < ns;
-        const int c = (live ? list[b0 + k] : 0) * kTileMaxCols + lane * 4;
-        f32x4_t q;
+        cbase[k] = (live ? list[b0 + k] : 0) * kTileMaxCols + lane * 4;
+        const int c = cbase[k];
         if (VEC == 4 && live && c + 4 <= V) {
-          q = *reinterpret_cast<const f32x4_t*>(row + c);
+          q[k] = *reinterpret_cast<const f32x4_t*>(row + c);
         } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) q[i] = (live && c + i < V) ? row[c + i] : 0.f;
+          for (int i = 0; i < 4; ++i) q[k][i] = (live && c + i < V) ? row[c + i] : -INFINITY;
         }
-        park[k][lane] = q;
       }
-      for (int k = 0; k < ns; ++k) {  // wave-uniform
-        const int c = list[b0 + k] * kTileMaxCols + lane * 4;
-        const f32x4_t q = park[k][lane];
+      // every tile starts with room for its 256 keys (see the merge below)
+      const uint32_t floor_ord = top.thr ? max(tau, (uint32_t)(top.thr >> 32)) : tau;
+#pragma unroll
+      for (int k = 0; k < kPruneBatch; ++k) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool p = c + i < V && may_enter(q[i], top.thr_f);
-          append(top, buf, count, p, key_of(q[i], (uint32_t)(c + i)));
+          const int c = cbase[k] + i;
+          const bool p = k < ns && c < V && ord_of(q[k][i]) >= floor_ord;
+          const uint64_t pm = __ballot(p);
+          if (p) cand[ncand + lanes_below(pm)] = key_of(q[k][i], (uint32_t)c);
+          ncand += __popcll(pm);
+        }
+        if (ncand > kCandCap - 4 * 64) {  // keep the next tile's keys in range
+          merge_cands(top, cand, ncand);
+          ncand = 0;
         }
       }
     }
   }
-  if (count) flush(top, buf, count);
+  if (ncand) merge_cands(top, cand, ncand);
   write_final(top, top_val + (size_t)m * kTopK, top_idx + (size_t)m * kTopK);
 }
 

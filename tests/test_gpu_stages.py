@@ -116,7 +116,8 @@ def conv_mm_tolerance(xo, ao, P, groups, want):
 @pytest.mark.parametrize("B,L,H,G,anchor", [(1, 1, 64, 4, True), (3, 5, 136, 17, True),
                                             (2, 16, 5120, 320, True), (37, 1, 128, 8, False),
                                             (5, 7, 2560, 160, True), (1, 3, 256, 256, True),
-                                            (4, 8, 1024, 1, True), (9, 8, 520, 65, False)])
+                                            (4, 8, 1024, 1, True), (9, 8, 520, 65, False),
+                                            (1100, 8, 1024, 64, True)])   # > 256 tiles
 def test_conv_mm_parity(B, L, H, G, anchor):
     g = np.random.default_rng(B * 1000 + G)
     x = WL.to_bf16_bits(g.standard_normal((B, L, H)).astype(np.float32))
