@@ -21,16 +21,30 @@ namespace {
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-constexpr int kGateWaves = 4;
-constexpr int kGateBK = 128;                    // k per LDS slice
-constexpr int kGateLd = kGateBK + 8;            // padded LDS row (bf16)
-constexpr int kGateCpr = kGateBK / 8;           // 16-byte chunks per row slice
-constexpr int kGateRowsPerPass = 64 * kGateWaves / kGateCpr;  // 16
-constexpr int kGatePasses = 32 / kGateRowsPerPass;            // 2 per operand
+// W waves share each tile; W = 8 takes 256-wide K slices (twice the bytes
+// in flight per tile, for launches of at most one tile per CU), W = 4
+// 128-wide ones (two tiles per CU).
+template <int W>
+struct GateCfg {
+  static constexpr int kWaves = W;
+  static constexpr int kBK = 32 * W;                          // k per LDS slice
+  static constexpr int kLd = kBK + 8;                         // padded LDS row (bf16)
+  static constexpr int kCpr = kBK / 8;                        // 16-byte chunks per row slice
+  static constexpr int kRowsPerPass = 64 * W / kCpr;          // 16
+  static constexpr int kPasses = 32 / kRowsPerPass;           // 2 per operand
+};
 
-__global__ __launch_bounds__(64 * kGateWaves) void gate_bf16_kernel(
+template <int W>
+__global__ __launch_bounds__(64 * W) void gate_bf16_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ Wg, float* __restrict__ gate,
     int M, int H, int r) {
+  using C = GateCfg<W>;
+  constexpr int kGateWaves = C::kWaves;
+  constexpr int kGateBK = C::kBK;
+  constexpr int kGateLd = C::kLd;
+  constexpr int kGateCpr = C::kCpr;
+  constexpr int kGateRowsPerPass = C::kRowsPerPass;
+  constexpr int kGatePasses = C::kPasses;
   __shared__ __attribute__((aligned(16))) uint16_t stage[2][2][32 * kGateLd];  // [buf][A/B]
   __shared__ float part[kGateWaves][16][64];
   const int m0 = blockIdx.x * 32;
@@ -157,9 +171,12 @@ hipError_t launch_context_gate(const void* h, const void* Wg, float* gate, int M
   if (M == 0) return hipSuccess;
   if (dtype == 1) {
     const dim3 grid((unsigned)((M + 31) / 32), (unsigned)((r + 31) / 32));
-    hipLaunchKernelGGL(gate_bf16_kernel, grid, dim3(64 * kGateWaves), 0, s,
-                       static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(Wg), gate, M,
-                       H, r);
+    const uint16_t* hb = static_cast<const uint16_t*>(h);
+    const uint16_t* wb = static_cast<const uint16_t*>(Wg);
+    if ((long long)grid.x * grid.y <= 256)
+      hipLaunchKernelGGL(gate_bf16_kernel<8>, grid, dim3(64 * 8), 0, s, hb, wb, gate, M, H, r);
+    else
+      hipLaunchKernelGGL(gate_bf16_kernel<4>, grid, dim3(64 * 4), 0, s, hb, wb, gate, M, H, r);
   } else {
     const long long n = (long long)M * r;
     hipLaunchKernelGGL(gate_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,

@@ -325,7 +325,8 @@ def test_pair_without_anchor_and_bad_ids_give_nan():
 # ------------------------------------------------------------------ context gate
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("M,H,r", [(1, 8, 1), (37, 136, 7), (300, 520, 64), (64, 2568, 33),
-                                   (513, 5120, 256), (4096, 256, 40)])
+                                   (513, 5120, 256), (4096, 256, 40),
+                                   (4100, 64, 100)])        # > 256 tiles: four-wave kernel
 def test_context_gate_parity(dt, M, H, r):
     g = np.random.default_rng(M + H + r)
     h = _bits_or_f32(g.standard_normal((M, H)).astype(np.float32), dt)
