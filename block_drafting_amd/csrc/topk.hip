@@ -277,25 +277,36 @@ __global__ __launch_bounds__(64) void topk16_merge_kernel(const uint64_t* __rest
 // columns [256 t, 256 t + 256)).  Any 16 tile maxima are 16 distinct
 // elements, so if tau is at most the 16th largest of some 16 of them, the
 // row's 16th best value is >= tau and every top-16 element is >= tau and
-// lies in a tile whose maximum is >= tau.  One wave per row: each lane takes
-// the maximum of its share of the tile maxima, tau = the 16th largest of
-// those 64 lane maxima (one sort; usually 16-20 tiles reach it), then only
-// the tiles that reach tau are read, kPruneBatch at a time in flight, and
-// their elements >= tau are compacted into an LDS buffer with one ballot
-// per 64 elements.  The buffer is merged into the sorted list 48 keys per
-// 64-lane sort.  Exact: the result is the full scan's, bit for bit.
+// lies in a tile whose maximum is >= tau.  One wave per row, two sorts for
+// the bound:
+//  - each lane takes the maximum of its share of the tile maxima; the 16th
+//    largest of those 64 lane maxima is a first bound, which ~35 tiles of a
+//    151936-token row of Gaussian logits reach;
+//  - when at most 64 tiles reach it, the 16th largest of their maxima is the
+//    exact 16th largest tile maximum, which usually only 16 tiles reach.
+// Only those tiles are read, kPruneBatch at a time in flight, and their
+// elements >= tau are compacted into an LDS buffer with one ballot per 64
+// elements.  The buffer is merged into the sorted list 48 keys per 64-lane
+// sort.  Exact: the result is the full scan's, bit for bit.
 constexpr int kPruneBatch = 16;
 constexpr int kMaxChunk = 16;      // tile maxima per lane per pass (1024 tiles)
 constexpr int kCandCap = 1024;     // LDS candidate keys before a merge
 
-// Merge n keys of cand into the list, 48 per sort.
-__device__ void merge_cands(WaveTop16& top, const uint64_t* cand, int n) {
+// Merge n keys of cand into the list (this lane's slot key), 48 per sort.
+// Not inlined: the call sites sit inside unrolled loops and are rarely taken.
+__device__ __attribute__((noinline)) uint64_t merge_keys(uint64_t key, const uint64_t* cand,
+                                                          int n) {
   const int lane = threadIdx.x & 63;
   for (int b = 0; b < n; b += 48) {
     const int e = b + lane - 16;
-    const uint64_t c = lane < 16 ? top.key : (e < n ? cand[e] : 0ull);
-    top.key = shfl64(wave_sort_desc(c), lane & 15);
+    const uint64_t c = lane < 16 ? key : (e < n ? cand[e] : 0ull);
+    key = shfl64(wave_sort_desc(c), lane & 15);
   }
+  return key;
+}
+
+__device__ __forceinline__ void merge_cands(WaveTop16& top, const uint64_t* cand, int n) {
+  top.key = merge_keys(top.key, cand, n);
   top.refresh();
 }
 
@@ -306,14 +317,15 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
                                                            int32_t* __restrict__ top_idx) {
   __shared__ uint64_t cand[kCandCap];
   __shared__ int list[64 * kMaxChunk];
+  __shared__ uint32_t lord[64 * kMaxChunk];
   const int m = blockIdx.x;
   const int lane = threadIdx.x;
   const float* tm = tmax + (size_t)m * nt;
   const float* row = logits + (size_t)m * V;
   // 1. tau from the lane maxima (all loads of a pass in flight at once)
   uint32_t lmax = 0;  // ord of this lane's largest tile maximum (0: none)
+  float v[kMaxChunk];  // the last pass's maxima (all of them when nt <= 64 * kMaxChunk)
   for (int c0 = 0; c0 < nt; c0 += 64 * kMaxChunk) {
-    float v[kMaxChunk];
 #pragma unroll
     for (int k = 0; k < kMaxChunk; ++k) {
       const int t = c0 + k * 64 + lane;
@@ -324,7 +336,7 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
       if (c0 + k * 64 + lane < nt) lmax = max(lmax, ord_of(v[k]));
   }
   const uint64_t srt = wave_sort_desc(((uint64_t)lmax << 32) | (uint32_t)(~lane));
-  const uint32_t tau = nt >= 16 ? (uint32_t)(readlane64(srt, 15) >> 32) : 0u;
+  uint32_t tau = nt >= 16 ? (uint32_t)(readlane64(srt, 15) >> 32) : 0u;
   // 2. read the tiles that reach tau; keep their elements >= tau
   WaveTop16 top;
   top.init();
@@ -332,18 +344,42 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
   for (int c0 = 0; c0 < nt; c0 += 64 * kMaxChunk) {
     int nsel = 0;
     float tv[kMaxChunk];
+    if (nt <= 64 * kMaxChunk) {
 #pragma unroll
-    for (int k = 0; k < kMaxChunk; ++k) {
-      const int t = c0 + k * 64 + lane;
-      tv[k] = t < nt ? tm[t] : -INFINITY;
+      for (int k = 0; k < kMaxChunk; ++k) tv[k] = v[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < kMaxChunk; ++k) {
+        const int t = c0 + k * 64 + lane;
+        tv[k] = t < nt ? tm[t] : -INFINITY;
+      }
     }
 #pragma unroll
     for (int k = 0; k < kMaxChunk; ++k) {
       const int t = c0 + k * 64 + lane;
       const bool s = t < nt && ord_of(tv[k]) >= tau;
       const uint64_t sel = __ballot(s);
-      if (s) list[nsel + lanes_below(sel)] = t;
+      if (s) {
+        const int at = nsel + lanes_below(sel);
+        list[at] = t;
+        lord[at] = ord_of(tv[k]);
+      }
       nsel += __popcll(sel);
+    }
+    // Tighter bound: the 16th largest of the selected tiles' maxima (the 16
+    // largest tile maxima are 16 distinct elements too).  Tiles below it are
+    // dropped, usually leaving 16.
+    if (nt >= 16 && nt <= 64 * kMaxChunk && nsel > 16 && nsel <= 64) {
+      const int t = lane < nsel ? list[lane] : 0;
+      const uint32_t o = lane < nsel ? lord[lane] : 0u;
+      const uint64_t srt2 = wave_sort_desc(((uint64_t)o << 32) | (uint32_t)(~lane));
+      tau = (uint32_t)(readlane64(srt2, 15) >> 32);
+      const bool s = lane < nsel && o >= tau;
+      const uint64_t sel = __ballot(s);
+      __builtin_amdgcn_wave_barrier();
+      if (s) list[lanes_below(sel)] = t;
+      __builtin_amdgcn_wave_barrier();
+      nsel = __popcll(sel);
     }
     for (int b0 = 0; b0 < nsel; b0 += kPruneBatch) {
       const int ns = min(kPruneBatch, nsel - b0);

@@ -277,6 +277,21 @@ def test_topk_tilemax_ties_zeros_nan_inf():
     _topk_tilemax_check(z)
 
 
+def test_topk_tilemax_bound_refinement():
+    """The second bound (the 16th largest of the tile maxima that reach the
+    lane-max bound) around its edges: ties at it, a graded run it cuts to 16
+    tiles, and more than 64 tiles at the first bound (refinement skipped)."""
+    g = np.random.default_rng(5)
+    z = (g.standard_normal((4, 151936)) * 0.5).astype(np.float32)
+    t = np.arange(594)
+    z[0, t[:30] * 256 + 7] = 5.0                        # 30 tiles tie at the 16th maximum
+    z[1, t[:40] * 256 + t[:40] % 256] = (5.0 - 0.01 * t[:40]).astype(np.float32)
+    z[2, t[::8][:70] * 256 + 100] = 5.0                 # 70 tied tiles: > 64 reach the first bound
+    z[3, t[:17] * 256 + 255] = 5.0                      # 17 tiles, last column of each
+    z[3, 16 * 256 + 254] = 5.0                          # a second 5.0 inside the 17th tile
+    _topk_tilemax_check(z)
+
+
 # ------------------------------------------------------------------ pair scores
 def _pair_case(B, L, V, r, dt, seed, anchor=True):
     g = np.random.default_rng(seed)
