@@ -59,6 +59,7 @@ DFLASH2_API int dflash2_twotap_conv(const void* x, const void* anchor_h, void* y
     if (groups < 1 || H % groups != 0 || !aligned16(proj)) return DFLASH2_EINVAL;
     if (groups > 1 && (size_t)(H + 2 * groups) * sizeof(double) > 65536)
       return DFLASH2_EUNSUPPORTED;
+    if ((long long)B * L > kInt32Max) return DFLASH2_EUNSUPPORTED;  // one workgroup per row
   }
   const size_t es = esize(dtype);
   const size_t xbytes = (size_t)B * L * H * es;

@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void conv_dyn1_kernel(const T* __restrict__ x,
   }
 }
 
-// General group count: the row is staged in LDS as fp32, all 2*groups
+// General group count: the row is staged in LDS as fp64, all 2*groups
 // corrections are computed (threads over outputs, coalesced proj reads), then
 // each channel mixes with its group's pair.  Dynamic LDS: (H + 2*groups) doubles.
 template <typename T>

@@ -35,7 +35,8 @@
  *   - Token ids are int32 in [0, V).  Kernels never read outside their
  *     buffers: an id outside [0, V) yields NaN scores instead of a read.
  *   - dtype selects the storage type of activations and weights:
- *     DFLASH2_F32 (fp32) or DFLASH2_BF16 (bf16).  Accumulation is fp32.
+ *     DFLASH2_F32 (fp32) or DFLASH2_BF16 (bf16).  Accumulation is fp32,
+ *     except where a call states otherwise (the convs evaluate in fp64).
  */
 #ifndef DFLASH2_H
 #define DFLASH2_H
@@ -84,7 +85,10 @@ const char* dflash2_strerror(int status);
  * proj     [H, 2*groups] fp32 correction map, or NULL for static taps.
  * groups   >= 1, divides H (ignored when proj is NULL).
  * B >= 0 (0 is a no-op), L >= 1, H >= 8 with H % 8 == 0.  All pointers 16-byte aligned.
- * Arithmetic in fp32; each output is rounded once to dtype (round to nearest even).
+ * Arithmetic in fp64 (taps, corrections, products and the sum); each output is rounded
+ * once to dtype (round to nearest even).
+ * EUNSUPPORTED with proj when B*L > 2^31 - 1, or when groups > 1 and (H + 2*groups)
+ * doubles exceed 64 KiB of LDS.
  */
 int dflash2_twotap_conv(const void* x, const void* anchor_h, void* y,
                         const float* k0, const float* k1,

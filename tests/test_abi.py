@@ -69,6 +69,8 @@ def test_conv_validation():
     assert call(pr=P + 0xa0000, g=3) == EINVAL   # groups must divide H
     assert call(pr=P + 0xa0000, g=0) == EINVAL
     assert call(B=-1) == EINVAL
+    # one workgroup per row with a projection: B*L must fit the grid
+    assert call(pr=P + 0xa0000, B=40_000_000, L=64, H=8) == EUNSUP
 
 
 def test_conv_mm_validation():
