@@ -277,6 +277,33 @@ def test_topk_tilemax_ties_zeros_nan_inf():
     _topk_tilemax_check(z)
 
 
+def test_topk_tilemax_more_than_1024_tiles():
+    """V > 262144: the tile maxima take more than one pass (1024 per pass) and
+    the second bound is skipped; values planted across passes."""
+    g = np.random.default_rng(9)
+    V = 300007                                          # 1172 tiles, ragged last tile
+    z = g.standard_normal((3, V)).astype(np.float32)
+    z[0, [5, 262143, 262144, 299999, 300006]] = 7.0     # around the pass boundary and the tail
+    z[1, 262144:262144 + 40] = 6.5                      # 40 ties inside the second pass
+    z[2, ::1000] = np.nan
+    _topk_tilemax_check(z)
+
+
+def test_logits_topk_more_than_1024_tiles():
+    g = np.random.default_rng(10)
+    M, H, V = 5, 64, 266240                             # 1040 tiles
+    h = g.standard_normal((M, H)).astype(np.float32)
+    W = (g.standard_normal((V, H)) / np.sqrt(H)).astype(np.float32)
+    z, tm = bd.lmhead_logits_tilemax(to_dev(_bits_or_f32(h, "bf16"), "bf16"),
+                                     to_dev(_bits_or_f32(W, "bf16"), "bf16"))
+    zh = z.cpu().numpy()
+    np.testing.assert_array_equal(tm.cpu().numpy(), _tile_max(zh))
+    tv, ti = bd.topk16_tilemax(z, tm)
+    wv, wi = O.topk16(zh)
+    np.testing.assert_array_equal(ti.cpu().numpy(), wi)
+    np.testing.assert_array_equal(tv.cpu().numpy().view(np.uint32), wv.view(np.uint32))
+
+
 def test_topk_tilemax_bound_refinement():
     """The second bound (the 16th largest of the tile maxima that reach the
     lane-max bound) around its edges: ties at it, a graded run it cuts to 16
