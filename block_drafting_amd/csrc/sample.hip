@@ -254,12 +254,25 @@ __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_kernel(
   //    tiles (in slot order), the inclusive prefix of the tile sums in token
   //    order, 64 at a time, then the first tile whose prefix passes u * total
   if (wave == 0) {
-    if (lane == 0 && resid) {
+    if (resid) {
+      // lanes 0..15 load their candidate's logit together; lane 0 then
+      // applies the corrections in slot order from registers (one memory
+      // round trip instead of sixteen dependent ones)
+      float corr = 0.f;
+      int ct = -1;
+      if (lane < kTopK) {
+        const int v = cand_id[lane];
+        if (v >= 0 && v < V) {
+          const float p = exp2f(zr[v] * s2 - l2);
+          corr = fminf(p, cand_q[lane]);
+          ct = v / kTile;
+        }
+      }
+#pragma unroll
       for (int c = 0; c < kTopK; ++c) {
-        const int v = cand_id[c];
-        if (v < 0 || v >= V) continue;
-        const float p = exp2f(zr[v] * s2 - l2);
-        tsum[v / kTile] -= fminf(p, cand_q[c]);
+        const int t = __builtin_amdgcn_readlane(ct, c);
+        const float cv = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(corr), c));
+        if (lane == 0 && t >= 0) tsum[t] -= cv;
       }
     }
     float carry = 0.f;
