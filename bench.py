@@ -5,7 +5,8 @@ One step = one pass of the whole hot path over one batch:
   two-tap conv(s) -> LM-head logits -> top-16 -> [context gate] -> pair
   scores -> path walk (max-plus, or greedy with --walk greedy / the gated
   workload) -> greedy verification,
-each stage a call into libdflash2 on the current HIP stream.  Inputs are
+each stage a call into libdflash2 on the current HIP stream; scores, walk
+and greedy verification run as one fused launch (--separate: three).  Inputs are
 seeded synthetic tensors already resident in HBM when timing starts.
 
 Prints ONE JSON line (rank 0, N = 1):
@@ -51,6 +52,9 @@ def parse_args(argv=None):
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--separate", action="store_true",
+                    help="pair scores, walk and greedy verification as three launches "
+                         "(default: one fused launch)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replays of the captured step")
     return ap.parse_args(argv)
@@ -189,8 +193,10 @@ def main(argv=None):
     else:
         target = torch.from_numpy(WL.make_targets(w, cand, buf.path_tok.cpu().numpy())).cuda()
 
-    order = (["conv", "gemm", "topk"] + (["gate"] if w.gate else []) + ["pair", "select"] +
-             (["lse"] if sampled else []) + ["verify"])
+    fused = not sampled and not a.separate
+    order = (["conv", "gemm", "topk"] + (["gate"] if w.gate else []) +
+             (["pair_select_verify"] if fused else
+              ["pair", "select"] + (["lse"] if sampled else []) + ["verify"]))
     ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)] for k in order}
     ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
 
@@ -216,13 +222,22 @@ def main(argv=None):
             if i is not None:
                 ev["gate"][i].record()
             gate = bd.context_gate(cur.view(M, H), Wg, buf.gate)
+        ti = buf.top_idx.view(B, L, 16)
+        if fused:
+            # scores, walk and verification in one launch; the scores stay on chip
+            if i is not None:
+                ev["pair_select_verify"][i].record()
+            bd.pair_select_verify(buf.top_val.view(B, L, 16), ti, anchor, U, Vf, target, gate,
+                                  w.walk, None, None, buf.path_slot, buf.path_tok,
+                                  buf.path_score, buf.accept_len, buf.next_tok)
+            if i is not None:
+                ev_end[i].record()
+            return
         if i is not None:
             ev["pair"][i].record()
-        bd.pair_score(buf.top_val.view(B, L, 16), buf.top_idx.view(B, L, 16), anchor, U, Vf, buf.S0, buf.S,
-                      gate=gate)
+        bd.pair_score(buf.top_val.view(B, L, 16), ti, anchor, U, Vf, buf.S0, buf.S, gate=gate)
         if i is not None:
             ev["select"][i].record()
-        ti = buf.top_idx.view(B, L, 16)
         if sampled:
             bd.path_sample(buf.S0, buf.S, ti, u_path, w.temperature, buf.path_slot, buf.path_tok, buf.q)
             if i is not None:
@@ -332,7 +347,8 @@ def main(argv=None):
         "config": {"workload": w.name, "B": B, "L": L, "H": H, "V": V, "r": w.r,
                    "convs": w.n_convs, "conv_groups": w.groups if w.dynamic else 0, "topk": 16,
                    "gate": w.gate, "walk": w.walk, "temperature": w.temperature,
-                   "launch": "hip-graph" if graph is not None else "eager"},
+                   "launch": "hip-graph" if graph is not None else "eager",
+                   "pair_walk_verify": "fused" if fused else "separate"},
         "tokens_per_s": round(M / (ms_step * 1e-3), 1),
         "accepted_tokens_per_s": round(float(acc.sum()) / (ms_step * 1e-3), 1),
         "mean_accept_len": round(float(acc.mean()), 3),

@@ -33,7 +33,7 @@ __all__ = [
     "DFlash2Error", "lib", "library_path", "twotap_conv", "twotap_conv_mm", "lmhead_logits",
     "lmhead_logits_tilemax", "topk16", "topk16_tilemax",
     "topk16_workspace", "logits_topk", "logits_topk_workspace", "context_gate", "pair_score",
-    "path_select", "path_sample", "target_lse", "verify_rejection", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
+    "path_select", "pair_select_verify", "path_sample", "target_lse", "verify_rejection", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
 ]
 
 TOPK = 16
@@ -64,6 +64,8 @@ _SIGS = {
     "dflash2_path_select": ([_P, _P, _P, _I, _I, _P, _P, _P, _P], _I),
     "dflash2_path_select_mode": ([_P, _P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
     "dflash2_verify_greedy": ([_P, _P, _I, _I, _P, _P, _P], _I),
+    "dflash2_pair_select_verify": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P,
+                                    _P, _P, _P, _P, _P, _P], _I),
     "dflash2_path_sample": ([_P, _P, _P, _P, ctypes.c_float, _I, _I, _P, _P, _P, _P], _I),
     "dflash2_target_lse": ([_P, _I, _I, ctypes.c_float, _P, _P], _I),
     "dflash2_verify_rejection": ([_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _I,
@@ -390,6 +392,53 @@ def verify_greedy(path_tok: torch.Tensor, target: torch.Tensor, accept_len=None,
     return accept_len, next_tok
 
 
+def pair_select_verify(top_val: torch.Tensor, top_idx: torch.Tensor,
+                       anchor_tok: Optional[torch.Tensor], U: torch.Tensor, Vf: torch.Tensor,
+                       target: torch.Tensor, gate: Optional[torch.Tensor] = None,
+                       mode: str = "viterbi", S0: Optional[torch.Tensor] = None,
+                       S: Optional[torch.Tensor] = None, path_slot=None, path_tok=None,
+                       path_score=None, accept_len=None, next_tok=None):
+    """pair_score, path_select and verify_greedy in one launch.  The scores
+    are written to S0 / S only when those are given.  Returns (path_slot,
+    path_tok, path_score, accept_len, next_tok)."""
+    if mode not in PATH_MODES:
+        raise ValueError(f"mode must be one of {sorted(PATH_MODES)}, got {mode!r}")
+    B, L, K = top_val.shape
+    V, r = U.shape
+    _shape(top_idx, (B, L, K), "top_idx", torch.int32)
+    _shape(Vf, (V, r), "Vf", U.dtype)
+    _shape(target, (B, L + 1), "target", torch.int32)
+    if anchor_tok is not None:
+        _shape(anchor_tok, (B,), "anchor_tok", torch.int32)
+    if gate is not None:
+        if gate.dim() == 2 and gate.shape[0] == B * L:
+            gate = gate.view(B, L, r)
+        _shape(gate, (B, L, r), "gate", torch.float32)
+    if S0 is not None:
+        _shape(S0, (B, TOPK), "S0", torch.float32)
+    if S is not None:
+        _shape(S, (B, L - 1, TOPK, TOPK), "S", torch.float32)
+    dev = top_val.device
+    if path_slot is None:
+        path_slot = torch.empty((B, L), dtype=torch.int32, device=dev)
+    if path_tok is None:
+        path_tok = torch.empty((B, L), dtype=torch.int32, device=dev)
+    if path_score is None:
+        path_score = torch.empty((B,), dtype=torch.float32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if next_tok is None:
+        next_tok = torch.empty((B,), dtype=torch.int32, device=dev)
+    _dev(top_val, top_idx, anchor_tok, U, Vf, target, gate, S0, S, path_slot, path_tok,
+         path_score, accept_len, next_tok)
+    _check("dflash2_pair_select_verify", lib().dflash2_pair_select_verify(
+        _ptr(top_val), _ptr(top_idx), _ptr(anchor_tok), _ptr(U), _ptr(Vf), _ptr(gate),
+        _ptr(target), B, L, V, r, _dt(U), PATH_MODES[mode], _ptr(S0),
+        _ptr(S) if L > 1 else None, _ptr(path_slot), _ptr(path_tok), _ptr(path_score),
+        _ptr(accept_len), _ptr(next_tok), _stream(dev)))
+    return path_slot, path_tok, path_score, accept_len, next_tok
+
+
 def path_sample(S0: torch.Tensor, S: Optional[torch.Tensor], top_idx: Optional[torch.Tensor],
                 u: torch.Tensor, temperature: float, path_slot=None, path_tok=None, q=None):
     """Sampling walk at temperature T with uniforms u [B, L].
@@ -497,8 +546,10 @@ def run_step(buf: StepBuffers, x: torch.Tensor, convs, W: torch.Tensor, U: torch
     walk (`walk`: "viterbi", "greedy", or "sample" at `temperature` with the
     uniforms `u_path`) and verification: greedy against `target` argmax ids,
     or, for a sampled walk given target logits `z_target` [B, L+1, V], the
-    lossless rejection rule with uniforms `u_acc`, `u_res`.  Every call is
-    enqueued on the current stream; nothing is synchronised."""
+    lossless rejection rule with uniforms `u_acc`, `u_res`.  A walk that is
+    not sampled, with targets given, runs scores, walk and verification in
+    one launch (pair_select_verify).  Every call is enqueued on the current
+    stream; nothing is synchronised."""
     B, L, H, V = buf.B, buf.L, buf.H, buf.V
     cur = x
     for j, c in enumerate(convs):
@@ -518,6 +569,11 @@ def run_step(buf: StepBuffers, x: torch.Tensor, convs, W: torch.Tensor, U: torch
         if buf.gate is None:
             raise ValueError("StepBuffers were made without gate_rank")
         gate = context_gate(cur.view(M, H), Wg, buf.gate)
+    if walk != "sample" and target is not None:
+        pair_select_verify(tv, ti, anchor_tok, U, Vf, target, gate, walk, buf.S0, buf.S,
+                           buf.path_slot, buf.path_tok, buf.path_score, buf.accept_len,
+                           buf.next_tok)
+        return buf
     pair_score(tv, ti, anchor_tok, U, Vf, buf.S0, buf.S, gate=gate)
     if walk == "sample":
         if buf.q is None or u_path is None:

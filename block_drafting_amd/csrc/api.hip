@@ -425,3 +425,48 @@ DFLASH2_API int dflash2_verify_greedy(const int32_t* path_tok, const int32_t* ta
   return status_of(
       launch_verify_greedy(path_tok, target, B, L, accept_len, next_tok, as_stream(stream)));
 }
+
+DFLASH2_API int dflash2_pair_select_verify(
+    const float* top_val, const int32_t* top_idx, const int32_t* anchor_tok, const void* U,
+    const void* Vf, const float* gate, const int32_t* target, int B, int L, int V, int r,
+    int dtype, int mode, float* S0, float* S, int32_t* path_slot, int32_t* path_tok,
+    float* path_score, int32_t* accept_len, int32_t* next_tok, void* stream) {
+  if (!valid_dtype(dtype) || B < 0 || L < 1 || L > DFLASH2_MAX_L || V < kTopK || r < 1 ||
+      r > DFLASH2_MAX_RANK)
+    return DFLASH2_EINVAL;
+  if (mode != DFLASH2_PATH_VITERBI && mode != DFLASH2_PATH_GREEDY) return DFLASH2_EINVAL;
+  if (B == 0) return DFLASH2_OK;
+  if (!top_val || !top_idx || !U || !Vf || !target || !path_slot || !path_score || !accept_len)
+    return DFLASH2_EINVAL;
+  if ((long long)V * r > (1LL << 40) || (long long)B * L * kTopK > kInt32Max)
+    return DFLASH2_EINVAL;
+  const void* a4[] = {top_val, top_idx, anchor_tok, gate,     target,     S0,
+                      S,       path_slot, path_tok, path_score, accept_len, next_tok};
+  for (const void* p : a4)
+    if (p && !aligned4(p)) return DFLASH2_EINVAL;
+  const size_t es = esize(dtype);
+  if (dtype == DFLASH2_BF16 ? ((reinterpret_cast<uintptr_t>(U) | reinterpret_cast<uintptr_t>(Vf)) & 1)
+                            : (!aligned4(U) || !aligned4(Vf)))
+    return DFLASH2_EINVAL;
+  const size_t tb = (size_t)B * L * kTopK * 4;
+  const size_t pb = (size_t)B * L * 4;
+  const size_t ob = (size_t)B * 4;
+  const void* ins[] = {top_val, top_idx, U, Vf, anchor_tok, gate, target};
+  const size_t insz[] = {tb, tb, (size_t)V * r * es, (size_t)V * r * es, ob,
+                         (size_t)B * L * r * 4, (size_t)B * (L + 1) * 4};
+  const void* outs[] = {S0, L > 1 ? S : nullptr, path_slot, path_tok, path_score, accept_len,
+                        next_tok};
+  const size_t outsz[] = {(size_t)B * kTopK * 4, (size_t)B * (L - 1) * kTopK * kTopK * 4, pb, pb,
+                          ob, ob, ob};
+  for (int o = 0; o < 7; ++o) {
+    if (!outs[o]) continue;
+    for (int k = 0; k < 7; ++k)
+      if (overlap(outs[o], outsz[o], ins[k], insz[k])) return DFLASH2_EINVAL;
+    for (int k = o + 1; k < 7; ++k)
+      if (outs[k] && overlap(outs[o], outsz[o], outs[k], outsz[k])) return DFLASH2_EINVAL;
+  }
+  return status_of(launch_pair_walk_verify(
+      top_val, top_idx, anchor_tok, U, Vf, gate, target, B, L, V, r, dtype,
+      mode == DFLASH2_PATH_GREEDY, S0, L > 1 ? S : nullptr, path_slot, path_tok, path_score,
+      accept_len, next_tok, as_stream(stream)));
+}

@@ -14,6 +14,7 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTopK = 16;
 constexpr int kWave = 64;
+constexpr int kMaxWalk = 64;  // longest block a path walk takes (one slot per lane)
 
 // bf16 storage <-> fp32 arithmetic.  A bf16 value is the upper half of an
 // IEEE single, so widening is a shift; narrowing uses the gfx950 hardware
@@ -86,6 +87,14 @@ hipError_t launch_topk16(const float* logits, float* top_val, int32_t* top_idx, 
 hipError_t launch_topk16_tilemax(const float* logits, const float* tmax, float* top_val,
                                  int32_t* top_idx, int M, int V, hipStream_t s);
 
+// Pair scores + walk (greedy != 0: best successor, else max-plus) + greedy
+// verification of each block in one launch; S0 / S may be NULL.
+hipError_t launch_pair_walk_verify(const float* top_val, const int32_t* top_idx,
+                                   const int32_t* anchor_tok, const void* U, const void* Vf,
+                                   const float* gate, const int32_t* target, int B, int L, int V,
+                                   int r, int dtype, int greedy, float* S0, float* S,
+                                   int32_t* path_slot, int32_t* path_tok, float* path_score,
+                                   int32_t* accept_len, int32_t* next_tok, hipStream_t s);
 hipError_t launch_pair_score(const float* top_val, const int32_t* top_idx,
                              const int32_t* anchor_tok, const void* U, const void* Vf,
                              const float* gate, int B, int L, int V, int r, int dtype, float* S0,

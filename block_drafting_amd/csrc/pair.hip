@@ -13,7 +13,7 @@
 // gathers one contiguous run of each factor row straight into registers
 // (16-byte loads, all in flight at once) and no LDS is needed.  Products and
 // sums are fp32, as in a plain fp32 dot.
-#include "common.hpp"
+#include "walk.hpp"
 
 namespace dflash2 {
 namespace {
@@ -83,18 +83,17 @@ __device__ __forceinline__ void load_chunk(Chunk<T, RC>& c, const T* __restrict_
 }
 
 // RC: the most elements one lane holds per factor row (>= ceil(r / 4)).
+// The 16 x 16 block of position t of block b, computed by one wave: lane
+// l = 16 q + i ends with tv = the logit of candidate i and, in res[e], the
+// match of previous candidate 4 q + e with candidate i, so the score
+// S_t[4 q + e][i] is tv + res[e] (for t = 0, row 0 holds the anchor's).
 template <typename T, int RC, bool VEC>
-__global__ __launch_bounds__(64) void pair_score_kernel(const float* __restrict__ top_val,
-                                                        const int32_t* __restrict__ top_idx,
-                                                        const int32_t* __restrict__ anchor_tok,
-                                                        const T* __restrict__ U,
-                                                        const T* __restrict__ Vf,
-                                                        const float* __restrict__ gate, int L,
-                                                        int V, int r, float* __restrict__ S0,
-                                                        float* __restrict__ S) {
-  const int b = blockIdx.x / L;
-  const int t = blockIdx.x - b * L;
-  const int lane = threadIdx.x;
+__device__ __forceinline__ void pair_block(const float* __restrict__ top_val,
+                                           const int32_t* __restrict__ top_idx,
+                                           const int32_t* __restrict__ anchor_tok,
+                                           const T* __restrict__ U, const T* __restrict__ Vf,
+                                           const float* __restrict__ gate, int b, int t, int L,
+                                           int V, int r, int lane, float& tv, f32x4_t& res) {
   const int i = lane & 15;  // row of the previous factors / column of the current ones
   const int q = lane >> 4;  // quarter of the rank this lane feeds
   const int rc = (r + 3) >> 2;
@@ -131,7 +130,7 @@ __global__ __launch_bounds__(64) void pair_score_kernel(const float* __restrict_
       }
     }
   }
-  const float tv = top_val[bt * kTopK + i];
+  tv = top_val[bt * kTopK + i];
 
   // C[i][j] = sum_k A[i][k] B[k][j]; two accumulators alternate so that
   // consecutive steps do not wait on each other.
@@ -149,13 +148,109 @@ __global__ __launch_bounds__(64) void pair_score_kernel(const float* __restrict_
   }
   // Lane l holds C[4 (l / 16) + e][l % 16] in element e: column j = i, whose
   // own logit this lane already holds.
+#pragma unroll
+  for (int e = 0; e < 4; ++e) res[e] = acc0[e] + acc1[e];
+}
+
+template <typename T, int RC, bool VEC>
+__global__ __launch_bounds__(64) void pair_score_kernel(const float* __restrict__ top_val,
+                                                        const int32_t* __restrict__ top_idx,
+                                                        const int32_t* __restrict__ anchor_tok,
+                                                        const T* __restrict__ U,
+                                                        const T* __restrict__ Vf,
+                                                        const float* __restrict__ gate, int L,
+                                                        int V, int r, float* __restrict__ S0,
+                                                        float* __restrict__ S) {
+  const int b = blockIdx.x / L;
+  const int t = blockIdx.x - b * L;
+  const int lane = threadIdx.x;
+  const int i = lane & 15;
+  const int q = lane >> 4;
+  float tv;
+  f32x4_t res;
+  pair_block<T, RC, VEC>(top_val, top_idx, anchor_tok, U, Vf, gate, b, t, L, V, r, lane, tv, res);
   if (t == 0) {
-    if (q == 0) S0[(size_t)b * kTopK + i] = tv + (acc0[0] + acc1[0]);
+    if (q == 0) S0[(size_t)b * kTopK + i] = tv + res[0];
     return;
   }
   float* dst = S + ((size_t)b * (L - 1) + (t - 1)) * kTopK * kTopK;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) dst[(4 * q + e) * kTopK + i] = tv + (acc0[e] + acc1[e]);
+  for (int e = 0; e < 4; ++e) dst[(4 * q + e) * kTopK + i] = tv + res[e];
+}
+
+// Pair scores, path walk and greedy verification of one block in one
+// workgroup: the step's three latency-bound stages in one launch, with the
+// scores kept in LDS between them.  Waves take the positions t = wave,
+// wave + waves, ... and leave each 16 x 16 block in LDS (and, when S0out /
+// Sout are given, in global memory too); wave 0 then walks the scores in LDS
+// (the max-plus walk keeps its back-pointer rows in score blocks it has
+// already walked) and compares the walked tokens with the targets.  Every
+// part runs the separate kernels' arithmetic, so the results are the same
+// bit for bit.  LDS: (L-1) x 1 KiB of scores plus 80 bytes.  Up to 16 waves
+// per block; 8 where r > 128, whose score registers would not fit 16.
+template <int RC>
+constexpr int pwv_max_waves() { return RC >= 32 ? 8 : 16; }
+
+template <typename T, int RC, bool VEC, bool GREEDY>
+__global__ __launch_bounds__(64 * pwv_max_waves<RC>()) void pair_walk_verify_kernel(
+    const float* __restrict__ top_val, const int32_t* __restrict__ top_idx,
+    const int32_t* __restrict__ anchor_tok, const T* __restrict__ U, const T* __restrict__ Vf,
+    const float* __restrict__ gate, const int32_t* __restrict__ target, int L, int V, int r,
+    float* __restrict__ S0out, float* __restrict__ Sout, int32_t* __restrict__ path_slot,
+    int32_t* __restrict__ path_tok, float* __restrict__ path_score,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ next_tok) {
+  extern __shared__ float sS[];         // (L - 1) x 16 x 16 scores
+  __shared__ float sS0[kTopK];          // S0, then the max-plus walk's running maxima
+  __shared__ uint8_t sslot[kMaxWalk];   // walked slots
+  const int b = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
+  const int i = lane & 15;
+  const int q = lane >> 4;
+  for (int t = wave; t < L; t += nw) {
+    float tv;
+    f32x4_t res;
+    pair_block<T, RC, VEC>(top_val, top_idx, anchor_tok, U, Vf, gate, b, t, L, V, r, lane, tv,
+                           res);
+    if (t == 0) {
+      if (q == 0) {
+        const float v = tv + res[0];
+        sS0[i] = v;
+        if (S0out) S0out[(size_t)b * kTopK + i] = v;
+      }
+    } else {
+      float* dl = sS + (size_t)(t - 1) * kTopK * kTopK;
+      float* dg = Sout ? Sout + ((size_t)b * (L - 1) + (t - 1)) * kTopK * kTopK : nullptr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = tv + res[e];
+        dl[(4 * q + e) * kTopK + i] = v;
+        if (dg) dg[(4 * q + e) * kTopK + i] = v;
+      }
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  if (GREEDY)
+    greedy_walk(sS0, sS, top_idx, b, L, path_slot, path_tok, path_score, sslot);
+  else
+    viterbi_walk<false>(sS0, sS, top_idx, b, L, sS0, reinterpret_cast<uint8_t*>(sS),
+                        kTopK * kTopK * (int)sizeof(float), path_slot, path_tok, path_score,
+                        sslot);
+  __builtin_amdgcn_wave_barrier();
+  // Greedy verification: accepted = the longest prefix of walked tokens equal
+  // to the targets, plus the target after it.
+  const size_t row = (size_t)b * L;
+  const int32_t* g = target + (size_t)b * (L + 1);
+  bool miss = false;
+  if (lane < L) miss = top_idx[(row + lane) * kTopK + sslot[lane]] != g[lane];
+  const uint64_t mm = __ballot(miss);
+  const int n = mm ? (int)__builtin_ctzll(mm) : L;
+  if (lane == 0) {
+    accept_len[b] = n + 1;
+    if (next_tok) next_tok[b] = g[n];
+  }
 }
 
 template <typename T, int RC>
@@ -205,6 +300,84 @@ hipError_t launch_pair_score(const float* top_val, const int32_t* top_idx,
   } else {
     const bool vec = r % 16 == 0 && (bases & 15) == 0;
     launch_t<float>(vec, grid, s, top_val, top_idx, anchor_tok, U, Vf, gate, L, V, r, S0, S);
+  }
+  return hipGetLastError();
+}
+
+namespace {
+template <typename T, int RC, bool GREEDY>
+void launch_pwv_rc(bool vec, dim3 grid, size_t lds, hipStream_t s,
+                   const float* top_val, const int32_t* top_idx, const int32_t* anchor_tok,
+                   const void* U, const void* Vf, const float* gate, const int32_t* target, int L,
+                   int V, int r, float* S0, float* S, int32_t* path_slot, int32_t* path_tok,
+                   float* path_score, int32_t* accept_len, int32_t* next_tok) {
+  const T* u = static_cast<const T*>(U);
+  const T* v = static_cast<const T*>(Vf);
+  const dim3 block((unsigned)(64 * min(L, pwv_max_waves<RC>())));
+  if (vec)
+    hipLaunchKernelGGL((pair_walk_verify_kernel<T, RC, true, GREEDY>), grid, block, lds, s,
+                       top_val, top_idx, anchor_tok, u, v, gate, target, L, V, r, S0, S,
+                       path_slot, path_tok, path_score, accept_len, next_tok);
+  else
+    hipLaunchKernelGGL((pair_walk_verify_kernel<T, RC, false, GREEDY>), grid, block, lds, s,
+                       top_val, top_idx, anchor_tok, u, v, gate, target, L, V, r, S0, S,
+                       path_slot, path_tok, path_score, accept_len, next_tok);
+}
+
+template <typename T, bool GREEDY>
+void launch_pwv_t(bool vec, dim3 grid, size_t lds, hipStream_t s,
+                  const float* top_val, const int32_t* top_idx, const int32_t* anchor_tok,
+                  const void* U, const void* Vf, const float* gate, const int32_t* target, int L,
+                  int V, int r, float* S0, float* S, int32_t* path_slot, int32_t* path_tok,
+                  float* path_score, int32_t* accept_len, int32_t* next_tok) {
+  const int rc = (r + 3) / 4;
+#define DFLASH2_PWV(RC)                                                                         \
+  launch_pwv_rc<T, RC, GREEDY>(vec, grid, lds, s, top_val, top_idx, anchor_tok, U, Vf,   \
+                               gate, target, L, V, r, S0, S, path_slot, path_tok, path_score,   \
+                               accept_len, next_tok)
+  if (rc <= 8)
+    DFLASH2_PWV(8);
+  else if (rc <= 16)
+    DFLASH2_PWV(16);
+  else if (rc <= 32)
+    DFLASH2_PWV(32);
+  else
+    DFLASH2_PWV(64);
+#undef DFLASH2_PWV
+}
+}  // namespace
+
+hipError_t launch_pair_walk_verify(const float* top_val, const int32_t* top_idx,
+                                   const int32_t* anchor_tok, const void* U, const void* Vf,
+                                   const float* gate, const int32_t* target, int B, int L, int V,
+                                   int r, int dtype, int greedy, float* S0, float* S,
+                                   int32_t* path_slot, int32_t* path_tok, float* path_score,
+                                   int32_t* accept_len, int32_t* next_tok, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const dim3 grid((unsigned)B);
+  const size_t lds = (size_t)(L - 1) * kTopK * kTopK * sizeof(float);
+  const uintptr_t bases = reinterpret_cast<uintptr_t>(U) | reinterpret_cast<uintptr_t>(Vf) |
+                          reinterpret_cast<uintptr_t>(gate);
+  if (dtype == 1) {
+    const bool vec = r % 32 == 0 && (bases & 15) == 0;
+    if (greedy)
+      launch_pwv_t<uint16_t, true>(vec, grid, lds, s, top_val, top_idx, anchor_tok, U, Vf,
+                                   gate, target, L, V, r, S0, S, path_slot, path_tok, path_score,
+                                   accept_len, next_tok);
+    else
+      launch_pwv_t<uint16_t, false>(vec, grid, lds, s, top_val, top_idx, anchor_tok, U, Vf,
+                                    gate, target, L, V, r, S0, S, path_slot, path_tok, path_score,
+                                    accept_len, next_tok);
+  } else {
+    const bool vec = r % 16 == 0 && (bases & 15) == 0;
+    if (greedy)
+      launch_pwv_t<float, true>(vec, grid, lds, s, top_val, top_idx, anchor_tok, U, Vf,
+                                gate, target, L, V, r, S0, S, path_slot, path_tok, path_score,
+                                accept_len, next_tok);
+    else
+      launch_pwv_t<float, false>(vec, grid, lds, s, top_val, top_idx, anchor_tok, U, Vf,
+                                 gate, target, L, V, r, S0, S, path_slot, path_tok, path_score,
+                                 accept_len, next_tok);
   }
   return hipGetLastError();
 }

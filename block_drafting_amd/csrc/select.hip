@@ -9,17 +9,10 @@
 // four predecessors i = 4q..4q+3 of candidate j; two cross-row exchanges
 // (xor 16, xor 32) finish the max with the lowest-index tie rule.  Scores of
 // step t+1 are prefetched while step t reduces.
-#include "common.hpp"
+#include "walk.hpp"
 
 namespace dflash2 {
 namespace {
-
-__device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
-  if (ov > bv || (ov == bv && oi < bi)) {
-    bv = ov;
-    bi = oi;
-  }
-}
 
 __global__ __launch_bounds__(64) void path_select_kernel(const float* __restrict__ S0,
                                                          const float* __restrict__ S,
@@ -30,78 +23,14 @@ __global__ __launch_bounds__(64) void path_select_kernel(const float* __restrict
   __shared__ float delta[kTopK];
   __shared__ uint8_t back[64][kTopK];
   const int b = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int j = lane & 15;
-  const int q = lane >> 4;
-  if (lane < kTopK) delta[lane] = S0[(size_t)b * kTopK + lane];
-  const float* Sb = S + (size_t)b * (L - 1) * kTopK * kTopK;
-  float s_next[4];
-  if (L > 1) {
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) s_next[ii] = Sb[(q * 4 + ii) * kTopK + j];
-  }
-  __syncthreads();
-  for (int t = 1; t < L; ++t) {
-    float s_cur[4];
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) s_cur[ii] = s_next[ii];
-    if (t + 1 < L) {
-      const float* St = Sb + (size_t)t * kTopK * kTopK;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) s_next[ii] = St[(q * 4 + ii) * kTopK + j];
-    }
-    float bv = delta[q * 4] + s_cur[0];
-    int bi = q * 4;
-#pragma unroll
-    for (int ii = 1; ii < 4; ++ii) {
-      const float v = delta[q * 4 + ii] + s_cur[ii];
-      if (v > bv) {
-        bv = v;
-        bi = q * 4 + ii;
-      }
-    }
-    better(bv, bi, __shfl_xor(bv, 16, 64), __shfl_xor(bi, 16, 64));
-    better(bv, bi, __shfl_xor(bv, 32, 64), __shfl_xor(bi, 32, 64));
-    __syncthreads();
-    if (q == 0) {
-      delta[j] = bv;
-      back[t][j] = (uint8_t)bi;
-    }
-    __syncthreads();
-  }
-  if (lane == 0) {
-    int js = 0;
-    float best = delta[0];
-    for (int jj = 1; jj < kTopK; ++jj) {
-      if (delta[jj] > best) {
-        best = delta[jj];
-        js = jj;
-      }
-    }
-    path_score[b] = best;
-    int slot = js;
-    for (int t = L - 1; t >= 0; --t) {
-      path_slot[(size_t)b * L + t] = slot;
-      if (path_tok) path_tok[(size_t)b * L + t] = top_idx[((size_t)b * L + t) * kTopK + slot];
-      if (t > 0) slot = back[t][slot];
-    }
-  }
+  viterbi_walk<true>(S0 + (size_t)b * kTopK, S + (size_t)b * (L - 1) * kTopK * kTopK, top_idx, b,
+                     L, delta, &back[1][0], kTopK, path_slot, path_tok, path_score, nullptr);
 }
 
-// Index-tracking max over one aligned group of 16 lanes (lowest slot on ties);
-// every lane of the group ends with the winner.
-__device__ __forceinline__ void argmax16(float& bv, int& bi) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) better(bv, bi, __shfl_xor(bv, m, 64), __shfl_xor(bi, m, 64));
-}
-
-// Best-successor walk, the post's own decoder: p_0 = argmax S0, then
-// p_t = argmax_j S[t-1, p_{t-1}, j], lowest slot on ties; the score is the fp32
-// running sum along the walk.  Each step depends on the previous argmax, so
-// the wave first copies every row the walk might visit ((L-1) x 16 x 16
-// floats, all loads in flight at once) into LDS and then walks there: one
-// memory latency per block instead of one per position.  Lanes j = lane & 15
-// hold candidate j; the four quarters of the wave walk the same block.
+// The greedy walk's next row depends on the last argmax, so the wave first
+// copies every row the walk might visit ((L-1) x 16 x 16 floats, all loads in
+// flight at once) into LDS and then walks there: one memory latency per block
+// instead of one per position.
 __global__ __launch_bounds__(64) void path_greedy_kernel(const float* __restrict__ S0,
                                                          const float* __restrict__ S,
                                                          const int32_t* __restrict__ top_idx,
@@ -112,7 +41,6 @@ __global__ __launch_bounds__(64) void path_greedy_kernel(const float* __restrict
   constexpr int kUnroll = 8;
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
-  const int j = lane & 15;
   const int n4 = (L - 1) * kTopK * kTopK / 4;
   const f32x4_t* src = reinterpret_cast<const f32x4_t*>(S + (size_t)b * (L - 1) * kTopK * kTopK);
   for (int base = 0; base < n4; base += 64 * kUnroll) {
@@ -128,29 +56,9 @@ __global__ __launch_bounds__(64) void path_greedy_kernel(const float* __restrict
       if (e < n4) stage[e] = v[u];
     }
   }
-  float bv = S0[(size_t)b * kTopK + j];
-  int p = j;
-  argmax16(bv, p);
-  float score = bv;
-  const size_t row = (size_t)b * L;
-  if (lane == 0) {
-    path_slot[row] = p;
-    if (path_tok) path_tok[row] = top_idx[row * kTopK + p];
-  }
   __syncthreads();
-  const float* sS = reinterpret_cast<const float*>(stage);
-  for (int t = 1; t < L; ++t) {
-    bv = sS[((t - 1) * kTopK + p) * kTopK + j];
-    int bi = j;
-    argmax16(bv, bi);
-    score = score + bv;
-    p = bi;
-    if (lane == 0) {
-      path_slot[row + t] = p;
-      if (path_tok) path_tok[row + t] = top_idx[(row + t) * kTopK + p];
-    }
-  }
-  if (lane == 0) path_score[b] = score;
+  greedy_walk(S0 + (size_t)b * kTopK, reinterpret_cast<const float*>(stage), top_idx, b, L,
+              path_slot, path_tok, path_score, nullptr);
 }
 
 __global__ __launch_bounds__(256) void verify_greedy_kernel(const int32_t* __restrict__ path_tok,

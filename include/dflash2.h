@@ -13,6 +13,7 @@
  *   per-16-channel conv corrections  dflash2_twotap_conv_mm
  *   context-gated pair scores        dflash2_context_gate, dflash2_pair_score_gated
  *   best-successor (greedy) walk     dflash2_path_select_mode(..., DFLASH2_PATH_GREEDY, ...)
+ *   steps 3-5 in one launch          dflash2_pair_select_verify
  *   sampling at T > 0, lossless      dflash2_path_sample, dflash2_target_lse,
  *   rejection verification           dflash2_verify_rejection
  *
@@ -317,6 +318,27 @@ int dflash2_verify_rejection(const int32_t* path_slot, const int32_t* path_tok,
 int dflash2_verify_greedy(const int32_t* path_tok, const int32_t* target,
                           int B, int L, int32_t* accept_len, int32_t* next_tok,
                           void* stream);
+
+/*
+ * Steps 3-5 in one launch: dflash2_pair_score_gated (gate != NULL) or
+ * dflash2_pair_score (gate == NULL), then dflash2_path_select_mode with
+ * `mode`, then dflash2_verify_greedy on the walked tokens, for each block in
+ * one workgroup with the scores kept on chip.  [POST] "A lightweight path
+ * selector" (scores, walk) and "The right token is already in the
+ * candidates", Table 1 (acceptance length).  The outputs are bit for bit
+ * those of the three calls.  Arguments, layouts, limits and errors are
+ * theirs, with these differences: S0 and S are optional outputs (NULL: the
+ * scores stay on chip); path_tok may be NULL; target [B, L+1], accept_len [B]
+ * are required, next_tok [B] may be NULL.  Every pointer is 4-byte aligned
+ * (U and Vf: 2-byte for bf16), and no output may overlap an input or another
+ * output.
+ */
+int dflash2_pair_select_verify(const float* top_val, const int32_t* top_idx,
+                               const int32_t* anchor_tok, const void* U, const void* Vf,
+                               const float* gate, const int32_t* target, int B, int L, int V,
+                               int r, int dtype, int mode, float* S0, float* S,
+                               int32_t* path_slot, int32_t* path_tok, float* path_score,
+                               int32_t* accept_len, int32_t* next_tok, void* stream);
 
 #ifdef __cplusplus
 }

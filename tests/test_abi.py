@@ -172,6 +172,43 @@ def test_pair_select_verify_validation():
     assert ver(P, Q, 0, 8, P + 0x1000, None, None) == 0
 
 
+def test_fused_pair_walk_verify_validation():
+    f = bd.lib().dflash2_pair_select_verify
+    ok = dict(tv=P, ti=P + 0x10000, anc=None, U=Q, Vf=Q + 0x100000, gate=None, tg=P + 0x50000,
+              B=2, L=4, V=100, r=8, dt=1, mode=0, S0=P + 0x20000, S=P + 0x30000,
+              slot=P + 0x60000, tok=P + 0x61000, score=P + 0x62000, acc=P + 0x63000,
+              nt=P + 0x64000)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(*(a[k] for k in ok), None)
+
+    # every call below is rejected (or empty) before anything is launched
+
+    assert call(B=0) == 0
+    assert call(B=-1) == EINVAL
+    assert call(mode=2) == EINVAL
+    assert call(mode=-1) == EINVAL
+    assert call(L=0) == EINVAL
+    assert call(L=65) == EINVAL
+    assert call(r=0) == EINVAL
+    assert call(r=257) == EINVAL
+    assert call(V=15) == EINVAL
+    assert call(dt=3) == EINVAL
+    for k in ("tv", "ti", "U", "Vf", "tg", "slot", "score", "acc"):
+        assert call(**{k: None}) == EINVAL, k
+    assert call(tg=P + 0x50002) == EINVAL        # misaligned target
+    assert call(U=Q + 1) == EINVAL                # odd bf16 factor address
+    assert call(acc=P + 0x50004) == EINVAL        # accept_len overlaps target
+    assert call(S=P) == EINVAL                    # S overlaps top_val
+    assert call(S0=P + 0x30000 + 64) == EINVAL    # S0 inside S
+    assert call(tok=P + 0x60000) == EINVAL        # path_tok aliases path_slot
+    assert call(nt=P + 0x63000) == EINVAL         # next_tok aliases accept_len
+    assert call(gate=P + 0x20000) == EINVAL       # gate overlaps S0
+    assert call(slot=Q + 0x100000) == EINVAL      # output over a factor
+    assert call(S0=None, S=None, B=0) == 0        # scores may stay on chip
+
+
 def test_gate_and_gated_pair_validation():
     L = bd.lib()
     cg = L.dflash2_context_gate

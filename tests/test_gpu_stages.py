@@ -26,6 +26,8 @@ Bars (floating point from the arithmetic, integers exact):
             1e-5 of the mass away from every bin edge, else inside that
             window; emitted tokens follow the target (chi-square, GPU)
   verify    exact
+  fused     scores, walk and verification in one launch: bit for bit the
+            three separate calls
 """
 import numpy as np
 import pytest
@@ -652,3 +654,99 @@ def test_verify_parity():
         a, n = bd.verify_greedy(torch.from_numpy(path).to(DEV), torch.from_numpy(tgt).to(DEV))
         np.testing.assert_array_equal(a.cpu().numpy(), wa)
         np.testing.assert_array_equal(n.cpu().numpy(), wn)
+
+
+# ------------------------------------------------------------------ fused scores + walk + verify
+def _plant_targets(path_tok, V, seed):
+    """Targets that follow the walked tokens for a random prefix of each block
+    (every length from 0 to L occurs), then differ."""
+    g = np.random.default_rng(seed)
+    B, L = path_tok.shape
+    tgt = np.empty((B, L + 1), np.int32)
+    tgt[:, :L] = path_tok
+    tgt[:, L] = g.integers(0, V, B)
+    n = np.arange(B) % (L + 1)
+    for b in range(B):
+        if n[b] < L:
+            tgt[b, n[b]] = (path_tok[b, n[b]] + 1 + g.integers(0, V - 1)) % V
+    return tgt
+
+
+@pytest.mark.parametrize("mode", ["viterbi", "greedy"])
+@pytest.mark.parametrize("dt,B,L,V,r,gated,ties", [
+    ("f32", 1, 1, 64, 1, False, False), ("bf16", 3, 2, 500, 7, True, False),
+    ("bf16", 64, 8, 4096, 32, False, True), ("f32", 5, 16, 151936, 64, True, False),
+    ("bf16", 40, 16, 151936, 256, False, False), ("bf16", 9, 17, 2000, 128, True, False),
+    ("f32", 2, 5, 300, 256, False, False), ("bf16", 3, 64, 1000, 16, False, True),
+    ("bf16", 5, 64, 3000, 256, True, False), ("f32", 300, 3, 700, 8, False, False)])
+def test_fused_pair_walk_verify_matches_the_separate_calls(mode, dt, B, L, V, r, gated, ties):
+    tv, ti, at, U, Vf = _pair_case(B, L, V, r, dt, seed=B * 7 + L + r)
+    if ties:                                   # dyadic scores, no pair term: ties everywhere
+        tv = (np.round(tv * 2) / 4).astype(np.float32)
+        U = np.zeros_like(U)
+    gate = (np.random.default_rng(r).random((B, L, r)).astype(np.float32) if gated else None)
+    d = dict(tv=torch.from_numpy(tv).to(DEV), ti=torch.from_numpy(ti).to(DEV),
+             at=torch.from_numpy(at).to(DEV), U=to_dev(U, dt), Vf=to_dev(Vf, dt),
+             gate=None if gate is None else torch.from_numpy(gate).to(DEV))
+    S0, S = bd.pair_score(d["tv"], d["ti"], d["at"], d["U"], d["Vf"], gate=d["gate"])
+    slot, tok, score = bd.path_select(S0, S if L > 1 else None, d["ti"], mode=mode)
+    tgt = _plant_targets(tok.cpu().numpy(), V, seed=B + L)
+    tg = torch.from_numpy(tgt).to(DEV)
+    acc, nxt = bd.verify_greedy(tok, tg)
+    # fused, scores written out
+    fS0 = torch.full_like(S0, 7.0)
+    fS = torch.full_like(S, 7.0)
+    f = bd.pair_select_verify(d["tv"], d["ti"], d["at"], d["U"], d["Vf"], tg, d["gate"], mode,
+                              fS0, fS)
+    assert torch.equal(fS0, S0) and torch.equal(fS, S)
+    for got, want in zip(f, (slot, tok, score, acc, nxt)):
+        assert torch.equal(got, want)
+    # fused, scores kept on chip: the same outputs
+    g2 = bd.pair_select_verify(d["tv"], d["ti"], d["at"], d["U"], d["Vf"], tg, d["gate"], mode)
+    for got, want in zip(g2, (slot, tok, score, acc, nxt)):
+        assert torch.equal(got, want)
+    # and the acceptance follows the oracle's rule on the walked tokens
+    wa, wn = O.verify_greedy(f[1].cpu().numpy(), tgt)
+    np.testing.assert_array_equal(f[3].cpu().numpy(), wa)
+    np.testing.assert_array_equal(f[4].cpu().numpy(), wn)
+    if B >= L + 1:
+        assert set(np.unique(wa)) == set(range(1, L + 2))
+
+
+def test_fused_pair_walk_verify_against_the_oracle():
+    B, L, V, r, dt = 6, 16, 4096, 64, "bf16"
+    tv, ti, at, U, Vf = _pair_case(B, L, V, r, dt, seed=11)
+    wS0, wS = O.pair_scores(tv, ti, at, U, Vf, dt)
+    d = [torch.from_numpy(tv).to(DEV), torch.from_numpy(ti).to(DEV), torch.from_numpy(at).to(DEV),
+         to_dev(U, dt), to_dev(Vf, dt)]
+    S0 = torch.empty((B, 16), device=DEV)
+    S = torch.empty((B, L - 1, 16, 16), device=DEV)
+    probe = bd.pair_select_verify(*d, torch.zeros((B, L + 1), dtype=torch.int32, device=DEV),
+                                  None, "viterbi", S0, S)
+    assert np.abs(S0.cpu().numpy() - wS0).max() <= 1e-4
+    assert np.abs(S.cpu().numpy() - wS).max() <= 1e-4
+    # the walk is exact on the scores the kernel computed
+    ws, wt, wsc = O.path_select(S0.cpu().numpy(), S.cpu().numpy(), ti)
+    np.testing.assert_array_equal(probe[0].cpu().numpy(), ws)
+    np.testing.assert_array_equal(probe[1].cpu().numpy(), wt)
+    np.testing.assert_array_equal(probe[2].cpu().numpy().view(np.uint32), wsc.view(np.uint32))
+    tgt = _plant_targets(wt, V, seed=3)
+    out = bd.pair_select_verify(*d, torch.from_numpy(tgt).to(DEV), None, "viterbi")
+    wa, wn = O.verify_greedy(wt, tgt)
+    np.testing.assert_array_equal(out[3].cpu().numpy(), wa)
+    np.testing.assert_array_equal(out[4].cpu().numpy(), wn)
+    gs, gt, gsc = O.path_select_greedy(S0.cpu().numpy(), S.cpu().numpy(), ti)
+    out = bd.pair_select_verify(*d, torch.from_numpy(tgt).to(DEV), None, "greedy")
+    np.testing.assert_array_equal(out[0].cpu().numpy(), gs)
+    np.testing.assert_array_equal(out[2].cpu().numpy().view(np.uint32), gsc.view(np.uint32))
+    ga, gn = O.verify_greedy(gt, tgt)
+    np.testing.assert_array_equal(out[3].cpu().numpy(), ga)
+    np.testing.assert_array_equal(out[4].cpu().numpy(), gn)
+
+
+def test_fused_pair_walk_verify_empty_batch():
+    U = torch.zeros((64, 8), device=DEV)
+    e = torch.empty((0, 4, 16), device=DEV)
+    out = bd.pair_select_verify(e, e.to(torch.int32), None, U, U,
+                                torch.empty((0, 5), dtype=torch.int32, device=DEV))
+    assert all(t.shape[0] == 0 for t in out)

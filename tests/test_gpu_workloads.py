@@ -408,6 +408,24 @@ def test_step_is_deterministic(case):
         assert torch.equal(a, b)
 
 
+def test_fused_step_matches_the_separate_calls(case):
+    """run_step with targets (scores, walk and verification in one launch)
+    reproduces the separate calls' scores, path and acceptance bit for bit."""
+    w, buf, dev = case["w"], case["buf"], case["dev"]
+    if w.temperature > 0:
+        pytest.skip("a sampled walk verifies by rejection, not fused")
+    outs = (buf.S0, buf.S, buf.path_slot, buf.path_tok, buf.path_score, buf.accept_len,
+            buf.next_tok)
+    want = [t.clone() for t in outs]
+    for t in outs:
+        t.fill_(-3)
+    bd.run_step(buf, dev["x"], dev["convs"], dev["W"], dev["U"], dev["Vf"], dev["anchor_tok"],
+                to_dev(case["tgt"], "i32"), Wg=dev["Wg"], walk=w.walk)
+    torch.cuda.synchronize()
+    for t, r in zip(outs, want):
+        assert torch.equal(t, r)
+
+
 def test_step_graph_replays_match_eager(case):
     """The whole step captured as a HIP graph (as the benchmark times it):
     every replay, with eager steps and synchronisations in between, gives the
@@ -417,12 +435,15 @@ def test_step_graph_replays_match_eager(case):
         pytest.skip("checked on the benchmark, the gated and the sampled workload")
     kw = dict(Wg=dev["Wg"], walk=w.walk, temperature=w.temperature, u_path=dev.get("u_path"),
               z_target=dev.get("z_target"), u_acc=dev.get("u_acc"), u_res=dev.get("u_res"))
+    # with targets, a walk that is not sampled runs the fused scores-walk-verify launch
+    tgt = None if w.temperature > 0 else to_dev(case["tgt"], "i32")
 
     def step():
         bd.run_step(buf, dev["x"], dev["convs"], dev["W"], dev["U"], dev["Vf"], dev["anchor_tok"],
-                    None, **kw)
+                    tgt, **kw)
 
-    outs = (buf.logits, buf.top_val, buf.top_idx, buf.S0, buf.S, buf.path_slot, buf.path_tok)
+    outs = (buf.logits, buf.top_val, buf.top_idx, buf.S0, buf.S, buf.path_slot, buf.path_tok,
+            buf.accept_len, buf.next_tok)
     step()
     torch.cuda.synchronize()
     want = [t.clone() for t in outs]
