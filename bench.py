@@ -14,7 +14,9 @@ Prints ONE JSON line (rank 0, N = 1):
   captured once as a HIP graph and replayed (--eager: plain launches);
   stage_ms = per-stage times from a second, eager pass with events;
   roofline = the LM-head GEMM kernel (the dominant kernel) against the bf16
-  matrix-core peak, its duration measured with HIP events on its stream;
+  matrix-core peak (against HBM when its flop per algorithmic byte is below
+  the ridge, as for the 4b-head workload), its duration measured with HIP
+  events on its stream;
   cpu_baseline = the CPU oracle on a bounded block sample, same inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
@@ -312,7 +314,15 @@ def main(argv=None):
     ms_step = wall * 1e3 / a.steps
     gemm_s = stage_ms["gemm"] * 1e-3
     flops = 2.0 * M * H * V
-    if bf16:
+    # algorithmic GEMM bytes: W and h read once, logits and tile maxima written
+    gemm_bytes = (V * H + M * H) * (2 if bf16 else 4) + M * V * 4 + M * ((V + 255) // 256) * 4
+    if bf16 and flops / gemm_bytes < PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
+        # below the ridge (small M): HBM-bound
+        achieved = gemm_bytes / gemm_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic(w.name)}
+    elif bf16:
         achieved = flops / gemm_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
