@@ -6,7 +6,10 @@ One step = one pass of the whole hot path over one batch:
   scores -> path walk (max-plus, or greedy with --walk greedy / the gated
   workload) -> greedy verification,
 each stage a call into libdflash2 on the current HIP stream; scores, walk
-and greedy verification run as one fused launch (--separate: three).  Inputs are
+and greedy verification run as one fused launch, and a sampled walk's
+rejection verification computes the target rows' log-sum-exp itself, only
+for the rows its test reaches (--separate: three launches, and an lse pass
+over every target row before the verification).  Inputs are
 seeded synthetic tensors already resident in HBM when timing starts.
 
 Prints ONE JSON line (rank 0, N = 1):
@@ -56,7 +59,8 @@ def parse_args(argv=None):
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--separate", action="store_true",
                     help="pair scores, walk and greedy verification as three launches "
-                         "(default: one fused launch)")
+                         "(default: one fused launch); sampled: the lse pass over every "
+                         "target row, then the verification (default: one lazy call)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replays of the captured step")
     return ap.parse_args(argv)
@@ -196,9 +200,10 @@ def main(argv=None):
         target = torch.from_numpy(WL.make_targets(w, cand, buf.path_tok.cpu().numpy())).cuda()
 
     fused = not sampled and not a.separate
+    two_pass = sampled and a.separate      # lse of every target row, then the verification
     order = (["conv", "gemm", "topk"] + (["gate"] if w.gate else []) +
              (["pair_select_verify"] if fused else
-              ["pair", "select"] + (["lse"] if sampled else []) + ["verify"]))
+              ["pair", "select"] + (["lse"] if two_pass else []) + ["verify"]))
     ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)] for k in order}
     ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
 
@@ -242,13 +247,20 @@ def main(argv=None):
             ev["select"][i].record()
         if sampled:
             bd.path_sample(buf.S0, buf.S, ti, u_path, w.temperature, buf.path_slot, buf.path_tok, buf.q)
-            if i is not None:
-                ev["lse"][i].record()
-            bd.target_lse(z_target, w.temperature, buf.lse)
-            if i is not None:
-                ev["verify"][i].record()
-            bd.verify_rejection(buf.path_slot, buf.path_tok, buf.q, ti, z_target, buf.lse, w.temperature,
-                                u_acc, u_res, buf.accept_len, buf.next_tok)
+            if two_pass:
+                if i is not None:
+                    ev["lse"][i].record()
+                bd.target_lse(z_target, w.temperature, buf.lse)
+                if i is not None:
+                    ev["verify"][i].record()
+                bd.verify_rejection(buf.path_slot, buf.path_tok, buf.q, ti, z_target, buf.lse,
+                                    w.temperature, u_acc, u_res, buf.accept_len, buf.next_tok)
+            else:
+                # each target row's log-sum-exp only where the accept test reaches it
+                if i is not None:
+                    ev["verify"][i].record()
+                bd.verify_rejection_lazy(buf.path_slot, buf.path_tok, buf.q, ti, z_target,
+                                         w.temperature, u_acc, u_res, buf.accept_len, buf.next_tok)
         else:
             bd.path_select(buf.S0, buf.S, ti, buf.path_slot, buf.path_tok, buf.path_score, mode=w.walk)
             if i is not None:
@@ -339,7 +351,7 @@ def main(argv=None):
     # (the top-16 reads only the tiles its maxima allow, ~1/37 of the logits
     # at V = 151936, so no HBM rate is quoted for it)
     hbm = {"conv": round(conv_bytes / (stage_ms["conv"] * 1e-3) / 1e9, 1)}
-    if sampled:
+    if two_pass:
         hbm["lse"] = round(B * (L + 1) * V * 4 / (stage_ms["lse"] * 1e-3) / 1e9, 1)
     out = {
         "metric": "draft-select-verify blocks/s at B=64,L=8,V=151936; % MFMA / HBM roofline",
@@ -358,7 +370,8 @@ def main(argv=None):
                    "convs": w.n_convs, "conv_groups": w.groups if w.dynamic else 0, "topk": 16,
                    "gate": w.gate, "walk": w.walk, "temperature": w.temperature,
                    "launch": "hip-graph" if graph is not None else "eager",
-                   "pair_walk_verify": "fused" if fused else "separate"},
+                   "pair_walk_verify": "fused" if fused else "separate",
+                   "rejection": ("two-pass" if two_pass else "lazy") if sampled else None},
         "tokens_per_s": round(M / (ms_step * 1e-3), 1),
         "accepted_tokens_per_s": round(float(acc.sum()) / (ms_step * 1e-3), 1),
         "mean_accept_len": round(float(acc.mean()), 3),

@@ -33,7 +33,7 @@ __all__ = [
     "DFlash2Error", "lib", "library_path", "twotap_conv", "twotap_conv_mm", "lmhead_logits",
     "lmhead_logits_tilemax", "topk16", "topk16_tilemax",
     "topk16_workspace", "logits_topk", "logits_topk_workspace", "context_gate", "pair_score",
-    "path_select", "pair_select_verify", "path_sample", "target_lse", "verify_rejection", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
+    "path_select", "pair_select_verify", "path_sample", "target_lse", "verify_rejection", "verify_rejection_lazy", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
 ]
 
 TOPK = 16
@@ -70,6 +70,8 @@ _SIGS = {
     "dflash2_target_lse": ([_P, _I, _I, ctypes.c_float, _P, _P], _I),
     "dflash2_verify_rejection": ([_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _I,
                                   _P, _P, _P], _I),
+    "dflash2_verify_rejection_lazy": ([_P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _I,
+                                       _P, _P, _P], _I),
 }
 
 
@@ -501,6 +503,32 @@ def verify_rejection(path_slot: torch.Tensor, path_tok: torch.Tensor, q: torch.T
     return accept_len, next_tok
 
 
+def verify_rejection_lazy(path_slot: torch.Tensor, path_tok: torch.Tensor, q: torch.Tensor,
+                          top_idx: torch.Tensor, z: torch.Tensor, temperature: float,
+                          u_acc: torch.Tensor, u_res: torch.Tensor, accept_len=None,
+                          next_tok=None):
+    """verify_rejection that computes each row's log-sum-exp itself, only for
+    the rows the accept test reaches: (accept_len [B], next_tok [B])."""
+    B, L = path_tok.shape
+    V = z.shape[-1]
+    _shape(path_slot, (B, L), "path_slot", torch.int32)
+    _shape(q, (B, L, TOPK), "q", torch.float32)
+    _shape(top_idx, (B, L, TOPK), "top_idx", torch.int32)
+    _shape(z, (B, L + 1, V), "z", torch.float32)
+    _shape(u_acc, (B, L), "u_acc", torch.float32)
+    _shape(u_res, (B,), "u_res", torch.float32)
+    dev = path_tok.device
+    if accept_len is None:
+        accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if next_tok is None:
+        next_tok = torch.empty((B,), dtype=torch.int32, device=dev)
+    _dev(path_slot, path_tok, q, top_idx, z, u_acc, u_res, accept_len, next_tok)
+    _check("dflash2_verify_rejection_lazy", lib().dflash2_verify_rejection_lazy(
+        _ptr(path_slot), _ptr(path_tok), _ptr(q), _ptr(top_idx), _ptr(z), float(temperature),
+        _ptr(u_acc), _ptr(u_res), B, L, V, _ptr(accept_len), _ptr(next_tok), _stream(dev)))
+    return accept_len, next_tok
+
+
 # ---------------------------------------------------------------- whole step
 class StepBuffers:
     """Preallocated device buffers for one step shape (B, L, H, V) so repeated
@@ -546,7 +574,8 @@ def run_step(buf: StepBuffers, x: torch.Tensor, convs, W: torch.Tensor, U: torch
     walk (`walk`: "viterbi", "greedy", or "sample" at `temperature` with the
     uniforms `u_path`) and verification: greedy against `target` argmax ids,
     or, for a sampled walk given target logits `z_target` [B, L+1, V], the
-    lossless rejection rule with uniforms `u_acc`, `u_res`.  A walk that is
+    lossless rejection rule with uniforms `u_acc`, `u_res` (each target row's
+    log-sum-exp computed only where the accept test reaches it).  A walk that is
     not sampled, with targets given, runs scores, walk and verification in
     one launch (pair_select_verify).  Every call is enqueued on the current
     stream; nothing is synchronised."""
@@ -580,9 +609,8 @@ def run_step(buf: StepBuffers, x: torch.Tensor, convs, W: torch.Tensor, U: torch
             raise ValueError("a sampled walk needs StepBuffers(sample=True) and u_path")
         path_sample(buf.S0, buf.S, ti, u_path, temperature, buf.path_slot, buf.path_tok, buf.q)
         if z_target is not None:
-            target_lse(z_target, temperature, buf.lse)
-            verify_rejection(buf.path_slot, buf.path_tok, buf.q, ti, z_target, buf.lse,
-                             temperature, u_acc, u_res, buf.accept_len, buf.next_tok)
+            verify_rejection_lazy(buf.path_slot, buf.path_tok, buf.q, ti, z_target, temperature,
+                                  u_acc, u_res, buf.accept_len, buf.next_tok)
         return buf
     path_select(buf.S0, buf.S, ti, buf.path_slot, buf.path_tok, buf.path_score, mode=walk)
     if target is not None:

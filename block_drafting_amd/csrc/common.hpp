@@ -115,6 +115,12 @@ hipError_t launch_target_lse(const float* z, int R, int V, float temperature, fl
                              hipStream_t s);
 
 size_t verify_rejection_lds(int V);
+size_t verify_rejection_lazy_lds(int V);
+hipError_t launch_verify_rejection_lazy(const int32_t* path_slot, const int32_t* path_tok,
+                                        const float* q, const int32_t* top_idx, const float* z,
+                                        float temperature, const float* u_acc, const float* u_res,
+                                        int B, int L, int V, int32_t* accept_len,
+                                        int32_t* next_tok, hipStream_t s);
 hipError_t launch_verify_rejection(const int32_t* path_slot, const int32_t* path_tok,
                                    const float* q, const int32_t* top_idx, const float* z,
                                    const float* lse, float temperature, const float* u_acc,

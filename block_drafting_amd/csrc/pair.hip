@@ -186,7 +186,7 @@ __global__ __launch_bounds__(64) void pair_score_kernel(const float* __restrict_
 // (the max-plus walk keeps its back-pointer rows in score blocks it has
 // already walked) and compares the walked tokens with the targets.  Every
 // part runs the separate kernels' arithmetic, so the results are the same
-// bit for bit.  LDS: (L-1) x 1 KiB of scores plus 80 bytes.  Up to 16 waves
+// bit for bit.  LDS: (L-1) x 1 KiB of scores plus 128 bytes.  Up to 16 waves
 // per block; 8 where r > 128, whose score registers would not fit 16.
 template <int RC>
 constexpr int pwv_max_waves() { return RC >= 32 ? 8 : 16; }

@@ -168,6 +168,108 @@ constexpr int kTile = 256;      // tokens per tile: 64 lanes x 4
 constexpr int kTileBatch = 8;   // tiles a wave has in flight
 constexpr int kVerWaves = 16;   // 128 KB of the row in flight per workgroup
 
+// Steps 3-4 of the draw, run by one wave: the candidates' residual
+// corrections -min(p, q) into their tiles (in slot order), the inclusive
+// prefix of the tile sums in token order, 64 at a time, the first tile whose
+// prefix passes u * total, then the first token inside it whose running sum
+// passes.  tsum [ntiles] holds each 256-token tile's mass of p; zr is the
+// drawn row, p(v) = 2^(zr[v] * s2 - l2).  Writes accept_len = n + 1 and the
+// token.
+__device__ __forceinline__ void draw_token(float* tsum, int ntiles, const float* __restrict__ zr, int V, float s2,
+                           float l2, bool resid, const int32_t* cand_id, const float* cand_q,
+                           float u, int lane, int32_t* accept_len, int32_t* next_tok, int n) {
+  const bool vec = (V & 3) == 0;
+  auto load4 = [&](int v0, float (&o)[4]) {
+    if (vec && v0 + 4 <= V) {
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(zr + v0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = x[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = v0 + i < V ? zr[v0 + i] : -__builtin_inff();
+    }
+  };
+  if (resid) {
+    // lanes 0..15 load their candidate's logit together; lane 0 then
+    // applies the corrections in slot order from registers (one memory
+    // round trip instead of sixteen dependent ones)
+    float corr = 0.f;
+    int ct = -1;
+    if (lane < kTopK) {
+      const int v = cand_id[lane];
+      if (v >= 0 && v < V) {
+        const float p = exp2f(zr[v] * s2 - l2);
+        corr = fminf(p, cand_q[lane]);
+        ct = v / kTile;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kTopK; ++c) {
+      const int t = __builtin_amdgcn_readlane(ct, c);
+      const float cv = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(corr), c));
+      if (lane == 0 && t >= 0) tsum[t] -= cv;
+    }
+  }
+  float carry = 0.f;
+  for (int c0 = 0; c0 < ntiles; c0 += 64) {
+    const int i = c0 + lane;
+    float c = i < ntiles ? fmaxf(tsum[i], 0.f) : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float nb = __shfl_up(c, o, 64);
+      if (lane >= o) c += nb;
+    }
+    if (i < ntiles) tsum[i] = carry + c;
+    carry += __shfl(c, 63, 64);
+  }
+  const float target = u * carry;
+  int k = 0x7fffffff;
+  for (int c0 = 0; c0 < ntiles && k == 0x7fffffff; c0 += 64) {
+    const int i = c0 + lane;
+    const uint64_t pass = __ballot(i < ntiles && tsum[i] > target);
+    if (pass) k = c0 + (int)__builtin_ctzll(pass);
+  }
+  if (k == 0x7fffffff) k = ntiles - 1;  // rounding: the last tile
+  // 4. inside tile k: the first token whose running sum passes the target
+  const float base = k > 0 ? tsum[k - 1] : 0.f;
+  const int v0 = k * kTile + lane * 4;
+  float zv[4], r[4];
+  load4(v0, zv);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float p = v0 + i < V ? exp2f(zv[i] * s2 - l2) : 0.f;
+#pragma unroll
+    for (int c = 0; c < kTopK; ++c)
+      if (cand_id[c] == v0 + i) p = fmaxf(p - cand_q[c], 0.f);
+    r[i] = p;
+  }
+  const float mine = r[0] + r[1] + r[2] + r[3];
+  float c = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float nb = __shfl_up(c, o, 64);
+    if (lane >= o) c += nb;
+  }
+  float run = base + (c - mine);
+  int hit = 0x7fffffff;
+  int lastv = -1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    run += r[i];
+    if (hit == 0x7fffffff && r[i] > 0.f && run > target) hit = v0 + i;
+    if (r[i] > 0.f) lastv = v0 + i;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    hit = min(hit, __shfl_xor(hit, o, 64));
+    lastv = max(lastv, __shfl_xor(lastv, o, 64));
+  }
+  if (lane == 0) {
+    *accept_len = n + 1;
+    *next_tok = hit != 0x7fffffff ? hit : lastv;  // rounding overshoot: last token with mass
+  }
+}
+
 __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_kernel(
     const int32_t* __restrict__ path_slot, const int32_t* __restrict__ path_tok,
     const float* __restrict__ q, const int32_t* __restrict__ top_idx,
@@ -250,90 +352,138 @@ __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_kernel(
     }
   }
   __syncthreads();
-  // 3. wave 0: the candidates' residual corrections -min(p, q) into their
-  //    tiles (in slot order), the inclusive prefix of the tile sums in token
-  //    order, 64 at a time, then the first tile whose prefix passes u * total
-  if (wave == 0) {
-    if (resid) {
-      // lanes 0..15 load their candidate's logit together; lane 0 then
-      // applies the corrections in slot order from registers (one memory
-      // round trip instead of sixteen dependent ones)
-      float corr = 0.f;
-      int ct = -1;
-      if (lane < kTopK) {
-        const int v = cand_id[lane];
-        if (v >= 0 && v < V) {
-          const float p = exp2f(zr[v] * s2 - l2);
-          corr = fminf(p, cand_q[lane]);
-          ct = v / kTile;
+  // 3-4. wave 0 draws the verifier's token from the tile sums
+  if (wave == 0)
+    draw_token(tsum, ntiles, zr, V, s2, l2, resid, cand_id, cand_q, u_res[b], lane,
+               accept_len + b, next_tok + b, n);
+}
+
+
+// Rejection verification that computes the normaliser of a target row only
+// when the accept test reaches it: row t is read once, as 256-token tiles
+// whose (reference maximum, sum of 2^(z * s2 - reference)) stay in LDS; the
+// tiles give the row's log-sum-exp for the test and, at the row where the
+// walk stops, the tile masses of the draw, so the stopping row is not read
+// again.  A block that stops at position n reads n + 1 rows instead of all
+// L + 1.  The accept rule and the draw are those of verify_rejection_kernel.
+__global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_lazy_kernel(
+    const int32_t* __restrict__ path_slot, const int32_t* __restrict__ path_tok,
+    const float* __restrict__ q, const int32_t* __restrict__ top_idx,
+    const float* __restrict__ z, float s2, const float* __restrict__ u_acc,
+    const float* __restrict__ u_res, int L, int V, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ next_tok) {
+  extern __shared__ float tiles[];  // [ntiles] reference maxima, then [ntiles] sums
+  __shared__ int32_t s_x[kMaxWalk];
+  __shared__ float s_thr[kMaxWalk];
+  __shared__ float s_wm[kVerWaves], s_ws[kVerWaves];
+  __shared__ float s_l2;
+  __shared__ int s_stop;
+  __shared__ int32_t cand_id[kTopK];
+  __shared__ float cand_q[kTopK];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const size_t brow = (size_t)b * L;
+  const size_t zrow = (size_t)b * (L + 1);
+  const int ntiles = (V + kTile - 1) / kTile;
+  float* tref = tiles;
+  float* tsum = tiles + ntiles;
+  constexpr float kNeg = -__builtin_inff();
+  // the accept tests' inputs: token (-1: fails), threshold u * q(slot)
+  if (tid < L) {
+    const size_t bt = brow + tid;
+    const int x = path_tok[bt];
+    const int sl = path_slot[bt];
+    const bool ok = x >= 0 && x < V && sl >= 0 && sl < kTopK;
+    s_x[tid] = ok ? x : -1;
+    s_thr[tid] = ok ? u_acc[bt] * q[bt * kTopK + sl] : 0.f;
+  }
+  __syncthreads();
+  const bool vec = (V & 3) == 0;
+  int n = L;
+  for (int t = 0; t <= L; ++t) {
+    const float* zr = z + (zrow + t) * V;
+    const int x = t < L ? s_x[t] : -1;
+    float zx = 0.f;
+    if (tid == 0 && x >= 0) zx = zr[x];  // in flight during the pass
+    // wave w takes tiles w, w + kVerWaves, ..., kTileBatch of them at a time;
+    // each batch shares one reference maximum
+    float Mw = kNeg, Sw = 0.f;
+    for (int t0 = wave; t0 < ntiles; t0 += kVerWaves * kTileBatch) {
+      float zv[kTileBatch][4];
+#pragma unroll
+      for (int k = 0; k < kTileBatch; ++k) {
+        const int v0 = (t0 + kVerWaves * k) * kTile + lane * 4;
+        if (vec && v0 + 4 <= V) {
+          const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(zr + v0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) zv[k][i] = xv[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) zv[k][i] = v0 + i < V ? zr[v0 + i] : kNeg;
         }
       }
+      float bm = kNeg;
 #pragma unroll
-      for (int c = 0; c < kTopK; ++c) {
-        const int t = __builtin_amdgcn_readlane(ct, c);
-        const float cv = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(corr), c));
-        if (lane == 0 && t >= 0) tsum[t] -= cv;
+      for (int k = 0; k < kTileBatch; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          zv[k][i] *= s2;
+          bm = fmaxf(bm, zv[k][i]);
+        }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o, 64));
+      float bs = 0.f;
+#pragma unroll
+      for (int k = 0; k < kTileBatch; ++k) {
+        float acc = 0.f;
+        if (bm != kNeg) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc += exp2f(zv[k][i] - bm);  // -inf -> 0
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+        const int tl = t0 + kVerWaves * k;
+        if (lane == 0 && tl < ntiles) {
+          tref[tl] = bm;
+          tsum[tl] = acc;
+        }
+        bs += acc;
       }
-    }
-    float carry = 0.f;
-    for (int c0 = 0; c0 < ntiles; c0 += 64) {
-      const int i = c0 + lane;
-      float c = i < ntiles ? fmaxf(tsum[i], 0.f) : 0.f;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float nb = __shfl_up(c, o, 64);
-        if (lane >= o) c += nb;
-      }
-      if (i < ntiles) tsum[i] = carry + c;
-      carry += __shfl(c, 63, 64);
-    }
-    const float target = u_res[b] * carry;
-    int k = 0x7fffffff;
-    for (int c0 = 0; c0 < ntiles && k == 0x7fffffff; c0 += 64) {
-      const int i = c0 + lane;
-      const uint64_t pass = __ballot(i < ntiles && tsum[i] > target);
-      if (pass) k = c0 + (int)__builtin_ctzll(pass);
-    }
-    if (k == 0x7fffffff) k = ntiles - 1;  // rounding: the last tile
-    // 4. inside tile k: the first token whose running sum passes the target
-    const float base = k > 0 ? tsum[k - 1] : 0.f;
-    const int v0 = k * kTile + lane * 4;
-    float zv[4], r[4];
-    load4(v0, zv);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float p = v0 + i < V ? exp2f(zv[i] * s2 - l2) : 0.f;
-#pragma unroll
-      for (int c = 0; c < kTopK; ++c)
-        if (cand_id[c] == v0 + i) p = fmaxf(p - cand_q[c], 0.f);
-      r[i] = p;
-    }
-    const float mine = r[0] + r[1] + r[2] + r[3];
-    float c = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float nb = __shfl_up(c, o, 64);
-      if (lane >= o) c += nb;
-    }
-    float run = base + (c - mine);
-    int hit = 0x7fffffff;
-    int lastv = -1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      run += r[i];
-      if (hit == 0x7fffffff && r[i] > 0.f && run > target) hit = v0 + i;
-      if (r[i] > 0.f) lastv = v0 + i;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      hit = min(hit, __shfl_xor(hit, o, 64));
-      lastv = max(lastv, __shfl_xor(lastv, o, 64));
+      lse_merge(Mw, Sw, bm, bs);
     }
     if (lane == 0) {
-      accept_len[b] = n + 1;
-      next_tok[b] = hit != 0x7fffffff ? hit : lastv;  // rounding overshoot: last token with mass
+      s_wm[wave] = Mw;
+      s_ws[wave] = Sw;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float mm = s_wm[0], ss = s_ws[0];
+      for (int w = 1; w < kVerWaves; ++w) lse_merge(mm, ss, s_wm[w], s_ws[w]);
+      const float l2 = mm + log2f(ss);
+      s_l2 = l2;
+      s_stop = t == L || !(x >= 0 && s_thr[t] < exp2f(zx * s2 - l2));
+    }
+    __syncthreads();
+    if (s_stop) {
+      n = t;
+      break;
     }
   }
+  const float l2 = s_l2;
+  const bool resid = n < L;  // draw from max(0, p - q) at the rejected position, else from p
+  if (tid < kTopK) {
+    cand_id[tid] = resid ? top_idx[(brow + n) * kTopK + tid] : -1;
+    cand_q[tid] = resid ? q[(brow + n) * kTopK + tid] : 0.f;
+  }
+  // tile masses of p: sum * 2^(reference - l2)
+  for (int i = tid; i < ntiles; i += 64 * kVerWaves)
+    tsum[i] = tref[i] == kNeg ? 0.f : tsum[i] * exp2f(tref[i] - l2);
+  __syncthreads();
+  if (wave == 0)
+    draw_token(tsum, ntiles, z + (zrow + n) * V, V, s2, l2, resid, cand_id, cand_q, u_res[b],
+               lane, accept_len + b, next_tok + b, n);
 }
 
 }  // namespace
@@ -356,7 +506,21 @@ hipError_t launch_target_lse(const float* z, int R, int V, float temperature, fl
   return hipGetLastError();
 }
 
+hipError_t launch_verify_rejection_lazy(const int32_t* path_slot, const int32_t* path_tok,
+                                        const float* q, const int32_t* top_idx, const float* z,
+                                        float temperature, const float* u_acc, const float* u_res,
+                                        int B, int L, int V, int32_t* accept_len,
+                                        int32_t* next_tok, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  hipLaunchKernelGGL(verify_rejection_lazy_kernel, dim3((unsigned)B), dim3(64 * kVerWaves),
+                     verify_rejection_lazy_lds(V), s, path_slot, path_tok, q, top_idx, z,
+                     kLog2e / temperature, u_acc, u_res, L, V, accept_len, next_tok);
+  return hipGetLastError();
+}
+
 size_t verify_rejection_lds(int V) { return (size_t)((V + kTile - 1) / kTile) * sizeof(float); }
+
+size_t verify_rejection_lazy_lds(int V) { return 2 * verify_rejection_lds(V); }
 
 hipError_t launch_verify_rejection(const int32_t* path_slot, const int32_t* path_tok,
                                    const float* q, const int32_t* top_idx, const float* z,

@@ -16,6 +16,7 @@
  *   steps 3-5 in one launch          dflash2_pair_select_verify
  *   sampling at T > 0, lossless      dflash2_path_sample, dflash2_target_lse,
  *   rejection verification           dflash2_verify_rejection
+ *                                    (dflash2_verify_rejection_lazy: no lse pass)
  *
  * Sources are cited by page title and section:
  *   [POST]   "DFlash 2: Keep Drafting Parallel" (Inco AI).
@@ -306,6 +307,25 @@ int dflash2_verify_rejection(const int32_t* path_slot, const int32_t* path_tok,
                              const float* lse, float temperature, const float* u_acc,
                              const float* u_res, int B, int L, int V,
                              int32_t* accept_len, int32_t* next_tok, void* stream);
+
+/*
+ * dflash2_verify_rejection without the lse pass: the same rule, with each
+ * row's log-sum-exp computed inside the call and only for the rows the test
+ * reaches.  Row t is read once, in 256-token tiles whose maxima and sums stay
+ * on chip; they give lse for the test at t and, at the row where the test
+ * stops, the tile masses of the draw.  A block that stops at position n
+ * reads n + 1 rows of z, where dflash2_target_lse and
+ * dflash2_verify_rejection together read L + 2.  The result follows the same
+ * rule as dflash2_target_lse then dflash2_verify_rejection; rounding of the
+ * sums differs, so a decision or a draw within a few fp32 ulps of the mass
+ * of a boundary can differ.  Arguments as for dflash2_verify_rejection
+ * without lse; V <= 2097152 (larger: DFLASH2_EUNSUPPORTED).  fp32 arithmetic.
+ */
+int dflash2_verify_rejection_lazy(const int32_t* path_slot, const int32_t* path_tok,
+                                  const float* q, const int32_t* top_idx, const float* z,
+                                  float temperature, const float* u_acc, const float* u_res,
+                                  int B, int L, int V, int32_t* accept_len, int32_t* next_tok,
+                                  void* stream);
 
 /*
  * Greedy verification.  [POST] "The right token is already in the candidates",

@@ -209,6 +209,34 @@ def test_fused_pair_walk_verify_validation():
     assert call(S0=None, S=None, B=0) == 0        # scores may stay on chip
 
 
+def test_lazy_rejection_validation():
+    f = bd.lib().dflash2_verify_rejection_lazy
+    #     slot  tok         q            ti           z   T    ua           ur
+    ok = [P, P + 0x1000, P + 0x2000, P + 0x4000, Q, 1.0, P + 0x6000, P + 0x7000,
+          4, 2, 1000, P + 0x8000, P + 0x9000]
+    #     B  L  V     acc          nxt
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a, None)
+
+    # every call below is rejected (or empty) before anything is launched
+    assert call(8, 0) == 0                        # B = 0
+    assert call(8, -1) == EINVAL
+    assert call(9, 0) == EINVAL                   # L = 0
+    assert call(9, 65) == EINVAL                  # L > 64
+    assert call(10, 15) == EINVAL                 # V < 16
+    assert call(10, 2097152 + 256) == EUNSUP      # tiles exceed 64 KiB of LDS
+    assert call(5, 0.0) == EINVAL                 # T must be > 0
+    assert call(5, float("nan")) == EINVAL
+    for i in (0, 1, 2, 3, 4, 6, 7, 11, 12):
+        assert call(i, None) == EINVAL, i
+    assert call(11, Q + 64) == EINVAL             # accept_len inside z
+    assert call(12, P + 0x8000) == EINVAL         # next_tok aliases accept_len
+    assert call(0, P + 2) == EINVAL               # misaligned
+
+
 def test_gate_and_gated_pair_validation():
     L = bd.lib()
     cg = L.dflash2_context_gate

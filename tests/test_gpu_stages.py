@@ -614,7 +614,50 @@ def test_verify_rejection_parity(B, L, V, T):
     assert ((a >= 1) & (a <= L + 1)).all() and len(np.unique(a)) > 1
 
 
-def test_rejection_sampling_is_lossless_on_gpu():
+@pytest.mark.parametrize("B,L,V,T", [(50, 1, 16, 1.0), (200, 4, 1000, 1.0), (24, 8, 151936, 1.0),
+                                     (31, 3, 4099, 0.5), (40, 64, 300, 1.0), (90, 2, 1001, 2.0)])
+def test_verify_rejection_lazy_parity(B, L, V, T):
+    g = np.random.default_rng(B + L + V + 7)
+    ti, slot, tok, q, z, ua, ur = _spec_case(g, B, L, V, T)
+    if L > 8:
+        # long acceptance runs of every length: block b's drafted tokens are
+        # likely under the target up to a position drawn per block
+        cut = g.integers(0, L + 1, B)
+        for b in range(B):
+            for t in range(cut[b]):
+                z[b, t, tok[b, t]] += np.float32(2 * np.log(V))
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    acc, nxt = bd.verify_rejection_lazy(d(slot), d(tok), d(q), d(ti), d(z), T, d(ua), d(ur))
+    exact = check_rejection(ti, slot, tok, q, z, T, ua, ur, acc.cpu().numpy(), nxt.cpu().numpy())
+    if V <= 10000:
+        assert exact >= 0.9 * B, exact
+    a = acc.cpu().numpy()
+    assert ((a >= 1) & (a <= L + 1)).all() and len(np.unique(a)) > 1
+
+
+def test_verify_rejection_lazy_bad_tokens_and_neg_inf():
+    # a token outside [0, V) or a slot outside [0, 16) fails its test; -inf
+    # logits carry no mass and are never drawn
+    g = np.random.default_rng(3)
+    B, L, V, T = 6, 3, 700, 1.0
+    ti, slot, tok, q, z, ua, ur = _spec_case(g, B, L, V, T)
+    z[:, :, 100:400] = -np.inf
+    tok[0, 0] = V
+    slot[1, 0] = 16
+    tok[2, 1] = -1
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    acc, nxt = bd.verify_rejection_lazy(d(slot), d(tok), d(q), d(ti), d(z), T, d(ua), d(ur))
+    a, nx = acc.cpu().numpy(), nxt.cpu().numpy()
+    assert a[0] == 1 and a[1] == 1 and a[2] <= 2
+    assert ((nx < 100) | (nx >= 400)).all() and ((nx >= 0) & (nx < V)).all()
+    # the two-call verification takes the same decisions here
+    lse = bd.target_lse(d(z), T)
+    acc2, _ = bd.verify_rejection(d(slot), d(tok), d(q), d(ti), d(z), lse, T, d(ua), d(ur))
+    np.testing.assert_array_equal(a, acc2.cpu().numpy())
+
+
+@pytest.mark.parametrize("lazy", [False, True])
+def test_rejection_sampling_is_lossless_on_gpu(lazy):
     # the whole sampled walk + verification on the GPU: emitted tokens follow
     # the target's softmax (chi-square on a 24-token vocabulary)
     from scipy.stats import chisquare
@@ -630,10 +673,12 @@ def test_rejection_sampling_is_lossless_on_gpu():
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
     slot, tok, q = bd.path_sample(d(S0), d(S), d(ti), d(g.random((N, L)).astype(np.float32)), T)
     zd = d(np.broadcast_to(zt, (N, L + 1, V)))
-    lse = bd.target_lse(zd, T)
-    acc, nxt = bd.verify_rejection(slot, tok, q, d(ti), zd, lse, T,
-                                   d(g.random((N, L)).astype(np.float32)),
-                                   d(g.random(N).astype(np.float32)))
+    ua, ur = d(g.random((N, L)).astype(np.float32)), d(g.random(N).astype(np.float32))
+    if lazy:
+        acc, nxt = bd.verify_rejection_lazy(slot, tok, q, d(ti), zd, T, ua, ur)
+    else:
+        lse = bd.target_lse(zd, T)
+        acc, nxt = bd.verify_rejection(slot, tok, q, d(ti), zd, lse, T, ua, ur)
     acc, nxt, tok = acc.cpu().numpy(), nxt.cpu().numpy(), tok.cpu().numpy()
     p = np.exp(zt / T - O.target_lse(zt, T)[:, None])
     first = np.where(acc > 1, tok[:, 0], nxt)

@@ -187,8 +187,15 @@ def test_topk_pair_select_verify_stagewise(case):
                                        to_dev(ua, "f32"), to_dev(ur, "f32"))
         exact = check_rejection(ora["top_idx"], ora["path_slot"], ora["path_tok"], qf, zt,
                                 w.temperature, ua, ur, acc.cpu().numpy(), nxt.cpu().numpy())
+        # the same verification with the log-sum-exp computed inside the call
+        acc2, nxt2 = bd.verify_rejection_lazy(to_dev(ora["path_slot"], "i32"),
+                                              to_dev(ora["path_tok"], "i32"), to_dev(qf, "f32"),
+                                              dti, zd, w.temperature, to_dev(ua, "f32"),
+                                              to_dev(ur, "f32"))
+        exact2 = check_rejection(ora["top_idx"], ora["path_slot"], ora["path_tok"], qf, zt,
+                                 w.temperature, ua, ur, acc2.cpu().numpy(), nxt2.cpu().numpy())
         print(f"sampled walk: {int((k == w.L).sum())}/{Bs} paths decided; rejection: "
-              f"{exact}/{Bs} verifier tokens compared exactly")
+              f"{exact}/{Bs} verifier tokens compared exactly ({exact2} without the lse pass)")
         return
     slot, tok, score = bd.path_select(dS0, dS, dti, mode=w.walk)
     np.testing.assert_array_equal(slot.cpu().numpy(), ora["path_slot"])
@@ -391,6 +398,26 @@ def test_properties_all_blocks(case):
     np.testing.assert_array_equal(acc, n + 1)
     np.testing.assert_array_equal(nxt, tgt[bb, n])
     print(f"mean acceptance {acc.mean():.3f} over {B} blocks")
+
+
+def test_lazy_rejection_all_blocks(case):
+    """Every block of a sampled workload: the verification that computes
+    each row's log-sum-exp itself follows the oracle's rule (same margins as
+    the two-call verification)."""
+    w, buf, dev = case["w"], case["buf"], case["dev"]
+    if w.temperature <= 0:
+        pytest.skip("greedy verification")
+    B, L = w.B, w.L
+    ti = buf.top_idx.view(B, L, 16)
+    ua, ur = case["inp"]["u_acc"], case["inp"]["u_res"]
+    acc, nxt = bd.verify_rejection_lazy(buf.path_slot, buf.path_tok, buf.q, ti, dev["z_target"],
+                                        w.temperature, dev["u_acc"], dev["u_res"])
+    exact = check_rejection(ti.cpu().numpy(), buf.path_slot.cpu().numpy(),
+                            buf.path_tok.cpu().numpy(), buf.q.cpu().numpy(), case["zt"],
+                            w.temperature, ua, ur, acc.cpu().numpy(), nxt.cpu().numpy())
+    a = acc.cpu().numpy()
+    assert ((a >= 1) & (a <= L + 1)).all()
+    print(f"lazy rejection: {exact}/{B} verifier tokens compared exactly")
 
 
 def test_step_is_deterministic(case):
