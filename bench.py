@@ -5,11 +5,12 @@ One step = one pass of the whole hot path over one batch:
   two-tap conv(s) -> LM-head logits -> top-16 -> [context gate] -> pair
   scores -> path walk (max-plus, or greedy with --walk greedy / the gated
   workload) -> greedy verification,
-each stage a call into libdflash2 on the current HIP stream; scores, walk
-and greedy verification run as one fused launch, and a sampled walk's
-rejection verification computes the target rows' log-sum-exp itself, only
-for the rows its test reaches (--separate: three launches, and an lse pass
-over every target row before the verification).  Inputs are
+each stage a call into libdflash2 on the current HIP stream.  Scores, walk
+and greedy verification run as one fused launch; a sampled walk runs scores
+and walk as one launch, then a rejection verification that computes the
+target rows' log-sum-exp itself, only for the rows its test reaches
+(--separate: scores, walk and verification as separate launches, and for a
+sampled walk an lse pass over every target row before the verification).  Inputs are
 seeded synthetic tensors already resident in HBM when timing starts.
 
 Prints ONE JSON line (rank 0, N = 1):
@@ -58,9 +59,9 @@ def parse_args(argv=None):
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--separate", action="store_true",
-                    help="pair scores, walk and greedy verification as three launches "
-                         "(default: one fused launch); sampled: the lse pass over every "
-                         "target row, then the verification (default: one lazy call)")
+                    help="pair scores, walk and verification as separate launches, and for a "
+                         "sampled walk the lse pass over every target row before the "
+                         "verification (default: fused scores + walk, lazy verification)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replays of the captured step")
     return ap.parse_args(argv)
@@ -199,11 +200,13 @@ def main(argv=None):
     else:
         target = torch.from_numpy(WL.make_targets(w, cand, buf.path_tok.cpu().numpy())).cuda()
 
-    fused = not sampled and not a.separate
+    fused = not a.separate                 # scores + walk (+ greedy verification) in one launch
     two_pass = sampled and a.separate      # lse of every target row, then the verification
-    order = (["conv", "gemm", "topk"] + (["gate"] if w.gate else []) +
-             (["pair_select_verify"] if fused else
-              ["pair", "select"] + (["lse"] if two_pass else []) + ["verify"]))
+    if fused:
+        tail = ["pair_sample", "verify"] if sampled else ["pair_select_verify"]
+    else:
+        tail = ["pair", "select"] + (["lse"] if two_pass else []) + ["verify"]
+    order = ["conv", "gemm", "topk"] + (["gate"] if w.gate else []) + tail
     ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)] for k in order}
     ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
 
@@ -230,6 +233,19 @@ def main(argv=None):
                 ev["gate"][i].record()
             gate = bd.context_gate(cur.view(M, H), Wg, buf.gate)
         ti = buf.top_idx.view(B, L, 16)
+        if fused and sampled:
+            # scores and the sampling walk in one launch, then the lazy verification
+            if i is not None:
+                ev["pair_sample"][i].record()
+            bd.pair_sample(buf.top_val.view(B, L, 16), ti, anchor, U, Vf, u_path, w.temperature,
+                           gate, None, None, buf.path_slot, buf.path_tok, buf.q)
+            if i is not None:
+                ev["verify"][i].record()
+            bd.verify_rejection_lazy(buf.path_slot, buf.path_tok, buf.q, ti, z_target,
+                                     w.temperature, u_acc, u_res, buf.accept_len, buf.next_tok)
+            if i is not None:
+                ev_end[i].record()
+            return
         if fused:
             # scores, walk and verification in one launch; the scores stay on chip
             if i is not None:
@@ -247,20 +263,13 @@ def main(argv=None):
             ev["select"][i].record()
         if sampled:
             bd.path_sample(buf.S0, buf.S, ti, u_path, w.temperature, buf.path_slot, buf.path_tok, buf.q)
-            if two_pass:
-                if i is not None:
-                    ev["lse"][i].record()
-                bd.target_lse(z_target, w.temperature, buf.lse)
-                if i is not None:
-                    ev["verify"][i].record()
-                bd.verify_rejection(buf.path_slot, buf.path_tok, buf.q, ti, z_target, buf.lse,
-                                    w.temperature, u_acc, u_res, buf.accept_len, buf.next_tok)
-            else:
-                # each target row's log-sum-exp only where the accept test reaches it
-                if i is not None:
-                    ev["verify"][i].record()
-                bd.verify_rejection_lazy(buf.path_slot, buf.path_tok, buf.q, ti, z_target,
-                                         w.temperature, u_acc, u_res, buf.accept_len, buf.next_tok)
+            if i is not None:
+                ev["lse"][i].record()
+            bd.target_lse(z_target, w.temperature, buf.lse)
+            if i is not None:
+                ev["verify"][i].record()
+            bd.verify_rejection(buf.path_slot, buf.path_tok, buf.q, ti, z_target, buf.lse,
+                                w.temperature, u_acc, u_res, buf.accept_len, buf.next_tok)
         else:
             bd.path_select(buf.S0, buf.S, ti, buf.path_slot, buf.path_tok, buf.path_score, mode=w.walk)
             if i is not None:
@@ -370,7 +379,7 @@ def main(argv=None):
                    "convs": w.n_convs, "conv_groups": w.groups if w.dynamic else 0, "topk": 16,
                    "gate": w.gate, "walk": w.walk, "temperature": w.temperature,
                    "launch": "hip-graph" if graph is not None else "eager",
-                   "pair_walk_verify": "fused" if fused else "separate",
+                   "pair_walk": "fused" if fused else "separate",
                    "rejection": ("two-pass" if two_pass else "lazy") if sampled else None},
         "tokens_per_s": round(M / (ms_step * 1e-3), 1),
         "accepted_tokens_per_s": round(float(acc.sum()) / (ms_step * 1e-3), 1),

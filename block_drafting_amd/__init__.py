@@ -33,7 +33,7 @@ __all__ = [
     "DFlash2Error", "lib", "library_path", "twotap_conv", "twotap_conv_mm", "lmhead_logits",
     "lmhead_logits_tilemax", "topk16", "topk16_tilemax",
     "topk16_workspace", "logits_topk", "logits_topk_workspace", "context_gate", "pair_score",
-    "path_select", "pair_select_verify", "path_sample", "target_lse", "verify_rejection", "verify_rejection_lazy", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
+    "path_select", "pair_select_verify", "pair_sample", "path_sample", "target_lse", "verify_rejection", "verify_rejection_lazy", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
 ]
 
 TOPK = 16
@@ -64,6 +64,8 @@ _SIGS = {
     "dflash2_path_select": ([_P, _P, _P, _I, _I, _P, _P, _P, _P], _I),
     "dflash2_path_select_mode": ([_P, _P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
     "dflash2_verify_greedy": ([_P, _P, _I, _I, _P, _P, _P], _I),
+    "dflash2_pair_sample": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I, _I, _I, _I, _I, _P,
+                             _P, _P, _P, _P, _P], _I),
     "dflash2_pair_select_verify": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P,
                                     _P, _P, _P, _P, _P, _P], _I),
     "dflash2_path_sample": ([_P, _P, _P, _P, ctypes.c_float, _I, _I, _P, _P, _P, _P], _I),
@@ -441,6 +443,42 @@ def pair_select_verify(top_val: torch.Tensor, top_idx: torch.Tensor,
     return path_slot, path_tok, path_score, accept_len, next_tok
 
 
+def pair_sample(top_val: torch.Tensor, top_idx: torch.Tensor, anchor_tok: Optional[torch.Tensor],
+                U: torch.Tensor, Vf: torch.Tensor, u: torch.Tensor, temperature: float,
+                gate: Optional[torch.Tensor] = None, S0: Optional[torch.Tensor] = None,
+                S: Optional[torch.Tensor] = None, path_slot=None, path_tok=None, q=None):
+    """pair_score and path_sample in one launch.  The scores are written to
+    S0 / S only when those are given.  Returns (path_slot, path_tok, q)."""
+    B, L, K = top_val.shape
+    V, r = U.shape
+    _shape(top_idx, (B, L, K), "top_idx", torch.int32)
+    _shape(Vf, (V, r), "Vf", U.dtype)
+    _shape(u, (B, L), "u", torch.float32)
+    if anchor_tok is not None:
+        _shape(anchor_tok, (B,), "anchor_tok", torch.int32)
+    if gate is not None:
+        if gate.dim() == 2 and gate.shape[0] == B * L:
+            gate = gate.view(B, L, r)
+        _shape(gate, (B, L, r), "gate", torch.float32)
+    if S0 is not None:
+        _shape(S0, (B, TOPK), "S0", torch.float32)
+    if S is not None:
+        _shape(S, (B, L - 1, TOPK, TOPK), "S", torch.float32)
+    dev = top_val.device
+    if path_slot is None:
+        path_slot = torch.empty((B, L), dtype=torch.int32, device=dev)
+    if path_tok is None:
+        path_tok = torch.empty((B, L), dtype=torch.int32, device=dev)
+    if q is None:
+        q = torch.empty((B, L, TOPK), dtype=torch.float32, device=dev)
+    _dev(top_val, top_idx, anchor_tok, U, Vf, u, gate, S0, S, path_slot, path_tok, q)
+    _check("dflash2_pair_sample", lib().dflash2_pair_sample(
+        _ptr(top_val), _ptr(top_idx), _ptr(anchor_tok), _ptr(U), _ptr(Vf), _ptr(gate), _ptr(u),
+        float(temperature), B, L, V, r, _dt(U), _ptr(S0), _ptr(S) if L > 1 else None,
+        _ptr(path_slot), _ptr(path_tok), _ptr(q), _stream(dev)))
+    return path_slot, path_tok, q
+
+
 def path_sample(S0: torch.Tensor, S: Optional[torch.Tensor], top_idx: Optional[torch.Tensor],
                 u: torch.Tensor, temperature: float, path_slot=None, path_tok=None, q=None):
     """Sampling walk at temperature T with uniforms u [B, L].
@@ -577,7 +615,8 @@ def run_step(buf: StepBuffers, x: torch.Tensor, convs, W: torch.Tensor, U: torch
     lossless rejection rule with uniforms `u_acc`, `u_res` (each target row's
     log-sum-exp computed only where the accept test reaches it).  A walk that is
     not sampled, with targets given, runs scores, walk and verification in
-    one launch (pair_select_verify).  Every call is enqueued on the current
+    one launch (pair_select_verify); a sampled walk runs scores and walk in
+    one launch (pair_sample).  Every call is enqueued on the current
     stream; nothing is synchronised."""
     B, L, H, V = buf.B, buf.L, buf.H, buf.V
     cur = x
@@ -603,16 +642,15 @@ def run_step(buf: StepBuffers, x: torch.Tensor, convs, W: torch.Tensor, U: torch
                            buf.path_slot, buf.path_tok, buf.path_score, buf.accept_len,
                            buf.next_tok)
         return buf
-    pair_score(tv, ti, anchor_tok, U, Vf, buf.S0, buf.S, gate=gate)
     if walk == "sample":
         if buf.q is None or u_path is None:
             raise ValueError("a sampled walk needs StepBuffers(sample=True) and u_path")
-        path_sample(buf.S0, buf.S, ti, u_path, temperature, buf.path_slot, buf.path_tok, buf.q)
+        pair_sample(tv, ti, anchor_tok, U, Vf, u_path, temperature, gate, buf.S0, buf.S,
+                    buf.path_slot, buf.path_tok, buf.q)
         if z_target is not None:
             verify_rejection_lazy(buf.path_slot, buf.path_tok, buf.q, ti, z_target, temperature,
                                   u_acc, u_res, buf.accept_len, buf.next_tok)
         return buf
+    pair_score(tv, ti, anchor_tok, U, Vf, buf.S0, buf.S, gate=gate)
     path_select(buf.S0, buf.S, ti, buf.path_slot, buf.path_tok, buf.path_score, mode=walk)
-    if target is not None:
-        verify_greedy(buf.path_tok, target, buf.accept_len, buf.next_tok)
     return buf

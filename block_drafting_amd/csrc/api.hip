@@ -499,3 +499,43 @@ DFLASH2_API int dflash2_pair_select_verify(
       mode == DFLASH2_PATH_GREEDY, S0, L > 1 ? S : nullptr, path_slot, path_tok, path_score,
       accept_len, next_tok, as_stream(stream)));
 }
+
+DFLASH2_API int dflash2_pair_sample(const float* top_val, const int32_t* top_idx,
+                                    const int32_t* anchor_tok, const void* U, const void* Vf,
+                                    const float* gate, const float* u, float temperature, int B,
+                                    int L, int V, int r, int dtype, float* S0, float* S,
+                                    int32_t* path_slot, int32_t* path_tok, float* q,
+                                    void* stream) {
+  if (!valid_dtype(dtype) || B < 0 || L < 1 || L > DFLASH2_MAX_L || V < kTopK || r < 1 ||
+      r > DFLASH2_MAX_RANK || !valid_temperature(temperature))
+    return DFLASH2_EINVAL;
+  if (B == 0) return DFLASH2_OK;
+  if (!top_val || !top_idx || !U || !Vf || !u || !path_slot || !q) return DFLASH2_EINVAL;
+  if ((long long)V * r > (1LL << 40) || (long long)B * L * kTopK > kInt32Max)
+    return DFLASH2_EINVAL;
+  const void* a4[] = {top_val, top_idx, anchor_tok, gate, u, S0, S, path_slot, path_tok, q};
+  for (const void* p : a4)
+    if (p && !aligned4(p)) return DFLASH2_EINVAL;
+  const size_t es = esize(dtype);
+  if (dtype == DFLASH2_BF16 ? ((reinterpret_cast<uintptr_t>(U) | reinterpret_cast<uintptr_t>(Vf)) & 1)
+                            : (!aligned4(U) || !aligned4(Vf)))
+    return DFLASH2_EINVAL;
+  const size_t tb = (size_t)B * L * kTopK * 4;
+  const size_t pb = (size_t)B * L * 4;
+  const void* ins[] = {top_val, top_idx, U, Vf, anchor_tok, gate, u};
+  const size_t insz[] = {tb, tb, (size_t)V * r * es, (size_t)V * r * es, (size_t)B * 4,
+                         (size_t)B * L * r * 4, pb};
+  const void* outs[] = {S0, L > 1 ? S : nullptr, path_slot, path_tok, q};
+  const size_t outsz[] = {(size_t)B * kTopK * 4, (size_t)B * (L - 1) * kTopK * kTopK * 4, pb, pb,
+                          tb};
+  for (int o = 0; o < 5; ++o) {
+    if (!outs[o]) continue;
+    for (int k = 0; k < 7; ++k)
+      if (overlap(outs[o], outsz[o], ins[k], insz[k])) return DFLASH2_EINVAL;
+    for (int k = o + 1; k < 5; ++k)
+      if (outs[k] && overlap(outs[o], outsz[o], outs[k], outsz[k])) return DFLASH2_EINVAL;
+  }
+  return status_of(launch_pair_sample(top_val, top_idx, anchor_tok, U, Vf, gate, u, temperature,
+                                      B, L, V, r, dtype, S0, L > 1 ? S : nullptr, path_slot,
+                                      path_tok, q, as_stream(stream)));
+}

@@ -95,6 +95,12 @@ hipError_t launch_pair_walk_verify(const float* top_val, const int32_t* top_idx,
                                    int r, int dtype, int greedy, float* S0, float* S,
                                    int32_t* path_slot, int32_t* path_tok, float* path_score,
                                    int32_t* accept_len, int32_t* next_tok, hipStream_t s);
+// Pair scores + the sampling walk of each block in one launch; S0 / S may be NULL.
+hipError_t launch_pair_sample(const float* top_val, const int32_t* top_idx,
+                              const int32_t* anchor_tok, const void* U, const void* Vf,
+                              const float* gate, const float* u, float temperature, int B, int L,
+                              int V, int r, int dtype, float* S0, float* S, int32_t* path_slot,
+                              int32_t* path_tok, float* q, hipStream_t s);
 hipError_t launch_pair_score(const float* top_val, const int32_t* top_idx,
                              const int32_t* anchor_tok, const void* U, const void* Vf,
                              const float* gate, int B, int L, int V, int r, int dtype, float* S0,

@@ -178,31 +178,17 @@ __global__ __launch_bounds__(64) void pair_score_kernel(const float* __restrict_
   for (int e = 0; e < 4; ++e) dst[(4 * q + e) * kTopK + i] = tv + res[e];
 }
 
-// Pair scores, path walk and greedy verification of one block in one
-// workgroup: the step's three latency-bound stages in one launch, with the
-// scores kept in LDS between them.  Waves take the positions t = wave,
-// wave + waves, ... and leave each 16 x 16 block in LDS (and, when S0out /
-// Sout are given, in global memory too); wave 0 then walks the scores in LDS
-// (the max-plus walk keeps its back-pointer rows in score blocks it has
-// already walked) and compares the walked tokens with the targets.  Every
-// part runs the separate kernels' arithmetic, so the results are the same
-// bit for bit.  LDS: (L-1) x 1 KiB of scores plus 128 bytes.  Up to 16 waves
-// per block; 8 where r > 128, whose score registers would not fit 16.
-template <int RC>
-constexpr int pwv_max_waves() { return RC >= 32 ? 8 : 16; }
-
-template <typename T, int RC, bool VEC, bool GREEDY>
-__global__ __launch_bounds__(64 * pwv_max_waves<RC>()) void pair_walk_verify_kernel(
-    const float* __restrict__ top_val, const int32_t* __restrict__ top_idx,
-    const int32_t* __restrict__ anchor_tok, const T* __restrict__ U, const T* __restrict__ Vf,
-    const float* __restrict__ gate, const int32_t* __restrict__ target, int L, int V, int r,
-    float* __restrict__ S0out, float* __restrict__ Sout, int32_t* __restrict__ path_slot,
-    int32_t* __restrict__ path_tok, float* __restrict__ path_score,
-    int32_t* __restrict__ accept_len, int32_t* __restrict__ next_tok) {
-  extern __shared__ float sS[];         // (L - 1) x 16 x 16 scores
-  __shared__ float sS0[kTopK];          // S0, then the max-plus walk's running maxima
-  __shared__ uint8_t sslot[kMaxWalk];   // walked slots
-  const int b = blockIdx.x;
+// The scores of block b, one wave per position (t = wave, wave + waves, ...):
+// each 16 x 16 block to LDS (sS [(L-1) x 16 x 16], sS0 [16]) and, when
+// S0out / Sout are given, to global memory too.
+template <typename T, int RC, bool VEC>
+__device__ __forceinline__ void pair_phase(const float* __restrict__ top_val,
+                                           const int32_t* __restrict__ top_idx,
+                                           const int32_t* __restrict__ anchor_tok,
+                                           const T* __restrict__ U, const T* __restrict__ Vf,
+                                           const float* __restrict__ gate, int b, int L, int V,
+                                           int r, float* sS, float* sS0, float* __restrict__ S0out,
+                                           float* __restrict__ Sout) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6;
@@ -230,6 +216,37 @@ __global__ __launch_bounds__(64 * pwv_max_waves<RC>()) void pair_walk_verify_ker
       }
     }
   }
+}
+
+// Pair scores, path walk and greedy verification of one block in one
+// workgroup: the step's three latency-bound stages in one launch, with the
+// scores kept in LDS between them.  Waves take the positions t = wave,
+// wave + waves, ... and leave each 16 x 16 block in LDS (and, when S0out /
+// Sout are given, in global memory too); wave 0 then walks the scores in LDS
+// (the max-plus walk keeps its back-pointer rows in score blocks it has
+// already walked) and compares the walked tokens with the targets.  Every
+// part runs the separate kernels' arithmetic, so the results are the same
+// bit for bit.  LDS: (L-1) x 1 KiB of scores plus 128 bytes.  Up to 16 waves
+// per block; 8 where r > 128, whose score registers would not fit 16.
+template <int RC>
+constexpr int pwv_max_waves() { return RC >= 32 ? 8 : 16; }
+
+template <typename T, int RC, bool VEC, bool GREEDY>
+__global__ __launch_bounds__(64 * pwv_max_waves<RC>()) void pair_walk_verify_kernel(
+    const float* __restrict__ top_val, const int32_t* __restrict__ top_idx,
+    const int32_t* __restrict__ anchor_tok, const T* __restrict__ U, const T* __restrict__ Vf,
+    const float* __restrict__ gate, const int32_t* __restrict__ target, int L, int V, int r,
+    float* __restrict__ S0out, float* __restrict__ Sout, int32_t* __restrict__ path_slot,
+    int32_t* __restrict__ path_tok, float* __restrict__ path_score,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ next_tok) {
+  extern __shared__ float sS[];         // (L - 1) x 16 x 16 scores
+  __shared__ float sS0[kTopK];          // S0, then the max-plus walk's running maxima
+  __shared__ uint8_t sslot[kMaxWalk];   // walked slots
+  const int b = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  pair_phase<T, RC, VEC>(top_val, top_idx, anchor_tok, U, Vf, gate, b, L, V, r, sS, sS0, S0out,
+                         Sout);
   __syncthreads();
   if (wave != 0) return;
   if (GREEDY)
@@ -251,6 +268,27 @@ __global__ __launch_bounds__(64 * pwv_max_waves<RC>()) void pair_walk_verify_ker
     accept_len[b] = n + 1;
     if (next_tok) next_tok[b] = g[n];
   }
+}
+
+// Pair scores and the sampling walk of one block in one workgroup (the
+// sampling twin of pair_walk_verify_kernel; the rejection verification needs
+// the target logits and runs on its own).  Bit for bit the separate calls.
+template <typename T, int RC, bool VEC>
+__global__ __launch_bounds__(64 * pwv_max_waves<RC>()) void pair_sample_kernel(
+    const float* __restrict__ top_val, const int32_t* __restrict__ top_idx,
+    const int32_t* __restrict__ anchor_tok, const T* __restrict__ U, const T* __restrict__ Vf,
+    const float* __restrict__ gate, const float* __restrict__ u, float inv_t, int L, int V, int r,
+    float* __restrict__ S0out, float* __restrict__ Sout, int32_t* __restrict__ path_slot,
+    int32_t* __restrict__ path_tok, float* __restrict__ qout) {
+  extern __shared__ float sS[];  // (L - 1) x 16 x 16 scores
+  __shared__ float sS0[kTopK];
+  const int b = blockIdx.x;
+  pair_phase<T, RC, VEC>(top_val, top_idx, anchor_tok, U, Vf, gate, b, L, V, r, sS, sS0, S0out,
+                         Sout);
+  __syncthreads();
+  if ((threadIdx.x >> 6) != 0) return;
+  sample_walk(sS0[threadIdx.x & 15], sS, top_idx, u + (size_t)b * L, inv_t, b, L, path_slot,
+              path_tok, qout);
 }
 
 template <typename T, int RC>
@@ -379,6 +417,65 @@ hipError_t launch_pair_walk_verify(const float* top_val, const int32_t* top_idx,
                                  gate, target, L, V, r, S0, S, path_slot, path_tok, path_score,
                                  accept_len, next_tok);
   }
+  return hipGetLastError();
+}
+
+namespace {
+template <typename T, int RC>
+void launch_ps_rc(bool vec, dim3 grid, size_t lds, hipStream_t s, const float* top_val,
+                  const int32_t* top_idx, const int32_t* anchor_tok, const void* U, const void* Vf,
+                  const float* gate, const float* u, float inv_t, int L, int V, int r, float* S0,
+                  float* S, int32_t* path_slot, int32_t* path_tok, float* q) {
+  const T* uu = static_cast<const T*>(U);
+  const T* vv = static_cast<const T*>(Vf);
+  const dim3 block((unsigned)(64 * min(L, pwv_max_waves<RC>())));
+  if (vec)
+    hipLaunchKernelGGL((pair_sample_kernel<T, RC, true>), grid, block, lds, s, top_val, top_idx,
+                       anchor_tok, uu, vv, gate, u, inv_t, L, V, r, S0, S, path_slot, path_tok, q);
+  else
+    hipLaunchKernelGGL((pair_sample_kernel<T, RC, false>), grid, block, lds, s, top_val, top_idx,
+                       anchor_tok, uu, vv, gate, u, inv_t, L, V, r, S0, S, path_slot, path_tok, q);
+}
+
+template <typename T>
+void launch_ps_t(bool vec, dim3 grid, size_t lds, hipStream_t s, const float* top_val,
+                 const int32_t* top_idx, const int32_t* anchor_tok, const void* U, const void* Vf,
+                 const float* gate, const float* u, float inv_t, int L, int V, int r, float* S0,
+                 float* S, int32_t* path_slot, int32_t* path_tok, float* q) {
+  const int rc = (r + 3) / 4;
+#define DFLASH2_PS(RC)                                                                          \
+  launch_ps_rc<T, RC>(vec, grid, lds, s, top_val, top_idx, anchor_tok, U, Vf, gate, u, inv_t, L, \
+                      V, r, S0, S, path_slot, path_tok, q)
+  if (rc <= 8)
+    DFLASH2_PS(8);
+  else if (rc <= 16)
+    DFLASH2_PS(16);
+  else if (rc <= 32)
+    DFLASH2_PS(32);
+  else
+    DFLASH2_PS(64);
+#undef DFLASH2_PS
+}
+}  // namespace
+
+hipError_t launch_pair_sample(const float* top_val, const int32_t* top_idx,
+                              const int32_t* anchor_tok, const void* U, const void* Vf,
+                              const float* gate, const float* u, float temperature, int B, int L,
+                              int V, int r, int dtype, float* S0, float* S, int32_t* path_slot,
+                              int32_t* path_tok, float* q, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const dim3 grid((unsigned)B);
+  const size_t lds = (size_t)(L - 1) * kTopK * kTopK * sizeof(float);
+  const float inv_t = 1.0f / temperature;
+  const uintptr_t bases = reinterpret_cast<uintptr_t>(U) | reinterpret_cast<uintptr_t>(Vf) |
+                          reinterpret_cast<uintptr_t>(gate);
+  if (dtype == 1)
+    launch_ps_t<uint16_t>(r % 32 == 0 && (bases & 15) == 0, grid, lds, s, top_val, top_idx,
+                          anchor_tok, U, Vf, gate, u, inv_t, L, V, r, S0, S, path_slot, path_tok,
+                          q);
+  else
+    launch_ps_t<float>(r % 16 == 0 && (bases & 15) == 0, grid, lds, s, top_val, top_idx,
+                       anchor_tok, U, Vf, gate, u, inv_t, L, V, r, S0, S, path_slot, path_tok, q);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@
 //                       256-token tiles wave by wave, moves the 16
 //                       candidates' corrections into their tiles, scans the
 //                       tile sums, then scans inside the chosen tile.
-#include "common.hpp"
+#include "walk.hpp"
 
 namespace dflash2 {
 namespace {
@@ -52,40 +52,8 @@ __global__ __launch_bounds__(64) void path_sample_kernel(
   float s = S0[(size_t)b * kTopK + j];
   const size_t row = (size_t)b * L;
   __syncthreads();
-  const float* sS = reinterpret_cast<const float*>(stage);
-  int p = 0;
-  for (int t = 0; t < L; ++t) {
-    if (t > 0) s = sS[((t - 1) * kTopK + p) * kTopK + j];
-    // softmax over the 16 lanes of each quarter (all four quarters agree)
-    float m = s;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    const float e = expf((s - m) * inv_t);
-    float z = e;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
-    const float qj = e / z;
-    // inclusive prefix sum in slot order
-    float c = qj;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const float n = __shfl_up(c, o, 16);
-      if (j >= o) c += n;
-    }
-    const float ut = u[row + t];
-    // first slot with u < c_j = number of slots with c_j <= u; rounding can
-    // leave u above every c_j: then the last slot with q > 0
-    const uint64_t le = __ballot(c <= ut) & 0xffffull;
-    const uint64_t pos = __ballot(qj > 0.f) & 0xffffull;
-    const int first = __popcll(le);
-    const int last = pos ? 63 - __clzll(pos) : 0;  // no finite score: slot 0 (q is NaN)
-    p = min(first, last);
-    if (lane < kTopK) q[(row + t) * kTopK + j] = qj;
-    if (lane == 0) {
-      path_slot[row + t] = p;
-      if (path_tok) path_tok[row + t] = top_idx[(row + t) * kTopK + p];
-    }
-  }
+  sample_walk(s, reinterpret_cast<const float*>(stage), top_idx, u + row, inv_t, b, L, path_slot,
+              path_tok, q);
 }
 
 // ---------------------------------------------------------------- target log-sum-exp

@@ -144,4 +144,50 @@ __device__ __forceinline__ void greedy_walk(const float* S0b, const float* sS,
   if (lane == 0) path_score[b] = score;
 }
 
+// Sampling walk at temperature T = 1 / inv_t, the sampling twin of the greedy
+// walk: position t's slot is drawn from softmax(row / T) of the successors of
+// the slot drawn before, by inverse CDF in slot order with the uniform u[t].
+// s: this lane's S0 value (candidate j = lane & 15); sS: this block's scores
+// in LDS; u [L]: this block's uniforms; q receives every position's proposal.
+__device__ __forceinline__ void sample_walk(float s, const float* sS, const int32_t* top_idx,
+                                            const float* u, float inv_t, int b, int L,
+                                            int32_t* path_slot, int32_t* path_tok, float* q) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15;
+  const size_t row = (size_t)b * L;
+  int p = 0;
+  for (int t = 0; t < L; ++t) {
+    if (t > 0) s = sS[((t - 1) * kTopK + p) * kTopK + j];
+    // softmax over the 16 lanes of each quarter (all four quarters agree)
+    float m = s;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float e = expf((s - m) * inv_t);
+    float z = e;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
+    const float qj = e / z;
+    // inclusive prefix sum in slot order
+    float c = qj;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const float n = __shfl_up(c, o, 16);
+      if (j >= o) c += n;
+    }
+    const float ut = u[t];
+    // first slot with u < c_j = number of slots with c_j <= u; rounding can
+    // leave u above every c_j: then the last slot with q > 0
+    const uint64_t le = __ballot(c <= ut) & 0xffffull;
+    const uint64_t pos = __ballot(qj > 0.f) & 0xffffull;
+    const int first = __popcll(le);
+    const int last = pos ? 63 - __clzll(pos) : 0;  // no finite score: slot 0 (q is NaN)
+    p = min(first, last);
+    if (lane < kTopK) q[(row + t) * kTopK + j] = qj;
+    if (lane == 0) {
+      path_slot[row + t] = p;
+      if (path_tok) path_tok[row + t] = top_idx[(row + t) * kTopK + p];
+    }
+  }
+}
+
 }  // namespace dflash2

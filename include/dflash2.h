@@ -14,6 +14,7 @@
  *   context-gated pair scores        dflash2_context_gate, dflash2_pair_score_gated
  *   best-successor (greedy) walk     dflash2_path_select_mode(..., DFLASH2_PATH_GREEDY, ...)
  *   steps 3-5 in one launch          dflash2_pair_select_verify
+ *   scores + sampling walk, one launch  dflash2_pair_sample
  *   sampling at T > 0, lossless      dflash2_path_sample, dflash2_target_lse,
  *   rejection verification           dflash2_verify_rejection
  *                                    (dflash2_verify_rejection_lazy: no lse pass)
@@ -359,6 +360,24 @@ int dflash2_pair_select_verify(const float* top_val, const int32_t* top_idx,
                                int r, int dtype, int mode, float* S0, float* S,
                                int32_t* path_slot, int32_t* path_tok, float* path_score,
                                int32_t* accept_len, int32_t* next_tok, void* stream);
+
+/*
+ * The sampling twin of dflash2_pair_select_verify: dflash2_pair_score_gated
+ * (gate != NULL) or dflash2_pair_score (gate == NULL), then
+ * dflash2_path_sample, for each block in one workgroup with the scores kept
+ * on chip.  [POST] "A lightweight path selector" (scores; sampling from the
+ * same scores).  The outputs are bit for bit those of the two calls.
+ * Arguments, layouts, limits and errors are theirs, with these differences:
+ * S0 and S are optional outputs (NULL: the scores stay on chip); path_tok
+ * may be NULL; u [B, L], path_slot [B, L] and q [B, L, 16] are required.
+ * Every pointer is 4-byte aligned (U and Vf: 2-byte for bf16), and no output
+ * may overlap an input or another output.
+ */
+int dflash2_pair_sample(const float* top_val, const int32_t* top_idx,
+                        const int32_t* anchor_tok, const void* U, const void* Vf,
+                        const float* gate, const float* u, float temperature, int B, int L,
+                        int V, int r, int dtype, float* S0, float* S, int32_t* path_slot,
+                        int32_t* path_tok, float* q, void* stream);
 
 #ifdef __cplusplus
 }

@@ -209,6 +209,34 @@ def test_fused_pair_walk_verify_validation():
     assert call(S0=None, S=None, B=0) == 0        # scores may stay on chip
 
 
+def test_fused_pair_sample_validation():
+    f = bd.lib().dflash2_pair_sample
+    ok = dict(tv=P, ti=P + 0x10000, anc=None, U=Q, Vf=Q + 0x100000, gate=None, u=P + 0x50000,
+              T=1.0, B=2, L=4, V=100, r=8, dt=1, S0=P + 0x20000, S=P + 0x30000,
+              slot=P + 0x60000, tok=P + 0x61000, q=P + 0x62000)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(*(a[k] for k in ok), None)
+
+    # every call below is rejected (or empty) before anything is launched
+    assert call(B=0) == 0
+    assert call(B=-1) == EINVAL
+    assert call(T=0.0) == EINVAL
+    assert call(T=float("inf")) == EINVAL
+    assert call(L=0) == EINVAL
+    assert call(L=65) == EINVAL
+    assert call(r=257) == EINVAL
+    assert call(V=15) == EINVAL
+    for k in ("tv", "ti", "U", "Vf", "u", "slot", "q"):
+        assert call(**{k: None}) == EINVAL, k
+    assert call(u=P + 0x50002) == EINVAL          # misaligned uniforms
+    assert call(q=P + 0x50000) == EINVAL          # q over the uniforms
+    assert call(S=P) == EINVAL                    # S over top_val
+    assert call(tok=P + 0x60000) == EINVAL        # path_tok aliases path_slot
+    assert call(S0=None, S=None, B=0) == 0
+
+
 def test_lazy_rejection_validation():
     f = bd.lib().dflash2_verify_rejection_lazy
     #     slot  tok         q            ti           z   T    ua           ur

@@ -27,7 +27,8 @@ Bars (floating point from the arithmetic, integers exact):
             window; emitted tokens follow the target (chi-square, GPU)
   verify    exact
   fused     scores, walk and verification in one launch: bit for bit the
-            three separate calls
+            three separate calls; scores and the sampling walk in one launch:
+            bit for bit the two separate calls
 """
 import numpy as np
 import pytest
@@ -794,4 +795,46 @@ def test_fused_pair_walk_verify_empty_batch():
     e = torch.empty((0, 4, 16), device=DEV)
     out = bd.pair_select_verify(e, e.to(torch.int32), None, U, U,
                                 torch.empty((0, 5), dtype=torch.int32, device=DEV))
+    assert all(t.shape[0] == 0 for t in out)
+
+
+@pytest.mark.parametrize("dt,B,L,V,r,gated,T", [
+    ("f32", 1, 1, 64, 1, False, 1.0), ("bf16", 3, 2, 500, 7, True, 0.7),
+    ("bf16", 64, 8, 4096, 32, False, 1.0), ("f32", 5, 16, 151936, 64, True, 2.0),
+    ("bf16", 40, 8, 151936, 64, False, 1.0), ("bf16", 9, 17, 2000, 128, True, 1.0),
+    ("bf16", 3, 64, 1000, 256, False, 0.5), ("f32", 300, 3, 700, 8, False, 1.0)])
+def test_fused_pair_sample_matches_the_separate_calls(dt, B, L, V, r, gated, T):
+    tv, ti, at, U, Vf = _pair_case(B, L, V, r, dt, seed=B * 5 + L + r)
+    g = np.random.default_rng(B + L)
+    gate = g.random((B, L, r)).astype(np.float32) if gated else None
+    u = g.random((B, L)).astype(np.float32)
+    d = dict(tv=torch.from_numpy(tv).to(DEV), ti=torch.from_numpy(ti).to(DEV),
+             at=torch.from_numpy(at).to(DEV), U=to_dev(U, dt), Vf=to_dev(Vf, dt),
+             gate=None if gate is None else torch.from_numpy(gate).to(DEV),
+             u=torch.from_numpy(u).to(DEV))
+    S0, S = bd.pair_score(d["tv"], d["ti"], d["at"], d["U"], d["Vf"], gate=d["gate"])
+    slot, tok, q = bd.path_sample(S0, S if L > 1 else None, d["ti"], d["u"], T)
+    fS0 = torch.full_like(S0, 7.0)
+    fS = torch.full_like(S, 7.0)
+    f = bd.pair_sample(d["tv"], d["ti"], d["at"], d["U"], d["Vf"], d["u"], T, d["gate"], fS0, fS)
+    assert torch.equal(fS0, S0) and torch.equal(fS, S)
+    for got, want in zip(f, (slot, tok, q)):
+        assert torch.equal(got, want)
+    g2 = bd.pair_sample(d["tv"], d["ti"], d["at"], d["U"], d["Vf"], d["u"], T, d["gate"])
+    for got, want in zip(g2, (slot, tok, q)):
+        assert torch.equal(got, want)
+    # the walk follows the oracle's sampling rule on the kernel's scores
+    ws, wt, wq = O.sample_path(S0.cpu().numpy(), S.cpu().numpy(), ti, T, u)
+    k = decided_prefix(O.sample_margin(wq, u), SAMPLE_TOL)
+    s_np = f[0].cpu().numpy()
+    for b in range(B):
+        np.testing.assert_array_equal(s_np[b, :k[b]], ws[b, :k[b]])
+    if B >= 20:
+        assert (k == L).mean() >= 0.9
+
+
+def test_fused_pair_sample_empty_batch():
+    U = torch.zeros((64, 8), device=DEV)
+    e = torch.empty((0, 4, 16), device=DEV)
+    out = bd.pair_sample(e, e.to(torch.int32), None, U, U, torch.empty((0, 4), device=DEV), 1.0)
     assert all(t.shape[0] == 0 for t in out)
