@@ -1,0 +1,202 @@
+"""The oracle's pins are sharp: each test plants one plausible mistake in an
+oracle function (on the CPU, through monkeypatch, for the duration of the
+test only) and checks that a pin in test_oracle_pins.py then fails.  A pin
+that still passed with the mistake planted would not be pinning that part of
+the function."""
+import numpy as np
+import pytest
+
+import oracle as O
+import test_oracle_pins as pins
+
+
+def _fails(*pin_calls):
+    for call in pin_calls:
+        with pytest.raises(AssertionError):
+            call()
+
+
+# ------------------------------------------------------------------ bf16 rounding
+def test_pins_catch_truncating_bf16_rounding(monkeypatch):
+    def truncate(v):
+        f = np.asarray(v, dtype=np.float64).astype(np.float32)
+        return (f.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+
+    monkeypatch.setattr(O, "round_to_bf16", truncate)
+    _fails(pins.test_bf16_round_matches_torch_cast_on_f32_values,
+           pins.test_bf16_round_ties_to_even_and_rounds_once)
+
+
+def test_pins_catch_double_rounding_through_fp32(monkeypatch):
+    orig = O.round_to_bf16
+    monkeypatch.setattr(O, "round_to_bf16",
+                        lambda v: orig(np.asarray(v, dtype=np.float64).astype(np.float32)
+                                       .astype(np.float64)))
+    _fails(pins.test_bf16_round_ties_to_even_and_rounds_once)
+
+
+# ------------------------------------------------------------------ conv
+def test_pins_catch_swapped_conv_taps(monkeypatch):
+    orig = O.twotap_conv
+    monkeypatch.setattr(O, "twotap_conv",
+                        lambda x, a, k0, k1, *r, **kw: orig(x, a, k1, k0, *r, **kw))
+    _fails(pins.test_conv_identity_taps_return_input_exactly,
+           pins.test_conv_shift_taps_read_predecessor_and_anchor)
+
+
+def test_pins_catch_a_dropped_anchor(monkeypatch):
+    orig = O.twotap_conv
+    monkeypatch.setattr(O, "twotap_conv",
+                        lambda x, a, k0, k1, *r, **kw: orig(x, None, k0, k1, *r, **kw))
+    _fails(pins.test_conv_shift_taps_read_predecessor_and_anchor)
+
+
+def test_pins_catch_a_wrong_channel_to_group_map(monkeypatch):
+    orig = O.twotap_conv
+
+    def strided_groups(x, a, k0, k1, P=None, G=1):
+        # channel c in group c % G instead of c // (H / G)
+        if P is None or G == 1:
+            return orig(x, a, k0, k1, P, G)
+        B, L, H = x.shape
+        first = np.zeros((B, 1, H)) if a is None else np.asarray(a, dtype=np.float64)[:, None]
+        prev = np.concatenate([first, x[:, :-1]], axis=1)
+        D = x @ P
+        grp = np.arange(H) % G
+        return (k0 + D[..., 2 * grp]) * x + (k1 + D[..., 2 * grp + 1]) * prev
+
+    monkeypatch.setattr(O, "twotap_conv", strided_groups)
+    _fails(pins.test_conv_one_hot_rows_recover_taps_and_corrections,
+           pins.test_conv_per_16_channel_groups_reduce_to_one_group)
+
+
+# ------------------------------------------------------------------ logits
+def test_pins_catch_fp32_accumulation_of_the_logits(monkeypatch):
+    def fp32_sums(y, W, w_dtype, chunk_elems=None):
+        Wd = O.as_f64(W, w_dtype)
+        return (np.asarray(y, np.float32) @ Wd.astype(np.float32).T).astype(np.float64)
+
+    monkeypatch.setattr(O, "lm_logits", fp32_sums)
+    _fails(pins.test_logits_are_exact_sums_rounded_once)
+
+
+def test_pins_catch_a_transposed_weight_read(monkeypatch):
+    orig = O.lm_logits
+
+    def reversed_rows(y, W, w_dtype, *a, **kw):
+        return orig(y, np.ascontiguousarray(np.asarray(W)[::-1]), w_dtype, *a, **kw)
+
+    monkeypatch.setattr(O, "lm_logits", reversed_rows)
+    _fails(pins.test_logits_one_hot_rows_return_weight_columns)
+
+
+# ------------------------------------------------------------------ top-16
+def test_pins_catch_ties_broken_by_the_higher_id(monkeypatch):
+    def topk_high_id_first(z):
+        z = np.asarray(z, dtype=np.float32)
+        zc = np.where(np.isnan(z), -np.inf, z) + np.float32(0.0)   # -0 -> +0
+        M, V = z.shape
+        ids = np.arange(V)
+        ti = np.stack([np.lexsort((-ids, -zc[m]))[:16] for m in range(M)]).astype(np.int32)
+        return np.take_along_axis(zc, ti, axis=1), ti
+
+    monkeypatch.setattr(O, "topk16", topk_high_id_first)
+    _fails(lambda: pins.test_topk_matches_rank_counting_with_ties_zeros_nan_inf(0))
+
+
+# ------------------------------------------------------------------ pair scores and gate
+def test_pins_catch_swapped_pair_factors(monkeypatch):
+    orig = O.pair_scores
+    monkeypatch.setattr(O, "pair_scores",
+                        lambda tv, ti, at, U, Vf, *r, **kw: orig(tv, ti, at, Vf, U, *r, **kw))
+    _fails(pins.test_pair_scores_one_hot_factors_give_indicator_matches)
+
+
+def test_pins_catch_a_dropped_anchor_match(monkeypatch):
+    orig = O.pair_scores
+    monkeypatch.setattr(O, "pair_scores",
+                        lambda tv, ti, at, U, Vf, *r, **kw: orig(tv, ti, None, U, Vf, *r, **kw))
+    _fails(pins.test_pair_scores_one_hot_factors_give_indicator_matches)
+
+
+def test_pins_catch_the_previous_positions_gate(monkeypatch):
+    orig = O.pair_scores
+
+    def lagged_gate(tv, ti, at, U, Vf, dt, gate=None):
+        return orig(tv, ti, at, U, Vf, dt, None if gate is None else np.roll(gate, 1, axis=1))
+
+    monkeypatch.setattr(O, "pair_scores", lagged_gate)
+    _fails(pins.test_gated_pair_scores_reduce_and_use_the_current_positions_gate)
+
+
+def test_pins_catch_a_permuted_gate_map(monkeypatch):
+    orig = O.context_gate
+    monkeypatch.setattr(O, "context_gate",
+                        lambda y, Wg, wd: orig(y, np.ascontiguousarray(np.asarray(Wg)[::-1]), wd))
+    _fails(pins.test_context_gate_hand_values_and_orientation)
+
+
+def test_pins_catch_a_missing_sigmoid(monkeypatch):
+    def linear_gate(y, Wg, wd):
+        return (np.asarray(y, np.float64) @ O.as_f64(Wg, wd).T).astype(np.float32)
+
+    monkeypatch.setattr(O, "context_gate", linear_gate)
+    _fails(pins.test_context_gate_hand_values_and_orientation,
+           pins.test_context_gate_symmetry_and_library_logistic)
+
+
+# ------------------------------------------------------------------ walks
+def test_pins_catch_the_highest_slot_winning_ties(monkeypatch):
+    orig = O.path_select
+
+    def high_slot(S0, S, ti):
+        slot, tok, score = orig(np.ascontiguousarray(S0[:, ::-1]),
+                                np.ascontiguousarray(S[:, :, ::-1, ::-1]),
+                                np.ascontiguousarray(ti[:, :, ::-1]))
+        return 15 - slot, tok, score
+
+    monkeypatch.setattr(O, "path_select", high_slot)
+    _fails(*[lambda L=L, s=s: pins.test_path_select_matches_brute_force_on_dyadic_scores_with_ties(L, s)
+             for L, s in ((2, 1), (3, 2))])
+
+
+def test_pins_catch_transposed_pair_scores_in_the_walks(monkeypatch):
+    ps, pg = O.path_select, O.path_select_greedy
+    monkeypatch.setattr(O, "path_select",
+                        lambda S0, S, ti: ps(S0, np.ascontiguousarray(S.transpose(0, 1, 3, 2)), ti))
+    monkeypatch.setattr(O, "path_select_greedy",
+                        lambda S0, S, ti: pg(S0, np.ascontiguousarray(S.transpose(0, 1, 3, 2)), ti))
+    _fails(lambda: pins.test_path_select_matches_brute_force_on_continuous_scores(3, 6),
+           pins.test_greedy_walk_hand_trap_differs_from_viterbi)
+
+
+def test_pins_catch_a_sampling_walk_that_ignores_the_temperature(monkeypatch):
+    orig = O.sample_path
+    monkeypatch.setattr(O, "sample_path", lambda S0, S, ti, T, u: orig(S0, S, ti, 1.0, u))
+    _fails(pins.test_sample_path_inverse_cdf_hand_case)
+
+
+# ------------------------------------------------------------------ verification
+def test_pins_catch_an_accept_test_without_the_uniform(monkeypatch):
+    orig = O.rejection_verify
+    monkeypatch.setattr(O, "rejection_verify",
+                        lambda tok, q, top, z, T, ua, ur: orig(tok, q, top, z, T, ua * 0.0, ur))
+    _fails(pins.test_rejection_verify_preserves_the_target_distribution)
+
+
+def test_pins_catch_an_acceptance_without_the_verifiers_token(monkeypatch):
+    orig = O.verify_greedy
+
+    def no_bonus(path, tgt):
+        acc, nxt = orig(path, tgt)
+        return acc - 1, nxt
+
+    monkeypatch.setattr(O, "verify_greedy", no_bonus)
+    _fails(pins.test_verify_hand_cases, pins.test_verify_invariants_random)
+
+
+def test_pins_catch_unconditional_recall_in_the_closed_form(monkeypatch):
+    # treating Table 1's recall as independent per position: 1 + sum p_t
+    monkeypatch.setattr(O, "expected_acceptance",
+                        lambda p: float(1.0 + np.sum(np.asarray(p, dtype=np.float64))))
+    _fails(pins.test_table1_acceptance_follows_from_recall_rows)
