@@ -200,3 +200,50 @@ def test_pins_catch_unconditional_recall_in_the_closed_form(monkeypatch):
     monkeypatch.setattr(O, "expected_acceptance",
                         lambda p: float(1.0 + np.sum(np.asarray(p, dtype=np.float64))))
     _fails(pins.test_table1_acceptance_follows_from_recall_rows)
+
+
+# ------------------------------------------------------------------ more planted mistakes
+def test_pins_catch_a_chain_rounded_only_at_the_end(monkeypatch):
+    def round_once(x, convs, dtype):
+        y = np.asarray(x, dtype=np.float64)
+        for c in convs:
+            y = O.twotap_conv(y, c["anchor_h"], c["k0"], c["k1"], c.get("proj"),
+                              c.get("groups", 1))
+        return O.round_to_dtype(y, dtype)
+
+    monkeypatch.setattr(O, "conv_chain", round_once)
+    _fails(pins.test_conv_chain_rounds_each_application_to_storage_type)
+
+
+def test_pins_catch_greedy_ties_to_the_highest_slot(monkeypatch):
+    orig = O.path_select_greedy
+
+    def high_slot(S0, S, ti):
+        slot, tok, score = orig(np.ascontiguousarray(S0[:, ::-1]),
+                                np.ascontiguousarray(S[:, :, ::-1, ::-1]),
+                                np.ascontiguousarray(ti[:, :, ::-1]))
+        return 15 - slot, tok, score
+
+    monkeypatch.setattr(O, "path_select_greedy", high_slot)
+    _fails(pins.test_greedy_walk_is_never_better_than_the_best_path)
+
+
+def test_pins_catch_a_greedy_walk_from_the_wrong_row(monkeypatch):
+    # the next row taken from the slot's position in the candidate list of
+    # the wrong step: scores of step t read with step t+1's row index
+    orig = O.path_select_greedy
+
+    def shifted_rows(S0, S, ti):
+        return orig(S0, np.ascontiguousarray(np.roll(S, 1, axis=1)), ti)
+
+    monkeypatch.setattr(O, "path_select_greedy", shifted_rows)
+    _fails(pins.test_greedy_walk_hand_trap_differs_from_viterbi)
+
+
+def test_pins_catch_sampling_from_the_transposed_row(monkeypatch):
+    orig = O.sample_path
+    monkeypatch.setattr(O, "sample_path",
+                        lambda S0, S, ti, T, u: orig(S0, np.ascontiguousarray(
+                            np.swapaxes(S, -1, -2)), ti, T, u))
+    _fails(pins.test_sample_path_inverse_cdf_hand_case,
+           pins.test_sample_path_frequencies_and_low_temperature_limit)

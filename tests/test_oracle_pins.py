@@ -455,7 +455,7 @@ def test_sample_path_inverse_cdf_hand_case():
     S0[0, :3] = np.log([1.0, 2.0, 7.0])
     S = np.zeros((1, 1, 16, 16))
     S[0, 0, 2, 9] = 50.0          # slot 2's successors: almost surely slot 9
-    S[0, 0, 9, 2] = 50.0          # transposed trap
+    S[0, 0, 7, 2] = 60.0          # trap: reading column 2 instead of row 2 gives slot 7
     ti = np.arange(32, dtype=np.int32).reshape(1, 2, 16)
     for u0, want0 in ((0.05, 0), (0.1000001, 1), (0.25, 1), (0.31, 2), (0.999999, 2)):
         slot, tok, q = O.sample_path(S0, S, ti, 1.0, np.array([[u0, 0.5]]))
