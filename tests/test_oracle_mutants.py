@@ -247,3 +247,91 @@ def test_pins_catch_sampling_from_the_transposed_row(monkeypatch):
                             np.swapaxes(S, -1, -2)), ti, T, u))
     _fails(pins.test_sample_path_inverse_cdf_hand_case,
            pins.test_sample_path_frequencies_and_low_temperature_limit)
+
+
+def test_pins_catch_an_unshifted_log_sum_exp(monkeypatch):
+    def unshifted(z, T):
+        with np.errstate(over="ignore"):
+            return np.log(np.exp(np.asarray(z, np.float64) / T).sum(axis=-1))
+
+    monkeypatch.setattr(O, "target_lse", unshifted)
+    _fails(pins.test_target_lse_matches_scipy_logsumexp)
+
+
+def test_pins_catch_a_log_sum_exp_without_the_temperature(monkeypatch):
+    orig = O.target_lse
+    monkeypatch.setattr(O, "target_lse", lambda z, T: orig(z, 1.0))
+    _fails(pins.test_target_lse_matches_scipy_logsumexp)
+
+
+def test_pins_catch_sampling_margins_without_the_first_edge(monkeypatch):
+    def upper_edges_only(q, u):
+        cum = np.cumsum(q, axis=-1)
+        return np.min(np.abs(cum - np.asarray(u, np.float64)[..., None]), axis=-1)
+
+    monkeypatch.setattr(O, "sample_margin", upper_edges_only)
+    _fails(pins.test_sample_margin_hand_case)
+
+
+def test_pins_catch_top16_gaps_measured_on_one_side(monkeypatch):
+    orig = O.topk_gaps
+
+    def above_only(z, top_val):
+        g = orig(z, top_val)
+        vals = top_val.astype(np.float64)
+        up = np.concatenate([np.full((g.shape[0], 1), np.inf), vals[:, :-1] - vals[:, 1:]], axis=1)
+        return up
+
+    monkeypatch.setattr(O, "topk_gaps", above_only)
+    _fails(pins.test_topk_gaps)
+
+
+def test_pins_catch_a_margin_between_final_states(monkeypatch):
+    # the gap between the two best final slots of the max-plus recursion,
+    # taken for the gap to the second best path (which may end in the same slot)
+    def final_state_gap(S0, S):
+        d = np.asarray(S0, np.float64)
+        for t in range(S.shape[1]):
+            d = (d[:, :, None] + np.asarray(S[:, t], np.float64)).max(axis=1)
+        srt = -np.sort(-d, axis=1)
+        return srt[:, 0] - srt[:, 1]
+
+    monkeypatch.setattr(O, "path_margin", final_state_gap)
+    _fails(pins.test_path_margin_when_the_second_path_shares_the_final_slot)
+
+
+def test_pins_catch_the_largest_instead_of_the_smallest_greedy_gap(monkeypatch):
+    def largest_gap(S0, S, slot):
+        S0 = np.asarray(S0, np.float64)
+        S = np.asarray(S, np.float64)
+        B, L = slot.shape
+        b = np.arange(B)
+        gap = lambda row: (lambda s: s[:, 0] - s[:, 1])(-np.sort(-row, axis=1))
+        m = gap(S0)
+        for t in range(1, L):
+            m = np.maximum(m, gap(S[b, t - 1, slot[:, t - 1]]))
+        return m
+
+    monkeypatch.setattr(O, "greedy_margin", largest_gap)
+    _fails(pins.test_greedy_walk_hand_trap_differs_from_viterbi)
+
+
+def test_pins_catch_a_residual_draw_from_p(monkeypatch):
+    # at a rejection, drawing from p instead of max(0, p - q): the verifier
+    # would re-propose the rejected candidates
+    orig = O.rejection_verify
+
+    def no_residual(path_tok, q, top_idx, z, T, u_acc, u_res):
+        acc, nxt = orig(path_tok, q, top_idx, z, T, u_acc, u_res)
+        zz = np.asarray(z, np.float64)
+        lse = O.target_lse(zz, T)
+        for b in range(len(acc)):
+            n = acc[b] - 1
+            p = np.exp(zz[b, n] / T - lse[b, n])
+            cum = np.cumsum(p)
+            v = int(np.searchsorted(cum, u_res[b] * cum[-1], side="right"))
+            nxt[b] = min(v, len(p) - 1)
+        return acc, nxt
+
+    monkeypatch.setattr(O, "rejection_verify", no_residual)
+    _fails(pins.test_rejection_verify_preserves_the_target_distribution)

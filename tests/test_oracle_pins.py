@@ -354,6 +354,18 @@ def test_path_select_matches_brute_force_on_continuous_scores(L, seed):
         assert abs(margin[b] - (best - second)) < 1e-9
 
 
+def test_path_margin_when_the_second_path_shares_the_final_slot():
+    # best 0 -> 5 (3 + 1), second best 1 -> 5 (2.5 + 1): both end in slot 5,
+    # so the gap between the best two final slots (7 or more) is not the margin
+    S0 = np.full((1, 16), -10.0, np.float32)
+    S0[0, 0], S0[0, 1] = 3.0, 2.5
+    S = np.full((1, 1, 16, 16), -10.0, np.float32)
+    S[0, 0, 0, 5] = S[0, 0, 1, 5] = 1.0
+    assert O.path_margin(S0, S).tolist() == [0.5]
+    slot, _, score = O.path_select(S0, S, np.zeros((1, 2, 16), np.int32))
+    assert slot.tolist() == [[0, 5]] and score.tolist() == [4.0]
+
+
 def test_path_select_invariances():
     g = np.random.default_rng(15)
     B, L = 6, 6
@@ -492,6 +504,30 @@ def test_sample_path_frequencies_and_low_temperature_limit():
     gs, _, _ = O.path_select_greedy(S0.astype(np.float32), S.astype(np.float32), ti)
     ss, _, _ = O.sample_path(S0, S, ti, 1e-4, g.uniform(0.001, 0.999, (B, L)))
     np.testing.assert_array_equal(ss, gs)
+
+
+def test_sample_margin_hand_case():
+    # bins of q = [0.1, 0.2, 0.7]: edges 0, 0.1, 0.3, 1.0
+    q = np.zeros((1, 4, 16))
+    q[0, :, :3] = [0.1, 0.2, 0.7]
+    u = np.array([[0.02, 0.25, 0.95, 0.1]])
+    np.testing.assert_allclose(O.sample_margin(q, u), [[0.02, 0.05, 0.05, 0.0]], atol=1e-15)
+
+
+def test_target_lse_matches_scipy_logsumexp():
+    # an independent library routine; large logits (no overflow), -inf
+    # entries (no mass) and temperatures
+    from scipy.special import logsumexp
+
+    g = np.random.default_rng(30)
+    z = g.standard_normal((3, 4, 500)) * 3
+    z[0, 0] += 1000.0
+    z[1, 2, ::3] = -np.inf
+    z[2, 1, 1:] = -np.inf                     # one finite entry: lse = that entry / T
+    for T in (1.0, 0.7, 2.0):
+        np.testing.assert_allclose(O.target_lse(z, T), logsumexp(z / T, axis=-1),
+                                   rtol=1e-13, atol=0)
+    assert O.target_lse(z, 0.5)[2, 1] == z[2, 1, 0] / 0.5
 
 
 def _tiny_spec_case(g, N, V=24, L=2):
