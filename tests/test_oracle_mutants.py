@@ -335,3 +335,38 @@ def test_pins_catch_a_residual_draw_from_p(monkeypatch):
 
     monkeypatch.setattr(O, "rejection_verify", no_residual)
     _fails(pins.test_rejection_verify_preserves_the_target_distribution)
+
+
+def test_pins_catch_the_previous_token_taken_from_the_same_position(monkeypatch):
+    orig = O.pair_scores
+
+    def same_position(tv, ti, at, U, Vf, dt, gate=None):
+        S0, S = orig(tv, ti, at, U, Vf, dt, gate)
+        Ud, Vd = O.as_f64(U, dt), O.as_f64(Vf, dt)
+        ti = np.asarray(ti)
+        # S[t-1, i, j] with the previous factors of position t's candidates
+        prev = Ud[ti[:, 1:]]
+        cur = Vd[ti[:, 1:]]
+        if gate is not None:
+            prev = prev * np.asarray(gate, np.float64)[:, 1:, None, :]
+        S = (np.asarray(tv, np.float64)[:, 1:, None, :] +
+             np.einsum("btik,btjk->btij", prev, cur)).astype(np.float32)
+        return S0, S
+
+    monkeypatch.setattr(O, "pair_scores", same_position)
+    _fails(pins.test_pair_scores_one_hot_factors_give_indicator_matches)
+
+
+def test_pins_catch_scores_with_the_candidates_logit_of_the_wrong_slot(monkeypatch):
+    # the unary term of the previous candidate i instead of the current j
+    orig = O.pair_scores
+
+    def row_unary(tv, ti, at, U, Vf, dt, gate=None):
+        S0, S = orig(tv, ti, at, U, Vf, dt, gate)
+        tvd = np.asarray(tv, np.float64)
+        S = (S.astype(np.float64) - tvd[:, 1:, None, :] + tvd[:, 1:, :, None]).astype(np.float32)
+        return S0, S
+
+    monkeypatch.setattr(O, "pair_scores", row_unary)
+    _fails(pins.test_pair_scores_zero_factors_reduce_to_unary,
+           pins.test_pair_scores_one_hot_factors_give_indicator_matches)
