@@ -838,3 +838,33 @@ def test_fused_pair_sample_empty_batch():
     e = torch.empty((0, 4, 16), device=DEV)
     out = bd.pair_sample(e, e.to(torch.int32), None, U, U, torch.empty((0, 4), device=DEV), 1.0)
     assert all(t.shape[0] == 0 for t in out)
+
+
+@pytest.mark.parametrize("mode", ["viterbi", "greedy"])
+def test_fused_calls_without_anchor_and_with_bad_ids(mode):
+    # no anchor token (no match term at t = 0) and candidate ids outside
+    # [0, V) (NaN scores): the fused calls still equal the separate ones bit
+    # for bit, and every slot stays in [0, 16)
+    B, L, V, r = 6, 5, 300, 16
+    tv, ti, _, U, Vf = _pair_case(B, L, V, r, "f32", seed=77, anchor=False)
+    ti[1, 2, 4] = V
+    ti[3, 0, 0] = -5
+    d = [torch.from_numpy(tv).to(DEV), torch.from_numpy(ti).to(DEV), None,
+         torch.from_numpy(U).to(DEV), torch.from_numpy(Vf).to(DEV)]
+    S0, S = bd.pair_score(*d)
+    slot, tok, score = bd.path_select(S0, S, d[1], mode=mode)
+    tg = torch.from_numpy(_plant_targets(tok.cpu().numpy(), V, seed=8)).to(DEV)
+    acc, nxt = bd.verify_greedy(tok, tg)
+    f = bd.pair_select_verify(*d, tg, None, mode)
+    for got, want in zip(f, (slot, tok, score, acc, nxt)):
+        assert torch.equal(got, want) or (got.dtype == torch.float32 and
+                                          torch.equal(torch.isnan(got), torch.isnan(want)) and
+                                          torch.equal(got[~torch.isnan(got)], want[~torch.isnan(want)]))
+    s = f[0].cpu().numpy()
+    assert ((s >= 0) & (s < 16)).all()
+    u = torch.from_numpy(np.random.default_rng(2).random((B, L)).astype(np.float32)).to(DEV)
+    ps, pt, pq = bd.path_sample(S0, S, d[1], u, 1.0)
+    fs = bd.pair_sample(*d, u, 1.0)
+    assert torch.equal(fs[0], ps) and torch.equal(fs[1], pt)
+    assert torch.equal(torch.isnan(fs[2]), torch.isnan(pq))
+    assert torch.equal(fs[2][~torch.isnan(pq)], pq[~torch.isnan(pq)])
