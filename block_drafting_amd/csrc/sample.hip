@@ -19,6 +19,14 @@
 //                       256-token tiles wave by wave, moves the 16
 //                       candidates' corrections into their tiles, scans the
 //                       tile sums, then scans inside the chosen tile.
+// verify_rejection_lazy_kernel  the same rule with each target row's
+//                       log-sum-exp computed here, only for the rows the
+//                       accept test reaches: one pass per row keeps every
+//                       tile's (reference max, sum) in LDS, which also gives
+//                       the draw's tile masses at the row where the test stops.
+//
+// The sampling walk itself (sample_walk) lives in walk.hpp, shared with the
+// fused scores-and-walk kernel.
 #include "walk.hpp"
 
 namespace dflash2 {

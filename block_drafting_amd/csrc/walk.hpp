@@ -1,8 +1,9 @@
 // Path walks over the pair scores of one block, by one wavefront ("DFlash 2:
 // Keep Drafting Parallel", section "A lightweight path selector": the one
-// serial step walks the scores from the last verified token).  Shared by the
-// walk kernels (scores in global memory) and the fused pair-walk-verify kernel
-// (scores in LDS), so both run the same arithmetic.
+// serial step walks the scores from the last verified token; sampling draws
+// from the same scores).  Shared by the walk kernels (scores staged from
+// global memory) and the fused scores-and-walk kernels (scores computed into
+// LDS), so both run the same arithmetic.
 #pragma once
 #include "common.hpp"
 
