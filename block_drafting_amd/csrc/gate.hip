@@ -23,7 +23,9 @@ __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-
 
 // W waves share each tile; W = 8 takes 256-wide K slices (twice the bytes
 // in flight per tile, for launches of at most one tile per CU), W = 4
-// 128-wide ones (two tiles per CU).
+// 128-wide ones (two tiles per CU).  (Sixteen waves with 512-wide slices,
+// half the serial chain of slices, ran no faster: a tile's operand stream is
+// bound by its CU's L2 bandwidth, not by the chain.)
 template <int W>
 struct GateCfg {
   static constexpr int kWaves = W;
@@ -45,8 +47,14 @@ __global__ __launch_bounds__(64 * W) void gate_bf16_kernel(
   constexpr int kGateCpr = C::kCpr;
   constexpr int kGateRowsPerPass = C::kRowsPerPass;
   constexpr int kGatePasses = C::kPasses;
-  __shared__ __attribute__((aligned(16))) uint16_t stage[2][2][32 * kGateLd];  // [buf][A/B]
-  __shared__ float part[kGateWaves][16][64];
+  // [buf][A/B] operand slices; after the K loop the same bytes hold the
+  // waves' partial tiles
+  constexpr int kStageBytes = 2 * 2 * 32 * kGateLd * 2;
+  constexpr int kPartBytes = kGateWaves * 16 * 64 * 4;
+  __shared__ __attribute__((aligned(16)))
+  uint8_t smem[kStageBytes > kPartBytes ? kStageBytes : kPartBytes];
+  auto stage = reinterpret_cast<uint16_t(*)[2][32 * kGateLd]>(smem);
+  auto part = reinterpret_cast<float(*)[16][64]>(smem);
   const int m0 = blockIdx.x * 32;
   const int n0 = blockIdx.y * 32;
   const int tid = threadIdx.x;
@@ -125,6 +133,7 @@ __global__ __launch_bounds__(64 * W) void gate_bf16_kernel(
     sstore(R0, 0);
     __syncthreads();
   }
+  __syncthreads();  // every wave is done with the stages
 #pragma unroll
   for (int i = 0; i < 16; ++i) part[wave][i][lane] = acc[i];
   __syncthreads();
