@@ -19,7 +19,17 @@ The five stages (names as in the C ABI):
                   path per block
   verify_greedy   greedy verification, acceptance length
 At T > 0: path_sample (sampled walk), target_lse + verify_rejection (lossless
-speculative-sampling verification against target logits).
+speculative-sampling verification against target logits), or
+verify_rejection_lazy (the same rule, each target row's log-sum-exp computed
+only for the rows the accept test reaches).
+One launch for several stages: pair_select_verify (scores, either walk and
+greedy verification) and pair_sample (scores and the sampling walk).
+run_step chains a whole step on preallocated StepBuffers.
+
+Example (one greedy-verified step of 64 blocks of 8 positions):
+    buf = StepBuffers(64, 8, H, V, torch.bfloat16, "cuda")
+    run_step(buf, x, [dict(k0=k0, k1=k1, anchor_h=a)], W, U, Vf, anchor_tok, target)
+    buf.accept_len, buf.next_tok      # int32 [64] each
 """
 from __future__ import annotations
 
