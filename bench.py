@@ -16,6 +16,8 @@ seeded synthetic tensors already resident in HBM when timing starts.
 Prints ONE JSON line (rank 0, N = 1):
   value = blocks/s over the timed steps (B / seconds per step), the step
   captured once as a HIP graph and replayed (--eager: plain launches);
+  a bf16 LM-head weight is packed once into the GEMM's tile layout before
+  timing (--row-major-w: read as given);
   stage_ms = per-stage times from a second, eager pass with events;
   roofline = the LM-head GEMM kernel (the dominant kernel) against the bf16
   matrix-core peak (against HBM when its flop per algorithmic byte is below
@@ -62,6 +64,9 @@ def parse_args(argv=None):
                     help="pair scores, walk and verification as separate launches, and for a "
                          "sampled walk the lse pass over every target row before the "
                          "verification (default: fused scores + walk, lazy verification)")
+    ap.add_argument("--row-major-w", action="store_true",
+                    help="LM-head GEMM reads W [V, H] as given (default for bf16: W packed once, "
+                         "before timing, into the GEMM's 256 x 64 tile layout)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replays of the captured step")
     return ap.parse_args(argv)
@@ -76,9 +81,10 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, w_layout: str):
     """HBM bytes per GEMM launch from the committed counter summary, if it
-    was taken on this workload with the current kernel source; else None."""
+    was taken on this workload and W layout with the current kernel source;
+    else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -86,7 +92,8 @@ def measured_traffic(workload: str):
         m = re.match(r"^\s*([a-z0-9_]+)\s*[:=]\s*(\S+)", line)
         if m:
             kv[m.group(1)] = m.group(2)
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash() or kv.get("workload") != workload:
+    if (kv.get("kernel_source_sha256_16") != kernel_source_hash() or kv.get("workload") != workload
+            or kv.get("w_layout") != w_layout):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -175,6 +182,11 @@ def main(argv=None):
               "projT": None if c["projT"] is None else dev(c["projT"], "act")}
              for c in inp["convs"]]
     W = dev(inp["W"], "act")
+    packed = bf16 and not a.row_major_w
+    w_layout = "packed" if packed else "row-major"
+    if packed:
+        # a decoding loop re-lays its LM-head weight out once, not per step
+        W = bd.lmhead_pack(W)
     U = dev(inp["U"], "act")
     Vf = dev(inp["Vf"], "act")
     anchor = dev(inp["anchor_tok"], "i32")
@@ -342,12 +354,12 @@ def main(argv=None):
         achieved = gemm_bytes / gemm_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": measured_traffic(w.name)}
+                "traffic": measured_traffic(w.name, w_layout)}
     elif bf16:
         achieved = flops / gemm_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(w.name)}
+                "traffic": measured_traffic(w.name, w_layout)}
     else:
         achieved = flops / gemm_s / 1e12
         roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_F32_TFLOPS,
@@ -379,7 +391,7 @@ def main(argv=None):
                    "convs": w.n_convs, "conv_groups": w.groups if w.dynamic else 0, "topk": 16,
                    "gate": w.gate, "walk": w.walk, "temperature": w.temperature,
                    "launch": "hip-graph" if graph is not None else "eager",
-                   "pair_walk": "fused" if fused else "separate",
+                   "pair_walk": "fused" if fused else "separate", "lm_head_w": w_layout,
                    "rejection": ("two-pass" if two_pass else "lazy") if sampled else None},
         "tokens_per_s": round(M / (ms_step * 1e-3), 1),
         "accepted_tokens_per_s": round(float(acc.sum()) / (ms_step * 1e-3), 1),

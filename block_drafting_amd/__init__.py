@@ -12,7 +12,8 @@ The five stages (names as in the C ABI):
                   (twotap_conv_mm: one correction per 16 channels, on the
                   matrix cores)
   logits_topk     LM-head logits and per-position top-16 candidates
-                  (= lmhead_logits then topk16)
+                  (= lmhead_logits then topk16; W may be a PackedWeight from
+                  lmhead_pack, the GEMM's tile layout, made once per weight)
   pair_score      16x16 scores of neighbouring candidates (optionally
                   weighted by a context gate from context_gate)
   path_select     max-plus walk (or the greedy best-successor walk) to one
@@ -41,7 +42,7 @@ import torch
 
 __all__ = [
     "DFlash2Error", "lib", "library_path", "twotap_conv", "twotap_conv_mm", "lmhead_logits",
-    "lmhead_logits_tilemax", "topk16", "topk16_tilemax",
+    "lmhead_logits_tilemax", "lmhead_pack", "PackedWeight", "topk16", "topk16_tilemax",
     "topk16_workspace", "logits_topk", "logits_topk_workspace", "context_gate", "pair_score",
     "path_select", "pair_select_verify", "pair_sample", "path_sample", "target_lse", "verify_rejection", "verify_rejection_lazy", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
 ]
@@ -63,6 +64,8 @@ _SIGS = {
     "dflash2_twotap_conv_mm": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
     "dflash2_lmhead_logits": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "dflash2_lmhead_logits_tilemax": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "dflash2_lmhead_pack_bytes": ([_I, _I], _Z),
+    "dflash2_lmhead_pack": ([_P, _P, _I, _I, _P], _I),
     "dflash2_topk16_tilemax": ([_P, _P, _P, _P, _I, _I, _I, _P], _I),
     "dflash2_topk16_workspace": ([_I, _I, _I], _Z),
     "dflash2_topk16": ([_P, _P, _P, _I, _I, _I, _P, _Z, _P], _I),
@@ -201,29 +204,66 @@ def twotap_conv_mm(x: torch.Tensor, k0: torch.Tensor, k1: torch.Tensor, projT: t
     return out
 
 
-def lmhead_logits(h: torch.Tensor, W: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """logits [M, V] fp32 = h [M, H] . W [V, H]^T."""
-    M, H = h.shape
+class PackedWeight:
+    """An LM-head weight [V, H] bf16 in the bf16 GEMM's tile layout
+    (dflash2_lmhead_pack): `data` holds the packed bytes.  The LM-head calls
+    take it wherever they take W, with bit-identical logits."""
+
+    def __init__(self, data: torch.Tensor, V: int, H: int):
+        self.data, self.V, self.H = data, V, H
+        self.dtype = torch.bfloat16
+        self.device = data.device
+        self.shape = (V, H)
+
+
+def lmhead_pack(W: torch.Tensor) -> PackedWeight:
+    """Copy W [V, H] bf16 into the GEMM's tile layout (one launch)."""
+    if W.dim() != 2 or W.dtype != torch.bfloat16:
+        raise TypeError("W must be a 2-D bf16 tensor")
+    V, H = W.shape
+    n = int(lib().dflash2_lmhead_pack_bytes(V, H))
+    if n == 0:
+        raise ValueError(f"no packed layout for V={V}, H={H}")
+    data = torch.empty(n, dtype=torch.uint8, device=W.device)
+    dev = _dev(W, data)
+    _check("dflash2_lmhead_pack", lib().dflash2_lmhead_pack(
+        _ptr(W), _ptr(data), V, H, _stream(dev)))
+    return PackedWeight(data, V, H)
+
+
+def _weight(W, h: torch.Tensor):
+    """(pointer, V, dtype code, tensor) of an LM-head weight for h [M, H]."""
+    H = h.shape[1]
+    if isinstance(W, PackedWeight):
+        if h.dtype != torch.bfloat16 or W.H != H:
+            raise ValueError(f"packed W is bf16 [{W.V}, {W.H}]; h is {h.dtype} [*, {H}]")
+        return W.data.data_ptr(), W.V, 2, W.data
     V = W.shape[0]
     _shape(W, (V, H), "W", h.dtype)
+    return W.data_ptr(), V, _dt(h), W
+
+
+def lmhead_logits(h: torch.Tensor, W, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """logits [M, V] fp32 = h [M, H] . W [V, H]^T (W a tensor or a PackedWeight)."""
+    M, H = h.shape
+    wp, V, code, wt = _weight(W, h)
     if out is None:
         out = torch.empty((M, V), dtype=torch.float32, device=h.device)
     _shape(out, (M, V), "out", torch.float32)
-    dev = _dev(h, W, out)
+    dev = _dev(h, wt, out)
     _check("dflash2_lmhead_logits", lib().dflash2_lmhead_logits(
-        _ptr(h), _ptr(W), _ptr(out), M, H, V, _dt(h), _stream(dev)))
+        _ptr(h), wp, _ptr(out), M, H, V, code, _stream(dev)))
     return out
 
 
 TILEMAX_COLS = 256
 
 
-def lmhead_logits_tilemax(h: torch.Tensor, W: torch.Tensor, out: Optional[torch.Tensor] = None,
+def lmhead_logits_tilemax(h: torch.Tensor, W, out: Optional[torch.Tensor] = None,
                           tilemax: Optional[torch.Tensor] = None):
     """Logits [M, V] and their 256-column tile maxima [M, ceil(V / 256)]."""
     M, H = h.shape
-    V = W.shape[0]
-    _shape(W, (V, H), "W", h.dtype)
+    wp, V, code, wt = _weight(W, h)
     nt = (V + TILEMAX_COLS - 1) // TILEMAX_COLS
     if out is None:
         out = torch.empty((M, V), dtype=torch.float32, device=h.device)
@@ -231,9 +271,9 @@ def lmhead_logits_tilemax(h: torch.Tensor, W: torch.Tensor, out: Optional[torch.
         tilemax = torch.empty((M, nt), dtype=torch.float32, device=h.device)
     _shape(out, (M, V), "logits", torch.float32)
     _shape(tilemax, (M, nt), "tilemax", torch.float32)
-    dev = _dev(h, W, out, tilemax)
+    dev = _dev(h, wt, out, tilemax)
     _check("dflash2_lmhead_logits_tilemax", lib().dflash2_lmhead_logits_tilemax(
-        _ptr(h), _ptr(W), _ptr(out), _ptr(tilemax), M, H, V, _dt(h), _stream(dev)))
+        _ptr(h), wp, _ptr(out), _ptr(tilemax), M, H, V, code, _stream(dev)))
     return out, tilemax
 
 
@@ -294,14 +334,13 @@ def logits_topk_workspace(M: int, H: int, V: int, dtype: torch.dtype, logits_giv
         M, H, V, TOPK, 1 if dtype == torch.bfloat16 else 0, int(bool(logits_given))))
 
 
-def logits_topk(h: torch.Tensor, W: torch.Tensor, logits: Optional[torch.Tensor] = None,
+def logits_topk(h: torch.Tensor, W, logits: Optional[torch.Tensor] = None,
                 top_val: Optional[torch.Tensor] = None, top_idx: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None):
     """LM-head logits (into `logits` when given, else into the workspace) and
     the per-row top-16.  Returns (top_val, top_idx)."""
     M, H = h.shape
-    V = W.shape[0]
-    _shape(W, (V, H), "W", h.dtype)
+    wp, V, code, wt = _weight(W, h)
     dev = h.device
     if logits is not None:
         _shape(logits, (M, V), "logits", torch.float32)
@@ -311,9 +350,9 @@ def logits_topk(h: torch.Tensor, W: torch.Tensor, logits: Optional[torch.Tensor]
         top_idx = torch.empty((M, TOPK), dtype=torch.int32, device=dev)
     need = logits_topk_workspace(M, H, V, h.dtype, logits is not None)
     ws = _workspace(need, dev, workspace)
-    _dev(h, W, logits, top_val, top_idx, ws)
+    _dev(h, wt, logits, top_val, top_idx, ws)
     _check("dflash2_logits_topk", lib().dflash2_logits_topk(
-        _ptr(h), _ptr(W), _ptr(logits), _ptr(top_val), _ptr(top_idx), M, H, V, TOPK, _dt(h),
+        _ptr(h), wp, _ptr(logits), _ptr(top_val), _ptr(top_idx), M, H, V, TOPK, code,
         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(dev)))
     return top_val, top_idx
 
@@ -608,7 +647,7 @@ class StepBuffers:
         self.lse = torch.empty((B, L + 1), dtype=torch.float32, **kw) if sample else None
 
 
-def run_step(buf: StepBuffers, x: torch.Tensor, convs, W: torch.Tensor, U: torch.Tensor,
+def run_step(buf: StepBuffers, x: torch.Tensor, convs, W, U: torch.Tensor,
              Vf: torch.Tensor, anchor_tok: Optional[torch.Tensor],
              target: Optional[torch.Tensor], Wg: Optional[torch.Tensor] = None,
              walk: str = "viterbi", temperature: float = 0.0,
@@ -617,7 +656,8 @@ def run_step(buf: StepBuffers, x: torch.Tensor, convs, W: torch.Tensor, U: torch
              u_res: Optional[torch.Tensor] = None) -> StepBuffers:
     """One draft-select-verify step: the conv chain (each entry of `convs` is a
     dict with k0, k1, anchor_h and either proj + groups, or projT for the
-    matrix-core corrections), logits + top-16, pair scores
+    matrix-core corrections), logits + top-16 (W a tensor or a PackedWeight),
+    pair scores
     (context-gated from the final hidden states when `Wg` is given), the path
     walk (`walk`: "viterbi", "greedy", or "sample" at `temperature` with the
     uniforms `u_path`) and verification: greedy against `target` argmax ids,

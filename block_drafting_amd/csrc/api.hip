@@ -15,8 +15,13 @@ constexpr int kVersion = 10000;  // 1.0.0
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
 
-size_t esize(int dtype) { return dtype == DFLASH2_BF16 ? 2 : 4; }
+size_t esize(int dtype) { return dtype == DFLASH2_F32 ? 4 : 2; }
 bool valid_dtype(int dtype) { return dtype == DFLASH2_F32 || dtype == DFLASH2_BF16; }
+// The LM-head calls also take bf16 h with W in the packed tile layout.
+bool lmhead_dtype(int dtype) { return valid_dtype(dtype) || dtype == DFLASH2_BF16_PACKED; }
+size_t w_bytes(int V, int H, int dtype) {
+  return dtype == DFLASH2_BF16_PACKED ? lmhead_pack_bytes(V, H) : (size_t)V * H * esize(dtype);
+}
 
 // Byte ranges [a, a+na) and [b, b+nb) overlap.
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -94,7 +99,7 @@ DFLASH2_API int dflash2_twotap_conv_mm(const void* x, const void* anchor_h, void
 
 namespace {
 int check_lmhead(const void* h, const void* W, int M, int H, int V, int dtype) {
-  if (!valid_dtype(dtype) || M < 0 || H < 8 || H % 8 != 0 || V < kTopK) return DFLASH2_EINVAL;
+  if (!lmhead_dtype(dtype) || M < 0 || H < 8 || H % 8 != 0 || V < kTopK) return DFLASH2_EINVAL;
   if ((long long)M * V > (1LL << 40) || (long long)V * H > (1LL << 40)) return DFLASH2_EINVAL;
   if (M > 0 && (!h || !W || !aligned16(h) || !aligned16(W))) return DFLASH2_EINVAL;
   if (H > (1 << 21)) return DFLASH2_EUNSUPPORTED;  // 32-bit tile offsets
@@ -110,7 +115,7 @@ DFLASH2_API int dflash2_lmhead_logits(const void* h, const void* W, float* logit
   if (!logits || !aligned16(logits)) return DFLASH2_EINVAL;
   const size_t zb = (size_t)M * V * sizeof(float);
   if (overlap(logits, zb, h, (size_t)M * H * esize(dtype)) ||
-      overlap(logits, zb, W, (size_t)V * H * esize(dtype)))
+      overlap(logits, zb, W, w_bytes(V, H, dtype)))
     return DFLASH2_EINVAL;
   return status_of(launch_lmhead(h, W, logits, nullptr, M, H, V, dtype, as_stream(stream)));
 }
@@ -129,11 +134,25 @@ DFLASH2_API int dflash2_lmhead_logits_tilemax(const void* h, const void* W, floa
   const size_t zb = (size_t)M * V * sizeof(float);
   const size_t tb = tilemax_bytes(M, V);
   const size_t es = esize(dtype);
-  if (overlap(logits, zb, h, (size_t)M * H * es) || overlap(logits, zb, W, (size_t)V * H * es) ||
-      overlap(tilemax, tb, h, (size_t)M * H * es) || overlap(tilemax, tb, W, (size_t)V * H * es) ||
+  const size_t wb = w_bytes(V, H, dtype);
+  if (overlap(logits, zb, h, (size_t)M * H * es) || overlap(logits, zb, W, wb) ||
+      overlap(tilemax, tb, h, (size_t)M * H * es) || overlap(tilemax, tb, W, wb) ||
       overlap(tilemax, tb, logits, zb))
     return DFLASH2_EINVAL;
   return status_of(launch_lmhead(h, W, logits, tilemax, M, H, V, dtype, as_stream(stream)));
+}
+
+DFLASH2_API size_t dflash2_lmhead_pack_bytes(int V, int H) {
+  if (V < 1 || H < 8 || H % 8 != 0 || (long long)V * H > (1LL << 40) || H > (1 << 21)) return 0;
+  return lmhead_pack_bytes(V, H);
+}
+
+DFLASH2_API int dflash2_lmhead_pack(const void* W, void* Wp, int V, int H, void* stream) {
+  if (V < 1 || H < 8 || H % 8 != 0 || (long long)V * H > (1LL << 40)) return DFLASH2_EINVAL;
+  if (H > (1 << 21)) return DFLASH2_EUNSUPPORTED;
+  if (!W || !Wp || !aligned16(W) || !aligned16(Wp)) return DFLASH2_EINVAL;
+  if (overlap(W, (size_t)V * H * 2, Wp, lmhead_pack_bytes(V, H))) return DFLASH2_EINVAL;
+  return status_of(launch_lmhead_pack(W, Wp, V, H, as_stream(stream)));
 }
 
 DFLASH2_API int dflash2_topk16_tilemax(const float* logits, const float* tilemax, float* top_val,
@@ -190,7 +209,7 @@ DFLASH2_API int dflash2_topk16(const float* logits, float* top_val, int32_t* top
 // gives no logits buffer) the logits, each start 256-byte aligned.
 DFLASH2_API size_t dflash2_logits_topk_workspace(int M, int H, int V, int K, int dtype,
                                                  int logits_given) {
-  if (K != kTopK || M < 0 || V < kTopK || H < 8 || !valid_dtype(dtype)) return 0;
+  if (K != kTopK || M < 0 || V < kTopK || H < 8 || !lmhead_dtype(dtype)) return 0;
   size_t ws = (tilemax_bytes(M, V) + 255) & ~(size_t)255;
   if (!logits_given) ws += (size_t)M * V * sizeof(float);
   return ws;
@@ -215,7 +234,8 @@ DFLASH2_API int dflash2_logits_topk(const void* h, const void* W, float* logits,
   float* z = logits ? logits : reinterpret_cast<float*>(static_cast<char*>(workspace) + part);
   const size_t zb = (size_t)M * V * sizeof(float);
   const size_t es = esize(dtype);
-  if (overlap(z, zb, h, (size_t)M * H * es) || overlap(z, zb, W, (size_t)V * H * es) ||
+  const size_t wb = w_bytes(V, H, dtype);
+  if (overlap(z, zb, h, (size_t)M * H * es) || overlap(z, zb, W, wb) ||
       overlap(top_val, (size_t)M * kTopK * 4, z, zb) ||
       overlap(top_idx, (size_t)M * kTopK * 4, z, zb) ||
       (logits && need && overlap(workspace, need, logits, zb)))
@@ -223,7 +243,7 @@ DFLASH2_API int dflash2_logits_topk(const void* h, const void* W, float* logits,
   if (overlap(top_val, (size_t)M * kTopK * 4, workspace, need) ||
       overlap(top_idx, (size_t)M * kTopK * 4, workspace, need) ||
       overlap(workspace, need, h, (size_t)M * H * es) ||
-      overlap(workspace, need, W, (size_t)V * H * es))
+      overlap(workspace, need, W, wb))
     return DFLASH2_EINVAL;
   hipStream_t s = as_stream(stream);
   hipError_t e = launch_lmhead(h, W, z, tmax, M, H, V, dtype, s);

@@ -77,6 +77,9 @@ hipError_t launch_twotap_conv_mm(const void* x, const void* anchor_h, void* y, c
 // Columns per tile maximum (the bf16 GEMM's N tile).
 constexpr int kTileMaxCols = 256;
 
+// The LM-head weight in the GEMM's tiled layout (dtype code 2 of launch_lmhead).
+size_t lmhead_pack_bytes(int V, int H);
+hipError_t launch_lmhead_pack(const void* W, void* Wp, int V, int H, hipStream_t s);
 hipError_t launch_lmhead(const void* h, const void* W, float* logits, float* tmax, int M, int H,
                          int V, int dtype, hipStream_t s);
 

@@ -44,7 +44,9 @@ struct GemmCfg {
   static_assert((BN * kChunksPerRow) % kThreads == 0, "B load split");
 };
 
-template <int BM, int BN, int BK, int WM, int WN, bool KTAIL>
+// PACKED: W comes in the tiled layout of lmhead_pack_kernel (each 256-row x
+// 64-column block contiguous), so every slice of a W tile is one 32 KB run.
+template <int BM, int BN, int BK, int WM, int WN, bool KTAIL, bool PACKED>
 __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bw, float* __restrict__ C,
     float* __restrict__ tmax, int M, int N, int K, int mtiles, int ntiles) {
@@ -83,15 +85,22 @@ __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
   const int rowsB = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(A + (size_t)m0 * K), (short)0, rowsA * K * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Bw + (size_t)n0 * K), (short)0, rowsB * K * 2, 0x00020000);
+  const int nk = (K + BK - 1) / BK;  // K slices (the packed layout's blocks per tile)
+  const __amdgpu_buffer_rsrc_t rsB =
+      PACKED ? __builtin_amdgcn_make_buffer_rsrc(
+                   const_cast<uint16_t*>(Bw + (size_t)nt * nk * BN * BK), (short)0,
+                   nk * BN * BK * 2, 0x00020000)
+             : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Bw + (size_t)n0 * K),
+                                                 (short)0, rowsB * K * 2, 0x00020000);
   const int voff0 = (row0 * K + kof) * 2;
   const int vstep = kRowStep * K * 2;
+  // packed W: row r, chunk kof of slice s at ((s * BN + r) * BK + kof) * 2 bytes
+  const int voffB0 = PACKED ? (row0 * BK + kof) * 2 : voff0;
+  const int vstepB = PACKED ? kRowStep * BK * 2 : vstep;
   // Two register staging sets: the loads of slice c are issued while slice
   // c-3 is multiplied and written to LDS while slice c-1 is, so HBM latency
   // (first touch of a W row) has about two slices of MFMA work to hide under.
   // Slices past the end of K re-read the last slice (an L2 hit, never used).
-  const int nk = (K + BK - 1) / BK;
   const int klast = (nk - 1) * BK;
   u32x4_t R0[kLoads], R1[kLoads];
   auto gload = [&](u32x4_t(&R)[kLoads], int k0) {
@@ -101,8 +110,9 @@ __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
       const bool isA = i < Cfg::kAPer;
       const int ii = isA ? i : i - Cfg::kAPer;
       // the whole offset sits in the per-lane part so the range check covers it
-      u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(isA ? rsA : rsB,
-                                                         voff0 + ii * vstep + k0 * 2, 0, 0);
+      const int off = isA ? voff0 + ii * vstep + k0 * 2
+                          : voffB0 + ii * vstepB + (PACKED ? (k0 / BK) * (BN * BK * 2) : k0 * 2);
+      u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(isA ? rsA : rsB, off, 0, 0);
       if (KTAIL && k0 + kof >= K) v = u32x4_t{0, 0, 0, 0};
       R[i] = v;
     }
@@ -331,19 +341,44 @@ __global__ __launch_bounds__(256) void tilemax_kernel(const float* __restrict__ 
   if (lane == 0) tmax[w] = v;
 }
 
-template <int BM, int BN, int BK, int WM, int WN>
+template <int BM, int BN, int BK, int WM, int WN, bool PACKED>
 hipError_t launch_bf16(const uint16_t* h, const uint16_t* W, float* z, float* tmax, int M, int H,
                        int V, hipStream_t s) {
   static_assert(BN == kTileMaxCols, "tile maxima follow the N tiles");
   const int mt = (M + BM - 1) / BM;
   const int nt = (V + BN - 1) / BN;
   if (H % BK == 0)
-    hipLaunchKernelGGL((lmhead_bf16_kernel<BM, BN, BK, WM, WN, false>), dim3((unsigned)(mt * nt)),
-                       dim3(WM * WN * 64), 0, s, h, W, z, tmax, M, V, H, mt, nt);
+    hipLaunchKernelGGL((lmhead_bf16_kernel<BM, BN, BK, WM, WN, false, PACKED>),
+                       dim3((unsigned)(mt * nt)), dim3(WM * WN * 64), 0, s, h, W, z, tmax, M, V,
+                       H, mt, nt);
   else
-    hipLaunchKernelGGL((lmhead_bf16_kernel<BM, BN, BK, WM, WN, true>), dim3((unsigned)(mt * nt)),
-                       dim3(WM * WN * 64), 0, s, h, W, z, tmax, M, V, H, mt, nt);
+    hipLaunchKernelGGL((lmhead_bf16_kernel<BM, BN, BK, WM, WN, true, PACKED>),
+                       dim3((unsigned)(mt * nt)), dim3(WM * WN * 64), 0, s, h, W, z, tmax, M, V,
+                       H, mt, nt);
   return hipGetLastError();
+}
+
+// The packed W layout: [ceil(V / 256)][ceil(H / 64)][256][64] bf16, rows past
+// V and columns past H zero.  One thread per 16-byte run of the output.
+constexpr int kPackRows = 256;
+constexpr int kPackCols = 64;
+__global__ __launch_bounds__(256) void lmhead_pack_kernel(const uint16_t* __restrict__ W,
+                                                          uint16_t* __restrict__ Wp, int V, int H,
+                                                          long long runs) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= runs) return;
+  const int nkt = (H + kPackCols - 1) / kPackCols;
+  const int c8 = (int)(i % (kPackCols / 8));            // run within the 64 columns
+  const long long rb = i / (kPackCols / 8);              // (tile, slice, row)
+  const int r = (int)(rb % kPackRows);
+  const long long ts = rb / kPackRows;
+  const int slice = (int)(ts % nkt);
+  const long long tile = ts / nkt;
+  const long long n = tile * kPackRows + r;
+  const int k = slice * kPackCols + c8 * 8;
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (n < V && k < H) v = *reinterpret_cast<const u32x4_t*>(W + n * H + k);  // H % 8 == 0
+  *reinterpret_cast<u32x4_t*>(Wp + i * 8) = v;
 }
 
 }  // namespace
@@ -351,10 +386,12 @@ hipError_t launch_bf16(const uint16_t* h, const uint16_t* W, float* z, float* tm
 hipError_t launch_lmhead(const void* h, const void* W, float* logits, float* tmax, int M, int H,
                          int V, int dtype, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  if (dtype == 1) {
+  static_assert(kPackRows == 256 && kPackCols == 64, "the packed layout follows the bf16 tiles");
+  if (dtype == 1 || dtype == 2) {  // 2: W packed by launch_lmhead_pack
     const uint16_t* hb = static_cast<const uint16_t*>(h);
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
-    return launch_bf16<256, 256, 64, 2, 4>(hb, Wb, logits, tmax, M, H, V, s);
+    if (dtype == 2) return launch_bf16<256, 256, 64, 2, 4, true>(hb, Wb, logits, tmax, M, H, V, s);
+    return launch_bf16<256, 256, 64, 2, 4, false>(hb, Wb, logits, tmax, M, H, V, s);
   }
   const dim3 grid((unsigned)((V + 255) / 256), (unsigned)((M + 7) / 8));
   hipLaunchKernelGGL(lmhead_f32_kernel, grid, dim3(256), 0, s, static_cast<const float*>(h),
@@ -365,6 +402,19 @@ hipError_t launch_lmhead(const void* h, const void* W, float* logits, float* tma
   const long long waves = (long long)M * nt;
   hipLaunchKernelGGL(tilemax_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, logits, M,
                      V, nt, tmax);
+  return hipGetLastError();
+}
+
+size_t lmhead_pack_bytes(int V, int H) {
+  return (size_t)((V + kPackRows - 1) / kPackRows) * ((H + kPackCols - 1) / kPackCols) *
+         kPackRows * kPackCols * 2;
+}
+
+hipError_t launch_lmhead_pack(const void* W, void* Wp, int V, int H, hipStream_t s) {
+  const long long runs = (long long)(lmhead_pack_bytes(V, H) / 16);
+  if (runs == 0) return hipSuccess;
+  hipLaunchKernelGGL(lmhead_pack_kernel, dim3((unsigned)((runs + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(Wp), V, H, runs);
   return hipGetLastError();
 }
 

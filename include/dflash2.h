@@ -40,6 +40,8 @@
  *   - dtype selects the storage type of activations and weights:
  *     DFLASH2_F32 (fp32) or DFLASH2_BF16 (bf16).  Accumulation is fp32,
  *     except where a call states otherwise (the convs evaluate in fp64).
+ *     The LM-head calls also take DFLASH2_BF16_PACKED: bf16 h with W
+ *     re-laid out once by dflash2_lmhead_pack.
  */
 #ifndef DFLASH2_H
 #define DFLASH2_H
@@ -59,7 +61,11 @@ typedef enum {
   DFLASH2_EWORKSPACE = -4     /* workspace missing or smaller than queried */
 } dflash2_status;
 
-typedef enum { DFLASH2_F32 = 0, DFLASH2_BF16 = 1 } dflash2_dtype;
+typedef enum {
+  DFLASH2_F32 = 0,
+  DFLASH2_BF16 = 1,
+  DFLASH2_BF16_PACKED = 2 /* LM-head calls only: bf16 h, W from dflash2_lmhead_pack */
+} dflash2_dtype;
 
 /* Path walks of dflash2_path_select_mode. */
 typedef enum { DFLASH2_PATH_VITERBI = 0, DFLASH2_PATH_GREEDY = 1 } dflash2_path_mode;
@@ -124,10 +130,26 @@ int dflash2_twotap_conv_mm(const void* x, const void* anchor_h, void* y,
  * h [M, H] of dtype, W [V, H] of dtype (K-contiguous: "NT" product),
  * logits [M, V] fp32.  M >= 0, H >= 8 with H % 8 == 0, V >= 16; h, W, logits
  * 16-byte aligned.
- * bf16 operands run on the gfx950 bf16 matrix cores.
+ * bf16 operands run on the gfx950 bf16 matrix cores.  With
+ * DFLASH2_BF16_PACKED, W is the output of dflash2_lmhead_pack for the same
+ * V and H (dflash2_lmhead_pack_bytes bytes); the logits are bit for bit those
+ * of DFLASH2_BF16 with the unpacked W.
  */
 int dflash2_lmhead_logits(const void* h, const void* W, float* logits,
                           int M, int H, int V, int dtype, void* stream);
+
+/*
+ * The LM-head weight in the bf16 GEMM's tile layout, for the repeated calls
+ * of a decoding loop: W [V, H] bf16 row-major is copied to
+ *   Wp[ceil(V / 256)][ceil(H / 64)][256][64]   (rows past V, columns past H: 0)
+ * so every 256 x 64 slice the GEMM reads is one contiguous 32 KiB run (fewer
+ * DRAM page switches than 256 rows of 128 bytes at a stride of H).
+ * dflash2_lmhead_pack_bytes returns the size of Wp (0 for invalid V, H).
+ * dflash2_lmhead_pack: V >= 1, H >= 8 with H % 8 == 0, H <= 2^21; W and Wp
+ * 16-byte aligned, not overlapping.  Wp is fully written (padding included).
+ */
+size_t dflash2_lmhead_pack_bytes(int V, int H);
+int dflash2_lmhead_pack(const void* W, void* Wp, int V, int H, void* stream);
 
 /* Columns covered by one tile maximum (see dflash2_lmhead_logits_tilemax). */
 #define DFLASH2_TILEMAX_COLS 256

@@ -117,6 +117,40 @@ def test_lmhead_and_topk_validation():
                                  None, 0, None) == EWS                             # no room for logits
 
 
+def test_lmhead_pack_validation():
+    L = bd.lib()
+    nb = L.dflash2_lmhead_pack_bytes
+    assert nb(151936, 5120) == 594 * 80 * 256 * 64 * 2       # whole 256 x 64 blocks
+    assert nb(1, 8) == nb(256, 64) == 32768
+    assert nb(257, 72) == 2 * 2 * 32768
+    assert nb(0, 64) == 0 and nb(100, 60) == 0 and nb(100, 0) == 0
+    assert nb(1, (1 << 21) + 8) == 0                          # beyond 32-bit tile offsets
+    pk = L.dflash2_lmhead_pack
+    far = P + 0x10000000
+    assert pk(P, far, 0, 64, None) == EINVAL                  # V < 1
+    assert pk(P, far, 100, 60, None) == EINVAL                # H % 8
+    assert pk(None, far, 100, 64, None) == EINVAL
+    assert pk(P, None, 100, 64, None) == EINVAL
+    assert pk(P, far + 8, 100, 64, None) == EINVAL            # misaligned
+    assert pk(P, P + 8192, 100, 64, None) == EINVAL           # inside W (12800 bytes)
+    assert pk(P + 16384, P, 100, 64, None) == EINVAL          # W inside the 32 KiB of Wp
+    assert pk(P, far, 1, (1 << 21) + 8, None) == EUNSUP
+    # packed W spans whole blocks: a logits buffer past V * H * 2 bytes but
+    # inside the packed size overlaps it
+    z = Q + 16384
+    assert L.dflash2_lmhead_logits(P, Q, z, 8, 64, 100, 2, None) == EINVAL
+    assert L.dflash2_lmhead_logits_tilemax(P, Q, z, far, 8, 64, 100, 2, None) == EINVAL
+    assert L.dflash2_lmhead_logits(P, Q, far, 8, 64, 100, 3, None) == EINVAL   # unknown dtype
+    assert L.dflash2_lmhead_logits(P, Q, None, 0, 64, 100, 2, None) == 0
+    assert (L.dflash2_logits_topk_workspace(512, 5120, 151936, 16, 2, 0) ==
+            L.dflash2_logits_topk_workspace(512, 5120, 151936, 16, 1, 0))
+    assert L.dflash2_logits_topk(P, Q, z, far, far + 4096, 8, 64, 100, 16, 2, far + 65536,
+                                 1 << 20, None) == EINVAL
+    # the packed code belongs to the LM head only
+    assert L.dflash2_pair_score(P, P, None, P, P, 2, 4, 1000, 8, 2, P, P, None) == EINVAL
+    assert L.dflash2_context_gate(P, Q, far, 8, 64, 8, 2, None) == EINVAL
+
+
 def test_tilemax_validation():
     L = bd.lib()
     f = L.dflash2_lmhead_logits_tilemax

@@ -189,6 +189,78 @@ def test_lmhead_one_hot_and_dyadic_bit_exact():
     np.testing.assert_array_equal(got.cpu().numpy(), want)
 
 
+def _pack_ref(W):
+    """The packed LM-head layout written out with torch ops: W [V, H] zero-padded
+    to whole 256-row x 64-column blocks, blocks ordered (row tile, column
+    slice), each block row-major."""
+    V, H = W.shape
+    Vp, Hp = -(-V // 256) * 256, -(-H // 64) * 64
+    pad = torch.zeros((Vp, Hp), dtype=W.dtype, device=W.device)
+    pad[:V, :H] = W
+    return pad.view(Vp // 256, 256, Hp // 64, 64).permute(0, 2, 1, 3).contiguous().view(-1)
+
+
+@pytest.mark.parametrize("V,H", [(1, 8), (16, 64), (300, 136), (4099, 200), (1000, 5120)])
+def test_lmhead_pack_layout(V, H):
+    g = torch.Generator(device=DEV).manual_seed(V * 31 + H)
+    W = torch.randn((V, H), generator=g, device=DEV).to(torch.bfloat16)
+    n = bd.lib().dflash2_lmhead_pack_bytes(V, H)
+    assert n == 2 * _pack_ref(W).numel()
+    Wp = torch.full((n,), 0xA5, dtype=torch.uint8, device=DEV)   # padding must be overwritten
+    assert bd.lib().dflash2_lmhead_pack(W.data_ptr(), Wp.data_ptr(), V, H,
+                                        bd._stream(W.device)) == 0
+    assert torch.equal(Wp.view(torch.int16), _pack_ref(W).view(torch.int16))
+
+
+@pytest.mark.parametrize("M,H,V", [(1, 8, 16), (37, 64, 1000), (300, 136, 4099), (513, 520, 2048),
+                                   (257, 2560, 777)])
+def test_packed_lmhead_matches_row_major_and_oracle(M, H, V):
+    """Packing W changes only where the GEMM reads it from: logits, tile maxima
+    and top-16 are bit for bit those of the row-major W, and the logits meet the
+    oracle's bound."""
+    g = np.random.default_rng(M * 3 + H + V)
+    y = _bits_or_f32(g.standard_normal((M, H)).astype(np.float32), "bf16")
+    Wb = _bits_or_f32((g.standard_normal((V, H)) / np.sqrt(H)).astype(np.float32), "bf16")
+    h, W = to_dev(y, "bf16"), to_dev(Wb, "bf16")
+    Wp = bd.lmhead_pack(W)
+    z1, t1 = bd.lmhead_logits_tilemax(h, W)
+    z2, t2 = bd.lmhead_logits_tilemax(h, Wp)
+    assert torch.equal(z1.view(torch.int32), z2.view(torch.int32))
+    assert torch.equal(t1.view(torch.int32), t2.view(torch.int32))
+    assert torch.equal(bd.lmhead_logits(h, Wp).view(torch.int32), z1.view(torch.int32))
+    v1, i1 = bd.logits_topk(h, W)
+    v2, i2 = bd.logits_topk(h, Wp)
+    assert torch.equal(i1, i2) and torch.equal(v1.view(torch.int32), v2.view(torch.int32))
+    want = O.lm_logits(O.as_f64(y, "bf16"), Wb, "bf16").astype(np.float64)
+    got = z2.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - want) <= 1e-3 * np.maximum(np.abs(want), 1.0))
+
+
+def test_packed_lmhead_full_vocabulary():
+    """512 rows x hidden 5120 x vocabulary 151936 (a ragged last row tile):
+    packed and row-major W give the same logits and tile maxima, bit for bit."""
+    M, H, V = 512, 5120, 151936
+    g = torch.Generator(device=DEV).manual_seed(5)
+    h = torch.randn((M, H), generator=g, device=DEV).to(torch.bfloat16)
+    W = (torch.randn((V, H), generator=g, device=DEV) / H ** 0.5).to(torch.bfloat16)
+    Wp = bd.lmhead_pack(W)
+    z1, t1 = bd.lmhead_logits_tilemax(h, W)
+    z2, t2 = bd.lmhead_logits_tilemax(h, Wp)
+    assert torch.equal(z1.view(torch.int32), z2.view(torch.int32))
+    assert torch.equal(t1.view(torch.int32), t2.view(torch.int32))
+
+
+def test_packed_weight_checks_its_partner():
+    W = torch.zeros((100, 64), dtype=torch.bfloat16, device=DEV)
+    Wp = bd.lmhead_pack(W)
+    with pytest.raises(ValueError):
+        bd.lmhead_logits(torch.zeros((4, 72), dtype=torch.bfloat16, device=DEV), Wp)   # H differs
+    with pytest.raises(ValueError):
+        bd.lmhead_logits(torch.zeros((4, 64), dtype=torch.float32, device=DEV), Wp)    # fp32 h
+    with pytest.raises(TypeError):
+        bd.lmhead_pack(W.float())
+
+
 # ------------------------------------------------------------------ top-16
 def _topk_check(z):
     tv, ti = bd.topk16(torch.from_numpy(z).to(DEV))

@@ -453,6 +453,30 @@ def test_fused_step_matches_the_separate_calls(case):
         assert torch.equal(t, r)
 
 
+def test_step_with_packed_weight_matches(case):
+    """The step with the LM-head weight packed once (lmhead_pack) gives every
+    output of the step with the row-major weight, bit for bit."""
+    w, buf, dev = case["w"], case["buf"], case["dev"]
+    if w.dtype != "bf16":
+        pytest.skip("the packed layout is for bf16 weights")
+    kw = dict(Wg=dev["Wg"], walk=w.walk, temperature=w.temperature, u_path=dev.get("u_path"),
+              z_target=dev.get("z_target"), u_acc=dev.get("u_acc"), u_res=dev.get("u_res"))
+    tgt = None if w.temperature > 0 else to_dev(case["tgt"], "i32")
+    outs = (buf.logits, buf.top_val, buf.top_idx, buf.S0, buf.S, buf.path_slot, buf.path_tok,
+            buf.accept_len, buf.next_tok)
+    bd.run_step(buf, dev["x"], dev["convs"], dev["W"], dev["U"], dev["Vf"], dev["anchor_tok"],
+                tgt, **kw)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outs]
+    Wp = bd.lmhead_pack(dev["W"])
+    for t in outs:
+        t.fill_(-3)
+    bd.run_step(buf, dev["x"], dev["convs"], Wp, dev["U"], dev["Vf"], dev["anchor_tok"], tgt, **kw)
+    torch.cuda.synchronize()
+    for t, r in zip(outs, want):
+        assert torch.equal(t, r)
+
+
 def test_step_graph_replays_match_eager(case):
     """The whole step captured as a HIP graph (as the benchmark times it):
     every replay, with eager steps and synchronisations in between, gives the
@@ -465,8 +489,11 @@ def test_step_graph_replays_match_eager(case):
     # with targets, a walk that is not sampled runs the fused scores-walk-verify launch
     tgt = None if w.temperature > 0 else to_dev(case["tgt"], "i32")
 
+    # bf16 weights packed once, as the benchmark runs them
+    W = bd.lmhead_pack(dev["W"]) if w.dtype == "bf16" else dev["W"]
+
     def step():
-        bd.run_step(buf, dev["x"], dev["convs"], dev["W"], dev["U"], dev["Vf"], dev["anchor_tok"],
+        bd.run_step(buf, dev["x"], dev["convs"], W, dev["U"], dev["Vf"], dev["anchor_tok"],
                     tgt, **kw)
 
     outs = (buf.logits, buf.top_val, buf.top_idx, buf.S0, buf.S, buf.path_slot, buf.path_tok,
