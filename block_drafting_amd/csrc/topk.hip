@@ -310,30 +310,43 @@ __device__ __forceinline__ void merge_cands(WaveTop16& top, const uint64_t* cand
   top.refresh();
 }
 
+// ord_of(-inf), the lowest order of any element (NaN ranks here too).
+constexpr uint32_t kOrdNegInf = 0x007fffffu;
+
+// The loops below are written without per-lane branches: every load is
+// issued (indices clamped into the buffer, results masked), and a lane whose
+// element is not kept writes to its own spare LDS slot instead of skipping
+// the write.  Per-lane branches (one exec-mask branch per element) made the
+// selection and compaction steps several times slower.
 template <int VEC>
 __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restrict__ logits,
                                                            const float* __restrict__ tmax, int V,
                                                            int nt, float* __restrict__ top_val,
                                                            int32_t* __restrict__ top_idx) {
-  __shared__ uint64_t cand[kCandCap];
-  __shared__ int list[64 * kMaxChunk];
-  __shared__ uint32_t lord[64 * kMaxChunk];
+  constexpr int kList = 64 * kMaxChunk;
+  __shared__ uint64_t cand[kCandCap + 64];  // + one spare slot per lane
+  __shared__ int list[kList + 64];
+  __shared__ uint32_t lord[kList + 64];
   const int m = blockIdx.x;
   const int lane = threadIdx.x;
   const float* tm = tmax + (size_t)m * nt;
   const float* row = logits + (size_t)m * V;
-  // 1. tau from the lane maxima (all loads of a pass in flight at once)
-  uint32_t lmax = 0;  // ord of this lane's largest tile maximum (0: none)
-  float v[kMaxChunk];  // the last pass's maxima (all of them when nt <= 64 * kMaxChunk)
-  for (int c0 = 0; c0 < nt; c0 += 64 * kMaxChunk) {
+  // 1. tau from the lane maxima.  o = order of a tile maximum, 0 for a tile
+  // index past nt (every element's order is > 0).
+  uint32_t lmax = 0;
+  uint32_t o[kMaxChunk];  // the last pass's orders (all of them when nt <= kList)
+  auto load_orders = [&](int c0) {
+    float v[kMaxChunk];
 #pragma unroll
-    for (int k = 0; k < kMaxChunk; ++k) {
-      const int t = c0 + k * 64 + lane;
-      v[k] = t < nt ? tm[t] : -INFINITY;
-    }
+    for (int k = 0; k < kMaxChunk; ++k) v[k] = tm[min(c0 + k * 64 + lane, nt - 1)];
 #pragma unroll
     for (int k = 0; k < kMaxChunk; ++k)
-      if (c0 + k * 64 + lane < nt) lmax = max(lmax, ord_of(v[k]));
+      o[k] = ord_of(v[k]) & (0u - (uint32_t)(c0 + k * 64 + lane < nt));
+  };
+  for (int c0 = 0; c0 < nt; c0 += kList) {
+    load_orders(c0);
+#pragma unroll
+    for (int k = 0; k < kMaxChunk; ++k) lmax = max(lmax, o[k]);
   }
   const uint64_t srt = wave_sort_desc(((uint64_t)lmax << 32) | (uint32_t)(~lane));
   uint32_t tau = nt >= 16 ? (uint32_t)(readlane64(srt, 15) >> 32) : 0u;
@@ -341,43 +354,32 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
   WaveTop16 top;
   top.init();
   int ncand = 0;
-  for (int c0 = 0; c0 < nt; c0 += 64 * kMaxChunk) {
+  for (int c0 = 0; c0 < nt; c0 += kList) {
+    if (nt > kList) load_orders(c0);
+    const uint32_t tmin = max(tau, 1u);
     int nsel = 0;
-    float tv[kMaxChunk];
-    if (nt <= 64 * kMaxChunk) {
-#pragma unroll
-      for (int k = 0; k < kMaxChunk; ++k) tv[k] = v[k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < kMaxChunk; ++k) {
-        const int t = c0 + k * 64 + lane;
-        tv[k] = t < nt ? tm[t] : -INFINITY;
-      }
-    }
 #pragma unroll
     for (int k = 0; k < kMaxChunk; ++k) {
-      const int t = c0 + k * 64 + lane;
-      const bool s = t < nt && ord_of(tv[k]) >= tau;
+      const bool s = o[k] >= tmin;
       const uint64_t sel = __ballot(s);
-      if (s) {
-        const int at = nsel + lanes_below(sel);
-        list[at] = t;
-        lord[at] = ord_of(tv[k]);
-      }
+      const int below = lanes_below(sel);
+      const int at = below + (s ? nsel : kList + lane - below);
+      list[at] = c0 + k * 64 + lane;
+      lord[at] = o[k];
       nsel += __popcll(sel);
     }
     // Tighter bound: the 16th largest of the selected tiles' maxima (the 16
     // largest tile maxima are 16 distinct elements too).  Tiles below it are
     // dropped, usually leaving 16.
-    if (nt >= 16 && nt <= 64 * kMaxChunk && nsel > 16 && nsel <= 64) {
+    if (nt >= 16 && nt <= kList && nsel > 16 && nsel <= 64) {
       const int t = lane < nsel ? list[lane] : 0;
-      const uint32_t o = lane < nsel ? lord[lane] : 0u;
-      const uint64_t srt2 = wave_sort_desc(((uint64_t)o << 32) | (uint32_t)(~lane));
+      const uint32_t ot = lane < nsel ? lord[lane] : 0u;
+      const uint64_t srt2 = wave_sort_desc(((uint64_t)ot << 32) | (uint32_t)(~lane));
       tau = (uint32_t)(readlane64(srt2, 15) >> 32);
-      const bool s = lane < nsel && o >= tau;
+      const bool s = lane < nsel && ot >= tau;
       const uint64_t sel = __ballot(s);
       __builtin_amdgcn_wave_barrier();
-      if (s) list[lanes_below(sel)] = t;
+      list[s ? lanes_below(sel) : kList + lane] = t;
       __builtin_amdgcn_wave_barrier();
       nsel = __popcll(sel);
     }
@@ -387,27 +389,36 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
       int cbase[kPruneBatch];
 #pragma unroll
       for (int k = 0; k < kPruneBatch; ++k) {
-        const bool live = k < ns;
-        cbase[k] = (live ? list[b0 + k] : 0) * kTileMaxCols + lane * 4;
+        const int tl = k < ns ? list[b0 + k] : 0;  // b0 + k < kList + 64
+        cbase[k] = tl * kTileMaxCols + lane * 4;
         const int c = cbase[k];
-        if (VEC == 4 && live && c + 4 <= V) {
-          q[k] = *reinterpret_cast<const f32x4_t*>(row + c);
+        if (VEC == 4) {
+          q[k] = *reinterpret_cast<const f32x4_t*>(row + min(c, V - 4));  // V % 4 == 0
         } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) q[k][i] = (live && c + i < V) ? row[c + i] : -INFINITY;
+          for (int i = 0; i < 4; ++i) q[k][i] = row[min(c + i, V - 1)];
         }
       }
-      // every tile starts with room for its 256 keys (see the merge below)
+      // Keep x when ord_of(x) >= floor.  For x not NaN that is x >= the
+      // floor's value (ord_of maps -0 and +0 together, as IEEE compares
+      // them); NaN ranks as -inf, kept only when the floor is at most -inf.
       const uint32_t floor_ord = top.thr ? max(tau, (uint32_t)(top.thr >> 32)) : tau;
+      const bool nan_pass = floor_ord <= kOrdNegInf;
+      const float floor_f = nan_pass ? -INFINITY : val_of(floor_ord);
 #pragma unroll
       for (int k = 0; k < kPruneBatch; ++k) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int c = cbase[k] + i;
-          const bool p = k < ns && c < V && ord_of(q[k][i]) >= floor_ord;
+          const float x = q[k][i];
+          // bitwise operators: short-circuit forms compile to branches
+          const bool p = (k < ns) & (c < V) & ((x >= floor_f) | (nan_pass & (x != x)));
           const uint64_t pm = __ballot(p);
-          if (p) cand[ncand + lanes_below(pm)] = key_of(q[k][i], (uint32_t)c);
-          ncand += __popcll(pm);
+          if (pm) {
+            const int below = lanes_below(pm);
+            cand[below + (p ? ncand : kCandCap + lane - below)] = key_of(x, (uint32_t)c);
+            ncand += __popcll(pm);
+          }
         }
         if (ncand > kCandCap - 4 * 64) {  // keep the next tile's keys in range
           merge_cands(top, cand, ncand);
