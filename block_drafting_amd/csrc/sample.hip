@@ -27,6 +27,8 @@
 //
 // The sampling walk itself (sample_walk) lives in walk.hpp, shared with the
 // fused scores-and-walk kernel.
+#include <type_traits>
+
 #include "walk.hpp"
 
 namespace dflash2 {
@@ -140,6 +142,34 @@ __global__ __launch_bounds__(256) void target_lse_kernel(const float* __restrict
 }
 
 // ---------------------------------------------------------------- rejection verification
+// Wave reductions through DPP / ds_swizzle exchanges (xor_lane), several
+// times cheaper per step than a __shfl_xor (an LDS permute each).
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __uint_as_float(xor_lane<1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(xor_lane<2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(xor_lane<4>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(xor_lane<8>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(xor_lane<16>(__float_as_uint(v))));
+  return fmaxf(v, __uint_as_float(xor_lane<32>(__float_as_uint(v))));
+}
+
+// N independent wave sums (every lane ends with the totals), the N chains
+// interleaved.
+template <int N>
+__device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
+  auto step = [&](auto jtag) {
+    constexpr int J = decltype(jtag)::value;
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] += __uint_as_float(xor_lane<J>(__float_as_uint(v[k])));
+  };
+  step(std::integral_constant<int, 1>{});
+  step(std::integral_constant<int, 2>{});
+  step(std::integral_constant<int, 4>{});
+  step(std::integral_constant<int, 8>{});
+  step(std::integral_constant<int, 16>{});
+  step(std::integral_constant<int, 32>{});
+}
+
 constexpr int kTile = 256;      // tokens per tile: 64 lanes x 4
 constexpr int kTileBatch = 8;   // tiles a wave has in flight
 constexpr int kVerWaves = 16;   // 128 KB of the row in flight per workgroup
@@ -246,6 +276,7 @@ __device__ __forceinline__ void draw_token(float* tsum, int ntiles, const float*
   }
 }
 
+template <bool VEC>
 __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_kernel(
     const int32_t* __restrict__ path_slot, const int32_t* __restrict__ path_tok,
     const float* __restrict__ q, const int32_t* __restrict__ top_idx,
@@ -291,41 +322,36 @@ __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_kernel(
   const float s2 = inv_t * kLog2e;
   const float l2 = lse[zrow + n] * kLog2e;
   const int ntiles = (V + kTile - 1) / kTile;
-  const bool vec = (V & 3) == 0;
-  auto load4 = [&](int v0, float (&o)[4]) {
-    if (vec && v0 + 4 <= V) {
-      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(zr + v0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = x[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = v0 + i < V ? zr[v0 + i] : -__builtin_inff();
-    }
-  };
   // 2. tile sums of p (candidates corrected below): wave w takes
   //    kTileBatch consecutive tiles at a time (8w .. 8w+7, then 128 further
-  //    on), so each wave streams 8 KB runs of the row
+  //    on), so each wave streams 8 KB runs of the row.  All the batch's
+  //    loads go out before the first use (indices clamped into the row,
+  //    tokens past V masked).
   for (int t0 = wave * kTileBatch; t0 < ntiles; t0 += kVerWaves * kTileBatch) {
-    float zv[kTileBatch][4];
+    f32x4_t raw[kTileBatch];
 #pragma unroll
     for (int k = 0; k < kTileBatch; ++k) {
       const int v0 = (t0 + k) * kTile + lane * 4;
-      if (v0 < V) {
-        load4(v0, zv[k]);
+      if constexpr (VEC) {
+        raw[k] = *reinterpret_cast<const f32x4_t*>(zr + min(v0, V - 4));  // V % 4 == 0
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) zv[k][i] = -__builtin_inff();
+        for (int i = 0; i < 4; ++i) raw[k][i] = zr[min(v0 + i, V - 1)];
       }
     }
+    float acc[kTileBatch];
 #pragma unroll
     for (int k = 0; k < kTileBatch; ++k) {
-      float acc = 0.f;
+      acc[k] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc += exp2f(zv[k][i] * s2 - l2);  // -inf -> 0
+      for (int i = 0; i < 4; ++i)
+        if ((t0 + k) * kTile + lane * 4 + i < V) acc[k] += exp2f(raw[k][i] * s2 - l2);
+    }
+    wave_sum_n<kTileBatch>(acc);
+    if (lane == 0) {
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-      const int tl = t0 + k;
-      if (lane == 0 && tl < ntiles) tsum[tl] = acc;
+      for (int k = 0; k < kTileBatch; ++k)
+        if (t0 + k < ntiles) tsum[t0 + k] = acc[k];
     }
   }
   __syncthreads();
@@ -343,6 +369,7 @@ __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_kernel(
 // walk stops, the tile masses of the draw, so the stopping row is not read
 // again.  A block that stops at position n reads n + 1 rows instead of all
 // L + 1.  The accept rule and the draw are those of verify_rejection_kernel.
+template <bool VEC>
 __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_lazy_kernel(
     const int32_t* __restrict__ path_slot, const int32_t* __restrict__ path_tok,
     const float* __restrict__ q, const int32_t* __restrict__ top_idx,
@@ -377,7 +404,6 @@ __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_lazy_kernel(
     s_thr[tid] = ok ? u_acc[bt] * q[bt * kTopK + sl] : 0.f;
   }
   __syncthreads();
-  const bool vec = (V & 3) == 0;
   int n = L;
   for (int t = 0; t <= L; ++t) {
     const float* zr = z + (zrow + t) * V;
@@ -389,45 +415,50 @@ __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_lazy_kernel(
     // batch shares one reference maximum
     float Mw = kNeg, Sw = 0.f;
     for (int t0 = wave * kTileBatch; t0 < ntiles; t0 += kVerWaves * kTileBatch) {
-      float zv[kTileBatch][4];
+      // every load is issued (index clamped into the row, tokens past V
+      // masked to -inf): per-lane branches around the loads cost more
+      // All kTileBatch loads go out before the first use: a use between
+      // two loads (or a branch per load) makes each wait for the last.
+      f32x4_t raw[kTileBatch];
 #pragma unroll
       for (int k = 0; k < kTileBatch; ++k) {
         const int v0 = (t0 + k) * kTile + lane * 4;
-        if (vec && v0 + 4 <= V) {
-          const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(zr + v0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) zv[k][i] = xv[i];
+        if constexpr (VEC) {
+          raw[k] = *reinterpret_cast<const f32x4_t*>(zr + min(v0, V - 4));  // V % 4 == 0
         } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) zv[k][i] = v0 + i < V ? zr[v0 + i] : kNeg;
+          for (int i = 0; i < 4; ++i) raw[k][i] = zr[min(v0 + i, V - 1)];
         }
       }
+      float zv[kTileBatch][4];
       float bm = kNeg;
 #pragma unroll
       for (int k = 0; k < kTileBatch; ++k)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          zv[k][i] *= s2;
+          zv[k][i] = (t0 + k) * kTile + lane * 4 + i < V ? raw[k][i] * s2 : kNeg;
           bm = fmaxf(bm, zv[k][i]);
         }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o, 64));
-      float bs = 0.f;
+      bm = wave_max(bm);
+      const float ref = bm == kNeg ? 0.f : bm;  // an empty batch sums exp2(-inf) = 0
+      float acc[kTileBatch];
 #pragma unroll
       for (int k = 0; k < kTileBatch; ++k) {
-        float acc = 0.f;
-        if (bm != kNeg) {
+        acc[k] = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc += exp2f(zv[k][i] - bm);  // -inf -> 0
-        }
+        for (int i = 0; i < 4; ++i) acc[k] += exp2f(zv[k][i] - ref);
+      }
+      wave_sum_n<kTileBatch>(acc);
+      float bs = 0.f;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-        const int tl = t0 + k;
-        if (lane == 0 && tl < ntiles) {
-          tref[tl] = bm;
-          tsum[tl] = acc;
-        }
-        bs += acc;
+      for (int k = 0; k < kTileBatch; ++k) bs += acc[k];
+      if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < kTileBatch; ++k)
+          if (t0 + k < ntiles) {
+            tref[t0 + k] = bm;
+            tsum[t0 + k] = acc[k];
+          }
       }
       lse_merge(Mw, Sw, bm, bs);
     }
@@ -490,9 +521,15 @@ hipError_t launch_verify_rejection_lazy(const int32_t* path_slot, const int32_t*
                                         int B, int L, int V, int32_t* accept_len,
                                         int32_t* next_tok, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  hipLaunchKernelGGL(verify_rejection_lazy_kernel, dim3((unsigned)B), dim3(64 * kVerWaves),
-                     verify_rejection_lazy_lds(V), s, path_slot, path_tok, q, top_idx, z,
-                     kLog2e / temperature, u_acc, u_res, L, V, accept_len, next_tok);
+  // 16-byte loads when the rows are 16-byte aligned (z is, and V % 4 == 0)
+  if ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0)
+    hipLaunchKernelGGL(verify_rejection_lazy_kernel<true>, dim3((unsigned)B), dim3(64 * kVerWaves),
+                       verify_rejection_lazy_lds(V), s, path_slot, path_tok, q, top_idx, z,
+                       kLog2e / temperature, u_acc, u_res, L, V, accept_len, next_tok);
+  else
+    hipLaunchKernelGGL(verify_rejection_lazy_kernel<false>, dim3((unsigned)B), dim3(64 * kVerWaves),
+                       verify_rejection_lazy_lds(V), s, path_slot, path_tok, q, top_idx, z,
+                       kLog2e / temperature, u_acc, u_res, L, V, accept_len, next_tok);
   return hipGetLastError();
 }
 
@@ -506,9 +543,14 @@ hipError_t launch_verify_rejection(const int32_t* path_slot, const int32_t* path
                                    const float* u_res, int B, int L, int V, int32_t* accept_len,
                                    int32_t* next_tok, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  hipLaunchKernelGGL(verify_rejection_kernel, dim3((unsigned)B), dim3(64 * kVerWaves),
-                     verify_rejection_lds(V), s, path_slot, path_tok, q, top_idx, z, lse,
-                     1.0f / temperature, u_acc, u_res, L, V, accept_len, next_tok);
+  if ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0)
+    hipLaunchKernelGGL(verify_rejection_kernel<true>, dim3((unsigned)B), dim3(64 * kVerWaves),
+                       verify_rejection_lds(V), s, path_slot, path_tok, q, top_idx, z, lse,
+                       1.0f / temperature, u_acc, u_res, L, V, accept_len, next_tok);
+  else
+    hipLaunchKernelGGL(verify_rejection_kernel<false>, dim3((unsigned)B), dim3(64 * kVerWaves),
+                       verify_rejection_lds(V), s, path_slot, path_tok, q, top_idx, z, lse,
+                       1.0f / temperature, u_acc, u_res, L, V, accept_len, next_tok);
   return hipGetLastError();
 }
 
