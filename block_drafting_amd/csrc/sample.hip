@@ -170,6 +170,34 @@ __device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
   step(std::integral_constant<int, 32>{});
 }
 
+// Inclusive prefix sum across the wave in six DPP steps: row_shr 1, 2, 4,
+// 8 scan each 16-lane row (a lane with no source adds 0), then row_bcast 15
+// adds row 0's total to row 1 and row 2's to row 3, and row_bcast 31 adds
+// the total of rows 0-1 to rows 2 and 3.
+__device__ __forceinline__ float wave_scan_incl(float v) {
+  auto add = [&](auto ctag, auto mtag) {
+    constexpr int C = decltype(ctag)::value;
+    constexpr int R = decltype(mtag)::value;
+    v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), C, R, 0xf, false));
+  };
+  add(std::integral_constant<int, 0x111>{}, std::integral_constant<int, 0xf>{});  // row_shr:1
+  add(std::integral_constant<int, 0x112>{}, std::integral_constant<int, 0xf>{});  // row_shr:2
+  add(std::integral_constant<int, 0x114>{}, std::integral_constant<int, 0xf>{});  // row_shr:4
+  add(std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0xf>{});  // row_shr:8
+  add(std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xa>{});  // row_bcast:15
+  add(std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xc>{});  // row_bcast:31
+  return v;
+}
+
+__device__ __forceinline__ int wave_min_int(int v) {
+  v = min(v, (int)xor_lane<1>((uint32_t)v));
+  v = min(v, (int)xor_lane<2>((uint32_t)v));
+  v = min(v, (int)xor_lane<4>((uint32_t)v));
+  v = min(v, (int)xor_lane<8>((uint32_t)v));
+  v = min(v, (int)xor_lane<16>((uint32_t)v));
+  return min(v, (int)xor_lane<32>((uint32_t)v));
+}
+
 constexpr int kTile = 256;      // tokens per tile: 64 lanes x 4
 constexpr int kTileBatch = 8;   // tiles a wave has in flight
 constexpr int kVerWaves = 16;   // 128 KB of the row in flight per workgroup
@@ -216,25 +244,27 @@ __device__ __forceinline__ void draw_token(float* tsum, int ntiles, const float*
       if (lane == 0 && t >= 0) tsum[t] -= cv;
     }
   }
-  float carry = 0.f;
-  for (int c0 = 0; c0 < ntiles; c0 += 64) {
-    const int i = c0 + lane;
-    float c = i < ntiles ? fmaxf(tsum[i], 0.f) : 0.f;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float nb = __shfl_up(c, o, 64);
-      if (lane >= o) c += nb;
-    }
-    if (i < ntiles) tsum[i] = carry + c;
-    carry += __shfl(c, 63, 64);
-  }
+  // Inclusive prefix of the tile masses (negative corrections clamped to
+  // 0): lane l sums its own run of consecutive tiles, one wave scan adds the
+  // runs before it, and the lane writes its run's prefixes.  The first tile
+  // whose prefix passes u * total is the lowest one over all lanes.
+  __builtin_amdgcn_wave_barrier();
+  const int per = (ntiles + 63) / 64;
+  const int lo = min(lane * per, ntiles), hi = min(lo + per, ntiles);
+  float mine_t = 0.f;
+  for (int i = lo; i < hi; ++i) mine_t += fmaxf(tsum[i], 0.f);
+  const float incl_t = wave_scan_incl(mine_t);
+  const float carry = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(incl_t), 63));
   const float target = u * carry;
-  int k = 0x7fffffff;
-  for (int c0 = 0; c0 < ntiles && k == 0x7fffffff; c0 += 64) {
-    const int i = c0 + lane;
-    const uint64_t pass = __ballot(i < ntiles && tsum[i] > target);
-    if (pass) k = c0 + (int)__builtin_ctzll(pass);
+  float run_t = incl_t - mine_t;
+  int first = 0x7fffffff;
+  for (int i = lo; i < hi; ++i) {
+    run_t += fmaxf(tsum[i], 0.f);
+    tsum[i] = run_t;
+    if (first == 0x7fffffff && run_t > target) first = i;
   }
+  __builtin_amdgcn_wave_barrier();
+  int k = wave_min_int(first);
   if (k == 0x7fffffff) k = ntiles - 1;  // rounding: the last tile
   // 4. inside tile k: the first token whose running sum passes the target
   const float base = k > 0 ? tsum[k - 1] : 0.f;
@@ -250,12 +280,7 @@ __device__ __forceinline__ void draw_token(float* tsum, int ntiles, const float*
     r[i] = p;
   }
   const float mine = r[0] + r[1] + r[2] + r[3];
-  float c = mine;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float nb = __shfl_up(c, o, 64);
-    if (lane >= o) c += nb;
-  }
+  const float c = wave_scan_incl(mine);
   float run = base + (c - mine);
   int hit = 0x7fffffff;
   int lastv = -1;
@@ -265,11 +290,8 @@ __device__ __forceinline__ void draw_token(float* tsum, int ntiles, const float*
     if (hit == 0x7fffffff && r[i] > 0.f && run > target) hit = v0 + i;
     if (r[i] > 0.f) lastv = v0 + i;
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    hit = min(hit, __shfl_xor(hit, o, 64));
-    lastv = max(lastv, __shfl_xor(lastv, o, 64));
-  }
+  hit = wave_min_int(hit);
+  lastv = -wave_min_int(-lastv);
   if (lane == 0) {
     *accept_len = n + 1;
     *next_tok = hit != 0x7fffffff ? hit : lastv;  // rounding overshoot: last token with mass
