@@ -31,8 +31,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // Value of lane (lane ^ J) for 32-bit data.  Partners within a 16-lane row
 // use DPP (quad_perm; xor 4 = quad reverse after row_half_mirror; xor 8 =
-// row_half_mirror after row_mirror), xor 16 uses ds_swizzle (bit-mask mode),
-// xor 32 a ds_bpermute.
+// row_half_mirror after row_mirror); xor 16 and xor 32 use the gfx950 lane
+// swaps (v_permlane16_swap: odd rows of the first operand trade places with
+// even rows of the second; v_permlane32_swap: the upper half of the first
+// with the lower half of the second; with both operands v, a lane finds its
+// partner in the first result when it sits in the odd row / upper half,
+// else in the second).  All are VALU operations, no LDS traffic.
 template <int J>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
   if constexpr (J == 1) {
@@ -46,9 +50,12 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
     const uint32_t m = __builtin_amdgcn_update_dpp(0u, v, 0x140, 0xf, 0xf, false);
     return __builtin_amdgcn_update_dpp(0u, m, 0x141, 0xf, 0xf, false);
   } else if constexpr (J == 16) {
-    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
   } else {
-    return (uint32_t)__shfl_xor((int)v, 32, 64);
+    static_assert(J == 32, "xor partner 1, 2, 4, 8, 16 or 32");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
   }
 }
 

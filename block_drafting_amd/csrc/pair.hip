@@ -245,28 +245,31 @@ __global__ __launch_bounds__(64 * pwv_max_waves<RC>()) void pair_walk_verify_ker
   const int b = blockIdx.x;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
+  // wave 0 loads the targets now (lane t: target t, t <= min(L, 63)); they
+  // are in registers by the time the walk ends
+  int gt = 0;
+  if (wave == 0 && lane <= L) gt = target[(size_t)b * (L + 1) + lane];
   pair_phase<T, RC, VEC>(top_val, top_idx, anchor_tok, U, Vf, gate, b, L, V, r, sS, sS0, S0out,
                          Sout);
   __syncthreads();
   if (wave != 0) return;
+  int tok;
   if (GREEDY)
-    greedy_walk(sS0, sS, top_idx, b, L, path_slot, path_tok, path_score, sslot);
+    tok = greedy_walk(sS0, sS, top_idx, b, L, path_slot, path_tok, path_score, sslot);
   else
-    viterbi_walk<false>(sS0, sS, top_idx, b, L, sS0, reinterpret_cast<uint8_t*>(sS),
-                        kTopK * kTopK * (int)sizeof(float), path_slot, path_tok, path_score,
-                        sslot);
-  __builtin_amdgcn_wave_barrier();
+    tok = viterbi_walk<false>(sS0, sS, top_idx, b, L, sS0, reinterpret_cast<uint8_t*>(sS),
+                              kTopK * kTopK * (int)sizeof(float), path_slot, path_tok,
+                              path_score, sslot);
   // Greedy verification: accepted = the longest prefix of walked tokens equal
   // to the targets, plus the target after it.
-  const size_t row = (size_t)b * L;
-  const int32_t* g = target + (size_t)b * (L + 1);
-  bool miss = false;
-  if (lane < L) miss = top_idx[(row + lane) * kTopK + sslot[lane]] != g[lane];
-  const uint64_t mm = __ballot(miss);
+  const uint64_t mm = __ballot(lane < L && tok != gt);
   const int n = mm ? (int)__builtin_ctzll(mm) : L;
+  // the target after the accepted prefix; at n = 64 (L = 64, all accepted)
+  // it has no lane and is read from memory
+  const int gn = __builtin_amdgcn_readlane(gt, n & 63);
   if (lane == 0) {
     accept_len[b] = n + 1;
-    if (next_tok) next_tok[b] = g[n];
+    if (next_tok) next_tok[b] = n < 64 ? gn : target[(size_t)b * (L + 1) + n];
   }
 }
 

@@ -22,9 +22,10 @@ __global__ __launch_bounds__(64) void path_select_kernel(const float* __restrict
                                                          float* __restrict__ path_score) {
   __shared__ float delta[kTopK];
   __shared__ uint8_t back[64][kTopK];
+  __shared__ uint8_t sslot[kMaxWalk];
   const int b = blockIdx.x;
   viterbi_walk<true>(S0 + (size_t)b * kTopK, S + (size_t)b * (L - 1) * kTopK * kTopK, top_idx, b,
-                     L, delta, &back[1][0], kTopK, path_slot, path_tok, path_score, nullptr);
+                     L, delta, &back[1][0], kTopK, path_slot, path_tok, path_score, sslot);
 }
 
 // The greedy walk's next row depends on the last argmax, so the wave first

@@ -16,11 +16,69 @@ __device__ __forceinline__ void walk_better(float& bv, int& bi, float ov, int oi
   }
 }
 
+template <int J>
+__device__ __forceinline__ void walk_better_xor(float& bv, int& bi) {
+  walk_better(bv, bi, __uint_as_float(xor_lane<J>(__float_as_uint(bv))),
+              (int)xor_lane<J>((uint32_t)bi));
+}
+
 // Index-tracking max over one aligned group of 16 lanes (lowest slot on ties);
-// every lane of the group ends with the winner.
+// every lane of the group ends with the winner.  DPP exchanges.
 __device__ __forceinline__ void walk_argmax16(float& bv, int& bi) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) walk_better(bv, bi, __shfl_xor(bv, m, 64), __shfl_xor(bi, m, 64));
+  walk_better_xor<1>(bv, bi);
+  walk_better_xor<2>(bv, bi);
+  walk_better_xor<4>(bv, bi);
+  walk_better_xor<8>(bv, bi);
+}
+
+// Max / sum over one aligned group of 16 lanes, in the butterfly order
+// 1, 2, 4, 8 (DPP exchanges).
+__device__ __forceinline__ float group16_max(float v) {
+  v = fmaxf(v, __uint_as_float(xor_lane<1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(xor_lane<2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(xor_lane<4>(__float_as_uint(v))));
+  return fmaxf(v, __uint_as_float(xor_lane<8>(__float_as_uint(v))));
+}
+__device__ __forceinline__ float group16_sum(float v) {
+  v += __uint_as_float(xor_lane<1>(__float_as_uint(v)));
+  v += __uint_as_float(xor_lane<2>(__float_as_uint(v)));
+  v += __uint_as_float(xor_lane<4>(__float_as_uint(v)));
+  return v + __uint_as_float(xor_lane<8>(__float_as_uint(v)));
+}
+
+// Inclusive prefix sum within each group of 16 lanes (a DPP row): row_shr
+// 1, 2, 4, 8, a lane with no source adding nothing.
+__device__ __forceinline__ float group16_scan(float v) {
+  const int j = threadIdx.x & 15;
+  float n;
+  n = __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x111, 0xf, 0xf, false));
+  if (j >= 1) v += n;
+  n = __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x112, 0xf, 0xf, false));
+  if (j >= 2) v += n;
+  n = __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x114, 0xf, 0xf, false));
+  if (j >= 4) v += n;
+  n = __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x118, 0xf, 0xf, false));
+  if (j >= 8) v += n;
+  return v;
+}
+
+// Every walk ends the same way: lane t (t < L) holds the slot walked at
+// position t; it writes path_slot (and sslot when given) and looks up its
+// token, all positions at once (one memory round trip per block instead of
+// one per position).  Returns the token in lanes t < L, -1 elsewhere.
+__device__ __forceinline__ int walk_finish(int my_slot, const int32_t* top_idx, int b, int L,
+                                           int32_t* path_slot, int32_t* path_tok,
+                                           uint8_t* sslot) {
+  const int lane = threadIdx.x & 63;
+  int tok = -1;
+  if (lane < L) {
+    const size_t rt = (size_t)b * L + lane;
+    path_slot[rt] = my_slot;
+    if (sslot) sslot[lane] = (uint8_t)my_slot;
+    tok = top_idx[rt * kTopK + my_slot];
+    if (path_tok) path_tok[rt] = tok;
+  }
+  return tok;
 }
 
 // Orders the wave's LDS accesses around a step.  WG_SYNC: the workgroup is
@@ -44,13 +102,13 @@ __device__ __forceinline__ void walk_sync() {
 // block; delta [16] (which may be S0b itself) and the back-pointer rows are
 // this wave's LDS scratch: row t (t >= 1, 16 bytes) sits at back1 + (t-1) * bstride.
 // Row t is written after every score of step t-1 has been read, so the rows
-// may overwrite score blocks already walked (bstride = one block).  When
-// sslot is given, lane 0 also leaves the walked slots there.
+// may overwrite score blocks already walked (bstride = one block).  sslot
+// (LDS, L bytes) receives the walked slots.  Returns lane t's token (t < L).
 template <bool WG_SYNC>
-__device__ void viterbi_walk(const float* S0b, const float* Sb, const int32_t* top_idx, int b,
-                             int L, float* delta, uint8_t* back1, int bstride,
-                             int32_t* path_slot, int32_t* path_tok, float* path_score,
-                             uint8_t* sslot) {
+__device__ int viterbi_walk(const float* S0b, const float* Sb, const int32_t* top_idx, int b,
+                            int L, float* delta, uint8_t* back1, int bstride,
+                            int32_t* path_slot, int32_t* path_tok, float* path_score,
+                            uint8_t* sslot) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15;
   const int q = lane >> 4;
@@ -80,8 +138,8 @@ __device__ void viterbi_walk(const float* S0b, const float* Sb, const int32_t* t
         bi = q * 4 + ii;
       }
     }
-    walk_better(bv, bi, __shfl_xor(bv, 16, 64), __shfl_xor(bi, 16, 64));
-    walk_better(bv, bi, __shfl_xor(bv, 32, 64), __shfl_xor(bi, 32, 64));
+    walk_better_xor<16>(bv, bi);
+    walk_better_xor<32>(bv, bi);
     walk_sync<WG_SYNC>();
     if (q == 0) {
       delta[j] = bv;
@@ -101,48 +159,42 @@ __device__ void viterbi_walk(const float* S0b, const float* Sb, const int32_t* t
     path_score[b] = best;
     int slot = js;
     for (int t = L - 1; t >= 0; --t) {
-      path_slot[(size_t)b * L + t] = slot;
-      if (sslot) sslot[t] = (uint8_t)slot;
-      if (path_tok) path_tok[(size_t)b * L + t] = top_idx[((size_t)b * L + t) * kTopK + slot];
+      sslot[t] = (uint8_t)slot;
       if (t > 0) slot = back1[(t - 1) * bstride + slot];
     }
   }
+  walk_sync<WG_SYNC>();
+  const int my_slot = lane < L ? sslot[lane] : 0;
+  return walk_finish(my_slot, top_idx, b, L, path_slot, path_tok, nullptr);
 }
 
 // Best-successor walk, the post's own decoder: p_0 = argmax S0, then
 // p_t = argmax_j S[t-1, p_{t-1}, j], lowest slot on ties; the score is the fp32
 // running sum along the walk.  sS: this block's scores in LDS.  Lanes
 // j = lane & 15 hold candidate j; the four quarters of the wave walk the same
-// block.  When sslot is given, lane 0 also leaves the walked slots there.
-__device__ __forceinline__ void greedy_walk(const float* S0b, const float* sS,
-                                            const int32_t* top_idx, int b, int L,
-                                            int32_t* path_slot, int32_t* path_tok,
-                                            float* path_score, uint8_t* sslot) {
+// block.  When sslot is given, the walked slots are left there.  Returns
+// lane t's token (t < L).
+__device__ __forceinline__ int greedy_walk(const float* S0b, const float* sS,
+                                           const int32_t* top_idx, int b, int L,
+                                           int32_t* path_slot, int32_t* path_tok,
+                                           float* path_score, uint8_t* sslot) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15;
   float bv = S0b[j];
   int p = j;
   walk_argmax16(bv, p);
   float score = bv;
-  const size_t row = (size_t)b * L;
-  if (lane == 0) {
-    path_slot[row] = p;
-    if (sslot) sslot[0] = (uint8_t)p;
-    if (path_tok) path_tok[row] = top_idx[row * kTopK + p];
-  }
+  int my_slot = p;  // lane t keeps the slot of position t
   for (int t = 1; t < L; ++t) {
     bv = sS[((t - 1) * kTopK + p) * kTopK + j];
     int bi = j;
     walk_argmax16(bv, bi);
     score = score + bv;
     p = bi;
-    if (lane == 0) {
-      path_slot[row + t] = p;
-      if (sslot) sslot[t] = (uint8_t)p;
-      if (path_tok) path_tok[row + t] = top_idx[(row + t) * kTopK + p];
-    }
+    if (lane == t) my_slot = p;
   }
   if (lane == 0) path_score[b] = score;
+  return walk_finish(my_slot, top_idx, b, L, path_slot, path_tok, sslot);
 }
 
 // Sampling walk at temperature T = 1 / inv_t, the sampling twin of the greedy
@@ -150,32 +202,25 @@ __device__ __forceinline__ void greedy_walk(const float* S0b, const float* sS,
 // the slot drawn before, by inverse CDF in slot order with the uniform u[t].
 // s: this lane's S0 value (candidate j = lane & 15); sS: this block's scores
 // in LDS; u [L]: this block's uniforms; q receives every position's proposal.
-__device__ __forceinline__ void sample_walk(float s, const float* sS, const int32_t* top_idx,
-                                            const float* u, float inv_t, int b, int L,
-                                            int32_t* path_slot, int32_t* path_tok, float* q) {
+__device__ __forceinline__ int sample_walk(float s, const float* sS, const int32_t* top_idx,
+                                           const float* u, float inv_t, int b, int L,
+                                           int32_t* path_slot, int32_t* path_tok, float* q) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15;
   const size_t row = (size_t)b * L;
+  const float my_u = lane < L ? u[lane] : 0.f;  // the uniforms, one per lane, loaded up front
   int p = 0;
+  int my_slot = 0;  // lane t keeps the slot of position t
   for (int t = 0; t < L; ++t) {
     if (t > 0) s = sS[((t - 1) * kTopK + p) * kTopK + j];
     // softmax over the 16 lanes of each quarter (all four quarters agree)
-    float m = s;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float m = group16_max(s);
     const float e = expf((s - m) * inv_t);
-    float z = e;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
+    const float z = group16_sum(e);
     const float qj = e / z;
     // inclusive prefix sum in slot order
-    float c = qj;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const float n = __shfl_up(c, o, 16);
-      if (j >= o) c += n;
-    }
-    const float ut = u[t];
+    const float c = group16_scan(qj);
+    const float ut = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_u), t));
     // first slot with u < c_j = number of slots with c_j <= u; rounding can
     // leave u above every c_j: then the last slot with q > 0
     const uint64_t le = __ballot(c <= ut) & 0xffffull;
@@ -184,11 +229,9 @@ __device__ __forceinline__ void sample_walk(float s, const float* sS, const int3
     const int last = pos ? 63 - __clzll(pos) : 0;  // no finite score: slot 0 (q is NaN)
     p = min(first, last);
     if (lane < kTopK) q[(row + t) * kTopK + j] = qj;
-    if (lane == 0) {
-      path_slot[row + t] = p;
-      if (path_tok) path_tok[row + t] = top_idx[(row + t) * kTopK + p];
-    }
+    if (lane == t) my_slot = p;
   }
+  return walk_finish(my_slot, top_idx, b, L, path_slot, path_tok, nullptr);
 }
 
 }  // namespace dflash2
