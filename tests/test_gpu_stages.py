@@ -345,6 +345,12 @@ def test_topk_tilemax_ties_zeros_nan_inf():
     z[5, :] = -np.inf
     z[5, 4242] = -1.0
     _topk_tilemax_check(z)
+    # rows whose every tile maximum is -inf: the bound sits at -inf, so NaN
+    # (ranked as -inf) must pass the filter too
+    z = np.full((3, 1000), np.nan, np.float32)
+    z[1, :] = -np.inf
+    z[2, ::2] = -np.inf                              # NaN and -inf mixed
+    _topk_tilemax_check(z)
     # top values spread over 16 different tiles vs packed in one
     z = np.zeros((2, 151936), np.float32)
     z[0, np.arange(16) * 9000] = 5.0
@@ -860,6 +866,33 @@ def test_fused_pair_walk_verify_against_the_oracle():
     ga, gn = O.verify_greedy(gt, tgt)
     np.testing.assert_array_equal(out[3].cpu().numpy(), ga)
     np.testing.assert_array_equal(out[4].cpu().numpy(), gn)
+
+
+@pytest.mark.parametrize("mode", ["viterbi", "greedy"])
+def test_fused_verify_at_the_longest_block(mode):
+    """L = 64, the longest walk: first mismatch at 0, 1, 62, 63, and no
+    mismatch at all (the bonus target then sits past the last lane of the
+    wave and comes from memory), checked against the oracle's rule."""
+    B, L, V, r, dt = 5, 64, 3000, 16, "bf16"
+    tv, ti, at, U, Vf = _pair_case(B, L, V, r, dt, seed=64)
+    d = [torch.from_numpy(tv).to(DEV), torch.from_numpy(ti).to(DEV), torch.from_numpy(at).to(DEV),
+         to_dev(U, dt), to_dev(Vf, dt)]
+    probe = bd.pair_select_verify(*d, torch.zeros((B, L + 1), dtype=torch.int32, device=DEV),
+                                  None, mode)
+    tok = probe[1].cpu().numpy()
+    g = np.random.default_rng(9)
+    tgt = np.empty((B, L + 1), np.int32)
+    tgt[:, :L] = tok
+    tgt[:, L] = g.integers(0, V, B)                    # the bonus token
+    for b, cut in enumerate([0, 1, 62, 63, None]):
+        if cut is not None:
+            tgt[b, cut] = (tok[b, cut] + 1) % V        # first mismatch at `cut`
+    out = bd.pair_select_verify(*d, torch.from_numpy(tgt).to(DEV), None, mode)
+    wa, wn = O.verify_greedy(tok, tgt)
+    np.testing.assert_array_equal(out[3].cpu().numpy(), wa)
+    np.testing.assert_array_equal(out[4].cpu().numpy(), wn)
+    np.testing.assert_array_equal(wa, [1, 2, 63, 64, 65])
+    assert wn[4] == tgt[4, L]
 
 
 def test_fused_pair_walk_verify_empty_batch():
