@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void target_lse_kernel(const float* __restrict
 }
 
 // ---------------------------------------------------------------- rejection verification
-// Wave reductions through DPP / ds_swizzle exchanges (xor_lane), several
+// Wave reductions through DPP / lane-swap exchanges (xor_lane), several
 // times cheaper per step than a __shfl_xor (an LDS permute each).
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, __uint_as_float(xor_lane<1>(__float_as_uint(v))));
