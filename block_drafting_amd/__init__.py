@@ -158,6 +158,19 @@ def _shape(t: torch.Tensor, shape, name: str, dtype=None):
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
 
 
+def _opt(t: Optional[torch.Tensor], shape, name: str, dtype=None):
+    """_shape for a tensor the caller may leave out (None)."""
+    if t is not None:
+        _shape(t, shape, name, dtype)
+
+
+def _rank(t: torch.Tensor, nd: int, name: str, dtype=None):
+    if t.dim() != nd:
+        raise ValueError(f"{name}: expected {nd} dimensions, got shape {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
 # ---------------------------------------------------------------- stages
 def twotap_conv(x: torch.Tensor, k0: torch.Tensor, k1: torch.Tensor,
                 anchor_h: Optional[torch.Tensor] = None, proj: Optional[torch.Tensor] = None,
@@ -279,8 +292,11 @@ def lmhead_logits_tilemax(h: torch.Tensor, W, out: Optional[torch.Tensor] = None
 
 def topk16_tilemax(logits: torch.Tensor, tilemax: torch.Tensor, top_val=None, top_idx=None):
     """Top-16 of logits [M, V] that reads only the tiles its maxima allow."""
+    _rank(logits, 2, "logits", torch.float32)
     M, V = logits.shape
     _shape(tilemax, (M, (V + TILEMAX_COLS - 1) // TILEMAX_COLS), "tilemax", torch.float32)
+    _opt(top_val, (M, TOPK), "top_val", torch.float32)
+    _opt(top_idx, (M, TOPK), "top_idx", torch.int32)
     dev = logits.device
     if top_val is None:
         top_val = torch.empty((M, TOPK), dtype=torch.float32, device=dev)
@@ -310,9 +326,8 @@ def topk16(logits: torch.Tensor, top_val: Optional[torch.Tensor] = None,
            top_idx: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per-row top-16 (value desc, id asc) of fp32 logits [M, V]."""
+    _rank(logits, 2, "logits", torch.float32)
     M, V = logits.shape
-    if logits.dtype != torch.float32:
-        raise TypeError("logits must be fp32")
     dev = logits.device
     if top_val is None:
         top_val = torch.empty((M, TOPK), dtype=torch.float32, device=dev)
@@ -339,11 +354,13 @@ def logits_topk(h: torch.Tensor, W, logits: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None):
     """LM-head logits (into `logits` when given, else into the workspace) and
     the per-row top-16.  Returns (top_val, top_idx)."""
+    _rank(h, 2, "h")
     M, H = h.shape
     wp, V, code, wt = _weight(W, h)
     dev = h.device
-    if logits is not None:
-        _shape(logits, (M, V), "logits", torch.float32)
+    _opt(logits, (M, V), "logits", torch.float32)
+    _opt(top_val, (M, TOPK), "top_val", torch.float32)
+    _opt(top_idx, (M, TOPK), "top_idx", torch.int32)
     if top_val is None:
         top_val = torch.empty((M, TOPK), dtype=torch.float32, device=dev)
     if top_idx is None:
@@ -376,8 +393,11 @@ def pair_score(top_val: torch.Tensor, top_idx: torch.Tensor, anchor_tok: Optiona
                S: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None):
     """S0 [B, 16], S [B, L-1, 16, 16] from candidates [B, L, 16] and factors
     [V, r]; with `gate` ([B, L, r] or [B*L, r] fp32) the gated scores."""
+    _rank(top_val, 3, "top_val", torch.float32)
+    _rank(U, 2, "U")
     B, L, K = top_val.shape
     V, r = U.shape
+    _shape(top_val, (B, L, TOPK), "top_val", torch.float32)
     _shape(top_idx, (B, L, K), "top_idx", torch.int32)
     _shape(Vf, (V, r), "Vf", U.dtype)
     if anchor_tok is not None:
@@ -411,11 +431,22 @@ def path_select(S0: torch.Tensor, S: Optional[torch.Tensor], top_idx: Optional[t
     Returns (path_slot, path_tok, path_score)."""
     if mode not in PATH_MODES:
         raise ValueError(f"mode must be one of {sorted(PATH_MODES)}, got {mode!r}")
+    _rank(S0, 2, "S0", torch.float32)
     B = S0.shape[0]
     if top_idx is not None:
+        _rank(top_idx, 3, "top_idx", torch.int32)
         L = top_idx.shape[1]
     else:
         L = 1 if S is None else S.shape[1] + 1
+    _shape(S0, (B, TOPK), "S0", torch.float32)
+    _opt(top_idx, (B, L, TOPK), "top_idx", torch.int32)
+    if L > 1:
+        if S is None:
+            raise ValueError("S: the scores are needed for L > 1")
+        _shape(S, (B, L - 1, TOPK, TOPK), "S", torch.float32)
+    _opt(path_slot, (B, L), "path_slot", torch.int32)
+    _opt(path_tok, (B, L), "path_tok", torch.int32)
+    _opt(path_score, (B,), "path_score", torch.float32)
     dev = S0.device
     if path_slot is None:
         path_slot = torch.empty((B, L), dtype=torch.int32, device=dev)
@@ -432,8 +463,11 @@ def path_select(S0: torch.Tensor, S: Optional[torch.Tensor], top_idx: Optional[t
 
 def verify_greedy(path_tok: torch.Tensor, target: torch.Tensor, accept_len=None, next_tok=None):
     """Greedy verification: (accept_len [B], next_tok [B])."""
+    _rank(path_tok, 2, "path_tok", torch.int32)
     B, L = path_tok.shape
     _shape(target, (B, L + 1), "target", torch.int32)
+    _opt(accept_len, (B,), "accept_len", torch.int32)
+    _opt(next_tok, (B,), "next_tok", torch.int32)
     dev = path_tok.device
     if accept_len is None:
         accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -456,11 +490,19 @@ def pair_select_verify(top_val: torch.Tensor, top_idx: torch.Tensor,
     path_tok, path_score, accept_len, next_tok)."""
     if mode not in PATH_MODES:
         raise ValueError(f"mode must be one of {sorted(PATH_MODES)}, got {mode!r}")
+    _rank(top_val, 3, "top_val", torch.float32)
+    _rank(U, 2, "U")
     B, L, K = top_val.shape
     V, r = U.shape
+    _shape(top_val, (B, L, TOPK), "top_val", torch.float32)
     _shape(top_idx, (B, L, K), "top_idx", torch.int32)
     _shape(Vf, (V, r), "Vf", U.dtype)
     _shape(target, (B, L + 1), "target", torch.int32)
+    _opt(path_slot, (B, L), "path_slot", torch.int32)
+    _opt(path_tok, (B, L), "path_tok", torch.int32)
+    _opt(path_score, (B,), "path_score", torch.float32)
+    _opt(accept_len, (B,), "accept_len", torch.int32)
+    _opt(next_tok, (B,), "next_tok", torch.int32)
     if anchor_tok is not None:
         _shape(anchor_tok, (B,), "anchor_tok", torch.int32)
     if gate is not None:
@@ -498,11 +540,17 @@ def pair_sample(top_val: torch.Tensor, top_idx: torch.Tensor, anchor_tok: Option
                 S: Optional[torch.Tensor] = None, path_slot=None, path_tok=None, q=None):
     """pair_score and path_sample in one launch.  The scores are written to
     S0 / S only when those are given.  Returns (path_slot, path_tok, q)."""
+    _rank(top_val, 3, "top_val", torch.float32)
+    _rank(U, 2, "U")
     B, L, K = top_val.shape
     V, r = U.shape
+    _shape(top_val, (B, L, TOPK), "top_val", torch.float32)
     _shape(top_idx, (B, L, K), "top_idx", torch.int32)
     _shape(Vf, (V, r), "Vf", U.dtype)
     _shape(u, (B, L), "u", torch.float32)
+    _opt(path_slot, (B, L), "path_slot", torch.int32)
+    _opt(path_tok, (B, L), "path_tok", torch.int32)
+    _opt(q, (B, L, TOPK), "q", torch.float32)
     if anchor_tok is not None:
         _shape(anchor_tok, (B,), "anchor_tok", torch.int32)
     if gate is not None:
@@ -532,9 +580,20 @@ def path_sample(S0: torch.Tensor, S: Optional[torch.Tensor], top_idx: Optional[t
                 u: torch.Tensor, temperature: float, path_slot=None, path_tok=None, q=None):
     """Sampling walk at temperature T with uniforms u [B, L].
     Returns (path_slot, path_tok, q [B, L, 16])."""
+    _rank(S0, 2, "S0", torch.float32)
+    _rank(u, 2, "u", torch.float32)
     B = S0.shape[0]
     L = u.shape[1]
+    _shape(S0, (B, TOPK), "S0", torch.float32)
     _shape(u, (B, L), "u", torch.float32)
+    if L > 1:
+        if S is None:
+            raise ValueError("S: the scores are needed for L > 1")
+        _shape(S, (B, L - 1, TOPK, TOPK), "S", torch.float32)
+    _opt(top_idx, (B, L, TOPK), "top_idx", torch.int32)
+    _opt(path_slot, (B, L), "path_slot", torch.int32)
+    _opt(path_tok, (B, L), "path_tok", torch.int32)
+    _opt(q, (B, L, TOPK), "q", torch.float32)
     dev = S0.device
     if path_slot is None:
         path_slot = torch.empty((B, L), dtype=torch.int32, device=dev)
@@ -551,6 +610,8 @@ def path_sample(S0: torch.Tensor, S: Optional[torch.Tensor], top_idx: Optional[t
 
 def target_lse(z: torch.Tensor, temperature: float, out: Optional[torch.Tensor] = None):
     """log sum exp(z / T) over the last axis of fp32 target logits."""
+    if z.dtype != torch.float32 or z.dim() < 1:
+        raise TypeError(f"z: expected fp32 logits, got {z.dtype} of shape {tuple(z.shape)}")
     V = z.shape[-1]
     R = z.numel() // V
     if out is None:
@@ -568,6 +629,7 @@ def verify_rejection(path_slot: torch.Tensor, path_tok: torch.Tensor, q: torch.T
                      temperature: float, u_acc: torch.Tensor, u_res: torch.Tensor,
                      accept_len=None, next_tok=None):
     """Speculative-sampling verification: (accept_len [B], next_tok [B])."""
+    _rank(path_tok, 2, "path_tok", torch.int32)
     B, L = path_tok.shape
     V = z.shape[-1]
     _shape(path_slot, (B, L), "path_slot", torch.int32)
@@ -577,6 +639,8 @@ def verify_rejection(path_slot: torch.Tensor, path_tok: torch.Tensor, q: torch.T
     _shape(lse, (B, L + 1), "lse", torch.float32)
     _shape(u_acc, (B, L), "u_acc", torch.float32)
     _shape(u_res, (B,), "u_res", torch.float32)
+    _opt(accept_len, (B,), "accept_len", torch.int32)
+    _opt(next_tok, (B,), "next_tok", torch.int32)
     dev = path_tok.device
     if accept_len is None:
         accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -596,6 +660,7 @@ def verify_rejection_lazy(path_slot: torch.Tensor, path_tok: torch.Tensor, q: to
                           next_tok=None):
     """verify_rejection that computes each row's log-sum-exp itself, only for
     the rows the accept test reaches: (accept_len [B], next_tok [B])."""
+    _rank(path_tok, 2, "path_tok", torch.int32)
     B, L = path_tok.shape
     V = z.shape[-1]
     _shape(path_slot, (B, L), "path_slot", torch.int32)
@@ -604,6 +669,8 @@ def verify_rejection_lazy(path_slot: torch.Tensor, path_tok: torch.Tensor, q: to
     _shape(z, (B, L + 1, V), "z", torch.float32)
     _shape(u_acc, (B, L), "u_acc", torch.float32)
     _shape(u_res, (B,), "u_res", torch.float32)
+    _opt(accept_len, (B,), "accept_len", torch.int32)
+    _opt(next_tok, (B,), "next_tok", torch.int32)
     dev = path_tok.device
     if accept_len is None:
         accept_len = torch.empty((B,), dtype=torch.int32, device=dev)

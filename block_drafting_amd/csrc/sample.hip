@@ -202,27 +202,78 @@ constexpr int kTile = 256;      // tokens per tile: 64 lanes x 4
 constexpr int kTileBatch = 8;   // tiles a wave has in flight
 constexpr int kVerWaves = 16;   // 128 KB of the row in flight per workgroup
 
+// Masses of the four tokens v0 .. v0+3 of the drawn row (0 past V):
+// p(v) = 2^(zr[v] * s2 - l2), less the candidate's q at the rejected
+// position (resid), clamped at 0.  praw gets p itself.
+__device__ __forceinline__ void token_masses(const float* __restrict__ zr, int V, float s2,
+                                             float l2, bool resid, const int32_t* cand_id,
+                                             const float* cand_q, int v0, float (&r)[4],
+                                             float (&praw)[4]) {
+  float zv[4];
+  if ((V & 3) == 0 && v0 + 4 <= V) {
+    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(zr + v0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zv[i] = x[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zv[i] = v0 + i < V ? zr[v0 + i] : -__builtin_inff();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p = v0 + i < V ? exp2f(zv[i] * s2 - l2) : 0.f;
+    float m = p;
+    if (resid) {
+#pragma unroll
+      for (int c = 0; c < kTopK; ++c)
+        if (cand_id[c] == v0 + i) m = fmaxf(m - cand_q[c], 0.f);
+    }
+    r[i] = m;
+    praw[i] = p;
+  }
+}
+
+// Fallback of the draw when the tile it chose holds no token with mass (the
+// prefix overshot every tile, u within rounding of 1, or the chosen tile's
+// sum was rounding residue): the last token with mass, searching the tiles
+// below `k` from the top down, then the tiles above it; if no tile has one,
+// the last token with p > 0 of the first tile that has any, starting with
+// tile k's (lastp, -1 if none); if none, V - 1.  After an overshoot k is the
+// last tile, so these are the last tokens of the row with residual mass and
+// with p > 0.  At most ntiles - 1 tile passes; rare, so kept out of line.
+__device__ __attribute__((noinline)) int draw_fallback(const float* __restrict__ zr, int V,
+                                                       float s2, float l2, bool resid,
+                                                       const int32_t* cand_id,
+                                                       const float* cand_q, int k, int ntiles,
+                                                       int lastp, int lane) {
+  for (int step = 1; step < ntiles; ++step) {
+    const int t = k - step >= 0 ? k - step : k - step + ntiles;  // k-1, ..., 0, ntiles-1, ..., k+1
+    const int v0 = t * kTile + lane * 4;
+    float r[4], pr[4];
+    token_masses(zr, V, s2, l2, resid, cand_id, cand_q, v0, r, pr);
+    int lr = -1, lp = -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (r[i] > 0.f) lr = v0 + i;
+      if (pr[i] > 0.f) lp = v0 + i;
+    }
+    lr = -wave_min_int(-lr);
+    lp = -wave_min_int(-lp);
+    if (lastp < 0) lastp = lp;
+    if (lr >= 0) return lr;
+  }
+  return lastp >= 0 ? lastp : V - 1;
+}
+
 // Steps 3-4 of the draw, run by one wave: the candidates' residual
 // corrections -min(p, q) into their tiles (in slot order), the inclusive
 // prefix of the tile sums in token order, 64 at a time, the first tile whose
 // prefix passes u * total, then the first token inside it whose running sum
 // passes.  tsum [ntiles] holds each 256-token tile's mass of p; zr is the
 // drawn row, p(v) = 2^(zr[v] * s2 - l2).  Writes accept_len = n + 1 and the
-// token.
+// token, always an id in [0, V).
 __device__ __forceinline__ void draw_token(float* tsum, int ntiles, const float* __restrict__ zr, int V, float s2,
                            float l2, bool resid, const int32_t* cand_id, const float* cand_q,
                            float u, int lane, int32_t* accept_len, int32_t* next_tok, int n) {
-  const bool vec = (V & 3) == 0;
-  auto load4 = [&](int v0, float (&o)[4]) {
-    if (vec && v0 + 4 <= V) {
-      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(zr + v0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = x[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = v0 + i < V ? zr[v0 + i] : -__builtin_inff();
-    }
-  };
   if (resid) {
     // lanes 0..15 load their candidate's logit together; lane 0 then
     // applies the corrections in slot order from registers (one memory
@@ -265,36 +316,33 @@ __device__ __forceinline__ void draw_token(float* tsum, int ntiles, const float*
   }
   __builtin_amdgcn_wave_barrier();
   int k = wave_min_int(first);
-  if (k == 0x7fffffff) k = ntiles - 1;  // rounding: the last tile
+  const bool over = k == 0x7fffffff;  // rounding: u * total passed every prefix
+  if (over) k = ntiles - 1;
   // 4. inside tile k: the first token whose running sum passes the target
   const float base = k > 0 ? tsum[k - 1] : 0.f;
   const int v0 = k * kTile + lane * 4;
-  float zv[4], r[4];
-  load4(v0, zv);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float p = v0 + i < V ? exp2f(zv[i] * s2 - l2) : 0.f;
-#pragma unroll
-    for (int c = 0; c < kTopK; ++c)
-      if (cand_id[c] == v0 + i) p = fmaxf(p - cand_q[c], 0.f);
-    r[i] = p;
-  }
+  float r[4], pr[4];
+  token_masses(zr, V, s2, l2, resid, cand_id, cand_q, v0, r, pr);
   const float mine = r[0] + r[1] + r[2] + r[3];
   const float c = wave_scan_incl(mine);
   float run = base + (c - mine);
   int hit = 0x7fffffff;
-  int lastv = -1;
+  int lastv = -1, lastp = -1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     run += r[i];
     if (hit == 0x7fffffff && r[i] > 0.f && run > target) hit = v0 + i;
     if (r[i] > 0.f) lastv = v0 + i;
+    if (pr[i] > 0.f) lastp = v0 + i;
   }
-  hit = wave_min_int(hit);
+  hit = over ? 0x7fffffff : wave_min_int(hit);  // an overshoot takes the last token with mass
   lastv = -wave_min_int(-lastv);
+  if (hit == 0x7fffffff && lastv < 0)
+    lastv = draw_fallback(zr, V, s2, l2, resid, cand_id, cand_q, k, ntiles,
+                          -wave_min_int(-lastp), lane);
   if (lane == 0) {
     *accept_len = n + 1;
-    *next_tok = hit != 0x7fffffff ? hit : lastv;  // rounding overshoot: last token with mass
+    *next_tok = hit != 0x7fffffff ? hit : lastv;
   }
 }
 

@@ -201,10 +201,19 @@ int dflash2_topk16(const float* logits, float* top_val, int32_t* top_idx,
 size_t dflash2_logits_topk_workspace(int M, int H, int V, int K, int dtype, int logits_given);
 
 /*
- * Logits and top-16 in one call: dflash2_lmhead_logits_tilemax then
+ * LM-head logits and the per-position top-16 candidates in one call.
+ * [POST] "A lightweight path selector": the unary term of every pair score
+ * is the drafter's own logit, computed once per position, and the walk
+ * chooses among the 16 best tokens of each position.
+ *   logits[m, n] = sum_c h[m, c] * W[n, c]   (fp32 accumulation, fp32 out)
+ *   top_val / top_idx [M, 16]: the 16 largest logits of row m, value
+ *   descending, equal values by lower token id (as dflash2_topk16).
+ * h [M, H] and W [V, H] of dtype (W may be packed, DFLASH2_BF16_PACKED),
+ * 16-byte aligned.  Runs dflash2_lmhead_logits_tilemax then
  * dflash2_topk16_tilemax, the tile maxima in the workspace.  logits may be
  * NULL (then the workspace holds them, see the query above).  The workspace
- * is required (256-byte aligned) whenever M > 0.
+ * is required (256-byte aligned) whenever M > 0.  K must be 16.  Errors as
+ * for the two calls it runs; nothing is launched unless every check passes.
  */
 int dflash2_logits_topk(const void* h, const void* W, float* logits,
                         float* top_val, int32_t* top_idx,

@@ -42,4 +42,5 @@ from .cpu_oracle import (  # noqa: F401
     oracle_selector,
     expected_acceptance,
     run_step_front,
+    run_step_head,
 )

@@ -271,8 +271,8 @@ def path_select(S0: np.ndarray, S: np.ndarray, top_idx: np.ndarray):
 
 
 def path_select_greedy(S0: np.ndarray, S: np.ndarray, top_idx: np.ndarray):
-    """The post's own walk ([POST] "A lightweight path selector"; [GLONCE]:
-    the final step picks a path by greedy selection): start from the last
+    """The post's own walk ([POST] "A lightweight path selector"; [GLONCE]
+    names a greedy choice as one way the serial walk ends): start from the last
     verified token and at every position take the best successor of the
     token chosen before,
 
@@ -361,9 +361,9 @@ def path_margin(S0: np.ndarray, S: np.ndarray) -> np.ndarray:
 # ------------------------------------------------------------------ f4 sampling
 def sample_path(S0: np.ndarray, S: np.ndarray, top_idx: np.ndarray, T: float, u: np.ndarray):
     """The sampling walk ([POST] "A lightweight path selector": besides the
-    greedy walk, sampling draws from the same precomputed scores; [GLONCE]:
-    the final step picks a path by greedy selection, sampling or rejection
-    sampling).
+    greedy walk, sampling draws from the same precomputed scores; [GLONCE]
+    lists a greedy choice, a draw, and a draw checked by rejection as the
+    three ways the serial walk can end).
 
     Reading: the sampling twin of the greedy best-successor walk.  Starting
     from the last verified token, each position's slot is drawn from the
@@ -414,8 +414,8 @@ def target_lse(z_target: np.ndarray, T: float) -> np.ndarray:
 def rejection_verify(path_tok: np.ndarray, q: np.ndarray, top_idx: np.ndarray,
                      z_target: np.ndarray, T: float, u_acc: np.ndarray, u_res: np.ndarray):
     """Lossless verification of a sampled path ([POST] "A lightweight path
-    selector": rejection sampling restores the exact target distribution;
-    [GLONCE]: it preserves the target model's exact output distribution).
+    selector": the rejection step makes the emitted tokens follow the
+    target's own distribution; [GLONCE] says the same of the final choice).
 
     The standard speculative-sampling rule (Leviathan et al. 2023; Chen et
     al. 2023).  The target's distribution at position t is
@@ -426,7 +426,10 @@ def rejection_verify(path_tok: np.ndarray, q: np.ndarray, top_idx: np.ndarray,
     p_t(x_t) (probability min(1, p/q)); at the first rejection n, the
     verifier's token is drawn from the residual max(0, p_n - q_n), normalised;
     if all L are accepted, it is drawn from p_L.  Draws use the inverse CDF
-    in token-id order with u_res[b] scaled by the residual mass.
+    in token-id order with u_res[b] scaled by the residual mass.  When
+    rounding puts u_res * mass past the last partial sum, the draw takes the
+    last token with mass; if no token has residual mass at all (possible only
+    through rounding), the last token with p > 0; if none, the last token.
     Returns (accept_len int32 [B] = n + 1, next_tok int32 [B]).
     """
     path_tok = np.asarray(path_tok)
@@ -456,7 +459,10 @@ def rejection_verify(path_tok: np.ndarray, q: np.ndarray, top_idx: np.ndarray,
         cum = np.cumsum(r)
         v = int(np.searchsorted(cum, u_res[b] * cum[-1], side="right"))
         if v >= len(r) or r[v] == 0.0:                       # rounding past the end
-            v = int(np.nonzero(r > 0)[0][-1])
+            nz = np.nonzero(r > 0)[0]
+            if len(nz) == 0:                                 # no residual mass at all
+                nz = np.nonzero(p > 0)[0]
+            v = int(nz[-1]) if len(nz) else len(r) - 1
         acc[b], nxt[b] = n + 1, v
     return acc, nxt
 
@@ -499,33 +505,16 @@ def expected_acceptance(p) -> float:
 
 
 # ------------------------------------------------------------------ composition
-def run_step_front(w, inp: Dict[str, object], blocks: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
-    """conv chain -> logits -> top-16 -> pair scores -> path, for the given
-    blocks (all when None).  Verification needs targets and is run by the
-    caller (verify_greedy, or rejection_verify for a sampled walk, whose
-    proposal distributions come back as "q").  Returns every intermediate."""
-    x = inp["x"]
-    convs = inp["convs"]
+def run_step_head(w, inp: Dict[str, object], y: np.ndarray,
+                  blocks: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """logits -> top-16 -> [context gate] -> pair scores -> path, from the
+    final hidden states y (fp64 values of the stored activations, [Bs, L, H])
+    of the given blocks (all when None).  Returns every intermediate."""
     anchor_tok = inp["anchor_tok"]
     u_path = inp.get("u_path")
     if blocks is not None:
-        x = x[blocks]
-        convs = [dict(c, anchor_h=c["anchor_h"][blocks]) for c in convs]
         anchor_tok = anchor_tok[blocks]
         u_path = None if u_path is None else u_path[blocks]
-    xd = as_f64(x, w.dtype)
-    cd = []
-    for c in convs:
-        if c.get("projT") is not None:          # [2G, H] storage -> [H, 2G] map
-            proj = as_f64(c["projT"], w.dtype).T
-        elif c["proj"] is not None:
-            proj = np.asarray(c["proj"], np.float64)
-        else:
-            proj = None
-        cd.append({"anchor_h": as_f64(c["anchor_h"], w.dtype),
-                   "k0": np.asarray(c["k0"], np.float64), "k1": np.asarray(c["k1"], np.float64),
-                   "proj": proj, "groups": c.get("groups", 1)})
-    y = conv_chain(xd, cd, w.dtype)
     Bs, L, H = y.shape
     z = lm_logits(y.reshape(Bs * L, H), inp["W"], w.dtype)
     top_val, top_idx = topk16(z)
@@ -543,3 +532,29 @@ def run_step_front(w, inp: Dict[str, object], blocks: Optional[np.ndarray] = Non
         slot, tok, score = (path_select_greedy if walk == "greedy" else path_select)(S0, S, ti)
     return {"y": y, "z": z, "top_val": tv, "top_idx": ti, "gate": gate, "S0": S0, "S": S,
             "path_slot": slot, "path_tok": tok, "path_score": score, "q": q}
+
+
+def run_step_front(w, inp: Dict[str, object], blocks: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """conv chain -> logits -> top-16 -> pair scores -> path, for the given
+    blocks (all when None).  Verification needs targets and is run by the
+    caller (verify_greedy, or rejection_verify for a sampled walk, whose
+    proposal distributions come back as "q").  Returns every intermediate."""
+    x = inp["x"]
+    convs = inp["convs"]
+    if blocks is not None:
+        x = x[blocks]
+        convs = [dict(c, anchor_h=c["anchor_h"][blocks]) for c in convs]
+    xd = as_f64(x, w.dtype)
+    cd = []
+    for c in convs:
+        if c.get("projT") is not None:          # [2G, H] storage -> [H, 2G] map
+            proj = as_f64(c["projT"], w.dtype).T
+        elif c["proj"] is not None:
+            proj = np.asarray(c["proj"], np.float64)
+        else:
+            proj = None
+        cd.append({"anchor_h": as_f64(c["anchor_h"], w.dtype),
+                   "k0": np.asarray(c["k0"], np.float64), "k1": np.asarray(c["k1"], np.float64),
+                   "proj": proj, "groups": c.get("groups", 1)})
+    y = conv_chain(xd, cd, w.dtype)
+    return run_step_head(w, inp, y, blocks)

@@ -736,6 +736,38 @@ def test_verify_rejection_lazy_bad_tokens_and_neg_inf():
 
 
 @pytest.mark.parametrize("lazy", [False, True])
+def test_verify_rejection_draw_past_the_last_prefix(lazy):
+    """u_res at 1 or one ulp below it, with the row's last 256-token tile all
+    -inf (V = 151936): when u * mass passes every tile prefix the draw takes
+    the last token with residual mass, as the oracle does, and never emits an
+    id outside [0, V).  Regression: the draw once fell back to the last tile
+    without checking its mass and emitted -1."""
+    g = np.random.default_rng(91)
+    B, L, V, T = 16, 3, 151936, 1.0
+    ti, slot, tok, q, z, ua, _ = _spec_case(g, B, L, V, T)
+    last_tile = (V - 1) // 256 * 256
+    z[:, :, last_tile:] = -np.inf
+    # u = 1 is one past the uniforms' range [0, 1): the largest value
+    # rounding of u * mass can reach
+    ur = np.where(np.arange(B) % 2 == 0, np.float32(1.0),
+                  np.nextafter(np.float32(1.0), np.float32(0.0))).astype(np.float32)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    if lazy:
+        acc, nxt = bd.verify_rejection_lazy(d(slot), d(tok), d(q), d(ti), d(z), T, d(ua), d(ur))
+    else:
+        lse = bd.target_lse(d(z), T)
+        acc, nxt = bd.verify_rejection(d(slot), d(tok), d(q), d(ti), d(z), lse, T, d(ua), d(ur))
+    a, nx = acc.cpu().numpy(), nxt.cpu().numpy()
+    assert ((nx >= 0) & (nx < last_tile)).all(), nx
+    check_rejection(ti, slot, tok, q, z, T, ua, ur, a, nx)
+    wa, wn = O.rejection_verify(tok, q.astype(np.float64), ti, z, T, ua.astype(np.float64),
+                                ur.astype(np.float64))
+    same = (a == wa) & (ur == 1.0)
+    assert same.sum() >= 4
+    np.testing.assert_array_equal(nx[same], wn[same])      # the last token with mass
+
+
+@pytest.mark.parametrize("lazy", [False, True])
 def test_rejection_sampling_is_lossless_on_gpu(lazy):
     # the whole sampled walk + verification on the GPU: emitted tokens follow
     # the target's softmax (chi-square on a 24-token vocabulary)

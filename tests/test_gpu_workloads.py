@@ -20,7 +20,8 @@ over all blocks (properties that hold at any size, checked with test-local
 numpy on the GPU's own outputs, not through the oracle):
   sorted distinct in-range candidates whose values are their logits, path
   tokens are candidates; greedy: every step is its row's first maximum;
-  max-plus: the score is the fp32 max-plus optimum of the GPU's scores;
+  max-plus: the path is the fp32 max-plus walk of the GPU's scores with
+  lowest-slot ties, and its score is the optimum;
   the score is the path's fp32 running sum; sampled: each slot is the
   inverse-CDF draw of its row's softmax where the uniform is clear of the
   bin edges, and q is that softmax; acceptance in [1, L+1] and, for greedy
@@ -253,11 +254,19 @@ def test_first_conv_all_blocks(case):
 def test_end_to_end_subset(case):
     w, buf, ora, blocks = case["w"], case["buf"], case["ora"], case["blocks"]
     if w.dynamic and w.groups > 1 and w.n_convs > 1:
-        pytest.skip("20 chained applications with fp32-accumulated per-group corrections are "
-                    "chaotic (a 1e-7 relative change of the corrections changes over 1% of the "
-                    "final activations: test_oracle_pins.py::"
-                    "test_conv_g16_chain_amplifies_rounding_of_the_corrections); parity is "
-                    "per application (stage-wise on the subset, first application on all blocks)")
+        # A chain of 20 applications with fp32-accumulated per-group
+        # corrections does not reproduce the exact chain (its logits miss
+        # the 1e-3 bar on most entries: test_oracle_pins.py::
+        # test_conv_g16_chain_with_fp32_corrections_breaks_the_logit_bar).
+        # The chain is checked per application (stage-wise); everything
+        # downstream of it is checked here from the GPU's own final
+        # activations: the oracle's logits, top-16, scores, walk and
+        # verification of exactly the values the GPU's LM head read.
+        y_last = buf.y[(w.n_convs - 1) % len(buf.y)]
+        yg = y_last[torch.from_numpy(blocks).to(DEV)]
+        yg = O.as_f64(to_host_bits(yg), w.dtype)
+        ora = O.run_step_head(w, case["inp"], yg, blocks)
+        print(f"e2e from the GPU's final activations ({len(blocks)} blocks)")
     B, L, V = w.B, w.L, w.V
     rows = (blocks[:, None] * L + np.arange(L)[None, :]).reshape(-1)
     z = buf.logits[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
@@ -382,11 +391,21 @@ def test_properties_all_blocks(case):
         # every step takes the first maximum of its row
         np.testing.assert_array_equal(slot, rows.argmax(axis=2))
     else:
-        # the path's fp32 score in position order is the max-plus optimum
-        # (the same fp32 additions along the path, maxima exact)
+        # the max-plus walk of the GPU's own scores, in fp32, with the lowest
+        # slot at every maximum and at the final argmax: the GPU's path is
+        # that walk bit for bit on every block (the stress workload's 1/64
+        # grid makes exact ties common), and its score is the optimum
         delta = S0_g.copy()
+        back = np.zeros((B, L, 16), dtype=np.int64)
         for t in range(1, L):
-            delta = (delta[:, :, None] + S_g[:, t - 1]).max(axis=1)
+            cand = delta[:, :, None] + S_g[:, t - 1]          # fp32 sums
+            back[:, t] = cand.argmax(axis=1)                   # first (lowest) slot
+            delta = cand.max(axis=1)
+        want = np.zeros((B, L), dtype=np.int64)
+        want[:, L - 1] = delta.argmax(axis=1)
+        for t in range(L - 1, 0, -1):
+            want[:, t - 1] = back[bb, t, want[:, t]]
+        np.testing.assert_array_equal(slot, want)
         np.testing.assert_array_equal(buf.path_score.cpu().numpy(), delta.max(axis=1))
     run = rows[bb, 0, slot[:, 0]].copy()
     for t in range(1, L):

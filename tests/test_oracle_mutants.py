@@ -337,6 +337,22 @@ def test_pins_catch_a_residual_draw_from_p(monkeypatch):
     _fails(pins.test_rejection_verify_preserves_the_target_distribution)
 
 
+def test_pins_catch_an_overshoot_that_takes_the_last_token(monkeypatch):
+    # u * mass past the last partial sum answered with the row's last token,
+    # whatever its mass (the GPU draw once did the same with its last tile)
+    orig = O.rejection_verify
+
+    def last_token(path_tok, q, top_idx, z, T, u_acc, u_res):
+        acc, nxt = orig(path_tok, q, top_idx, z, T, u_acc, u_res)
+        for b in range(len(acc)):
+            if u_res[b] >= np.nextafter(1.0, 0.0):
+                nxt[b] = np.asarray(z).shape[-1] - 1
+        return acc, nxt
+
+    monkeypatch.setattr(O, "rejection_verify", last_token)
+    _fails(pins.test_rejection_verify_draw_edges)
+
+
 def test_pins_catch_the_previous_token_taken_from_the_same_position(monkeypatch):
     orig = O.pair_scores
 

@@ -588,6 +588,31 @@ def test_rejection_verify_limits():
         assert nxt[b] == rest[int(ur[b] * len(rest))]
 
 
+def test_rejection_verify_draw_edges():
+    """The draw's edge rules, on a hand case whose residual is uniform over
+    tokens 16..29: u = 0 draws the first token with mass; u = 1 (u * mass
+    equal to the last partial sum, the largest value rounding can give) draws
+    the last token with mass, never a later token without it; with no
+    residual mass at all (p equal to q on every candidate), the last token
+    with p > 0."""
+    V, T = 40, 1.0
+    top = np.arange(16, dtype=np.int32)[None, None, :]
+    q = np.full((1, 1, 16), 1.0 / 16)
+    tok = np.array([[0]], dtype=np.int32)
+    zt = np.zeros((1, 2, V))
+    zt[0, 0, :16] = -np.inf             # no target mass on the candidates: reject at 0
+    zt[0, 0, 30:] = -np.inf             # nor on tokens 30..39
+    for u, want in ((0.0, 16), (1.0, 29), (np.nextafter(1.0, 0.0), 29)):
+        acc, nxt = O.rejection_verify(tok, q, top, zt, T, np.array([[0.5]]), np.array([u]))
+        assert acc[0] == 1 and nxt[0] == want, (u, nxt[0])
+    # V = 16, every token a candidate, p = q = 1/16 exactly; an accept test
+    # with u = 1 rejects (1 * q < p fails), and max(0, p - q) is 0 everywhere
+    V = 16
+    zt = np.zeros((1, 2, V))
+    acc, nxt = O.rejection_verify(tok, q, top, zt, T, np.array([[1.0]]), np.array([0.3]))
+    assert acc[0] == 1 and nxt[0] == 15
+
+
 # ------------------------------------------------------------------ verify
 def test_verify_hand_cases():
     path = np.array([[1, 2, 3, 4], [1, 2, 3, 4], [1, 2, 3, 4], [9, 2, 3, 4]])
@@ -710,6 +735,43 @@ def test_conv_g16_chain_amplifies_rounding_of_the_corrections():
     last = (O.conv_chain(x, exact, "bf16") != O.conv_chain(x, nudged, "bf16")).mean()
     assert first < 1e-3
     assert last > 0.01 and last > 20 * first
+
+
+def test_conv_g16_chain_with_fp32_corrections_breaks_the_logit_bar():
+    """The same property at the level where end-to-end parity is judged: the
+    chain with its per-group corrections accumulated in fp32 (the mix still
+    exact with one rounding, as a matrix-core implementation computes it)
+    leaves about half of the final activations different from the exact
+    chain's, and the logits of those activations miss the step's 1e-3
+    relative logit bar on most entries.  So the conv-heavy-g16 step is
+    checked per application and, downstream of the chain, from the GPU's
+    own final activations, never as chain-level logit parity."""
+    w = WL.WORKLOADS[6].with_blocks(2)
+    inp = WL.make_inputs(w, with_head=False)
+    x = O.as_f64(inp["x"], "bf16")
+
+    def conv_fp32_corrections(x, a, k0, k1, P, G):
+        B, L, H = x.shape
+        D = (x.reshape(-1, H).astype(np.float32) @ P.astype(np.float32)).astype(np.float64)
+        D = D.reshape(B, L, G, 2)
+        grp = np.arange(H) // (H // G)
+        prev = np.concatenate([a[:, None, :], x[:, :-1]], axis=1)
+        return (k0 + D[:, :, grp, 0]) * x + (k1 + D[:, :, grp, 1]) * prev
+
+    exact, fp32 = x, x
+    for c in inp["convs"]:
+        P = O.as_f64(c["projT"], "bf16").T
+        a = O.as_f64(c["anchor_h"], "bf16")
+        k0, k1 = c["k0"].astype(np.float64), c["k1"].astype(np.float64)
+        exact = O.round_to_bf16(O.twotap_conv(exact, a, k0, k1, P, c["groups"]))
+        fp32 = O.round_to_bf16(conv_fp32_corrections(fp32, a, k0, k1, P, c["groups"]))
+    assert (exact != fp32).mean() > 0.3
+    V = 4096           # a slice of an LM head of the workload's distribution
+    W = WL.to_bf16_bits(WL.normal_f32((V, w.H), 1.0 / w.H, w.seed, WL.TAG_W))
+    ze = O.lm_logits(exact.reshape(-1, w.H), W, "bf16").astype(np.float64)
+    z32 = O.lm_logits(fp32.reshape(-1, w.H), W, "bf16").astype(np.float64)
+    over = np.abs(ze - z32) > 1e-3 * np.maximum(np.abs(ze), 1.0)
+    assert over.mean() > 0.5 and np.abs(ze - z32).max() > 0.05
 
 
 def test_stress_construction_is_dyadic():
