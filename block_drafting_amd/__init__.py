@@ -43,7 +43,8 @@ import torch
 __all__ = [
     "DFlash2Error", "lib", "library_path", "twotap_conv", "twotap_conv_mm", "lmhead_logits",
     "lmhead_logits_tilemax", "lmhead_pack", "PackedWeight", "topk16", "topk16_tilemax",
-    "topk16_workspace", "logits_topk", "logits_topk_workspace", "context_gate", "pair_score",
+    "topk16_workspace", "logits_topk", "logits_topk_workspace", "logits_topk_noalloc",
+    "context_gate", "pair_score",
     "path_select", "pair_select_verify", "pair_sample", "path_sample", "target_lse", "verify_rejection", "verify_rejection_lazy", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
 ]
 
@@ -71,6 +72,7 @@ _SIGS = {
     "dflash2_topk16": ([_P, _P, _P, _I, _I, _I, _P, _Z, _P], _I),
     "dflash2_logits_topk_workspace": ([_I, _I, _I, _I, _I, _I], _Z),
     "dflash2_logits_topk": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
+    "dflash2_logits_topk_noalloc": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
     "dflash2_pair_score": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "dflash2_context_gate": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "dflash2_pair_score_gated": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
@@ -371,6 +373,25 @@ def logits_topk(h: torch.Tensor, W, logits: Optional[torch.Tensor] = None,
     _check("dflash2_logits_topk", lib().dflash2_logits_topk(
         _ptr(h), wp, _ptr(logits), _ptr(top_val), _ptr(top_idx), M, H, V, TOPK, code,
         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(dev)))
+    return top_val, top_idx
+
+
+def logits_topk_noalloc(h: torch.Tensor, W, logits: torch.Tensor,
+                        top_val: torch.Tensor, top_idx: torch.Tensor):
+    """logits_topk without a workspace, for callers that cannot allocate:
+    the tile maxima live in the library's fixed device scratch (shared by
+    every call on one GPU; overlapping calls on one GPU race).  Every output
+    is caller-given.  Returns (top_val, top_idx)."""
+    _rank(h, 2, "h")
+    M, H = h.shape
+    wp, V, code, wt = _weight(W, h)
+    _shape(logits, (M, V), "logits", torch.float32)
+    _shape(top_val, (M, TOPK), "top_val", torch.float32)
+    _shape(top_idx, (M, TOPK), "top_idx", torch.int32)
+    dev = _dev(h, wt, logits, top_val, top_idx)
+    _check("dflash2_logits_topk_noalloc", lib().dflash2_logits_topk_noalloc(
+        _ptr(h), wp, _ptr(logits), _ptr(top_val), _ptr(top_idx), M, H, V, TOPK, code,
+        _stream(dev)))
     return top_val, top_idx
 
 

@@ -1,6 +1,8 @@
 // extern "C" entry points of libdflash2: argument validation on the host,
 // then kernel launches on the caller's stream.  Nothing is launched and no
 // output is touched unless every check passes.
+#include <mutex>
+
 #include "dflash2.h"
 #include "common.hpp"
 
@@ -47,6 +49,8 @@ DFLASH2_API const char* dflash2_strerror(int status) {
     case DFLASH2_EUNSUPPORTED: return "unsupported configuration";
     case DFLASH2_EHIP: return "HIP launch or runtime error";
     case DFLASH2_EWORKSPACE: return "workspace missing or too small";
+    case DFLASH2_ESCRATCH:
+      return "problem larger than the fixed scratch of the allocation-free call";
     default: return "unknown status";
   }
 }
@@ -558,4 +562,62 @@ DFLASH2_API int dflash2_pair_sample(const float* top_val, const int32_t* top_idx
   return status_of(launch_pair_sample(top_val, top_idx, anchor_tok, U, Vf, gate, u, temperature,
                                       B, L, V, r, dtype, S0, L > 1 ? S : nullptr, path_slot,
                                       path_tok, q, as_stream(stream)));
+}
+
+// ---------------------------------------------------------------- allocation-free logits + top-16
+// dflash2_logits_topk for callers that cannot allocate: the tile maxima
+// between the GEMM and the top-16 live in this fixed device array (each GPU
+// the library runs on holds its own copy until the process ends).  Host
+// code never passes the array's name to a kernel: its device address on the
+// current device is looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[DFLASH2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call made with that device current).
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DFLASH2_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DFLASH2_EHIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return DFLASH2_OK;
+}
+}  // namespace
+
+DFLASH2_API int dflash2_logits_topk_noalloc(const void* h, const void* W, float* logits,
+                                            float* top_val, int32_t* top_idx, int M, int H,
+                                            int V, int K, int dtype, void* stream) {
+  if (K != kTopK) return DFLASH2_EINVAL;
+  int st = check_lmhead(h, W, M, H, V, dtype);
+  if (st != DFLASH2_OK) return st;
+  if (M == 0) return DFLASH2_OK;
+  st = check_topk_out(top_val, top_idx, M);
+  if (st != DFLASH2_OK) return st;
+  if (!logits || !aligned16(logits)) return DFLASH2_EINVAL;
+  if (tilemax_bytes(M, V) > (size_t)DFLASH2_NOALLOC_SCRATCH_BYTES) return DFLASH2_ESCRATCH;
+  const size_t zb = (size_t)M * V * sizeof(float);
+  const size_t ob = (size_t)M * kTopK * 4;
+  const size_t es = esize(dtype);
+  const size_t wb = w_bytes(V, H, dtype);
+  if (overlap(logits, zb, h, (size_t)M * H * es) || overlap(logits, zb, W, wb) ||
+      overlap(top_val, ob, logits, zb) || overlap(top_idx, ob, logits, zb) ||
+      overlap(top_val, ob, top_idx, ob))
+    return DFLASH2_EINVAL;
+  void* sp = nullptr;
+  st = scratch_on_current_device(&sp);
+  if (st != DFLASH2_OK) return st;
+  float* tmax = static_cast<float*>(sp);
+  hipStream_t s = as_stream(stream);
+  hipError_t e = launch_lmhead(h, W, logits, tmax, M, H, V, dtype, s);
+  if (e != hipSuccess) return DFLASH2_EHIP;
+  return status_of(launch_topk16_tilemax(logits, tmax, top_val, top_idx, M, V, s));
 }

@@ -58,7 +58,8 @@ typedef enum {
   DFLASH2_EINVAL = -1,        /* bad pointer, size, shape or aliasing */
   DFLASH2_EUNSUPPORTED = -2,  /* valid request this build does not implement */
   DFLASH2_EHIP = -3,          /* a HIP launch or runtime call failed */
-  DFLASH2_EWORKSPACE = -4     /* workspace missing or smaller than queried */
+  DFLASH2_EWORKSPACE = -4,    /* workspace missing or smaller than queried */
+  DFLASH2_ESCRATCH = -5       /* larger than the fixed scratch of an allocation-free call */
 } dflash2_status;
 
 typedef enum {
@@ -219,6 +220,33 @@ int dflash2_logits_topk(const void* h, const void* W, float* logits,
                         float* top_val, int32_t* top_idx,
                         int M, int H, int V, int K, int dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the fixed device scratch of dflash2_logits_topk_noalloc (16 MiB). */
+#define DFLASH2_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * dflash2_logits_topk for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, and harnesses that forbid
+ * allocation.  It takes no workspace and calls no allocating routine: the
+ * tile maxima between the GEMM and the top-16 (M * ceil(V / 256) * 4 bytes)
+ * live in a fixed device array of DFLASH2_NOALLOC_SCRATCH_BYTES that each
+ * GPU the library runs on holds until the process ends (its address is
+ * looked up on the first call made on that device; the stream must belong
+ * to the current device).
+ *   logits [M, V] fp32 is required here (a caller-given output, 16-byte
+ *   aligned); every other argument, result and error is as for
+ *   dflash2_logits_topk, and the results equal its results bit for bit.
+ * Returns DFLASH2_ESCRATCH, before any launch, when the tile maxima do not
+ * fit (M * ceil(V / 256) * 4 > DFLASH2_NOALLOC_SCRATCH_BYTES; at V = 151936
+ * that is M > 7061).  Every call on one GPU shares that GPU's array and
+ * leaves its tile maxima there; each call writes all the entries it reads,
+ * so nothing needs clearing, but calls that overlap in time on one GPU
+ * (other streams, other threads) race on the array and must be serialised
+ * by the caller.
+ */
+int dflash2_logits_topk_noalloc(const void* h, const void* W, float* logits,
+                                float* top_val, int32_t* top_idx,
+                                int M, int H, int V, int K, int dtype, void* stream);
 
 /*
  * Adjacent-pair scores.  [POST] "A lightweight path selector", eq. S_t(a,b):

@@ -13,7 +13,7 @@ import block_drafting_amd as bd
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dflash2.h")
 
-EINVAL, EUNSUP, EHIP, EWS = -1, -2, -3, -4
+EINVAL, EUNSUP, EHIP, EWS, ESCRATCH = -1, -2, -3, -4, -5
 P = 0x7f0000001000          # 4 KiB-aligned fake device address (never dereferenced)
 Q = 0x7f0000100000          # another, far from P
 
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_strerror():
     L = bd.lib()
     assert L.dflash2_version() >= 10000
-    for s in (0, EINVAL, EUNSUP, EHIP, EWS):
+    for s in (0, EINVAL, EUNSUP, EHIP, EWS, ESCRATCH):
         assert len(L.dflash2_strerror(s)) > 0
     assert L.dflash2_strerror(12345) == b"unknown status"
 
@@ -349,3 +349,25 @@ def test_python_binding_refuses_cpu_tensors():
     k = torch.zeros(64)
     with pytest.raises(ValueError):
         bd.twotap_conv(x, k, k)
+
+
+def test_logits_topk_noalloc_validation():
+    """The allocation-free logits + top-16: the logits are required, and a
+    problem whose tile maxima exceed the fixed scratch is refused with its
+    own status before anything touches the device."""
+    f = bd.lib().dflash2_logits_topk_noalloc
+    MB = 1 << 20
+    h, W, z, tv, ti = P, P + 512 * MB, P + 4096 * MB, P + 16384 * MB, P + 16400 * MB
+
+    def call(M=512, H=5120, V=151936, K=16, dt=1, z_=z, h_=h):
+        return f(h_, W, z_, tv, ti, M, H, V, K, dt, None)
+
+    assert call(M=0) == 0
+    assert call(K=8) == EINVAL
+    assert call(z_=None) == EINVAL                       # logits are a caller-given output
+    assert call(z_=z + 4) == EINVAL                      # 16-byte alignment
+    assert call(h_=None) == EINVAL
+    assert call(z_=h) == EINVAL                          # logits overlap h
+    assert call(M=7062) == ESCRATCH                      # 7062 * 594 * 4 > 16 MiB
+    assert call(M=4096, V=1 << 20) == ESCRATCH
+    assert bd.lib().dflash2_strerror(ESCRATCH).startswith(b"problem larger")
