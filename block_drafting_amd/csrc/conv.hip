@@ -183,6 +183,261 @@ __global__ __launch_bounds__(256) void conv_dyn1_kernel(const T* __restrict__ x,
   }
 }
 
+// ---------------------------------------------------------------- rows of a block per workgroup
+// Raw storage of 8 consecutive channels (one 16-byte bf16 vector or two
+// fp32 vectors), widened to fp64 on use.
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+  u32x4_t w;
+  __device__ void load(const uint16_t* p) { w = *reinterpret_cast<const u32x4_t*>(p); }
+  __device__ void zero() { w = u32x4_t{0u, 0u, 0u, 0u}; }
+  __device__ void widen(double v[8]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = (double)bf16_lo(w[i]);
+      v[2 * i + 1] = (double)bf16_hi(w[i]);
+    }
+  }
+  // channel i (a compile-time index once unrolled)
+  __device__ double at(int i) const {
+    return (double)((i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]));
+  }
+};
+template <>
+struct Raw8<float> {
+  f32x4_t a, b;
+  __device__ void load(const float* p) {
+    a = reinterpret_cast<const f32x4_t*>(p)[0];
+    b = reinterpret_cast<const f32x4_t*>(p)[1];
+  }
+  __device__ void zero() {
+    a = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    b = a;
+  }
+  __device__ void widen(double v[8]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = (double)a[i];
+      v[4 + i] = (double)b[i];
+    }
+  }
+  __device__ double at(int i) const { return (double)(i < 4 ? a[i] : b[i - 4]); }
+};
+
+// Eight output channels, each rounded once from fp64 as it is produced:
+// bf16 by round-to-odd to fp32 then the hardware's nearest-even (one
+// correct rounding), fp32 by nearest-even.
+template <typename T>
+struct Out8;
+template <>
+struct Out8<uint16_t> {
+  float f[8];
+  __device__ void set(int i, double v) { f[i] = f64_to_f32_odd(v); }
+  __device__ void store(uint16_t* p) const {
+    u32x4_t w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    *reinterpret_cast<u32x4_t*>(p) = w;
+  }
+};
+template <>
+struct Out8<float> {
+  float f[8];
+  __device__ void set(int i, double v) { f[i] = (float)v; }
+  __device__ void store(float* p) const {
+    reinterpret_cast<f32x4_t*>(p)[0] = f32x4_t{f[0], f[1], f[2], f[3]};
+    reinterpret_cast<f32x4_t*>(p)[1] = f32x4_t{f[4], f[5], f[6], f[7]};
+  }
+};
+
+// Value of lane (lane ^ D) for fp64 data (two 32-bit exchanges).
+template <int D>
+__device__ __forceinline__ double xor_f64(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = xor_lane<D>((uint32_t)u);
+  const uint32_t hi = xor_lane<D>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// One reduce-scatter step over partner lane ^ D on the first N values: the
+// lane with bit D set keeps the upper half, the other the lower half, each
+// adding its partner's copy; the lane's value index advances accordingly.
+template <int D, int N>
+__device__ __forceinline__ void rs_step(double* v, int lane, int& idx) {
+  const bool up = (lane & D) != 0;
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    const double send = up ? v[k] : v[k + N / 2];
+    const double keep = up ? v[k + N / 2] : v[k];
+    v[k] = keep + xor_f64<D>(send);
+  }
+  if (up) idx += N / 2;
+}
+
+// Sums of N values (N a power of two, 2..32) over the 64 lanes of a wave:
+// a reduce-scatter over partners 32, 16, ... (log2 N steps) leaves each lane
+// one value, then full exchanges over the remaining partners finish it.
+// Returns the total of value `idx`; the lanes whose low 6 - log2 N bits are
+// zero hold each value once.
+template <int N>
+__device__ __forceinline__ double wave_reduce_scatter(double* v, int lane, int& idx) {
+  static_assert(N >= 2 && N <= 32 && (N & (N - 1)) == 0, "2..32 values");
+  idx = 0;
+  rs_step<32, N>(v, lane, idx);
+  if constexpr (N >= 4) rs_step<16, N / 2>(v, lane, idx); else v[0] += xor_f64<16>(v[0]);
+  if constexpr (N >= 8) rs_step<8, N / 4>(v, lane, idx); else v[0] += xor_f64<8>(v[0]);
+  if constexpr (N >= 16) rs_step<4, N / 8>(v, lane, idx); else v[0] += xor_f64<4>(v[0]);
+  if constexpr (N >= 32) rs_step<2, N / 16>(v, lane, idx); else v[0] += xor_f64<2>(v[0]);
+  v[0] += xor_f64<1>(v[0]);
+  return v[0];
+}
+
+// NG groups of R consecutive positions of one block per workgroup (rows
+// t0 .. t0 + NG*R - 1), every channel.  Thread i holds channel chunks i,
+// i + blockDim, ... (CPT of them, 8 channels each) of a group's R rows in
+// registers, so the taps (and the projection) are read once per workgroup,
+// each row's predecessor is the previous row's registers (only t0's is
+// read: x[b, t0 - 1], or the anchor at t0 = 0), and every load is issued
+// before the first use.  The groups are software-pipelined: group g+1's
+// rows are loading while group g reduces, mixes and stores.  DYN (one
+// correction pair per row): each group's 2R dot products are summed in
+// fp64, per wave by a reduce-scatter, then across the waves in LDS in wave
+// order, so the result does not depend on timing.  The mix is the fp64
+// formula with one rounding per output, as in the kernels above.
+template <typename T, int R, int NG, int CPT, bool DYN>
+__global__ __launch_bounds__(1024 / CPT) void conv_rows_kernel(const T* __restrict__ x,
+                                                         const T* __restrict__ anchor,
+                                                         T* __restrict__ y,
+                                                         const float* __restrict__ k0,
+                                                         const float* __restrict__ k1,
+                                                         const float* __restrict__ proj, int L,
+                                                         int H, int wgs_per_block) {
+  constexpr int N = 2 * R;  // correction dot products of a group
+  __shared__ double red[16 * N];
+  __shared__ double tot[N];
+  const int b = blockIdx.x / wgs_per_block;
+  const int t0 = (blockIdx.x - b * wgs_per_block) * (R * NG);
+  const int H8 = H >> 3;
+  const int tid = threadIdx.x;
+  const int nth = blockDim.x;
+  Raw8<T> xr[2][CPT][R], pr[CPT];
+  f32x4_t kv[CPT][4];       // k0 (2 vectors) then k1 (2 vectors) of the chunk
+  f32x4_t pj[CPT][DYN ? 4 : 1];
+  auto load_group = [&](Raw8<T>(&dst)[CPT][R], int g) {
+    const int tg = t0 + g * R;
+    const int nr = min(R, L - tg);
+    const size_t base = ((size_t)b * L + tg) * H;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c8 = tid + j * nth;
+      if (c8 < H8) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          if (r < nr) dst[j][r].load(x + base + (size_t)r * H + c8 * 8);
+      }
+    }
+  };
+  load_group(xr[0], 0);
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int c8 = tid + j * nth;
+    if (c8 < H8) {
+      const int c = c8 * 8;
+      if (t0 > 0)
+        pr[j].load(x + ((size_t)b * L + t0 - 1) * H + c);
+      else if (anchor)
+        pr[j].load(anchor + (size_t)b * H + c);
+      else
+        pr[j].zero();
+      if constexpr (DYN) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pj[j][q] = reinterpret_cast<const f32x4_t*>(proj + 2 * c)[q];
+      }
+      kv[j][0] = reinterpret_cast<const f32x4_t*>(k0 + c)[0];
+      kv[j][1] = reinterpret_cast<const f32x4_t*>(k0 + c)[1];
+      kv[j][2] = reinterpret_cast<const f32x4_t*>(k1 + c)[0];
+      kv[j][3] = reinterpret_cast<const f32x4_t*>(k1 + c)[1];
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int tg = t0 + g * R;
+    const int nr = min(R, L - tg);
+    if (nr <= 0) break;  // uniform over the workgroup
+    Raw8<T>(&cur)[CPT][R] = xr[g & 1];
+    if (g > 0) {
+      // the predecessor of this group's first row, before the next group's
+      // loads reuse the buffer that holds it
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) pr[j] = xr[(g - 1) & 1][j][R - 1];
+    }
+    if (g + 1 < NG && tg + R < L) load_group(xr[(g + 1) & 1], g + 1);
+    double d[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) d[i] = 0.0;
+    if constexpr (DYN) {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        if (tid + j * nth < H8) {
+          // channel by channel: the channel's two projection entries, then
+          // its value in every row (few fp64 values live at once)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const double p0 = (double)pj[j][i / 2][2 * (i % 2)];
+            const double p1 = (double)pj[j][i / 2][2 * (i % 2) + 1];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              if (r < nr) {
+                const double xv = cur[j][r].at(i);
+                d[2 * r] += xv * p0;
+                d[2 * r + 1] += xv * p1;
+              }
+            }
+          }
+        }
+      }
+      const int lane = tid & 63;
+      const int wave = tid >> 6;
+      int idx;
+      const double part = wave_reduce_scatter<N>(d, lane, idx);
+      if ((lane & (64 / N - 1)) == 0) red[wave * N + idx] = part;
+      __syncthreads();
+      if (tid < N) {
+        double sacc = red[tid];
+        for (int w = 1; w < (nth >> 6); ++w) sacc += red[w * N + tid];
+        tot[tid] = sacc;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < N; ++i) d[i] = tot[i];
+    }
+    const size_t base = ((size_t)b * L + tg) * H;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c8 = tid + j * nth;
+      if (c8 < H8) {
+        const int c = c8 * 8;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (r < nr) {
+            const Raw8<T>& prev = r == 0 ? pr[j] : cur[j][r - 1];
+            Out8<T> o;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const double c0 = (double)kv[j][i / 4][i % 4] + d[2 * r];
+              const double c1 = (double)kv[j][2 + i / 4][i % 4] + d[2 * r + 1];
+              o.set(i, c0 * cur[j][r].at(i) + c1 * prev.at(i));
+            }
+            o.store(y + base + (size_t)r * H + c);
+          }
+        }
+      }
+    }
+  }
+}
+
 // General group count: the row is staged in LDS as fp64, all 2*groups
 // corrections are computed (threads over outputs, coalesced proj reads), then
 // each channel mixes with its group's pair.  Dynamic LDS: (H + 2*groups) doubles.
@@ -477,6 +732,53 @@ hipError_t launch_typed(const void* x, const void* anchor_h, void* y, const floa
   const T* ap = static_cast<const T*>(anchor_h);
   T* yp = static_cast<T*>(y);
   const long long rows = (long long)B * L;
+  // Rows of a block per workgroup, measured at H = 5120 (20 launches back to
+  // back): the corrections' workgroups take 8 rows (15.9 us per application
+  // at 2048 rows against 18.3 for one row per workgroup, 16.0 with 4);
+  // static taps take 2 rows up to 2047 rows (4.9 against 6.3 us at 512) and
+  // 4 pipelined single rows from 2048 on (18.0 against 21.7 us at 4096).
+  // One thread per 8-channel chunk, so H <= 8192 (1024 threads); wider
+  // rows take the one-row kernels below.
+  const int H8 = H / 8;
+  if ((!proj || groups == 1) && H8 <= 1024) {
+    int R = 1, NG = 1;
+    if (proj) {
+      const int rmax = sizeof(T) == 2 ? 8 : 2;  // fp32 rows take twice the registers
+      while (R < rmax && R * 2 <= L && rows / (R * 2) >= 256) R *= 2;
+    } else if (rows >= 2048 && L >= 4) {
+      NG = 4;
+    } else if (rows >= 512 && L >= 2) {
+      R = 2;
+    }
+    const int nth = (H8 + 63) / 64 * 64;
+    const int wpb = (L + R * NG - 1) / (R * NG);
+    const long long wgs = (long long)B * wpb;
+    if (wgs <= 0x7fffffffLL) {
+      const dim3 grid((unsigned)wgs), blk((unsigned)nth);
+#define DFLASH2_CONV_ROWS(RR, NN, CC, DD)                                                       \
+  hipLaunchKernelGGL((conv_rows_kernel<T, RR, NN, CC, DD>), grid, blk, 0, s, xp, ap, yp, k0, k1, \
+                     proj, L, H, wpb)
+#define DFLASH2_CONV_ROWS_C(CC)                                  \
+  do {                                                           \
+    if (proj) {                                                  \
+      if constexpr (sizeof(T) == 2) {                            \
+        if (R == 8) DFLASH2_CONV_ROWS(8, 1, CC, true);           \
+        else if (R == 4) DFLASH2_CONV_ROWS(4, 1, CC, true);      \
+      }                                                          \
+      if (R == 2) DFLASH2_CONV_ROWS(2, 1, CC, true);             \
+      else if (R == 1) DFLASH2_CONV_ROWS(1, 1, CC, true);        \
+    } else {                                                     \
+      if (NG == 4) DFLASH2_CONV_ROWS(1, 4, CC, false);           \
+      else if (R == 2) DFLASH2_CONV_ROWS(2, 1, CC, false);       \
+      else DFLASH2_CONV_ROWS(1, 1, CC, false);                   \
+    }                                                            \
+  } while (0)
+      DFLASH2_CONV_ROWS_C(1);
+#undef DFLASH2_CONV_ROWS_C
+#undef DFLASH2_CONV_ROWS
+      return hipGetLastError();
+    }
+  }
   if (!proj) {
     const long long total8 = rows * (H / 8);
     long long blocks = (total8 + 255) / 256;

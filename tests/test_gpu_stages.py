@@ -91,6 +91,30 @@ def test_conv_parity(dt, B, L, H, mode, groups):
     assert frac == 0.0 if dt == "bf16" else frac < 1e-4
 
 
+# Shapes that reach each row-group layout of the conv kernel: several
+# positions per workgroup (2, 4 or 8 with a projection; 2, or four
+# pipelined single rows with static taps), with L not a multiple of the
+# group so the last group is partial, no anchor, and rows wider than one
+# workgroup's 1024 chunks (H = 10240, 20480: the one-row kernels).
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,H,mode,anchor", [
+    (110, 5, 136, 0, True),      # 550 rows, static: 2 positions per workgroup, L odd
+    (300, 7, 64, 0, True),       # 2100 rows, static: 4 pipelined rows, 7 = 4 + 3
+    (300, 7, 64, 0, False),
+    (70, 9, 520, 1, True),       # 630 rows, projection: 2 positions
+    (130, 9, 64, 1, True),       # 1170 rows: 4 positions, 9 = 4 + 4 + 1
+    (300, 11, 136, 1, False),    # 3300 rows: 8 positions, 11 = 8 + 3
+    (2, 3, 10240, 1, True),      # wider than 8192 channels: one-row kernels
+    (520, 2, 20480, 0, True),
+])
+def test_conv_row_groups_parity(dt, B, L, H, mode, anchor):
+    x, a, k0, k1, P = _conv_case(B, L, H, dt, mode, 1, seed=B + L + H)
+    if not anchor:
+        a = None
+    frac = _conv_check(x, a, k0, k1, P, 1, dt)
+    assert frac == 0.0 if dt == "bf16" else frac < 1e-4
+
+
 def test_conv_no_anchor_and_special_taps_bit_exact():
     B, L, H = 3, 6, 128
     x, a, _, _, _ = _conv_case(B, L, H, "bf16", 0, 1, seed=5)
