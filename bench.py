@@ -70,7 +70,7 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--walk", choices=["viterbi", "greedy"], default=None,
                     help="path walk (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -182,7 +182,7 @@ def cpu_baseline(w, inp, targets, n_blocks: int, n_single: int):
     # margins for the parity gate (oracle helpers, computed in this leg)
     ora["gaps"] = O.topk_gaps(ora["z"], ora["top_val"].reshape(-1, 16)).reshape(
         ora["top_idx"].shape)
-    if w.walk == "sample":
+    if w.walk in ("sample", "sample-path"):
         ora["margin"] = O.sample_margin(ora["q"], inp["u_path"][blocks])
     elif w.walk == "greedy":
         ora["margin"] = O.greedy_margin(ora["S0"], ora["S"], ora["path_slot"])
@@ -225,6 +225,12 @@ def parity_gate(w, blocks, ora, z_rows, top_val, top_idx, S0, S, slot, accept_le
             drift = max(drift, np.abs(S[k] - ora["S"][k]).max())
         if w.walk == "sample":
             clear = (ora["margin"][k] > 1e-5 + 2 * 16 * drift / w.temperature).all()
+        elif w.walk == "sample-path":
+            # the fp32 backward messages' error bound, plus the drift
+            # carried through L messages
+            smax = max(np.abs(ora["S0"][k]).max(), np.abs(ora["S"][k]).max() if L > 1 else 0)
+            tol = 8 * 2.0 ** -24 * L * (smax / w.temperature + 4.0)
+            clear = (ora["margin"][k] > tol + 2 * 16 * L * drift / w.temperature).all()
         else:
             clear = ora["margin"][k] > 1e-3 + 2 * L * drift
         if not clear:
@@ -232,7 +238,7 @@ def parity_gate(w, blocks, ora, z_rows, top_val, top_idx, S0, S, slot, accept_le
         checked += 1
         if slot[k].tolist() != ora["path_slot"][k].tolist():
             bad.append(f"path of block {blocks[k]}")
-        elif w.walk != "sample" and accept_len[k] != ora["accept_len"][k]:
+        elif w.temperature <= 0 and accept_len[k] != ora["accept_len"][k]:
             bad.append(f"acceptance of block {blocks[k]}")
     return bad, checked
 
@@ -324,6 +330,7 @@ def main(argv=None):
     fused = not a.separate                 # scores + walk (+ greedy verification) in one launch
     two_pass = sampled and a.separate      # lse of every target row, then the verification
     final_y = buf.y[(len(convs) - 1) % len(buf.y)] if convs else x   # the chain's output
+    smode = "path" if w.walk == "sample-path" else "chain"
     gate = buf.gate if w.gate else None
     tv3, ti3 = buf.top_val.view(B, L, 16), buf.top_idx.view(B, L, 16)
 
@@ -349,7 +356,7 @@ def main(argv=None):
         stages += [
             ("pair_sample", lambda: bd.pair_sample(tv3, ti3, anchor, U, Vf, u_path, w.temperature,
                                                    gate, None, None, buf.path_slot,
-                                                   buf.path_tok, buf.q)),
+                                                   buf.path_tok, buf.q, mode=smode)),
             ("verify", lambda: bd.verify_rejection_lazy(buf.path_slot, buf.path_tok, buf.q, ti3,
                                                         z_target, w.temperature, u_acc, u_res,
                                                         buf.accept_len, buf.next_tok))]
@@ -364,7 +371,8 @@ def main(argv=None):
         if sampled:
             stages += [
                 ("select", lambda: bd.path_sample(buf.S0, buf.S, ti3, u_path, w.temperature,
-                                                  buf.path_slot, buf.path_tok, buf.q)),
+                                                  buf.path_slot, buf.path_tok, buf.q,
+                                                  mode=smode)),
                 ("lse", lambda: bd.target_lse(z_target, w.temperature, buf.lse)),
                 ("verify", lambda: bd.verify_rejection(buf.path_slot, buf.path_tok, buf.q, ti3,
                                                        z_target, buf.lse, w.temperature, u_acc,

@@ -45,11 +45,12 @@ __all__ = [
     "lmhead_logits_tilemax", "lmhead_pack", "PackedWeight", "topk16", "topk16_tilemax",
     "topk16_workspace", "logits_topk", "logits_topk_workspace", "logits_topk_noalloc",
     "context_gate", "pair_score",
-    "path_select", "pair_select_verify", "pair_sample", "path_sample", "target_lse", "verify_rejection", "verify_rejection_lazy", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
+    "path_select", "pair_select_verify", "pair_sample", "path_sample", "SAMPLE_MODES", "target_lse", "verify_rejection", "verify_rejection_lazy", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
 ]
 
 TOPK = 16
 PATH_MODES = {"viterbi": 0, "greedy": 1}
+SAMPLE_MODES = {"chain": 0, "path": 1}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libdflash2.so")
 _lib = None
@@ -84,6 +85,9 @@ _SIGS = {
     "dflash2_pair_select_verify": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P,
                                     _P, _P, _P, _P, _P, _P], _I),
     "dflash2_path_sample": ([_P, _P, _P, _P, ctypes.c_float, _I, _I, _P, _P, _P, _P], _I),
+    "dflash2_path_sample_mode": ([_P, _P, _P, _P, ctypes.c_float, _I, _I, _I, _P, _P, _P, _P], _I),
+    "dflash2_pair_sample_mode": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I, _I, _I, _I, _I,
+                                  _I, _P, _P, _P, _P, _P, _P], _I),
     "dflash2_target_lse": ([_P, _I, _I, ctypes.c_float, _P, _P], _I),
     "dflash2_verify_rejection": ([_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _I,
                                   _P, _P, _P], _I),
@@ -558,9 +562,14 @@ def pair_select_verify(top_val: torch.Tensor, top_idx: torch.Tensor,
 def pair_sample(top_val: torch.Tensor, top_idx: torch.Tensor, anchor_tok: Optional[torch.Tensor],
                 U: torch.Tensor, Vf: torch.Tensor, u: torch.Tensor, temperature: float,
                 gate: Optional[torch.Tensor] = None, S0: Optional[torch.Tensor] = None,
-                S: Optional[torch.Tensor] = None, path_slot=None, path_tok=None, q=None):
+                S: Optional[torch.Tensor] = None, path_slot=None, path_tok=None, q=None,
+                mode: str = "chain"):
     """pair_score and path_sample in one launch.  The scores are written to
-    S0 / S only when those are given.  Returns (path_slot, path_tok, q)."""
+    S0 / S only when those are given.  mode "chain" draws each position from
+    its predecessor's row, "path" the whole path from exp(score / T).
+    Returns (path_slot, path_tok, q)."""
+    if mode not in SAMPLE_MODES:
+        raise ValueError(f"mode must be one of {sorted(SAMPLE_MODES)}, got {mode!r}")
     _rank(top_val, 3, "top_val", torch.float32)
     _rank(U, 2, "U")
     B, L, K = top_val.shape
@@ -590,17 +599,21 @@ def pair_sample(top_val: torch.Tensor, top_idx: torch.Tensor, anchor_tok: Option
     if q is None:
         q = torch.empty((B, L, TOPK), dtype=torch.float32, device=dev)
     _dev(top_val, top_idx, anchor_tok, U, Vf, u, gate, S0, S, path_slot, path_tok, q)
-    _check("dflash2_pair_sample", lib().dflash2_pair_sample(
+    _check("dflash2_pair_sample_mode", lib().dflash2_pair_sample_mode(
         _ptr(top_val), _ptr(top_idx), _ptr(anchor_tok), _ptr(U), _ptr(Vf), _ptr(gate), _ptr(u),
-        float(temperature), B, L, V, r, _dt(U), _ptr(S0), _ptr(S) if L > 1 else None,
-        _ptr(path_slot), _ptr(path_tok), _ptr(q), _stream(dev)))
+        float(temperature), B, L, V, r, _dt(U), SAMPLE_MODES[mode], _ptr(S0),
+        _ptr(S) if L > 1 else None, _ptr(path_slot), _ptr(path_tok), _ptr(q), _stream(dev)))
     return path_slot, path_tok, q
 
 
 def path_sample(S0: torch.Tensor, S: Optional[torch.Tensor], top_idx: Optional[torch.Tensor],
-                u: torch.Tensor, temperature: float, path_slot=None, path_tok=None, q=None):
-    """Sampling walk at temperature T with uniforms u [B, L].
-    Returns (path_slot, path_tok, q [B, L, 16])."""
+                u: torch.Tensor, temperature: float, path_slot=None, path_tok=None, q=None,
+                mode: str = "chain"):
+    """Sampling walk at temperature T with uniforms u [B, L]: mode "chain"
+    draws each position from its predecessor's row, "path" the whole path
+    from exp(score / T).  Returns (path_slot, path_tok, q [B, L, 16])."""
+    if mode not in SAMPLE_MODES:
+        raise ValueError(f"mode must be one of {sorted(SAMPLE_MODES)}, got {mode!r}")
     _rank(S0, 2, "S0", torch.float32)
     _rank(u, 2, "u", torch.float32)
     B = S0.shape[0]
@@ -623,9 +636,9 @@ def path_sample(S0: torch.Tensor, S: Optional[torch.Tensor], top_idx: Optional[t
     if q is None:
         q = torch.empty((B, L, TOPK), dtype=torch.float32, device=dev)
     _dev(S0, S, top_idx, u, path_slot, path_tok, q)
-    _check("dflash2_path_sample", lib().dflash2_path_sample(
+    _check("dflash2_path_sample_mode", lib().dflash2_path_sample_mode(
         _ptr(S0), _ptr(S) if L > 1 else None, _ptr(top_idx), _ptr(u), float(temperature), B, L,
-        _ptr(path_slot), _ptr(path_tok), _ptr(q), _stream(dev)))
+        SAMPLE_MODES[mode], _ptr(path_slot), _ptr(path_tok), _ptr(q), _stream(dev)))
     return path_slot, path_tok, q
 
 
@@ -747,8 +760,9 @@ def run_step(buf: StepBuffers, x: torch.Tensor, convs, W, U: torch.Tensor,
     matrix-core corrections), logits + top-16 (W a tensor or a PackedWeight),
     pair scores
     (context-gated from the final hidden states when `Wg` is given), the path
-    walk (`walk`: "viterbi", "greedy", or "sample" at `temperature` with the
-    uniforms `u_path`) and verification: greedy against `target` argmax ids,
+    walk (`walk`: "viterbi", "greedy", "sample" (each position from its
+    predecessor's row) or "sample-path" (the whole path from exp(score / T))
+    at `temperature` with the uniforms `u_path`) and verification: greedy against `target` argmax ids,
     or, for a sampled walk given target logits `z_target` [B, L+1, V], the
     lossless rejection rule with uniforms `u_acc`, `u_res` (each target row's
     log-sum-exp computed only where the accept test reaches it).  A walk that is
@@ -775,16 +789,18 @@ def run_step(buf: StepBuffers, x: torch.Tensor, convs, W, U: torch.Tensor,
         if buf.gate is None:
             raise ValueError("StepBuffers were made without gate_rank")
         gate = context_gate(cur.view(M, H), Wg, buf.gate)
-    if walk != "sample" and target is not None:
+    sampled = walk in ("sample", "sample-path")
+    smode = "path" if walk == "sample-path" else "chain"
+    if not sampled and target is not None:
         pair_select_verify(tv, ti, anchor_tok, U, Vf, target, gate, walk, buf.S0, buf.S,
                            buf.path_slot, buf.path_tok, buf.path_score, buf.accept_len,
                            buf.next_tok)
         return buf
-    if walk == "sample":
+    if sampled:
         if buf.q is None or u_path is None:
             raise ValueError("a sampled walk needs StepBuffers(sample=True) and u_path")
         pair_sample(tv, ti, anchor_tok, U, Vf, u_path, temperature, gate, buf.S0, buf.S,
-                    buf.path_slot, buf.path_tok, buf.q)
+                    buf.path_slot, buf.path_tok, buf.q, mode=smode)
         if z_target is not None:
             verify_rejection_lazy(buf.path_slot, buf.path_tok, buf.q, ti, z_target, temperature,
                                   u_acc, u_res, buf.accept_len, buf.next_tok)

@@ -363,11 +363,15 @@ DFLASH2_API int dflash2_path_select_mode(const float* S0, const float* S, const 
 
 static bool valid_temperature(float T) { return T > 0.f && T <= 1e30f && T == T; }
 
-DFLASH2_API int dflash2_path_sample(const float* S0, const float* S, const int32_t* top_idx,
-                                    const float* u, float temperature, int B, int L,
-                                    int32_t* path_slot, int32_t* path_tok, float* q,
-                                    void* stream) {
-  if (B < 0 || L < 1 || L > DFLASH2_MAX_L || !valid_temperature(temperature))
+static bool valid_sample_mode(int mode) {
+  return mode == DFLASH2_SAMPLE_CHAIN || mode == DFLASH2_SAMPLE_PATH;
+}
+
+static int path_sample(const float* S0, const float* S, const int32_t* top_idx, const float* u,
+                       float temperature, int B, int L, int mode, int32_t* path_slot,
+                       int32_t* path_tok, float* q, void* stream) {
+  if (B < 0 || L < 1 || L > DFLASH2_MAX_L || !valid_temperature(temperature) ||
+      !valid_sample_mode(mode))
     return DFLASH2_EINVAL;
   if (B == 0) return DFLASH2_OK;
   if (!S0 || (L > 1 && !S) || !u || !path_slot || !q) return DFLASH2_EINVAL;
@@ -390,7 +394,23 @@ DFLASH2_API int dflash2_path_sample(const float* S0, const float* S, const int32
       if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return DFLASH2_EINVAL;
   }
   return status_of(launch_path_sample(S0, L > 1 ? S : nullptr, top_idx, u, temperature, B, L,
-                                      path_slot, path_tok, q, as_stream(stream)));
+                                      mode == DFLASH2_SAMPLE_PATH, path_slot, path_tok, q,
+                                      as_stream(stream)));
+}
+
+DFLASH2_API int dflash2_path_sample(const float* S0, const float* S, const int32_t* top_idx,
+                                    const float* u, float temperature, int B, int L,
+                                    int32_t* path_slot, int32_t* path_tok, float* q,
+                                    void* stream) {
+  return path_sample(S0, S, top_idx, u, temperature, B, L, DFLASH2_SAMPLE_CHAIN, path_slot,
+                     path_tok, q, stream);
+}
+
+DFLASH2_API int dflash2_path_sample_mode(const float* S0, const float* S, const int32_t* top_idx,
+                                         const float* u, float temperature, int B, int L,
+                                         int mode, int32_t* path_slot, int32_t* path_tok,
+                                         float* q, void* stream) {
+  return path_sample(S0, S, top_idx, u, temperature, B, L, mode, path_slot, path_tok, q, stream);
 }
 
 DFLASH2_API int dflash2_target_lse(const float* z, int R, int V, float temperature, float* lse,
@@ -524,14 +544,13 @@ DFLASH2_API int dflash2_pair_select_verify(
       accept_len, next_tok, as_stream(stream)));
 }
 
-DFLASH2_API int dflash2_pair_sample(const float* top_val, const int32_t* top_idx,
-                                    const int32_t* anchor_tok, const void* U, const void* Vf,
-                                    const float* gate, const float* u, float temperature, int B,
-                                    int L, int V, int r, int dtype, float* S0, float* S,
-                                    int32_t* path_slot, int32_t* path_tok, float* q,
-                                    void* stream) {
+static int pair_sample(const float* top_val, const int32_t* top_idx, const int32_t* anchor_tok,
+                       const void* U, const void* Vf, const float* gate, const float* u,
+                       float temperature, int B, int L, int V, int r, int dtype, int mode,
+                       float* S0, float* S, int32_t* path_slot, int32_t* path_tok, float* q,
+                       void* stream) {
   if (!valid_dtype(dtype) || B < 0 || L < 1 || L > DFLASH2_MAX_L || V < kTopK || r < 1 ||
-      r > DFLASH2_MAX_RANK || !valid_temperature(temperature))
+      r > DFLASH2_MAX_RANK || !valid_temperature(temperature) || !valid_sample_mode(mode))
     return DFLASH2_EINVAL;
   if (B == 0) return DFLASH2_OK;
   if (!top_val || !top_idx || !U || !Vf || !u || !path_slot || !q) return DFLASH2_EINVAL;
@@ -560,8 +579,30 @@ DFLASH2_API int dflash2_pair_sample(const float* top_val, const int32_t* top_idx
       if (outs[k] && overlap(outs[o], outsz[o], outs[k], outsz[k])) return DFLASH2_EINVAL;
   }
   return status_of(launch_pair_sample(top_val, top_idx, anchor_tok, U, Vf, gate, u, temperature,
-                                      B, L, V, r, dtype, S0, L > 1 ? S : nullptr, path_slot,
-                                      path_tok, q, as_stream(stream)));
+                                      B, L, V, r, dtype, mode == DFLASH2_SAMPLE_PATH, S0,
+                                      L > 1 ? S : nullptr, path_slot, path_tok, q,
+                                      as_stream(stream)));
+}
+
+DFLASH2_API int dflash2_pair_sample(const float* top_val, const int32_t* top_idx,
+                                    const int32_t* anchor_tok, const void* U, const void* Vf,
+                                    const float* gate, const float* u, float temperature, int B,
+                                    int L, int V, int r, int dtype, float* S0, float* S,
+                                    int32_t* path_slot, int32_t* path_tok, float* q,
+                                    void* stream) {
+  return pair_sample(top_val, top_idx, anchor_tok, U, Vf, gate, u, temperature, B, L, V, r, dtype,
+                     DFLASH2_SAMPLE_CHAIN, S0, S, path_slot, path_tok, q, stream);
+}
+
+DFLASH2_API int dflash2_pair_sample_mode(const float* top_val, const int32_t* top_idx,
+                                         const int32_t* anchor_tok, const void* U,
+                                         const void* Vf, const float* gate, const float* u,
+                                         float temperature, int B, int L, int V, int r,
+                                         int dtype, int mode, float* S0, float* S,
+                                         int32_t* path_slot, int32_t* path_tok, float* q,
+                                         void* stream) {
+  return pair_sample(top_val, top_idx, anchor_tok, U, Vf, gate, u, temperature, B, L, V, r, dtype,
+                     mode, S0, S, path_slot, path_tok, q, stream);
 }
 
 // ---------------------------------------------------------------- allocation-free logits + top-16

@@ -106,11 +106,13 @@ hipError_t launch_pair_walk_verify(const float* top_val, const int32_t* top_idx,
                                    int32_t* path_slot, int32_t* path_tok, float* path_score,
                                    int32_t* accept_len, int32_t* next_tok, hipStream_t s);
 // Pair scores + the sampling walk of each block in one launch; S0 / S may be NULL.
+// joint != 0: the whole path drawn from exp(score / T) (backward messages),
+// else the chain sampler.
 hipError_t launch_pair_sample(const float* top_val, const int32_t* top_idx,
                               const int32_t* anchor_tok, const void* U, const void* Vf,
                               const float* gate, const float* u, float temperature, int B, int L,
-                              int V, int r, int dtype, float* S0, float* S, int32_t* path_slot,
-                              int32_t* path_tok, float* q, hipStream_t s);
+                              int V, int r, int dtype, int joint, float* S0, float* S,
+                              int32_t* path_slot, int32_t* path_tok, float* q, hipStream_t s);
 hipError_t launch_pair_score(const float* top_val, const int32_t* top_idx,
                              const int32_t* anchor_tok, const void* U, const void* Vf,
                              const float* gate, int B, int L, int V, int r, int dtype, float* S0,
@@ -124,7 +126,7 @@ hipError_t launch_path_select(const float* S0, const float* S, const int32_t* to
                               float* path_score, hipStream_t s);
 
 hipError_t launch_path_sample(const float* S0, const float* S, const int32_t* top_idx,
-                              const float* u, float temperature, int B, int L,
+                              const float* u, float temperature, int B, int L, int joint,
                               int32_t* path_slot, int32_t* path_tok, float* q, hipStream_t s);
 
 hipError_t launch_target_lse(const float* z, int R, int V, float temperature, float* lse,

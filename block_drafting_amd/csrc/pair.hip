@@ -281,17 +281,19 @@ __global__ __launch_bounds__(64 * pwv_max_waves<RC>()) void pair_sample_kernel(
     const float* __restrict__ top_val, const int32_t* __restrict__ top_idx,
     const int32_t* __restrict__ anchor_tok, const T* __restrict__ U, const T* __restrict__ Vf,
     const float* __restrict__ gate, const float* __restrict__ u, float inv_t, int L, int V, int r,
-    float* __restrict__ S0out, float* __restrict__ Sout, int32_t* __restrict__ path_slot,
-    int32_t* __restrict__ path_tok, float* __restrict__ qout) {
+    int joint, float* __restrict__ S0out, float* __restrict__ Sout,
+    int32_t* __restrict__ path_slot, int32_t* __restrict__ path_tok, float* __restrict__ qout) {
   extern __shared__ float sS[];  // (L - 1) x 16 x 16 scores
   __shared__ float sS0[kTopK];
+  __shared__ float sbeta[kMaxWalk * kTopK];  // backward messages (whole-path draws)
   const int b = blockIdx.x;
   pair_phase<T, RC, VEC>(top_val, top_idx, anchor_tok, U, Vf, gate, b, L, V, r, sS, sS0, S0out,
                          Sout);
   __syncthreads();
   if ((threadIdx.x >> 6) != 0) return;
+  if (joint) path_messages(sS, inv_t, L, sbeta);
   sample_walk(sS0[threadIdx.x & 15], sS, top_idx, u + (size_t)b * L, inv_t, b, L, path_slot,
-              path_tok, qout);
+              path_tok, qout, joint ? sbeta : nullptr);
 }
 
 template <typename T, int RC>
@@ -427,28 +429,30 @@ namespace {
 template <typename T, int RC>
 void launch_ps_rc(bool vec, dim3 grid, size_t lds, hipStream_t s, const float* top_val,
                   const int32_t* top_idx, const int32_t* anchor_tok, const void* U, const void* Vf,
-                  const float* gate, const float* u, float inv_t, int L, int V, int r, float* S0,
-                  float* S, int32_t* path_slot, int32_t* path_tok, float* q) {
+                  const float* gate, const float* u, float inv_t, int L, int V, int r, int joint,
+                  float* S0, float* S, int32_t* path_slot, int32_t* path_tok, float* q) {
   const T* uu = static_cast<const T*>(U);
   const T* vv = static_cast<const T*>(Vf);
   const dim3 block((unsigned)(64 * min(L, pwv_max_waves<RC>())));
   if (vec)
     hipLaunchKernelGGL((pair_sample_kernel<T, RC, true>), grid, block, lds, s, top_val, top_idx,
-                       anchor_tok, uu, vv, gate, u, inv_t, L, V, r, S0, S, path_slot, path_tok, q);
+                       anchor_tok, uu, vv, gate, u, inv_t, L, V, r, joint, S0, S, path_slot,
+                       path_tok, q);
   else
     hipLaunchKernelGGL((pair_sample_kernel<T, RC, false>), grid, block, lds, s, top_val, top_idx,
-                       anchor_tok, uu, vv, gate, u, inv_t, L, V, r, S0, S, path_slot, path_tok, q);
+                       anchor_tok, uu, vv, gate, u, inv_t, L, V, r, joint, S0, S, path_slot,
+                       path_tok, q);
 }
 
 template <typename T>
 void launch_ps_t(bool vec, dim3 grid, size_t lds, hipStream_t s, const float* top_val,
                  const int32_t* top_idx, const int32_t* anchor_tok, const void* U, const void* Vf,
-                 const float* gate, const float* u, float inv_t, int L, int V, int r, float* S0,
-                 float* S, int32_t* path_slot, int32_t* path_tok, float* q) {
+                 const float* gate, const float* u, float inv_t, int L, int V, int r, int joint,
+                 float* S0, float* S, int32_t* path_slot, int32_t* path_tok, float* q) {
   const int rc = (r + 3) / 4;
 #define DFLASH2_PS(RC)                                                                          \
   launch_ps_rc<T, RC>(vec, grid, lds, s, top_val, top_idx, anchor_tok, U, Vf, gate, u, inv_t, L, \
-                      V, r, S0, S, path_slot, path_tok, q)
+                      V, r, joint, S0, S, path_slot, path_tok, q)
   if (rc <= 8)
     DFLASH2_PS(8);
   else if (rc <= 16)
@@ -464,8 +468,8 @@ void launch_ps_t(bool vec, dim3 grid, size_t lds, hipStream_t s, const float* to
 hipError_t launch_pair_sample(const float* top_val, const int32_t* top_idx,
                               const int32_t* anchor_tok, const void* U, const void* Vf,
                               const float* gate, const float* u, float temperature, int B, int L,
-                              int V, int r, int dtype, float* S0, float* S, int32_t* path_slot,
-                              int32_t* path_tok, float* q, hipStream_t s) {
+                              int V, int r, int dtype, int joint, float* S0, float* S,
+                              int32_t* path_slot, int32_t* path_tok, float* q, hipStream_t s) {
   if (B == 0) return hipSuccess;
   const dim3 grid((unsigned)B);
   const size_t lds = (size_t)(L - 1) * kTopK * kTopK * sizeof(float);
@@ -474,11 +478,12 @@ hipError_t launch_pair_sample(const float* top_val, const int32_t* top_idx,
                           reinterpret_cast<uintptr_t>(gate);
   if (dtype == 1)
     launch_ps_t<uint16_t>(r % 32 == 0 && (bases & 15) == 0, grid, lds, s, top_val, top_idx,
-                          anchor_tok, U, Vf, gate, u, inv_t, L, V, r, S0, S, path_slot, path_tok,
-                          q);
+                          anchor_tok, U, Vf, gate, u, inv_t, L, V, r, joint, S0, S, path_slot,
+                          path_tok, q);
   else
     launch_ps_t<float>(r % 16 == 0 && (bases & 15) == 0, grid, lds, s, top_val, top_idx,
-                       anchor_tok, U, Vf, gate, u, inv_t, L, V, r, S0, S, path_slot, path_tok, q);
+                       anchor_tok, U, Vf, gate, u, inv_t, L, V, r, joint, S0, S, path_slot,
+                       path_tok, q);
   return hipGetLastError();
 }
 

@@ -37,9 +37,10 @@ namespace {
 // ---------------------------------------------------------------- path sampling
 __global__ __launch_bounds__(64) void path_sample_kernel(
     const float* __restrict__ S0, const float* __restrict__ S, const int32_t* __restrict__ top_idx,
-    const float* __restrict__ u, float inv_t, int L, int32_t* __restrict__ path_slot,
+    const float* __restrict__ u, float inv_t, int L, int joint, int32_t* __restrict__ path_slot,
     int32_t* __restrict__ path_tok, float* __restrict__ q) {
   extern __shared__ f32x4_t stage[];  // (L-1) * 64 vectors of 4 scores
+  __shared__ float sbeta[kMaxWalk * kTopK];  // backward messages (whole-path draws)
   constexpr int kUnroll = 8;
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
@@ -62,8 +63,10 @@ __global__ __launch_bounds__(64) void path_sample_kernel(
   float s = S0[(size_t)b * kTopK + j];
   const size_t row = (size_t)b * L;
   __syncthreads();
-  sample_walk(s, reinterpret_cast<const float*>(stage), top_idx, u + row, inv_t, b, L, path_slot,
-              path_tok, q);
+  const float* sS = reinterpret_cast<const float*>(stage);
+  if (joint) path_messages(sS, inv_t, L, sbeta);
+  sample_walk(s, sS, top_idx, u + row, inv_t, b, L, path_slot, path_tok, q,
+              joint ? sbeta : nullptr);
 }
 
 // ---------------------------------------------------------------- target log-sum-exp
@@ -568,12 +571,12 @@ __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_lazy_kernel(
 }  // namespace
 
 hipError_t launch_path_sample(const float* S0, const float* S, const int32_t* top_idx,
-                              const float* u, float temperature, int B, int L,
+                              const float* u, float temperature, int B, int L, int joint,
                               int32_t* path_slot, int32_t* path_tok, float* q, hipStream_t s) {
   if (B == 0) return hipSuccess;
   const size_t lds = (size_t)(L - 1) * kTopK * kTopK * sizeof(float);
   hipLaunchKernelGGL(path_sample_kernel, dim3((unsigned)B), dim3(64), lds, s, S0, S, top_idx, u,
-                     1.0f / temperature, L, path_slot, path_tok, q);
+                     1.0f / temperature, L, joint, path_slot, path_tok, q);
   return hipGetLastError();
 }
 

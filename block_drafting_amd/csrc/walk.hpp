@@ -197,14 +197,48 @@ __device__ __forceinline__ int greedy_walk(const float* S0b, const float* sS,
   return walk_finish(my_slot, top_idx, b, L, path_slot, path_tok, sslot);
 }
 
-// Sampling walk at temperature T = 1 / inv_t, the sampling twin of the greedy
-// walk: position t's slot is drawn from softmax(row / T) of the successors of
-// the slot drawn before, by inverse CDF in slot order with the uniform u[t].
-// s: this lane's S0 value (candidate j = lane & 15); sS: this block's scores
-// in LDS; u [L]: this block's uniforms; q receives every position's proposal.
+// Backward messages of the whole-path distribution P(path) proportional to
+// exp(score / T), the sampling twin of the max-plus walk: beta[L-1][.] = 0,
+//   beta[t][i] = log sum_j exp(S[t, i, j] / T + beta[t+1][j]),  t = L-2 .. 0,
+// in fp32 with each row shifted by its maximum.  Lane (q, j) = (lane >> 4,
+// lane & 15) holds S[t, 4q + ii, j] for ii < 4; each row's max and sum reduce
+// over the 16 lanes of its quarter (DPP), and lane (q, ii) writes row 4q + ii.
+// sS: this block's scores in LDS; beta: [L][16] in LDS.  One wave.
+__device__ __forceinline__ void path_messages(const float* sS, float inv_t, int L, float* beta) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15;
+  const int q = lane >> 4;
+  if (lane < kTopK) beta[(L - 1) * kTopK + lane] = 0.f;
+  __builtin_amdgcn_wave_barrier();
+  for (int t = L - 2; t >= 0; --t) {
+    const float bn = beta[(t + 1) * kTopK + j];
+    float mine = 0.f;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const float a = sS[(t * kTopK + 4 * q + ii) * kTopK + j] * inv_t + bn;
+      const float m = group16_max(a);
+      const float z = group16_sum(expf(a - m));
+      if (j == ii) mine = m + logf(z);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (j < 4) beta[t * kTopK + 4 * q + j] = mine;
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Sampling walk at temperature T = 1 / inv_t.  Without messages (beta
+// NULL), the sampling twin of the greedy walk: position t's slot is drawn
+// from softmax(row / T) of the successors of the slot drawn before.  With
+// the backward messages of path_messages, a draw of the whole path from
+// exp(score / T): position t's slot is drawn from softmax(row / T +
+// beta[t]), the conditional of slot t given the slots before it.  Draws are
+// by inverse CDF in slot order with the uniform u[t].  s: this lane's S0
+// value (candidate j = lane & 15); sS: this block's scores in LDS; u [L]:
+// this block's uniforms; q receives every position's proposal.
 __device__ __forceinline__ int sample_walk(float s, const float* sS, const int32_t* top_idx,
                                            const float* u, float inv_t, int b, int L,
-                                           int32_t* path_slot, int32_t* path_tok, float* q) {
+                                           int32_t* path_slot, int32_t* path_tok, float* q,
+                                           const float* beta = nullptr) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15;
   const size_t row = (size_t)b * L;
@@ -214,8 +248,14 @@ __device__ __forceinline__ int sample_walk(float s, const float* sS, const int32
   for (int t = 0; t < L; ++t) {
     if (t > 0) s = sS[((t - 1) * kTopK + p) * kTopK + j];
     // softmax over the 16 lanes of each quarter (all four quarters agree)
-    const float m = group16_max(s);
-    const float e = expf((s - m) * inv_t);
+    float e;
+    if (beta) {
+      const float a = s * inv_t + beta[t * kTopK + j];
+      e = expf(a - group16_max(a));
+    } else {
+      const float m = group16_max(s);
+      e = expf((s - m) * inv_t);
+    }
     const float z = group16_sum(e);
     const float qj = e / z;
     // inclusive prefix sum in slot order

@@ -14,8 +14,8 @@
  *   context-gated pair scores        dflash2_context_gate, dflash2_pair_score_gated
  *   best-successor (greedy) walk     dflash2_path_select_mode(..., DFLASH2_PATH_GREEDY, ...)
  *   steps 3-5 in one launch          dflash2_pair_select_verify
- *   scores + sampling walk, one launch  dflash2_pair_sample
- *   sampling at T > 0, lossless      dflash2_path_sample, dflash2_target_lse,
+ *   scores + sampling walk, one launch  dflash2_pair_sample (_mode: whole-path draws)
+ *   sampling at T > 0, lossless      dflash2_path_sample (_mode), dflash2_target_lse,
  *   rejection verification           dflash2_verify_rejection
  *                                    (dflash2_verify_rejection_lazy: no lse pass)
  *
@@ -70,6 +70,9 @@ typedef enum {
 
 /* Path walks of dflash2_path_select_mode. */
 typedef enum { DFLASH2_PATH_VITERBI = 0, DFLASH2_PATH_GREEDY = 1 } dflash2_path_mode;
+/* What a sampling walk draws: each position from its chosen predecessor's
+ * row (CHAIN), or the whole path from exp(score / T) (PATH). */
+typedef enum { DFLASH2_SAMPLE_CHAIN = 0, DFLASH2_SAMPLE_PATH = 1 } dflash2_sample_mode;
 
 #define DFLASH2_TOPK 16      /* candidates per position ([POST] "A lightweight path selector") */
 #define DFLASH2_MAX_L 64     /* longest block the path walk accepts */
@@ -341,6 +344,27 @@ int dflash2_path_sample(const float* S0, const float* S, const int32_t* top_idx,
                         int32_t* path_slot, int32_t* path_tok, float* q, void* stream);
 
 /*
+ * dflash2_path_sample with a choice of what is drawn.  DFLASH2_SAMPLE_CHAIN
+ * is dflash2_path_sample.  DFLASH2_SAMPLE_PATH draws the whole slot path
+ * from the distribution the same scores define over all 16^L paths, the
+ * sampling twin of the max-plus walk ([POST] "A lightweight path selector":
+ * sampling draws from the precomputed scores):
+ *   P(p) proportional to exp(score(p) / T),
+ *   score(p) = S0[p_0] + sum_t S[t-1, p_{t-1}, p_t].
+ * Drawn by backward messages, then forward draws:
+ *   beta[L-1][.] = 0,  beta[t][i] = log sum_j exp(S[b,t,i,j] / T + beta[t+1][j]),
+ *   q[b,0,:] = softmax(S0[b] / T + beta[0]),
+ *   q[b,t,:] = softmax(S[b,t-1,p_{t-1},:] / T + beta[t]),
+ * each p_t by inverse CDF with u[b,t] as above, so q[b,t] is position t's
+ * proposal given the slots before it (what dflash2_verify_rejection needs).
+ * fp32 messages (each row shifted by its maximum), softmax and sums.  Other
+ * mode values: EINVAL.  Everything else as for dflash2_path_sample.
+ */
+int dflash2_path_sample_mode(const float* S0, const float* S, const int32_t* top_idx,
+                             const float* u, float temperature, int B, int L, int mode,
+                             int32_t* path_slot, int32_t* path_tok, float* q, void* stream);
+
+/*
  * Log-sum-exp of target logits at temperature T:
  *   lse[r] = log sum_v exp(z[r, v] / T),  z [R, V] fp32 (16-byte aligned),
  * lse [R] fp32.  -inf entries carry no mass.  One pass over z.
@@ -437,6 +461,17 @@ int dflash2_pair_sample(const float* top_val, const int32_t* top_idx,
                         const float* gate, const float* u, float temperature, int B, int L,
                         int V, int r, int dtype, float* S0, float* S, int32_t* path_slot,
                         int32_t* path_tok, float* q, void* stream);
+
+/*
+ * dflash2_pair_sample with the sampling walk's mode (dflash2_sample_mode,
+ * as in dflash2_path_sample_mode); bit for bit dflash2_pair_score(_gated)
+ * followed by dflash2_path_sample_mode.  Other mode values: EINVAL.
+ */
+int dflash2_pair_sample_mode(const float* top_val, const int32_t* top_idx,
+                             const int32_t* anchor_tok, const void* U, const void* Vf,
+                             const float* gate, const float* u, float temperature, int B, int L,
+                             int V, int r, int dtype, int mode, float* S0, float* S,
+                             int32_t* path_slot, int32_t* path_tok, float* q, void* stream);
 
 #ifdef __cplusplus
 }

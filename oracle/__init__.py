@@ -36,6 +36,7 @@ from .cpu_oracle import (  # noqa: F401
     path_margin,
     verify_greedy,
     sample_path,
+    sample_path_joint,
     sample_margin,
     target_lse,
     rejection_verify,

@@ -396,6 +396,59 @@ def sample_path(S0: np.ndarray, S: np.ndarray, top_idx: np.ndarray, T: float, u:
     return slot.astype(np.int32), tok.astype(np.int32), q
 
 
+def sample_path_joint(S0: np.ndarray, S: np.ndarray, top_idx: np.ndarray, T: float,
+                      u: np.ndarray):
+    """Sampling of a whole path from the same scores ([POST] "A lightweight
+    path selector": sampling draws from the precomputed scores), the
+    sampling twin of the max-plus walk: a slot path p is drawn with
+    probability proportional to exp(score(p) / T), where
+    score(p) = S0[p_0] + sum_t S[t-1, p_{t-1}, p_t].
+
+    Reading: where the max-plus walk takes the best path, this draws from
+    the distribution over all 16^L paths that the same scores define.  It is
+    drawn by backward messages and forward draws (the same distribution as
+    forward filtering and backward sampling; the forward order gives each
+    position's proposal conditioned on the slots before it, which is what
+    the rejection verification reads):
+      beta_{L-1}[j] = 0,
+      beta_t[i] = log sum_j exp(S[t, i, j] / T + beta_{t+1}[j])   (t = L-2 .. 0),
+      q_0[j] proportional to exp(S0[j] / T + beta_0[j]),
+      q_t[j] proportional to exp(S[t-1, p_{t-1}, j] / T + beta_t[j]),
+    each p_t drawn by inverse CDF in slot order with u[b, t] (as in
+    sample_path; if rounding leaves u above the last sum, the last slot with
+    q > 0).  fp64 throughout.
+    Returns (slot int32 [B, L], tok int32 [B, L], q fp64 [B, L, 16]): q[b, t]
+    is the conditional proposal position t's token was drawn from.
+    """
+    S0 = np.asarray(S0, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    B = S0.shape[0]
+    L = S.shape[1] + 1
+    b = np.arange(B)
+
+    def lse(a, axis):
+        m = a.max(axis=axis, keepdims=True)
+        return (m + np.log(np.exp(a - m).sum(axis=axis, keepdims=True))).squeeze(axis)
+
+    beta = np.zeros((B, L, K))
+    for t in range(L - 2, -1, -1):
+        beta[:, t] = lse(S[:, t] / T + beta[:, t + 1][:, None, :], axis=2)
+    slot = np.zeros((B, L), dtype=np.int64)
+    q = np.zeros((B, L, K))
+    for t in range(L):
+        row = S0 if t == 0 else S[b, t - 1, slot[:, t - 1]]
+        a = row / T + beta[:, t]
+        e = np.exp(a - a.max(axis=1, keepdims=True))
+        q[:, t] = e / e.sum(axis=1, keepdims=True)
+        cum = np.cumsum(q[:, t], axis=1)
+        j = (u[:, t, None] >= cum).sum(axis=1)          # first j with u < cum_j
+        last = K - 1 - np.argmax(q[:, t, ::-1] > 0, axis=1)
+        slot[:, t] = np.minimum(j, last)
+    tok = np.take_along_axis(np.asarray(top_idx), slot[:, :, None], axis=2)[:, :, 0]
+    return slot.astype(np.int32), tok.astype(np.int32), q
+
+
 def sample_margin(q: np.ndarray, u: np.ndarray) -> np.ndarray:
     """Distance of each uniform to the nearest boundary of its inverse-CDF
     bins (fp64, [B, L]): a perturbation of the probabilities smaller than
@@ -528,6 +581,8 @@ def run_step_head(w, inp: Dict[str, object], y: np.ndarray,
     q = score = None
     if walk == "sample":
         slot, tok, q = sample_path(S0, S, ti, w.temperature, u_path)
+    elif walk == "sample-path":
+        slot, tok, q = sample_path_joint(S0, S, ti, w.temperature, u_path)
     else:
         slot, tok, score = (path_select_greedy if walk == "greedy" else path_select)(S0, S, ti)
     return {"y": y, "z": z, "top_val": tv, "top_idx": ti, "gate": gate, "S0": S0, "S": S,

@@ -371,3 +371,21 @@ def test_logits_topk_noalloc_validation():
     assert call(M=7062) == ESCRATCH                      # 7062 * 594 * 4 > 16 MiB
     assert call(M=4096, V=1 << 20) == ESCRATCH
     assert bd.lib().dflash2_strerror(ESCRATCH).startswith(b"problem larger")
+
+
+def test_sample_mode_validation():
+    """The sampling calls' mode argument: chain (0) or whole path (1); any
+    other value is refused before any launch."""
+    L = bd.lib()
+    f = L.dflash2_path_sample_mode
+    S0, S, u, slot, q = P, P + 0x10000, P + 0x80000, P + 0x90000, P + 0xA0000
+    assert f(S0, S, None, u, 1.0, 0, 4, 1, slot, None, q, None) == 0      # empty batch
+    assert f(S0, S, None, u, 1.0, 2, 4, 2, slot, None, q, None) == EINVAL
+    assert f(S0, S, None, u, 1.0, 2, 4, -1, slot, None, q, None) == EINVAL
+    assert f(S0, S, None, u, 0.0, 2, 4, 1, slot, None, q, None) == EINVAL  # T must be > 0
+    g = L.dflash2_pair_sample_mode
+    tv, ti, U, Vf = P, P + 0x10000, P + 0x100000, P + 0x200000
+    args = lambda mode, B=2: (tv, ti, None, U, Vf, None, u + 0x400000, 1.0, B, 4, 1000, 8, 1,
+                              mode, None, None, slot + 0x400000, None, q + 0x400000, None)
+    assert g(*args(1, B=0)) == 0
+    assert g(*args(3)) == EINVAL

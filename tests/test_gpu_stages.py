@@ -618,6 +618,81 @@ def test_path_sample_parity(B, L, T):
     np.testing.assert_allclose(q.sum(axis=2), 1.0, atol=2e-6)
 
 
+def joint_sample_tol(S0, S, T):
+    """Bound on |q_gpu - q_oracle| for whole-path draws.  The backward
+    message beta_t is a chain of L - 1 - t fp32 log-sum-exps over values of
+    magnitude at most max|S| / T + beta_{t+1}; each adds a few roundings of
+    2^-24 relative, so |d beta| <= 4 2^-24 L (max|S| / T + log 16) and
+    |dq| <= 2 |da| q.  Twice that again for the softmax's own roundings; an
+    fp32 emulation of the kernel stays 10x or more inside it."""
+    L = (S.shape[1] if S is not None and S.ndim == 4 else 0) + 1
+    smax = max(float(np.abs(S0).max()), float(np.abs(S).max()) if L > 1 else 0.0)
+    return 8 * 2.0 ** -24 * L * (smax / T + 4.0)
+
+
+@pytest.mark.parametrize("B,L,T", [(1, 1, 1.0), (7, 2, 0.7), (64, 8, 1.0), (33, 16, 2.0),
+                                   (5, 64, 1.0), (300, 3, 0.3), (64, 16, 0.5)])
+def test_path_sample_whole_path_parity(B, L, T):
+    """Whole-path draws (backward messages, forward draws) against the
+    oracle's fp64 sampler: slots equal wherever the uniform is clear of every
+    bin edge by the fp32 messages' error bound, proposals within it."""
+    g = np.random.default_rng(B * L + 11)
+    S0 = (g.standard_normal((B, 16)) * 2).astype(np.float32)
+    S = (g.standard_normal((B, L - 1, 16, 16)) * 1.5).astype(np.float32)
+    ti = g.integers(0, 151936, (B, L, 16)).astype(np.int32)
+    u = g.random((B, L)).astype(np.float32)
+    ws, wt, wq = O.sample_path_joint(S0, S, ti, T, u)
+    slot, tok, q = bd.path_sample(torch.from_numpy(S0).to(DEV),
+                                  torch.from_numpy(S).to(DEV) if L > 1 else None,
+                                  torch.from_numpy(ti).to(DEV), torch.from_numpy(u).to(DEV), T,
+                                  mode="path")
+    slot, tok, q = slot.cpu().numpy(), tok.cpu().numpy(), q.cpu().numpy()
+    tol = joint_sample_tol(S0, S, T)
+    k = decided_prefix(O.sample_margin(wq, u), tol)
+    # a position is undecided with probability ~32 tol (~1% at L = 64), so
+    # long blocks are compared up to their first undecided position
+    assert k.mean() >= min(0.9 * L, 16), k.mean()
+    for b in range(B):
+        assert slot[b, :k[b]].tolist() == ws[b, :k[b]].tolist(), b
+        assert tok[b, :k[b]].tolist() == wt[b, :k[b]].tolist(), b
+        upto = min(k[b] + 1, L)
+        assert np.abs(q[b, :upto] - wq[b, :upto]).max() <= tol, b
+    np.testing.assert_allclose(q.sum(axis=2), 1.0, atol=2e-6)
+    if L == 1:                                  # one position: the chain sampler's draw
+        c = bd.path_sample(torch.from_numpy(S0).to(DEV), None, torch.from_numpy(ti).to(DEV),
+                           torch.from_numpy(u).to(DEV), T)
+        np.testing.assert_array_equal(c[0].cpu().numpy(), slot)
+
+
+def test_whole_path_draws_follow_the_path_distribution_on_gpu():
+    """GPU draws of whole paths (L = 3, one score set, 200,000 blocks) against
+    the enumerated distribution exp(score / T) over all 4096 paths."""
+    from scipy.stats import chisquare
+    import itertools
+
+    g = np.random.default_rng(44)
+    N, L, T = 200000, 3, 1.0
+    S0 = (g.standard_normal(16) * 1.5).astype(np.float32)
+    S = (g.standard_normal((L - 1, 16, 16)) * 1.5).astype(np.float32)
+    paths = np.array(list(itertools.product(range(16), repeat=L)))
+    sc = S0[paths[:, 0]].astype(np.float64)
+    for t in range(1, L):
+        sc = sc + S[t - 1, paths[:, t - 1], paths[:, t]]
+    probs = np.exp((sc - sc.max()) / T)
+    probs /= probs.sum()
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    slot, _, _ = bd.path_sample(d(np.broadcast_to(S0, (N, 16))),
+                                d(np.broadcast_to(S, (N, L - 1, 16, 16))), None,
+                                d(g.random((N, L)).astype(np.float32)), T, mode="path")
+    idx = (slot.cpu().numpy().astype(np.int64) * np.array([256, 16, 1])).sum(axis=1)
+    counts = np.bincount(idx, minlength=4096)
+    exp = probs * N
+    big = exp >= 5
+    obs = np.concatenate([counts[big], [counts[~big].sum()]])
+    ex = np.concatenate([exp[big], [exp[~big].sum()]])
+    assert chisquare(obs, ex).pvalue > 1e-4
+
+
 @pytest.mark.parametrize("R,V,T,neg", [(1, 16, 1.0, False), (7, 1001, 0.7, False),
                                        (64, 151936, 1.0, False), (3, 4096, 2.0, True)])
 def test_target_lse_parity(R, V, T, neg):
@@ -791,8 +866,8 @@ def test_verify_rejection_draw_past_the_last_prefix(lazy):
     np.testing.assert_array_equal(nx[same], wn[same])      # the last token with mass
 
 
-@pytest.mark.parametrize("lazy", [False, True])
-def test_rejection_sampling_is_lossless_on_gpu(lazy):
+@pytest.mark.parametrize("lazy,mode", [(False, "chain"), (True, "chain"), (True, "path")])
+def test_rejection_sampling_is_lossless_on_gpu(lazy, mode):
     # the whole sampled walk + verification on the GPU: emitted tokens follow
     # the target's softmax (chi-square on a 24-token vocabulary)
     from scipy.stats import chisquare
@@ -806,7 +881,8 @@ def test_rejection_sampling_is_lossless_on_gpu(lazy):
                          (N, L, 16)).copy()
     zt = (g.standard_normal((L + 1, V)) * 1.5).astype(np.float32)
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
-    slot, tok, q = bd.path_sample(d(S0), d(S), d(ti), d(g.random((N, L)).astype(np.float32)), T)
+    slot, tok, q = bd.path_sample(d(S0), d(S), d(ti), d(g.random((N, L)).astype(np.float32)), T,
+                                  mode=mode)
     zd = d(np.broadcast_to(zt, (N, L + 1, V)))
     ua, ur = d(g.random((N, L)).astype(np.float32)), d(g.random(N).astype(np.float32))
     if lazy:
@@ -959,12 +1035,13 @@ def test_fused_pair_walk_verify_empty_batch():
     assert all(t.shape[0] == 0 for t in out)
 
 
+@pytest.mark.parametrize("mode", ["chain", "path"])
 @pytest.mark.parametrize("dt,B,L,V,r,gated,T", [
     ("f32", 1, 1, 64, 1, False, 1.0), ("bf16", 3, 2, 500, 7, True, 0.7),
     ("bf16", 64, 8, 4096, 32, False, 1.0), ("f32", 5, 16, 151936, 64, True, 2.0),
     ("bf16", 40, 8, 151936, 64, False, 1.0), ("bf16", 9, 17, 2000, 128, True, 1.0),
     ("bf16", 3, 64, 1000, 256, False, 0.5), ("f32", 300, 3, 700, 8, False, 1.0)])
-def test_fused_pair_sample_matches_the_separate_calls(dt, B, L, V, r, gated, T):
+def test_fused_pair_sample_matches_the_separate_calls(dt, B, L, V, r, gated, T, mode):
     tv, ti, at, U, Vf = _pair_case(B, L, V, r, dt, seed=B * 5 + L + r)
     g = np.random.default_rng(B + L)
     gate = g.random((B, L, r)).astype(np.float32) if gated else None
@@ -974,19 +1051,27 @@ def test_fused_pair_sample_matches_the_separate_calls(dt, B, L, V, r, gated, T):
              gate=None if gate is None else torch.from_numpy(gate).to(DEV),
              u=torch.from_numpy(u).to(DEV))
     S0, S = bd.pair_score(d["tv"], d["ti"], d["at"], d["U"], d["Vf"], gate=d["gate"])
-    slot, tok, q = bd.path_sample(S0, S if L > 1 else None, d["ti"], d["u"], T)
+    slot, tok, q = bd.path_sample(S0, S if L > 1 else None, d["ti"], d["u"], T, mode=mode)
     fS0 = torch.full_like(S0, 7.0)
     fS = torch.full_like(S, 7.0)
-    f = bd.pair_sample(d["tv"], d["ti"], d["at"], d["U"], d["Vf"], d["u"], T, d["gate"], fS0, fS)
+    f = bd.pair_sample(d["tv"], d["ti"], d["at"], d["U"], d["Vf"], d["u"], T, d["gate"], fS0, fS,
+                       mode=mode)
     assert torch.equal(fS0, S0) and torch.equal(fS, S)
     for got, want in zip(f, (slot, tok, q)):
         assert torch.equal(got, want)
-    g2 = bd.pair_sample(d["tv"], d["ti"], d["at"], d["U"], d["Vf"], d["u"], T, d["gate"])
+    g2 = bd.pair_sample(d["tv"], d["ti"], d["at"], d["U"], d["Vf"], d["u"], T, d["gate"],
+                        mode=mode)
     for got, want in zip(g2, (slot, tok, q)):
         assert torch.equal(got, want)
     # the walk follows the oracle's sampling rule on the kernel's scores
-    ws, wt, wq = O.sample_path(S0.cpu().numpy(), S.cpu().numpy(), ti, T, u)
-    k = decided_prefix(O.sample_margin(wq, u), SAMPLE_TOL)
+    S0n, Sn = S0.cpu().numpy(), S.cpu().numpy()
+    if mode == "path":
+        ws, wt, wq = O.sample_path_joint(S0n, Sn, ti, T, u)
+        tol = joint_sample_tol(S0n, Sn, T)
+    else:
+        ws, wt, wq = O.sample_path(S0n, Sn, ti, T, u)
+        tol = SAMPLE_TOL
+    k = decided_prefix(O.sample_margin(wq, u), tol)
     s_np = f[0].cpu().numpy()
     for b in range(B):
         np.testing.assert_array_equal(s_np[b, :k[b]], ws[b, :k[b]])

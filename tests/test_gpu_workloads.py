@@ -38,7 +38,8 @@ import block_drafting_amd as bd
 import oracle as O
 import workloads as WL
 from _devutil import bf16_ulp, convs_to_dev, to_dev, to_host_bits
-from test_gpu_stages import SAMPLE_TOL, check_rejection, conv_mm_tolerance, decided_prefix
+from test_gpu_stages import (SAMPLE_TOL, check_rejection, conv_mm_tolerance, decided_prefix,
+                             joint_sample_tol)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -169,13 +170,16 @@ def test_topk_pair_select_verify_stagewise(case):
     dti = torch.from_numpy(ora["top_idx"]).to(DEV)
     if w.temperature > 0:
         u = case["inp"]["u_path"][case["blocks"]]
-        slot, tok, q = bd.path_sample(dS0, dS, dti, to_dev(u, "f32"), w.temperature)
-        k = decided_prefix(O.sample_margin(ora["q"], u), SAMPLE_TOL)
+        joint = w.walk == "sample-path"
+        slot, tok, q = bd.path_sample(dS0, dS, dti, to_dev(u, "f32"), w.temperature,
+                                      mode="path" if joint else "chain")
+        tol = joint_sample_tol(ora["S0"], ora["S"], w.temperature) if joint else SAMPLE_TOL
+        k = decided_prefix(O.sample_margin(ora["q"], u), tol)
         slot, tok, q = slot.cpu().numpy(), tok.cpu().numpy(), q.cpu().numpy()
         for b in range(Bs):
             assert slot[b, :k[b]].tolist() == ora["path_slot"][b, :k[b]].tolist()
             upto = min(k[b] + 1, w.L)
-            assert np.abs(q[b, :upto] - ora["q"][b, :upto]).max() <= 2e-6
+            assert np.abs(q[b, :upto] - ora["q"][b, :upto]).max() <= (tol if joint else 2e-6)
         # verification fed the oracle's path and proposals (as fp32)
         qf = ora["q"].astype(np.float32)
         zt = case["zt_sub"]
@@ -296,9 +300,11 @@ def test_end_to_end_subset(case):
     slot = buf.path_slot.cpu().numpy()[blocks]
     tok = buf.path_tok.cpu().numpy()[blocks]
     acc = buf.accept_len.cpu().numpy()[blocks]
-    if w.walk == "sample":
+    if w.walk in ("sample", "sample-path"):
         # a draw is decided when its uniform is farther from every bin edge
-        # than the scores' drift can move the edges (|dq| <= 2 |dS| / T)
+        # than the scores' drift can move the edges (|dq| <= 2 |dS| / T; the
+        # whole-path draws carry it through L messages, and the fp32 messages'
+        # own error)
         S_g = buf.S.cpu().numpy()[blocks]
         S0_g = buf.S0.cpu().numpy()[blocks]
         same_cands = (ti == ora["top_idx"]).all(axis=(1, 2))
@@ -309,7 +315,12 @@ def test_end_to_end_subset(case):
             drift = max(np.abs(S_g[k] - ora["S"][k]).max() if L > 1 else 0.0,
                         np.abs(S0_g[k] - ora["S0"][k]).max())
             m = O.sample_margin(ora["q"][k:k + 1], case["inp"]["u_path"][blocks[k:k + 1]])
-            if (m > SAMPLE_TOL + 2 * 16 * drift / w.temperature).all():
+            if w.walk == "sample-path":
+                tol = (joint_sample_tol(ora["S0"][k], ora["S"][k], w.temperature)
+                       + 2 * 16 * L * drift / w.temperature)
+            else:
+                tol = SAMPLE_TOL + 2 * 16 * drift / w.temperature
+            if (m > tol).all():
                 n_exact += 1
                 assert slot[k].tolist() == ora["path_slot"][k].tolist(), k
         print(f"e2e: logits max |dz| {zdrift:.2e}; sampled paths checked exactly {n_exact}/{len(blocks)}")
@@ -373,15 +384,27 @@ def test_properties_all_blocks(case):
     acc = buf.accept_len.cpu().numpy()
     nxt = buf.next_tok.cpu().numpy()
     assert ((acc >= 1) & (acc <= L + 1)).all()
-    if w.walk == "sample":
-        # each slot is the inverse-CDF draw of the softmax of its row, where
-        # the uniform is clear of the bin edges; q is that softmax
+    if w.walk in ("sample", "sample-path"):
+        # each slot is the inverse-CDF draw of the softmax of its row (plus,
+        # for whole-path draws, the backward message of its position,
+        # computed here in fp64 from the GPU's own scores), where the uniform
+        # is clear of the bin edges; q is that softmax
         u = case["inp"]["u_path"]
-        e = np.exp((rows - rows.max(axis=2, keepdims=True)) / w.temperature)
+        a = rows.astype(np.float64) / w.temperature
+        tol = 2e-6
+        if w.walk == "sample-path":
+            beta = np.zeros((B, L, 16))
+            for t in range(L - 2, -1, -1):
+                x = S_g[:, t].astype(np.float64) / w.temperature + beta[:, t + 1][:, None, :]
+                mx = x.max(axis=2)
+                beta[:, t] = mx + np.log(np.exp(x - mx[:, :, None]).sum(axis=2))
+            a = a + beta
+            tol = max(joint_sample_tol(S0_g[k], S_g[k], w.temperature) for k in range(B))
+        e = np.exp(a - a.max(axis=2, keepdims=True))
         qq = e / e.sum(axis=2, keepdims=True)
-        np.testing.assert_allclose(buf.q.cpu().numpy(), qq, atol=2e-6)
+        np.testing.assert_allclose(buf.q.cpu().numpy(), qq, atol=tol)
         cum = np.cumsum(qq, axis=2)
-        clear = np.abs(cum - u[:, :, None]).min(axis=2) > SAMPLE_TOL
+        clear = np.abs(cum - u[:, :, None]).min(axis=2) > max(SAMPLE_TOL, tol)
         draw = (u[:, :, None] >= cum).sum(axis=2)
         assert (slot[clear] == draw[clear]).all()
         assert ((nxt >= 0) & (nxt < V)).all()
@@ -441,8 +464,8 @@ def test_lazy_rejection_all_blocks(case):
 
 def test_step_is_deterministic(case):
     w, buf, dev = case["w"], case["buf"], case["dev"]
-    if w.cid not in (0, 2, 5, 7):
-        pytest.skip("checked on the tiny, the benchmark, the gated and the sampled workload")
+    if w.cid not in (0, 2, 5, 7, 8):
+        pytest.skip("checked on the tiny, the benchmark, the gated and the sampled workloads")
     snap = [t.clone() for t in (buf.logits, buf.top_val, buf.top_idx, buf.S0, buf.S, buf.path_slot,
                                 buf.path_score)]
     bd.run_step(buf, dev["x"], dev["convs"], dev["W"], dev["U"], dev["Vf"], dev["anchor_tok"], None,
@@ -501,8 +524,8 @@ def test_step_graph_replays_match_eager(case):
     every replay, with eager steps and synchronisations in between, gives the
     eager step's outputs."""
     w, buf, dev = case["w"], case["buf"], case["dev"]
-    if w.cid not in (2, 5, 7):
-        pytest.skip("checked on the benchmark, the gated and the sampled workload")
+    if w.cid not in (2, 5, 7, 8):
+        pytest.skip("checked on the benchmark, the gated and the sampled workloads")
     kw = dict(Wg=dev["Wg"], walk=w.walk, temperature=w.temperature, u_path=dev.get("u_path"),
               z_target=dev.get("z_target"), u_acc=dev.get("u_acc"), u_res=dev.get("u_res"))
     # with targets, a walk that is not sampled runs the fused scores-walk-verify launch

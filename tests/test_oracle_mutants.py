@@ -386,3 +386,46 @@ def test_pins_catch_scores_with_the_candidates_logit_of_the_wrong_slot(monkeypat
     monkeypatch.setattr(O, "pair_scores", row_unary)
     _fails(pins.test_pair_scores_zero_factors_reduce_to_unary,
            pins.test_pair_scores_one_hot_factors_give_indicator_matches)
+
+
+# ------------------------------------------------------------------ whole-path sampling
+def _joint_mutant(mistake):
+    """sample_path_joint with one planted mistake in the backward messages or
+    in the forward draws that read them."""
+    def f(S0, S, top_idx, T, u):
+        S0 = np.asarray(S0, np.float64)
+        S = np.asarray(S, np.float64)
+        u = np.asarray(u, np.float64)
+        B, L = S0.shape[0], S.shape[1] + 1
+        b = np.arange(B)
+        beta = np.zeros((B, L + 1, 16))
+        for t in range(L - 2, -1, -1):
+            St = S[:, t].transpose(0, 2, 1) if mistake == "transposed" else S[:, t]
+            a = St / T + beta[:, t + 1][:, None, :]
+            m = a.max(axis=2)
+            if mistake == "max":
+                beta[:, t] = m
+            elif mistake != "none":
+                beta[:, t] = m + np.log(np.exp(a - m[:, :, None]).sum(axis=2))
+        slot = np.zeros((B, L), np.int64)
+        q = np.zeros((B, L, 16))
+        for t in range(L):
+            row = S0 if t == 0 else S[b, t - 1, slot[:, t - 1]]
+            bt = beta[:, t + 1] if mistake == "next" else beta[:, t]
+            a = row / T + bt
+            e = np.exp(a - a.max(axis=1, keepdims=True))
+            q[:, t] = e / e.sum(axis=1, keepdims=True)
+            slot[:, t] = np.minimum((u[:, t, None] >= np.cumsum(q[:, t], axis=1)).sum(axis=1), 15)
+        tok = np.take_along_axis(np.asarray(top_idx), slot[:, :, None], axis=2)[:, :, 0]
+        return slot.astype(np.int32), tok.astype(np.int32), q
+    return f
+
+
+@pytest.mark.parametrize("mistake", ["none", "max", "transposed", "next"])
+def test_pins_catch_mistakes_in_the_whole_path_sampler(monkeypatch, mistake):
+    # none: no backward messages (the chain sampler); max: messages by max
+    # instead of log-sum-exp; transposed: the recursion reads S[t, j, i];
+    # next: position t's draw reads the message of position t + 1
+    monkeypatch.setattr(O, "sample_path_joint", _joint_mutant(mistake))
+    _fails(lambda: pins.test_joint_sampler_draws_the_path_distribution(3, 1.0),
+           pins.test_joint_sampler_proposals_are_the_exact_conditionals)

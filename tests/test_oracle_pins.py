@@ -506,6 +506,101 @@ def test_sample_path_frequencies_and_low_temperature_limit():
     np.testing.assert_array_equal(ss, gs)
 
 
+# ------------------------------------------------------------------ whole-path sampling
+def _brute_path_probs(S0, S, T):
+    """P(path) for every slot path of one block, by enumeration: the
+    normalised exp(score / T) over all 16^L paths (path index = slots read
+    as base-16 digits, position 0 most significant)."""
+    L = S.shape[0] + 1
+    paths = np.array(list(itertools.product(range(16), repeat=L)))
+    sc = S0[paths[:, 0]].astype(np.float64)
+    for t in range(1, L):
+        sc = sc + S[t - 1, paths[:, t - 1], paths[:, t]]
+    w = np.exp((sc - sc.max()) / T)
+    return paths, w / w.sum()
+
+
+@pytest.mark.parametrize("L,T", [(2, 1.0), (3, 1.0), (3, 0.7)])
+def test_joint_sampler_draws_the_path_distribution(L, T):
+    """The draws of sample_path_joint follow exp(score / T) over all 16^L
+    paths (chi-square against the enumerated distribution), and not the
+    chain sampler's distribution, which differs when the scores depend on
+    the predecessor."""
+    from scipy.stats import chisquare
+
+    g = np.random.default_rng(40 + L)
+    N = 200000
+    S0 = g.standard_normal(16) * 1.5
+    S = g.standard_normal((L - 1, 16, 16)) * 1.5
+    _, probs = _brute_path_probs(S0, S, T)
+    u = g.random((N, L))
+    top = np.broadcast_to(np.arange(16, dtype=np.int32), (N, L, 16))
+    slot, _, _ = O.sample_path_joint(np.broadcast_to(S0, (N, 16)),
+                                     np.broadcast_to(S, (N, L - 1, 16, 16)), top, T, u)
+    idx = (slot.astype(np.int64) * (16 ** np.arange(L - 1, -1, -1))).sum(axis=1)
+    counts = np.bincount(idx, minlength=16 ** L)
+    exp = probs * N
+    big = exp >= 5
+    obs = np.concatenate([counts[big], [counts[~big].sum()]])
+    ex = np.concatenate([exp[big], [exp[~big].sum()]])
+    assert chisquare(obs, ex).pvalue > 1e-4
+    # the chain sampler's draws do not follow it
+    cslot, _, _ = O.sample_path(np.broadcast_to(S0, (N, 16)), np.broadcast_to(S, (N, L - 1, 16, 16)),
+                                top, T, u)
+    cidx = (cslot.astype(np.int64) * (16 ** np.arange(L - 1, -1, -1))).sum(axis=1)
+    ccounts = np.bincount(cidx, minlength=16 ** L)
+    cobs = np.concatenate([ccounts[big], [ccounts[~big].sum()]])
+    assert chisquare(cobs, ex).pvalue < 1e-6
+
+
+def test_joint_sampler_proposals_are_the_exact_conditionals():
+    """q[b, t] is P(p_t = j | p_0 .. p_{t-1}) under the path distribution,
+    by marginalising the enumerated paths."""
+    g = np.random.default_rng(17)
+    L, T, N = 3, 0.8, 40
+    S0 = g.standard_normal(16) * 2.0
+    S = g.standard_normal((L - 1, 16, 16)) * 2.0
+    paths, probs = _brute_path_probs(S0, S, T)
+    top = np.broadcast_to(np.arange(16, dtype=np.int32), (N, L, 16))
+    slot, _, q = O.sample_path_joint(np.broadcast_to(S0, (N, 16)),
+                                     np.broadcast_to(S, (N, L - 1, 16, 16)), top, T,
+                                     g.random((N, L)))
+    for b in range(N):
+        for t in range(L):
+            prefix = np.all(paths[:, :t] == slot[b, :t], axis=1)
+            cond = np.bincount(paths[prefix, t], weights=probs[prefix], minlength=16)
+            np.testing.assert_allclose(q[b, t], cond / cond.sum(), rtol=0, atol=1e-12)
+
+
+def test_joint_sampler_limits():
+    """One position: the chain sampler's draw.  Scores that do not depend on
+    the predecessor: the chain sampler's draws (the backward messages are
+    then constant in the slot).  T -> 0: the max-plus path."""
+    g = np.random.default_rng(23)
+    N = 500
+    S0 = g.standard_normal((N, 16)).astype(np.float32)
+    top = np.broadcast_to(np.arange(16, dtype=np.int32), (N, 4, 16))
+    u = g.random((N, 4))
+    a = O.sample_path_joint(S0, np.zeros((N, 0, 16, 16)), top[:, :1], 1.0, u[:, :1])
+    c = O.sample_path(S0, np.zeros((N, 0, 16, 16)), top[:, :1], 1.0, u[:, :1])
+    np.testing.assert_array_equal(a[0], c[0])
+    np.testing.assert_allclose(a[2], c[2], rtol=0, atol=1e-15)
+    f = g.standard_normal((N, 3, 1, 16))
+    S = np.broadcast_to(f, (N, 3, 16, 16))                  # S[t, i, j] = f_t(j)
+    a = O.sample_path_joint(S0, S, top, 0.9, u)
+    c = O.sample_path(S0, S, top, 0.9, u)
+    np.testing.assert_allclose(a[2], c[2], rtol=0, atol=1e-12)
+    clear = (O.sample_margin(c[2], u) > 1e-9).all(axis=1)
+    assert clear.mean() > 0.99
+    np.testing.assert_array_equal(a[0][clear], c[0][clear])
+    S = g.standard_normal((N, 3, 16, 16))
+    a = O.sample_path_joint(S0, S, top, 1e-3, u)
+    best = O.path_select(S0, S.astype(np.float32), top)
+    sure = O.path_margin(S0, S) > 0.05                     # exp(-50) of the mass elsewhere
+    assert sure.mean() > 0.8
+    np.testing.assert_array_equal(a[0][sure], best[0][sure])
+
+
 def test_sample_margin_hand_case():
     # bins of q = [0.1, 0.2, 0.7]: edges 0, 0.1, 0.3, 1.0
     q = np.zeros((1, 4, 16))

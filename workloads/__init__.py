@@ -84,7 +84,9 @@ class Workload:
     dyadic: bool          # integer / dyadic construction (exact sums, ties)
     parity_blocks: int    # seeded block subset the oracle checks at full size
     gate: bool = False    # pair match weighted by a context gate from h_t (Wg [r, H])
-    walk: str = "viterbi"  # path walk: "viterbi" (max-plus) or "greedy" (best successor)
+    walk: str = "viterbi"  # "viterbi" (max-plus), "greedy" (best successor), "sample"
+    #                        (each position from its predecessor's row) or "sample-path"
+    #                        (the whole path from exp(score / T))
     groups: int = 1       # correction groups of a dynamic conv (H/16: one per 16 channels)
     profile: str = "table1"  # recall profile: "table1" or "decay" (linear 0.85 -> 0.60)
     temperature: float = 0.0  # > 0: sampled walk and lossless rejection verification
@@ -134,6 +136,10 @@ WORKLOADS: Dict[int, Workload] = {
     # rejection verification against synthetic target logits.
     7: Workload(7, "27b-sampled", 64, 8, 5120, 151936, 64, "bf16", 1, False, "logits", False, 8,
                 walk="sample", temperature=1.0),
+    # The same with the whole path drawn from exp(score / T) over all 16^L
+    # paths (the sampling twin of the max-plus walk).
+    8: Workload(8, "27b-sampled-path", 64, 8, 5120, 151936, 64, "bf16", 1, False, "logits", False,
+                8, walk="sample-path", temperature=1.0),
 }
 
 
