@@ -63,6 +63,19 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector peak (fp32 workload)
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_gemm_27b_head_traffic.txt")
+PEAKS_FILE = os.path.join(ROOT, "profiles", "peaks_mfma_hbm.txt")
+
+
+def measured_peaks():
+    """The attainable peaks measured on this part (profiles/peaks_mfma_hbm.txt:
+    bench.py --peaks), or {} when the summary is missing."""
+    out = {}
+    if os.path.exists(PEAKS_FILE):
+        for line in open(PEAKS_FILE):
+            m = re.match(r"^([a-z0-9_]+):\s*([0-9.]+)\s*$", line)
+            if m:
+                out[m.group(1)] = float(m.group(2))
+    return out
 
 
 def parse_args(argv=None):
@@ -83,6 +96,13 @@ def parse_args(argv=None):
                     help="seconds of step replays after the warmup steps, before timing")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure attainable peaks (matrix-core probe, HBM copy) and exit")
+    ap.add_argument("--sweep", choices=["topk", "pair"], default=None,
+                    help="scaled-batch sweep of the top-16 or the fused pair + walk + verify; "
+                         "one JSON line per size, then exit")
+    ap.add_argument("--sweep-sizes", default=None,
+                    help="comma-separated rows (topk) or blocks (pair) for --sweep")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--separate", action="store_true",
                     help="pair scores, walk and verification as separate launches, and for a "
@@ -136,6 +156,119 @@ def copy_calibration():
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+
+
+def _time_events(fn, reps: int, settle_s: float = 0.3):
+    """Median milliseconds of fn() over reps launches, each bracketed by
+    events on the current stream, after settle_s seconds of launches."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        fn()
+        torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    return ts[len(ts) // 2]
+
+
+def peaks():
+    """Attainable peaks on this GPU, measured: the GEMM's matrix-core work
+    without memory traffic (the library's probe: 256 workgroups of eight
+    waves, v_mfma_f32_32x32x16_bf16 on register operands) with operands of
+    the benchmark's bit statistics (N(0, 1) in bf16) and with zeros, and a
+    plain 4 GiB device copy (above the 256 MB MALL)."""
+    import torch
+    import block_drafting_amd as bd
+    nwg, iters = 256, 20000
+    flops = nwg * 8 * iters * 8 * 2 * 32 * 32 * 16
+    nbytes = bd.probe_mfma_operand_bytes(nwg)
+    rnd = torch.randn(nbytes // 2, device="cuda").to(torch.bfloat16)
+    zero = torch.zeros(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(nwg * 512, device="cuda")
+    for name, ops in (("normal", rnd), ("zeros", zero)):
+        ms = _time_events(lambda: bd.probe_mfma(ops, nwg, iters, out), 7, settle_s=1.0)
+        print(json.dumps({"peak": "mfma_bf16", "operands": name, "workgroups": nwg,
+                          "iters": iters, "ms": round(ms, 4),
+                          "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}), flush=True)
+    n = 4 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    ms = _time_events(lambda: b.copy_(a), 7, settle_s=1.0)
+    print(json.dumps({"peak": "hbm_copy", "bytes_read": n, "bytes_written": n,
+                      "ms": round(ms, 4), "gbs": round(2 * n / (ms * 1e-3) / 1e9, 1)}),
+          flush=True)
+
+
+def sweep(kind: str, sizes):
+    """Scaled-batch sweep of the small stages, synthetic inputs of the
+    27b-head shapes, one JSON line per size (median of 7 timed launches
+    after 0.3 s of launches).
+
+    topk: rows M of N(0, 1) fp32 logits over V = 151936 tokens and their
+      256-column tile maxima; the pruned top-16 (dflash2_topk16_tilemax) and
+      the full scan (dflash2_topk16).  Algorithmic bytes: the full scan reads
+      M V 4; the pruned one reads the tile maxima and at least the 16 tiles
+      that hold the top-16, M (ceil(V / 256) 4 + 16 1024).
+    pair: B blocks of L = 8 random candidates (ids uniform over V), bf16
+      factor tables [V, 64], random targets; the fused scores + max-plus walk
+      + greedy verification (dflash2_pair_select_verify).  Algorithmic bytes
+      per block: the factor rows gathered, 2 L 16 r 2, the candidates,
+      L 16 8, the targets and the outputs, (4 L + 3) 4."""
+    import torch
+    import block_drafting_amd as bd
+    g = torch.Generator(device="cuda").manual_seed(7)
+    V = 151936
+    if kind == "topk":
+        nt = (V + 255) // 256
+        for M in sizes:
+            z = torch.randn((M, V), generator=g, device="cuda")
+            tm = torch.empty((M, nt), device="cuda")
+            for r0 in range(0, M, 4096):          # tile maxima, a band of rows at a time
+                zz = z[r0:r0 + 4096]
+                zp = torch.nn.functional.pad(zz, (0, nt * 256 - V), value=float("-inf"))
+                tm[r0:r0 + 4096] = zp.view(zz.shape[0], nt, 256).amax(dim=2)
+                del zp
+            tv = torch.empty((M, 16), device="cuda")
+            ti = torch.empty((M, 16), dtype=torch.int32, device="cuda")
+            ws = torch.empty(max(bd.topk16_workspace(M, V), 1), dtype=torch.uint8, device="cuda")
+            ms_p = _time_events(lambda: bd.topk16_tilemax(z, tm, tv, ti), 7)
+            ms_f = _time_events(lambda: bd.topk16(z, tv, ti, ws), 7)
+            alg_p = M * (nt * 4 + 16 * 1024)
+            alg_f = M * V * 4
+            print(json.dumps({"sweep": "topk", "rows": M, "V": V,
+                              "pruned_us": round(ms_p * 1e3, 1), "pruned_alg_bytes": alg_p,
+                              "pruned_gbs": round(alg_p / (ms_p * 1e-3) / 1e9, 1),
+                              "scan_us": round(ms_f * 1e3, 1), "scan_bytes": alg_f,
+                              "scan_gbs": round(alg_f / (ms_f * 1e-3) / 1e9, 1)}), flush=True)
+            del z, tm
+            torch.cuda.empty_cache()
+    else:
+        L, r = 8, 64
+        U = (torch.randn((V, r), generator=g, device="cuda") * 0.316).to(torch.bfloat16)
+        Vf = (torch.randn((V, r), generator=g, device="cuda") * 0.316).to(torch.bfloat16)
+        for B in sizes:
+            tv = torch.randn((B, L, 16), generator=g, device="cuda").sort(dim=2, descending=True)[0]
+            ti = torch.randint(0, V, (B, L, 16), generator=g, device="cuda", dtype=torch.int32)
+            at = torch.randint(0, V, (B,), generator=g, device="cuda", dtype=torch.int32)
+            tgt = torch.randint(0, V, (B, L + 1), generator=g, device="cuda", dtype=torch.int32)
+            outs = [torch.empty((B, L), dtype=torch.int32, device="cuda"),
+                    torch.empty((B, L), dtype=torch.int32, device="cuda"),
+                    torch.empty((B,), device="cuda"),
+                    torch.empty((B,), dtype=torch.int32, device="cuda"),
+                    torch.empty((B,), dtype=torch.int32, device="cuda")]
+            ms = _time_events(lambda: bd.pair_select_verify(tv, ti, at, U, Vf, tgt, None,
+                                                            "viterbi", None, None, *outs), 7)
+            alg = B * (2 * L * 16 * r * 2 + L * 16 * 8 + (4 * L + 3) * 4)
+            print(json.dumps({"sweep": "pair_select_verify", "blocks": B, "L": L, "r": r,
+                              "us": round(ms * 1e3, 1), "alg_bytes": alg,
+                              "gbs": round(alg / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(w, inp, targets, n_blocks: int, n_single: int):
@@ -261,6 +394,14 @@ def main(argv=None):
         return 2
     if a.copy_calib:
         copy_calibration()
+        return 0
+    if a.peaks or a.sweep:
+        sys.path.insert(0, ROOT)
+        if a.peaks:
+            peaks()
+        else:
+            default = "512,4096,16384,65536" if a.sweep == "topk" else "64,1024,8192,32768"
+            sweep(a.sweep, [int(v) for v in (a.sweep_sizes or default).split(",")])
         return 0
 
     sys.path.insert(0, ROOT)
@@ -513,16 +654,37 @@ def main(argv=None):
         achieved = flops / gemm_s / 1e12
         roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_F32_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32_TFLOPS, 5), "traffic": None}
-    # algorithmic HBM rates of the streaming stages
+    pk = measured_peaks()
+    if roof["bound"] == "mfma" and "mfma_bf16_attainable_tflops_normal_operands" in pk:
+        # the matrix-core rate this part sustains on operands of these
+        # statistics (the GEMM's work without memory traffic), as context
+        att = pk["mfma_bf16_attainable_tflops_normal_operands"]
+        roof["attainable"] = att
+        roof["frac_of_attainable"] = round(achieved / att, 4)
+    # algorithmic HBM rates of the streaming stages, against 8 TB/s
     es = 2 if bf16 else 4
     conv_bytes = w.n_convs * (2 * L + 1) * B * H * es
     if w.dynamic and w.groups > 1:
         conv_bytes += w.n_convs * 2 * w.groups * H * es      # the correction maps
-    # (the top-16 reads only the tiles its maxima allow, ~1/37 of the logits
-    # at V = 151936, so no HBM rate is quoted for it)
     hbm = {"conv": round(conv_bytes / (stage_ms["conv"] * 1e-3) / 1e9, 1)}
     if two_pass:
         hbm["lse"] = round(B * (L + 1) * V * 4 / (stage_ms["lse"] * 1e-3) / 1e9, 1)
+    # per-stage rooflines: bytes per launch (the basis stated), GB/s and the
+    # fraction of 8 TB/s; the top-16 reads the tile maxima and at least the
+    # 16 tiles that hold the top-16 (the counters read 1.03x that at this
+    # size); the fused pair stage gathers two factor rows per candidate
+    nt = (V + 255) // 256
+    basis = {"conv": (conv_bytes, "(2L+1) B H per application: x, predecessors, y"),
+             "topk": (M * (nt * 4 + 16 * 1024), "M (ceil(V/256) 4 + 16 KiB): tile maxima + 16 tiles")}
+    if fused and not sampled:
+        basis["pair_select_verify"] = (
+            B * (2 * L * 16 * w.r * 2 + L * 16 * 8 + (4 * L + 3) * 4),
+            "B (2 L 16 r 2 + L 16 8 + (4 L + 3) 4): factor rows, candidates, targets, outputs")
+    stage_roof = {}
+    for k, (nb, why) in basis.items():
+        gbs = nb / (stage_ms[k] * 1e-3) / 1e9
+        stage_roof[k] = {"bytes": int(nb), "basis": why, "gbs": round(gbs, 1),
+                         "frac": round(gbs / PEAK_HBM_GBS, 4)}
     accept = {"path": round(float(acc.mean()), 3)}
     if not sampled and w.target_mode != "mix":
         # the same planted targets read by the top-1 path and by the oracle
@@ -567,6 +729,7 @@ def main(argv=None):
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "stage_pass_ms_per_step": round(stage_wall_ms, 4),
         "stage_hbm_gbs": hbm,
+        "stage_roofline": stage_roof,
         "roofline": roof,
     }
     if w.dynamic and w.groups > 1:

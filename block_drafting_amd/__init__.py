@@ -74,6 +74,8 @@ _SIGS = {
     "dflash2_logits_topk_workspace": ([_I, _I, _I, _I, _I, _I], _Z),
     "dflash2_logits_topk": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
     "dflash2_logits_topk_noalloc": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
+    "dflash2_probe_mfma_operand_bytes": ([_I], _Z),
+    "dflash2_probe_mfma": ([_P, _I, _I, _P, _P], _I),
     "dflash2_pair_score": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "dflash2_context_gate": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "dflash2_pair_score_gated": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
@@ -397,6 +399,29 @@ def logits_topk_noalloc(h: torch.Tensor, W, logits: torch.Tensor,
         _ptr(h), wp, _ptr(logits), _ptr(top_val), _ptr(top_idx), M, H, V, TOPK, code,
         _stream(dev)))
     return top_val, top_idx
+
+
+def probe_mfma(operands: torch.Tensor, workgroups: int, iters: int,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Measurement aid (not a step): the GEMM's matrix-core work without its
+    memory traffic, `workgroups` x 8 waves x `iters` x 8 bf16 32x32x16
+    MFMAs on register operands loaded once from `operands` (uint8 or bf16
+    bits, probe_mfma_operand_bytes(workgroups) bytes).  Returns out
+    [workgroups * 512] fp32."""
+    need = int(lib().dflash2_probe_mfma_operand_bytes(workgroups))
+    if operands.numel() * operands.element_size() < need:
+        raise ValueError(f"operands: need {need} bytes")
+    if out is None:
+        out = torch.empty(workgroups * 512, dtype=torch.float32, device=operands.device)
+    _shape(out, (workgroups * 512,), "out", torch.float32)
+    dev = _dev(operands, out)
+    _check("dflash2_probe_mfma", lib().dflash2_probe_mfma(
+        _ptr(operands), workgroups, iters, _ptr(out), _stream(dev)))
+    return out
+
+
+def probe_mfma_operand_bytes(workgroups: int) -> int:
+    return int(lib().dflash2_probe_mfma_operand_bytes(workgroups))
 
 
 def context_gate(h: torch.Tensor, Wg: torch.Tensor, out: Optional[torch.Tensor] = None):

@@ -605,6 +605,22 @@ DFLASH2_API int dflash2_pair_sample_mode(const float* top_val, const int32_t* to
                      mode, S0, S, path_slot, path_tok, q, stream);
 }
 
+// ---------------------------------------------------------------- attainable-peak probe
+DFLASH2_API size_t dflash2_probe_mfma_operand_bytes(int workgroups) {
+  if (workgroups < 1 || workgroups > (1 << 20)) return 0;
+  return probe_mfma_operand_bytes(workgroups);
+}
+
+DFLASH2_API int dflash2_probe_mfma(const void* operands, int workgroups, int iters, float* out,
+                                   void* stream) {
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1) return DFLASH2_EINVAL;
+  if (!operands || !out || !aligned16(operands) || !aligned4(out)) return DFLASH2_EINVAL;
+  if (overlap(out, (size_t)workgroups * 512 * 4, operands,
+              probe_mfma_operand_bytes(workgroups)))
+    return DFLASH2_EINVAL;
+  return status_of(launch_probe_mfma(operands, workgroups, iters, out, as_stream(stream)));
+}
+
 // ---------------------------------------------------------------- allocation-free logits + top-16
 // dflash2_logits_topk for callers that cannot allocate: the tile maxima
 // between the GEMM and the top-16 live in this fixed device array (each GPU

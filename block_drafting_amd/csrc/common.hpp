@@ -145,6 +145,10 @@ hipError_t launch_verify_rejection(const int32_t* path_slot, const int32_t* path
                                    const float* u_res, int B, int L, int V, int32_t* accept_len,
                                    int32_t* next_tok, hipStream_t s);
 
+// Attainable-peak probe: the GEMM's matrix-core work without memory traffic.
+size_t probe_mfma_operand_bytes(int nwg);
+hipError_t launch_probe_mfma(const void* operands, int nwg, int iters, float* out, hipStream_t s);
+
 hipError_t launch_verify_greedy(const int32_t* path_tok, const int32_t* target, int B, int L,
                                 int32_t* accept_len, int32_t* next_tok, hipStream_t s);
 

@@ -224,6 +224,21 @@ int dflash2_logits_topk(const void* h, const void* W, float* logits,
                         int M, int H, int V, int K, int dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Measurement aid, not a step of the path: the attainable matrix-core rate
+ * behind the LM-head GEMM's roofline.  `workgroups` workgroups of the
+ * GEMM's eight waves each issue `iters` x 8 v_mfma_f32_32x32x16_bf16 on
+ * register operands loaded once from `operands` (bf16 bit patterns,
+ * dflash2_probe_mfma_operand_bytes(workgroups) bytes, 16-byte aligned: the
+ * bits set the power the matrix cores draw); no other memory traffic.
+ * Work: workgroups * 8 * iters * 8 * 32768 flop.  out [workgroups * 512]
+ * fp32 receives per-thread sums of the accumulators (so nothing is
+ * optimised away).  EINVAL for iters < 1, workgroups outside [1, 2^20],
+ * null, misaligned or overlapping buffers.
+ */
+size_t dflash2_probe_mfma_operand_bytes(int workgroups);
+int dflash2_probe_mfma(const void* operands, int workgroups, int iters, float* out, void* stream);
+
 /* Bytes of the fixed device scratch of dflash2_logits_topk_noalloc (16 MiB). */
 #define DFLASH2_NOALLOC_SCRATCH_BYTES (16u << 20)
 
