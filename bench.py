@@ -62,7 +62,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector peak (fp32 workload)
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_gemm_27b_head_traffic.txt")
+# counter summaries of the GEMM: logits written, and the candidate form
+TRAFFIC_FILES = [os.path.join(ROOT, "profiles", f) for f in
+                 ("lmhead_gemm_27b_head_traffic.txt", "lmhead_candidates_27b_head_traffic.txt")]
 PEAKS_FILE = os.path.join(ROOT, "profiles", "peaks_mfma_hbm.txt")
 
 
@@ -111,6 +113,9 @@ def parse_args(argv=None):
     ap.add_argument("--row-major-w", action="store_true",
                     help="LM-head GEMM reads W [V, H] as given (default for bf16: W packed once, "
                          "before timing, into the GEMM's 256 x 64 tile layout)")
+    ap.add_argument("--keep-logits", action="store_true",
+                    help="write all [M, V] logits (default for bf16: the GEMM's candidate form, "
+                         "which writes only the tiles and values the top-16 may need)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replays of the captured step")
     return ap.parse_args(argv)
@@ -125,24 +130,26 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str, w_layout: str):
-    """HBM bytes per GEMM launch from the committed counter summary, if it
-    was taken on this workload and W layout with the current kernel source;
-    else None."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    kv = {}
-    for line in open(TRAFFIC_FILE):
-        m = re.match(r"^\s*([a-z0-9_]+)\s*[:=]\s*(\S+)", line)
-        if m:
-            kv[m.group(1)] = m.group(2)
-    if (kv.get("kernel_source_sha256_16") != kernel_source_hash() or kv.get("workload") != workload
-            or kv.get("w_layout") != w_layout):
-        return None
-    try:
-        return float(kv["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+def measured_traffic(workload: str, w_layout: str, form: str):
+    """HBM bytes per GEMM launch from a committed counter summary, if one was
+    taken on this workload, W layout and output form ("logits" or
+    "candidates") with the current kernel source; else None."""
+    for path in TRAFFIC_FILES:
+        if not os.path.exists(path):
+            continue
+        kv = {}
+        for line in open(path):
+            m = re.match(r"^\s*([a-z0-9_]+)\s*[:=]\s*(\S+)", line)
+            if m:
+                kv[m.group(1)] = m.group(2)
+        if (kv.get("kernel_source_sha256_16") == kernel_source_hash()
+                and kv.get("workload") == workload and kv.get("w_layout") == w_layout
+                and kv.get("output", "logits") == form):
+            try:
+                return float(kv["traffic_bytes_per_launch"])
+            except (KeyError, ValueError):
+                return None
+    return None
 
 
 def copy_calibration():
@@ -445,10 +452,12 @@ def main(argv=None):
     B, L, H, V = w.B, w.L, w.H, w.V
     M = B * L
     sampled = w.temperature > 0
-    buf = bd.StepBuffers(B, L, H, V, tdt, "cuda", n_convs=w.n_convs, keep_logits=True,
+    cand_form = bf16 and not a.keep_logits   # GEMM writes candidates, not the logits
+    buf = bd.StepBuffers(B, L, H, V, tdt, "cuda", n_convs=w.n_convs, keep_logits=not cand_form,
                          gate_rank=w.r if w.gate else 0, sample=sampled)
-    tilemax = torch.empty((M, (V + bd.TILEMAX_COLS - 1) // bd.TILEMAX_COLS), dtype=torch.float32,
-                          device="cuda")
+    tilemax = (None if cand_form else
+               torch.empty((M, (V + bd.TILEMAX_COLS - 1) // bd.TILEMAX_COLS),
+                           dtype=torch.float32, device="cuda"))
     if sampled:
         u_path, u_acc, u_res = (dev(inp[k], "f32") for k in ("u_path", "u_acc", "u_res"))
 
@@ -485,11 +494,20 @@ def main(argv=None):
                 bd.twotap_conv(cur, c["k0"], c["k1"], c["anchor_h"], c["proj"], c["groups"], out=out)
             cur = out
 
-    stages = [
-        ("conv", st_conv),
-        ("gemm", lambda: bd.lmhead_logits_tilemax(final_y.view(M, H), W, buf.logits, tilemax)),
-        ("topk", lambda: bd.topk16_tilemax(buf.logits, tilemax, buf.top_val, buf.top_idx)),
-    ]
+    if cand_form:
+        stages = [
+            ("conv", st_conv),
+            ("gemm", lambda: bd.lmhead_candidates(final_y.view(M, H), W, buf.workspace)),
+            ("topk", lambda: bd.topk16_candidates(buf.workspace, M, H, V, buf.top_val,
+                                                  buf.top_idx)),
+        ]
+    else:
+        stages = [
+            ("conv", st_conv),
+            ("gemm", lambda: bd.lmhead_logits_tilemax(final_y.view(M, H), W, buf.logits,
+                                                      tilemax)),
+            ("topk", lambda: bd.topk16_tilemax(buf.logits, tilemax, buf.top_val, buf.top_idx)),
+        ]
     if w.gate:
         stages.append(("gate", lambda: bd.context_gate(final_y.view(M, H), Wg, buf.gate)))
     if fused and sampled:
@@ -542,7 +560,12 @@ def main(argv=None):
         cpu, ora = cpu_baseline(w, inp, targets, a.cpu_blocks, a.cpu_blocks_single)
         blocks = np.arange(len(ora["top_idx"]))
         rows = (blocks[:, None] * L + np.arange(L)[None, :]).reshape(-1)
-        z_rows = buf.logits[torch.from_numpy(rows).cuda()].cpu().numpy()
+        rows_t = torch.from_numpy(rows).cuda()
+        if cand_form:
+            # the candidate form keeps no logits: the same GEMM once more, untimed
+            z_rows = bd.lmhead_logits(final_y.view(M, H), W)[rows_t].cpu().numpy()
+        else:
+            z_rows = buf.logits[rows_t].cpu().numpy()
         bad, checked = parity_gate(w, blocks, ora, z_rows, first["top_val"][blocks],
                                    first["top_idx"][blocks], first["S0"][blocks],
                                    first["S"][blocks], first["path_slot"][blocks],
@@ -637,19 +660,23 @@ def main(argv=None):
     ms_step = wall * 1e3 / a.steps
     gemm_s = float(np.mean(gemm_ms)) * 1e-3
     flops = 2.0 * M * H * V
-    # algorithmic GEMM bytes: W and h read once, logits and tile maxima written
-    gemm_bytes = (V * H + M * H) * (2 if bf16 else 4) + M * V * 4 + M * ((V + 255) // 256) * 4
+    # algorithmic GEMM bytes: W and h read once, tile maxima written, and the
+    # logits (logits form) or the per-tile counts (candidate form)
+    nt = (V + 255) // 256
+    gemm_bytes = ((V * H + M * H) * (2 if bf16 else 4) + M * nt * 4
+                  + (M * nt * 4 if cand_form else M * V * 4))
+    form = "candidates" if cand_form else "logits"
     if bf16 and flops / gemm_bytes < PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
         # below the ridge (small M): HBM-bound
         achieved = gemm_bytes / gemm_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": measured_traffic(w.name, w_layout)}
+                "traffic": measured_traffic(w.name, w_layout, form)}
     elif bf16:
         achieved = flops / gemm_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(w.name, w_layout)}
+                "traffic": measured_traffic(w.name, w_layout, form)}
     else:
         achieved = flops / gemm_s / 1e12
         roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_F32_TFLOPS,
@@ -673,9 +700,12 @@ def main(argv=None):
     # fraction of 8 TB/s; the top-16 reads the tile maxima and at least the
     # 16 tiles that hold the top-16 (the counters read 1.03x that at this
     # size); the fused pair stage gathers two factor rows per candidate
-    nt = (V + 255) // 256
     basis = {"conv": (conv_bytes, "(2L+1) B H per application: x, predecessors, y"),
-             "topk": (M * (nt * 4 + 16 * 1024), "M (ceil(V/256) 4 + 16 KiB): tile maxima + 16 tiles")}
+             "topk": ((M * (nt * 8 + 16 * 32),
+                       "M (ceil(V/256) 8 + 16 x 32): tile maxima, counts, 16 tiles' slots")
+                      if cand_form else
+                      (M * (nt * 4 + 16 * 1024),
+                       "M (ceil(V/256) 4 + 16 KiB): tile maxima + 16 tiles"))}
     if fused and not sampled:
         basis["pair_select_verify"] = (
             B * (2 * L * 16 * w.r * 2 + L * 16 * 8 + (4 * L + 3) * 4),
@@ -716,6 +746,7 @@ def main(argv=None):
                    "gate": w.gate, "walk": w.walk, "temperature": w.temperature,
                    "launch": "hip-graph" if graphK is not None else "eager",
                    "pair_walk": "fused" if fused else "separate", "lm_head_w": w_layout,
+                   "lm_head_out": form,
                    "rejection": ("two-pass" if two_pass else "lazy") if sampled else None},
         "tokens_per_s": round(M / (ms_step * 1e-3), 1),
         "accepted_tokens_per_s": round(float(acc.sum()) / (ms_step * 1e-3), 1),

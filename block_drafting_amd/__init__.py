@@ -44,6 +44,7 @@ __all__ = [
     "DFlash2Error", "lib", "library_path", "twotap_conv", "twotap_conv_mm", "lmhead_logits",
     "lmhead_logits_tilemax", "lmhead_pack", "PackedWeight", "topk16", "topk16_tilemax",
     "topk16_workspace", "logits_topk", "logits_topk_workspace", "logits_topk_noalloc",
+    "lmhead_candidates", "topk16_candidates",
     "context_gate", "pair_score",
     "path_select", "pair_select_verify", "pair_sample", "path_sample", "SAMPLE_MODES", "target_lse", "verify_rejection", "verify_rejection_lazy", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
 ]
@@ -74,6 +75,8 @@ _SIGS = {
     "dflash2_logits_topk_workspace": ([_I, _I, _I, _I, _I, _I], _Z),
     "dflash2_logits_topk": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P], _I),
     "dflash2_logits_topk_noalloc": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
+    "dflash2_lmhead_candidates": ([_P, _P, _I, _I, _I, _I, _P, _Z, _P], _I),
+    "dflash2_topk16_candidates": ([_P, _Z, _P, _P, _I, _I, _I, _I, _P], _I),
     "dflash2_probe_mfma_operand_bytes": ([_I], _Z),
     "dflash2_probe_mfma": ([_P, _I, _I, _P, _P], _I),
     "dflash2_pair_score": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
@@ -379,6 +382,41 @@ def logits_topk(h: torch.Tensor, W, logits: Optional[torch.Tensor] = None,
     _check("dflash2_logits_topk", lib().dflash2_logits_topk(
         _ptr(h), wp, _ptr(logits), _ptr(top_val), _ptr(top_idx), M, H, V, TOPK, code,
         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(dev)))
+    return top_val, top_idx
+
+
+def lmhead_candidates(h: torch.Tensor, W, workspace: torch.Tensor) -> torch.Tensor:
+    """The GEMM of logits_topk without a logits buffer (bf16 h; W a tensor or
+    a PackedWeight): its candidate form into `workspace`
+    (logits_topk_workspace(M, H, V, bf16, False) bytes).  Returns workspace."""
+    _rank(h, 2, "h")
+    M, H = h.shape
+    wp, V, code, wt = _weight(W, h)
+    if h.dtype != torch.bfloat16:
+        raise TypeError("the candidate form takes bf16 operands")
+    ws = _workspace(logits_topk_workspace(M, H, V, h.dtype, False), h.device, workspace)
+    _dev(h, wt, ws)
+    _check("dflash2_lmhead_candidates", lib().dflash2_lmhead_candidates(
+        _ptr(h), wp, M, H, V, code, _ptr(ws), ws.numel() * ws.element_size(), _stream(h.device)))
+    return ws
+
+
+def topk16_candidates(workspace: torch.Tensor, M: int, H: int, V: int,
+                      top_val: Optional[torch.Tensor] = None,
+                      top_idx: Optional[torch.Tensor] = None):
+    """The top-16 of logits_topk without a logits buffer, from the workspace
+    lmhead_candidates filled for the same M, H, V.  Returns (top_val, top_idx)."""
+    dev = workspace.device
+    _opt(top_val, (M, TOPK), "top_val", torch.float32)
+    _opt(top_idx, (M, TOPK), "top_idx", torch.int32)
+    if top_val is None:
+        top_val = torch.empty((M, TOPK), dtype=torch.float32, device=dev)
+    if top_idx is None:
+        top_idx = torch.empty((M, TOPK), dtype=torch.int32, device=dev)
+    _dev(workspace, top_val, top_idx)
+    _check("dflash2_topk16_candidates", lib().dflash2_topk16_candidates(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(top_val),
+        _ptr(top_idx), M, H, V, TOPK, _stream(dev)))
     return top_val, top_idx
 
 

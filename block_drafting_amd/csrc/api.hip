@@ -209,14 +209,40 @@ DFLASH2_API int dflash2_topk16(const float* logits, float* top_val, int32_t* top
   return status_of(launch_topk16(logits, top_val, top_idx, M, V, workspace, as_stream(stream)));
 }
 
-// Workspace of dflash2_logits_topk: the tile maxima, then (when the caller
-// gives no logits buffer) the logits, each start 256-byte aligned.
+// Workspace of dflash2_logits_topk, each part 256-byte aligned: the tile
+// maxima; when the caller gives no logits buffer, for bf16 the candidate
+// form's group maxima [M, 16], counts [M, nt] and slots [M, nt, 4] (uint2),
+// and then the logits [M, V] (only the tiles the GEMM stores are written).
+namespace {
+struct TopkWs {
+  size_t gmax = 0, cnt = 0, slots = 0, z = 0, total = 0;
+  bool cand = false;
+};
+size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
+TopkWs topk_ws(int M, int V, int dtype, bool logits_given) {
+  TopkWs w;
+  const size_t nt = (size_t)((V + kTileMaxCols - 1) / kTileMaxCols);
+  size_t at = al256(tilemax_bytes(M, V));
+  w.cand = !logits_given && (dtype == DFLASH2_BF16 || dtype == DFLASH2_BF16_PACKED);
+  if (w.cand) {
+    w.gmax = at;
+    at += al256((size_t)M * kTopK * 4);
+    w.cnt = at;
+    at += al256((size_t)M * nt * 4);
+    w.slots = at;
+    at += al256((size_t)M * nt * kCandSlots * 8);
+  }
+  w.z = at;
+  if (!logits_given) at += (size_t)M * V * sizeof(float);
+  w.total = at;
+  return w;
+}
+}  // namespace
+
 DFLASH2_API size_t dflash2_logits_topk_workspace(int M, int H, int V, int K, int dtype,
                                                  int logits_given) {
   if (K != kTopK || M < 0 || V < kTopK || H < 8 || !lmhead_dtype(dtype)) return 0;
-  size_t ws = (tilemax_bytes(M, V) + 255) & ~(size_t)255;
-  if (!logits_given) ws += (size_t)M * V * sizeof(float);
-  return ws;
+  return topk_ws(M, V, dtype, logits_given != 0).total;
 }
 
 DFLASH2_API int dflash2_logits_topk(const void* h, const void* W, float* logits, float* top_val,
@@ -233,9 +259,10 @@ DFLASH2_API int dflash2_logits_topk(const void* h, const void* W, float* logits,
   if (need > 0 && (!workspace || workspace_bytes < need ||
                    (reinterpret_cast<uintptr_t>(workspace) & 255) != 0))
     return DFLASH2_EWORKSPACE;
-  const size_t part = (tilemax_bytes(M, V) + 255) & ~(size_t)255;
+  const TopkWs lay = topk_ws(M, V, dtype, logits != nullptr);
+  char* wsb = static_cast<char*>(workspace);
   float* tmax = static_cast<float*>(workspace);
-  float* z = logits ? logits : reinterpret_cast<float*>(static_cast<char*>(workspace) + part);
+  float* z = logits ? logits : reinterpret_cast<float*>(wsb + lay.z);
   const size_t zb = (size_t)M * V * sizeof(float);
   const size_t es = esize(dtype);
   const size_t wb = w_bytes(V, H, dtype);
@@ -250,9 +277,61 @@ DFLASH2_API int dflash2_logits_topk(const void* h, const void* W, float* logits,
       overlap(workspace, need, W, wb))
     return DFLASH2_EINVAL;
   hipStream_t s = as_stream(stream);
+  if (lay.cand) {
+    uint32_t* gmax = reinterpret_cast<uint32_t*>(wsb + lay.gmax);
+    int* cnt = reinterpret_cast<int*>(wsb + lay.cnt);
+    void* slots = wsb + lay.slots;
+    hipError_t e = launch_lmhead_cand(h, W, z, tmax, gmax, cnt, slots, M, H, V, dtype, s);
+    if (e != hipSuccess) return DFLASH2_EHIP;
+    return status_of(launch_topk16_cand(z, tmax, cnt, slots, top_val, top_idx, M, V, s));
+  }
   hipError_t e = launch_lmhead(h, W, z, tmax, M, H, V, dtype, s);
   if (e != hipSuccess) return DFLASH2_EHIP;
   return status_of(launch_topk16_tilemax(z, tmax, top_val, top_idx, M, V, s));
+}
+
+DFLASH2_API int dflash2_lmhead_candidates(const void* h, const void* W, int M, int H, int V,
+                                          int dtype, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  int st = check_lmhead(h, W, M, H, V, dtype);
+  if (st != DFLASH2_OK) return st;
+  if (dtype != DFLASH2_BF16 && dtype != DFLASH2_BF16_PACKED) return DFLASH2_EUNSUPPORTED;
+  if (M == 0) return DFLASH2_OK;
+  const TopkWs lay = topk_ws(M, V, dtype, false);
+  if (!workspace || workspace_bytes < lay.total ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return DFLASH2_EWORKSPACE;
+  if (overlap(workspace, lay.total, h, (size_t)M * H * 2) ||
+      overlap(workspace, lay.total, W, w_bytes(V, H, dtype)))
+    return DFLASH2_EINVAL;
+  char* wsb = static_cast<char*>(workspace);
+  return status_of(launch_lmhead_cand(
+      h, W, reinterpret_cast<float*>(wsb + lay.z), reinterpret_cast<float*>(wsb),
+      reinterpret_cast<uint32_t*>(wsb + lay.gmax), reinterpret_cast<int*>(wsb + lay.cnt),
+      wsb + lay.slots, M, H, V, dtype, as_stream(stream)));
+}
+
+DFLASH2_API int dflash2_topk16_candidates(const void* workspace, size_t workspace_bytes,
+                                          float* top_val, int32_t* top_idx, int M, int H, int V,
+                                          int K, void* stream) {
+  if (K != kTopK || M < 0 || V < kTopK || H < 8 || (long long)M * V > (1LL << 40))
+    return DFLASH2_EINVAL;
+  if (M == 0) return DFLASH2_OK;
+  int st = check_topk_out(top_val, top_idx, M);
+  if (st != DFLASH2_OK) return st;
+  const TopkWs lay = topk_ws(M, V, DFLASH2_BF16, false);
+  if (!workspace || workspace_bytes < lay.total ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return DFLASH2_EWORKSPACE;
+  const size_t ob = (size_t)M * kTopK * 4;
+  if (overlap(top_val, ob, workspace, lay.total) || overlap(top_idx, ob, workspace, lay.total) ||
+      overlap(top_val, ob, top_idx, ob))
+    return DFLASH2_EINVAL;
+  const char* wsb = static_cast<const char*>(workspace);
+  return status_of(launch_topk16_cand(
+      reinterpret_cast<const float*>(wsb + lay.z), reinterpret_cast<const float*>(wsb),
+      reinterpret_cast<const int*>(wsb + lay.cnt), wsb + lay.slots, top_val, top_idx, M, V,
+      as_stream(stream)));
 }
 
 static int pair_score(const float* top_val, const int32_t* top_idx, const int32_t* anchor_tok,

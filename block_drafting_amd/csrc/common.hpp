@@ -90,6 +90,19 @@ hipError_t launch_lmhead_pack(const void* W, void* Wp, int V, int H, hipStream_t
 hipError_t launch_lmhead(const void* h, const void* W, float* logits, float* tmax, int M, int H,
                          int V, int dtype, hipStream_t s);
 
+// Candidate form of the bf16 GEMM + tile maxima (logits kept only where the
+// top-16 may need them): per (row, N tile) a count cnt (kCandDense: the
+// tile's logits were stored) and kCandSlots (value bits, column) slots; gmax
+// [M, 16] is the GEMM's own scratch (reset by the launch).  dtype 1 or 2.
+constexpr int kCandSlots = 4;
+constexpr int kCandDense = -1;
+hipError_t launch_lmhead_cand(const void* h, const void* W, float* logits, float* tmax,
+                              uint32_t* gmax, int* cnt, void* slots, int M, int H, int V,
+                              int dtype, hipStream_t s);
+hipError_t launch_topk16_cand(const float* logits, const float* tmax, const int* cnt,
+                              const void* slots, float* top_val, int32_t* top_idx, int M, int V,
+                              hipStream_t s);
+
 int topk16_splits(int M, int V);
 size_t topk16_workspace_bytes(int M, int V);
 hipError_t launch_topk16(const float* logits, float* top_val, int32_t* top_idx, int M, int V,

@@ -28,6 +28,18 @@
 namespace dflash2 {
 namespace {
 
+// ord(): canonical floats (-0 -> +0, NaN -> -inf) onto uint32 in the same order.
+__device__ __forceinline__ uint32_t cand_ord(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (f != f) u = 0xff800000u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float cand_val(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+constexpr uint32_t kCandOrdNegInf = 0x007fffffu;  // cand_ord(-inf)
+
 template <int BM, int BN, int BK, int WM, int WN>
 struct GemmCfg {
   static constexpr int kThreads = WM * WN * 64;
@@ -46,10 +58,30 @@ struct GemmCfg {
 
 // PACKED: W comes in the tiled layout of lmhead_pack_kernel (each 256-row x
 // 64-column block contiguous), so every slice of a W tile is one 32 KB run.
-template <int BM, int BN, int BK, int WM, int WN, bool KTAIL, bool PACKED>
+//
+// CAND (logits not wanted, only the top-16): a row of a tile writes its
+// logits only when it cannot prove they are not needed.  Each row keeps 16
+// group maxima in memory (group = N tile mod 16): every finished tile raises
+// its group's entry to its row maximum (an atomic max of the order-preserving
+// uint32 of the value).  The 16 group maxima are 16 distinct elements of the
+// row, so their minimum theta is at most the row's 16th largest logit, at
+// any moment and whatever a reader sees of the other tiles' updates (entries
+// only grow).  A tile row that finds all 16 groups filled stores only its
+// values >= theta, as (value bits, column) pairs in kCandSlots slots, with
+// their count; a row whose groups are not all filled yet (the first round
+// of tiles) or that has more than kCandSlots such values stores its 256
+// logits to C and count kCandDense.  Every top-16 element of the row is
+// then either in a stored tile or in a slot.
+struct CandOut {
+  uint32_t* gmax;  // [M, 16] group maxima (orders), reset to cand_ord(-inf) before the launch
+  int* cnt;        // [M, ntiles] slots used, or kCandDense
+  uint2* slots;    // [M, ntiles, kCandSlots] (value bits, column)
+};
+
+template <int BM, int BN, int BK, int WM, int WN, bool KTAIL, bool PACKED, bool CAND>
 __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bw, float* __restrict__ C,
-    float* __restrict__ tmax, int M, int N, int K, int mtiles, int ntiles) {
+    float* __restrict__ tmax, int M, int N, int K, int mtiles, int ntiles, CandOut cand) {
   using Cfg = GemmCfg<BM, BN, BK, WM, WN>;
   constexpr int kT = Cfg::kThreads;
   constexpr int kLdk = Cfg::kLdk;
@@ -59,6 +91,9 @@ __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
   constexpr int kSteps = BK / 16;
   constexpr int kLoads = Cfg::kAPer + Cfg::kBPer;
   static_assert(kSteps >= 3 && kSteps % 2 == 0, "pipeline needs an even step count >= 4");
+  static_assert(!CAND || kT >= BM, "one thread per tile row in the candidate epilogue");
+  static_assert((WN + 2) * BM * 4 + BM * kCandSlots * 8 + 8 <= 2 * Cfg::kStage * 2,
+                "epilogue LDS fits in the stages");
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg::kStage];
 
   const int tile = xcd_tile(blockIdx.x, mtiles * ntiles);
@@ -218,6 +253,15 @@ __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
 
   // Accumulator layout of a 32x32 block: register r of lane l holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.  Half-waves store 128-byte runs.
+  // CAND: this row's group maxima, loaded during the last exchange steps
+  // (earlier they would compete with the 64 values per lane for registers)
+  u32x4_t gq[4];
+  float* red = reinterpret_cast<float*>(lds);  // [WN][BM]; the stages are done
+  float* cth = red + WN * BM;                  // CAND: per row, theta (-inf: dense)
+  int* cpos = reinterpret_cast<int*>(cth + BM);  // CAND: per row, slots taken
+  uint2* cslot = reinterpret_cast<uint2*>(cpos + BM);  // CAND: per row, kCandSlots slots
+  int* cflag = reinterpret_cast<int*>(cslot + BM * kCandSlots);  // CAND: [0] some row dense,
+                                                                 // [1] every row dense
   if (tmax) {
     // Maximum of every row over this tile's BN columns (columns past N
     // excluded, NaN ignored by fmaxf).  Each lane holds kTm * 16 rows of its
@@ -226,7 +270,6 @@ __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
     // place of 64 full butterflies) leaves every lane two finished rows,
     // and the WN waves of a row band meet in LDS.
     static_assert(kTm * 16 == 64, "reduce-scatter sized for 64 rows per lane");
-    float* red = reinterpret_cast<float*>(lds);  // [WN][BM]; the stages are done
     float v[64];
 #pragma unroll
     for (int i = 0; i < kTm; ++i)
@@ -258,6 +301,11 @@ __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
     step(std::integral_constant<int, 1>{}, 64);
     step(std::integral_constant<int, 2>{}, 32);
     step(std::integral_constant<int, 4>{}, 16);
+    if (CAND && tid < BM && m0 + tid < M) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        gq[q] = reinterpret_cast<const u32x4_t*>(cand.gmax + (size_t)(m0 + tid) * 16)[q];
+    }
     step(std::integral_constant<int, 8>{}, 8);
     step(std::integral_constant<int, 16>{}, 4);
     __syncthreads();  // every wave is done with the stages
@@ -273,13 +321,112 @@ __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
       const int r = idx & 15;
       red[wn * BM + wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)] = v[j];
     }
+    if (CAND && tid == 0) {
+      cflag[0] = 0;
+      cflag[1] = 1;
+    }
     __syncthreads();
     for (int row = tid; row < BM; row += kT) {
       float v = red[row];
 #pragma unroll
       for (int w = 1; w < WN; ++w) v = fmaxf(v, red[w * BM + row]);
       if (m0 + row < M) tmax[(size_t)(m0 + row) * ntiles + nt] = v;
+      if constexpr (CAND) {
+        float th = -INFINITY;
+        if (m0 + row < M) {
+          atomicMax(cand.gmax + (size_t)(m0 + row) * 16 + (nt & 15), cand_ord(v));
+          uint32_t lo = gq[0][0];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) lo = min(lo, gq[q][e]);
+          if (lo > kCandOrdNegInf) th = cand_val(lo);  // all 16 groups filled
+        }
+        cth[row] = th;
+        cpos[row] = 0;
+        if (m0 + row < M) {
+          if (th == -INFINITY) cflag[0] = 1;  // some row stores densely
+          else cflag[1] = 0;                  // not every row does
+        }
+      }
     }
+  }
+  if constexpr (CAND) {
+    // Tile rows with theta: their values >= theta into LDS slots (a ballot
+    // per value; slot positions from an LDS counter per row), then one
+    // thread per row writes the row's slots out.  Rows without theta (dense)
+    // are skipped here and stored below.
+    __syncthreads();
+    const bool all_dense = cflag[1] != 0;
+    if (!all_dense) {
+#pragma unroll
+      for (int i = 0; i < kTm; ++i) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int rl0 = wm * (BM / WM) + i * 32 + 8 * r4 + 4 * (lane >> 5);
+          const f32x4_t t4 = *reinterpret_cast<const f32x4_t*>(cth + rl0);
+#pragma unroll
+          for (int j = 0; j < kTn; ++j) {
+            const int col = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x = acc[i][j][r4 * 4 + e];
+              // bitwise operators: short-circuit forms compile to branches
+              const bool pass = (x >= t4[e]) & (t4[e] != -INFINITY) & (col < N) &
+                                (m0 + rl0 + e < M);
+              if (__ballot(pass)) {
+                if (pass) {
+                  const int q = atomicAdd(cpos + rl0 + e, 1);
+                  if (q < kCandSlots)
+                    cslot[(rl0 + e) * kCandSlots + q] = uint2{__float_as_uint(x), (uint32_t)col};
+                }
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // counts; a row with more values >= theta than slots stores densely
+      for (int row = tid; row < BM; row += kT) {
+        const int np = cpos[row];
+        const bool dense = cth[row] == -INFINITY || np > kCandSlots;
+        if (m0 + row < M) {
+          const size_t rt = (size_t)(m0 + row) * ntiles + nt;
+          cand.cnt[rt] = dense ? kCandDense : np;
+          if (!dense)
+            for (int q = 0; q < np; ++q) cand.slots[rt * kCandSlots + q] = cslot[row * kCandSlots + q];
+        }
+        if (dense) {
+          cth[row] = -INFINITY;
+          if (m0 + row < M) cflag[0] = 1;
+        }
+      }
+      __syncthreads();
+      if (!cflag[0]) return;  // no dense row in this tile (uniform)
+    } else {
+      for (int row = tid; row < BM; row += kT)
+        if (m0 + row < M) cand.cnt[(size_t)(m0 + row) * ntiles + nt] = kCandDense;
+    }
+    // dense rows: every logit, as without CAND
+#pragma unroll
+    for (int i = 0; i < kTm; ++i) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int rl0 = wm * (BM / WM) + i * 32 + 8 * r4 + 4 * (lane >> 5);
+        const f32x4_t t4 = *reinterpret_cast<const f32x4_t*>(cth + rl0);
+#pragma unroll
+        for (int j = 0; j < kTn; ++j) {
+          const int col = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = m0 + rl0 + e;
+            if (t4[e] == -INFINITY && col < N && row < M)
+              __builtin_nontemporal_store(acc[i][j][r4 * 4 + e], C + (size_t)row * N + col);
+          }
+        }
+      }
+    }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < kTm; ++i) {
@@ -341,21 +488,28 @@ __global__ __launch_bounds__(256) void tilemax_kernel(const float* __restrict__ 
   if (lane == 0) tmax[w] = v;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool PACKED>
+template <int BM, int BN, int BK, int WM, int WN, bool PACKED, bool CAND>
 hipError_t launch_bf16(const uint16_t* h, const uint16_t* W, float* z, float* tmax, int M, int H,
-                       int V, hipStream_t s) {
+                       int V, CandOut cand, hipStream_t s) {
   static_assert(BN == kTileMaxCols, "tile maxima follow the N tiles");
   const int mt = (M + BM - 1) / BM;
   const int nt = (V + BN - 1) / BN;
   if (H % BK == 0)
-    hipLaunchKernelGGL((lmhead_bf16_kernel<BM, BN, BK, WM, WN, false, PACKED>),
+    hipLaunchKernelGGL((lmhead_bf16_kernel<BM, BN, BK, WM, WN, false, PACKED, CAND>),
                        dim3((unsigned)(mt * nt)), dim3(WM * WN * 64), 0, s, h, W, z, tmax, M, V,
-                       H, mt, nt);
+                       H, mt, nt, cand);
   else
-    hipLaunchKernelGGL((lmhead_bf16_kernel<BM, BN, BK, WM, WN, true, PACKED>),
+    hipLaunchKernelGGL((lmhead_bf16_kernel<BM, BN, BK, WM, WN, true, PACKED, CAND>),
                        dim3((unsigned)(mt * nt)), dim3(WM * WN * 64), 0, s, h, W, z, tmax, M, V,
-                       H, mt, nt);
+                       H, mt, nt, cand);
   return hipGetLastError();
+}
+
+// Group maxima back to "unfilled" before a candidate launch.
+__global__ __launch_bounds__(256) void cand_reset_kernel(uint32_t* __restrict__ gmax,
+                                                         long long n) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) gmax[i] = kCandOrdNegInf;
 }
 
 // The packed W layout: [ceil(V / 256)][ceil(H / 64)][256][64] bf16, rows past
@@ -390,8 +544,9 @@ hipError_t launch_lmhead(const void* h, const void* W, float* logits, float* tma
   if (dtype == 1 || dtype == 2) {  // 2: W packed by launch_lmhead_pack
     const uint16_t* hb = static_cast<const uint16_t*>(h);
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
-    if (dtype == 2) return launch_bf16<256, 256, 64, 2, 4, true>(hb, Wb, logits, tmax, M, H, V, s);
-    return launch_bf16<256, 256, 64, 2, 4, false>(hb, Wb, logits, tmax, M, H, V, s);
+    if (dtype == 2)
+      return launch_bf16<256, 256, 64, 2, 4, true, false>(hb, Wb, logits, tmax, M, H, V, {}, s);
+    return launch_bf16<256, 256, 64, 2, 4, false, false>(hb, Wb, logits, tmax, M, H, V, {}, s);
   }
   const dim3 grid((unsigned)((V + 255) / 256), (unsigned)((M + 7) / 8));
   hipLaunchKernelGGL(lmhead_f32_kernel, grid, dim3(256), 0, s, static_cast<const float*>(h),
@@ -403,6 +558,23 @@ hipError_t launch_lmhead(const void* h, const void* W, float* logits, float* tma
   hipLaunchKernelGGL(tilemax_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, logits, M,
                      V, nt, tmax);
   return hipGetLastError();
+}
+
+hipError_t launch_lmhead_cand(const void* h, const void* W, float* logits, float* tmax,
+                              uint32_t* gmax, int* cnt, void* slots, int M, int H, int V,
+                              int dtype, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const long long n = (long long)M * kTopK;
+  hipLaunchKernelGGL(cand_reset_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gmax,
+                     n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const CandOut cand{gmax, cnt, static_cast<uint2*>(slots)};
+  const uint16_t* hb = static_cast<const uint16_t*>(h);
+  const uint16_t* Wb = static_cast<const uint16_t*>(W);
+  if (dtype == 2)
+    return launch_bf16<256, 256, 64, 2, 4, true, true>(hb, Wb, logits, tmax, M, H, V, cand, s);
+  return launch_bf16<256, 256, 64, 2, 4, false, true>(hb, Wb, logits, tmax, M, H, V, cand, s);
 }
 
 size_t lmhead_pack_bytes(int V, int H) {

@@ -318,15 +318,26 @@ constexpr uint32_t kOrdNegInf = 0x007fffffu;
 // element is not kept writes to its own spare LDS slot instead of skipping
 // the write.  Per-lane branches (one exec-mask branch per element) made the
 // selection and compaction steps several times slower.
-template <int VEC>
+//
+// CAND: the logits come from the GEMM's candidate form.  A tile whose count
+// cnt[m, t] is kCandDense was stored whole; any other tile left only its
+// values >= a lower bound of the row's 16th value (so every top-16 element
+// of the tile) in kCandSlots (value bits, column) slots, the first cnt of
+// them used.  Such a tile is read as those slots: lanes 0 and 1 load two
+// slots each in place of the tile's 1 KB.
+template <int VEC, bool CAND>
 __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restrict__ logits,
                                                            const float* __restrict__ tmax, int V,
                                                            int nt, float* __restrict__ top_val,
-                                                           int32_t* __restrict__ top_idx) {
+                                                           int32_t* __restrict__ top_idx,
+                                                           const int* __restrict__ cnt,
+                                                           const uint2* __restrict__ slots) {
+  static_assert(!CAND || kCandSlots == 4, "two slots per 16-byte load, lanes 0 and 1");
   constexpr int kList = 64 * kMaxChunk;
   __shared__ uint64_t cand[kCandCap + 64];  // + one spare slot per lane
   __shared__ int list[kList + 64];
   __shared__ uint32_t lord[kList + 64];
+  __shared__ int lcnt[CAND ? kList + 64 : 1];
   const int m = blockIdx.x;
   const int lane = threadIdx.x;
   const float* tm = tmax + (size_t)m * nt;
@@ -335,10 +346,16 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
   // index past nt (every element's order is > 0).
   uint32_t lmax = 0;
   uint32_t o[kMaxChunk];  // the last pass's orders (all of them when nt <= kList)
+  int cn[kMaxChunk];      // CAND: the same tiles' counts
   auto load_orders = [&](int c0) {
     float v[kMaxChunk];
 #pragma unroll
     for (int k = 0; k < kMaxChunk; ++k) v[k] = tm[min(c0 + k * 64 + lane, nt - 1)];
+    if constexpr (CAND) {
+#pragma unroll
+      for (int k = 0; k < kMaxChunk; ++k)
+        cn[k] = cnt[(size_t)m * nt + min(c0 + k * 64 + lane, nt - 1)];
+    }
 #pragma unroll
     for (int k = 0; k < kMaxChunk; ++k)
       o[k] = ord_of(v[k]) & (0u - (uint32_t)(c0 + k * 64 + lane < nt));
@@ -366,6 +383,7 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
       const int at = below + (s ? nsel : kList + lane - below);
       list[at] = c0 + k * 64 + lane;
       lord[at] = o[k];
+      if constexpr (CAND) lcnt[at] = cn[k];
       nsel += __popcll(sel);
     }
     // Tighter bound: the 16th largest of the selected tiles' maxima (the 16
@@ -374,12 +392,14 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
     if (nt >= 16 && nt <= kList && nsel > 16 && nsel <= 64) {
       const int t = lane < nsel ? list[lane] : 0;
       const uint32_t ot = lane < nsel ? lord[lane] : 0u;
+      const int ct = CAND && lane < nsel ? lcnt[CAND ? lane : 0] : 0;
       const uint64_t srt2 = wave_sort_desc(((uint64_t)ot << 32) | (uint32_t)(~lane));
       tau = (uint32_t)(readlane64(srt2, 15) >> 32);
       const bool s = lane < nsel && ot >= tau;
       const uint64_t sel = __ballot(s);
       __builtin_amdgcn_wave_barrier();
       list[s ? lanes_below(sel) : kList + lane] = t;
+      if constexpr (CAND) lcnt[s ? lanes_below(sel) : kList + lane] = ct;
       __builtin_amdgcn_wave_barrier();
       nsel = __popcll(sel);
     }
@@ -387,12 +407,19 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
       const int ns = min(kPruneBatch, nsel - b0);
       f32x4_t q[kPruneBatch];
       int cbase[kPruneBatch];
+      int ncn[kPruneBatch];  // CAND: slots used of a sparse tile, -1 for a stored tile
 #pragma unroll
       for (int k = 0; k < kPruneBatch; ++k) {
         const int tl = k < ns ? list[b0 + k] : 0;  // b0 + k < kList + 64
         cbase[k] = tl * kTileMaxCols + lane * 4;
         const int c = cbase[k];
-        if (VEC == 4) {
+        ncn[k] = CAND ? __builtin_amdgcn_readfirstlane(k < ns ? lcnt[CAND ? b0 + k : 0] : 0)
+                      : kCandDense;
+        if (CAND && ncn[k] != kCandDense) {
+          // slots 2 lane, 2 lane + 1 as (v, col, v, col); lanes past 1 re-read
+          const uint2* sp = slots + ((size_t)m * nt + tl) * kCandSlots + 2 * min(lane, 1);
+          q[k] = *reinterpret_cast<const f32x4_t*>(sp);
+        } else if (VEC == 4) {
           q[k] = *reinterpret_cast<const f32x4_t*>(row + min(c, V - 4));  // V % 4 == 0
         } else {
 #pragma unroll
@@ -409,10 +436,17 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
       for (int k = 0; k < kPruneBatch; ++k) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int c = cbase[k] + i;
-          const float x = q[k][i];
+          int c = cbase[k] + i;
+          float x = q[k][i];
+          bool ok = c < V;
+          if (CAND && ncn[k] != kCandDense) {  // wave-uniform
+            if (i >= 2) continue;
+            x = q[k][2 * i];
+            c = (int)__float_as_uint(q[k][2 * i + 1]);
+            ok = 2 * lane + i < ncn[k];
+          }
           // bitwise operators: short-circuit forms compile to branches
-          const bool p = (k < ns) & (c < V) & ((x >= floor_f) | (nan_pass & (x != x)));
+          const bool p = (k < ns) & ok & ((x >= floor_f) | (nan_pass & (x != x)));
           const uint64_t pm = __ballot(p);
           if (pm) {
             const int below = lanes_below(pm);
@@ -439,11 +473,27 @@ hipError_t launch_topk16_tilemax(const float* logits, const float* tmax, float* 
   const int nt = (V + kTileMaxCols - 1) / kTileMaxCols;
   const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
   if (vec)
-    hipLaunchKernelGGL(topk16_pruned_kernel<4>, dim3((unsigned)M), dim3(64), 0, s, logits, tmax, V,
-                       nt, top_val, top_idx);
+    hipLaunchKernelGGL((topk16_pruned_kernel<4, false>), dim3((unsigned)M), dim3(64), 0, s, logits,
+                       tmax, V, nt, top_val, top_idx, nullptr, nullptr);
   else
-    hipLaunchKernelGGL(topk16_pruned_kernel<1>, dim3((unsigned)M), dim3(64), 0, s, logits, tmax, V,
-                       nt, top_val, top_idx);
+    hipLaunchKernelGGL((topk16_pruned_kernel<1, false>), dim3((unsigned)M), dim3(64), 0, s, logits,
+                       tmax, V, nt, top_val, top_idx, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk16_cand(const float* logits, const float* tmax, const int* cnt,
+                              const void* slots, float* top_val, int32_t* top_idx, int M, int V,
+                              hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int nt = (V + kTileMaxCols - 1) / kTileMaxCols;
+  const uint2* sl = static_cast<const uint2*>(slots);  // 16-byte aligned
+  const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
+  if (vec)
+    hipLaunchKernelGGL((topk16_pruned_kernel<4, true>), dim3((unsigned)M), dim3(64), 0, s, logits,
+                       tmax, V, nt, top_val, top_idx, cnt, sl);
+  else
+    hipLaunchKernelGGL((topk16_pruned_kernel<1, true>), dim3((unsigned)M), dim3(64), 0, s, logits,
+                       tmax, V, nt, top_val, top_idx, cnt, sl);
   return hipGetLastError();
 }
 

@@ -4,7 +4,9 @@
  * The step (per block of L drafted positions):
  *   1. two-tap local conv            dflash2_twotap_conv
  *   2. LM-head logits + top-16       dflash2_logits_topk  (= dflash2_lmhead_logits_tilemax
- *                                                            then dflash2_topk16_tilemax)
+ *                                                            then dflash2_topk16_tilemax;
+ *                                    without a logits buffer, bf16: dflash2_lmhead_candidates
+ *                                                            then dflash2_topk16_candidates)
  *   3. adjacent-pair scores          dflash2_pair_score
  *   4. max-plus path walk            dflash2_path_select
  *   5. greedy verification           dflash2_verify_greedy
@@ -200,7 +202,9 @@ int dflash2_topk16(const float* logits, float* top_val, int32_t* top_idx,
 
 /*
  * Workspace for dflash2_logits_topk: the tile maxima, and the logits too
- * when logits_given == 0 (the caller passes no logits buffer).
+ * when logits_given == 0 (the caller passes no logits buffer); for bf16
+ * operands without a logits buffer also the candidate form's parts (below):
+ * 64 bytes per row and 36 bytes per row and 256-column tile.
  */
 size_t dflash2_logits_topk_workspace(int M, int H, int V, int K, int dtype, int logits_given);
 
@@ -223,6 +227,39 @@ int dflash2_logits_topk(const void* h, const void* W, float* logits,
                         float* top_val, int32_t* top_idx,
                         int M, int H, int V, int K, int dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dflash2_logits_topk with logits == NULL and bf16 operands (DFLASH2_BF16 or
+ * DFLASH2_BF16_PACKED) runs the GEMM in a candidate form that leaves out
+ * most of the [M, V] logits, and is these two calls on its workspace
+ * (dflash2_logits_topk_workspace(M, H, V, 16, dtype, 0) bytes, 256-byte
+ * aligned), which a caller may also make itself (to time or schedule the
+ * two launches apart; nothing may touch the workspace in between).
+ * [POST] "A lightweight path selector": only the 16 best tokens of each
+ * position are used, so the logits outside them need not leave the chip.
+ *   dflash2_lmhead_candidates: the GEMM.  Every row keeps 16 running group
+ *     maxima (group = 256-column tile index mod 16, reset at the start of
+ *     the call); once all 16 are set, their minimum is a lower bound on the
+ *     row's 16th largest logit.  A row of a tile that finishes with that
+ *     bound in hand writes only its values at or above it (at most 4, as
+ *     value and column); a row without the bound, or with more than 4 such
+ *     values, writes its 256 logits.  Tile maxima as for
+ *     dflash2_lmhead_logits_tilemax.  EUNSUPPORTED for fp32 operands; other
+ *     errors as for dflash2_lmhead_logits; the workspace may not overlap h
+ *     or W.
+ *   dflash2_topk16_candidates: the top-16 from that workspace (M and V as
+ *     given to the GEMM): the tiles whose maximum reaches the 16th largest
+ *     tile maximum, each read whole or as its slots.  Results bit for bit
+ *     those of dflash2_logits_topk with a logits buffer (the same GEMM
+ *     values, the same order and ties).  top_val / top_idx may not overlap
+ *     the workspace.
+ * Both return DFLASH2_EWORKSPACE for a missing, short or misaligned
+ * workspace and DFLASH2_EINVAL for K != 16 or bad sizes.
+ */
+int dflash2_lmhead_candidates(const void* h, const void* W, int M, int H, int V, int dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
+int dflash2_topk16_candidates(const void* workspace, size_t workspace_bytes, float* top_val,
+                              int32_t* top_idx, int M, int H, int V, int K, void* stream);
 
 /*
  * Measurement aid, not a step of the path: the attainable matrix-core rate

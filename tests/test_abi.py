@@ -110,9 +110,13 @@ def test_lmhead_and_topk_validation():
     assert L.dflash2_topk16(big, Q, Q + 65536, 64, 151936, 16, None, 0, None) == EWS
     assert L.dflash2_topk16(big, Q, Q + 65536, 64, 151936, 16, P, need - 1, None) == EWS
     assert L.dflash2_topk16(big, Q, Q + 65536, 64, 151936, 16, P + 16, need, None) == EWS  # align
-    ws_given = L.dflash2_logits_topk_workspace(512, 5120, 151936, 16, 1, 1)
-    ws_none = L.dflash2_logits_topk_workspace(512, 5120, 151936, 16, 1, 0)
-    assert ws_none - ws_given == 512 * 151936 * 4
+    ws_given = L.dflash2_logits_topk_workspace(512, 5120, 151936, 16, 0, 1)
+    ws_none = L.dflash2_logits_topk_workspace(512, 5120, 151936, 16, 0, 0)
+    assert ws_none - ws_given == 512 * 151936 * 4                  # fp32: the logits
+    # bf16 without logits: + group maxima [M, 16], counts [M, 594], slots [M, 594, 4] x 8 bytes
+    cand = 512 * 16 * 4 + 512 * 594 * 4 + 512 * 594 * 32
+    assert (L.dflash2_logits_topk_workspace(512, 5120, 151936, 16, 1, 0) ==
+            L.dflash2_logits_topk_workspace(512, 5120, 151936, 16, 1, 1) + cand + 512 * 151936 * 4)
     assert L.dflash2_logits_topk(P, Q, None, P + 4096, P + 8192, 512, 5120, 151936, 16, 1,
                                  None, 0, None) == EWS                             # no room for logits
 
@@ -389,3 +393,30 @@ def test_sample_mode_validation():
                               mode, None, None, slot + 0x400000, None, q + 0x400000, None)
     assert g(*args(1, B=0)) == 0
     assert g(*args(3)) == EINVAL
+
+
+def test_candidate_form_validation():
+    """dflash2_lmhead_candidates / dflash2_topk16_candidates reject bad
+    arguments on the host before any launch."""
+    L = bd.lib()
+    g, t = L.dflash2_lmhead_candidates, L.dflash2_topk16_candidates
+    need = L.dflash2_logits_topk_workspace(64, 256, 4096, 16, 1, 0)
+    assert need == L.dflash2_logits_topk_workspace(64, 256, 4096, 16, 2, 0)
+    ws = P + 0x40000000
+    #       h  W   M   H    V     dt ws  bytes
+    assert g(P, Q, 64, 256, 4096, 0, ws, need, None) == EUNSUP            # fp32 operands
+    assert g(P, Q, 64, 256, 4096, 1, None, 0, None) == EWS
+    assert g(P, Q, 64, 256, 4096, 1, ws, need - 1, None) == EWS
+    assert g(P, Q, 64, 256, 4096, 1, ws + 16, need, None) == EWS          # 256-byte alignment
+    assert g(P, Q, 64, 256, 4096, 1, P, need, None) == EINVAL             # over h
+    assert g(P, Q, 64, 60, 4096, 1, ws, need, None) == EINVAL             # H % 8
+    assert g(P, Q, 0, 256, 4096, 1, None, 0, None) == 0                   # M == 0
+    out = P + 0x80000000
+    #       ws  bytes  top_val  top_idx     M   H    V     K
+    assert t(ws, need, out, out + 8192, 64, 256, 4096, 8, None) == EINVAL  # K != 16
+    assert t(ws, need - 1, out, out + 8192, 64, 256, 4096, 16, None) == EWS
+    assert t(None, 0, out, out + 8192, 64, 256, 4096, 16, None) == EWS
+    assert t(ws, need, ws, out + 8192, 64, 256, 4096, 16, None) == EINVAL  # top_val in the workspace
+    assert t(ws, need, out, out, 64, 256, 4096, 16, None) == EINVAL        # outputs alias
+    assert t(ws, need, None, out, 64, 256, 4096, 16, None) == EINVAL
+    assert t(ws, need, out, out + 8192, 0, 256, 4096, 16, None) == 0

@@ -35,21 +35,26 @@ def test_bench_has_no_cpu_fallback():
 
 def test_bench_reports_traffic_only_for_the_measured_kernel(tmp_path, monkeypatch):
     """The roofline's traffic comes from a committed counter summary only when
-    it was taken on the same workload, W layout and GEMM source."""
+    it was taken on the same workload, W layout, output form and GEMM source."""
     sys.path.insert(0, ROOT)
     import bench
     src_hash = bench.kernel_source_hash()
     f = tmp_path / "traffic.txt"
+    g = tmp_path / "traffic_cand.txt"
     f.write_text("# comment: 1\nworkload: 27b-head\nw_layout: packed\n"
                  f"kernel_source_sha256_16: {src_hash}\ntraffic_bytes_per_launch: 123456\n")
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    assert bench.measured_traffic("27b-head", "packed") == 123456.0
-    assert bench.measured_traffic("27b-head", "row-major") is None      # other W layout
-    assert bench.measured_traffic("4b-head", "packed") is None          # other workload
+    g.write_text("workload: 27b-head\nw_layout: packed\noutput: candidates\n"
+                 f"kernel_source_sha256_16: {src_hash}\ntraffic_bytes_per_launch: 654321\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILES", [str(f), str(g)])
+    assert bench.measured_traffic("27b-head", "packed", "logits") == 123456.0
+    assert bench.measured_traffic("27b-head", "packed", "candidates") == 654321.0
+    assert bench.measured_traffic("27b-head", "row-major", "logits") is None   # other W layout
+    assert bench.measured_traffic("4b-head", "packed", "logits") is None       # other workload
     f.write_text(f.read_text().replace(src_hash, "0" * 16))
-    assert bench.measured_traffic("27b-head", "packed") is None          # kernel changed since
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.txt"))
-    assert bench.measured_traffic("27b-head", "packed") is None
+    assert bench.measured_traffic("27b-head", "packed", "logits") is None      # kernel changed
+    assert bench.measured_traffic("27b-head", "packed", "candidates") == 654321.0
+    monkeypatch.setattr(bench, "TRAFFIC_FILES", [str(tmp_path / "missing.txt")])
+    assert bench.measured_traffic("27b-head", "packed", "logits") is None
 
 
 def test_chunked_fill_does_not_depend_on_thread_count(monkeypatch):
