@@ -254,6 +254,30 @@ def test_first_conv_all_blocks(case):
     print(f"first conv over {w.B} blocks: {(got != want).mean():.2e} of elements off by 1 ulp")
 
 
+def test_candidate_form_topk_all_rows(case):
+    """The LM head + top-16 without a logits buffer (for bf16 the GEMM's
+    candidate form: most logits never leave the chip) over every row of the
+    workload, fed the GPU's own final activations: bit for bit the
+    materialised step's top-16 (row-major and packed W), and the oracle's
+    top-16 of the GPU's logits on the parity subset."""
+    w, buf, blocks = case["w"], case["buf"], case["blocks"]
+    M = w.B * w.L
+    h = buf.y[(w.n_convs - 1) % len(buf.y)].view(M, w.H)
+    weights = [case["dev"]["W"]]
+    if w.dtype == "bf16":
+        weights.append(bd.lmhead_pack(case["dev"]["W"]))
+    for W in weights:
+        tv, ti = bd.logits_topk(h, W)
+        torch.cuda.synchronize()
+        assert torch.equal(ti, buf.top_idx)
+        assert torch.equal(tv.view(torch.int32), buf.top_val.view(torch.int32))
+    rows = (blocks[:, None] * w.L + np.arange(w.L)[None, :]).reshape(-1)
+    zr = buf.logits[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    wv, wi = O.topk16(zr)
+    np.testing.assert_array_equal(ti.cpu().numpy()[rows], wi)
+    np.testing.assert_array_equal(tv.cpu().numpy()[rows].view(np.uint32), wv.view(np.uint32))
+
+
 # ------------------------------------------------------------------ end to end
 def test_end_to_end_subset(case):
     w, buf, ora, blocks = case["w"], case["buf"], case["ora"], case["blocks"]
