@@ -302,9 +302,18 @@ __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
     step(std::integral_constant<int, 2>{}, 32);
     step(std::integral_constant<int, 4>{}, 16);
     if (CAND && tid < BM && m0 + tid < M) {
+      // relaxed atomic loads: other workgroups raise these entries meanwhile,
+      // and any value read is a valid (possibly older, so lower) group
+      // maximum.  Workgroup scope reads this XCD's L2, which its own
+      // workgroups' atomics keep up to date; an agent-scope load reads a
+      // copy further out that lags it, which lowers the bound and makes
+      // more tile rows overflow their slots.
+      uint32_t* gm = cand.gmax + (size_t)(m0 + tid) * 16;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        gq[q] = reinterpret_cast<const u32x4_t*>(cand.gmax + (size_t)(m0 + tid) * 16)[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          gq[q][e] = __hip_atomic_load(gm + 4 * q + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     step(std::integral_constant<int, 8>{}, 8);
     step(std::integral_constant<int, 16>{}, 4);
