@@ -53,7 +53,9 @@ TOPK = 16
 PATH_MODES = {"viterbi": 0, "greedy": 1}
 SAMPLE_MODES = {"chain": 0, "path": 1}
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libdflash2.so")
+# DFLASH2_LIBRARY selects another build of the same library (the host
+# AddressSanitizer build that the CPU tests load, for instance)
+library_path = os.environ.get("DFLASH2_LIBRARY") or os.path.join(_HERE, "libdflash2.so")
 _lib = None
 
 _P = ctypes.c_void_p

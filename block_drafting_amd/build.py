@@ -1,9 +1,14 @@
 """Build libdflash2.so (the HIP kernels and their C ABI) for gfx950 with hipcc.
 
-Usage:  python -m block_drafting_amd.build [--verbose]
+Usage:  python -m block_drafting_amd.build [--verbose] [--asan]
 
 Each .hip source compiles to an object in parallel, then the objects link
 into block_drafting_amd/libdflash2.so next to this file.  Always rebuilds.
+
+--asan builds a second copy, _build/asan/libdflash2.so, whose host code (the
+C ABI's argument checks and launch set-up) is instrumented with
+AddressSanitizer; the device code is built as usual.  Load it with the
+clang runtime preloaded (asan_runtime()) and DFLASH2_LIBRARY pointing at it.
 """
 from __future__ import annotations
 
@@ -30,6 +35,8 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# host-only instrumentation: each -fsanitize= directly after -Xarch_host
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
 
 
 def hipcc() -> str:
@@ -51,30 +58,48 @@ def _run(cmd, verbose):
         print(out)
 
 
-def build(verbose: bool = False) -> str:
+def asan_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime that an --asan build needs
+    preloaded (it is not linked into a shared library)."""
     cc = hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    r = subprocess.run([cc, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang AddressSanitizer runtime not found")
+    return path
+
+
+def build(verbose: bool = False, asan: bool = False) -> str:
+    cc = hipcc()
+    out_dir = os.path.join(BUILD_DIR, "asan") if asan else BUILD_DIR
+    lib = os.path.join(out_dir, "libdflash2.so") if asan else LIB
+    flags = HIPCC_FLAGS + (ASAN_FLAGS if asan else [])
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in srcs]
+    objs = [os.path.join(out_dir, os.path.basename(s) + ".o") for s in srcs]
 
     def compile_one(pair):
         src, obj = pair
-        _run([cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj], verbose)
+        _run([cc, *flags, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj], verbose)
 
     jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", "8"))))
     with ThreadPoolExecutor(jobs) as ex:
         list(ex.map(compile_one, zip(srcs, objs)))
-    tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = lib + ".tmp"
+    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + (ASAN_FLAGS if asan else [])
+    _run(link + ["-o", tmp, *objs], verbose)
+    os.replace(tmp, lib)
+    return lib
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--asan", action="store_true",
+                    help="host AddressSanitizer build into _build/asan (the in-tree library is untouched)")
     a = ap.parse_args(argv)
-    print(build(a.verbose))
+    print(build(a.verbose, a.asan))
 
 
 if __name__ == "__main__":
