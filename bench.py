@@ -657,6 +657,10 @@ def main(argv=None):
         for k, s_, e_ in zip(order, marks[:-1], marks[1:]):
             stage_ms[k] += s_.elapsed_time(e_) / a.steps
     gemm_ms = [ev_all[i]["gemm"].elapsed_time(ev_all[i]["topk"]) for i in range(a.steps)]
+    # per-step times of the stage pass (the timed region is one replay of K
+    # steps, so its per-step spread is taken here)
+    step_ms = sorted(ev_all[i]["conv"].elapsed_time(ev_all[i]["end"]) for i in range(a.steps))
+    pct = lambda q: step_ms[min(len(step_ms) - 1, int(round(q * (len(step_ms) - 1))))]
     ms_step = wall * 1e3 / a.steps
     gemm_s = float(np.mean(gemm_ms)) * 1e-3
     flops = 2.0 * M * H * V
@@ -759,6 +763,8 @@ def main(argv=None):
                     "source": "events around its launch in the stage pass after the timed region"},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "stage_pass_ms_per_step": round(stage_wall_ms, 4),
+        "stage_pass_step_ms": {"p10": round(pct(0.1), 4), "median": round(pct(0.5), 4),
+                               "p90": round(pct(0.9), 4)},
         "stage_hbm_gbs": hbm,
         "stage_roofline": stage_roof,
         "roofline": roof,
