@@ -153,3 +153,49 @@ def test_fused_step_matches_materialised_step():
                                          buf.accept_len, buf.next_tok)])
     for a, b in zip(*outs):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_candidate_form_graph_replays():
+    """logits + top-16 in the candidate form captured in a HIP graph (the
+    group-maxima reset, GEMM and merge as three nodes): every replay, with
+    eager calls on other inputs and synchronisations in between (which leave
+    other group maxima in the workspace), gives the eager result; so does an
+    eager call afterwards."""
+    M, H, V = 512, 512, 151936
+    g = torch.Generator(device=DEV).manual_seed(21)
+    W = bd.lmhead_pack(_bf16(torch.randn((V, H), generator=g, device=DEV) / H ** 0.5))
+    h = _bf16(torch.randn((M, H), generator=g, device=DEV))
+    h_other = _bf16(torch.randn((M, H), generator=g, device=DEV) * 3.0)   # larger logits
+    ws = torch.empty(bd.logits_topk_workspace(M, H, V, torch.bfloat16, False), dtype=torch.uint8,
+                     device=DEV)
+    tv = torch.empty((M, 16), dtype=torch.float32, device=DEV)
+    ti = torch.empty((M, 16), dtype=torch.int32, device=DEV)
+
+    def call(x):
+        bd.logits_topk(x, W, top_val=tv, top_idx=ti, workspace=ws)
+
+    call(h)
+    torch.cuda.synchronize()
+    want_v, want_i = tv.clone(), ti.clone()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        call(h)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            call(h)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        call(h_other)                      # other inputs through the same workspace
+        torch.cuda.synchronize()
+        tv.zero_()
+        ti.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ti, want_i)
+        assert torch.equal(tv.view(torch.int32), want_v.view(torch.int32))
+    call(h)
+    torch.cuda.synchronize()
+    assert torch.equal(ti, want_i)
