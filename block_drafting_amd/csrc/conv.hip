@@ -486,6 +486,213 @@ __global__ __launch_bounds__(256) void conv_dyng_kernel(const T* __restrict__ x,
   }
 }
 
+// ---------------------------------------------------------------- bf16 rows, ten channels per thread
+// The bf16 path for H a multiple of 640 up to 5120 (H = 5120: 512 threads,
+// eight waves, two per SIMD).  Thread t owns channels [10t, 10t + 10) of
+// every row of its workgroup: NG groups of R consecutive positions of one
+// block.  Group g + PD's rows load while group g is mixed.
+//
+// Every access is a buffer access.  A group's descriptor ends at its last
+// row inside the block, so rows past L read zeros and store nothing, and
+// the loop body has no branches: the compiler then counts outstanding
+// loads exactly and only waits for the group it is about to use.  With a
+// projection the 2R partial dot products of a group are reduced over the
+// wave (reduce-scatter), then over the waves in LDS in wave order (so the
+// sum does not depend on timing) behind one barrier per group.  That
+// barrier waits for LDS traffic only: __syncthreads() also waits for every
+// outstanding global load, which would drain the next group's loads.
+//
+// Rounding (one correct rounding to bf16 of the fp64 value v): (float)v is
+// the nearest fp32 value to v.  Every bf16 midpoint is an fp32 value, so
+// v and (float)v lie on the same side of every midpoint unless (float)v
+// is a midpoint itself (low 16 bits 0x8000); the nearest-even bf16 of
+// (float)v is then v's.  When any lane of the wave meets a midpoint, the
+// row takes the round-to-odd conversion above.
+constexpr int kC10 = 10;         // channels per thread
+constexpr int kC10Threads = 512;  // largest workgroup (H = 5120)
+constexpr int kRsrcFlags = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           kRsrcFlags);
+}
+
+// Ten bf16 channels: a 16-byte and a 4-byte load (dword aligned).
+struct Raw10 {
+  uint32_t w[5];
+  __device__ double at(int i) const {
+    return (double)((i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]));
+  }
+  __device__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = a[i];
+    w[4] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 16, 0, 0);
+  }
+};
+
+// NF fp32 values (NF = 4q or 4q + 2) from byte offset off.
+template <int NF>
+__device__ __forceinline__ void load_floats(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                            float (&f)[NF]) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int q = 0; q + 4 <= NF; q += 4) {
+    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, off + q * 4, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[q + i] = __uint_as_float(a[i]);
+  }
+  if constexpr (NF % 4 == 2) {
+    const u32x2_t a = __builtin_bit_cast(
+        u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off + (NF - 2) * 4, 0, 0));
+    f[NF - 2] = __uint_as_float(a[0]);
+    f[NF - 1] = __uint_as_float(a[1]);
+  }
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two fp32 values to a bf16 pair, nearest even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+__device__ __forceinline__ bool on_bf16_midpoint(float f) {
+  return (__float_as_uint(f) & 0xffffu) == 0x8000u;
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), l);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Workgroup barrier ordering LDS accesses only (global loads stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int R, int NG, int PD, bool DYN>
+__global__ __launch_bounds__(kC10Threads) void conv_rows10_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ anchor,
+    uint16_t* __restrict__ y, const float* __restrict__ k0, const float* __restrict__ k1,
+    const float* __restrict__ proj, int L, int H, int wgs_per_block) {
+  constexpr int C = kC10;
+  constexpr int N = 2 * R;       // correction dot products of a group
+  constexpr int NB = PD + 1;     // row buffers: the group in use and PD in flight
+  constexpr int NWMAX = kC10Threads / 64;
+  __shared__ double red[2][DYN ? NWMAX * N : 1];
+  const int nw = (int)(blockDim.x >> 6);
+  const int b = blockIdx.x / wgs_per_block;
+  const int t0 = (blockIdx.x - b * wgs_per_block) * (R * NG);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const uint32_t row_bytes = (uint32_t)H * 2;
+  const uint32_t cb = (uint32_t)tid * (2 * C);  // byte offset of the thread's channels in a row
+  auto group_rsrc = [&](const uint16_t* base, int g) {
+    const int tg = t0 + g * R;
+    const int nr = max(0, min(R, L - tg));
+    return byte_rsrc(base + ((size_t)b * L + tg) * H,
+                     __builtin_amdgcn_readfirstlane((uint32_t)nr * row_bytes));
+  };
+  Raw10 xr[NB][R];
+  auto load_group = [&](int g) {
+    const __amdgpu_buffer_rsrc_t rx = group_rsrc(x, g);
+#pragma unroll
+    for (int r = 0; r < R; ++r) xr[g % NB][r].load(rx, cb + r * row_bytes);
+  };
+#pragma unroll
+  for (int g = 0; g < PD && g < NG; ++g) load_group(g);
+  float ka[C], kb[C], pj[DYN ? 2 * C : 2];
+  double pv[C];  // the predecessor of the group's first row
+  {
+    const uint16_t* pp = t0 > 0 ? x + ((size_t)b * L + t0 - 1) * H
+                                : (anchor ? anchor + (size_t)b * H : x);
+    const uint32_t pbytes =
+        __builtin_amdgcn_readfirstlane((t0 > 0 || anchor) ? row_bytes : 0u);  // 0: zeros
+    Raw10 pr;
+    pr.load(byte_rsrc(pp, pbytes), cb);
+    if constexpr (DYN)
+      load_floats<2 * C>(byte_rsrc(proj, (uint32_t)H * 8), (uint32_t)tid * (8 * C), pj);
+    load_floats<C>(byte_rsrc(k0, (uint32_t)H * 4), (uint32_t)tid * (4 * C), ka);
+    load_floats<C>(byte_rsrc(k1, (uint32_t)H * 4), (uint32_t)tid * (4 * C), kb);
+#pragma unroll
+    for (int i = 0; i < C; ++i) pv[i] = pr.at(i);
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (t0 + g * R >= L) break;  // uniform over the workgroup
+    if (g + PD < NG) load_group(g + PD);
+    double xv[R][C];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < C; ++i) xv[r][i] = xr[g % NB][r].at(i);
+    double d[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) d[i] = 0.0;
+    if constexpr (DYN) {
+      // channel by channel, every row of the group
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        const double p0 = (double)pj[2 * i];
+        const double p1 = (double)pj[2 * i + 1];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          d[2 * r] += xv[r][i] * p0;
+          d[2 * r + 1] += xv[r][i] * p1;
+        }
+      }
+      int idx;
+      const double part = wave_reduce_scatter<N>(d, lane, idx);
+      if ((lane & (64 / N - 1)) == 0) red[g & 1][wave * N + idx] = part;
+      // one barrier per group: red[g & 1] is next written two groups on,
+      // after every wave has passed the barrier of the group in between
+      lds_barrier();
+      double tot = 0.0;
+      if (lane < N) {
+        tot = red[g & 1][lane];
+        for (int w = 1; w < nw; ++w) tot += red[g & 1][w * N + lane];
+      }
+#pragma unroll
+      for (int i = 0; i < N; ++i) d[i] = readlane_f64(tot, i);
+    }
+    const __amdgpu_buffer_rsrc_t ry = group_rsrc(y, g);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const double* prev = r == 0 ? pv : xv[r - 1];
+      float f[C];
+      uint64_t mid = 0;
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        const double c0 = DYN ? (double)ka[i] + d[2 * r] : (double)ka[i];
+        const double c1 = DYN ? (double)kb[i] + d[2 * r + 1] : (double)kb[i];
+        f[i] = (float)(c0 * xv[r][i] + c1 * prev[i]);
+        mid |= __builtin_amdgcn_ballot_w64(on_bf16_midpoint(f[i]));
+      }
+      if (mid) {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+          const double c0 = DYN ? (double)ka[i] + d[2 * r] : (double)ka[i];
+          const double c1 = DYN ? (double)kb[i] + d[2 * r + 1] : (double)kb[i];
+          f[i] = f64_to_f32_odd(c0 * xv[r][i] + c1 * prev[i]);
+        }
+      }
+      const uint32_t off = cb + r * row_bytes;
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4_t{pk_bf16(f[0], f[1]), pk_bf16(f[2], f[3]), pk_bf16(f[4], f[5]),
+                  pk_bf16(f[6], f[7])},
+          ry, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(pk_bf16(f[8], f[9]), ry, off + 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < C; ++i) pv[i] = xv[R - 1][i];
+  }
+}
+
 // ---------------------------------------------------------------- corrections on the matrix cores
 // The post's coefficients carry one correction pair per 16 channels, so the
 // correction of a whole batch is a real product D = X . P^T, [M x H] by
@@ -732,6 +939,44 @@ hipError_t launch_typed(const void* x, const void* anchor_h, void* y, const floa
   const T* ap = static_cast<const T*>(anchor_h);
   T* yp = static_cast<T*>(y);
   const long long rows = (long long)B * L;
+  if constexpr (sizeof(T) == 2) {
+    // bf16 rows of H = 640 k <= 5120 channels: ten channels per thread.
+    // Positions per workgroup from a sweep at H = 5120 (kernel trace, us):
+    // 2048 rows with a projection, 2 x 4 rows (one ahead): 11.0 (8 rows of
+    // the eight-channel kernel below: 16.1; 2 x 4 rows with the next two
+    // ahead: 12.0; 4 x 2: 12.1); 4096 static rows, 8 single rows, two
+    // ahead: 14.1 (18.0); 512 static rows, 2 rows: 4.9 (5.3).  Fewer
+    // positions when that leaves under 256 workgroups.
+    if ((!proj || groups == 1) && H % 640 == 0 && H <= 10 * kC10Threads) {
+      long long units = rows / 256;
+      int rn = 1;
+      while (rn < 8 && rn * 2 <= L && rn * 2 <= units) rn *= 2;
+      const int wpb = (L + rn - 1) / rn;
+      const long long wgs = (long long)B * wpb;
+      if (wgs <= 0x7fffffffLL) {
+        const dim3 grid((unsigned)wgs), blk((unsigned)(H / kC10));
+        const uint16_t* xq = static_cast<const uint16_t*>(x);
+        const uint16_t* aq = static_cast<const uint16_t*>(anchor_h);
+        uint16_t* yq = static_cast<uint16_t*>(y);
+#define DFLASH2_CONV10(RR, NN, PP, DD)                                                         \
+  hipLaunchKernelGGL((conv_rows10_kernel<RR, NN, PP, DD>), grid, blk, 0, s, xq, aq, yq, k0, k1, \
+                     proj, L, H, wpb)
+        if (proj) {
+          if (rn == 8) DFLASH2_CONV10(2, 4, 1, true);
+          else if (rn == 4) DFLASH2_CONV10(2, 2, 1, true);
+          else if (rn == 2) DFLASH2_CONV10(2, 1, 1, true);
+          else DFLASH2_CONV10(1, 1, 1, true);
+        } else {
+          if (rn == 8) DFLASH2_CONV10(1, 8, 2, false);
+          else if (rn == 4) DFLASH2_CONV10(2, 2, 1, false);
+          else if (rn == 2) DFLASH2_CONV10(2, 1, 1, false);
+          else DFLASH2_CONV10(1, 1, 1, false);
+        }
+#undef DFLASH2_CONV10
+        return hipGetLastError();
+      }
+    }
+  }
   // Rows of a block per workgroup, measured at H = 5120 (20 launches back to
   // back): the corrections' workgroups take 8 rows (15.9 us per application
   // at 2048 rows against 18.3 for one row per workgroup, 16.0 with 4);

@@ -91,11 +91,14 @@ def test_conv_parity(dt, B, L, H, mode, groups):
     assert frac == 0.0 if dt == "bf16" else frac < 1e-4
 
 
-# Shapes that reach each row-group layout of the conv kernel: several
+# Shapes that reach each row-group layout of the conv kernels: several
 # positions per workgroup (2, 4 or 8 with a projection; 2, or four
 # pipelined single rows with static taps), with L not a multiple of the
 # group so the last group is partial, no anchor, and rows wider than one
-# workgroup's 1024 chunks (H = 10240, 20480: the one-row kernels).
+# workgroup's 1024 chunks (H = 10240, 20480: the one-row kernels).  bf16
+# rows of H = 640 k <= 5120 take the ten-channels-per-thread kernel: 2 x 4,
+# 2 x 2, 2 and 1 positions with a projection, 8 single rows (two groups
+# ahead), 2 x 2, 2 and 1 static (the last from the 5120-channel shapes above).
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("B,L,H,mode,anchor", [
     (110, 5, 136, 0, True),      # 550 rows, static: 2 positions per workgroup, L odd
@@ -106,6 +109,12 @@ def test_conv_parity(dt, B, L, H, mode, groups):
     (300, 11, 136, 1, False),    # 3300 rows: 8 positions, 11 = 8 + 3
     (2, 3, 10240, 1, True),      # wider than 8192 channels: one-row kernels
     (520, 2, 20480, 0, True),
+    (230, 9, 640, 1, True),      # ten channels per thread: 2 x 4 positions, 9 = 8 + 1
+    (130, 9, 1280, 1, False),    # 2 x 2, 9 = 4 + 4 + 1, no anchor
+    (80, 7, 640, 1, True),       # 2 positions, 7 odd
+    (300, 11, 640, 0, True),     # static, 8 single rows, 11 = 8 + 3
+    (130, 9, 1280, 0, False),    # static, 2 x 2
+    (110, 5, 2560, 0, True),     # static, 2 positions (4 waves)
 ])
 def test_conv_row_groups_parity(dt, B, L, H, mode, anchor):
     x, a, k0, k1, P = _conv_case(B, L, H, dt, mode, 1, seed=B + L + H)
@@ -128,6 +137,35 @@ def test_conv_no_anchor_and_special_taps_bit_exact():
     y = to_host_bits(bd.twotap_conv(xd, torch.from_numpy(zeros).to(DEV), torch.from_numpy(ones).to(DEV), None))
     assert not np.any(y[:, 0] & 0x7fff)                                  # zero anchor
     _conv_check(x, None, (np.arange(H) % 3).astype(np.float32), np.full(H, 0.5, np.float32), None, 1, "bf16")
+
+
+@pytest.mark.parametrize("H,mode", [(640, 0), (640, 1), (5120, 1), (136, 0), (136, 1)])
+def test_conv_bf16_rounds_once_near_midpoints(H, mode):
+    """Outputs a hair above a bf16 midpoint: x alternates 2^-8 and 1 (every
+    third channel negated, anchor +-1), k0 = 1, k1 = 1 + 2^-23, so every odd
+    position is +-(1 + 2^-8 + 2^-31).  Its nearest fp32 is the midpoint
+    1 + 2^-8 itself, whose nearest-even bf16 would be 1; the one correct
+    rounding gives 1 + 2^-7.  Even positions are 1 + 2^-8 + 2^-23 (an fp32 value above the
+    midpoint).  A zero projection (mode 1) runs the corrections' kernels
+    with D = 0.  H = 640: ten channels per thread; H = 136: eight."""
+    B, L = 3, 8
+    mag = np.where(np.arange(L) % 2 == 0, 2.0 ** -8, 1.0)   # x_t
+    sgn = np.where(np.arange(H) % 3 == 0, -1.0, 1.0)         # channels negated throughout
+    xs = WL.to_bf16_bits((mag[None, :, None] * sgn[None, None, :] * np.ones((B, L, H))).astype(np.float32))
+    a = WL.to_bf16_bits(np.broadcast_to(sgn, (B, H)).astype(np.float32))
+    k0 = np.ones(H, np.float32)
+    k1 = np.full(H, 1.0 + 2.0 ** -23, np.float32)
+    P = np.zeros((H, 2), np.float32) if mode else None
+    xo, ao = O.as_f64(xs, "bf16"), O.as_f64(a, "bf16")
+    want = O.round_to_bf16(O.twotap_conv(xo, ao, k0.astype(np.float64), k1.astype(np.float64),
+                                         None if P is None else P.astype(np.float64), 1))
+    y = bd.twotap_conv(to_dev(xs, "bf16"), torch.from_numpy(k0).to(DEV), torch.from_numpy(k1).to(DEV),
+                       to_dev(a, "bf16"), None if P is None else torch.from_numpy(P).to(DEV))
+    assert np.all(np.abs(want) == 1.0 + 2.0 ** -7)  # the single rounding goes up
+    got = to_host_bits(y)
+    np.testing.assert_array_equal(O.as_f64(got, "bf16"), want)
+    assert np.all((got & 0x7fff) == 0x3F81)
+    np.testing.assert_array_equal(got[0, 1] >> 15, (sgn < 0).astype(got.dtype))
 
 
 def conv_mm_tolerance(xo, ao, P, groups, want):
