@@ -498,9 +498,8 @@ __global__ __launch_bounds__(256) void conv_dyng_kernel(const T* __restrict__ x,
 // loads exactly and only waits for the group it is about to use.  With a
 // projection the 2R partial dot products of a group are reduced over the
 // wave (reduce-scatter), then over the waves in LDS in wave order (so the
-// sum does not depend on timing) behind one barrier per group.  That
-// barrier waits for LDS traffic only: __syncthreads() also waits for every
-// outstanding global load, which would drain the next group's loads.
+// sum does not depend on timing) behind one barrier per group; the next
+// group's loads stay in flight across it.
 //
 // Rounding (one correct rounding to bf16 of the fp64 value v): (float)v is
 // the nearest fp32 value to v.  Every bf16 midpoint is an fp32 value, so
@@ -565,13 +564,6 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, l);
   const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), l);
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
-
-// Workgroup barrier ordering LDS accesses only (global loads stay in flight).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 template <int R, int NG, int PD, bool DYN>
@@ -651,7 +643,7 @@ __global__ __launch_bounds__(kC10Threads) void conv_rows10_kernel(
       if ((lane & (64 / N - 1)) == 0) red[g & 1][wave * N + idx] = part;
       // one barrier per group: red[g & 1] is next written two groups on,
       // after every wave has passed the barrier of the group in between
-      lds_barrier();
+      __syncthreads();
       double tot = 0.0;
       if (lane < N) {
         tot = red[g & 1][lane];
