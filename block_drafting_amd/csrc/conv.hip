@@ -566,11 +566,19 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
-template <int R, int NG, int PD, bool DYN>
+// Corrections of conv_rows10_kernel: none (static taps), one pair per row
+// from an [H, 2] projection, or one pair per group of gw >= 16 channels
+// whose split-K partial sums conv_mm_partial_kernel left in the rows of y.
+enum Conv10Mode { kStaticTaps = 0, kOnePair = 1, kSplitParts = 2 };
+constexpr int kSplitK = 4;  // K splits of the per-group corrections
+
+template <int R, int NG, int PD, int MODE>
 __global__ __launch_bounds__(kC10Threads) void conv_rows10_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ anchor,
     uint16_t* __restrict__ y, const float* __restrict__ k0, const float* __restrict__ k1,
-    const float* __restrict__ proj, int L, int H, int wgs_per_block) {
+    const float* __restrict__ proj, int L, int H, int wgs_per_block, int ncols, int gw) {
+  constexpr bool DYN = MODE == kOnePair;
+  constexpr bool PARTS = MODE == kSplitParts;
   constexpr int C = kC10;
   constexpr int N = 2 * R;       // correction dot products of a group
   constexpr int NB = PD + 1;     // row buffers: the group in use and PD in flight
@@ -591,10 +599,28 @@ __global__ __launch_bounds__(kC10Threads) void conv_rows10_kernel(
                      __builtin_amdgcn_readfirstlane((uint32_t)nr * row_bytes));
   };
   Raw10 xr[NB][R];
+  // Split-K partials: row r of y holds float [kSplitK][ncols]; the thread's
+  // channels belong to groups ga and ga + 1 at most (gw >= 16), whose four
+  // columns 2 ga .. 2 ga + 3 one 16-byte load per split brings.  The last
+  // group loads columns ncols - 4 .. ncols - 1 instead (psh = 2), so no load
+  // runs past the row's partials; it has no second group.
+  u32x4_t pa[PARTS ? NB : 1][PARTS ? R : 1][kSplitK];
+  const int ga = PARTS ? (C * tid) / gw : 0;
+  const int pbase = PARTS && ncols >= 4 ? min(2 * ga, ncols - 4) : 2 * ga;
+  const bool psh = 2 * ga != pbase;
   auto load_group = [&](int g) {
     const __amdgpu_buffer_rsrc_t rx = group_rsrc(x, g);
 #pragma unroll
     for (int r = 0; r < R; ++r) xr[g % NB][r].load(rx, cb + r * row_bytes);
+    if constexpr (PARTS) {
+      const __amdgpu_buffer_rsrc_t rp = group_rsrc(y, g);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int k = 0; k < kSplitK; ++k)
+          pa[g % NB][r][k] = __builtin_amdgcn_raw_buffer_load_b128(
+              rp, r * row_bytes + (uint32_t)(k * ncols + pbase) * 4, 0, 0);
+    }
   };
 #pragma unroll
   for (int g = 0; g < PD && g < NG; ++g) load_group(g);
@@ -652,24 +678,58 @@ __global__ __launch_bounds__(kC10Threads) void conv_rows10_kernel(
 #pragma unroll
       for (int i = 0; i < N; ++i) d[i] = readlane_f64(tot, i);
     }
+    // per-group corrections of the group's rows: the K splits in order
+    double dp[PARTS ? R : 1][2][2];
+    if constexpr (PARTS) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float sum[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sum[e] = __uint_as_float(pa[g % NB][r][0][e]);
+#pragma unroll
+          for (int k = 1; k < kSplitK; ++k) sum[e] += __uint_as_float(pa[g % NB][r][k][e]);
+        }
+        dp[r][0][0] = (double)(psh ? sum[2] : sum[0]);
+        dp[r][0][1] = (double)(psh ? sum[3] : sum[1]);
+        dp[r][1][0] = (double)sum[2];  // group ga + 1 (unused with psh)
+        dp[r][1][1] = (double)sum[3];
+      }
+      // every thread has read these rows' partials before any writes them
+      __syncthreads();
+    }
+    const int na = PARTS ? min(C, (ga + 1) * gw - C * tid) : C;  // channels in group ga
     const __amdgpu_buffer_rsrc_t ry = group_rsrc(y, g);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const double* prev = r == 0 ? pv : xv[r - 1];
       float f[C];
       uint64_t mid = 0;
+      auto tap = [&](int i, double& c0, double& c1) {
+        if constexpr (DYN) {
+          c0 = (double)ka[i] + d[2 * r];
+          c1 = (double)kb[i] + d[2 * r + 1];
+        } else if constexpr (PARTS) {
+          const int q = i < na ? 0 : 1;
+          c0 = (double)ka[i] + dp[PARTS ? r : 0][q][0];
+          c1 = (double)kb[i] + dp[PARTS ? r : 0][q][1];
+        } else {
+          c0 = (double)ka[i];
+          c1 = (double)kb[i];
+        }
+      };
 #pragma unroll
       for (int i = 0; i < C; ++i) {
-        const double c0 = DYN ? (double)ka[i] + d[2 * r] : (double)ka[i];
-        const double c1 = DYN ? (double)kb[i] + d[2 * r + 1] : (double)kb[i];
+        double c0, c1;
+        tap(i, c0, c1);
         f[i] = (float)(c0 * xv[r][i] + c1 * prev[i]);
         mid |= __builtin_amdgcn_ballot_w64(on_bf16_midpoint(f[i]));
       }
       if (mid) {
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-          const double c0 = DYN ? (double)ka[i] + d[2 * r] : (double)ka[i];
-          const double c1 = DYN ? (double)kb[i] + d[2 * r + 1] : (double)kb[i];
+          double c0, c1;
+          tap(i, c0, c1);
           f[i] = f64_to_f32_odd(c0 * xv[r][i] + c1 * prev[i]);
         }
       }
@@ -923,6 +983,188 @@ __global__ __launch_bounds__(MmCfg<KH>::kThreads) void conv_mm_kernel(
   }
 }
 
+// ---------------------------------------------------------------- split-K per-group corrections
+// For gw >= 16 channels per group the corrections of a batch can also be
+// computed as kSplitK partial products over quarters of K, each workgroup a
+// 128 x 160 tile of D over one quarter (0.72 MB of operands per workgroup
+// against 1.28 MB for a whole-K 64 x 64 tile), and the fp32 partials parked
+// in the rows of y: row m holds float [kSplitK][2G], which fits its 2H bytes
+// exactly when G = H / 16.  conv_rows10_kernel<..., kSplitParts> then sums
+// the quarters in order, mixes and overwrites each row.
+//
+// Eight waves: four bands of 32 rows x two halves of 80 columns, each a
+// 2 x 5 grid of 16 x 16 blocks on v_mfma_f32_16x16x32_bf16 (lane l: row or
+// column l % 16, k values 8 (l / 16) .. +7 of a 32-step; accumulator r:
+// row 4 (l / 16) + r, column l % 16).  K is staged through LDS in 128-wide
+// slices with two register staging sets, as in conv_mm_kernel.
+constexpr int kSkBM = 128;
+constexpr int kSkBN = 160;
+constexpr int kSkBK = 128;
+constexpr int kSkLd = kSkBK + 8;              // padded LDS row (bf16)
+constexpr int kSkThreads = 512;
+constexpr int kSkCpr = kSkBK / 8;             // 16-byte chunks per row slice
+constexpr int kSkRows = kSkThreads / kSkCpr;  // rows per loader pass
+constexpr int kSkPA = kSkBM / kSkRows;        // loads per thread: x
+constexpr int kSkPB = kSkBN / kSkRows;        // ... P^T
+constexpr int kSkLoads = kSkPA + kSkPB;
+static_assert(kSkBM % kSkRows == 0 && kSkBN % kSkRows == 0, "whole loader passes");
+
+__global__ __launch_bounds__(kSkThreads) void conv_mm_partial_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ pt, float* __restrict__ part,
+    int M, int N, int H, int mtiles, int ntiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t stage[2][(kSkBM + kSkBN) * kSkLd];
+  const int ntile = mtiles * ntiles;
+  const int split = blockIdx.x / ntile;
+  // tiles that share x rows run on one XCD: n fastest
+  const int tile = xcd_tile(blockIdx.x - split * ntile, ntile);
+  const int mt = tile / ntiles;
+  const int nt = tile - mt * ntiles;
+  const int m0 = mt * kSkBM;
+  const int n0 = nt * kSkBN;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rowsA = min(kSkBM, M - m0);
+  const int rowsB = min(kSkBN, N - n0);
+  const int kq = (H / 8 + kSplitK - 1) / kSplitK * 8;  // K per split (a multiple of 8)
+  const int kbeg = split * kq;
+  const int kend = min(H, kbeg + kq);
+  const int lrow = tid / kSkCpr;
+  const int lk = (tid % kSkCpr) * 8;
+  // Rows past the edge repeat the last row (their results are not stored).
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x + (size_t)m0 * H), (short)0, rowsA * H * 2, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(pt + (size_t)n0 * H), (short)0, rowsB * H * 2, kRsrcFlags);
+  int off[kSkLoads];
+#pragma unroll
+  for (int p = 0; p < kSkPA; ++p) off[p] = (min(lrow + p * kSkRows, rowsA - 1) * H + lk) * 2;
+#pragma unroll
+  for (int p = 0; p < kSkPB; ++p)
+    off[kSkPA + p] = (min(lrow + p * kSkRows, rowsB - 1) * H + lk) * 2;
+  const int nsl = max(1, (kend - kbeg + kSkBK - 1) / kSkBK);
+  // Slices past the end re-read the last slice (in range, never used);
+  // chunks past the split's end read as zero.
+  u32x4_t R0[kSkLoads], R1[kSkLoads];
+  auto gload = [&](u32x4_t(&R)[kSkLoads], int sl) {
+    const int k = kbeg + min(sl, nsl - 1) * kSkBK;
+    const bool in = k + lk < kend;
+    const u32x4_t z = {0, 0, 0, 0};
+#pragma unroll
+    for (int p = 0; p < kSkLoads; ++p) {
+      const u32x4_t v =
+          __builtin_amdgcn_raw_buffer_load_b128(p < kSkPA ? rsA : rsB, off[p] + k * 2, 0, 0);
+      R[p] = in ? v : z;
+    }
+  };
+  auto sstore = [&](const u32x4_t(&R)[kSkLoads], int buf) {
+#pragma unroll
+    for (int p = 0; p < kSkLoads; ++p) {
+      const int row = p < kSkPA ? lrow + p * kSkRows : kSkBM + lrow + (p - kSkPA) * kSkRows;
+      *reinterpret_cast<u32x4_t*>(&stage[buf][row * kSkLd + lk]) = R[p];
+    }
+  };
+  f32x4_t acc[2][5];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 5; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int wr = wave & 3;   // rows 32 wr ..
+  const int wc = wave >> 2;  // columns 80 wc ..
+  const int fa = (wr * 32 + (lane & 15)) * kSkLd + (lane >> 4) * 8;
+  const int fb = (kSkBM + wc * 80 + (lane & 15)) * kSkLd + (lane >> 4) * 8;
+  auto multiply = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < kSkBK / 32; ++ks) {
+      bf16x8_t a[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(&stage[buf][fa + i * 16 * kSkLd + ks * 32]);
+#pragma unroll
+      for (int j = 0; j < 5; ++j) {
+        const bf16x8_t bv =
+            *reinterpret_cast<const bf16x8_t*>(&stage[buf][fb + j * 16 * kSkLd + ks * 32]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bv, acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  gload(R0, 0);
+  gload(R1, 1);
+  sstore(R0, 0);
+  __syncthreads();
+  // Slice sl sits in LDS buffer sl & 1; the set that carried it reloads
+  // slice sl + 2, the other set (slice sl + 1) is stored after the MFMAs.
+  for (int sl = 0; sl < nsl; sl += 2) {
+    gload(R0, sl + 2);
+    multiply(0);
+    sstore(R1, 1);
+    __syncthreads();
+    if (sl + 1 >= nsl) break;
+    gload(R1, sl + 3);
+    multiply(1);
+    sstore(R0, 0);
+    __syncthreads();
+  }
+  const size_t pitch = (size_t)H / 2;  // floats per row of y
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 5; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wr * 32 + 16 * i + 4 * (lane >> 4) + r;
+        const int col = wc * 80 + 16 * j + (lane & 15);
+        if (row < rowsA && col < rowsB)
+          part[(size_t)(m0 + row) * pitch + (size_t)split * N + n0 + col] = acc[i][j][r];
+      }
+}
+
+// bf16 rows of H = 640 k <= 5120 channels: ten channels per thread.
+bool conv10_fits(int H) { return H % 640 == 0 && H <= kC10 * kC10Threads; }
+
+// Launches conv_rows10_kernel in the given mode; false (nothing launched)
+// when the grid would not fit.  Positions per workgroup from a sweep at
+// H = 5120 (kernel trace, us): 2048 rows with a projection, 2 x 4 rows (one
+// ahead): 11.0 (8 rows of the eight-channel kernel below: 16.1; 2 x 4 rows
+// with the next two ahead: 12.0; 4 x 2: 12.1); 4096 static rows, 8 single
+// rows, two ahead: 14.1 (18.0); 512 static rows, 2 rows: 4.9 (5.3).  Fewer
+// positions when that leaves under 256 workgroups.
+bool launch_rows10(int mode, const uint16_t* xq, const uint16_t* aq, uint16_t* yq, const float* k0,
+                   const float* k1, const float* proj, int ncols, int gw, int B, int L, int H,
+                   hipStream_t s) {
+  const long long rows = (long long)B * L;
+  const long long units = rows / 256;
+  int rn = 1;
+  while (rn < 8 && rn * 2 <= L && rn * 2 <= units) rn *= 2;
+  const int wpb = (L + rn - 1) / rn;
+  const long long wgs = (long long)B * wpb;
+  if (wgs > 0x7fffffffLL) return false;
+  const dim3 grid((unsigned)wgs), blk((unsigned)(H / kC10));
+#define DFLASH2_CONV10(RR, NN, PP, MM)                                                         \
+  hipLaunchKernelGGL((conv_rows10_kernel<RR, NN, PP, MM>), grid, blk, 0, s, xq, aq, yq, k0, k1, \
+                     proj, L, H, wpb, ncols, gw)
+  if (mode == kOnePair) {
+    if (rn == 8) DFLASH2_CONV10(2, 4, 1, kOnePair);
+    else if (rn == 4) DFLASH2_CONV10(2, 2, 1, kOnePair);
+    else if (rn == 2) DFLASH2_CONV10(2, 1, 1, kOnePair);
+    else DFLASH2_CONV10(1, 1, 1, kOnePair);
+  } else if (mode == kSplitParts) {
+    if (rn == 8) DFLASH2_CONV10(2, 4, 1, kSplitParts);
+    else if (rn == 4) DFLASH2_CONV10(2, 2, 1, kSplitParts);
+    else if (rn == 2) DFLASH2_CONV10(2, 1, 1, kSplitParts);
+    else DFLASH2_CONV10(1, 1, 1, kSplitParts);
+  } else {
+    if (rn == 8) DFLASH2_CONV10(1, 8, 2, kStaticTaps);
+    else if (rn == 4) DFLASH2_CONV10(2, 2, 1, kStaticTaps);
+    else if (rn == 2) DFLASH2_CONV10(2, 1, 1, kStaticTaps);
+    else DFLASH2_CONV10(1, 1, 1, kStaticTaps);
+  }
+#undef DFLASH2_CONV10
+  return true;
+}
+
 template <typename T>
 hipError_t launch_typed(const void* x, const void* anchor_h, void* y, const float* k0,
                         const float* k1, const float* proj, int groups, int B, int L, int H,
@@ -932,42 +1174,11 @@ hipError_t launch_typed(const void* x, const void* anchor_h, void* y, const floa
   T* yp = static_cast<T*>(y);
   const long long rows = (long long)B * L;
   if constexpr (sizeof(T) == 2) {
-    // bf16 rows of H = 640 k <= 5120 channels: ten channels per thread.
-    // Positions per workgroup from a sweep at H = 5120 (kernel trace, us):
-    // 2048 rows with a projection, 2 x 4 rows (one ahead): 11.0 (8 rows of
-    // the eight-channel kernel below: 16.1; 2 x 4 rows with the next two
-    // ahead: 12.0; 4 x 2: 12.1); 4096 static rows, 8 single rows, two
-    // ahead: 14.1 (18.0); 512 static rows, 2 rows: 4.9 (5.3).  Fewer
-    // positions when that leaves under 256 workgroups.
-    if ((!proj || groups == 1) && H % 640 == 0 && H <= 10 * kC10Threads) {
-      long long units = rows / 256;
-      int rn = 1;
-      while (rn < 8 && rn * 2 <= L && rn * 2 <= units) rn *= 2;
-      const int wpb = (L + rn - 1) / rn;
-      const long long wgs = (long long)B * wpb;
-      if (wgs <= 0x7fffffffLL) {
-        const dim3 grid((unsigned)wgs), blk((unsigned)(H / kC10));
-        const uint16_t* xq = static_cast<const uint16_t*>(x);
-        const uint16_t* aq = static_cast<const uint16_t*>(anchor_h);
-        uint16_t* yq = static_cast<uint16_t*>(y);
-#define DFLASH2_CONV10(RR, NN, PP, DD)                                                         \
-  hipLaunchKernelGGL((conv_rows10_kernel<RR, NN, PP, DD>), grid, blk, 0, s, xq, aq, yq, k0, k1, \
-                     proj, L, H, wpb)
-        if (proj) {
-          if (rn == 8) DFLASH2_CONV10(2, 4, 1, true);
-          else if (rn == 4) DFLASH2_CONV10(2, 2, 1, true);
-          else if (rn == 2) DFLASH2_CONV10(2, 1, 1, true);
-          else DFLASH2_CONV10(1, 1, 1, true);
-        } else {
-          if (rn == 8) DFLASH2_CONV10(1, 8, 2, false);
-          else if (rn == 4) DFLASH2_CONV10(2, 2, 1, false);
-          else if (rn == 2) DFLASH2_CONV10(2, 1, 1, false);
-          else DFLASH2_CONV10(1, 1, 1, false);
-        }
-#undef DFLASH2_CONV10
-        return hipGetLastError();
-      }
-    }
+    if ((!proj || groups == 1) && conv10_fits(H) &&
+        launch_rows10(proj ? kOnePair : kStaticTaps, static_cast<const uint16_t*>(x),
+                      static_cast<const uint16_t*>(anchor_h), static_cast<uint16_t*>(y), k0, k1,
+                      proj, 0, 0, B, L, H, s))
+      return hipGetLastError();
   }
   // Rows of a block per workgroup, measured at H = 5120 (20 launches back to
   // back): the corrections' workgroups take 8 rows (15.9 us per application
@@ -1047,6 +1258,20 @@ hipError_t launch_twotap_conv_mm(const void* x, const void* anchor_h, void* y, c
   const uint16_t* ab = static_cast<const uint16_t*>(anchor_h);
   uint16_t* yb = static_cast<uint16_t*>(y);
   const uint16_t* pb = static_cast<const uint16_t*>(projT);
+  // Split-K (groups of gw >= 16 channels, whose partials fit in y's rows;
+  // rows of H = 640 k <= 5120) when its partial tiles fill half the CUs.
+  const int gw = H / groups;
+  if (gw >= 16 && conv10_fits(H)) {
+    const int smt = (M + kSkBM - 1) / kSkBM;
+    const int snt = (N + kSkBN - 1) / kSkBN;
+    const long long swgs = (long long)smt * snt * kSplitK;
+    if (swgs >= 128 && swgs <= 0x7fffffffLL) {
+      hipLaunchKernelGGL(conv_mm_partial_kernel, dim3((unsigned)swgs), dim3(kSkThreads), 0, s, xb,
+                         pb, reinterpret_cast<float*>(yb), M, N, H, smt, snt);
+      if (launch_rows10(kSplitParts, xb, ab, yb, k0, k1, nullptr, N, gw, B, L, H, s))
+        return hipGetLastError();
+    }
+  }
   // One round of tiles over the CUs: two wave groups per tile (a tile's K
   // loop is latency-bound, the second group halves it; 135 KB of LDS, one
   // tile per CU).  More tiles than CUs: one group, two tiles per CU.

@@ -123,7 +123,10 @@ int dflash2_twotap_conv(const void* x, const void* anchor_h, void* y,
  * DFLASH2_BF16 (DFLASH2_F32 returns DFLASH2_EUNSUPPORTED).  Other arguments
  * as for dflash2_twotap_conv; y must not overlap x, anchor_h or projT.
  * D is accumulated in fp32 from the exact bf16 products; the mix is
- * evaluated in fp64 from it and rounded once to bf16.
+ * evaluated in fp64 from it and rounded once to bf16.  With groups of at
+ * least 16 channels the call may compute D in four K quarters whose fp32
+ * partial sums it keeps in y's rows until it writes them (y is then scratch
+ * as well as output; it must not overlap the inputs in any case).
  */
 int dflash2_twotap_conv_mm(const void* x, const void* anchor_h, void* y,
                            const float* k0, const float* k1, const void* projT, int groups,

@@ -182,7 +182,13 @@ def conv_mm_tolerance(xo, ao, P, groups, want):
                                             (2, 16, 5120, 320, True), (37, 1, 128, 8, False),
                                             (5, 7, 2560, 160, True), (1, 3, 256, 256, True),
                                             (4, 8, 1024, 1, True), (9, 8, 520, 65, False),
-                                            (1100, 8, 1024, 64, True)])   # > 256 tiles
+                                            (1100, 8, 1024, 64, True),    # > 256 tiles
+                                            # split-K partials parked in y, then the
+                                            # ten-channel mix: ragged M tile (915 rows),
+                                            # 32-channel groups with a ragged N tile,
+                                            # 256-thread rows
+                                            (61, 15, 5120, 320, True), (267, 15, 1280, 40, False),
+                                            (63, 31, 2560, 160, True)])
 def test_conv_mm_parity(B, L, H, G, anchor):
     g = np.random.default_rng(B * 1000 + G)
     x = WL.to_bf16_bits(g.standard_normal((B, L, H)).astype(np.float32))
@@ -204,8 +210,8 @@ def test_conv_mm_parity(B, L, H, G, anchor):
     assert (got != want).mean() <= 1e-3, (got != want).mean()
 
 
-def test_conv_mm_zero_map_is_the_static_conv_bit_exact():
-    B, L, H, G = 3, 8, 640, 40
+@pytest.mark.parametrize("B,L,H,G", [(3, 8, 640, 40), (61, 15, 5120, 320)])
+def test_conv_mm_zero_map_is_the_static_conv_bit_exact(B, L, H, G):
     x, a, k0, k1, _ = _conv_case(B, L, H, "bf16", False, 1, seed=31)
     pt = np.zeros((2 * G, H), np.uint16)
     args = (to_dev(x, "bf16"), torch.from_numpy(k0).to(DEV), torch.from_numpy(k1).to(DEV))
