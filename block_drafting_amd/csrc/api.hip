@@ -72,7 +72,11 @@ DFLASH2_API int dflash2_twotap_conv(const void* x, const void* anchor_h, void* y
   }
   const size_t es = esize(dtype);
   const size_t xbytes = (size_t)B * L * H * es;
-  if (overlap(x, xbytes, y, xbytes)) return DFLASH2_EINVAL;
+  // workgroups read the parameters while others already write y
+  if (overlap(x, xbytes, y, xbytes) || overlap(k0, (size_t)H * 4, y, xbytes) ||
+      overlap(k1, (size_t)H * 4, y, xbytes) ||
+      (proj && overlap(proj, (size_t)H * 2 * groups * 4, y, xbytes)))
+    return DFLASH2_EINVAL;
   if (anchor_h && overlap(anchor_h, (size_t)B * H * es, y, xbytes)) return DFLASH2_EINVAL;
   return status_of(launch_twotap_conv(x, anchor_h, y, k0, k1, proj, proj ? groups : 1, B, L, H,
                                       dtype, as_stream(stream)));
@@ -95,7 +99,8 @@ DFLASH2_API int dflash2_twotap_conv_mm(const void* x, const void* anchor_h, void
   const size_t xbytes = (size_t)B * L * H * 2;
   if (overlap(x, xbytes, y, xbytes) ||
       (anchor_h && overlap(anchor_h, (size_t)B * H * 2, y, xbytes)) ||
-      overlap(projT, (size_t)2 * groups * H * 2, y, xbytes))
+      overlap(projT, (size_t)2 * groups * H * 2, y, xbytes) ||
+      overlap(k0, (size_t)H * 4, y, xbytes) || overlap(k1, (size_t)H * 4, y, xbytes))
     return DFLASH2_EINVAL;
   return status_of(launch_twotap_conv_mm(x, anchor_h, y, k0, k1, projT, groups, B, L, H,
                                          as_stream(stream)));

@@ -94,7 +94,7 @@ const char* dflash2_strerror(int status);
  *              token's representation; zeros when anchor_h is NULL)
  *   D[b,t,g,j] = sum_c x[b,t,c] * proj[c, 2g+j]   (0 when proj is NULL)
  *   g(c) = c / (H / groups)
- * x, y     [B, L, H] of dtype; y must not overlap x (or anchor_h).
+ * x, y     [B, L, H] of dtype; y must not overlap x, anchor_h, k0, k1 or proj.
  * anchor_h [B, H] of dtype, or NULL.
  * k0, k1   [H] fp32 base taps.
  * proj     [H, 2*groups] fp32 correction map, or NULL for static taps.
@@ -121,7 +121,7 @@ int dflash2_twotap_conv(const void* x, const void* anchor_h, void* y,
  * and y is dflash2_twotap_conv's formula with these D.
  * projT [2*groups, H] bf16; groups >= 1 divides H; dtype must be
  * DFLASH2_BF16 (DFLASH2_F32 returns DFLASH2_EUNSUPPORTED).  Other arguments
- * as for dflash2_twotap_conv; y must not overlap x, anchor_h or projT.
+ * as for dflash2_twotap_conv; y must not overlap x, anchor_h, k0, k1 or projT.
  * D is accumulated in fp32 from the exact bf16 products; the mix is
  * evaluated in fp64 from it and rounded once to bf16.  With groups of at
  * least 16 channels the call may compute D in four K quarters whose fp32

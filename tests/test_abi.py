@@ -65,6 +65,9 @@ def test_conv_validation():
     assert call(dt=7) == EINVAL
     assert call(y=P) == EINVAL                # y aliases x
     assert call(y=P + 64) == EINVAL           # partial overlap
+    assert call(y=Q, k0=Q + 0x100) == EINVAL  # y overlaps a tap vector
+    assert call(y=Q, k1=Q + 0x7f0) == EINVAL
+    assert call(y=Q, pr=Q + 0x10, g=1) == EINVAL   # ... or the projection
     assert call(x=P + 4) == EINVAL            # misaligned
     assert call(pr=P + 0xa0000, g=3) == EINVAL   # groups must divide H
     assert call(pr=P + 0xa0000, g=0) == EINVAL
@@ -91,6 +94,8 @@ def test_conv_mm_validation():
     assert call(g=0) == EINVAL
     assert call(y=P + 0xa0000) == EINVAL      # y overlaps the map
     assert call(y=P) == EINVAL                # y aliases x
+    assert call(y=Q, k0=Q + 0x100) == EINVAL  # y overlaps a tap vector (it holds partial sums)
+    assert call(y=Q, k1=Q + 0x7f0) == EINVAL
     assert call(H=12) == EINVAL
     assert call(H=(1 << 21) + 64, g=1) == EUNSUP
 
