@@ -220,11 +220,14 @@ size_t dflash2_logits_topk_workspace(int M, int H, int V, int K, int dtype, int 
  *   top_val / top_idx [M, 16]: the 16 largest logits of row m, value
  *   descending, equal values by lower token id (as dflash2_topk16).
  * h [M, H] and W [V, H] of dtype (W may be packed, DFLASH2_BF16_PACKED),
- * 16-byte aligned.  Runs dflash2_lmhead_logits_tilemax then
- * dflash2_topk16_tilemax, the tile maxima in the workspace.  logits may be
- * NULL (then the workspace holds them, see the query above).  The workspace
- * is required (256-byte aligned) whenever M > 0.  K must be 16.  Errors as
- * for the two calls it runs; nothing is launched unless every check passes.
+ * 16-byte aligned.  With a logits buffer it runs
+ * dflash2_lmhead_logits_tilemax then dflash2_topk16_tilemax, the tile maxima
+ * in the workspace.  logits may be NULL: with fp32 operands the workspace
+ * then holds the logits (same two calls); with bf16 operands the call runs
+ * the candidate form below and no [M, V] logits are written.  Either way
+ * top_val / top_idx are the same bit for bit.  The workspace is required
+ * (256-byte aligned) whenever M > 0.  K must be 16.  Errors as for the calls
+ * it runs; nothing is launched unless every check passes.
  */
 int dflash2_logits_topk(const void* h, const void* W, float* logits,
                         float* top_val, int32_t* top_idx,
