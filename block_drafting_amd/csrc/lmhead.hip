@@ -452,32 +452,57 @@ __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
   }
 }
 
-// fp32 operands: thread per vocabulary row, 8 output rows per block row.
+// fp32 operands: a workgroup owns 64 vocabulary rows x 8 output rows.  The
+// W rows are staged through LDS in 64-wide K chunks with coalesced 16-byte
+// loads (a row per thread would read 64 rows per load instruction); thread
+// (n, q) then accumulates outputs (2q, 2q + 1) of vocabulary row n, one
+// fmaf per k in k order, so every output is the same sequential fp32 sum
+// as a plain loop.
+constexpr int kF32N = 64;   // vocabulary rows per workgroup
+constexpr int kF32M = 8;    // output rows per workgroup
+constexpr int kF32K = 64;   // K chunk
 __global__ __launch_bounds__(256) void lmhead_f32_kernel(const float* __restrict__ A,
                                                          const float* __restrict__ W,
                                                          float* __restrict__ C, int M, int N,
                                                          int K) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  const int m0 = blockIdx.y * 8;
-  if (n >= N) return;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const float* w = W + (size_t)n * K;
-  for (int k = 0; k < K; k += 4) {
-    const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(w + k);
+  __shared__ float ws[kF32N][kF32K + 1];  // padded: lanes of a wave read 64 rows, 64 banks
+  __shared__ float as[kF32M][kF32K];
+  const int n0 = blockIdx.x * kF32N;
+  const int m0 = blockIdx.y * kF32M;
+  const int tid = threadIdx.x;
+  const int nl = tid & 63;   // vocabulary row of this thread
+  const int q = tid >> 6;    // output rows 2q, 2q + 1
+  const int rows = min(kF32N, N - n0);
+  float acc0 = 0.f, acc1 = 0.f;
+  for (int kc = 0; kc < K; kc += kF32K) {
+    const int kn = min(kF32K, K - kc);  // a multiple of 4 (K % 8 == 0)
+    // 64 rows x kn floats: 16 threads per row, 16 bytes each, four passes
 #pragma unroll
-    for (int mm = 0; mm < 8; ++mm) {
-      if (m0 + mm < M) {
-        const f32x4_t av = *reinterpret_cast<const f32x4_t*>(A + (size_t)(m0 + mm) * K + k);
-        acc[mm] = fmaf(av[0], wv[0], acc[mm]);
-        acc[mm] = fmaf(av[1], wv[1], acc[mm]);
-        acc[mm] = fmaf(av[2], wv[2], acc[mm]);
-        acc[mm] = fmaf(av[3], wv[3], acc[mm]);
+    for (int pass = 0; pass < 4; ++pass) {
+      const int r = (tid >> 4) + 16 * pass;
+      const int c = (tid & 15) * 4;
+      if (r < rows && c < kn) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(W + (size_t)(n0 + r) * K + kc + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ws[r][c + i] = v[i];
       }
     }
+    for (int e = tid; e < kF32M * kF32K; e += 256) {
+      const int mm = e / kF32K, c = e - mm * kF32K;
+      if (m0 + mm < M && c < kn) as[mm][c] = A[(size_t)(m0 + mm) * K + kc + c];
+    }
+    __syncthreads();
+    for (int k = 0; k < kn; ++k) {
+      const float w = ws[nl][k];
+      acc0 = fmaf(as[2 * q][k], w, acc0);
+      acc1 = fmaf(as[2 * q + 1][k], w, acc1);
+    }
+    __syncthreads();
   }
-#pragma unroll
-  for (int mm = 0; mm < 8; ++mm)
-    if (m0 + mm < M) C[(size_t)(m0 + mm) * N + n] = acc[mm];
+  if (nl < rows) {
+    if (m0 + 2 * q < M) C[(size_t)(m0 + 2 * q) * N + n0 + nl] = acc0;
+    if (m0 + 2 * q + 1 < M) C[(size_t)(m0 + 2 * q + 1) * N + n0 + nl] = acc1;
+  }
 }
 
 // Row maxima of every kTileMaxCols-column tile of finished logits (the
@@ -557,7 +582,7 @@ hipError_t launch_lmhead(const void* h, const void* W, float* logits, float* tma
       return launch_bf16<256, 256, 64, 2, 4, true, false>(hb, Wb, logits, tmax, M, H, V, {}, s);
     return launch_bf16<256, 256, 64, 2, 4, false, false>(hb, Wb, logits, tmax, M, H, V, {}, s);
   }
-  const dim3 grid((unsigned)((V + 255) / 256), (unsigned)((M + 7) / 8));
+  const dim3 grid((unsigned)((V + kF32N - 1) / kF32N), (unsigned)((M + kF32M - 1) / kF32M));
   hipLaunchKernelGGL(lmhead_f32_kernel, grid, dim3(256), 0, s, static_cast<const float*>(h),
                      static_cast<const float*>(W), logits, M, V, H);
   hipError_t e = hipGetLastError();
