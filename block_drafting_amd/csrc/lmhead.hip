@@ -81,7 +81,8 @@ struct CandOut {
 template <int BM, int BN, int BK, int WM, int WN, bool KTAIL, bool PACKED, bool CAND>
 __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bw, float* __restrict__ C,
-    float* __restrict__ tmax, int M, int N, int K, int mtiles, int ntiles, CandOut cand) {
+    float* __restrict__ tmax, int M, int N, int K, int mtiles, int ntiles, int nt0,
+    CandOut cand) {
   using Cfg = GemmCfg<BM, BN, BK, WM, WN>;
   constexpr int kT = Cfg::kThreads;
   constexpr int kLdk = Cfg::kLdk;
@@ -96,9 +97,10 @@ __global__ __launch_bounds__(WM* WN * 64) void lmhead_bf16_kernel(
                 "epilogue LDS fits in the stages");
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg::kStage];
 
-  const int tile = xcd_tile(blockIdx.x, mtiles * ntiles);
+  // this launch's tiles: N tiles nt0, nt0 + 1, ... of all ntiles, M fastest
+  const int tile = xcd_tile(blockIdx.x, (int)gridDim.x);
   const int mt = tile % mtiles;
-  const int nt = tile / mtiles;
+  const int nt = nt0 + tile / mtiles;
   const int m0 = mt * BM;
   const int n0 = nt * BN;
   const int tid = threadIdx.x;
@@ -523,20 +525,41 @@ __global__ __launch_bounds__(256) void tilemax_kernel(const float* __restrict__ 
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool PACKED, bool CAND>
-hipError_t launch_bf16(const uint16_t* h, const uint16_t* W, float* z, float* tmax, int M, int H,
-                       int V, CandOut cand, hipStream_t s) {
+hipError_t launch_bf16_part(const uint16_t* h, const uint16_t* W, float* z, float* tmax, int M,
+                            int H, int V, int nt0, int ntl, CandOut cand, hipStream_t s) {
   static_assert(BN == kTileMaxCols, "tile maxima follow the N tiles");
   const int mt = (M + BM - 1) / BM;
   const int nt = (V + BN - 1) / BN;
   if (H % BK == 0)
     hipLaunchKernelGGL((lmhead_bf16_kernel<BM, BN, BK, WM, WN, false, PACKED, CAND>),
-                       dim3((unsigned)(mt * nt)), dim3(WM * WN * 64), 0, s, h, W, z, tmax, M, V,
-                       H, mt, nt, cand);
+                       dim3((unsigned)(mt * ntl)), dim3(WM * WN * 64), 0, s, h, W, z, tmax, M, V,
+                       H, mt, nt, nt0, cand);
   else
     hipLaunchKernelGGL((lmhead_bf16_kernel<BM, BN, BK, WM, WN, true, PACKED, CAND>),
-                       dim3((unsigned)(mt * nt)), dim3(WM * WN * 64), 0, s, h, W, z, tmax, M, V,
-                       H, mt, nt, cand);
+                       dim3((unsigned)(mt * ntl)), dim3(WM * WN * 64), 0, s, h, W, z, tmax, M, V,
+                       H, mt, nt, nt0, cand);
   return hipGetLastError();
+}
+
+// All N tiles of the product.  One M tile of 256 rows (129 <= M <= 256) whose
+// last round of N tiles fills at most half the CUs runs that round as
+// 128-row tiles in a second launch: the same columns on twice the
+// workgroups, each reading half of h (M = 256, K = 2560, V = 151936: 594
+// tiles, 82 in the third round).
+template <bool PACKED, bool CAND>
+hipError_t launch_bf16(const uint16_t* h, const uint16_t* W, float* z, float* tmax, int M, int H,
+                       int V, CandOut cand, hipStream_t s) {
+  constexpr int kCus = 256;
+  const int nt = (V + 255) / 256;
+  const int tail = nt % kCus;
+  if (M > 128 && M <= 256 && nt > kCus && tail <= kCus / 2) {
+    hipError_t e = launch_bf16_part<256, 256, 64, 2, 4, PACKED, CAND>(h, W, z, tmax, M, H, V, 0,
+                                                                      nt - tail, cand, s);
+    if (e != hipSuccess || tail == 0) return e;
+    return launch_bf16_part<128, 256, 64, 1, 8, PACKED, CAND>(h, W, z, tmax, M, H, V, nt - tail,
+                                                              tail, cand, s);
+  }
+  return launch_bf16_part<256, 256, 64, 2, 4, PACKED, CAND>(h, W, z, tmax, M, H, V, 0, nt, cand, s);
 }
 
 // Group maxima back to "unfilled" before a candidate launch.
@@ -579,8 +602,8 @@ hipError_t launch_lmhead(const void* h, const void* W, float* logits, float* tma
     const uint16_t* hb = static_cast<const uint16_t*>(h);
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
     if (dtype == 2)
-      return launch_bf16<256, 256, 64, 2, 4, true, false>(hb, Wb, logits, tmax, M, H, V, {}, s);
-    return launch_bf16<256, 256, 64, 2, 4, false, false>(hb, Wb, logits, tmax, M, H, V, {}, s);
+      return launch_bf16<true, false>(hb, Wb, logits, tmax, M, H, V, {}, s);
+    return launch_bf16<false, false>(hb, Wb, logits, tmax, M, H, V, {}, s);
   }
   const dim3 grid((unsigned)((V + kF32N - 1) / kF32N), (unsigned)((M + kF32M - 1) / kF32M));
   hipLaunchKernelGGL(lmhead_f32_kernel, grid, dim3(256), 0, s, static_cast<const float*>(h),
@@ -607,8 +630,8 @@ hipError_t launch_lmhead_cand(const void* h, const void* W, float* logits, float
   const uint16_t* hb = static_cast<const uint16_t*>(h);
   const uint16_t* Wb = static_cast<const uint16_t*>(W);
   if (dtype == 2)
-    return launch_bf16<256, 256, 64, 2, 4, true, true>(hb, Wb, logits, tmax, M, H, V, cand, s);
-  return launch_bf16<256, 256, 64, 2, 4, false, true>(hb, Wb, logits, tmax, M, H, V, cand, s);
+    return launch_bf16<true, true>(hb, Wb, logits, tmax, M, H, V, cand, s);
+  return launch_bf16<false, true>(hb, Wb, logits, tmax, M, H, V, cand, s);
 }
 
 size_t lmhead_pack_bytes(int V, int H) {

@@ -58,6 +58,8 @@ def _oracle_rows(fused, z, rows):
     (37, 64, 1000, True),          # 4 N tiles: no bound ever, every tile stored
     (513, 520, 4099, False),       # 17 N tiles: one beyond the 16 groups
     (1, 64, 70001, True),          # one row, odd V (scalar reads)
+    (256, 192, 151936, True),      # the last round of N tiles as 128-row tiles
+    (200, 136, 70001, False),      # the same with a K tail and row-major W
 ])
 def test_fused_topk_random(M, H, V, packed):
     g = torch.Generator(device=DEV).manual_seed(M * 7 + V)

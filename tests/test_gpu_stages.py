@@ -240,6 +240,34 @@ def test_lmhead_parity(dt, M, H, V):
     assert np.all(err <= 1e-3 * np.maximum(np.abs(want), 1.0)), err.max()
 
 
+# One M tile of 129..256 rows whose last round of N tiles fills at most half
+# the CUs runs that round as 128-row tiles in a second launch (594 tiles,
+# 82 in the third round, at M = 256, V = 151936; one tail tile at
+# V = 257 x 256 - 5; a K tail at H = 136).  Every output is the same
+# sequence of MFMA accumulations whatever the tile's height, so the rows
+# equal, bit for bit, those of a product of more than 256 rows (one
+# launch of 256-row tiles); the tile maxima are those rows' maxima.
+@pytest.mark.parametrize("M,H,V,packed", [(256, 192, 151936, True), (129, 64, 257 * 256 - 5, False),
+                                          (200, 136, 70001, True)])
+def test_lmhead_tail_launch_bit_exact(M, H, V, packed):
+    g = torch.Generator(device=DEV).manual_seed(M + V)
+    h_big = torch.randn((300, H), generator=g, device=DEV).to(torch.bfloat16)
+    W = (torch.randn((V, H), generator=g, device=DEV) / H ** 0.5).to(torch.bfloat16)
+    Wx = bd.lmhead_pack(W) if packed else W
+    z_big = bd.lmhead_logits(h_big, Wx)                      # 300 rows: no tail launch
+    z, tmax = bd.lmhead_logits_tilemax(h_big[:M].contiguous(), Wx)
+    torch.cuda.synchronize()
+    assert torch.equal(z.view(torch.int32), z_big[:M].view(torch.int32))
+    nt = (V + 255) // 256
+    zp = torch.full((M, nt * 256), -float("inf"), device=DEV)
+    zp[:, :V] = z
+    assert torch.equal(tmax, zp.view(M, nt, 256).amax(dim=2))
+    rows = [0, 127, 128, M - 1]
+    want = O.lm_logits(O.as_f64(to_host_bits(h_big[rows]), "bf16"), to_host_bits(W), "bf16")
+    err = np.abs(z[rows].cpu().numpy().astype(np.float64) - want)
+    assert np.all(err <= 1e-3 * np.maximum(np.abs(want), 1.0)), err.max()
+
+
 def test_lmhead_one_hot_and_dyadic_bit_exact():
     M, H, V = 70, 256, 1100
     g = np.random.default_rng(3)
