@@ -12,8 +12,9 @@
 // followed by rounding to 8 bits equals a single correct rounding, so each
 // output is the exactly rounded value of the formula (up to the 2^-53
 // relative error of the fp64 evaluation).  Chained convs therefore do not
-// drift apart from the definition through double rounding.  The kernel is
-// HBM-bound, so the fp64 rate is not the limit.
+// drift apart from the definition through double rounding.  The
+// ten-channel kernel takes the nearest fp32 value instead and falls back to
+// round-to-odd only where that value is a bf16 midpoint (same result).
 #include "common.hpp"
 
 namespace dflash2 {
