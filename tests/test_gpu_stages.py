@@ -220,6 +220,38 @@ def test_conv_mm_zero_map_is_the_static_conv_bit_exact(B, L, H, G):
     assert torch.equal(y_mm.view(torch.int16), y_st.view(torch.int16))
 
 
+def test_conv_mm_split_graph_replays():
+    """The split-K per-group conv (partials parked in y, then the mix)
+    captured as a HIP graph: every replay, with eager calls on other inputs
+    into the same output in between, gives the eager result."""
+    B, L, H, G = 64, 16, 5120, 320          # 1024 rows: the split path
+    g = torch.Generator(device=DEV).manual_seed(9)
+    x = torch.randn((B, L, H), generator=g, device=DEV).to(torch.bfloat16)
+    x2 = torch.randn((B, L, H), generator=g, device=DEV).to(torch.bfloat16)
+    a = torch.randn((B, H), generator=g, device=DEV).to(torch.bfloat16)
+    k0 = torch.randn(H, generator=g, device=DEV) * 0.7
+    k1 = torch.randn(H, generator=g, device=DEV) * 0.7
+    pt = (torch.randn((2 * G, H), generator=g, device=DEV) * (0.01 / H) ** 0.5).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    want = bd.twotap_conv_mm(x, k0, k1, pt, a).clone()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        bd.twotap_conv_mm(x, k0, k1, pt, a, out=y)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            bd.twotap_conv_mm(x, k0, k1, pt, a, out=y)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        bd.twotap_conv_mm(x2, k0, k1, pt, a, out=y)   # other inputs, same output buffer
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), want.view(torch.int16))
+
+
 def test_conv_empty_batch_is_noop():
     x = torch.empty((0, 8, 64), dtype=torch.bfloat16, device=DEV)
     k = torch.zeros(64, device=DEV)
