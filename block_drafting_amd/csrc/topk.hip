@@ -290,7 +290,7 @@ __global__ __launch_bounds__(64) void topk16_merge_kernel(const uint64_t* __rest
 // sort.  Exact: the result is the full scan's, bit for bit.
 constexpr int kPruneBatch = 16;
 constexpr int kMaxChunk = 16;      // tile maxima per lane per pass (1024 tiles)
-constexpr int kCandCap = 1024;     // LDS candidate keys before a merge
+constexpr int kCandCap = 512;      // LDS candidate keys before a merge (a tile adds at most 256)
 
 // Merge n keys of cand into the list (this lane's slot key), 48 per sort.
 // Not inlined: the call sites sit inside unrolled loops and are rarely taken.
@@ -334,10 +334,14 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
                                                            const uint2* __restrict__ slots) {
   static_assert(!CAND || kCandSlots == 4, "two slots per 16-byte load, lanes 0 and 1");
   constexpr int kList = 64 * kMaxChunk;
+  // LDS kept small (9.5 KB) so that many rows are in flight per CU.  A list
+  // entry is tile * 8 + (count + 1), the count (CAND) of kCandDense = -1 ..
+  // kCandSlots; the tile maxima's orders are only read for the first 64
+  // entries (the tighter bound below), so later ones go to spare slots.
+  static_assert(kCandDense == -1 && kCandSlots <= 6, "a count fits 3 bits");
   __shared__ uint64_t cand[kCandCap + 64];  // + one spare slot per lane
   __shared__ int list[kList + 64];
-  __shared__ uint32_t lord[kList + 64];
-  __shared__ int lcnt[CAND ? kList + 64 : 1];
+  __shared__ uint32_t lord[64 + 64];
   const int m = blockIdx.x;
   const int lane = threadIdx.x;
   const float* tm = tmax + (size_t)m * nt;
@@ -381,9 +385,8 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
       const uint64_t sel = __ballot(s);
       const int below = lanes_below(sel);
       const int at = below + (s ? nsel : kList + lane - below);
-      list[at] = c0 + k * 64 + lane;
-      lord[at] = o[k];
-      if constexpr (CAND) lcnt[at] = cn[k];
+      list[at] = (c0 + k * 64 + lane) * 8 + (CAND ? cn[k] + 1 : 0);
+      lord[at < 64 ? at : 64 + lane] = o[k];
       nsel += __popcll(sel);
     }
     // Tighter bound: the 16th largest of the selected tiles' maxima (the 16
@@ -392,14 +395,12 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
     if (nt >= 16 && nt <= kList && nsel > 16 && nsel <= 64) {
       const int t = lane < nsel ? list[lane] : 0;
       const uint32_t ot = lane < nsel ? lord[lane] : 0u;
-      const int ct = CAND && lane < nsel ? lcnt[CAND ? lane : 0] : 0;
       const uint64_t srt2 = wave_sort_desc(((uint64_t)ot << 32) | (uint32_t)(~lane));
       tau = (uint32_t)(readlane64(srt2, 15) >> 32);
       const bool s = lane < nsel && ot >= tau;
       const uint64_t sel = __ballot(s);
       __builtin_amdgcn_wave_barrier();
       list[s ? lanes_below(sel) : kList + lane] = t;
-      if constexpr (CAND) lcnt[s ? lanes_below(sel) : kList + lane] = ct;
       __builtin_amdgcn_wave_barrier();
       nsel = __popcll(sel);
     }
@@ -410,10 +411,11 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
       int ncn[kPruneBatch];  // CAND: slots used of a sparse tile, -1 for a stored tile
 #pragma unroll
       for (int k = 0; k < kPruneBatch; ++k) {
-        const int tl = k < ns ? list[b0 + k] : 0;  // b0 + k < kList + 64
+        const int le = k < ns ? list[b0 + k] : 0;  // b0 + k < kList + 64
+        const int tl = le >> 3;
         cbase[k] = tl * kTileMaxCols + lane * 4;
         const int c = cbase[k];
-        ncn[k] = CAND ? __builtin_amdgcn_readfirstlane(k < ns ? lcnt[CAND ? b0 + k : 0] : 0)
+        ncn[k] = CAND ? __builtin_amdgcn_readfirstlane(k < ns ? (le & 7) - 1 : 0)
                       : kCandDense;
         if (CAND && ncn[k] != kCandDense) {
           // slots 2 lane, 2 lane + 1 as (v, col, v, col); lanes past 1 re-read
