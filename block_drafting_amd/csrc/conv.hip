@@ -691,6 +691,11 @@ __global__ __launch_bounds__(kC10Threads) void conv_rows10_kernel(
 #pragma unroll
           for (int k = 1; k < kSplitK; ++k) sum[e] += __uint_as_float(pa[g % NB][r][k][e]);
         }
+        // The sums, and so the loads they read, must be done before the
+        // barrier below: the barrier waits for LDS operations only, and left
+        // to itself the compiler finishes some rows' sums after it, with
+        // their loads still in flight when other waves store into these rows.
+        asm volatile("" ::"v"(sum[0]), "v"(sum[1]), "v"(sum[2]), "v"(sum[3]));
         dp[r][0][0] = (double)(psh ? sum[2] : sum[0]);
         dp[r][0][1] = (double)(psh ? sum[3] : sum[1]);
         dp[r][1][0] = (double)sum[2];  // group ga + 1 (unused with psh)
