@@ -105,6 +105,10 @@ def parse_args(argv=None):
                          "one JSON line per size, then exit")
     ap.add_argument("--sweep-sizes", default=None,
                     help="comma-separated rows (topk) or blocks (pair) for --sweep")
+    ap.add_argument("--gemm-vs-vendor", type=int, default=None, metavar="M",
+                    help="time the LM-head GEMM (logits form and candidate form, W packed) "
+                         "beside the vendor GEMM (torch.mm: hipBLASLt) at M rows of the 27b-head "
+                         "shape (K = 5120, N = 151936), one JSON line, then exit")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--separate", action="store_true",
                     help="pair scores, walk and verification as separate launches, and for a "
@@ -211,6 +215,40 @@ def peaks():
     print(json.dumps({"peak": "hbm_copy", "bytes_read": n, "bytes_written": n,
                       "ms": round(ms, 4), "gbs": round(2 * n / (ms * 1e-3) / 1e9, 1)}),
           flush=True)
+
+
+def gemm_vs_vendor(M: int):
+    """The LM-head GEMM beside the vendor GEMM at M rows of the 27b-head
+    shape (K = 5120, N = 151936, bf16 operands of the benchmark's
+    statistics): ours writing the fp32 logits (dflash2_lmhead_logits, W
+    packed) and in the candidate form (dflash2_logits_topk without a logits
+    buffer: the group-maxima reset, the GEMM and the top-16 merge), and
+    torch.mm (hipBLASLt) with bf16 and with fp32 output.  Medians of 10
+    event-timed calls after 0.5 s of calls each."""
+    import torch
+    import block_drafting_amd as bd
+    H, V = 5120, 151936
+    g = torch.Generator(device="cuda").manual_seed(3)
+    h = torch.randn((M, H), generator=g, device="cuda").to(torch.bfloat16)
+    W = (torch.randn((V, H), generator=g, device="cuda") / H ** 0.5).to(torch.bfloat16)
+    Wp = bd.lmhead_pack(W)
+    Wt = W.t()
+    z = torch.empty((M, V), device="cuda")
+    o16 = torch.empty((M, V), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(bd.logits_topk_workspace(M, H, V, torch.bfloat16, False), dtype=torch.uint8,
+                     device="cuda")
+    tv = torch.empty((M, 16), device="cuda")
+    ti = torch.empty((M, 16), dtype=torch.int32, device="cuda")
+    fns = {"lmhead_logits": lambda: bd.lmhead_logits(h, Wp, z),
+           "logits_topk_candidates": lambda: bd.logits_topk(h, Wp, top_val=tv, top_idx=ti,
+                                                            workspace=ws),
+           "torch_mm_bf16_out": lambda: torch.mm(h, Wt, out=o16),
+           "torch_mm_f32_out": lambda: torch.mm(h, Wt, out_dtype=torch.float32)}
+    rec = {"gemm_vs_vendor": {"M": M, "K": H, "N": V}}
+    for name, fn in fns.items():
+        us = _time_events(fn, 10, settle_s=0.5) * 1e3
+        rec[name] = {"us": round(us, 1), "tflops": round(2 * M * H * V / (us * 1e-6) / 1e12, 1)}
+    print(json.dumps(rec), flush=True)
 
 
 def sweep(kind: str, sizes):
@@ -402,10 +440,12 @@ def main(argv=None):
     if a.copy_calib:
         copy_calibration()
         return 0
-    if a.peaks or a.sweep:
+    if a.peaks or a.sweep or a.gemm_vs_vendor:
         sys.path.insert(0, ROOT)
         if a.peaks:
             peaks()
+        elif a.gemm_vs_vendor:
+            gemm_vs_vendor(a.gemm_vs_vendor)
         else:
             default = "512,4096,16384,65536" if a.sweep == "topk" else "64,1024,8192,32768"
             sweep(a.sweep, [int(v) for v in (a.sweep_sizes or default).split(",")])
