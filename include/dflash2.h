@@ -58,7 +58,7 @@ extern "C" {
 typedef enum {
   DFLASH2_OK = 0,
   DFLASH2_EINVAL = -1,        /* bad pointer, size, shape or aliasing */
-  DFLASH2_EUNSUPPORTED = -2,  /* valid request this build does not implement */
+  DFLASH2_EUNSUPPORTED = -2,  /* valid request the library does not implement */
   DFLASH2_EHIP = -3,          /* a HIP launch or runtime call failed */
   DFLASH2_EWORKSPACE = -4,    /* workspace missing or smaller than queried */
   DFLASH2_ESCRATCH = -5       /* larger than the fixed scratch of an allocation-free call */
