@@ -8,8 +8,10 @@ One step = one pass of the whole hot path over one batch:
 each stage a call into libdflash2 on the current HIP stream.  Scores, walk
 and greedy verification run as one fused launch; a sampled walk runs scores
 and walk as one launch, then a rejection verification that computes the
-target rows' log-sum-exp itself, only for the rows its test reaches
-(--separate: scores, walk and verification as separate launches, and for a
+target rows' log-sum-exp itself: every block's first two rows summed up
+front, all blocks at once, further rows only where its test reaches them
+(--rejection lazy: every row only where the test reaches it; --separate:
+scores, walk and verification as separate launches, and for a
 sampled walk an lse pass over every target row before the verification).  Inputs are
 seeded synthetic tensors already resident in HBM when timing starts.
 
@@ -120,6 +122,10 @@ def parse_args(argv=None):
     ap.add_argument("--keep-logits", action="store_true",
                     help="write all [M, V] logits (default for bf16: the GEMM's candidate form, "
                          "which writes only the tiles and values the top-16 may need)")
+    ap.add_argument("--rejection", choices=["staged", "lazy"], default="staged",
+                    help="sampled walks: the lazy verification with every block's first two "
+                         "target rows summed up front (staged, default) or each row read "
+                         "only when the accept test reaches it (lazy); the same results")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replays of the captured step")
     return ap.parse_args(argv)
@@ -551,14 +557,18 @@ def main(argv=None):
     if w.gate:
         stages.append(("gate", lambda: bd.context_gate(final_y.view(M, H), Wg, buf.gate)))
     if fused and sampled:
-        # scores and the sampling walk in one launch, then the lazy verification
+        # scores and the sampling walk in one launch, then the staged (or lazy) verification
         stages += [
             ("pair_sample", lambda: bd.pair_sample(tv3, ti3, anchor, U, Vf, u_path, w.temperature,
                                                    gate, None, None, buf.path_slot,
                                                    buf.path_tok, buf.q, mode=smode)),
-            ("verify", lambda: bd.verify_rejection_lazy(buf.path_slot, buf.path_tok, buf.q, ti3,
-                                                        z_target, w.temperature, u_acc, u_res,
-                                                        buf.accept_len, buf.next_tok))]
+            ("verify", (lambda: bd.verify_rejection_staged(
+                buf.path_slot, buf.path_tok, buf.q, ti3, z_target, w.temperature, u_acc, u_res,
+                buf.accept_len, buf.next_tok, workspace=buf.staged))
+             if a.rejection == "staged" else
+             (lambda: bd.verify_rejection_lazy(buf.path_slot, buf.path_tok, buf.q, ti3,
+                                               z_target, w.temperature, u_acc, u_res,
+                                               buf.accept_len, buf.next_tok)))]
     elif fused:
         # scores, walk and verification in one launch; the scores stay on chip
         stages.append(("pair_select_verify", lambda: bd.pair_select_verify(
@@ -791,7 +801,7 @@ def main(argv=None):
                    "launch": "hip-graph" if graphK is not None else "eager",
                    "pair_walk": "fused" if fused else "separate", "lm_head_w": w_layout,
                    "lm_head_out": form,
-                   "rejection": ("two-pass" if two_pass else "lazy") if sampled else None},
+                   "rejection": ("two-pass" if two_pass else a.rejection) if sampled else None},
         "tokens_per_s": round(M / (ms_step * 1e-3), 1),
         "accepted_tokens_per_s": round(float(acc.sum()) / (ms_step * 1e-3), 1),
         "mean_accept_len": round(float(acc.mean()), 3),

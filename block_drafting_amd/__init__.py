@@ -22,7 +22,9 @@ The five stages (names as in the C ABI):
 At T > 0: path_sample (sampled walk), target_lse + verify_rejection (lossless
 speculative-sampling verification against target logits), or
 verify_rejection_lazy (the same rule, each target row's log-sum-exp computed
-only for the rows the accept test reaches).
+only for the rows the accept test reaches) or verify_rejection_staged (the
+lazy rule with every block's first rows summed up front, all blocks at once;
+the same results bit for bit).
 One launch for several stages: pair_select_verify (scores, either walk and
 greedy verification) and pair_sample (scores and the sampling walk).
 run_step chains a whole step on preallocated StepBuffers.
@@ -46,7 +48,7 @@ __all__ = [
     "topk16_workspace", "logits_topk", "logits_topk_workspace", "logits_topk_noalloc",
     "lmhead_candidates", "topk16_candidates",
     "context_gate", "pair_score",
-    "path_select", "pair_select_verify", "pair_sample", "path_sample", "SAMPLE_MODES", "target_lse", "verify_rejection", "verify_rejection_lazy", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
+    "path_select", "pair_select_verify", "pair_sample", "path_sample", "SAMPLE_MODES", "target_lse", "verify_rejection", "verify_rejection_lazy", "verify_rejection_staged", "verify_rejection_staged_workspace", "STAGED_ROWS", "verify_greedy", "StepBuffers", "run_step", "TOPK", "PATH_MODES",
 ]
 
 TOPK = 16
@@ -100,6 +102,9 @@ _SIGS = {
                                   _P, _P, _P], _I),
     "dflash2_verify_rejection_lazy": ([_P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _I,
                                        _P, _P, _P], _I),
+    "dflash2_verify_rejection_staged_workspace": ([_I, _I, _I, _I], ctypes.c_size_t),
+    "dflash2_verify_rejection_staged": ([_P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _I,
+                                         _I, _P, ctypes.c_size_t, _P, _P, _P], _I),
 }
 
 
@@ -782,6 +787,50 @@ def verify_rejection_lazy(path_slot: torch.Tensor, path_tok: torch.Tensor, q: to
     return accept_len, next_tok
 
 
+STAGED_ROWS = 2   # target rows per block the staged verification sums up front
+
+
+def verify_rejection_staged_workspace(B: int, L: int, V: int, rows: int = STAGED_ROWS) -> int:
+    return int(lib().dflash2_verify_rejection_staged_workspace(B, L, V, rows))
+
+
+def verify_rejection_staged(path_slot: torch.Tensor, path_tok: torch.Tensor, q: torch.Tensor,
+                            top_idx: torch.Tensor, z: torch.Tensor, temperature: float,
+                            u_acc: torch.Tensor, u_res: torch.Tensor, accept_len=None,
+                            next_tok=None, rows: Optional[int] = None,
+                            workspace: Optional[torch.Tensor] = None):
+    """verify_rejection_lazy with the first `rows` target rows of every block
+    (default min(2, L + 1)) summed up front, all blocks at once; the same
+    (accept_len [B], next_tok [B]) bit for bit."""
+    _rank(path_tok, 2, "path_tok", torch.int32)
+    B, L = path_tok.shape
+    V = z.shape[-1]
+    rows = min(STAGED_ROWS, L + 1) if rows is None else int(rows)
+    _shape(path_slot, (B, L), "path_slot", torch.int32)
+    _shape(q, (B, L, TOPK), "q", torch.float32)
+    _shape(top_idx, (B, L, TOPK), "top_idx", torch.int32)
+    _shape(z, (B, L + 1, V), "z", torch.float32)
+    _shape(u_acc, (B, L), "u_acc", torch.float32)
+    _shape(u_res, (B,), "u_res", torch.float32)
+    _opt(accept_len, (B,), "accept_len", torch.int32)
+    _opt(next_tok, (B,), "next_tok", torch.int32)
+    dev = path_tok.device
+    if accept_len is None:
+        accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if next_tok is None:
+        next_tok = torch.empty((B,), dtype=torch.int32, device=dev)
+    need = verify_rejection_staged_workspace(B, L, V, rows) if 1 <= rows <= L + 1 else 0
+    ws = _workspace(need, dev, workspace)
+    _dev(path_slot, path_tok, q, top_idx, z, u_acc, u_res, accept_len, next_tok,
+         *([ws] if ws is not None else []))
+    _check("dflash2_verify_rejection_staged", lib().dflash2_verify_rejection_staged(
+        _ptr(path_slot), _ptr(path_tok), _ptr(q), _ptr(top_idx), _ptr(z), float(temperature),
+        _ptr(u_acc), _ptr(u_res), B, L, V, rows, _ptr(ws),
+        ws.numel() * ws.element_size() if ws is not None else 0, _ptr(accept_len),
+        _ptr(next_tok), _stream(dev)))
+    return accept_len, next_tok
+
+
 # ---------------------------------------------------------------- whole step
 class StepBuffers:
     """Preallocated device buffers for one step shape (B, L, H, V) so repeated
@@ -811,6 +860,8 @@ class StepBuffers:
                      if gate_rank else None)
         self.q = torch.empty((B, L, TOPK), dtype=torch.float32, **kw) if sample else None
         self.lse = torch.empty((B, L + 1), dtype=torch.float32, **kw) if sample else None
+        sw = verify_rejection_staged_workspace(B, L, V, min(STAGED_ROWS, L + 1)) if sample else 0
+        self.staged = torch.empty(max(sw, 1), dtype=torch.uint8, **kw) if sample else None
 
 
 def run_step(buf: StepBuffers, x: torch.Tensor, convs, W, U: torch.Tensor,
@@ -829,8 +880,9 @@ def run_step(buf: StepBuffers, x: torch.Tensor, convs, W, U: torch.Tensor,
     predecessor's row) or "sample-path" (the whole path from exp(score / T))
     at `temperature` with the uniforms `u_path`) and verification: greedy against `target` argmax ids,
     or, for a sampled walk given target logits `z_target` [B, L+1, V], the
-    lossless rejection rule with uniforms `u_acc`, `u_res` (each target row's
-    log-sum-exp computed only where the accept test reaches it).  A walk that is
+    lossless rejection rule with uniforms `u_acc`, `u_res` (the first two target
+    rows of every block summed up front, further rows only where the accept
+    test reaches them).  A walk that is
     not sampled, with targets given, runs scores, walk and verification in
     one launch (pair_select_verify); a sampled walk runs scores and walk in
     one launch (pair_sample).  Every call is enqueued on the current
@@ -867,8 +919,9 @@ def run_step(buf: StepBuffers, x: torch.Tensor, convs, W, U: torch.Tensor,
         pair_sample(tv, ti, anchor_tok, U, Vf, u_path, temperature, gate, buf.S0, buf.S,
                     buf.path_slot, buf.path_tok, buf.q, mode=smode)
         if z_target is not None:
-            verify_rejection_lazy(buf.path_slot, buf.path_tok, buf.q, ti, z_target, temperature,
-                                  u_acc, u_res, buf.accept_len, buf.next_tok)
+            verify_rejection_staged(buf.path_slot, buf.path_tok, buf.q, ti, z_target,
+                                    temperature, u_acc, u_res, buf.accept_len, buf.next_tok,
+                                    workspace=buf.staged)
         return buf
     pair_score(tv, ti, anchor_tok, U, Vf, buf.S0, buf.S, gate=gate)
     path_select(buf.S0, buf.S, ti, buf.path_slot, buf.path_tok, buf.path_score, mode=walk)

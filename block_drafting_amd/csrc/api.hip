@@ -566,6 +566,48 @@ DFLASH2_API int dflash2_verify_rejection_lazy(const int32_t* path_slot, const in
                                                 as_stream(stream)));
 }
 
+DFLASH2_API size_t dflash2_verify_rejection_staged_workspace(int B, int L, int V, int rows) {
+  if (B < 0 || L < 1 || L > DFLASH2_MAX_L || V < kTopK || rows < 1 || rows > L + 1) return 0;
+  return verify_rejection_staged_bytes(B, V, rows);
+}
+
+DFLASH2_API int dflash2_verify_rejection_staged(const int32_t* path_slot, const int32_t* path_tok,
+                                                const float* q, const int32_t* top_idx,
+                                                const float* z, float temperature,
+                                                const float* u_acc, const float* u_res, int B,
+                                                int L, int V, int rows, void* workspace,
+                                                size_t workspace_bytes, int32_t* accept_len,
+                                                int32_t* next_tok, void* stream) {
+  if (B < 0 || L < 1 || L > DFLASH2_MAX_L || V < kTopK || !valid_temperature(temperature))
+    return DFLASH2_EINVAL;
+  if (rows < 1 || rows > L + 1) return DFLASH2_EINVAL;
+  if ((long long)B * (L + 1) * V > (1LL << 40)) return DFLASH2_EINVAL;
+  if (verify_rejection_lazy_lds(V) > 65536) return DFLASH2_EUNSUPPORTED;  // tiles in LDS
+  if (B == 0) return DFLASH2_OK;
+  if (!path_slot || !path_tok || !q || !top_idx || !z || !u_acc || !u_res || !accept_len ||
+      !next_tok || !workspace)
+    return DFLASH2_EINVAL;
+  const size_t need = verify_rejection_staged_bytes(B, V, rows);
+  if (workspace_bytes < need) return DFLASH2_EINVAL;
+  const void* all[] = {path_slot, path_tok, q, top_idx, z, u_acc, u_res, accept_len, next_tok,
+                       workspace};
+  for (const void* p : all)
+    if (!aligned4(p)) return DFLASH2_EINVAL;
+  const size_t pb = (size_t)B * L * 4, tib = (size_t)B * L * kTopK * 4, ob = (size_t)B * 4;
+  const void* ins[] = {path_slot, path_tok, q, top_idx, z, u_acc, u_res};
+  const size_t insz[] = {pb, pb, tib, tib, (size_t)B * (L + 1) * V * 4, pb, ob};
+  for (int j = 0; j < 7; ++j)
+    if (overlap(accept_len, ob, ins[j], insz[j]) || overlap(next_tok, ob, ins[j], insz[j]) ||
+        overlap(workspace, need, ins[j], insz[j]))
+      return DFLASH2_EINVAL;
+  if (overlap(accept_len, ob, next_tok, ob) || overlap(workspace, need, accept_len, ob) ||
+      overlap(workspace, need, next_tok, ob))
+    return DFLASH2_EINVAL;
+  return status_of(launch_verify_rejection_staged(
+      path_slot, path_tok, q, top_idx, z, temperature, u_acc, u_res, B, L, V, rows,
+      static_cast<float*>(workspace), accept_len, next_tok, as_stream(stream)));
+}
+
 DFLASH2_API int dflash2_verify_greedy(const int32_t* path_tok, const int32_t* target, int B, int L,
                                       int32_t* accept_len, int32_t* next_tok, void* stream) {
   if (B < 0 || L < 1) return DFLASH2_EINVAL;

@@ -146,6 +146,15 @@ hipError_t launch_target_lse(const float* z, int R, int V, float temperature, fl
                              hipStream_t s);
 
 size_t verify_rejection_lds(int V);
+// The staged rows' records ([B, rows] of them) and the two-launch form of the
+// lazy verification that fills them first.
+size_t verify_rejection_staged_bytes(int B, int V, int rows);
+hipError_t launch_verify_rejection_staged(const int32_t* path_slot, const int32_t* path_tok,
+                                          const float* q, const int32_t* top_idx, const float* z,
+                                          float temperature, const float* u_acc,
+                                          const float* u_res, int B, int L, int V, int rows,
+                                          float* staged, int32_t* accept_len, int32_t* next_tok,
+                                          hipStream_t s);
 size_t verify_rejection_lazy_lds(int V);
 hipError_t launch_verify_rejection_lazy(const int32_t* path_slot, const int32_t* path_tok,
                                         const float* q, const int32_t* top_idx, const float* z,

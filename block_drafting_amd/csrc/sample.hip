@@ -435,6 +435,127 @@ __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_kernel(
 }
 
 
+// One batch of a target row: kTileBatch consecutive tiles from tile t0,
+// values scaled by s2 (base 2), tokens past V as -inf.  Every lane ends with
+// the batch maximum bm (the tiles' common reference, 0 in its place when
+// the batch is empty), the tiles' sums acc[k] of 2^(value - reference) and
+// their total bs.  Every load is issued before the first use (index
+// clamped into the row): a use or a per-lane branch between two loads makes
+// each wait for the one before.  The lazy verification's row pass and the
+// staged rows share this code, so their sums are the same bit for bit.
+template <bool VEC>
+__device__ __forceinline__ void tile_batch_load(const float* __restrict__ zr, int V, int t0,
+                                                int lane, f32x4_t (&raw)[kTileBatch]) {
+#pragma unroll
+  for (int k = 0; k < kTileBatch; ++k) {
+    const int v0 = (t0 + k) * kTile + lane * 4;
+    if constexpr (VEC) {
+      raw[k] = *reinterpret_cast<const f32x4_t*>(zr + min(v0, V - 4));  // V % 4 == 0
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw[k][i] = zr[min(v0 + i, V - 1)];
+    }
+  }
+}
+
+__device__ __forceinline__ void tile_batch_sum(const f32x4_t (&raw)[kTileBatch], int V, int t0,
+                                               int lane, float s2, float& bm,
+                                               float (&acc)[kTileBatch], float& bs) {
+  constexpr float kNeg = -__builtin_inff();
+  float zv[kTileBatch][4];
+  bm = kNeg;
+#pragma unroll
+  for (int k = 0; k < kTileBatch; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      zv[k][i] = (t0 + k) * kTile + lane * 4 + i < V ? raw[k][i] * s2 : kNeg;
+      bm = fmaxf(bm, zv[k][i]);
+    }
+  bm = wave_max(bm);
+  const float ref = bm == kNeg ? 0.f : bm;  // an empty batch sums exp2(-inf) = 0
+#pragma unroll
+  for (int k = 0; k < kTileBatch; ++k) {
+    acc[k] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[k] += exp2f(zv[k][i] - ref);
+  }
+  wave_sum_n<kTileBatch>(acc);
+  bs = 0.f;
+#pragma unroll
+  for (int k = 0; k < kTileBatch; ++k) bs += acc[k];
+}
+
+// One batch of a target row: kTileBatch consecutive tiles from tile t0,
+// values scaled by s2 (base 2), tokens past V as -inf.  Every lane ends with
+// the batch maximum bm (the tiles' common reference, 0 in its place when
+// the batch is empty), the tiles' sums acc[k] of 2^(value - reference) and
+// their total bs.  Every load is issued before the first use (index
+// clamped into the row): a use or a per-lane branch between two loads makes
+// each wait for the one before.  The lazy verification's row pass and the
+// staged rows share this code, so their sums are the same bit for bit.
+template <bool VEC>
+__device__ __forceinline__ void tile_batch(const float* __restrict__ zr, int V, int t0, int lane,
+                                           float s2, float& bm, float (&acc)[kTileBatch],
+                                           float& bs) {
+  f32x4_t raw[kTileBatch];
+  tile_batch_load<VEC>(zr, V, t0, lane, raw);
+  tile_batch_sum(raw, V, t0, lane, s2, bm, acc, bs);
+}
+
+// Per (block, row) record of a staged row: the tiles' batch maxima [ntiles],
+// the tiles' sums [ntiles], then the batches' maxima [nbatch] and totals
+// [nbatch].
+__host__ __device__ constexpr size_t staged_row_floats(int ntiles) {
+  return 2 * (size_t)ntiles + 2 * (size_t)((ntiles + kTileBatch - 1) / kTileBatch);
+}
+
+// The first `rows` target rows of every block, all at once: one wave per
+// kStageBatches consecutive batches of kTileBatch tiles, (block, row,
+// batches) in that order, writing the batches' record entries.  A wave
+// issues the loads of all its batches before summing the first.  No wave
+// depends on another.  One batch per wave (8 KB of the row) is the fastest:
+// with two or four, fewer waves are resident and each one's exponentials
+// and reductions run longer after its loads land.
+constexpr int kStageBatches = 1;
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void stage_rows_kernel(const float* __restrict__ z, float s2,
+                                                         int L, int V, int rows, int nwaves,
+                                                         float* __restrict__ staged) {
+  const int lane = threadIdx.x & 63;
+  const int g = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (g >= nwaves) return;  // whole waves
+  const int ntiles = (V + kTile - 1) / kTile;
+  const int nbatch = (ntiles + kTileBatch - 1) / kTileBatch;
+  const int per_row = (nbatch + kStageBatches - 1) / kStageBatches;  // waves per row
+  const int j0 = (g % per_row) * kStageBatches;
+  const int bt = g / per_row;
+  const int t = bt % rows, b = bt / rows;
+  const float* zr = z + ((size_t)b * (L + 1) + t) * V;
+  f32x4_t raw[kStageBatches][kTileBatch];
+#pragma unroll
+  for (int i = 0; i < kStageBatches; ++i)  // a batch past the row reads (clamped) and is dropped
+    tile_batch_load<VEC>(zr, V, min(j0 + i, nbatch - 1) * kTileBatch, lane, raw[i]);
+  float* rec = staged + (size_t)bt * staged_row_floats(ntiles);
+#pragma unroll
+  for (int i = 0; i < kStageBatches; ++i) {
+    const int j = j0 + i;
+    if (j >= nbatch) break;  // uniform
+    float bm, bs, acc[kTileBatch];
+    tile_batch_sum(raw[i], V, j * kTileBatch, lane, s2, bm, acc, bs);
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < kTileBatch; ++k)
+        if (j * kTileBatch + k < ntiles) {
+          rec[j * kTileBatch + k] = bm;
+          rec[ntiles + j * kTileBatch + k] = acc[k];
+        }
+      rec[2 * ntiles + j] = bm;
+      rec[2 * ntiles + nbatch + j] = bs;
+    }
+  }
+}
+
 // Rejection verification that computes the normaliser of a target row only
 // when the accept test reaches it: row t is read once, as 256-token tiles
 // whose (reference maximum, sum of 2^(z * s2 - reference)) stay in LDS; the
@@ -442,13 +563,13 @@ __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_kernel(
 // walk stops, the tile masses of the draw, so the stopping row is not read
 // again.  A block that stops at position n reads n + 1 rows instead of all
 // L + 1.  The accept rule and the draw are those of verify_rejection_kernel.
-template <bool VEC>
+template <bool VEC, bool STAGED>
 __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_lazy_kernel(
     const int32_t* __restrict__ path_slot, const int32_t* __restrict__ path_tok,
     const float* __restrict__ q, const int32_t* __restrict__ top_idx,
     const float* __restrict__ z, float s2, const float* __restrict__ u_acc,
     const float* __restrict__ u_res, int L, int V, int32_t* __restrict__ accept_len,
-    int32_t* __restrict__ next_tok) {
+    int32_t* __restrict__ next_tok, const float* __restrict__ staged, int rows) {
   extern __shared__ float tiles[];  // [ntiles] reference maxima, then [ntiles] sums
   __shared__ int32_t s_x[kMaxWalk];
   __shared__ float s_thr[kMaxWalk];
@@ -485,55 +606,29 @@ __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_lazy_kernel(
     if (tid == 0 && x >= 0) zx = zr[x];  // in flight during the pass
     // wave w takes kTileBatch consecutive tiles at a time (8 KB runs of the
     // row: 14% faster per row than tiles strided across the waves); each
-    // batch shares one reference maximum
+    // batch shares one reference maximum.  A staged row's batches were summed
+    // ahead (stage_rows_kernel, the same arithmetic); its waves merge their
+    // batches' (maximum, total) in the same order.
     float Mw = kNeg, Sw = 0.f;
-    for (int t0 = wave * kTileBatch; t0 < ntiles; t0 += kVerWaves * kTileBatch) {
-      // every load is issued (index clamped into the row, tokens past V
-      // masked to -inf): per-lane branches around the loads cost more
-      // All kTileBatch loads go out before the first use: a use between
-      // two loads (or a branch per load) makes each wait for the last.
-      f32x4_t raw[kTileBatch];
+    if (STAGED && t < rows) {
+      const float* rec = staged + ((size_t)b * rows + t) * staged_row_floats(ntiles);
+      const int nbatch = (ntiles + kTileBatch - 1) / kTileBatch;
+      for (int j = wave; j < nbatch; j += kVerWaves)
+        lse_merge(Mw, Sw, rec[2 * ntiles + j], rec[2 * ntiles + nbatch + j]);
+    } else {
+      for (int t0 = wave * kTileBatch; t0 < ntiles; t0 += kVerWaves * kTileBatch) {
+        float bm, bs, acc[kTileBatch];
+        tile_batch<VEC>(zr, V, t0, lane, s2, bm, acc, bs);
+        if (lane == 0) {
 #pragma unroll
-      for (int k = 0; k < kTileBatch; ++k) {
-        const int v0 = (t0 + k) * kTile + lane * 4;
-        if constexpr (VEC) {
-          raw[k] = *reinterpret_cast<const f32x4_t*>(zr + min(v0, V - 4));  // V % 4 == 0
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) raw[k][i] = zr[min(v0 + i, V - 1)];
+          for (int k = 0; k < kTileBatch; ++k)
+            if (t0 + k < ntiles) {
+              tref[t0 + k] = bm;
+              tsum[t0 + k] = acc[k];
+            }
         }
+        lse_merge(Mw, Sw, bm, bs);
       }
-      float zv[kTileBatch][4];
-      float bm = kNeg;
-#pragma unroll
-      for (int k = 0; k < kTileBatch; ++k)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          zv[k][i] = (t0 + k) * kTile + lane * 4 + i < V ? raw[k][i] * s2 : kNeg;
-          bm = fmaxf(bm, zv[k][i]);
-        }
-      bm = wave_max(bm);
-      const float ref = bm == kNeg ? 0.f : bm;  // an empty batch sums exp2(-inf) = 0
-      float acc[kTileBatch];
-#pragma unroll
-      for (int k = 0; k < kTileBatch; ++k) {
-        acc[k] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[k] += exp2f(zv[k][i] - ref);
-      }
-      wave_sum_n<kTileBatch>(acc);
-      float bs = 0.f;
-#pragma unroll
-      for (int k = 0; k < kTileBatch; ++k) bs += acc[k];
-      if (lane == 0) {
-#pragma unroll
-        for (int k = 0; k < kTileBatch; ++k)
-          if (t0 + k < ntiles) {
-            tref[t0 + k] = bm;
-            tsum[t0 + k] = acc[k];
-          }
-      }
-      lse_merge(Mw, Sw, bm, bs);
     }
     if (lane == 0) {
       s_wm[wave] = Mw;
@@ -559,9 +654,16 @@ __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_lazy_kernel(
     cand_id[tid] = resid ? top_idx[(brow + n) * kTopK + tid] : -1;
     cand_q[tid] = resid ? q[(brow + n) * kTopK + tid] : 0.f;
   }
-  // tile masses of p: sum * 2^(reference - l2)
-  for (int i = tid; i < ntiles; i += 64 * kVerWaves)
-    tsum[i] = tref[i] == kNeg ? 0.f : tsum[i] * exp2f(tref[i] - l2);
+  // tile masses of p: sum * 2^(reference - l2) (a staged row's tiles from
+  // its record, read by the thread that uses them)
+  const float* srec = STAGED && n < rows
+                          ? staged + ((size_t)b * rows + n) * staged_row_floats(ntiles)
+                          : nullptr;
+  for (int i = tid; i < ntiles; i += 64 * kVerWaves) {
+    const float r = srec ? srec[i] : tref[i];
+    const float sm = srec ? srec[ntiles + i] : tsum[i];
+    tsum[i] = r == kNeg ? 0.f : sm * exp2f(r - l2);
+  }
   __syncthreads();
   if (wave == 0)
     draw_token(tsum, ntiles, z + (zrow + n) * V, V, s2, l2, resid, cand_id, cand_q, u_res[b],
@@ -588,21 +690,63 @@ hipError_t launch_target_lse(const float* z, int R, int V, float temperature, fl
   return hipGetLastError();
 }
 
+template <bool STAGED>
+static void launch_lazy(const int32_t* path_slot, const int32_t* path_tok, const float* q,
+                        const int32_t* top_idx, const float* z, float temperature,
+                        const float* u_acc, const float* u_res, int B, int L, int V,
+                        int32_t* accept_len, int32_t* next_tok, const float* staged, int rows,
+                        hipStream_t s) {
+  // 16-byte loads when the rows are 16-byte aligned (z is, and V % 4 == 0)
+  if ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0)
+    hipLaunchKernelGGL((verify_rejection_lazy_kernel<true, STAGED>), dim3((unsigned)B),
+                       dim3(64 * kVerWaves), verify_rejection_lazy_lds(V), s, path_slot, path_tok,
+                       q, top_idx, z, kLog2e / temperature, u_acc, u_res, L, V, accept_len,
+                       next_tok, staged, rows);
+  else
+    hipLaunchKernelGGL((verify_rejection_lazy_kernel<false, STAGED>), dim3((unsigned)B),
+                       dim3(64 * kVerWaves), verify_rejection_lazy_lds(V), s, path_slot, path_tok,
+                       q, top_idx, z, kLog2e / temperature, u_acc, u_res, L, V, accept_len,
+                       next_tok, staged, rows);
+}
+
 hipError_t launch_verify_rejection_lazy(const int32_t* path_slot, const int32_t* path_tok,
                                         const float* q, const int32_t* top_idx, const float* z,
                                         float temperature, const float* u_acc, const float* u_res,
                                         int B, int L, int V, int32_t* accept_len,
                                         int32_t* next_tok, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  // 16-byte loads when the rows are 16-byte aligned (z is, and V % 4 == 0)
+  launch_lazy<false>(path_slot, path_tok, q, top_idx, z, temperature, u_acc, u_res, B, L, V,
+                     accept_len, next_tok, nullptr, 0, s);
+  return hipGetLastError();
+}
+
+size_t verify_rejection_staged_bytes(int B, int V, int rows) {
+  const int ntiles = (V + kTile - 1) / kTile;
+  return (size_t)B * (size_t)rows * staged_row_floats(ntiles) * sizeof(float);
+}
+
+hipError_t launch_verify_rejection_staged(const int32_t* path_slot, const int32_t* path_tok,
+                                          const float* q, const int32_t* top_idx, const float* z,
+                                          float temperature, const float* u_acc,
+                                          const float* u_res, int B, int L, int V, int rows,
+                                          float* staged, int32_t* accept_len, int32_t* next_tok,
+                                          hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const int ntiles = (V + kTile - 1) / kTile;
+  const int nbatch = (ntiles + kTileBatch - 1) / kTileBatch;
+  const int per_row = (nbatch + kStageBatches - 1) / kStageBatches;
+  const long long nwaves = (long long)B * rows * per_row;  // < 2^31: checked by the caller
+  const unsigned grid = (unsigned)((nwaves + 3) / 4);
   if ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0)
-    hipLaunchKernelGGL(verify_rejection_lazy_kernel<true>, dim3((unsigned)B), dim3(64 * kVerWaves),
-                       verify_rejection_lazy_lds(V), s, path_slot, path_tok, q, top_idx, z,
-                       kLog2e / temperature, u_acc, u_res, L, V, accept_len, next_tok);
+    hipLaunchKernelGGL(stage_rows_kernel<true>, dim3(grid), dim3(256), 0, s, z,
+                       kLog2e / temperature, L, V, rows, (int)nwaves, staged);
   else
-    hipLaunchKernelGGL(verify_rejection_lazy_kernel<false>, dim3((unsigned)B), dim3(64 * kVerWaves),
-                       verify_rejection_lazy_lds(V), s, path_slot, path_tok, q, top_idx, z,
-                       kLog2e / temperature, u_acc, u_res, L, V, accept_len, next_tok);
+    hipLaunchKernelGGL(stage_rows_kernel<false>, dim3(grid), dim3(256), 0, s, z,
+                       kLog2e / temperature, L, V, rows, (int)nwaves, staged);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch_lazy<true>(path_slot, path_tok, q, top_idx, z, temperature, u_acc, u_res, B, L, V,
+                    accept_len, next_tok, staged, rows, s);
   return hipGetLastError();
 }
 

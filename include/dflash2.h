@@ -19,7 +19,9 @@
  *   scores + sampling walk, one launch  dflash2_pair_sample (_mode: whole-path draws)
  *   sampling at T > 0, lossless      dflash2_path_sample (_mode), dflash2_target_lse,
  *   rejection verification           dflash2_verify_rejection
- *                                    (dflash2_verify_rejection_lazy: no lse pass)
+ *                                    (dflash2_verify_rejection_lazy: no lse pass;
+ *                                    dflash2_verify_rejection_staged: the first
+ *                                    rows of every block summed up front)
  *
  * Sources are cited by page title and section:
  *   [POST]   "DFlash 2: Keep Drafting Parallel" (Inco AI).
@@ -468,6 +470,33 @@ int dflash2_verify_rejection_lazy(const int32_t* path_slot, const int32_t* path_
                                   float temperature, const float* u_acc, const float* u_res,
                                   int B, int L, int V, int32_t* accept_len, int32_t* next_tok,
                                   void* stream);
+
+/*
+ * dflash2_verify_rejection_lazy with the first `rows` target rows of every
+ * block summed up front, all blocks at once.  [POST] "A lightweight path
+ * selector": rejection sampling restores the target's exact distribution.
+ * A first launch sums rows 0 .. rows-1 of every block (one wave per batch of
+ * 2048 tokens) into the workspace; the second runs the accept tests and the
+ * draw, one workgroup per block, and reads a row of z itself only when the
+ * test reaches a position past those rows.  Every row is summed with the
+ * same arithmetic, in the same order, as in dflash2_verify_rejection_lazy,
+ * so accept_len and next_tok are bit for bit those of that call.  A block
+ * that stops at position n reads max(n + 1, rows) rows of z.
+ * Arguments as for dflash2_verify_rejection_lazy, plus:
+ *   rows       1 .. L + 1 (else DFLASH2_EINVAL);
+ *   workspace  device memory of at least
+ *              dflash2_verify_rejection_staged_workspace(B, L, V, rows)
+ *              bytes, 4-byte aligned, overlapping no input or output; the
+ *              call overwrites it (DFLASH2_EINVAL if NULL or too small).
+ * V <= 2097152 (larger: DFLASH2_EUNSUPPORTED).  fp32 arithmetic.
+ */
+size_t dflash2_verify_rejection_staged_workspace(int B, int L, int V, int rows);
+int dflash2_verify_rejection_staged(const int32_t* path_slot, const int32_t* path_tok,
+                                    const float* q, const int32_t* top_idx, const float* z,
+                                    float temperature, const float* u_acc, const float* u_res,
+                                    int B, int L, int V, int rows, void* workspace,
+                                    size_t workspace_bytes, int32_t* accept_len,
+                                    int32_t* next_tok, void* stream);
 
 /*
  * Greedy verification.  [POST] "The right token is already in the candidates",

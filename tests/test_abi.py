@@ -308,6 +308,38 @@ def test_lazy_rejection_validation():
     assert call(0, P + 2) == EINVAL               # misaligned
 
 
+def test_staged_rejection_validation():
+    f = bd.lib().dflash2_verify_rejection_staged
+    need = bd.lib().dflash2_verify_rejection_staged_workspace(4, 2, 1000, 2)
+    assert need == 4 * 2 * (2 * 4 + 2 * 1) * 4            # [B, rows] records of 4 tiles, 1 batch
+    assert bd.lib().dflash2_verify_rejection_staged_workspace(4, 2, 1000, 0) == 0
+    assert bd.lib().dflash2_verify_rejection_staged_workspace(4, 2, 1000, 4) == 0   # rows > L + 1
+    W = P + 0x20000
+    #     slot  tok         q            ti           z   T    ua           ur
+    ok = [P, P + 0x1000, P + 0x2000, P + 0x4000, Q, 1.0, P + 0x6000, P + 0x7000,
+          4, 2, 1000, 2, W, need, P + 0x8000, P + 0x9000]
+    #     B  L  V    rows ws need  acc          nxt
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a, None)
+
+    assert call(8, 0) == 0                        # B = 0
+    assert call(11, 0) == EINVAL                  # rows < 1
+    assert call(11, 4) == EINVAL                  # rows > L + 1
+    assert call(12, None) == EINVAL               # no workspace
+    assert call(13, need - 4) == EINVAL           # workspace too small
+    assert call(12, W + 2) == EINVAL              # misaligned workspace
+    assert call(12, Q + 64) == EINVAL             # workspace inside z
+    assert call(12, P + 0x8000 - 16) == EINVAL    # workspace over accept_len
+    assert call(10, 2097152 + 256) == EUNSUP      # tiles exceed 64 KiB of LDS
+    assert call(5, 0.0) == EINVAL
+    for i in (0, 1, 2, 3, 4, 6, 7, 14, 15):
+        assert call(i, None) == EINVAL, i
+    assert call(14, Q + 64) == EINVAL             # accept_len inside z
+
+
 def test_gate_and_gated_pair_validation():
     L = bd.lib()
     cg = L.dflash2_context_gate

@@ -938,7 +938,60 @@ def test_verify_rejection_lazy_bad_tokens_and_neg_inf():
     np.testing.assert_array_equal(a, acc2.cpu().numpy())
 
 
-@pytest.mark.parametrize("lazy", [False, True])
+@pytest.mark.parametrize("B,L,V,T,rows", [
+    (50, 1, 16, 1.0, 1), (50, 1, 16, 1.0, 2),          # every row staged (L + 1 = 2)
+    (200, 4, 1000, 1.0, 2), (200, 4, 1000, 1.0, 5),
+    (24, 8, 151936, 1.0, 2), (24, 8, 151936, 1.0, 9),
+    (31, 3, 4099, 0.5, 2),                             # V % 4 != 0: scalar loads
+    (40, 64, 300, 1.0, 2), (40, 64, 300, 1.0, 65),     # long acceptance runs
+    (90, 2, 1001, 2.0, 3), (64, 8, 151936, 1.0, 1)])
+def test_verify_rejection_staged_matches_lazy(B, L, V, T, rows):
+    """The staged verification sums the first `rows` rows of every block up
+    front with the lazy verification's arithmetic and merge order: accept
+    lengths and drawn tokens equal the lazy call's bit for bit, and follow
+    the oracle under the margin rules."""
+    g = np.random.default_rng(B + L + V + rows)
+    ti, slot, tok, q, z, ua, ur = _spec_case(g, B, L, V, T)
+    if L > 8:
+        cut = g.integers(0, L + 1, B)
+        for b in range(B):
+            for t in range(cut[b]):
+                z[b, t, tok[b, t]] += np.float32(2 * np.log(V))
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    args = (d(slot), d(tok), d(q), d(ti), d(z), T, d(ua), d(ur))
+    acc0, nxt0 = bd.verify_rejection_lazy(*args)
+    ws = torch.full((bd.verify_rejection_staged_workspace(B, L, V, rows),), 255, dtype=torch.uint8,
+                    device=DEV)
+    for _ in range(2):                        # the records are rewritten by every call
+        acc1, nxt1 = bd.verify_rejection_staged(*args, rows=rows, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(acc0, acc1)
+        assert torch.equal(nxt0, nxt1)
+    a = acc1.cpu().numpy()
+    check_rejection(ti, slot, tok, q, z, T, ua, ur, a, nxt1.cpu().numpy())
+    assert ((a >= 1) & (a <= L + 1)).all()
+
+
+def test_verify_rejection_staged_bad_tokens_and_neg_inf():
+    g = np.random.default_rng(3)
+    B, L, V, T = 6, 3, 700, 1.0
+    ti, slot, tok, q, z, ua, ur = _spec_case(g, B, L, V, T)
+    z[:, :, 100:400] = -np.inf
+    z[3, 0, :] = -np.inf                      # a staged row whose mass sits on one token
+    z[3, 0, 5] = 0.0
+    tok[0, 0] = V
+    slot[1, 0] = 16
+    tok[2, 1] = -1
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    args = (d(slot), d(tok), d(q), d(ti), d(z), T, d(ua), d(ur))
+    acc0, nxt0 = bd.verify_rejection_lazy(*args)
+    acc1, nxt1 = bd.verify_rejection_staged(*args)
+    assert torch.equal(acc0, acc1) and torch.equal(nxt0, nxt1)
+    a = acc1.cpu().numpy()
+    assert a[0] == 1 and a[1] == 1 and a[2] <= 2
+
+
+@pytest.mark.parametrize("lazy", [False, True, "staged"])
 def test_verify_rejection_draw_past_the_last_prefix(lazy):
     """u_res at 1 or one ulp below it, with the row's last 256-token tile all
     -inf (V = 151936): when u * mass passes every tile prefix the draw takes
@@ -955,7 +1008,9 @@ def test_verify_rejection_draw_past_the_last_prefix(lazy):
     ur = np.where(np.arange(B) % 2 == 0, np.float32(1.0),
                   np.nextafter(np.float32(1.0), np.float32(0.0))).astype(np.float32)
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
-    if lazy:
+    if lazy == "staged":
+        acc, nxt = bd.verify_rejection_staged(d(slot), d(tok), d(q), d(ti), d(z), T, d(ua), d(ur))
+    elif lazy:
         acc, nxt = bd.verify_rejection_lazy(d(slot), d(tok), d(q), d(ti), d(z), T, d(ua), d(ur))
     else:
         lse = bd.target_lse(d(z), T)
@@ -970,7 +1025,8 @@ def test_verify_rejection_draw_past_the_last_prefix(lazy):
     np.testing.assert_array_equal(nx[same], wn[same])      # the last token with mass
 
 
-@pytest.mark.parametrize("lazy,mode", [(False, "chain"), (True, "chain"), (True, "path")])
+@pytest.mark.parametrize("lazy,mode", [(False, "chain"), (True, "chain"), (True, "path"),
+                                       ("staged", "chain")])
 def test_rejection_sampling_is_lossless_on_gpu(lazy, mode):
     # the whole sampled walk + verification on the GPU: emitted tokens follow
     # the target's softmax (chi-square on a 24-token vocabulary)
@@ -989,7 +1045,9 @@ def test_rejection_sampling_is_lossless_on_gpu(lazy, mode):
                                   mode=mode)
     zd = d(np.broadcast_to(zt, (N, L + 1, V)))
     ua, ur = d(g.random((N, L)).astype(np.float32)), d(g.random(N).astype(np.float32))
-    if lazy:
+    if lazy == "staged":
+        acc, nxt = bd.verify_rejection_staged(slot, tok, q, d(ti), zd, T, ua, ur)
+    elif lazy:
         acc, nxt = bd.verify_rejection_lazy(slot, tok, q, d(ti), zd, T, ua, ur)
     else:
         lse = bd.target_lse(zd, T)
