@@ -611,10 +611,23 @@ __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_lazy_kernel(
     // batches' (maximum, total) in the same order.
     float Mw = kNeg, Sw = 0.f;
     if (STAGED && t < rows) {
+      // lane i loads the record of batch wave + 16 i (every load in one
+      // round trip; at most 64 batches per wave as V <= 2^21), then the
+      // wave merges them in batch order
       const float* rec = staged + ((size_t)b * rows + t) * staged_row_floats(ntiles);
       const int nbatch = (ntiles + kTileBatch - 1) / kTileBatch;
-      for (int j = wave; j < nbatch; j += kVerWaves)
-        lse_merge(Mw, Sw, rec[2 * ntiles + j], rec[2 * ntiles + nbatch + j]);
+      const int nbw = (nbatch - wave + kVerWaves - 1) / kVerWaves;  // this wave's batches
+      float pm = kNeg, ps = 0.f;
+      if (lane < nbw) {
+        const int j = wave + kVerWaves * lane;
+        pm = rec[2 * ntiles + j];
+        ps = rec[2 * ntiles + nbatch + j];
+      }
+      for (int i = 0; i < nbw; ++i)
+        lse_merge(Mw, Sw, __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                              __builtin_bit_cast(int, pm), i)),
+                  __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                __builtin_bit_cast(int, ps), i)));
     } else {
       for (int t0 = wave * kTileBatch; t0 < ntiles; t0 += kVerWaves * kTileBatch) {
         float bm, bs, acc[kTileBatch];
