@@ -764,6 +764,20 @@ def main(argv=None):
         basis["pair_select_verify"] = (
             B * (2 * L * 16 * w.r * 2 + L * 16 * 8 + (4 * L + 3) * 4),
             "B (2 L 16 r 2 + L 16 8 + (4 L + 3) 4): factor rows, candidates, targets, outputs")
+    if fused and sampled:
+        # the target rows the verification reads, from this run's acceptance
+        # lengths n + 1: the staged form sums the first min(2, L + 1) rows of
+        # every block and reads the rows past them that a test reaches; the
+        # lazy form reads rows 0 .. n of each block
+        n_rows = acc.astype(np.int64)
+        if a.rejection == "staged":
+            k = min(bd.STAGED_ROWS, L + 1)
+            rows_read = B * k + int(np.maximum(n_rows - k, 0).sum())
+            why = "V 4 x (B 2 staged rows + the rows past them the tests reach)"
+        else:
+            rows_read = int(n_rows.sum())
+            why = "V 4 x (n + 1 rows of each block, n = tokens accepted)"
+        basis["verify"] = (rows_read * V * 4, why)
     stage_roof = {}
     for k, (nb, why) in basis.items():
         gbs = nb / (stage_ms[k] * 1e-3) / 1e9
