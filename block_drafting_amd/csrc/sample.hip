@@ -464,20 +464,32 @@ __device__ __forceinline__ void tile_batch_sum(const f32x4_t (&raw)[kTileBatch],
   constexpr float kNeg = -__builtin_inff();
   float zv[kTileBatch][4];
   bm = kNeg;
+  if ((t0 + kTileBatch) * kTile <= V) {  // the whole batch inside the row (uniform)
 #pragma unroll
-  for (int k = 0; k < kTileBatch; ++k)
+    for (int k = 0; k < kTileBatch; ++k)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      zv[k][i] = (t0 + k) * kTile + lane * 4 + i < V ? raw[k][i] * s2 : kNeg;
-      bm = fmaxf(bm, zv[k][i]);
-    }
+      for (int i = 0; i < 4; ++i) {
+        zv[k][i] = raw[k][i] * s2;
+        bm = fmaxf(bm, zv[k][i]);
+      }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kTileBatch; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        zv[k][i] = (t0 + k) * kTile + lane * 4 + i < V ? raw[k][i] * s2 : kNeg;
+        bm = fmaxf(bm, zv[k][i]);
+      }
+  }
   bm = wave_max(bm);
   const float ref = bm == kNeg ? 0.f : bm;  // an empty batch sums exp2(-inf) = 0
+  // The hardware exponential without exp2f's denormal-range fix-up: a term
+  // below 2^-126 cannot change a sum that holds the batch maximum's 1.
 #pragma unroll
   for (int k = 0; k < kTileBatch; ++k) {
     acc[k] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[k] += exp2f(zv[k][i] - ref);
+    for (int i = 0; i < 4; ++i) acc[k] += __builtin_amdgcn_exp2f(zv[k][i] - ref);
   }
   wave_sum_n<kTileBatch>(acc);
   bs = 0.f;
