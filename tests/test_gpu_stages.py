@@ -972,6 +972,46 @@ def test_verify_rejection_staged_matches_lazy(B, L, V, T, rows):
     assert ((a >= 1) & (a <= L + 1)).all()
 
 
+def test_verify_rejection_staged_graph_replays():
+    """The staged verification's two launches captured in a HIP graph: every
+    replay, with eager calls on other inputs through the same workspace and
+    synchronisations in between, gives the eager result."""
+    g = np.random.default_rng(17)
+    B, L, V, T = 64, 8, 151936, 1.0
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    case = [d(a) for a in _spec_case(g, B, L, V, T)]
+    other = [d(a) for a in _spec_case(g, B, L, V, T)]
+
+    def args(c):
+        ti, slot, tok, q, z, ua, ur = c
+        return (slot, tok, q, ti, z, T, ua, ur)
+
+    ws = torch.empty(bd.verify_rejection_staged_workspace(B, L, V, 2), dtype=torch.uint8, device=DEV)
+    acc = torch.empty((B,), dtype=torch.int32, device=DEV)
+    nxt = torch.empty((B,), dtype=torch.int32, device=DEV)
+    bd.verify_rejection_staged(*args(case), acc, nxt, rows=2, workspace=ws)
+    torch.cuda.synchronize()
+    want = (acc.clone(), nxt.clone())
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        bd.verify_rejection_staged(*args(case), acc, nxt, rows=2, workspace=ws)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            bd.verify_rejection_staged(*args(case), acc, nxt, rows=2, workspace=ws)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        a2, n2 = bd.verify_rejection_staged(*args(other), rows=2, workspace=ws)
+        torch.cuda.synchronize()
+        acc.fill_(-7)
+        nxt.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(acc, want[0]) and torch.equal(nxt, want[1])
+
+
 def test_verify_rejection_staged_bad_tokens_and_neg_inf():
     g = np.random.default_rng(3)
     B, L, V, T = 6, 3, 700, 1.0
