@@ -434,15 +434,8 @@ __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_kernel(
                accept_len + b, next_tok + b, n);
 }
 
-
-// One batch of a target row: kTileBatch consecutive tiles from tile t0,
-// values scaled by s2 (base 2), tokens past V as -inf.  Every lane ends with
-// the batch maximum bm (the tiles' common reference, 0 in its place when
-// the batch is empty), the tiles' sums acc[k] of 2^(value - reference) and
-// their total bs.  Every load is issued before the first use (index
-// clamped into the row): a use or a per-lane branch between two loads makes
-// each wait for the one before.  The lazy verification's row pass and the
-// staged rows share this code, so their sums are the same bit for bit.
+// The loads of one batch (tile_batch below): lane l takes 16 bytes of each
+// of the kTileBatch tiles, index clamped into the row.
 template <bool VEC>
 __device__ __forceinline__ void tile_batch_load(const float* __restrict__ zr, int V, int t0,
                                                 int lane, f32x4_t (&raw)[kTileBatch]) {
@@ -459,8 +452,9 @@ __device__ __forceinline__ void tile_batch_load(const float* __restrict__ zr, in
 }
 
 __device__ __forceinline__ void tile_batch_sum(const f32x4_t (&raw)[kTileBatch], int V, int t0,
-                                               int lane, float s2, float& bm,
-                                               float (&acc)[kTileBatch], float& bs) {
+                                               int lane, float s2, float& bm, float& tile,
+                                               float& bs) {
+  static_assert(kTileBatch == 8, "the reduce-scatter below is sized for 8 tiles");
   constexpr float kNeg = -__builtin_inff();
   float zv[kTileBatch][4];
   bm = kNeg;
@@ -485,33 +479,58 @@ __device__ __forceinline__ void tile_batch_sum(const f32x4_t (&raw)[kTileBatch],
   const float ref = bm == kNeg ? 0.f : bm;  // an empty batch sums exp2(-inf) = 0
   // The hardware exponential without exp2f's denormal-range fix-up: a term
   // below 2^-126 cannot change a sum that holds the batch maximum's 1.
+  float v[kTileBatch];
 #pragma unroll
   for (int k = 0; k < kTileBatch; ++k) {
-    acc[k] = 0.f;
+    v[k] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[k] += __builtin_amdgcn_exp2f(zv[k][i] - ref);
+    for (int i = 0; i < 4; ++i) v[k] += __builtin_amdgcn_exp2f(zv[k][i] - ref);
   }
-  wave_sum_n<kTileBatch>(acc);
-  bs = 0.f;
+  // Reduce-scatter over lane bits 5, 4, 3: each step a lane keeps half of
+  // its tiles (the upper half when the bit is set) and adds its partner's
+  // sums of them, so after three steps lane l holds tile (l >> 3) & 7 of
+  // the batch; a butterfly over bits 2..0 finishes that tile in its group
+  // of 8 lanes, and one over bits 3..5 the batch total (13 exchanges in
+  // place of 48).
+  auto half = [&](auto dtag, int n) {
+    constexpr int D = decltype(dtag)::value;
+    const bool hi = (lane & D) != 0;
 #pragma unroll
-  for (int k = 0; k < kTileBatch; ++k) bs += acc[k];
+    for (int j = 0; j < 4; ++j)
+      if (j < n / 2) {
+        const float send = hi ? v[j] : v[j + n / 2];
+        const float keep = hi ? v[j + n / 2] : v[j];
+        v[j] = keep + __uint_as_float(xor_lane<D>(__float_as_uint(send)));
+      }
+  };
+  half(std::integral_constant<int, 32>{}, 8);
+  half(std::integral_constant<int, 16>{}, 4);
+  half(std::integral_constant<int, 8>{}, 2);
+  tile = v[0];
+  tile += __uint_as_float(xor_lane<4>(__float_as_uint(tile)));
+  tile += __uint_as_float(xor_lane<2>(__float_as_uint(tile)));
+  tile += __uint_as_float(xor_lane<1>(__float_as_uint(tile)));
+  bs = tile;
+  bs += __uint_as_float(xor_lane<8>(__float_as_uint(bs)));
+  bs += __uint_as_float(xor_lane<16>(__float_as_uint(bs)));
+  bs += __uint_as_float(xor_lane<32>(__float_as_uint(bs)));
 }
 
 // One batch of a target row: kTileBatch consecutive tiles from tile t0,
 // values scaled by s2 (base 2), tokens past V as -inf.  Every lane ends with
 // the batch maximum bm (the tiles' common reference, 0 in its place when
-// the batch is empty), the tiles' sums acc[k] of 2^(value - reference) and
-// their total bs.  Every load is issued before the first use (index
-// clamped into the row): a use or a per-lane branch between two loads makes
-// each wait for the one before.  The lazy verification's row pass and the
-// staged rows share this code, so their sums are the same bit for bit.
+// the batch is empty) and the total bs of 2^(value - reference); lane l
+// holds in `tile` the sum of tile t0 + ((l >> 3) & 7).  Every load is issued
+// before the first use (index clamped into the row): a use or a per-lane
+// branch between two loads makes each wait for the one before.  The lazy
+// verification's row pass and the staged rows share this code, so their
+// sums are the same bit for bit.
 template <bool VEC>
 __device__ __forceinline__ void tile_batch(const float* __restrict__ zr, int V, int t0, int lane,
-                                           float s2, float& bm, float (&acc)[kTileBatch],
-                                           float& bs) {
+                                           float s2, float& bm, float& tile, float& bs) {
   f32x4_t raw[kTileBatch];
   tile_batch_load<VEC>(zr, V, t0, lane, raw);
-  tile_batch_sum(raw, V, t0, lane, s2, bm, acc, bs);
+  tile_batch_sum(raw, V, t0, lane, s2, bm, tile, bs);
 }
 
 // Per (block, row) record of a staged row: the tiles' batch maxima [ntiles],
@@ -553,15 +572,14 @@ __global__ __launch_bounds__(256) void stage_rows_kernel(const float* __restrict
   for (int i = 0; i < kStageBatches; ++i) {
     const int j = j0 + i;
     if (j >= nbatch) break;  // uniform
-    float bm, bs, acc[kTileBatch];
-    tile_batch_sum(raw[i], V, j * kTileBatch, lane, s2, bm, acc, bs);
+    float bm, tile, bs;
+    tile_batch_sum(raw[i], V, j * kTileBatch, lane, s2, bm, tile, bs);
+    const int tk = j * kTileBatch + ((lane >> 3) & 7);  // the tile this lane's group holds
+    if ((lane & 7) == 0 && tk < ntiles) {
+      rec[tk] = bm;
+      rec[ntiles + tk] = tile;
+    }
     if (lane == 0) {
-#pragma unroll
-      for (int k = 0; k < kTileBatch; ++k)
-        if (j * kTileBatch + k < ntiles) {
-          rec[j * kTileBatch + k] = bm;
-          rec[ntiles + j * kTileBatch + k] = acc[k];
-        }
       rec[2 * ntiles + j] = bm;
       rec[2 * ntiles + nbatch + j] = bs;
     }
@@ -642,15 +660,12 @@ __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_lazy_kernel(
                                                 __builtin_bit_cast(int, ps), i)));
     } else {
       for (int t0 = wave * kTileBatch; t0 < ntiles; t0 += kVerWaves * kTileBatch) {
-        float bm, bs, acc[kTileBatch];
-        tile_batch<VEC>(zr, V, t0, lane, s2, bm, acc, bs);
-        if (lane == 0) {
-#pragma unroll
-          for (int k = 0; k < kTileBatch; ++k)
-            if (t0 + k < ntiles) {
-              tref[t0 + k] = bm;
-              tsum[t0 + k] = acc[k];
-            }
+        float bm, tile, bs;
+        tile_batch<VEC>(zr, V, t0, lane, s2, bm, tile, bs);
+        const int tk = t0 + ((lane >> 3) & 7);  // the tile this lane's group holds
+        if ((lane & 7) == 0 && tk < ntiles) {
+          tref[tk] = bm;
+          tsum[tk] = tile;
         }
         lse_merge(Mw, Sw, bm, bs);
       }
