@@ -24,6 +24,9 @@
 //                       accept test reaches: one pass per row keeps every
 //                       tile's (reference max, sum) in LDS, which also gives
 //                       the draw's tile masses at the row where the test stops.
+// stage_rows_kernel     the first rows of every block summed up front, all
+//                       blocks at once, with the row pass's own batch code;
+//                       the lazy kernel (STAGED) then starts from those sums.
 //
 // The sampling walk itself (sample_walk) lives in walk.hpp, shared with the
 // fused scores-and-walk kernel.
@@ -593,6 +596,8 @@ __global__ __launch_bounds__(256) void stage_rows_kernel(const float* __restrict
 // walk stops, the tile masses of the draw, so the stopping row is not read
 // again.  A block that stops at position n reads n + 1 rows instead of all
 // L + 1.  The accept rule and the draw are those of verify_rejection_kernel.
+// STAGED: rows below `rows` come from stage_rows_kernel's records instead,
+// merged in the order the row pass would merge them.
 template <bool VEC, bool STAGED>
 __global__ __launch_bounds__(64 * kVerWaves) void verify_rejection_lazy_kernel(
     const int32_t* __restrict__ path_slot, const int32_t* __restrict__ path_tok,
