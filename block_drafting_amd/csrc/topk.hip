@@ -290,6 +290,7 @@ __global__ __launch_bounds__(64) void topk16_merge_kernel(const uint64_t* __rest
 // sort.  Exact: the result is the full scan's, bit for bit.
 constexpr int kPruneBatch = 16;
 constexpr int kMaxChunk = 16;      // tile maxima per lane per pass (1024 tiles)
+constexpr int kFewChunk = 10;      // rows of at most 640 tiles (V <= 163840) take 10
 constexpr int kCandCap = 512;      // LDS candidate keys before a merge (a tile adds at most 256)
 
 // Merge n keys of cand into the list (this lane's slot key), 48 per sort.
@@ -325,7 +326,9 @@ constexpr uint32_t kOrdNegInf = 0x007fffffu;
 // of the tile) in kCandSlots (value bits, column) slots, the first cnt of
 // them used.  Such a tile is read as those slots: lanes 0 and 1 load two
 // slots each in place of the tile's 1 KB.
-template <int VEC, bool CAND>
+// CH: tile maxima per lane per pass; each wave's work is mostly instruction
+// issue on a SIMD of its own, so rows of few tiles take a shorter unroll.
+template <int VEC, bool CAND, int CH>
 __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restrict__ logits,
                                                            const float* __restrict__ tmax, int V,
                                                            int nt, float* __restrict__ top_val,
@@ -333,7 +336,7 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
                                                            const int* __restrict__ cnt,
                                                            const uint2* __restrict__ slots) {
   static_assert(!CAND || kCandSlots == 4, "two slots per 16-byte load, lanes 0 and 1");
-  constexpr int kList = 64 * kMaxChunk;
+  constexpr int kList = 64 * CH;
   // LDS kept small (9.5 KB) so that many rows are in flight per CU.  A list
   // entry is tile * 8 + (count + 1), the count (CAND) of kCandDense = -1 ..
   // kCandSlots; the tile maxima's orders are only read for the first 64
@@ -349,25 +352,25 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
   // 1. tau from the lane maxima.  o = order of a tile maximum, 0 for a tile
   // index past nt (every element's order is > 0).
   uint32_t lmax = 0;
-  uint32_t o[kMaxChunk];  // the last pass's orders (all of them when nt <= kList)
-  int cn[kMaxChunk];      // CAND: the same tiles' counts
+  uint32_t o[CH];  // the last pass's orders (all of them when nt <= kList)
+  int cn[CH];      // CAND: the same tiles' counts
   auto load_orders = [&](int c0) {
-    float v[kMaxChunk];
+    float v[CH];
 #pragma unroll
-    for (int k = 0; k < kMaxChunk; ++k) v[k] = tm[min(c0 + k * 64 + lane, nt - 1)];
+    for (int k = 0; k < CH; ++k) v[k] = tm[min(c0 + k * 64 + lane, nt - 1)];
     if constexpr (CAND) {
 #pragma unroll
-      for (int k = 0; k < kMaxChunk; ++k)
+      for (int k = 0; k < CH; ++k)
         cn[k] = cnt[(size_t)m * nt + min(c0 + k * 64 + lane, nt - 1)];
     }
 #pragma unroll
-    for (int k = 0; k < kMaxChunk; ++k)
+    for (int k = 0; k < CH; ++k)
       o[k] = ord_of(v[k]) & (0u - (uint32_t)(c0 + k * 64 + lane < nt));
   };
   for (int c0 = 0; c0 < nt; c0 += kList) {
     load_orders(c0);
 #pragma unroll
-    for (int k = 0; k < kMaxChunk; ++k) lmax = max(lmax, o[k]);
+    for (int k = 0; k < CH; ++k) lmax = max(lmax, o[k]);
   }
   const uint64_t srt = wave_sort_desc(((uint64_t)lmax << 32) | (uint32_t)(~lane));
   uint32_t tau = nt >= 16 ? (uint32_t)(readlane64(srt, 15) >> 32) : 0u;
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
     const uint32_t tmin = max(tau, 1u);
     int nsel = 0;
 #pragma unroll
-    for (int k = 0; k < kMaxChunk; ++k) {
+    for (int k = 0; k < CH; ++k) {
       const bool s = o[k] >= tmin;
       const uint64_t sel = __ballot(s);
       const int below = lanes_below(sel);
@@ -467,6 +470,25 @@ __global__ __launch_bounds__(64) void topk16_pruned_kernel(const float* __restri
   write_final(top, top_val + (size_t)m * kTopK, top_idx + (size_t)m * kTopK);
 }
 
+template <bool CAND>
+void launch_pruned(bool vec, bool few, const float* logits, const float* tmax, int V, int nt,
+                   float* top_val, int32_t* top_idx, const int* cnt, const uint2* sl, int M,
+                   hipStream_t s) {
+  const dim3 g((unsigned)M), b(64);
+  if (vec && few)
+    hipLaunchKernelGGL((topk16_pruned_kernel<4, CAND, kFewChunk>), g, b, 0, s, logits, tmax, V,
+                       nt, top_val, top_idx, cnt, sl);
+  else if (vec)
+    hipLaunchKernelGGL((topk16_pruned_kernel<4, CAND, kMaxChunk>), g, b, 0, s, logits, tmax, V,
+                       nt, top_val, top_idx, cnt, sl);
+  else if (few)
+    hipLaunchKernelGGL((topk16_pruned_kernel<1, CAND, kFewChunk>), g, b, 0, s, logits, tmax, V,
+                       nt, top_val, top_idx, cnt, sl);
+  else
+    hipLaunchKernelGGL((topk16_pruned_kernel<1, CAND, kMaxChunk>), g, b, 0, s, logits, tmax, V,
+                       nt, top_val, top_idx, cnt, sl);
+}
+
 }  // namespace
 
 hipError_t launch_topk16_tilemax(const float* logits, const float* tmax, float* top_val,
@@ -474,12 +496,8 @@ hipError_t launch_topk16_tilemax(const float* logits, const float* tmax, float* 
   if (M == 0) return hipSuccess;
   const int nt = (V + kTileMaxCols - 1) / kTileMaxCols;
   const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
-  if (vec)
-    hipLaunchKernelGGL((topk16_pruned_kernel<4, false>), dim3((unsigned)M), dim3(64), 0, s, logits,
-                       tmax, V, nt, top_val, top_idx, nullptr, nullptr);
-  else
-    hipLaunchKernelGGL((topk16_pruned_kernel<1, false>), dim3((unsigned)M), dim3(64), 0, s, logits,
-                       tmax, V, nt, top_val, top_idx, nullptr, nullptr);
+  launch_pruned<false>(vec, nt <= 64 * kFewChunk, logits, tmax, V, nt, top_val, top_idx, nullptr,
+                       nullptr, M, s);
   return hipGetLastError();
 }
 
@@ -490,12 +508,8 @@ hipError_t launch_topk16_cand(const float* logits, const float* tmax, const int*
   const int nt = (V + kTileMaxCols - 1) / kTileMaxCols;
   const uint2* sl = static_cast<const uint2*>(slots);  // 16-byte aligned
   const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
-  if (vec)
-    hipLaunchKernelGGL((topk16_pruned_kernel<4, true>), dim3((unsigned)M), dim3(64), 0, s, logits,
-                       tmax, V, nt, top_val, top_idx, cnt, sl);
-  else
-    hipLaunchKernelGGL((topk16_pruned_kernel<1, true>), dim3((unsigned)M), dim3(64), 0, s, logits,
-                       tmax, V, nt, top_val, top_idx, cnt, sl);
+  launch_pruned<true>(vec, nt <= 64 * kFewChunk, logits, tmax, V, nt, top_val, top_idx, cnt, sl,
+                      M, s);
   return hipGetLastError();
 }
 
