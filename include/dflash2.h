@@ -489,6 +489,8 @@ int dflash2_verify_rejection_lazy(const int32_t* path_slot, const int32_t* path_
  *              bytes, 4-byte aligned, overlapping no input or output; the
  *              call overwrites it (DFLASH2_EINVAL if NULL or too small).
  * V <= 2097152 (larger: DFLASH2_EUNSUPPORTED).  fp32 arithmetic.
+ * dflash2_verify_rejection_staged_workspace returns the workspace bytes, or
+ * 0 when B, L, V or rows is out of range.
  */
 size_t dflash2_verify_rejection_staged_workspace(int B, int L, int V, int rows);
 int dflash2_verify_rejection_staged(const int32_t* path_slot, const int32_t* path_tok,
